@@ -1,0 +1,189 @@
+"""fp64 CPU oracle for the fused pointwise + row-reduction operations.
+
+TEST INFRASTRUCTURE ONLY. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package. The GPU library
+(``pointwise_reduction_amd``) never imports, loads or calls it, and the two
+share no code: the only common dependency is the seeded input generator
+(``synth``).
+
+The arithmetic lives in ``oracle.c`` (plain C, fp64, sequential loops; each
+function cites the passage it implements). This module only compiles it with
+gcc and marshals numpy arrays through ctypes.
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SO = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+I64, I32, F64, U16 = ctypes.c_int64, ctypes.c_int32, ctypes.c_double, ctypes.c_uint16
+P = ctypes.c_void_p
+
+
+def build(verbose=False):
+    """Compile oracle.c into liboracle.so (gcc, no GPU toolchain involved)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-fno-fast-math", "-shared", "-fPIC", "-o", _SO,
+           os.path.join(_HERE, "oracle.c"), "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.check_call(cmd)
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_SO):
+        build()
+    lib = ctypes.CDLL(_SO)
+    sig = {
+        "orc_bf16_to_double": (F64, [U16]),
+        "orc_double_to_bf16": (U16, [F64]),
+        "orc_sum_relu_add": (None, [P, P, I64, I64, I64, I64, P, P]),
+        "orc_softmax_f64": (None, [P, I64, P]),
+        "orc_softmax_rows": (None, [P, I64, I64, I64, P, P, P, I64, P, P]),
+        "orc_md_combine": (None, [F64, F64, F64, F64, P, P]),
+        "orc_md_fold": (None, [P, I64, P, P]),
+        "orc_online_attention_row": (None, [P, P, I64, I64, P, P, P, P]),
+        "orc_layernorm_rows": (None, [P, P, P, I64, I64, I64, F64, P, P, P, I64]),
+        "orc_sumsq": (F64, [P, I64]),
+        "orc_sumsq_rows": (None, [P, I64, I64, I64, P]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _rows2d(x, dtype):
+    """Return (array, rows, cols, row_stride) for a 2-D array whose inner stride is 1."""
+    x = np.asarray(x)
+    assert x.dtype == dtype and x.ndim == 2
+    assert x.strides[1] == x.itemsize, "inner stride must be 1"
+    return x, x.shape[0], x.shape[1], x.strides[0] // x.itemsize
+
+
+# ------------------------------------------------------------------ bf16
+
+
+def bf16_to_f64(bits):
+    return float(_load().orc_bf16_to_double(int(bits)))
+
+
+def f64_to_bf16(v):
+    return int(_load().orc_double_to_bf16(float(v)))
+
+
+# ------------------------------------------------------------------ C1
+
+
+def sum_relu_add(a, b):
+    """out[i] = sum_r 2*relu(a[i,r]+b[i,r]); returns (out fp32, out fp64)."""
+    a, rows, cols, a_rs = _rows2d(a, np.float32)
+    b, rows_b, cols_b, b_rs = _rows2d(b, np.float32)
+    assert (rows, cols) == (rows_b, cols_b)
+    out = np.empty(rows, dtype=np.float32)
+    out64 = np.empty(rows, dtype=np.float64)
+    _load().orc_sum_relu_add(_p(a), _p(b), rows, cols, a_rs, b_rs, _p(out), _p(out64))
+    return out, out64
+
+
+# ------------------------------------------------------------------ softmax
+
+
+def softmax_f64(x):
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    y = np.empty_like(x)
+    _load().orc_softmax_f64(_p(x), x.size, _p(y))
+    return y
+
+
+def softmax_rows(x, lengths=None, cols=None):
+    """Row softmax of fp32 rows (ragged when `lengths` is given).
+
+    x may be a 2-D view with unit inner stride. `cols` (default x.shape[1]) is
+    the row capacity lengths are clamped to. Returns (y64, argmax): y64 is a
+    float64 array shaped like x[:, :cols] holding NaN wherever the oracle did
+    not write (j >= len), argmax is int32 (-1 for an empty row).
+    """
+    x, rows, xc, x_rs = _rows2d(x, np.float32)
+    cols = xc if cols is None else cols
+    assert cols <= xc
+    L = None
+    if lengths is not None:
+        L = np.ascontiguousarray(lengths, dtype=np.int32)
+        assert L.shape == (rows,)
+    y64 = np.full((rows, cols), np.nan, dtype=np.float64)
+    am = np.empty(rows, dtype=np.int32)
+    scratch = np.empty(2 * max(cols, 1), dtype=np.float64)
+    _load().orc_softmax_rows(_p(x), rows, cols, x_rs, _p(L), None, _p(y64), cols, _p(am), _p(scratch))
+    return y64, am
+
+
+def md_combine(m1, d1, m2, d2):
+    m = ctypes.c_double()
+    d = ctypes.c_double()
+    _load().orc_md_combine(m1, d1, m2, d2, ctypes.byref(m), ctypes.byref(d))
+    return m.value, d.value
+
+
+def md_fold(x):
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    m = ctypes.c_double()
+    d = ctypes.c_double()
+    _load().orc_md_fold(_p(x), x.size, ctypes.byref(m), ctypes.byref(d))
+    return m.value, d.value
+
+
+def online_attention_row(scores, V):
+    """(m, l, a, o) after the online update over all scores ([HG12] 12.3)."""
+    s = np.ascontiguousarray(scores, dtype=np.float64)
+    V = np.ascontiguousarray(V, dtype=np.float64)
+    n, dv = V.shape
+    assert s.shape == (n,)
+    a = np.empty(dv)
+    o = np.empty(dv)
+    m = ctypes.c_double()
+    l = ctypes.c_double()
+    _load().orc_online_attention_row(_p(s), _p(V), n, dv, ctypes.byref(m), ctypes.byref(l), _p(a), _p(o))
+    return m.value, l.value, a, o
+
+
+# ------------------------------------------------------------------ LayerNorm
+
+
+def layernorm_rows(x_bf16, gamma=None, beta=None, eps=1e-5):
+    """LayerNorm over rows of bf16 bits (uint16). Returns (y_bf16, y64, mag)."""
+    x, rows, cols, x_rs = _rows2d(x_bf16, np.uint16)
+    g = None if gamma is None else np.ascontiguousarray(gamma, dtype=np.uint16)
+    b = None if beta is None else np.ascontiguousarray(beta, dtype=np.uint16)
+    y = np.empty((rows, cols), dtype=np.uint16)
+    y64 = np.empty((rows, cols), dtype=np.float64)
+    mag = np.empty((rows, cols), dtype=np.float64)
+    _load().orc_layernorm_rows(_p(x), _p(g), _p(b), rows, cols, x_rs, float(eps), _p(y), _p(y64), _p(mag), cols)
+    return y, y64, mag
+
+
+# ------------------------------------------------------------------ sum of squares
+
+
+def sumsq(x):
+    x = np.ascontiguousarray(x, dtype=np.float32).reshape(-1)
+    return float(_load().orc_sumsq(_p(x), x.size))
+
+
+def sumsq_rows(x):
+    x, rows, cols, rs = _rows2d(x, np.float32)
+    out = np.empty(rows, dtype=np.float64)
+    _load().orc_sumsq_rows(_p(x), rows, cols, rs, _p(out))
+    return out

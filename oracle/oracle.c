@@ -1,0 +1,257 @@
+/*
+ * oracle.c - plain, slow, fp64 CPU reference for the fused pointwise-prologue
+ * + row-reduction operations.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path may link, load or
+ * call this file: it exists so that tests, the smoke check and the CPU
+ * baseline leg of the benchmark can check the GPU library against the plain
+ * definitions. It shares no code, header, table or helper with the GPU
+ * library; the only thing both sides see is the seeded input generator.
+ *
+ * Every function below is the plain definition written out with sequential
+ * loops and fp64 accumulation. No blocking, fusion or reordering is done
+ * beyond what the cited definition states. Sources (web pages):
+ *   [Stax4]  "Stax (4): GPU Codegen and Dynamic Shapes" (TensorPlay blog),
+ *            section 9.2 (Listing 9.1, Example 1.1), 9.4 (Listing 9.4,
+ *            Example 6.2), 9.5 (softmax definition, Listing 9.5, the (m, d)
+ *            merge and Proposition 9.1), 10.2 (Example 10.1).
+ *   [HG12]   "hello-gpu, Chapter 12: Fusion", section 12.1 (worked example)
+ *            and 12.3 (online m, l, a update).
+ *   [L8]     "CMU 15-779 Lecture 8: ML Compilers Part 1, Tile-based DSLs",
+ *            section 3 (fused softmax) and Exercise 1 (row L2 norm).
+ * Readings of points the pages leave open are stated at each function.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------ bf16 */
+
+double orc_bf16_to_double(uint16_t h) {
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+/*
+ * Round an fp64 value once to bf16 (1 sign, 8 exponent, 7 fraction bits),
+ * round-to-nearest, ties to even. Done on the value, not on bit patterns:
+ * the quantum of a bf16 number with unbiased exponent E is 2^(E-7), with E
+ * clamped below at -126 (subnormals). NaN -> quiet NaN 0x7FC0 (sign kept).
+ */
+uint16_t orc_double_to_bf16(double v) {
+    uint16_t sign = signbit(v) ? 0x8000u : 0u;
+    if (isnan(v)) return (uint16_t)(sign | 0x7FC0u);
+    double a = fabs(v);
+    if (isinf(a)) return (uint16_t)(sign | 0x7F80u);
+    if (a == 0.0) return sign;
+    int e;
+    frexp(a, &e);          /* a = f * 2^e, f in [0.5, 1) */
+    int E = e - 1;         /* a = g * 2^E, g in [1, 2) */
+    if (E < -126) E = -126;
+    double q = ldexp(a, 7 - E);     /* a in units of the quantum, exact */
+    double r = nearbyint(q);        /* default rounding mode: ties to even */
+    double res = ldexp(r, E - 7);
+    const double maxbf = ldexp(255.0, 120); /* (2 - 2^-7) * 2^127 */
+    if (res > maxbf) return (uint16_t)(sign | 0x7F80u);
+    float f = (float)res;           /* exact: every bf16 value is an fp32 value */
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    return (uint16_t)(sign | (u >> 16));
+}
+
+/* ------------------------------------------------- Example 1.1 (C1) */
+
+/*
+ * out[i] = sum_r 2 * relu(a[i,r] + b[i,r])      [Stax4] 9.2, Listing 9.1;
+ *                                               10.2, Example 10.1.
+ * The add is an fp32 add (the kernel adds two fp32 loads); relu propagates
+ * NaN (maximum with NaN propagation, [Stax4] 9.2 part (3)); the sum is fp64.
+ * Reading: relu(-0) = +0 and +/-inf follow IEEE; neither changes a sum whose
+ * identity is +0. out64 (nullable) receives the fp64 value before rounding.
+ */
+void orc_sum_relu_add(const float* a, const float* b, int64_t rows, int64_t cols, int64_t a_rs, int64_t b_rs,
+                      float* out, double* out64) {
+    for (int64_t i = 0; i < rows; ++i) {
+        double acc = 0.0;
+        for (int64_t r = 0; r < cols; ++r) {
+            float t = (float)((double)a[i * a_rs + r] + (double)b[i * b_rs + r]); /* fp32 add */
+            double rt = isnan(t) ? (double)t : (t > 0.0f ? (double)t : 0.0);
+            acc += 2.0 * rt;
+        }
+        out[i] = (float)acc;
+        if (out64) out64[i] = acc;
+    }
+}
+
+/* --------------------------------------------------- softmax (C2, C5) */
+
+/*
+ * Softmax of one row held in fp64, the definition of [Stax4] 9.5:
+ *   m = max_k x_k,  y_j = e^(x_j - m) / sum_k e^(x_k - m).
+ * Two passes (max, then sum of exponentials), exp from the C library in
+ * fp64. Reading: a NaN anywhere makes m NaN and so the whole row NaN.
+ * Returns the argmax: the smallest j with x_j == m (first occurrence;
+ * reading, the pages are silent on ties); with a NaN, the first NaN.
+ */
+static int64_t softmax_row_f64(const double* x, int64_t n, double* y) {
+    if (n <= 0) return -1;
+    double m = x[0];
+    int64_t am = 0;
+    for (int64_t j = 1; j < n; ++j) {
+        if (isnan(m)) break;
+        if (isnan(x[j]) || x[j] > m) {
+            m = x[j];
+            am = j;
+        }
+    }
+    double d = 0.0;
+    for (int64_t j = 0; j < n; ++j) d += exp(x[j] - m);
+    for (int64_t j = 0; j < n; ++j) y[j] = exp(x[j] - m) / d;
+    return am;
+}
+
+void orc_softmax_f64(const double* x, int64_t n, double* y) { (void)softmax_row_f64(x, n, y); }
+
+/*
+ * Row softmax over fp32 rows, optionally ragged: row r covers j < len_r
+ * where len_r = lengths[r] clamped to [0, cols] (lengths NULL: len_r = cols).
+ * Only j < len_r is read or written; the padded tail of x is never read and
+ * the tail of y is left untouched ([Stax4] 10.3: loop bounds are runtime
+ * values, so the masks stay).
+ *   y   (nullable): fp32 result, rounded once from fp64.
+ *   y64 (nullable): fp64 result, row stride y_rs.
+ *   argmax (nullable): first index of the row maximum; -1 for an empty row.
+ * `scratch` must hold 2 * cols doubles.
+ */
+void orc_softmax_rows(const float* x, int64_t rows, int64_t cols, int64_t x_rs, const int32_t* lengths, float* y,
+                      double* y64, int64_t y_rs, int32_t* argmax, double* scratch) {
+    double* xin = scratch;
+    double* yout = scratch + cols;
+    for (int64_t r = 0; r < rows; ++r) {
+        int64_t L = cols;
+        if (lengths) {
+            L = lengths[r];
+            if (L < 0) L = 0;
+            if (L > cols) L = cols;
+        }
+        for (int64_t j = 0; j < L; ++j) xin[j] = (double)x[r * x_rs + j];
+        int64_t am = softmax_row_f64(xin, L, yout);
+        for (int64_t j = 0; j < L; ++j) {
+            if (y) y[r * y_rs + j] = (float)yout[j];
+            if (y64) y64[r * y_rs + j] = yout[j];
+        }
+        if (argmax) argmax[r] = (int32_t)am;
+    }
+}
+
+/* ------------------------------------------ the (m, d) monoid, online update */
+
+/*
+ * (m1, d1) (+) (m2, d2) = (M, d1 e^(m1 - M) + d2 e^(m2 - M)), M = max(m1, m2)
+ * [Stax4] 9.5. The identity is (-inf, 0); (-inf,0) (+) (-inf,0) = (-inf,0).
+ */
+void orc_md_combine(double m1, double d1, double m2, double d2, double* m, double* d) {
+    double M = m1 > m2 ? m1 : m2;
+    if (isinf(M) && M < 0) {
+        *m = M;
+        *d = 0.0;
+        return;
+    }
+    *m = M;
+    *d = d1 * exp(m1 - M) + d2 * exp(m2 - M);
+}
+
+/* Fold a sequence with (+), left to right, each element x as (x, 1). */
+void orc_md_fold(const double* x, int64_t n, double* m, double* d) {
+    double cm = -INFINITY, cd = 0.0;
+    for (int64_t j = 0; j < n; ++j) orc_md_combine(cm, cd, x[j], 1.0, &cm, &cd);
+    *m = cm;
+    *d = cd;
+}
+
+/*
+ * One query row of attention by the online update of [HG12] 12.3: state
+ * (m, l, a) starts at (-inf, 0, 0); for each score s_j with value row V_j:
+ *   m' = max(m, s_j), alpha = e^(m - m'), beta = e^(s_j - m'),
+ *   l' = alpha l + beta,  a' = alpha a + beta V_j;  output o = a / l.
+ * V is n x dv row-major. Outputs the final m, l, a[dv] and o[dv].
+ */
+void orc_online_attention_row(const double* s, const double* V, int64_t n, int64_t dv, double* m_out, double* l_out,
+                              double* a, double* o) {
+    double m = -INFINITY, l = 0.0;
+    for (int64_t k = 0; k < dv; ++k) a[k] = 0.0;
+    for (int64_t j = 0; j < n; ++j) {
+        double mp = s[j] > m ? s[j] : m;
+        double alpha = exp(m - mp); /* m = -inf on the first step gives 0 */
+        double beta = exp(s[j] - mp);
+        l = alpha * l + beta;
+        for (int64_t k = 0; k < dv; ++k) a[k] = alpha * a[k] + beta * V[j * dv + k];
+        m = mp;
+    }
+    *m_out = m;
+    *l_out = l;
+    for (int64_t k = 0; k < dv; ++k) o[k] = a[k] / l;
+}
+
+/* ------------------------------------------------------ LayerNorm (C3) */
+
+/*
+ * y = (x - mu) / sqrt(var + eps) * gamma + beta over each row, on bf16 data.
+ * The pages do not define LayerNorm. They name variance reductions that also
+ * output the mean ([Stax4] 10.4) and state that half-precision arithmetic is
+ * carried out in float32 ([Stax4] 9.8, tensor cores and mixed precision;
+ * Listing 9.5 upcasts its load). Readings: mu = sum(x)/N;
+ * var = sum((x - mu)^2)/N (biased, the
+ * two-pass definition, not Welford); eps inside the square root; gamma and
+ * beta per column (NULL: 1 and 0). All arithmetic in fp64, one rounding to
+ * bf16 at the end (round to nearest even).
+ *   y   (nullable): bf16 result bits.
+ *   y64 (nullable): fp64 result before rounding.
+ *   mag (nullable): |(x - mu) * rstd * gamma| + |beta|, the size of the
+ *                   terms that make y (used for the near-zero tolerance).
+ * Output arrays use row stride y_rs.
+ */
+void orc_layernorm_rows(const uint16_t* x, const uint16_t* gamma, const uint16_t* beta, int64_t rows, int64_t cols,
+                        int64_t x_rs, double eps, uint16_t* y, double* y64, double* mag, int64_t y_rs) {
+    for (int64_t r = 0; r < rows; ++r) {
+        const uint16_t* xr = x + r * x_rs;
+        double s = 0.0;
+        for (int64_t j = 0; j < cols; ++j) s += orc_bf16_to_double(xr[j]);
+        double mu = s / (double)cols;
+        double q = 0.0;
+        for (int64_t j = 0; j < cols; ++j) {
+            double t = orc_bf16_to_double(xr[j]) - mu;
+            q += t * t;
+        }
+        double var = q / (double)cols;
+        double rstd = 1.0 / sqrt(var + eps);
+        for (int64_t j = 0; j < cols; ++j) {
+            double g = gamma ? orc_bf16_to_double(gamma[j]) : 1.0;
+            double b = beta ? orc_bf16_to_double(beta[j]) : 0.0;
+            double t = (orc_bf16_to_double(xr[j]) - mu) * rstd * g;
+            double v = t + b;
+            if (y) y[r * y_rs + j] = orc_double_to_bf16(v);
+            if (y64) y64[r * y_rs + j] = v;
+            if (mag) mag[r * y_rs + j] = fabs(t) + fabs(b);
+        }
+    }
+}
+
+/* --------------------------------------------------------- sum of squares (C4) */
+
+/*
+ * sum_i x_i^2 ([Stax4] 9.4, Listing 9.4: the x * x prologue of Example 6.2;
+ * [L8] Exercise 1: the row L2 norm is the square root of this sum).
+ * Squares are exact in fp64 (24 x 24 bits); the sum is sequential fp64.
+ */
+double orc_sumsq(const float* x, int64_t n) {
+    double acc = 0.0;
+    for (int64_t i = 0; i < n; ++i) acc += (double)x[i] * (double)x[i];
+    return acc;
+}
+
+void orc_sumsq_rows(const float* x, int64_t rows, int64_t cols, int64_t x_rs, double* out) {
+    for (int64_t r = 0; r < rows; ++r) out[r] = orc_sumsq(x + r * x_rs, cols);
+}

@@ -1,0 +1,343 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+CPU only. Each test ties an oracle function to something other than itself:
+values printed on the pages (tests/golden), closed forms, invariants, exact
+rational brute force on tiny inputs, or library routines (scipy, torch,
+math.fsum) for the special cases that reduce to them. They are chosen so that
+a dropped term, a wrong sign or index, or a transposed operand in the oracle
+fails at least one of them.
+"""
+import itertools
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+# ------------------------------------------------------------ Example 1.1 (C1)
+
+
+def test_sum_relu_add_tiny_by_hand():
+    # 2*(relu(1.5) + relu(-1) + relu(-0.5)) = 3
+    a = np.array([[1.0, -2.0, 0.5]], dtype=np.float32)
+    b = np.array([[0.5, 1.0, -1.0]], dtype=np.float32)
+    out, out64 = oracle.sum_relu_add(a, b)
+    assert out[0] == 3.0 and out64[0] == 3.0
+
+
+def test_sum_relu_add_closed_forms():
+    R = 128
+    c = np.float32(0.25)
+    a = np.full((4, R), c, dtype=np.float32)
+    out, _ = oracle.sum_relu_add(a, a)
+    assert np.all(out == 4 * c * R)  # 2 * (2c) * R
+    u = synth.uniform((8, R), seed=11)
+    out, _ = oracle.sum_relu_add(u, -u)
+    assert np.all(out == 0.0)
+    neg = -np.abs(synth.uniform((8, R), seed=12)) - np.float32(0.01)
+    out, _ = oracle.sum_relu_add(neg, neg)
+    assert np.all(out == 0.0)
+
+
+def test_sum_relu_add_exact_grid_brute_force():
+    # entries on {-1,-1/2,0,1/2,1}: brute force in exact rationals
+    rng = np.random.default_rng(5)
+    grid = np.array([-1.0, -0.5, 0.0, 0.5, 1.0], dtype=np.float32)
+    a = grid[rng.integers(0, 5, size=(16, 37))]
+    b = grid[rng.integers(0, 5, size=(16, 37))]
+    out, _ = oracle.sum_relu_add(a, b)
+    for i in range(16):
+        s = sum(2 * max(Fraction(float(a[i, r])) + Fraction(float(b[i, r])), Fraction(0)) for r in range(37))
+        assert Fraction(float(out[i])) == s
+
+
+def test_sum_relu_add_matches_example_10_1_expression():
+    # Example 10.1 writes the operation as (relu(x + w) * 2).sum(-1); torch's
+    # fp32 add then an fp64 sum is the same definition as a library routine.
+    torch = pytest.importorskip("torch")
+    a, b, _ = synth.sum_relu_add_inputs(64, 128, seed=1001)
+    b = b[:, ::-1].copy()  # break any symmetry between the operands
+    out, out64 = oracle.sum_relu_add(a, b)
+    ref = (torch.relu(torch.from_numpy(a) + torch.from_numpy(b)).double() * 2).sum(-1).numpy()
+    np.testing.assert_allclose(out64, ref, rtol=1e-13, atol=0)
+
+
+def test_sum_relu_add_row_stride():
+    a, b, _ = synth.sum_relu_add_inputs(8, 40, seed=3)
+    big = np.zeros((8, 64), dtype=np.float32)
+    big[:, :40] = a
+    big[:, 40:] = 1e6  # must never be read
+    out_view, _ = oracle.sum_relu_add(big[:, :40], b)
+    out, _ = oracle.sum_relu_add(a, b)
+    assert np.array_equal(out_view, out)
+
+
+def test_sum_relu_add_nan_propagates_to_exactly_the_nan_rows():
+    a, b, nan_rows = synth.sum_relu_add_inputs(64, 128, seed=1002, n_nan=4)
+    assert len(nan_rows) == 4
+    out, _ = oracle.sum_relu_add(a, b)
+    assert set(np.nonzero(np.isnan(out))[0].tolist()) == set(nan_rows.tolist())
+
+
+def test_sum_relu_add_inf_rules():
+    inf = np.float32(np.inf)
+    a = np.array([[inf, 1.0], [inf, 1.0], [-inf, 1.0]], dtype=np.float32)
+    b = np.array([[-inf, 1.0], [1.0, 1.0], [1.0, 1.0]], dtype=np.float32)
+    out, _ = oracle.sum_relu_add(a, b)
+    assert math.isnan(out[0])  # inf + -inf = NaN, propagated by relu
+    assert out[1] == np.inf
+    assert out[2] == 4.0  # relu(-inf) = 0
+
+
+# ------------------------------------------------------------ softmax (C2, C5)
+
+
+def test_worked_example_probabilities(golden):
+    g = golden("hello_gpu_ch12_worked_example.txt")
+    tol = g["tolerance"]
+    p = oracle.softmax_f64(g["scores"])
+    np.testing.assert_allclose(p, g["probabilities"], atol=tol, rtol=0)
+    m, d = oracle.md_fold(g["scores"])
+    assert m == 4.0
+    assert abs(d - g["exp_sum"]) < tol
+    np.testing.assert_allclose(p * d, g["shifted_exps"], atol=tol, rtol=0)
+    # the fp32-row entry point gives the same values
+    y64, am = oracle.softmax_rows(np.array([g["scores"]], dtype=np.float32))
+    np.testing.assert_allclose(y64[0], p, rtol=1e-15)
+    assert am[0] == 2
+
+
+def test_worked_example_weighted_output(golden):
+    g = golden("hello_gpu_ch12_worked_example.txt")
+    V = np.array(g["values"])
+    p = oracle.softmax_f64(g["scores"])
+    two_pass = p @ V
+    np.testing.assert_allclose(two_pass, g["output"], atol=g["tolerance"], rtol=0)
+    _, _, _, o = oracle.online_attention_row(g["scores"], V)
+    np.testing.assert_allclose(o, two_pass, rtol=1e-14)
+
+
+def test_online_trace_matches_figure_12_2(golden):
+    g = golden("hello_gpu_ch12_worked_example.txt")
+    tol = g["tolerance"]
+    s = np.array(g["scores"])
+    V = np.array(g["values"])
+    m2, l2, a2, _ = oracle.online_attention_row(s[:2], V[:2])
+    assert m2 == g["after_2_m"]
+    assert abs(l2 - g["after_2_l"]) < tol
+    np.testing.assert_allclose(a2, g["after_2_a"], atol=tol, rtol=0)
+    m3, l3, a3, _ = oracle.online_attention_row(s, V)
+    assert abs(math.exp(m2 - m3) - g["after_3_alpha"]) < tol
+    assert abs(l3 - g["after_3_l"]) < tol
+    np.testing.assert_allclose(a3, g["after_3_a"], atol=tol, rtol=0)
+    # the page truncated a[1]: exact value 1 * e^-2 * 2e^-1... = 2 e^-3 + 1
+    assert abs(a3[1] - (2 * math.exp(-3) + 1)) < 1e-15
+
+
+def test_online_state_equals_two_pass_on_random_rows():
+    rng = np.random.default_rng(7)
+    for n in (1, 2, 3, 17, 300):
+        s = rng.normal(size=n) * 5
+        V = rng.normal(size=(n, 4))
+        m, l, a, o = oracle.online_attention_row(s, V)
+        assert m == s.max()
+        assert abs(l - math.fsum(np.exp(s - s.max()))) <= 1e-13 * l
+        np.testing.assert_allclose(o, oracle.softmax_f64(s) @ V, rtol=1e-12, atol=1e-15)
+
+
+def _fold_segments(xs, cuts):
+    parts = np.split(np.asarray(xs, dtype=np.float64), cuts)
+    m, d = -math.inf, 0.0
+    for part in parts:
+        pm, pd = oracle.md_fold(part)
+        m, d = oracle.md_combine(m, d, pm, pd)
+    return m, d
+
+
+def test_prop_9_1_every_order_and_segmentation():
+    x = [2.0, 1.0, 4.0]
+    ref = (4.0, math.exp(-2) + math.exp(-3) + 1.0)
+    for perm in itertools.permutations(x):
+        for k in range(0, 3):
+            for cuts in itertools.combinations([1, 2], k):
+                m, d = _fold_segments(perm, list(cuts))
+                assert m == ref[0]
+                assert abs(d - ref[1]) <= 2 * np.spacing(ref[1])
+
+
+def test_md_monoid_identity_and_random_segmentation():
+    assert oracle.md_combine(-math.inf, 0.0, -math.inf, 0.0) == (-math.inf, 0.0)
+    assert oracle.md_combine(-math.inf, 0.0, 3.5, 1.0) == (3.5, 1.0)
+    assert oracle.md_combine(3.5, 1.0, -math.inf, 0.0) == (3.5, 1.0)
+    rng = np.random.default_rng(9)
+    x = rng.normal(size=1000) * 4
+    exact = math.fsum(np.exp(x - x.max()))
+    for _ in range(5):
+        cuts = sorted(rng.choice(np.arange(1, 1000), size=rng.integers(1, 30), replace=False).tolist())
+        m, d = _fold_segments(rng.permutation(x), cuts)
+        assert m == x.max()
+        assert abs(d - exact) <= 1e-12 * exact
+
+
+def test_softmax_rows_match_scipy():
+    special = pytest.importorskip("scipy.special")
+    x = synth.softmax_inputs(64, 1000, seed=2001)
+    y64, am = oracle.softmax_rows(x)
+    np.testing.assert_allclose(y64, special.softmax(x.astype(np.float64), axis=1), rtol=1e-13, atol=1e-300)
+    assert np.array_equal(am, np.argmax(x, axis=1))
+
+
+def test_softmax_closed_forms():
+    for n in (1, 2, 3, 1000, 1024, 4097):
+        y64, am = oracle.softmax_rows(np.full((1, n), 0.37, dtype=np.float32))
+        assert np.all(np.float32(y64) == np.float32(1.0) / np.float32(n))
+        assert am[0] == 0
+    x = synth.softmax_inputs(4, 781, seed=3)
+    y64, _ = oracle.softmax_rows(x)
+    assert np.allclose(y64.sum(axis=1), 1.0, rtol=1e-14)
+    # shift invariance with an exact shift (grid inputs, shift of 8)
+    g = np.round(x * 4) / 4
+    y1, _ = oracle.softmax_rows(g.astype(np.float32))
+    y2, _ = oracle.softmax_rows((g + 8).astype(np.float32))
+    np.testing.assert_allclose(y1, y2, rtol=1e-13)
+    # permutation invariance
+    perm = np.random.default_rng(1).permutation(781)
+    y3, _ = oracle.softmax_rows(np.ascontiguousarray(x[:, perm]))
+    np.testing.assert_allclose(y3, y64[:, perm], rtol=1e-13)
+
+
+def test_argmax_first_occurrence_and_nan_reading():
+    x = np.array([[1, 5, 5, 2], [7, 7, 7, 7], [0, 1, np.nan, 9], [-3, np.nan, np.nan, 0]], dtype=np.float32)
+    y64, am = oracle.softmax_rows(x)
+    assert am.tolist() == [1, 0, 2, 1]
+    assert np.all(np.isnan(y64[2])) and np.all(np.isnan(y64[3]))
+    assert np.all(np.isfinite(y64[:2]))
+
+
+def test_ragged_rows_read_and_write_only_the_prefix():
+    x, L = synth.ragged_softmax_inputs(8, 4096, seed=21, choices=(1, 7, 1000, 4095))
+    assert np.isnan(x[0, L[0]:]).all()  # tails hold NaN
+    y64, am = oracle.softmax_rows(x, lengths=L)
+    for r in range(8):
+        n = L[r]
+        assert np.all(np.isfinite(y64[r, :n])) and np.all(np.isnan(y64[r, n:]))
+        np.testing.assert_allclose(y64[r, :n], oracle.softmax_f64(x[r, :n]), rtol=1e-15)
+        assert am[r] == np.argmax(x[r, :n])
+    y0, am0 = oracle.softmax_rows(x[:2], lengths=np.array([0, -5], dtype=np.int32))
+    assert am0.tolist() == [-1, -1] and np.isnan(y0).all()
+
+
+# ------------------------------------------------------------ LayerNorm (C3)
+
+
+def test_bf16_rounding_known_values():
+    assert oracle.f64_to_bf16(1.0) == 0x3F80
+    assert oracle.f64_to_bf16(1.0 + 2.0**-8) == 0x3F80  # tie -> even
+    assert oracle.f64_to_bf16(1.0 + 3 * 2.0**-8) == 0x3F82  # tie -> even (up)
+    assert oracle.f64_to_bf16(1.0 + 2.0**-8 + 2.0**-30) == 0x3F81  # above the tie
+    assert oracle.f64_to_bf16(-2.0) == 0xC000
+    assert oracle.f64_to_bf16(0.0) == 0 and oracle.f64_to_bf16(-0.0) == 0x8000
+    assert oracle.f64_to_bf16(math.inf) == 0x7F80 and oracle.f64_to_bf16(-math.inf) == 0xFF80
+    assert oracle.f64_to_bf16(math.nan) & 0x7FC0 == 0x7FC0
+    assert oracle.f64_to_bf16(3.4e38) == 0x7F80 and oracle.f64_to_bf16(3.389e38) == 0x7F7F
+    assert oracle.f64_to_bf16(math.ldexp(2 - 2.0**-8, 127)) == 0x7F80  # tie above the max -> even = inf
+    assert oracle.f64_to_bf16(2.0**-133) == 0x0001  # smallest subnormal
+    assert oracle.f64_to_bf16(2.0**-134) == 0x0000  # tie -> even (0)
+    for h in (0x0001, 0x3F80, 0x7F7F, 0x8123, 0x4049):
+        assert oracle.f64_to_bf16(oracle.bf16_to_f64(h)) == h
+
+
+def test_bf16_rounding_matches_torch_on_fp32_values():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(3)
+    bits = rng.integers(0, 2**32, size=20000, dtype=np.uint64).astype(np.uint32)
+    f = bits.view(np.float32)
+    f = f[np.isfinite(f)]
+    ref = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = np.array([oracle.f64_to_bf16(float(v)) for v in f], dtype=np.uint16)
+    assert np.array_equal(got, ref)
+
+
+def test_layernorm_textbook_row():
+    x = synth.to_bf16(np.array([[1, 2, 3, 4]], dtype=np.float32))
+    _, y64, _ = oracle.layernorm_rows(x, eps=0.0)
+    np.testing.assert_allclose(y64[0], [-1.34164, -0.44721, 0.44721, 1.34164], atol=1e-5)
+    _, y64e, _ = oracle.layernorm_rows(x, eps=1e-5)
+    np.testing.assert_allclose(y64e[0], (np.arange(1, 5) - 2.5) / math.sqrt(1.25 + 1e-5), rtol=1e-15)
+
+
+def test_layernorm_constant_row_gives_beta_exactly():
+    x, g, b = synth.layernorm_inputs(3, 4096, seed=31)
+    x[:] = synth.to_bf16(np.full((3, 4096), 1.6875, dtype=np.float32))
+    y, y64, _ = oracle.layernorm_rows(x, g, b)
+    assert np.array_equal(y, np.broadcast_to(b, y.shape))
+
+
+def test_layernorm_matches_torch_fp64():
+    torch = pytest.importorskip("torch")
+    x, g, b = synth.layernorm_inputs(16, 3000, seed=3001)
+    y, y64, mag = oracle.layernorm_rows(x, g, b, eps=1e-5)
+    xf = torch.from_numpy(synth.bf16_to_f32(x)).double()
+    gf = torch.from_numpy(synth.bf16_to_f32(g)).double()
+    bf = torch.from_numpy(synth.bf16_to_f32(b)).double()
+    ref = torch.nn.functional.layer_norm(xf, (3000,), gf, bf, eps=1e-5).numpy()
+    np.testing.assert_allclose(y64, ref, rtol=1e-12, atol=1e-13)
+    assert np.all(mag >= np.abs(y64) - 1e-12)
+    ref_bits = torch.from_numpy(ref).float().to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    # single fp64 rounding vs torch's fp64->fp32->bf16: equal or adjacent
+    diff = np.abs(y.astype(np.int32) - ref_bits.astype(np.int32))
+    assert diff.max() <= 1 and (diff == 0).mean() > 0.999
+
+
+def test_layernorm_moments_and_affine_invariance():
+    x, _, _ = synth.layernorm_inputs(4, 2048, seed=33)
+    _, y64, _ = oracle.layernorm_rows(x, eps=1e-5)
+    xf = synth.bf16_to_f32(x).astype(np.float64)
+    var = xf.var(axis=1)
+    assert np.all(np.abs(y64.mean(axis=1)) < 1e-12)
+    np.testing.assert_allclose(y64.var(axis=1), var / (var + 1e-5), rtol=1e-12)
+    # LN(2x + 1) == LN(x) with eps = 0: on a 1/8 grid within +/-15 both x and
+    # 2x + 1 are exact in bf16 (at most 8 significant bits)
+    xg = np.clip(np.round(xf * 8) / 8, -15, 15)
+    x0 = synth.to_bf16(xg.astype(np.float32))
+    xs = synth.to_bf16((xg * 2 + 1).astype(np.float32))
+    assert np.array_equal(synth.bf16_to_f32(xs).astype(np.float64), xg * 2 + 1)
+    _, y64s, _ = oracle.layernorm_rows(xs, eps=0.0)
+    _, y640, _ = oracle.layernorm_rows(x0, eps=0.0)
+    np.testing.assert_allclose(y64s, y640, rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------------ sum of squares (C4)
+
+
+def test_sumsq_closed_forms():
+    assert oracle.sumsq(np.ones(1 << 20, dtype=np.float32)) == float(1 << 20)
+    assert oracle.sumsq(np.arange(10, dtype=np.float32)) == 285.0
+    n = 4096
+    assert oracle.sumsq(np.arange(n, dtype=np.float32)) == (n - 1) * n * (2 * n - 1) // 6
+    assert oracle.sumsq(np.zeros(0, dtype=np.float32)) == 0.0
+
+
+def test_sumsq_matches_fsum():
+    x = synth.sumsq_inputs(1 << 18, seed=4001)
+    exact = math.fsum((x.astype(np.float64)) ** 2)
+    # sequential fp64 summation of n nonnegative terms: |error| <= (n-1) u sum
+    assert abs(oracle.sumsq(x) - exact) <= (x.size - 1) * 2.0**-53 * exact
+    assert abs(exact - (1 << 18) / 3) < 0.01 * (1 << 18) / 3  # E[x^2] = 1/3 (sanity)
+
+
+def test_example_6_2_split_rows_and_l2_norm(golden):
+    g = golden("stax4_example_6_2.txt")
+    rows, cols, splits = int(g["rows"]), int(g["cols"]), int(g["splits"])
+    assert int(g["partial_elems"]) * splits == cols
+    assert rows * splits * 4 == g["workspace_bytes"]
+    x = synth.uniform((rows, cols), seed=62)
+    s = oracle.sumsq_rows(x)
+    halves = [[math.fsum(x[r, k * 8192:(k + 1) * 8192].astype(np.float64) ** 2) for k in range(splits)]
+              for r in range(rows)]
+    np.testing.assert_allclose(s, [h0 + h1 for h0, h1 in halves], rtol=1e-13)
+    # CMU 15-779 Lecture 8, Exercise 1: the row L2 norm is sqrt of this sum
+    np.testing.assert_allclose(np.sqrt(s), np.linalg.norm(x.astype(np.float64), axis=1), rtol=1e-13)
