@@ -1,0 +1,194 @@
+/*
+ * fr.h - C ABI of libfr, fused pointwise-prologue + row-reduction kernels
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The operations are the non-template reduction nodes of a tensor compiler,
+ * as described in "Stax (4): GPU Codegen and Dynamic Shapes" (TensorPlay
+ * blog), section 9.4 (three reduction forms), 9.5 (multi-reduction fusion and
+ * the online (m, d) merge), 9.7 (the wrapper that checks sizes and strides,
+ * hands workspaces to the kernels and launches them in stream order), and
+ * 10.3 (sizes are runtime values, so masks stay).
+ *
+ * Conventions shared by every entry point:
+ *  - Memory. Every data pointer is a device pointer (HBM) owned by the
+ *    caller. The library never allocates or frees memory; where a split
+ *    reduction needs scratch, the caller passes a workspace sized by the
+ *    matching *_workspace_bytes query.
+ *  - Layout. Row-major: element (i, j) of a matrix lives at
+ *    base + i * row_stride + j * col_stride, strides counted in elements.
+ *    The column stride must be 1 and the row stride >= cols; other strides
+ *    are an error (FR_E_STRIDE), not a slow path.
+ *  - Streams. `stream` is a hipStream_t passed as void* (NULL = the default
+ *    stream). Work is enqueued asynchronously; the library never
+ *    synchronizes. Kernels of one call run in stream order.
+ *  - Errors. Invalid arguments return a negative status before any HIP call
+ *    and launch nothing. FR_E_DEVICE means the current device is not gfx950
+ *    or could not be queried; FR_E_LAUNCH means a kernel launch failed.
+ *  - Sizes. rows and cols are counted in elements; 0 <= rows < 2^31 and
+ *    0 <= cols < 2^30 (in-row offsets are 32-bit, row offsets 64-bit);
+ *    larger sizes return FR_E_SIZE.
+ *  - Determinism. For a given device model, library build and arguments,
+ *    results are bit-identical from run to run (fixed partitions, fixed
+ *    reduction trees, no floating-point atomics).
+ *  - Aliasing. y may equal x (in place, same row stride); any other overlap
+ *    between inputs and outputs is undefined.
+ */
+#ifndef FR_H
+#define FR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------ status codes */
+#define FR_OK 0
+#define FR_E_NULL (-1)      /* a required pointer is NULL */
+#define FR_E_SIZE (-2)      /* a size is negative or too large */
+#define FR_E_STRIDE (-3)    /* column stride != 1, or row stride < cols */
+#define FR_E_DTYPE (-4)     /* dtype not supported by this entry point */
+#define FR_E_ALIGN (-5)     /* pointer not aligned to its element (or workspace to 16 B) */
+#define FR_E_WORKSPACE (-6) /* workspace required but missing, or too small */
+#define FR_E_ARG (-7)       /* another argument is invalid (eps, form, plan) */
+#define FR_E_DEVICE (-8)    /* no usable gfx950 device */
+#define FR_E_LAUNCH (-9)    /* a kernel launch failed */
+
+/* ------------------------------------------------------------ element types */
+#define FR_F32 0  /* IEEE binary32 */
+#define FR_BF16 1 /* bfloat16 (upper half of a binary32), stored as uint16 */
+
+/* ------------------------------------------------------------ reduction forms
+ * "Stax (4)", 9.4: persistent (the whole row in registers, one pass), looped
+ * (the row streamed in chunks with a register accumulator), split (too few
+ * outputs: per-chunk partials in a workspace, then a finishing pass). */
+#define FR_FORM_AUTO 0
+#define FR_FORM_PER 1
+#define FR_FORM_RED 2
+#define FR_FORM_SPLIT 3
+
+/* ------------------------------------------------------------ operations */
+#define FR_OP_SUM_RELU_ADD 1
+#define FR_OP_SOFTMAX 2
+#define FR_OP_LAYERNORM 3
+#define FR_OP_SUMSQ 4
+
+/* Launch plan chosen for one call: the reduction form and its launch
+ * configuration ("Stax (4)", 9.6: block sizes and warp counts are launch
+ * parameters; the grid follows from them). */
+typedef struct fr_plan {
+    int32_t op;           /* FR_OP_* */
+    int32_t form;         /* FR_FORM_PER / _RED / _SPLIT */
+    int32_t threads;      /* threads per workgroup (multiple of 64) */
+    int32_t seg;          /* lanes that share one row (persistent form) */
+    int32_t vec;          /* 16-byte vectors per lane: per pass (PER, SPLIT chunk) or per loop step (RED) */
+    int32_t rows_per_wg;  /* rows handled by one workgroup */
+    int32_t splits;       /* chunks per row (SPLIT), else 1 */
+    int32_t chunk;        /* elements per chunk (SPLIT), else 0 */
+    int32_t vec16;        /* 1: 16-byte vector accesses; 0: element accesses */
+    int32_t reserved;
+    int64_t grid;         /* workgroups of the main kernel */
+    int64_t grid2;        /* workgroups of the finishing kernel (0: none) */
+    uint64_t ws_bytes;    /* workspace bytes this plan uses */
+} fr_plan;
+
+/* Human-readable name of a status code (static string). */
+const char* fr_status_string(int status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int fr_version(void);
+
+/* Compute the plan a call with these arguments would use, without touching
+ * the GPU (no HIP call). num_cus is the compute-unit count of the target
+ * device (256 on MI355X). has_lengths: ragged softmax. ws_bytes: workspace
+ * the caller would pass (0 = none). aligned16: all row bases and strides
+ * allow 16-byte accesses. Honours fr_force_form. Returns FR_OK or an error
+ * status for arguments the entry point itself would reject. */
+int fr_plan_query(int op, int64_t rows, int64_t cols, int dtype, int num_cus, int has_lengths,
+                  uint64_t ws_bytes, int aligned16, fr_plan* plan);
+
+/* Test and tuning hook: force a reduction form for every later call in this
+ * process (FR_FORM_AUTO restores the automatic choice). A call whose shape or
+ * workspace cannot use the forced form returns FR_E_ARG. Not thread-safe;
+ * returns the previous setting. */
+int fr_force_form(int form);
+
+/* ------------------------------------------------------------ Example 1.1
+ * out[i] = sum_j 2 * relu(a[i,j] + b[i,j])   ("Stax (4)", 9.2, Listing 9.1,
+ * the kernel of Example 1.1; 10.2, Example 10.1 with a runtime row count).
+ * The add is an fp32 add; relu propagates NaN (a NaN anywhere in a row makes
+ * out[i] NaN). a, b: fp32 [rows, cols] with row strides a_rs, b_rs and column
+ * strides a_cs, b_cs (must be 1); out: fp32 [rows] with element stride
+ * out_s >= 1. cols = 0 writes 0 (the empty sum). ws/ws_bytes: optional
+ * workspace (NULL/0 allowed) enabling the split form for few, long rows; size
+ * it with fr_sum_workspace_bytes. dtype must be FR_F32. */
+int fr_sum_relu_add(const void* a, const void* b, void* out, int64_t rows, int64_t cols, int64_t a_rs,
+                    int64_t a_cs, int64_t b_rs, int64_t b_cs, int64_t out_s, void* ws, uint64_t ws_bytes,
+                    int dtype, void* stream);
+
+/* Workspace bytes that make the split form available to fr_sum_relu_add and
+ * fr_sumsq_rows for this shape (0 for an empty shape). With it the library
+ * splits rows only where there are too few rows to fill the device. */
+uint64_t fr_sum_workspace_bytes(int64_t rows, int64_t cols, int dtype);
+
+/* ------------------------------------------------------------ row softmax
+ * y[i,j] = e^(x[i,j] - m_i) / sum_k e^(x[i,k] - m_i), m_i = max_k x[i,k]
+ * ("Stax (4)", 9.5, the softmax definition and Listing 9.5), fused into one
+ * kernel per form: the max and the sum of exponentials are two reductions
+ * with different identities (-inf and 0), and long rows merge them with the
+ * online (m, d) rescaling (9.5, the monoid and Proposition 9.1; hello-gpu,
+ * Chapter 12, 12.3).
+ *  x, y:     fp32 [rows, cols]; strides as in the conventions (y may be x).
+ *  lengths:  optional int32[rows] device array. Row i then covers
+ *            j < len_i = clamp(lengths[i], 0, cols) only: elements at
+ *            j >= len_i are neither read in x nor written in y. NULL: every
+ *            row has length cols.
+ *  argmax:   optional int32[rows] device output: the smallest j < len_i with
+ *            x[i,j] equal to the row maximum (a NaN counts as the maximum),
+ *            -1 for an empty row.
+ *  ws:       optional workspace (16-byte aligned) of at least
+ *            fr_softmax_rows_workspace_bytes(rows, cols, dtype) bytes. With
+ *            it, rows too long for registers may be split across
+ *            workgroups; without it they are streamed by one workgroup each.
+ * A NaN in a row makes that row's outputs NaN. dtype must be FR_F32. */
+uint64_t fr_softmax_rows_workspace_bytes(int64_t rows, int64_t cols, int dtype);
+int fr_softmax_rows(const void* x, void* y, int64_t rows, int64_t cols, int64_t x_rs, int64_t x_cs, int64_t y_rs,
+                    int64_t y_cs, const int32_t* lengths, int32_t* argmax, void* ws, uint64_t ws_bytes, int dtype,
+                    void* stream);
+
+/* ------------------------------------------------------------ LayerNorm
+ * y[i,j] = (x[i,j] - mu_i) * rstd_i * gamma[j] + beta[j],
+ * mu_i = mean_j x[i,j], rstd_i = 1 / sqrt(var_i + eps), var_i the biased
+ * (divide by cols) variance of row i. Mean and variance are fused reductions
+ * over the row ("Stax (4)", 10.4 names variance reductions that also output
+ * the mean; 9.8 states that half-precision arithmetic is done in fp32).
+ *  x, y:        bf16 [rows, cols] (uint16 storage), fp32 arithmetic, y
+ *               rounded to nearest even.
+ *  gamma, beta: optional bf16 [cols] (NULL: 1 and 0).
+ *  eps:         finite and >= 0 (else FR_E_ARG).
+ * cols must be >= 1 (FR_E_SIZE otherwise). dtype must be FR_BF16. */
+int fr_layernorm_rows(const void* x, const void* gamma, const void* beta, void* y, int64_t rows, int64_t cols,
+                      int64_t x_rs, int64_t x_cs, int64_t y_rs, int64_t y_cs, float eps, int dtype, void* stream);
+
+/* ------------------------------------------------------------ sum of squares
+ * fr_sumsq_rows: out[i] = sum_j x[i,j]^2 (fp32 squares, fp32 accumulation;
+ * "Stax (4)", 9.4, Listing 9.4, the x * x prologue of Example 6.2, whose
+ * [64, 16384] rows are split into partial sums plus a finishing pass). out:
+ * fp32 [rows], contiguous. ws optional as for fr_sum_relu_add.
+ * fr_sumsq_full: *out = sum_i x[i]^2 over a contiguous fp32 vector of n
+ * elements, as per-workgroup partials in the workspace plus one finishing
+ * workgroup, in a fixed order: repeated runs are bit-identical. A workspace
+ * of fr_sumsq_full_workspace_bytes(n, dtype) bytes is required whenever that
+ * query returns a non-zero size. n = 0 writes 0; n < 2^30. dtype must be
+ * FR_F32. */
+int fr_sumsq_rows(const void* x, void* out, int64_t rows, int64_t cols, int64_t x_rs, int64_t x_cs, void* ws,
+                  uint64_t ws_bytes, int dtype, void* stream);
+uint64_t fr_sumsq_full_workspace_bytes(int64_t n, int dtype);
+int fr_sumsq_full(const void* x, int64_t n, void* out, void* ws, uint64_t ws_bytes, int dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FR_H */

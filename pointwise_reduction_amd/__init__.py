@@ -1,0 +1,205 @@
+"""pointwise_reduction_amd - fused pointwise-prologue + row-reduction kernels
+for AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over ``libfr.so`` (C ABI in ``include/fr.h``). The
+functions below carry the names of the C entry points and only marshal
+arguments: every step of every operation runs in the HIP kernels of libfr.
+PyTorch is used for device memory and streams only; tensors are passed as
+raw device pointers with their sizes and strides.
+
+There is no CPU fallback: if the library is missing, importing this package
+raises, and on a machine without a gfx950 GPU every compute call returns
+FR_E_DEVICE (raised as FrError).
+"""
+import ctypes
+import os
+
+try:  # load torch first so that libfr binds to the same HIP runtime as torch
+    import torch  # noqa: F401
+except ImportError:  # the C ABI is usable without torch
+    torch = None
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfr.so")
+
+FR_OK = 0
+FR_E_NULL, FR_E_SIZE, FR_E_STRIDE, FR_E_DTYPE, FR_E_ALIGN = -1, -2, -3, -4, -5
+FR_E_WORKSPACE, FR_E_ARG, FR_E_DEVICE, FR_E_LAUNCH = -6, -7, -8, -9
+FR_F32, FR_BF16 = 0, 1
+FR_FORM_AUTO, FR_FORM_PER, FR_FORM_RED, FR_FORM_SPLIT = 0, 1, 2, 3
+FR_OP_SUM_RELU_ADD, FR_OP_SOFTMAX, FR_OP_LAYERNORM, FR_OP_SUMSQ = 1, 2, 3, 4
+FORM_NAMES = {FR_FORM_PER: "per", FR_FORM_RED: "red", FR_FORM_SPLIT: "split"}
+
+# Every symbol include/fr.h declares.
+EXPORTS = (
+    "fr_status_string", "fr_version", "fr_plan_query", "fr_force_form",
+    "fr_sum_relu_add", "fr_sum_workspace_bytes",
+    "fr_softmax_rows_workspace_bytes", "fr_softmax_rows",
+    "fr_layernorm_rows",
+    "fr_sumsq_rows", "fr_sumsq_full_workspace_bytes", "fr_sumsq_full",
+)
+
+
+class FrError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+
+
+class fr_plan(ctypes.Structure):
+    _fields_ = [
+        ("op", ctypes.c_int32), ("form", ctypes.c_int32), ("threads", ctypes.c_int32),
+        ("seg", ctypes.c_int32), ("vec", ctypes.c_int32), ("rows_per_wg", ctypes.c_int32),
+        ("splits", ctypes.c_int32), ("chunk", ctypes.c_int32), ("vec16", ctypes.c_int32),
+        ("reserved", ctypes.c_int32), ("grid", ctypes.c_int64), ("grid2", ctypes.c_int64),
+        ("ws_bytes", ctypes.c_uint64),
+    ]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                          "or python pointwise_reduction_amd/build.py (there is no CPU fallback)")
+    lib = ctypes.CDLL(LIB_PATH)
+    I64, I32, U64, P = ctypes.c_int64, ctypes.c_int, ctypes.c_uint64, ctypes.c_void_p
+    sig = {
+        "fr_status_string": (ctypes.c_char_p, [I32]),
+        "fr_version": (I32, []),
+        "fr_plan_query": (I32, [I32, I64, I64, I32, I32, I32, U64, I32, ctypes.POINTER(fr_plan)]),
+        "fr_force_form": (I32, [I32]),
+        "fr_sum_relu_add": (I32, [P, P, P, I64, I64, I64, I64, I64, I64, I64, P, U64, I32, P]),
+        "fr_sum_workspace_bytes": (U64, [I64, I64, I32]),
+        "fr_softmax_rows_workspace_bytes": (U64, [I64, I64, I32]),
+        "fr_softmax_rows": (I32, [P, P, I64, I64, I64, I64, I64, I64, P, P, P, U64, I32, P]),
+        "fr_layernorm_rows": (I32, [P, P, P, P, I64, I64, I64, I64, I64, I64, ctypes.c_float, I32, P]),
+        "fr_sumsq_rows": (I32, [P, P, I64, I64, I64, I64, P, U64, I32, P]),
+        "fr_sumsq_full_workspace_bytes": (U64, [I64, I32]),
+        "fr_sumsq_full": (I32, [P, I64, P, P, U64, I32, P]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+def status_string(status):
+    return lib.fr_status_string(int(status)).decode()
+
+
+def _check(status, where):
+    if status != FR_OK:
+        raise FrError(status, where)
+
+
+# ------------------------------------------------------------------ marshalling helpers
+
+
+def _ptr(t):
+    """Device pointer of a tensor (None -> NULL)."""
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream) if torch is not None else None
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return FR_F32
+    if t.dtype == torch.bfloat16:
+        return FR_BF16
+    return -1
+
+
+def _mat(t):
+    """(rows, cols, row_stride, col_stride) of a 2-D tensor view."""
+    if t.dim() != 2:
+        raise ValueError("expected a 2-D tensor")
+    return t.shape[0], t.shape[1], t.stride(0), t.stride(1)
+
+
+# ------------------------------------------------------------------ entry points
+
+
+def fr_plan_query(op, rows, cols, dtype=FR_F32, num_cus=256, has_lengths=False, ws_bytes=0, aligned16=True):
+    plan = fr_plan()
+    _check(lib.fr_plan_query(op, rows, cols, dtype, num_cus, int(has_lengths), ws_bytes, int(aligned16),
+                             ctypes.byref(plan)), "fr_plan_query")
+    return plan
+
+
+def fr_force_form(form):
+    return lib.fr_force_form(form)
+
+
+def fr_sum_workspace_bytes(rows, cols, dtype=FR_F32):
+    return int(lib.fr_sum_workspace_bytes(rows, cols, dtype))
+
+
+def fr_softmax_rows_workspace_bytes(rows, cols, dtype=FR_F32):
+    return int(lib.fr_softmax_rows_workspace_bytes(rows, cols, dtype))
+
+
+def fr_sumsq_full_workspace_bytes(n, dtype=FR_F32):
+    return int(lib.fr_sumsq_full_workspace_bytes(n, dtype))
+
+
+def fr_sum_relu_add(a, b, out, ws=None, stream=None):
+    """out[i] = sum_j 2*relu(a[i,j] + b[i,j]) (fp32). out: 1-D, len rows."""
+    rows, cols, a_rs, a_cs = _mat(a)
+    rb, cb, b_rs, b_cs = _mat(b)
+    if (rb, cb) != (rows, cols) or out.shape[0] != rows:
+        raise ValueError("shape mismatch")
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.fr_sum_relu_add(_ptr(a), _ptr(b), _ptr(out), rows, cols, a_rs, a_cs, b_rs, b_cs, out.stride(0),
+                               _ptr(ws), ws_bytes, _dtype_code(a), _stream(stream)), "fr_sum_relu_add")
+    return out
+
+
+def fr_softmax_rows(x, y, lengths=None, argmax=None, ws=None, stream=None):
+    rows, cols, x_rs, x_cs = _mat(x)
+    ry, cy, y_rs, y_cs = _mat(y)
+    if (ry, cy) != (rows, cols):
+        raise ValueError("shape mismatch")
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.fr_softmax_rows(_ptr(x), _ptr(y), rows, cols, x_rs, x_cs, y_rs, y_cs, _ptr(lengths), _ptr(argmax),
+                               _ptr(ws), ws_bytes, _dtype_code(x), _stream(stream)), "fr_softmax_rows")
+    return y
+
+
+def fr_layernorm_rows(x, y, gamma=None, beta=None, eps=1e-5, stream=None):
+    rows, cols, x_rs, x_cs = _mat(x)
+    ry, cy, y_rs, y_cs = _mat(y)
+    if (ry, cy) != (rows, cols):
+        raise ValueError("shape mismatch")
+    _check(lib.fr_layernorm_rows(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), rows, cols, x_rs, x_cs, y_rs, y_cs,
+                                 float(eps), _dtype_code(x), _stream(stream)), "fr_layernorm_rows")
+    return y
+
+
+def fr_sumsq_rows(x, out, ws=None, stream=None):
+    rows, cols, x_rs, x_cs = _mat(x)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.fr_sumsq_rows(_ptr(x), _ptr(out), rows, cols, x_rs, x_cs, _ptr(ws), ws_bytes, _dtype_code(x),
+                             _stream(stream)), "fr_sumsq_rows")
+    return out
+
+
+def fr_sumsq_full(x, out, ws=None, stream=None):
+    if x.dim() != 1 or (x.numel() > 1 and x.stride(0) != 1):
+        raise ValueError("expected a contiguous 1-D tensor")
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.fr_sumsq_full(_ptr(x), x.numel(), _ptr(out), _ptr(ws), ws_bytes, _dtype_code(x), _stream(stream)),
+           "fr_sumsq_full")
+    return out

@@ -1,0 +1,263 @@
+// fr_api.cpp - the C ABI of libfr: argument checks, plan, launch.
+//
+// Mirrors the wrapper of "Stax (4): GPU Codegen and Dynamic Shapes", 9.7
+// (Listing 9.6): sizes and strides are checked before anything runs, the
+// kernels of one call are enqueued on the caller's stream in program order
+// with no synchronization, and scratch memory comes from the caller. Every
+// argument error is reported before the first HIP call. An unsupported
+// device or dtype is an error, never a silent fallback (9.10 makes the same
+// choice for an unavailable attention backend).
+#include <hip/hip_runtime_api.h>
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "fr.h"
+#include "fr_internal.h"
+
+namespace fr {
+uint64_t sum_split_ws(int64_t rows, int64_t cols);
+uint64_t softmax_split_ws(int64_t rows, int64_t cols);
+}  // namespace fr
+
+using namespace fr;
+
+namespace {
+
+int g_forced_form = FR_FORM_AUTO;
+
+constexpr int kMaxDevices = 64;
+struct DeviceInfo {
+    int state = 0;  // 0 unknown, 1 usable gfx950, -1 unusable
+    int num_cus = 0;
+};
+DeviceInfo g_dev[kMaxDevices];
+std::mutex g_dev_mu;
+
+// Current device: usable gfx950? Queried once per device, then cached.
+int device_check(int* num_cus) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FR_E_DEVICE;
+    std::lock_guard<std::mutex> lock(g_dev_mu);
+    DeviceInfo& d = g_dev[dev];
+    if (d.state == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+            d.state = -1;
+        } else {
+            d.state = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+            d.num_cus = prop.multiProcessorCount;
+        }
+    }
+    if (d.state != 1) return FR_E_DEVICE;
+    *num_cus = d.num_cus;
+    return FR_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return p == nullptr || ((uintptr_t)p % a) == 0; }
+
+// Checks common to every row-major [rows, cols] operand.
+// A [rows, 0] operand is never dereferenced and may be NULL.
+int check_matrix(const void* p, int64_t rows, int64_t cols, int64_t rs, int64_t cs, size_t elem) {
+    if (!p) return cols == 0 ? FR_OK : FR_E_NULL;
+    if (cs != 1) return FR_E_STRIDE;
+    if (rs < 0 || (rows > 1 && rs < cols)) return FR_E_STRIDE;
+    if (!aligned(p, elem)) return FR_E_ALIGN;
+    return FR_OK;
+}
+
+bool vec_ok(const void* p, int64_t rs, int64_t elems_per_vec) {
+    return p == nullptr || (((uintptr_t)p % 16) == 0 && rs % elems_per_vec == 0);
+}
+
+// rows < 2^31; cols < 2^30 keeps every in-row offset, including the padding
+// of the last loop step, inside a 32-bit int.
+constexpr int64_t kMaxRows = int64_t(1) << 31;
+constexpr int64_t kMaxCols = int64_t(1) << 30;
+
+int check_sizes(int64_t rows, int64_t cols) {
+    if (rows < 0 || cols < 0) return FR_E_SIZE;
+    if (rows >= kMaxRows || cols >= kMaxCols) return FR_E_SIZE;
+    return FR_OK;
+}
+
+int finish_launch(hipError_t e) { return e == hipSuccess ? FR_OK : FR_E_LAUNCH; }
+
+int run_sum(int prologue, const void* a, const void* b, void* out, int64_t rows, int64_t cols, int64_t a_rs,
+            int64_t b_rs, int64_t out_s, void* ws, uint64_t ws_bytes, void* stream) {
+    int num_cus = 0;
+    int st = device_check(&num_cus);
+    if (st != FR_OK) return st;
+    const int v16 = vec_ok(a, a_rs, 4) && vec_ok(b, b_rs, 4);
+    fr_plan plan;
+    const int op = prologue == kReluAdd ? FR_OP_SUM_RELU_ADD : FR_OP_SUMSQ;
+    st = make_plan(op, rows, cols, FR_F32, num_cus, 0, ws ? ws_bytes : 0, v16, g_forced_form, &plan);
+    if (st != FR_OK) return st;
+    SumArgs args{prologue, (const float*)a, (const float*)b, (float*)out, (int)rows, (int)cols, a_rs, b_rs, out_s,
+                 (float*)ws};
+    (void)hipGetLastError();  // clear a stale error so the launch status is ours
+    return finish_launch(launch_sum(plan, args, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fr_status_string(int status) {
+    switch (status) {
+        case FR_OK: return "FR_OK: success";
+        case FR_E_NULL: return "FR_E_NULL: a required pointer is NULL";
+        case FR_E_SIZE: return "FR_E_SIZE: a size is negative or too large";
+        case FR_E_STRIDE: return "FR_E_STRIDE: column stride must be 1 and row stride >= cols";
+        case FR_E_DTYPE: return "FR_E_DTYPE: dtype not supported by this entry point";
+        case FR_E_ALIGN: return "FR_E_ALIGN: pointer not aligned to its element (workspace: 16 bytes)";
+        case FR_E_WORKSPACE: return "FR_E_WORKSPACE: workspace missing or too small";
+        case FR_E_ARG: return "FR_E_ARG: invalid argument";
+        case FR_E_DEVICE: return "FR_E_DEVICE: no usable gfx950 device";
+        case FR_E_LAUNCH: return "FR_E_LAUNCH: kernel launch failed";
+    }
+    return "unknown status";
+}
+
+int fr_version(void) { return 100; }
+
+int fr_force_form(int form) {
+    const int prev = g_forced_form;
+    if (form >= FR_FORM_AUTO && form <= FR_FORM_SPLIT) g_forced_form = form;
+    return prev;
+}
+
+int fr_plan_query(int op, int64_t rows, int64_t cols, int dtype, int num_cus, int has_lengths, uint64_t ws_bytes,
+                  int aligned16, fr_plan* plan) {
+    if (!plan) return FR_E_NULL;
+    return make_plan(op, rows, cols, dtype, num_cus, has_lengths, ws_bytes, aligned16, g_forced_form, plan);
+}
+
+uint64_t fr_sum_workspace_bytes(int64_t rows, int64_t cols, int dtype) {
+    if (dtype != FR_F32 || check_sizes(rows, cols) != FR_OK) return 0;
+    return sum_split_ws(rows, cols);
+}
+
+int fr_sum_relu_add(const void* a, const void* b, void* out, int64_t rows, int64_t cols, int64_t a_rs,
+                    int64_t a_cs, int64_t b_rs, int64_t b_cs, int64_t out_s, void* ws, uint64_t ws_bytes,
+                    int dtype, void* stream) {
+    int st = check_sizes(rows, cols);
+    if (st != FR_OK) return st;
+    if (dtype != FR_F32) return FR_E_DTYPE;
+    if (rows == 0) return FR_OK;
+    if ((st = check_matrix(a, rows, cols, a_rs, a_cs, 4)) != FR_OK) return st;
+    if ((st = check_matrix(b, rows, cols, b_rs, b_cs, 4)) != FR_OK) return st;
+    if (!out) return FR_E_NULL;
+    if (out_s < 1) return FR_E_STRIDE;
+    if (!aligned(out, 4)) return FR_E_ALIGN;
+    if (ws && !aligned(ws, 16)) return FR_E_ALIGN;
+    return run_sum(kReluAdd, a, b, out, rows, cols, a_rs, b_rs, out_s, ws, ws_bytes, stream);
+}
+
+int fr_sumsq_rows(const void* x, void* out, int64_t rows, int64_t cols, int64_t x_rs, int64_t x_cs, void* ws,
+                  uint64_t ws_bytes, int dtype, void* stream) {
+    int st = check_sizes(rows, cols);
+    if (st != FR_OK) return st;
+    if (dtype != FR_F32) return FR_E_DTYPE;
+    if (rows == 0) return FR_OK;
+    if ((st = check_matrix(x, rows, cols, x_rs, x_cs, 4)) != FR_OK) return st;
+    if (!out) return FR_E_NULL;
+    if (!aligned(out, 4)) return FR_E_ALIGN;
+    if (ws && !aligned(ws, 16)) return FR_E_ALIGN;
+    return run_sum(kSquare, x, nullptr, out, rows, cols, x_rs, 0, 1, ws, ws_bytes, stream);
+}
+
+uint64_t fr_sumsq_full_workspace_bytes(int64_t n, int dtype) {
+    if (dtype != FR_F32 || n <= 2048 || n >= kMaxCols) return 0;
+    return sum_split_ws(1, n);
+}
+
+int fr_sumsq_full(const void* x, int64_t n, void* out, void* ws, uint64_t ws_bytes, int dtype, void* stream) {
+    if (n < 0 || n >= kMaxCols) return FR_E_SIZE;
+    if (dtype != FR_F32) return FR_E_DTYPE;
+    if (!out) return FR_E_NULL;
+    if (n > 0 && !x) return FR_E_NULL;
+    if (!aligned(x, 4) || !aligned(out, 4)) return FR_E_ALIGN;
+    const uint64_t need = fr_sumsq_full_workspace_bytes(n, dtype);
+    if (need > 0) {
+        if (!ws || ws_bytes < need) return FR_E_WORKSPACE;
+        if (!aligned(ws, 16)) return FR_E_ALIGN;
+    }
+    int num_cus = 0;
+    int st = device_check(&num_cus);
+    if (st != FR_OK) return st;
+    const int v16 = vec_ok(x, 0, 4);
+    fr_plan plan;
+    // A full reduction has a single output: split whenever the vector does
+    // not fit one persistent row (the form is not left to the row heuristics).
+    const int form = need > 0 ? FR_FORM_SPLIT : FR_FORM_PER;
+    st = make_plan(FR_OP_SUMSQ, 1, n, FR_F32, num_cus, 0, need > 0 ? ws_bytes : 0, v16, form, &plan);
+    if (st != FR_OK) return st;
+    SumArgs args{kSquare, (const float*)x, nullptr, (float*)out, 1, (int)n, n, 0, 1, (float*)ws};
+    (void)hipGetLastError();
+    return finish_launch(launch_sum(plan, args, (hipStream_t)stream));
+}
+
+uint64_t fr_softmax_rows_workspace_bytes(int64_t rows, int64_t cols, int dtype) {
+    if (dtype != FR_F32 || check_sizes(rows, cols) != FR_OK) return 0;
+    return softmax_split_ws(rows, cols);
+}
+
+int fr_softmax_rows(const void* x, void* y, int64_t rows, int64_t cols, int64_t x_rs, int64_t x_cs, int64_t y_rs,
+                    int64_t y_cs, const int32_t* lengths, int32_t* argmax, void* ws, uint64_t ws_bytes, int dtype,
+                    void* stream) {
+    int st = check_sizes(rows, cols);
+    if (st != FR_OK) return st;
+    if (dtype != FR_F32) return FR_E_DTYPE;
+    if (rows == 0) return FR_OK;
+    if (cols == 0 && !argmax) return FR_OK;  // nothing to read or write
+    if ((st = check_matrix(x, rows, cols, x_rs, x_cs, 4)) != FR_OK) return st;
+    if ((st = check_matrix(y, rows, cols, y_rs, y_cs, 4)) != FR_OK) return st;
+    if (x == y && x_rs != y_rs) return FR_E_STRIDE;
+    if (!aligned(lengths, 4) || !aligned(argmax, 4)) return FR_E_ALIGN;
+    if (ws) {
+        if (!aligned(ws, 16)) return FR_E_ALIGN;
+        if (cols > 0 && ws_bytes < softmax_split_ws(rows, cols)) return FR_E_WORKSPACE;
+    }
+    int num_cus = 0;
+    st = device_check(&num_cus);
+    if (st != FR_OK) return st;
+    const int v16 = vec_ok(x, x_rs, 4) && vec_ok(y, y_rs, 4);
+    fr_plan plan;
+    st = make_plan(FR_OP_SOFTMAX, rows, cols, FR_F32, num_cus, lengths != nullptr, ws ? ws_bytes : 0, v16,
+                   g_forced_form, &plan);
+    if (st != FR_OK) return st;
+    SoftmaxArgs args{(const float*)x, (float*)y, (int)rows, (int)cols, x_rs, y_rs, lengths, argmax, ws};
+    (void)hipGetLastError();
+    return finish_launch(launch_softmax(plan, args, (hipStream_t)stream));
+}
+
+int fr_layernorm_rows(const void* x, const void* gamma, const void* beta, void* y, int64_t rows, int64_t cols,
+                      int64_t x_rs, int64_t x_cs, int64_t y_rs, int64_t y_cs, float eps, int dtype, void* stream) {
+    int st = check_sizes(rows, cols);
+    if (st != FR_OK) return st;
+    if (dtype != FR_BF16) return FR_E_DTYPE;
+    if (cols < 1) return FR_E_SIZE;
+    if (!(eps >= 0.0f) || isinf(eps)) return FR_E_ARG;
+    if (rows == 0) return FR_OK;
+    if ((st = check_matrix(x, rows, cols, x_rs, x_cs, 2)) != FR_OK) return st;
+    if ((st = check_matrix(y, rows, cols, y_rs, y_cs, 2)) != FR_OK) return st;
+    if (x == y && x_rs != y_rs) return FR_E_STRIDE;
+    if (!aligned(gamma, 2) || !aligned(beta, 2)) return FR_E_ALIGN;
+    int num_cus = 0;
+    st = device_check(&num_cus);
+    if (st != FR_OK) return st;
+    const int v16 = cols % 8 == 0 && vec_ok(x, x_rs, 8) && vec_ok(y, y_rs, 8) && vec_ok(gamma, 0, 8) &&
+                    vec_ok(beta, 0, 8);
+    fr_plan plan;
+    st = make_plan(FR_OP_LAYERNORM, rows, cols, FR_BF16, num_cus, 0, 0, v16, g_forced_form, &plan);
+    if (st != FR_OK) return st;
+    LayerNormArgs args{(const uint16_t*)x, (const uint16_t*)gamma, (const uint16_t*)beta, (uint16_t*)y,
+                       (int)rows, (int)cols, x_rs, y_rs, eps};
+    (void)hipGetLastError();
+    return finish_launch(launch_layernorm(plan, args, (hipStream_t)stream));
+}
+
+}  // extern "C"

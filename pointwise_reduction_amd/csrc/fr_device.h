@@ -1,0 +1,251 @@
+// fr_device.h - wave64 building blocks for the fused row-reduction kernels
+// on gfx950 (CDNA4): lane-group butterflies on DPP, cross-wave combines
+// through LDS, masked 16-byte loads and stores, bf16 packing.
+//
+// Reductions here are deterministic: every butterfly step and every
+// cross-wave fold runs in a fixed order, and every combine operator is
+// written so that op(a, b) and op(b, a) give the same bits. All lanes of a
+// group therefore end with the identical result, and repeated runs give the
+// same bits ("Stax (4): GPU Codegen and Dynamic Shapes", 9.5: the merge is
+// associative and commutative, so the order is ours to fix).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fr {
+
+constexpr int kWave = 64;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ------------------------------------------------------------------ DPP moves
+// dpp_ctrl encodings (GCN/CDNA DPP): quad_perm [1,0,3,2] = 0xB1 (lane ^ 1),
+// quad_perm [2,3,0,1] = 0x4E (lane ^ 2), row_half_mirror = 0x141 (lane i of
+// 8 reads 7 - i), row_mirror = 0x140 (lane i of 16 reads 15 - i).
+constexpr int kDppXor1 = 0xB1;
+constexpr int kDppXor2 = 0x4E;
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+
+__device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, kWave); }
+__device__ __forceinline__ int shfl_xor(int v, int m) { return __shfl_xor(v, m, kWave); }
+
+// Value of the partner lane at butterfly step STEP (1, 2, 4, 8). After the
+// steps up to k every lane of an aligned 2k-lane group holds the group
+// result: xor 1 and xor 2 inside quads, then the half-row and row mirrors,
+// whose partner always lies in the other (already reduced) half of the
+// group. Steps 16 and 32 cross DPP rows and go through ds_bpermute.
+template <int STEP, typename T>
+__device__ __forceinline__ T partner(T v) {
+    static_assert(STEP == 1 || STEP == 2 || STEP == 4 || STEP == 8, "DPP butterfly step");
+    if constexpr (STEP == 1) return dpp<kDppXor1>(v);
+    else if constexpr (STEP == 2) return dpp<kDppXor2>(v);
+    else if constexpr (STEP == 4) return dpp<kDppHalfMirror>(v);
+    else return dpp<kDppMirror>(v);
+}
+
+// ------------------------------------------------------------------ operators
+// NaN-propagating maximum (v_maximum3_f32 on gfx950).
+__device__ __forceinline__ float fmax_nan(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+struct OpSum {
+    __device__ __forceinline__ float operator()(float a, float b) const { return a + b; }
+};
+struct OpMax {
+    __device__ __forceinline__ float operator()(float a, float b) const { return fmax_nan(a, b); }
+};
+struct OpMinI {
+    __device__ __forceinline__ int operator()(int a, int b) const { return a < b ? a : b; }
+};
+
+// Reduce over aligned groups of SEG lanes (SEG a power of two, <= 64).
+template <int SEG, typename T, typename Op>
+__device__ __forceinline__ T group_reduce(T v, Op op) {
+    if constexpr (SEG >= 2) v = op(v, partner<1>(v));
+    if constexpr (SEG >= 4) v = op(v, partner<2>(v));
+    if constexpr (SEG >= 8) v = op(v, partner<4>(v));
+    if constexpr (SEG >= 16) v = op(v, partner<8>(v));
+    if constexpr (SEG >= 32) v = op(v, shfl_xor(v, 16));
+    if constexpr (SEG >= 64) v = op(v, shfl_xor(v, 32));
+    return v;
+}
+
+// ------------------------------------------------------------------ (m, d) monoid
+// (m1, d1) (+) (m2, d2) = (M, d1 e^(m1-M) + d2 e^(m2-M)), M = max(m1, m2);
+// identity (-inf, 0) ("Stax (4)", 9.5). Exponentials use e^t = 2^(t log2 e)
+// on the hardware exp2. A side whose m is -inf contributes 0; the sum is
+// symmetric in its two terms, so op(a, b) and op(b, a) agree bit for bit.
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float exp_fast(float t) { return __builtin_amdgcn_exp2f(t * kLog2e); }
+
+struct MD {
+    float m, d;
+};
+__device__ __forceinline__ MD md_combine(MD a, MD b) {
+    float M = fmax_nan(a.m, b.m);
+    float ta = a.m == -INFINITY ? 0.f : a.d * exp_fast(a.m - M);
+    float tb = b.m == -INFINITY ? 0.f : b.d * exp_fast(b.m - M);
+    return MD{M, ta + tb};
+}
+
+// (max, first index of the max) with NaN counted as the largest value and the
+// lower index winning ties. Symmetric by construction.
+struct MI {
+    float m;
+    int i;
+};
+__device__ __forceinline__ MI mi_combine(MI a, MI b) {
+    bool an = a.m != a.m, bn = b.m != b.m;
+    if (an || bn) {
+        if (an && bn) return MI{a.m, a.i < b.i ? a.i : b.i};
+        return an ? a : b;
+    }
+    if (a.m > b.m) return a;
+    if (b.m > a.m) return b;
+    return MI{a.m, a.i < b.i ? a.i : b.i};
+}
+
+// ------------------------------------------------------------------ Chan merge
+// Mean/M2 statistics (count n, mean mu, sum of squared deviations M2), merged
+// with the pairwise update of Chan, Golub & LeVeque (1979), written
+// symmetrically: mu = (na mu_a + nb mu_b) / n, M2 = M2a + M2b + delta^2 na nb / n.
+struct Stat {
+    float n, mu, m2;
+};
+__device__ __forceinline__ Stat stat_combine(Stat a, Stat b) {
+    if (a.n == 0.f) return b;
+    if (b.n == 0.f) return a;
+    float n = a.n + b.n;
+    float delta = b.mu - a.mu;
+    // divide (not multiply by 1/n) so that equal means merge to exactly that mean
+    float mu = (a.n * a.mu + b.n * b.mu) / n;
+    float m2 = (a.m2 + b.m2) + delta * delta * (a.n * b.n) / n;
+    return Stat{n, mu, m2};
+}
+
+// Group reductions of the composite states: each field rides the same DPP step.
+template <int STEP>
+__device__ __forceinline__ MD partner(MD v) {
+    return MD{partner<STEP>(v.m), partner<STEP>(v.d)};
+}
+template <int STEP>
+__device__ __forceinline__ MI partner(MI v) {
+    return MI{partner<STEP>(v.m), partner<STEP>(v.i)};
+}
+template <int STEP>
+__device__ __forceinline__ Stat partner(Stat v) {
+    return Stat{partner<STEP>(v.n), partner<STEP>(v.mu), partner<STEP>(v.m2)};
+}
+__device__ __forceinline__ MD shfl_xor(MD v, int m) { return MD{shfl_xor(v.m, m), shfl_xor(v.d, m)}; }
+__device__ __forceinline__ MI shfl_xor(MI v, int m) { return MI{shfl_xor(v.m, m), shfl_xor(v.i, m)}; }
+__device__ __forceinline__ Stat shfl_xor(Stat v, int m) {
+    return Stat{shfl_xor(v.n, m), shfl_xor(v.mu, m), shfl_xor(v.m2, m)};
+}
+
+struct OpMD {
+    __device__ __forceinline__ MD operator()(MD a, MD b) const { return md_combine(a, b); }
+};
+struct OpMI {
+    __device__ __forceinline__ MI operator()(MI a, MI b) const { return mi_combine(a, b); }
+};
+struct OpStat {
+    __device__ __forceinline__ Stat operator()(Stat a, Stat b) const { return stat_combine(a, b); }
+};
+
+// ------------------------------------------------------------------ workgroup fold
+// All-reduce a wave-uniform value across the NW waves of a workgroup. Lane 0
+// of each wave writes its slot, one barrier, then every thread folds the
+// slots in wave order, so all threads hold the same bits. `slots` must be
+// private to this call (a later reuse needs a barrier first).
+template <typename T, typename Op>
+__device__ __forceinline__ T block_fold(T v, T* slots, int nw, Op op) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    if (lane == 0) slots[wave] = v;
+    __syncthreads();
+    T r = slots[0];
+    for (int w = 1; w < nw; ++w) r = op(r, slots[w]);
+    return r;
+}
+
+// ------------------------------------------------------------------ memory
+// Streaming loads/stores: the data is touched once, so they carry the
+// non-temporal hint (the role of evict_first in "Stax (4)", 9.2).
+template <bool NT>
+__device__ __forceinline__ f32x4 ld4(const float* p) {
+    if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    else return *reinterpret_cast<const f32x4*>(p);
+}
+template <bool NT>
+__device__ __forceinline__ float ld1(const float* p) {
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+template <bool NT>
+__device__ __forceinline__ void st4(float* p, f32x4 v) {
+    if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
+    else *reinterpret_cast<f32x4*>(p) = v;
+}
+template <bool NT>
+__device__ __forceinline__ void st1(float* p, float v) {
+    if constexpr (NT) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
+template <bool NT>
+__device__ __forceinline__ u32x4 ld4u(const uint16_t* p) {
+    if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    else return *reinterpret_cast<const u32x4*>(p);
+}
+template <bool NT>
+__device__ __forceinline__ void st4u(uint16_t* p, u32x4 v) {
+    if constexpr (NT) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+    else *reinterpret_cast<u32x4*>(p) = v;
+}
+
+// Load the 4 elements j0..j0+3 of a row of length L. A full vector is one
+// 16-byte load when VEC; elements at j >= L are never touched and read as
+// `fill` (the identity of the reduction that follows).
+template <bool VEC, bool NT>
+__device__ __forceinline__ f32x4 load4_masked(const float* row, int j0, int L, float fill) {
+    if (VEC && j0 + 3 < L) return ld4<NT>(row + j0);
+    f32x4 v = {fill, fill, fill, fill};
+    if (j0 + 0 < L) v.x = ld1<NT>(row + j0 + 0);
+    if (j0 + 1 < L) v.y = ld1<NT>(row + j0 + 1);
+    if (j0 + 2 < L) v.z = ld1<NT>(row + j0 + 2);
+    if (j0 + 3 < L) v.w = ld1<NT>(row + j0 + 3);
+    return v;
+}
+template <bool VEC, bool NT>
+__device__ __forceinline__ void store4_masked(float* row, int j0, int L, f32x4 v) {
+    if (VEC && j0 + 3 < L) {
+        st4<NT>(row + j0, v);
+        return;
+    }
+    if (j0 + 0 < L) st1<NT>(row + j0 + 0, v.x);
+    if (j0 + 1 < L) st1<NT>(row + j0 + 1, v.y);
+    if (j0 + 2 < L) st1<NT>(row + j0 + 2, v.z);
+    if (j0 + 3 < L) st1<NT>(row + j0 + 3, v.w);
+}
+
+// ------------------------------------------------------------------ bf16
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
+// Two fp32 -> packed bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    bf16x2 p = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, p);
+}
+
+}  // namespace fr

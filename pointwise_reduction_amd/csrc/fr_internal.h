@@ -1,0 +1,59 @@
+// fr_internal.h - what the host entry points hand to the kernel launchers.
+// Arguments are validated and a plan is chosen before any of these runs.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fr.h"
+
+namespace fr {
+
+enum Prologue : int { kReluAdd = 0, kSquare = 1 };
+
+// Row sums with a pointwise prologue: out[i] = post * sum_j f(a[i,j], b[i,j]).
+struct SumArgs {
+    int prologue;      // kReluAdd (2 * relu(a + b)) or kSquare (a * a)
+    const float* a;
+    const float* b;    // kReluAdd only
+    float* out;
+    int rows, cols;
+    int64_t a_rs, b_rs, out_s;
+    float* ws;         // split form: rows x splits partial sums
+};
+
+struct SoftmaxArgs {
+    const float* x;
+    float* y;
+    int rows, cols;
+    int64_t x_rs, y_rs;
+    const int32_t* lengths;  // nullable
+    int32_t* argmax;         // nullable
+    void* ws;                // split form: rows x splits partial states
+};
+
+struct LayerNormArgs {
+    const uint16_t* x;
+    const uint16_t* gamma;  // nullable
+    const uint16_t* beta;   // nullable
+    uint16_t* y;
+    int rows, cols;
+    int64_t x_rs, y_rs;
+    float eps;
+};
+
+// Partial state of one chunk of a split softmax row: the (m, d) pair of the
+// chunk and the first index of its maximum. 16 bytes, 16-byte aligned.
+struct alignas(16) SoftmaxPartial {
+    float m, d;
+    int32_t idx, pad;
+};
+
+hipError_t launch_sum(const fr_plan& p, const SumArgs& a, hipStream_t s);
+hipError_t launch_softmax(const fr_plan& p, const SoftmaxArgs& a, hipStream_t s);
+hipError_t launch_layernorm(const fr_plan& p, const LayerNormArgs& a, hipStream_t s);
+
+// Planner (host only, no HIP calls).
+int make_plan(int op, int64_t rows, int64_t cols, int dtype, int num_cus, int has_lengths, uint64_t ws_bytes,
+              int aligned16, int forced_form, fr_plan* plan);
+
+}  // namespace fr

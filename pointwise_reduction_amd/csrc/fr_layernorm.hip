@@ -1,0 +1,230 @@
+// fr_layernorm.hip - LayerNorm over bf16 rows with fp32 arithmetic: the mean
+// and the variance are two fused reductions over the row, followed by the
+// normalize / affine / round-to-bf16 epilogue ("Stax (4): GPU Codegen and
+// Dynamic Shapes", 10.4 names variance reductions that also output the mean;
+// 9.8: half precision is computed in fp32).
+//   persistent  fr_per_layernorm_bf16  one workgroup holds the whole row in
+//                                      registers (8 bf16 per 16-byte vector,
+//                                      NV vectors per lane): exact two-pass
+//                                      mean and variance over registers, one
+//                                      read and one write of the row
+//   looped      fr_red_layernorm_bf16  one workgroup streams the row: per-lane
+//                                      Welford statistics, merged per 8-value
+//                                      vector and across lanes and waves with
+//                                      Chan's pairwise update; a second pass
+//                                      re-reads the row and writes y
+#include "fr_device.h"
+#include "fr_internal.h"
+
+namespace fr {
+
+// Load the 8 bf16 at j0..j0+7 of a row of length L as packed words; element
+// j >= L is never touched and reads as +0. VEC kernels run only when L is a
+// multiple of 8 (and rows are 16-byte aligned), so a vector is either wholly
+// inside the row or wholly outside it.
+template <bool VEC, bool NT>
+__device__ __forceinline__ u32x4 load8_masked(const uint16_t* row, int j0, int L) {
+    if constexpr (VEC) return j0 < L ? ld4u<NT>(row + j0) : u32x4{0u, 0u, 0u, 0u};
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+        if (j0 + c < L) w[c >> 1] |= (uint32_t)row[j0 + c] << ((c & 1) * 16);
+    return u32x4{w[0], w[1], w[2], w[3]};
+}
+
+template <bool VEC, bool NT>
+__device__ __forceinline__ void store8_masked(uint16_t* row, int j0, int L, u32x4 v) {
+    if constexpr (VEC) {
+        if (j0 < L) st4u<NT>(row + j0, v);
+        return;
+    }
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+        if (j0 + c < L) row[j0 + c] = (uint16_t)(w[c >> 1] >> ((c & 1) * 16));
+}
+
+__device__ __forceinline__ uint32_t word(u32x4 v, int i) { return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w)); }
+
+// y = (x - mu) * rstd * gamma + beta for the 8 values of one vector, packed
+// back to bf16 with round-to-nearest-even. When x == mu the product is an
+// exact 0 and y is exactly beta.
+template <bool VEC>
+__device__ __forceinline__ u32x4 normalize8(u32x4 xv, int j0, int L, const uint16_t* __restrict__ gamma,
+                                            const uint16_t* __restrict__ beta, float mu, float rstd) {
+    u32x4 gv = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // 1.0 in bf16
+    u32x4 bv = {0u, 0u, 0u, 0u};
+    if (gamma) gv = load8_masked<VEC, false>(gamma, j0, L);
+    if (beta) bv = load8_masked<VEC, false>(beta, j0, L);
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t xw = word(xv, i), gw = word(gv, i), bw = word(bv, i);
+        const float lo = (bf16_lo(xw) - mu) * rstd * bf16_lo(gw) + bf16_lo(bw);
+        const float hi = (bf16_hi(xw) - mu) * rstd * bf16_hi(gw) + bf16_hi(bw);
+        o[i] = pack_bf16(lo, hi);
+    }
+    return u32x4{o[0], o[1], o[2], o[3]};
+}
+
+// ------------------------------------------------------------------ persistent
+template <int T, int NV, bool VEC>
+__global__ __launch_bounds__(T) void fr_per_layernorm_bf16(const uint16_t* x, const uint16_t* __restrict__ gamma,
+                                                           const uint16_t* __restrict__ beta, uint16_t* y, int rows,
+                                                           int cols, int64_t x_rs, int64_t y_rs, float eps) {
+    __shared__ float sl_s[T / kWave];
+    __shared__ float sl_q[T / kWave];
+    const int tid = threadIdx.x;
+    const float n = (float)cols;
+    for (int r = blockIdx.x; r < rows; r += gridDim.x) {
+        const uint16_t* xr = x + (int64_t)r * x_rs;
+        u32x4 v[NV];
+#pragma unroll
+        for (int k = 0; k < NV; ++k) v[k] = load8_masked<VEC, true>(xr, (k * T + tid) * 8, cols);
+        // pass 1 over registers: the sum (masked elements read as +0)
+        float s = 0.f;
+#pragma unroll
+        for (int k = 0; k < NV; ++k)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s += bf16_lo(word(v[k], i)) + bf16_hi(word(v[k], i));
+        s = group_reduce<kWave>(s, OpSum());
+        s = block_fold(s, sl_s, T / kWave, OpSum());
+        const float mu = s / n;  // correctly rounded: a constant row gives mu == x exactly
+        // pass 2 over registers: sum of squared deviations of valid elements
+        float q = 0.f;
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            const int j0 = (k * T + tid) * 8;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float dl = j0 + 2 * i < cols ? bf16_lo(word(v[k], i)) - mu : 0.f;
+                const float dh = j0 + 2 * i + 1 < cols ? bf16_hi(word(v[k], i)) - mu : 0.f;
+                q += dl * dl + dh * dh;
+            }
+        }
+        q = group_reduce<kWave>(q, OpSum());
+        q = block_fold(q, sl_q, T / kWave, OpSum());
+        const float rstd = 1.0f / sqrtf(q / n + eps);
+        uint16_t* yr = y + (int64_t)r * y_rs;
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            const int j0 = (k * T + tid) * 8;
+            if (j0 < cols) store8_masked<VEC, true>(yr, j0, cols, normalize8<VEC>(v[k], j0, cols, gamma, beta, mu, rstd));
+        }
+        __syncthreads();  // slots are rewritten by the next row
+    }
+}
+
+// ------------------------------------------------------------------ looped (Welford)
+// Statistics of the (up to) 8 valid values of one vector: count, mean and
+// sum of squared deviations, computed exactly in two steps over registers.
+__device__ __forceinline__ Stat stat8(u32x4 v, int j0, int L) {
+    const int cnt = L - j0 >= 8 ? 8 : (L - j0 > 0 ? L - j0 : 0);
+    if (cnt == 0) return Stat{0.f, 0.f, 0.f};
+    float val[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        val[2 * i] = bf16_lo(word(v, i));
+        val[2 * i + 1] = bf16_hi(word(v, i));
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) s += val[c];  // masked values are +0
+    const float n = (float)cnt;
+    const float mean = cnt == 8 ? s * 0.125f : s / n;
+    float m2 = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const float d = c < cnt ? val[c] - mean : 0.f;
+        m2 += d * d;
+    }
+    return Stat{n, mean, m2};
+}
+
+template <int T, int U, bool VEC>
+__global__ __launch_bounds__(T) void fr_red_layernorm_bf16(const uint16_t* x, const uint16_t* __restrict__ gamma,
+                                                           const uint16_t* __restrict__ beta, uint16_t* y, int rows,
+                                                           int cols, int64_t x_rs, int64_t y_rs, float eps) {
+    __shared__ Stat sl[T / kWave];
+    const int tid = threadIdx.x;
+    for (int r = blockIdx.x; r < rows; r += gridDim.x) {
+        const uint16_t* xr = x + (int64_t)r * x_rs;
+        Stat st{0.f, 0.f, 0.f};
+        for (int base = 0; base < cols; base += T * 8 * U) {
+            u32x4 v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) v[u] = load8_masked<VEC, false>(xr, base + (u * T + tid) * 8, cols);
+#pragma unroll
+            for (int u = 0; u < U; ++u) st = stat_combine(st, stat8(v[u], base + (u * T + tid) * 8, cols));
+        }
+        st = group_reduce<kWave>(st, OpStat());
+        st = block_fold(st, sl, T / kWave, OpStat());
+        const float mu = st.mu;
+        const float rstd = 1.0f / sqrtf(st.m2 / (float)cols + eps);
+        uint16_t* yr = y + (int64_t)r * y_rs;
+        for (int base = 0; base < cols; base += T * 8 * U) {
+            u32x4 v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) v[u] = load8_masked<VEC, true>(xr, base + (u * T + tid) * 8, cols);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int j0 = base + (u * T + tid) * 8;
+                if (j0 < cols) store8_masked<VEC, true>(yr, j0, cols, normalize8<VEC>(v[u], j0, cols, gamma, beta, mu, rstd));
+            }
+        }
+        __syncthreads();  // slots are rewritten by the next row
+    }
+}
+
+// ------------------------------------------------------------------ launchers
+namespace {
+
+using LnFn = void (*)(const uint16_t*, const uint16_t*, const uint16_t*, uint16_t*, int, int, int64_t, int64_t,
+                      float);
+
+// Persistent configurations: 16-byte vector kernels hold up to 8 vectors
+// (64 bf16) per lane without spilling; element-wise kernels (unaligned rows)
+// up to 4.
+template <bool VEC>
+LnFn pick_per(int threads, int nv) {
+    if (threads == 64) {
+        switch (nv) {
+            case 1: return fr_per_layernorm_bf16<64, 1, VEC>;
+            case 2: return fr_per_layernorm_bf16<64, 2, VEC>;
+            case 4: return fr_per_layernorm_bf16<64, 4, VEC>;
+            case 8: return VEC ? fr_per_layernorm_bf16<64, 8, VEC> : nullptr;
+        }
+        return nullptr;
+    }
+    if (nv == (VEC ? 8 : 4)) {
+        switch (threads) {
+            case 128: return fr_per_layernorm_bf16<128, VEC ? 8 : 4, VEC>;
+            case 256: return fr_per_layernorm_bf16<256, VEC ? 8 : 4, VEC>;
+            case 512: return fr_per_layernorm_bf16<512, VEC ? 8 : 4, VEC>;
+        }
+    }
+    return nullptr;
+}
+
+template <bool VEC>
+LnFn pick_red(int threads, int u) {
+    if (threads == 256 && u == 4) return fr_red_layernorm_bf16<256, 4, VEC>;
+    if (threads == 512 && u == 2) return fr_red_layernorm_bf16<512, 2, VEC>;
+    if (threads == 1024 && u == 2) return fr_red_layernorm_bf16<1024, 2, VEC>;
+    return nullptr;
+}
+
+}  // namespace
+
+hipError_t launch_layernorm(const fr_plan& p, const LayerNormArgs& a, hipStream_t s) {
+    const bool vec = p.vec16 != 0;
+    LnFn f = nullptr;
+    if (p.form == FR_FORM_PER) f = vec ? pick_per<true>(p.threads, p.vec) : pick_per<false>(p.threads, p.vec);
+    else if (p.form == FR_FORM_RED) f = vec ? pick_red<true>(p.threads, p.vec) : pick_red<false>(p.threads, p.vec);
+    if (!f) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(f, dim3((unsigned)p.grid), dim3(p.threads), 0, s, a.x, a.gamma, a.beta, a.y, a.rows, a.cols,
+                       a.x_rs, a.y_rs, a.eps);
+    return hipGetLastError();
+}
+
+}  // namespace fr

@@ -1,0 +1,345 @@
+// fr_softmax.hip - row softmax with fused max / sum-of-exponentials
+// reductions ("Stax (4): GPU Codegen and Dynamic Shapes", 9.5), optional
+// ragged runtime row lengths (10.3: bounds are runtime values, masks stay)
+// and optional argmax.
+//   persistent  fr_per_softmax_f32      the row lives in a lane group's
+//                                       registers: max, exp, sum, scale; one
+//                                       read and one write per element
+//                                       (Listing 9.5; two passes over
+//                                       registers, as 9.5 notes for short rows)
+//   looped      fr_red_softmax_f32      one workgroup streams the row with
+//                                       the online (m, d) rescaling (9.5, the
+//                                       merge; hello-gpu Chapter 12, 12.3),
+//                                       then a normalizing pass
+//   split       fr_split_softmax_part + fr_split_softmax_fin
+//                                       chunks of long rows on separate
+//                                       workgroups; per-chunk (m, d, argmax)
+//                                       partials merged in chunk order
+//                                       (Proposition 9.1: any segmentation)
+// Masked lanes take the identity of each reduction: -inf for the max, 0 for
+// the sum (9.5, Listing 9.5), never 0 for the max.
+#include <limits.h>
+
+#include "fr_device.h"
+#include "fr_internal.h"
+
+namespace fr {
+
+__device__ __forceinline__ int row_len(const int32_t* __restrict__ lengths, int r, int cols) {
+    if (!lengths) return cols;
+    int L = lengths[r];
+    return L < 0 ? 0 : (L > cols ? cols : L);
+}
+
+// Element c of a 4-vector.
+__device__ __forceinline__ float comp(f32x4 v, int c) { return c == 0 ? v.x : (c == 1 ? v.y : (c == 2 ? v.z : v.w)); }
+
+// Does x match the row maximum m (a NaN maximum matches the first NaN)?
+__device__ __forceinline__ bool is_max(float x, float m) { return x == m || (m != m && x != x); }
+
+// ------------------------------------------------------------------ persistent
+template <int SEG, int NV, bool VEC>
+__global__ __launch_bounds__(256) void fr_per_softmax_f32(const float* x, float* y, int rows, int cols,
+                                                          int64_t x_rs, int64_t y_rs,
+                                                          const int32_t* __restrict__ lengths,
+                                                          int32_t* __restrict__ argmax) {
+    constexpr int RPB = 256 / SEG;
+    const int g = threadIdx.x / SEG;
+    const int l = threadIdx.x % SEG;
+    const int ngroups = (rows + RPB - 1) / RPB;
+    for (int grp = blockIdx.x; grp < ngroups; grp += gridDim.x) {
+        const int r = grp * RPB + g;
+        const bool live = r < rows;
+        const int L = live ? row_len(lengths, r, cols) : 0;
+        const float* xr = x + (int64_t)(live ? r : 0) * x_rs;
+        f32x4 v[NV];
+#pragma unroll
+        for (int k = 0; k < NV; ++k) v[k] = load4_masked<VEC, true>(xr, (k * SEG + l) * 4, L, -INFINITY);
+        float m = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < NV; ++k) m = fmax_nan(fmax_nan(m, fmax_nan(v[k].x, v[k].y)), fmax_nan(v[k].z, v[k].w));
+        m = group_reduce<SEG>(m, OpMax());
+        if (argmax) {
+            int cand = INT_MAX;
+#pragma unroll
+            for (int k = NV - 1; k >= 0; --k)
+#pragma unroll
+                for (int c = 3; c >= 0; --c) {
+                    const int j = (k * SEG + l) * 4 + c;
+                    if (j < L && is_max(comp(v[k], c), m)) cand = j;
+                }
+            cand = group_reduce<SEG>(cand, OpMinI());
+            if (live && l == 0) argmax[r] = L > 0 ? cand : -1;
+        }
+        float s = 0.f;
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            const int j0 = (k * SEG + l) * 4;
+            v[k].x = j0 + 0 < L ? exp_fast(v[k].x - m) : 0.f;
+            v[k].y = j0 + 1 < L ? exp_fast(v[k].y - m) : 0.f;
+            v[k].z = j0 + 2 < L ? exp_fast(v[k].z - m) : 0.f;
+            v[k].w = j0 + 3 < L ? exp_fast(v[k].w - m) : 0.f;
+            s += (v[k].x + v[k].y) + (v[k].z + v[k].w);
+        }
+        s = group_reduce<SEG>(s, OpSum());
+        const float inv = 1.0f / s;  // one correctly rounded division per row
+        float* yr = y + (int64_t)(live ? r : 0) * y_rs;
+#pragma unroll
+        for (int k = 0; k < NV; ++k) store4_masked<VEC, true>(yr, (k * SEG + l) * 4, L, v[k] * inv);
+    }
+}
+
+// ------------------------------------------------------------------ looped (online)
+// One workgroup of T threads per row. Pass 1 keeps a per-lane (m, d) state:
+// for each step of U vectors it takes the step maximum m', rescales the old
+// sum by e^(m - m') and adds the new terms e^(x - m') - the online update of
+// hello-gpu Chapter 12, 12.3, one rescale per step rather than per element.
+// The lane states are merged with the (m, d) monoid. Pass 2 re-reads the row,
+// writes e^(x - M) / D and finds the first index of the maximum.
+template <int T, int U, bool VEC>
+__global__ __launch_bounds__(T) void fr_red_softmax_f32(const float* x, float* y, int rows, int cols,
+                                                        int64_t x_rs, int64_t y_rs,
+                                                        const int32_t* __restrict__ lengths,
+                                                        int32_t* __restrict__ argmax) {
+    __shared__ MD sl_md[T / kWave];
+    __shared__ int sl_i[T / kWave];
+    const int tid = threadIdx.x;
+    for (int r = blockIdx.x; r < rows; r += gridDim.x) {
+        const int L = row_len(lengths, r, cols);
+        const float* xr = x + (int64_t)r * x_rs;
+        MD st{-INFINITY, 0.f};
+        for (int base = 0; base < L; base += T * 4 * U) {
+            f32x4 v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) v[u] = load4_masked<VEC, false>(xr, base + (u * T + tid) * 4, L, -INFINITY);
+            float cm = -INFINITY;
+#pragma unroll
+            for (int u = 0; u < U; ++u) cm = fmax_nan(fmax_nan(cm, fmax_nan(v[u].x, v[u].y)), fmax_nan(v[u].z, v[u].w));
+            const float M = fmax_nan(st.m, cm);
+            float add = 0.f;
+            if (M != -INFINITY) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int j0 = base + (u * T + tid) * 4;
+                    add += j0 + 0 < L ? exp_fast(v[u].x - M) : 0.f;
+                    add += j0 + 1 < L ? exp_fast(v[u].y - M) : 0.f;
+                    add += j0 + 2 < L ? exp_fast(v[u].z - M) : 0.f;
+                    add += j0 + 3 < L ? exp_fast(v[u].w - M) : 0.f;
+                }
+            }
+            const float scale = st.m == -INFINITY ? 0.f : exp_fast(st.m - M);
+            st = MD{M, st.d * scale + add};
+        }
+        st = group_reduce<kWave>(st, OpMD());
+        st = block_fold(st, sl_md, T / kWave, OpMD());
+        const float M = st.m;
+        const float inv = 1.0f / st.d;
+        float* yr = y + (int64_t)r * y_rs;
+        int cand = INT_MAX;
+        for (int base = 0; base < L; base += T * 4 * U) {
+            f32x4 v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) v[u] = load4_masked<VEC, true>(xr, base + (u * T + tid) * 4, L, -INFINITY);
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int j0 = base + (u * T + tid) * 4;
+                if (argmax && cand == INT_MAX) {
+                    for (int c = 0; c < 4; ++c)
+                        if (j0 + c < L && cand == INT_MAX && is_max(comp(v[u], c), M)) cand = j0 + c;
+                }
+                f32x4 e = {exp_fast(v[u].x - M), exp_fast(v[u].y - M), exp_fast(v[u].z - M), exp_fast(v[u].w - M)};
+                store4_masked<VEC, true>(yr, j0, L, e * inv);
+            }
+        }
+        if (argmax) {
+            cand = group_reduce<kWave>(cand, OpMinI());
+            cand = block_fold(cand, sl_i, T / kWave, OpMinI());
+            if (tid == 0) argmax[r] = L > 0 ? cand : -1;
+        }
+        __syncthreads();  // slots are rewritten by the next row
+    }
+}
+
+// ------------------------------------------------------------------ split
+// Chunk c of row r (workgroup r * S + c) covers [c * C, min(len_r, (c+1) * C))
+// with C = 4 * T * NV. Part 1 keeps the chunk in registers and writes its
+// partial (m, d, first index of m). Part 2 merges the row's partials in chunk
+// order, writes the argmax (chunk 0) and the normalized chunk.
+template <int T, int NV, bool VEC>
+__global__ __launch_bounds__(T) void fr_split_softmax_part(const float* __restrict__ x, int rows, int cols,
+                                                           int64_t x_rs, const int32_t* __restrict__ lengths,
+                                                           SoftmaxPartial* __restrict__ ws, int S) {
+    constexpr int C = 4 * T * NV;
+    __shared__ float sl_m[T / kWave];
+    __shared__ float sl_d[T / kWave];
+    __shared__ int sl_i[T / kWave];
+    const int64_t w = blockIdx.x;
+    const int r = (int)(w / S);
+    const int c = (int)(w % S);
+    if (r >= rows) return;
+    const int L = row_len(lengths, r, cols);
+    const int start = c * C;
+    if (start >= L) return;
+    const int end = min(L, start + C);
+    const float* xr = x + (int64_t)r * x_rs;
+    const int tid = threadIdx.x;
+    f32x4 v[NV];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) v[k] = load4_masked<VEC, false>(xr, start + (k * T + tid) * 4, end, -INFINITY);
+    float m = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) m = fmax_nan(fmax_nan(m, fmax_nan(v[k].x, v[k].y)), fmax_nan(v[k].z, v[k].w));
+    m = group_reduce<kWave>(m, OpMax());
+    m = block_fold(m, sl_m, T / kWave, OpMax());
+    int cand = INT_MAX;
+    float s = 0.f;
+#pragma unroll
+    for (int k = NV - 1; k >= 0; --k)
+#pragma unroll
+        for (int cc = 3; cc >= 0; --cc) {
+            const int j = start + (k * T + tid) * 4 + cc;
+            if (j < end && is_max(comp(v[k], cc), m)) cand = j;
+        }
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+        const int j0 = start + (k * T + tid) * 4;
+        s += j0 + 0 < end ? exp_fast(v[k].x - m) : 0.f;
+        s += j0 + 1 < end ? exp_fast(v[k].y - m) : 0.f;
+        s += j0 + 2 < end ? exp_fast(v[k].z - m) : 0.f;
+        s += j0 + 3 < end ? exp_fast(v[k].w - m) : 0.f;
+    }
+    cand = group_reduce<kWave>(cand, OpMinI());
+    cand = block_fold(cand, sl_i, T / kWave, OpMinI());
+    s = group_reduce<kWave>(s, OpSum());
+    s = block_fold(s, sl_d, T / kWave, OpSum());
+    if (tid == 0) ws[w] = SoftmaxPartial{m, s, cand, 0};
+}
+
+template <int T, int NV, bool VEC>
+__global__ __launch_bounds__(T) void fr_split_softmax_fin(const float* x, float* y, int rows, int cols,
+                                                          int64_t x_rs, int64_t y_rs,
+                                                          const int32_t* __restrict__ lengths,
+                                                          int32_t* __restrict__ argmax,
+                                                          const SoftmaxPartial* __restrict__ ws, int S) {
+    constexpr int C = 4 * T * NV;
+    const int64_t w = blockIdx.x;
+    const int r = (int)(w / S);
+    const int c = (int)(w % S);
+    if (r >= rows) return;
+    const int L = row_len(lengths, r, cols);
+    const int start = c * C;
+    if (start >= L) {
+        if (c == 0 && argmax && threadIdx.x == 0) argmax[r] = -1;
+        return;
+    }
+    const int end = min(L, start + C);
+    const int nc = (L + C - 1) / C;
+    MD st{-INFINITY, 0.f};
+    MI best{-INFINITY, INT_MAX};
+    const SoftmaxPartial* pr = ws + (int64_t)r * S;
+    for (int k = 0; k < nc; ++k) {
+        const SoftmaxPartial p = pr[k];
+        st = md_combine(st, MD{p.m, p.d});
+        best = mi_combine(best, MI{p.m, p.idx});
+    }
+    if (c == 0 && argmax && threadIdx.x == 0) argmax[r] = best.i;
+    const float M = st.m;
+    const float inv = 1.0f / st.d;
+    const float* xr = x + (int64_t)r * x_rs;
+    float* yr = y + (int64_t)r * y_rs;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+        const int j0 = start + (k * T + tid) * 4;
+        f32x4 v = load4_masked<VEC, true>(xr, j0, end, -INFINITY);
+        f32x4 e = {exp_fast(v.x - M), exp_fast(v.y - M), exp_fast(v.z - M), exp_fast(v.w - M)};
+        store4_masked<VEC, true>(yr, j0, end, e * inv);
+    }
+}
+
+// ------------------------------------------------------------------ launchers
+namespace {
+
+using SmFn = void (*)(const float*, float*, int, int, int64_t, int64_t, const int32_t*, int32_t*);
+using PartFn = void (*)(const float*, int, int, int64_t, const int32_t*, SoftmaxPartial*, int);
+using FinFn = void (*)(const float*, float*, int, int, int64_t, int64_t, const int32_t*, int32_t*,
+                       const SoftmaxPartial*, int);
+
+template <bool VEC>
+SmFn pick_per(int seg, int nv) {
+    switch (seg) {
+        case 8: return fr_per_softmax_f32<8, 1, VEC>;
+        case 16: return fr_per_softmax_f32<16, 1, VEC>;
+        case 32: return fr_per_softmax_f32<32, 1, VEC>;
+        case 64:
+            switch (nv) {
+                case 1: return fr_per_softmax_f32<64, 1, VEC>;
+                case 2: return fr_per_softmax_f32<64, 2, VEC>;
+                case 4: return fr_per_softmax_f32<64, 4, VEC>;
+                case 8: return fr_per_softmax_f32<64, 8, VEC>;
+            }
+    }
+    return nullptr;
+}
+
+template <bool VEC>
+SmFn pick_red(int threads, int u) {
+    if (threads == 256 && u == 4) return fr_red_softmax_f32<256, 4, VEC>;
+    if (threads == 512 && u == 2) return fr_red_softmax_f32<512, 2, VEC>;
+    if (threads == 1024 && u == 2) return fr_red_softmax_f32<1024, 2, VEC>;
+    return nullptr;
+}
+
+template <bool VEC>
+void pick_split(int threads, int nv, PartFn* part, FinFn* fin) {
+    *part = nullptr;
+    *fin = nullptr;
+    if (threads == 256 && nv == 8) {
+        *part = fr_split_softmax_part<256, 8, VEC>;
+        *fin = fr_split_softmax_fin<256, 8, VEC>;
+    } else if (threads == 256 && nv == 4) {
+        *part = fr_split_softmax_part<256, 4, VEC>;
+        *fin = fr_split_softmax_fin<256, 4, VEC>;
+    } else if (threads == 512 && nv == 4) {
+        *part = fr_split_softmax_part<512, 4, VEC>;
+        *fin = fr_split_softmax_fin<512, 4, VEC>;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_softmax(const fr_plan& p, const SoftmaxArgs& a, hipStream_t s) {
+    const bool vec = p.vec16 != 0;
+    if (p.form == FR_FORM_PER) {
+        SmFn f = vec ? pick_per<true>(p.seg, p.vec) : pick_per<false>(p.seg, p.vec);
+        if (!f) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(f, dim3((unsigned)p.grid), dim3(256), 0, s, a.x, a.y, a.rows, a.cols, a.x_rs, a.y_rs,
+                           a.lengths, a.argmax);
+        return hipGetLastError();
+    }
+    if (p.form == FR_FORM_RED) {
+        SmFn f = vec ? pick_red<true>(p.threads, p.vec) : pick_red<false>(p.threads, p.vec);
+        if (!f) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(f, dim3((unsigned)p.grid), dim3(p.threads), 0, s, a.x, a.y, a.rows, a.cols, a.x_rs,
+                           a.y_rs, a.lengths, a.argmax);
+        return hipGetLastError();
+    }
+    if (p.form == FR_FORM_SPLIT) {
+        PartFn part;
+        FinFn fin;
+        if (vec) pick_split<true>(p.threads, p.vec, &part, &fin);
+        else pick_split<false>(p.threads, p.vec, &part, &fin);
+        if (!part || !fin) return hipErrorInvalidValue;
+        SoftmaxPartial* ws = static_cast<SoftmaxPartial*>(a.ws);
+        hipLaunchKernelGGL(part, dim3((unsigned)p.grid), dim3(p.threads), 0, s, a.x, a.rows, a.cols, a.x_rs,
+                           a.lengths, ws, p.splits);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(fin, dim3((unsigned)p.grid2), dim3(p.threads), 0, s, a.x, a.y, a.rows, a.cols, a.x_rs,
+                           a.y_rs, a.lengths, a.argmax, (const SoftmaxPartial*)ws, p.splits);
+        return hipGetLastError();
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace fr

@@ -1,0 +1,88 @@
+"""GPU parity: fr_layernorm_rows against the fp64 oracle.
+
+bf16 in and out, fp32 arithmetic. Each output must be within one bf16 ulp of
+the oracle's bf16 value (the oracle rounds its fp64 result once; the kernel
+rounds an fp32 result), or - where y is a near-cancellation of its terms -
+within 1e-5 * (|(x - mu) * rstd * gamma| + |beta|) + 1e-6 of the exact
+value. Bit-exact pin: a constant row gives exactly beta.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import bf16_bits_of, bf16_bits_tensor, check_bf16, forced
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+import pointwise_reduction_amd as fr  # noqa: E402
+
+FORMS = {"per": fr.FR_FORM_PER, "red": fr.FR_FORM_RED}
+
+
+def gpu_ln(x_bits, g_bits, b_bits, form=fr.FR_FORM_AUTO, eps=1e-5):
+    x = bf16_bits_tensor(x_bits)
+    y = torch.empty_like(x)
+    g = None if g_bits is None else bf16_bits_tensor(g_bits)
+    b = None if b_bits is None else bf16_bits_tensor(b_bits)
+    with forced(form):
+        fr.fr_layernorm_rows(x, y, gamma=g, beta=b, eps=eps)
+    return bf16_bits_of(y)
+
+
+def compare(x, g, b, got, rows=None, eps=1e-5, what=""):
+    xs = x if rows is None else x[rows]
+    gs = got if rows is None else got[rows]
+    ref, y64, mag = oracle.layernorm_rows(xs, g, b, eps=eps)
+    check_bf16(gs, ref, y64, mag, what=what)
+
+
+@pytest.mark.parametrize("form", ["per", "red"])
+def test_layernorm_2048x32768_sampled(form):
+    x, g, b = synth.layernorm_inputs(2048, 32768, seed=3001)
+    got = gpu_ln(x, g, b, form=FORMS[form])
+    rows = np.unique(np.concatenate([[0, 1, 1023, 2047], np.random.default_rng(3).integers(0, 2048, 60)]))
+    compare(x, g, b, got, rows=rows, what=f"2048x32768 {form}")
+
+
+SHAPES = [(1, 8), (7, 13), (33, 31), (65, 33), (4, 4096), (3, 1000), (5, 32768), (2, 40000), (3, 16385)]
+
+
+@pytest.mark.parametrize("form", ["per", "red"])
+@pytest.mark.parametrize("shape", SHAPES, ids=[f"{r}x{c}" for r, c in SHAPES])
+def test_layernorm_forms(form, shape):
+    rows, cols = shape
+    plan_ok = cols <= (32768 if cols % 8 == 0 else 16384)
+    if form == "per" and not plan_ok:
+        pytest.skip("row does not fit the persistent form")
+    x, g, b = synth.layernorm_inputs(rows, cols, seed=3100 + cols)
+    got = gpu_ln(x, g, b, form=FORMS[form])
+    compare(x, g, b, got, what=f"{form} {rows}x{cols}")
+
+
+@pytest.mark.parametrize("form", ["per", "red"])
+def test_layernorm_constant_row_is_beta(form):
+    for cols in (8, 1000, 4096, 32768):
+        x, g, b = synth.layernorm_inputs(2, cols, seed=3200)
+        x[:] = synth.to_bf16(np.full((2, cols), -2.5625, dtype=np.float32))
+        got = gpu_ln(x, g, b, form=FORMS[form])
+        assert np.array_equal(got, np.broadcast_to(b, got.shape)), f"{form} cols={cols}"
+
+
+def test_layernorm_without_affine_and_eps():
+    x, _, _ = synth.layernorm_inputs(16, 3000, seed=3300)
+    for eps in (1e-5, 0.0, 1.0):
+        got = gpu_ln(x, None, None, eps=eps)
+        compare(x, None, None, got, eps=eps, what=f"no affine eps={eps}")
+
+
+def test_layernorm_row_stride():
+    x, g, b = synth.layernorm_inputs(6, 1000, seed=3400)
+    xp = np.zeros((6, 1024), dtype=np.uint16)
+    xp[:, :1000] = x
+    xd = bf16_bits_tensor(xp)[:, :1000]
+    y = torch.zeros((6, 1024), dtype=torch.bfloat16, device="cuda")
+    fr.fr_layernorm_rows(xd, y[:, :1000], gamma=bf16_bits_tensor(g), beta=bf16_bits_tensor(b))
+    got = bf16_bits_of(y)
+    assert np.all(got[:, 1000:] == 0)
+    compare(x, g, b, np.ascontiguousarray(got[:, :1000]), what="row stride 1024")

@@ -1,0 +1,200 @@
+"""GPU parity: fr_softmax_rows against the fp64 oracle.
+
+Covers the persistent, looped and split forms (forced), the 4096 x 1024
+workload in full, the ragged 512-row workload in full (lengths from
+{1000, 3000, 50257, 131071}, padded to 131072, tails never read or written),
+the pages' boundary shapes, bit-exact pins (argmax, constant rows) and
+determinism. Tolerance per element: |y - y_ref| <= 1e-5 * y_ref + 1e-6.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import check_fp32, dev, forced, host
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+import pointwise_reduction_amd as fr  # noqa: E402
+
+FORMS = {"per": fr.FR_FORM_PER, "red": fr.FR_FORM_RED, "split": fr.FR_FORM_SPLIT}
+
+
+def run(x_np, lengths=None, form=fr.FR_FORM_AUTO, use_ws=None, cols=None, y_fill=np.nan, argmax=True):
+    """Run the GPU softmax on x_np[:, :cols]; returns (y, argmax)."""
+    rows = x_np.shape[0]
+    cols = x_np.shape[1] if cols is None else cols
+    xd = dev(x_np)
+    x = xd[:, :cols]
+    yd = torch.full(xd.shape, float(y_fill), dtype=torch.float32, device="cuda")
+    y = yd[:, :cols]
+    L = None if lengths is None else dev(np.asarray(lengths, dtype=np.int32))
+    am = torch.full((rows,), -7, dtype=torch.int32, device="cuda") if argmax else None
+    if use_ws is None:
+        use_ws = form == fr.FR_FORM_SPLIT
+    ws = None
+    if use_ws:
+        nbytes = fr.fr_softmax_rows_workspace_bytes(rows, cols)
+        ws = torch.empty(max(nbytes, 16) // 4 + 4, dtype=torch.float32, device="cuda")
+    with forced(form):
+        fr.fr_softmax_rows(x, y, lengths=L, argmax=am, ws=ws)
+    return host(yd)[:, :cols], (host(am) if argmax else None), host(yd)
+
+
+def valid_mask(rows, cols, lengths):
+    L = np.full(rows, cols) if lengths is None else np.clip(np.asarray(lengths, dtype=np.int64), 0, cols)
+    return np.arange(cols)[None, :] < L[:, None]
+
+
+def compare(x_np, y, am, lengths=None, cols=None, what=""):
+    cols = x_np.shape[1] if cols is None else cols
+    y64, am_ref = oracle.softmax_rows(x_np[:, :cols] if cols != x_np.shape[1] else x_np, lengths=lengths)
+    written = valid_mask(x_np.shape[0], cols, lengths)  # j < len_i
+    check_fp32(np.where(written, y, 0.0), np.where(written, y64, 0.0), what=what)
+    if am is not None:
+        assert np.array_equal(am, am_ref), f"{what}: argmax differs at rows {np.nonzero(am != am_ref)[0][:8]}"
+
+
+# ------------------------------------------------------------------ the headline workload
+
+
+@pytest.mark.parametrize("seed", [2001, 2002, 2003])
+def test_softmax_4096x1024(seed):
+    x = synth.softmax_inputs(4096, 1024, seed=seed)
+    y, am, _ = run(x)
+    compare(x, y, am, what=f"4096x1024 seed {seed}")
+    assert np.allclose(y.sum(axis=1), 1.0, atol=1e-5)
+
+
+# ------------------------------------------------------------------ forms on the pages' shapes
+
+SMALL = [(1, 1), (7, 13), (33, 31), (65, 33), (256, 1000), (1823, 781), (3, 1024), (5, 2048), (2, 257)]
+
+
+@pytest.mark.parametrize("form", ["per", "red", "split"])
+@pytest.mark.parametrize("shape", SMALL, ids=[f"{r}x{c}" for r, c in SMALL])
+def test_softmax_forms_small(form, shape):
+    rows, cols = shape
+    x = synth.softmax_inputs(rows, cols, seed=2100 + rows + cols)
+    y, am, _ = run(x, form=FORMS[form])
+    compare(x, y, am, what=f"{form} {rows}x{cols}")
+
+
+LONG = [2049, 4097, 8192, 8193, 20000, 50257, 131071]
+
+
+@pytest.mark.parametrize("form", ["red", "split"])
+@pytest.mark.parametrize("cols", LONG)
+def test_softmax_forms_long_rows(form, cols):
+    x = synth.softmax_inputs(3, cols, seed=2200 + cols)
+    y, am, _ = run(x, form=FORMS[form])
+    compare(x, y, am, what=f"{form} 3x{cols}")
+
+
+@pytest.mark.parametrize("form", ["per", "red", "split"])
+def test_softmax_constant_rows_are_exactly_one_over_n(form):
+    lengths = [1, 3, 64, 1000, 1024, 2048] + ([5000, 50257] if form != "per" else [])
+    for n in lengths:
+        x = np.full((2, n), 0.3125, dtype=np.float32)
+        y, am, _ = run(x, form=FORMS[form])
+        assert np.all(y == np.float32(1.0) / np.float32(n)), f"{form} n={n}"
+        assert np.all(am == 0)
+
+
+def test_softmax_worked_example(golden):
+    g = golden("hello_gpu_ch12_worked_example.txt")
+    x = np.array([g["scores"]], dtype=np.float32)
+    for form in ("per", "red", "split"):
+        y, am, _ = run(x, form=FORMS[form])
+        np.testing.assert_allclose(y[0], g["probabilities"], atol=g["tolerance"])
+        assert am[0] == 2
+
+
+# ------------------------------------------------------------------ ragged rows
+
+
+@pytest.mark.parametrize("form", ["per", "red", "split"])
+def test_softmax_ragged_small(form):
+    cap = 2048 if form == "per" else 4100
+    lens = [0, 1, 2, 3, 63, 64, 65, 127, 1000, 1023, 1024, 1025, 2047, 2048]
+    if form != "per":
+        lens += [2049, 4095, 4097, 4100]
+    L = np.array(lens, dtype=np.int32)
+    x, _ = synth.ragged_softmax_inputs(len(L), cap, seed=2300, lengths=L)
+    y, am, yfull = run(x, lengths=L, form=FORMS[form])
+    compare(x, y, am, lengths=L, what=f"ragged {form}")
+    for r, n in enumerate(L):
+        assert np.isnan(yfull[r, n:]).all(), f"row {r}: output tail beyond len {n} was written"
+    assert am[0] == -1
+
+
+def test_softmax_lengths_are_clamped():
+    L = np.array([-5, 0, 40, 1 << 30], dtype=np.int32)
+    x = synth.softmax_inputs(4, 40, seed=2400)
+    y, am, _ = run(x, lengths=L)
+    compare(x, y, am, lengths=L, what="clamped lengths")
+    assert am[0] == -1 and am[1] == -1
+
+
+@pytest.mark.parametrize("use_ws", [True, False], ids=["split", "looped"])
+def test_softmax_ragged_512x131072_full(use_ws):
+    """The ragged workload at full size. Input tails hold NaN (a read would
+    poison the row) and the output tails hold a sentinel that must survive."""
+    x, L = synth.ragged_softmax_inputs(512, 131072, seed=5001)
+    sentinel = -12345.0
+    y, am, yfull = run(x, lengths=L, use_ws=use_ws, y_fill=sentinel)
+    plan = fr.fr_plan_query(fr.FR_OP_SOFTMAX, 512, 131072, has_lengths=True,
+                            ws_bytes=fr.fr_softmax_rows_workspace_bytes(512, 131072) if use_ws else 0)
+    assert plan.form == (fr.FR_FORM_SPLIT if use_ws else fr.FR_FORM_RED)
+    y64, am_ref = oracle.softmax_rows(x, lengths=L)
+    assert np.array_equal(am, am_ref)
+    for r in range(512):
+        n = L[r]
+        assert np.all(yfull[r, n:] == sentinel), f"row {r}: tail written"
+    written = valid_mask(512, 131072, L)
+    check_fp32(np.where(written, y, 0.0), np.where(written, y64, 0.0), what="ragged 512x131072")
+    assert np.isfinite(y[written]).all()
+
+
+# ------------------------------------------------------------------ semantics
+
+
+def test_softmax_nan_row_and_first_argmax():
+    x = synth.softmax_inputs(6, 300, seed=2500)
+    x[1, 17] = np.nan
+    x[2, 5] = x[2].max() + 1
+    x[2, 250] = x[2, 5]  # tie: the first index wins
+    x[3, :] = -np.inf
+    x[4, 10] = np.inf
+    for form in ("per", "red", "split"):
+        y, am, _ = run(x, form=FORMS[form])
+        compare(x, y, am, what=f"special values {form}")
+        assert am[1] == 17 and am[2] == 5 and np.isnan(y[1]).all()
+
+
+def test_softmax_in_place_and_row_stride():
+    x = synth.softmax_inputs(64, 1000, seed=2600)
+    xd = dev(np.pad(x, ((0, 0), (0, 24))))  # row stride 1024, 24 padding columns
+    view = xd[:, :1000]
+    fr.fr_softmax_rows(view, view)  # in place
+    y = host(xd)
+    assert np.all(y[:, 1000:] == 0)
+    y64, _ = oracle.softmax_rows(x)
+    check_fp32(y[:, :1000], y64, what="in place, strided")
+
+
+def test_softmax_unaligned_rows_use_element_path():
+    x = synth.softmax_inputs(9, 1001, seed=2700)
+    xd = dev(x)  # row stride 1001: rows are not 16-byte aligned
+    y = torch.empty_like(xd)
+    am = torch.empty(9, dtype=torch.int32, device="cuda")
+    for form in ("per", "red"):
+        with forced(FORMS[form]):
+            fr.fr_softmax_rows(xd, y, argmax=am)
+        compare(x, host(y), host(am), what=f"unaligned {form}")
+
+
+def test_softmax_is_deterministic():
+    x, L = synth.ragged_softmax_inputs(64, 60000, seed=2800, choices=(1000, 59999, 60000))
+    outs = [run(x, lengths=L, use_ws=True)[2] for _ in range(3)]
+    assert all(np.array_equal(outs[0].view(np.uint32), o.view(np.uint32)) for o in outs[1:])

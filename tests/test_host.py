@@ -1,0 +1,209 @@
+"""Host-side tests of libfr (no GPU needed).
+
+The C ABI library must load, export every symbol include/fr.h declares,
+reject invalid arguments with the documented status before any HIP call, and
+plan the expected reduction form and launch configuration for the five
+workloads. No compute call is made here.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import pointwise_reduction_amd as fr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "fr.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fr_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    declared = header_functions()
+    assert set(declared) == set(fr.EXPORTS)
+    for name in declared:
+        assert hasattr(fr.lib, name), name
+
+
+def test_status_strings_and_version():
+    assert fr.status_string(fr.FR_OK).startswith("FR_OK")
+    for code in range(-1, -10, -1):
+        assert fr.status_string(code).startswith("FR_E_")
+    assert fr.status_string(12345) == "unknown status"
+    assert fr.lib.fr_version() >= 100
+
+
+# ------------------------------------------------------------------ validation (returns before any HIP call)
+
+P = ctypes.c_void_p
+FAKE = P(0x10000)  # never dereferenced: every call below fails validation first
+FAKE_ODD = P(0x10002)
+
+
+def softmax(x=FAKE, y=FAKE, rows=4, cols=8, x_rs=8, x_cs=1, y_rs=8, y_cs=1, lengths=None, argmax=None, ws=None,
+            ws_bytes=0, dtype=fr.FR_F32):
+    return fr.lib.fr_softmax_rows(x, y, rows, cols, x_rs, x_cs, y_rs, y_cs, lengths, argmax, ws, ws_bytes, dtype,
+                                  None)
+
+
+def test_softmax_argument_errors():
+    assert softmax(rows=-1) == fr.FR_E_SIZE
+    assert softmax(cols=1 << 30) == fr.FR_E_SIZE
+    assert softmax(dtype=fr.FR_BF16) == fr.FR_E_DTYPE
+    assert softmax(x=None) == fr.FR_E_NULL
+    assert softmax(y=None) == fr.FR_E_NULL
+    assert softmax(x_cs=2) == fr.FR_E_STRIDE
+    assert softmax(y_rs=7) == fr.FR_E_STRIDE
+    assert softmax(x_rs=-8) == fr.FR_E_STRIDE
+    assert softmax(x=FAKE_ODD) == fr.FR_E_ALIGN
+    assert softmax(y=FAKE, x=FAKE, y_rs=16) == fr.FR_E_STRIDE  # in place needs equal strides
+    assert softmax(ws=P(0x10008), ws_bytes=1 << 20) == fr.FR_E_ALIGN
+    assert softmax(cols=100000, x_rs=100000, y_rs=100000, ws=FAKE, ws_bytes=16) == fr.FR_E_WORKSPACE
+    # empty work returns before touching anything
+    assert softmax(rows=0, x=None, y=None) == fr.FR_OK
+    assert softmax(cols=0, x=None, y=None) == fr.FR_OK
+
+
+def test_sum_relu_add_argument_errors():
+    f = fr.lib.fr_sum_relu_add
+    ok = dict(a=FAKE, b=FAKE, out=FAKE, rows=4, cols=8, a_rs=8, a_cs=1, b_rs=8, b_cs=1, out_s=1, ws=None,
+              ws_bytes=0, dtype=fr.FR_F32)
+
+    def call(**kw):
+        args = dict(ok, **kw)
+        return f(args["a"], args["b"], args["out"], args["rows"], args["cols"], args["a_rs"], args["a_cs"],
+                 args["b_rs"], args["b_cs"], args["out_s"], args["ws"], args["ws_bytes"], args["dtype"], None)
+
+    assert call(rows=-3) == fr.FR_E_SIZE
+    assert call(dtype=fr.FR_BF16) == fr.FR_E_DTYPE
+    assert call(b=None) == fr.FR_E_NULL
+    assert call(out=None) == fr.FR_E_NULL
+    assert call(b_cs=0) == fr.FR_E_STRIDE
+    assert call(a_rs=4) == fr.FR_E_STRIDE
+    assert call(out_s=0) == fr.FR_E_STRIDE
+    assert call(out=FAKE_ODD) == fr.FR_E_ALIGN
+    assert call(rows=0, a=None, b=None, out=None) == fr.FR_OK
+
+
+def test_layernorm_argument_errors():
+    f = fr.lib.fr_layernorm_rows
+
+    def call(x=FAKE, g=None, b=None, y=FAKE, rows=2, cols=16, x_rs=16, x_cs=1, y_rs=16, y_cs=1, eps=1e-5,
+             dtype=fr.FR_BF16):
+        return f(x, g, b, y, rows, cols, x_rs, x_cs, y_rs, y_cs, eps, dtype, None)
+
+    assert call(dtype=fr.FR_F32) == fr.FR_E_DTYPE
+    assert call(cols=0) == fr.FR_E_SIZE
+    assert call(eps=-1.0) == fr.FR_E_ARG
+    assert call(eps=float("nan")) == fr.FR_E_ARG
+    assert call(eps=float("inf")) == fr.FR_E_ARG
+    assert call(x=None) == fr.FR_E_NULL
+    assert call(y_cs=3) == fr.FR_E_STRIDE
+    assert call(x=P(0x10001)) == fr.FR_E_ALIGN
+    assert call(g=P(0x10001)) == fr.FR_E_ALIGN
+    assert call(rows=0, x=None, y=None) == fr.FR_OK
+
+
+def test_sumsq_argument_errors():
+    full = fr.lib.fr_sumsq_full
+    n = 1 << 20
+    need = fr.fr_sumsq_full_workspace_bytes(n)
+    assert need > 0
+    assert full(FAKE, -1, FAKE, None, 0, fr.FR_F32, None) == fr.FR_E_SIZE
+    assert full(FAKE, n, FAKE, None, 0, fr.FR_BF16, None) == fr.FR_E_DTYPE
+    assert full(FAKE, n, None, FAKE, need, fr.FR_F32, None) == fr.FR_E_NULL
+    assert full(None, n, FAKE, FAKE, need, fr.FR_F32, None) == fr.FR_E_NULL
+    assert full(FAKE, n, FAKE, None, 0, fr.FR_F32, None) == fr.FR_E_WORKSPACE
+    assert full(FAKE, n, FAKE, FAKE, need - 4, fr.FR_F32, None) == fr.FR_E_WORKSPACE
+    assert full(FAKE, n, FAKE, P(0x10004), need, fr.FR_F32, None) == fr.FR_E_ALIGN
+    rows_f = fr.lib.fr_sumsq_rows
+    assert rows_f(FAKE, FAKE, 4, 8, 8, 2, None, 0, fr.FR_F32, None) == fr.FR_E_STRIDE
+    assert rows_f(FAKE, None, 4, 8, 8, 1, None, 0, fr.FR_F32, None) == fr.FR_E_NULL
+
+
+# ------------------------------------------------------------------ planning
+
+
+def test_plans_for_the_five_workloads():
+    # Example 1.1, 64 x 128 fp32: half a wave per row, one vector per lane
+    p = fr.fr_plan_query(fr.FR_OP_SUM_RELU_ADD, 64, 128)
+    assert (p.form, p.seg, p.vec, p.rows_per_wg, p.grid) == (fr.FR_FORM_PER, 32, 1, 8, 8)
+    # softmax 4096 x 1024: a wave per row, 4 x 16-byte vectors per lane
+    p = fr.fr_plan_query(fr.FR_OP_SOFTMAX, 4096, 1024)
+    assert (p.form, p.seg, p.vec, p.grid) == (fr.FR_FORM_PER, 64, 4, 1024)
+    # LayerNorm 2048 x 32768 bf16: a 512-thread workgroup holds each row
+    p = fr.fr_plan_query(fr.FR_OP_LAYERNORM, 2048, 32768, dtype=fr.FR_BF16)
+    assert (p.form, p.threads, p.vec, p.grid) == (fr.FR_FORM_PER, 512, 8, 2048)
+    # sum of squares over 2^28: 2048 chunks of 2^17 plus a finishing pass
+    n = 1 << 28
+    ws = fr.fr_sumsq_full_workspace_bytes(n)
+    assert ws == 2048 * 4
+    p = fr.fr_plan_query(fr.FR_OP_SUMSQ, 1, n, ws_bytes=ws)
+    assert (p.form, p.splits, p.chunk, p.grid, p.grid2) == (fr.FR_FORM_SPLIT, 2048, 1 << 17, 2048, 1)
+    # ragged softmax, 512 rows of capacity 131072, with a workspace: 16 chunks of 8192
+    ws = fr.fr_softmax_rows_workspace_bytes(512, 131072)
+    assert ws == 512 * 16 * 16
+    p = fr.fr_plan_query(fr.FR_OP_SOFTMAX, 512, 131072, has_lengths=True, ws_bytes=ws)
+    assert (p.form, p.splits, p.chunk, p.grid, p.grid2) == (fr.FR_FORM_SPLIT, 16, 8192, 8192, 8192)
+    # ... and without one: one workgroup streams each row
+    p = fr.fr_plan_query(fr.FR_OP_SOFTMAX, 512, 131072, has_lengths=True)
+    assert (p.form, p.threads, p.grid) == (fr.FR_FORM_RED, 512, 512)
+
+
+def test_plan_thresholds_and_forms():
+    # persistent up to 2048 fp32 per row, then looped
+    assert fr.fr_plan_query(fr.FR_OP_SOFTMAX, 100, 2048).form == fr.FR_FORM_PER
+    assert fr.fr_plan_query(fr.FR_OP_SOFTMAX, 100, 2049).form == fr.FR_FORM_RED
+    # lane-group sizes follow the row length; masked tails round up
+    assert fr.fr_plan_query(fr.FR_OP_SOFTMAX, 1, 1).seg == 8
+    assert (fr.fr_plan_query(fr.FR_OP_SOFTMAX, 256, 1000).seg, fr.fr_plan_query(fr.FR_OP_SOFTMAX, 256, 1000).vec) == (64, 4)
+    assert fr.fr_plan_query(fr.FR_OP_SOFTMAX, 1, 65).seg == 32
+    # many long rows: looped even with a workspace; few long rows: split
+    ws = fr.fr_sum_workspace_bytes(4096, 65536)
+    assert fr.fr_plan_query(fr.FR_OP_SUMSQ, 4096, 65536, ws_bytes=ws).form == fr.FR_FORM_RED
+    ws = fr.fr_sum_workspace_bytes(64, 16384)
+    p = fr.fr_plan_query(fr.FR_OP_SUMSQ, 64, 16384, ws_bytes=ws)
+    assert p.form == fr.FR_FORM_SPLIT and p.splits * p.chunk >= 16384 and p.ws_bytes == ws
+    # unaligned bf16 rows use element accesses and smaller register tiles
+    p = fr.fr_plan_query(fr.FR_OP_LAYERNORM, 4, 16384, dtype=fr.FR_BF16, aligned16=False)
+    assert (p.form, p.vec16, p.vec) == (fr.FR_FORM_PER, 0, 4)
+    assert fr.fr_plan_query(fr.FR_OP_LAYERNORM, 4, 16385, dtype=fr.FR_BF16, aligned16=False).form == fr.FR_FORM_RED
+    assert fr.fr_plan_query(fr.FR_OP_LAYERNORM, 4, 32769, dtype=fr.FR_BF16).form == fr.FR_FORM_RED
+
+
+def test_forced_forms():
+    prev = fr.fr_force_form(fr.FR_FORM_RED)
+    try:
+        assert fr.fr_plan_query(fr.FR_OP_SOFTMAX, 7, 13).form == fr.FR_FORM_RED
+        fr.fr_force_form(fr.FR_FORM_SPLIT)
+        with pytest.raises(fr.FrError) as e:
+            fr.fr_plan_query(fr.FR_OP_SOFTMAX, 7, 13)  # no workspace
+        assert e.value.status == fr.FR_E_ARG
+        ws = fr.fr_softmax_rows_workspace_bytes(7, 13)
+        p = fr.fr_plan_query(fr.FR_OP_SOFTMAX, 7, 13, ws_bytes=ws)
+        assert (p.form, p.splits) == (fr.FR_FORM_SPLIT, 1)
+        with pytest.raises(fr.FrError):
+            fr.fr_plan_query(fr.FR_OP_LAYERNORM, 7, 13, dtype=fr.FR_BF16)  # LayerNorm rows never split
+        fr.fr_force_form(fr.FR_FORM_PER)
+        with pytest.raises(fr.FrError):
+            fr.fr_plan_query(fr.FR_OP_SOFTMAX, 7, 4096)  # too long for registers
+    finally:
+        fr.fr_force_form(prev)
+    assert fr.fr_force_form(fr.FR_FORM_AUTO) == prev
+
+
+def test_workspace_matches_example_6_2_layout(golden):
+    # Example 6.2 keeps 2 fp32 partials per row for 64 rows (512 bytes). Our
+    # plan for the same shape keeps more partials per row (more workgroups
+    # for 256 CUs), still one fp32 per (row, chunk).
+    g = golden("stax4_example_6_2.txt")
+    rows, cols = int(g["rows"]), int(g["cols"])
+    p = fr.fr_plan_query(fr.FR_OP_SUMSQ, rows, cols, ws_bytes=1 << 20)
+    assert p.form == fr.FR_FORM_SPLIT
+    assert p.ws_bytes == rows * p.splits * 4
+    assert p.splits >= g["splits"]
+    assert fr.fr_sum_workspace_bytes(rows, cols) == p.ws_bytes
