@@ -1,0 +1,420 @@
+"""Benchmark of the fused row-reduction kernels on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--warm] [--eager]
+
+A step is one pass of the whole operation over one batch of synthetic input
+already resident in HBM. The default workload is the row softmax over
+4096 x 1024 fp32 (the headline configuration). The other workloads (Example
+1.1 sums, LayerNorm 2048 x 32768 bf16, the 2^28 sum of squares, the ragged
+512-row softmax) are selected with --workload.
+
+Timing: W untimed steps, then exactly K steps between two events on the
+launch stream, with a device synchronization on both sides. Consecutive
+steps rotate through enough distinct buffer sets (>= 1 GiB in total) that
+the 256 MB MALL cannot serve a step's reads from the previous use of the same
+buffers (--warm uses one set). The K launches are captured once into a HIP
+graph and replayed, so host launch overhead does not enter the device time
+(--eager launches them one by one instead); the graph's output is checked
+against an eager launch before the timing is reported.
+
+Output: one JSON line with the effective HBM bandwidth (logical bytes: each
+input read once, each output written once), the roofline entry for the
+dominant kernel and the fp64 oracle timed on the host (cpu_baseline).
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+METRIC = "effective HBM GB/s and % of MI355X peak for fused reductions (softmax 4096x1024)"
+ROTATE_BYTES = 1 << 30
+
+
+# ------------------------------------------------------------------ logical bytes
+
+
+def softmax_bytes(rows, cols, lengths=None, argmax=False):
+    """Each valid input element read once and each output written once
+    ("Stax (4)", 9.5: the fused softmax moves 2N elements), plus the length
+    array and the argmax output when present."""
+    n = rows * cols if lengths is None else int(np.clip(lengths, 0, cols).sum())
+    extra = (rows * 4 if lengths is not None else 0) + (rows * 4 if argmax else 0)
+    return 8 * n + extra
+
+
+def sum_relu_add_bytes(rows, cols):
+    return 2 * rows * cols * 4 + rows * 4
+
+
+def layernorm_bytes(rows, cols):
+    return 2 * rows * cols * 2 + 2 * cols * 2
+
+
+def sumsq_bytes(n):
+    return n * 4 + 4
+
+
+def unfused_softmax_elements(M, N):
+    """Element reads and writes of softmax as five separate kernels (amax,
+    subtract, exp, sum, divide): reads 5MN + 2M, writes 3MN + 2M (CMU 15-779
+    Lecture 8, section 3)."""
+    return 5 * M * N + 2 * M, 3 * M * N + 2 * M
+
+
+# ------------------------------------------------------------------ workloads
+
+
+class Workload:
+    """Inputs for `sets` rotating buffer sets, one launch per step, the
+    logical bytes of a step and an oracle closure for the CPU baseline."""
+
+    name = ""
+    kernel = ""
+
+    def config(self):
+        raise NotImplementedError
+
+
+def make_workload(name, torch, fr, synth):
+    dev = "cuda"
+
+    def d(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    if name == "softmax":
+        rows, cols = 4096, 1024
+        x_host = synth.softmax_inputs(rows, cols, seed=2001)
+        per_set = 2 * rows * cols * 4
+
+        class W(Workload):
+            kernel = "fr_per_softmax_f32"
+            bytes = softmax_bytes(rows, cols)
+            dtype = "f32"
+
+            def alloc(self, sets):
+                x0 = d(x_host)
+                self.x = [x0] + [x0.clone() for _ in range(sets - 1)]
+                self.y = [torch.empty_like(x0) for _ in range(sets)]
+                self.args = [(x, y) for x, y in zip(self.x, self.y)]
+
+            def launch(self, k):
+                x, y = self.args[k]
+                fr.fr_softmax_rows(x, y)
+
+            def output(self, k):
+                return self.y[k]
+
+            def config(self):
+                p = fr.fr_plan_query(fr.FR_OP_SOFTMAX, rows, cols)
+                return {"workload": "row softmax 4096x1024 fp32, x ~ N(0,1)*4 with 1% entries +/-30",
+                        "rows": rows, "cols": cols, "form": fr.FORM_NAMES[p.form],
+                        "launch": {"threads": p.threads, "lanes_per_row": p.seg, "vec16_per_lane": p.vec,
+                                   "grid": p.grid}}
+
+            def oracle_fn(self):
+                import oracle
+                return lambda: oracle.softmax_rows(x_host), self.bytes, "full 4096x1024 batch"
+
+        return W(), per_set
+
+    if name == "sum_relu_add":
+        rows, cols = 64, 128
+        a_h, b_h, _ = synth.sum_relu_add_inputs(rows, cols, seed=1001)
+        per_set = sum_relu_add_bytes(rows, cols)
+
+        class W(Workload):
+            kernel = "fr_per_sum_f32"
+            bytes = sum_relu_add_bytes(rows, cols)
+            dtype = "f32"
+
+            def alloc(self, sets):
+                self.args = [(d(a_h), d(b_h), torch.empty(rows, dtype=torch.float32, device=dev))
+                             for _ in range(sets)]
+
+            def launch(self, k):
+                a, b, o = self.args[k]
+                fr.fr_sum_relu_add(a, b, o)
+
+            def output(self, k):
+                return self.args[k][2]
+
+            def config(self):
+                return {"workload": "Example 1.1 sum_r 2*relu(a+b), fp32 [64,128] (latency-bound)",
+                        "rows": rows, "cols": cols, "form": "per"}
+
+            def oracle_fn(self):
+                import oracle
+                return lambda: oracle.sum_relu_add(a_h, b_h), self.bytes, "full 64x128 batch"
+
+        return W(), per_set
+
+    if name == "layernorm":
+        rows, cols = 2048, 32768
+        x_h, g_h, b_h = synth.layernorm_inputs(rows, cols, seed=3001)
+        per_set = 2 * rows * cols * 2
+
+        def bf(u):
+            return torch.from_numpy(np.ascontiguousarray(u).view(np.int16)).to(dev).view(torch.bfloat16)
+
+        class W(Workload):
+            kernel = "fr_per_layernorm_bf16"
+            bytes = layernorm_bytes(rows, cols)
+            dtype = "bf16 in/out, f32 math"
+
+            def alloc(self, sets):
+                x0 = bf(x_h)
+                self.g, self.b = bf(g_h), bf(b_h)
+                self.args = [(x0 if i == 0 else x0.clone(), torch.empty_like(x0)) for i in range(sets)]
+
+            def launch(self, k):
+                x, y = self.args[k]
+                fr.fr_layernorm_rows(x, y, gamma=self.g, beta=self.b)
+
+            def output(self, k):
+                return self.args[k][1]
+
+            def config(self):
+                p = fr.fr_plan_query(fr.FR_OP_LAYERNORM, rows, cols, dtype=fr.FR_BF16)
+                return {"workload": "LayerNorm bf16 [2048,32768], eps 1e-5", "rows": rows, "cols": cols,
+                        "form": fr.FORM_NAMES[p.form], "launch": {"threads": p.threads, "vec16_per_lane": p.vec}}
+
+            def oracle_fn(self):
+                import oracle
+                r = 64
+                return (lambda: oracle.layernorm_rows(x_h[:r], g_h, b_h), layernorm_bytes(r, cols),
+                        f"first {r} of 2048 rows")
+
+        return W(), per_set
+
+    if name == "sumsq":
+        n = 1 << 28
+        x_h = synth.sumsq_inputs(n, seed=4001)
+        per_set = n * 4
+
+        class W(Workload):
+            kernel = "fr_split_sum_f32"
+            bytes = sumsq_bytes(n)
+            dtype = "f32"
+
+            def alloc(self, sets):
+                x0 = d(x_h)
+                ws_n = fr.fr_sumsq_full_workspace_bytes(n) // 4
+                self.args = [(x0 if i == 0 else x0.clone(), torch.empty(1, dtype=torch.float32, device=dev),
+                              torch.empty(ws_n, dtype=torch.float32, device=dev)) for i in range(sets)]
+
+            def launch(self, k):
+                x, o, ws = self.args[k]
+                fr.fr_sumsq_full(x, o, ws=ws)
+
+            def output(self, k):
+                return self.args[k][1]
+
+            def config(self):
+                return {"workload": "sum of x^2 over fp32 [2^28] to one scalar (split + finish)", "n": n,
+                        "form": "split"}
+
+            def oracle_fn(self):
+                import oracle
+                m = 1 << 26
+                return lambda: oracle.sumsq(x_h[:m]), sumsq_bytes(m), "first 2^26 of 2^28 elements"
+
+        return W(), per_set
+
+    if name == "ragged":
+        rows, cap = 512, 131072
+        x_h, L_h = synth.ragged_softmax_inputs(rows, cap, seed=5001)
+        nbytes = softmax_bytes(rows, cap, lengths=L_h, argmax=True)
+        per_set = 2 * rows * cap * 4
+
+        class W(Workload):
+            kernel = "fr_split_softmax_fin"
+            bytes = nbytes
+            dtype = "f32"
+
+            def alloc(self, sets):
+                x0 = d(x_h)
+                self.L = d(L_h)
+                ws_n = fr.fr_softmax_rows_workspace_bytes(rows, cap) // 4
+                self.args = [(x0 if i == 0 else x0.clone(), torch.empty_like(x0),
+                              torch.empty(rows, dtype=torch.int32, device=dev),
+                              torch.empty(ws_n, dtype=torch.float32, device=dev)) for i in range(sets)]
+
+            def launch(self, k):
+                x, y, am, ws = self.args[k]
+                fr.fr_softmax_rows(x, y, lengths=self.L, argmax=am, ws=ws)
+
+            def output(self, k):
+                return self.args[k][2]
+
+            def config(self):
+                return {"workload": "ragged softmax + argmax, 512 rows padded to 131072, lengths from "
+                                    "{1000,3000,50257,131071}", "rows": rows, "row_capacity": cap,
+                        "valid_elements": int(L_h.sum()), "form": "split"}
+
+            def oracle_fn(self):
+                import oracle
+                r = 64
+                return (lambda: oracle.softmax_rows(x_h[:r], lengths=L_h[:r]),
+                        softmax_bytes(r, cap, lengths=L_h[:r], argmax=True), f"first {r} of 512 rows")
+
+        return W(), per_set
+
+    raise SystemExit(f"unknown workload {name}")
+
+
+# ------------------------------------------------------------------ measurement
+
+
+def cpu_baseline(oracle_fn, budget_s):
+    fn, nbytes, sample = oracle_fn
+    t0 = time.perf_counter()
+    fn()
+    one = time.perf_counter() - t0
+    reps = max(1, int(budget_s / max(one, 1e-6)))
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        fn()
+    dt = time.perf_counter() - t0
+    return {"value": round(nbytes * reps / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{sample}, {reps} passes in {dt:.1f} s, single thread, fp64"}
+
+
+def read_traffic(kernel, workload):
+    """HBM bytes per launch from a committed counter summary, if its recorded
+    kernel-source digest matches the current sources; else None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"counters_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "pointwise_reduction_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    if fields.get("csrc_sha256") != h.hexdigest() or fields.get("kernel") != kernel:
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="softmax",
+                    choices=["softmax", "sum_relu_add", "layernorm", "sumsq", "ragged"])
+    ap.add_argument("--warm", action="store_true", help="one buffer set: reads may hit the MALL")
+    ap.add_argument("--eager", action="store_true", help="launch each step from the host (no graph)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import pointwise_reduction_amd as fr
+    import synth
+
+    torch.cuda.set_device(0)
+    wl, per_set = make_workload(args.workload, torch, fr, synth)
+    sets = 1 if args.warm else max(2, math.ceil(ROTATE_BYTES / per_set))
+    sets = min(sets, args.steps) if args.steps > 0 else sets
+    wl.alloc(sets)
+    stream = torch.cuda.current_stream()
+
+    # eager reference output of set 0
+    wl.launch(0)
+    torch.cuda.synchronize()
+    ref_out = wl.output(0).clone()
+
+    K, W = args.steps, args.warmup
+    for k in range(W):
+        wl.launch(k % sets)
+    torch.cuda.synchronize()
+
+    graph = None
+    if not args.eager:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for k in range(K):
+                wl.launch(k % sets)
+        torch.cuda.synchronize()
+        graph.replay()  # untimed replay: first replay uploads the graph
+        torch.cuda.synchronize()
+
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    if graph is not None:
+        graph.replay()
+    else:
+        for k in range(K):
+            wl.launch(k % sets)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end)
+
+    # the replayed (or eager) launches computed what an eager launch computes
+    same = torch.equal(wl.output(0).view(torch.uint8), ref_out.view(torch.uint8))
+    if not same:
+        print("bench.py: timed output differs from the eager reference", file=sys.stderr)
+        sys.exit(1)
+
+    ms_per_step = ms / K
+    gbs = wl.bytes / (ms_per_step * 1e-3) / 1e9
+    cfg = wl.config()
+    cfg.update({"buffer_sets": sets, "rotated_bytes": sets * per_set, "timing": "eager" if args.eager else
+                "hip graph of K launches", "cache": "warm (one set)" if args.warm else
+                "rotating sets >= 1 GiB to defeat the 256 MB MALL"})
+    result = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": cfg,
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(gbs, 2),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "traffic": read_traffic(wl.kernel, args.workload),
+            "kernel": wl.kernel,
+            "algorithmic_bytes_per_launch": wl.bytes,
+        },
+    }
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(wl.oracle_fn(), args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
