@@ -339,8 +339,6 @@ def main():
     sets = 1 if args.warm else max(2, math.ceil(ROTATE_BYTES / per_set))
     sets = min(sets, args.steps) if args.steps > 0 else sets
     wl.alloc(sets)
-    stream = torch.cuda.current_stream()
-
     # eager reference output of set 0
     wl.launch(0)
     torch.cuda.synchronize()
@@ -351,28 +349,17 @@ def main():
         wl.launch(k % sets)
     torch.cuda.synchronize()
 
-    graph = None
-    if not args.eager:
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for k in range(K):
-                wl.launch(k % sets)
-        torch.cuda.synchronize()
-        graph.replay()  # untimed replay: first replay uploads the graph
-        torch.cuda.synchronize()
+    from pointwise_reduction_amd import timing
 
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
+    graph = None if args.eager else timing.capture(lambda k: wl.launch(k % sets), K)
+    # poison every output so the check below sees what the timed steps wrote
+    for k in range(sets):
+        wl.output(k).view(torch.uint8).fill_(0xFF)
     torch.cuda.synchronize()
-    start.record(stream)
     if graph is not None:
-        graph.replay()
+        ms = timing.time_replays(graph, K, reps=1)[0] * K
     else:
-        for k in range(K):
-            wl.launch(k % sets)
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end)
+        ms = timing.time_eager(lambda k: wl.launch(k % sets), K) * K
 
     # the replayed (or eager) launches computed what an eager launch computes
     same = torch.equal(wl.output(0).view(torch.uint8), ref_out.view(torch.uint8))

@@ -87,7 +87,7 @@ typedef struct fr_plan {
     int32_t splits;       /* chunks per row (SPLIT), else 1 */
     int32_t chunk;        /* elements per chunk (SPLIT), else 0 */
     int32_t vec16;        /* 1: 16-byte vector accesses; 0: element accesses */
-    int32_t reserved;
+    int32_t occupancy;    /* minimum waves per SIMD requested from the compiler (0: none) */
     int64_t grid;         /* workgroups of the main kernel */
     int64_t grid2;        /* workgroups of the finishing kernel (0: none) */
     uint64_t ws_bytes;    /* workspace bytes this plan uses */
@@ -113,6 +113,16 @@ int fr_plan_query(int op, int64_t rows, int64_t cols, int dtype, int num_cus, in
  * workspace cannot use the forced form returns FR_E_ARG. Not thread-safe;
  * returns the previous setting. */
 int fr_force_form(int form);
+
+/* Tuning hook ("Stax (4)", 9.6, Algorithm 9.1: time candidate launch
+ * configurations and keep the fastest). Every later call of operation `op`
+ * uses the form and launch knobs of `plan` (form, threads, seg, vec,
+ * rows_per_wg, chunk, occupancy); grid, splits and workspace size are
+ * recomputed for each call's shape. A candidate that cannot serve a shape,
+ * or has no compiled kernel, makes that call return FR_E_ARG; a split
+ * candidate needing more workspace than given returns FR_E_WORKSPACE.
+ * plan = NULL clears the override. Not thread-safe. */
+int fr_tune_override(int op, const fr_plan* plan);
 
 /* ------------------------------------------------------------ Example 1.1
  * out[i] = sum_j 2 * relu(a[i,j] + b[i,j])   ("Stax (4)", 9.2, Listing 9.1,

@@ -32,7 +32,7 @@ FORM_NAMES = {FR_FORM_PER: "per", FR_FORM_RED: "red", FR_FORM_SPLIT: "split"}
 
 # Every symbol include/fr.h declares.
 EXPORTS = (
-    "fr_status_string", "fr_version", "fr_plan_query", "fr_force_form",
+    "fr_status_string", "fr_version", "fr_plan_query", "fr_force_form", "fr_tune_override",
     "fr_sum_relu_add", "fr_sum_workspace_bytes",
     "fr_softmax_rows_workspace_bytes", "fr_softmax_rows",
     "fr_layernorm_rows",
@@ -51,12 +51,12 @@ class fr_plan(ctypes.Structure):
         ("op", ctypes.c_int32), ("form", ctypes.c_int32), ("threads", ctypes.c_int32),
         ("seg", ctypes.c_int32), ("vec", ctypes.c_int32), ("rows_per_wg", ctypes.c_int32),
         ("splits", ctypes.c_int32), ("chunk", ctypes.c_int32), ("vec16", ctypes.c_int32),
-        ("reserved", ctypes.c_int32), ("grid", ctypes.c_int64), ("grid2", ctypes.c_int64),
+        ("occupancy", ctypes.c_int32), ("grid", ctypes.c_int64), ("grid2", ctypes.c_int64),
         ("ws_bytes", ctypes.c_uint64),
     ]
 
     def as_dict(self):
-        return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
+        return {name: getattr(self, name) for name, _ in self._fields_}
 
 
 def _load():
@@ -70,6 +70,7 @@ def _load():
         "fr_version": (I32, []),
         "fr_plan_query": (I32, [I32, I64, I64, I32, I32, I32, U64, I32, ctypes.POINTER(fr_plan)]),
         "fr_force_form": (I32, [I32]),
+        "fr_tune_override": (I32, [I32, ctypes.POINTER(fr_plan)]),
         "fr_sum_relu_add": (I32, [P, P, P, I64, I64, I64, I64, I64, I64, I64, P, U64, I32, P]),
         "fr_sum_workspace_bytes": (U64, [I64, I64, I32]),
         "fr_softmax_rows_workspace_bytes": (U64, [I64, I64, I32]),
@@ -141,6 +142,17 @@ def fr_plan_query(op, rows, cols, dtype=FR_F32, num_cus=256, has_lengths=False, 
 
 def fr_force_form(form):
     return lib.fr_force_form(form)
+
+
+def fr_tune_override(op, plan=None, **knobs):
+    """Use a candidate launch configuration for every later call of `op`
+    (tuning). Pass an fr_plan or keyword knobs (form, threads, seg, vec,
+    rows_per_wg, chunk, occupancy); plan=None and no knobs clears it."""
+    if plan is None and knobs:
+        plan = fr_plan()
+        for k, v in knobs.items():
+            setattr(plan, k, v)
+    _check(lib.fr_tune_override(op, None if plan is None else ctypes.byref(plan)), "fr_tune_override")
 
 
 def fr_sum_workspace_bytes(rows, cols, dtype=FR_F32):

@@ -42,6 +42,23 @@ def common_flags():
     ]
 
 
+def parse_resource_usage(lines):
+    """Per-kernel VGPRs, scratch bytes and occupancy from the compiler's
+    kernel-resource-usage remarks."""
+    usage, cur = {}, None
+    for line in lines:
+        if "Function Name:" in line:
+            cur = line.split("Function Name:", 1)[1].strip()
+            usage[cur] = {}
+        elif cur and "VGPRs:" in line and "AGPR" not in line:
+            usage[cur]["vgpr"] = int(line.rsplit(":", 1)[1].split()[0])
+        elif cur and "ScratchSize" in line:
+            usage[cur]["scratch"] = int(line.rsplit(":", 1)[1].split()[0])
+        elif cur and "Occupancy" in line:
+            usage[cur]["occupancy"] = int(line.rsplit(":", 1)[1].split()[0])
+    return usage
+
+
 def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
@@ -52,25 +69,35 @@ def build(verbose=False, jobs=None):
     cc = hipcc()
     flags = common_flags()
 
+    usage = {}
+
     def compile_one(src):
         obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-        lang = ["-x", "hip"] if src.endswith(".hip") else []
+        lang = ["-x", "hip", "-Rpass-analysis=kernel-resource-usage"] if src.endswith(".hip") else []
         cmd = [cc] + flags + lang + ["-c", src, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         res = subprocess.run(cmd, capture_output=True, text=True)
-        out = "\n".join(l for l in (res.stdout + res.stderr).splitlines()
-                        if "packed-fp32-ops" not in l)  # host pass does not know the feature
+        lines = [l for l in (res.stdout + res.stderr).splitlines()
+                 if "packed-fp32-ops" not in l]  # host pass does not know the feature
         if res.returncode != 0:
-            raise RuntimeError(f"hipcc failed on {src}:\n{out}")
-        if out.strip() and verbose:
-            print(out)
+            raise RuntimeError(f"hipcc failed on {src}:\n" + "\n".join(lines))
+        usage.update(parse_resource_usage(lines))
+        rest = [l for l in lines if "remark" not in l and "kernel-resource-usage" not in l]
+        if rest and verbose:
+            print("\n".join(rest))
         return obj
 
     srcs = sources()
     jobs = jobs or min(8, len(srcs))
     with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(compile_one, srcs))
+    with open(os.path.join(BUILD_DIR, "resource_usage.txt"), "w") as f:
+        for name, u in sorted(usage.items()):
+            f.write(f"{name} vgpr={u.get('vgpr')} scratch={u.get('scratch')} occupancy={u.get('occupancy')}\n")
+    spills = sorted(n for n, u in usage.items() if u.get("scratch", 0) > 0)
+    if spills:  # Algorithm 9.1 rejects configurations that spill registers
+        raise RuntimeError("kernels spill registers to scratch: " + ", ".join(spills))
     tmp = LIB + ".tmp"
     cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     if verbose:

@@ -28,6 +28,13 @@ namespace {
 
 int g_forced_form = FR_FORM_AUTO;
 
+// Tuning overrides, one per operation (index = FR_OP_*).
+constexpr int kOps = 5;
+fr_plan g_override[kOps];
+bool g_has_override[kOps] = {false, false, false, false, false};
+
+const fr_plan* override_for(int op) { return (op > 0 && op < kOps && g_has_override[op]) ? &g_override[op] : nullptr; }
+
 constexpr int kMaxDevices = 64;
 struct DeviceInfo {
     int state = 0;  // 0 unknown, 1 usable gfx950, -1 unusable
@@ -83,7 +90,12 @@ int check_sizes(int64_t rows, int64_t cols) {
     return FR_OK;
 }
 
-int finish_launch(hipError_t e) { return e == hipSuccess ? FR_OK : FR_E_LAUNCH; }
+// A plan whose kernel was not compiled (only reachable through a tuning
+// override) is an argument error; any other failure is a launch error.
+int finish_launch(hipError_t e) {
+    if (e == hipSuccess) return FR_OK;
+    return e == hipErrorInvalidDeviceFunction ? FR_E_ARG : FR_E_LAUNCH;
+}
 
 int run_sum(int prologue, const void* a, const void* b, void* out, int64_t rows, int64_t cols, int64_t a_rs,
             int64_t b_rs, int64_t out_s, void* ws, uint64_t ws_bytes, void* stream) {
@@ -93,7 +105,7 @@ int run_sum(int prologue, const void* a, const void* b, void* out, int64_t rows,
     const int v16 = vec_ok(a, a_rs, 4) && vec_ok(b, b_rs, 4);
     fr_plan plan;
     const int op = prologue == kReluAdd ? FR_OP_SUM_RELU_ADD : FR_OP_SUMSQ;
-    st = make_plan(op, rows, cols, FR_F32, num_cus, 0, ws ? ws_bytes : 0, v16, g_forced_form, &plan);
+    st = make_plan(op, rows, cols, FR_F32, num_cus, 0, ws ? ws_bytes : 0, v16, g_forced_form, override_for(op), &plan);
     if (st != FR_OK) return st;
     SumArgs args{prologue, (const float*)a, (const float*)b, (float*)out, (int)rows, (int)cols, a_rs, b_rs, out_s,
                  (float*)ws};
@@ -132,7 +144,19 @@ int fr_force_form(int form) {
 int fr_plan_query(int op, int64_t rows, int64_t cols, int dtype, int num_cus, int has_lengths, uint64_t ws_bytes,
                   int aligned16, fr_plan* plan) {
     if (!plan) return FR_E_NULL;
-    return make_plan(op, rows, cols, dtype, num_cus, has_lengths, ws_bytes, aligned16, g_forced_form, plan);
+    return make_plan(op, rows, cols, dtype, num_cus, has_lengths, ws_bytes, aligned16, g_forced_form,
+                     override_for(op), plan);
+}
+
+int fr_tune_override(int op, const fr_plan* plan) {
+    if (op <= 0 || op >= kOps) return FR_E_ARG;
+    if (plan) {
+        g_override[op] = *plan;
+        g_has_override[op] = true;
+    } else {
+        g_has_override[op] = false;
+    }
+    return FR_OK;
 }
 
 uint64_t fr_sum_workspace_bytes(int64_t rows, int64_t cols, int dtype) {
@@ -193,7 +217,8 @@ int fr_sumsq_full(const void* x, int64_t n, void* out, void* ws, uint64_t ws_byt
     // A full reduction has a single output: split whenever the vector does
     // not fit one persistent row (the form is not left to the row heuristics).
     const int form = need > 0 ? FR_FORM_SPLIT : FR_FORM_PER;
-    st = make_plan(FR_OP_SUMSQ, 1, n, FR_F32, num_cus, 0, need > 0 ? ws_bytes : 0, v16, form, &plan);
+    st = make_plan(FR_OP_SUMSQ, 1, n, FR_F32, num_cus, 0, need > 0 ? ws_bytes : 0, v16, form,
+                   override_for(FR_OP_SUMSQ), &plan);
     if (st != FR_OK) return st;
     SumArgs args{kSquare, (const float*)x, nullptr, (float*)out, 1, (int)n, n, 0, 1, (float*)ws};
     (void)hipGetLastError();
@@ -227,7 +252,7 @@ int fr_softmax_rows(const void* x, void* y, int64_t rows, int64_t cols, int64_t 
     const int v16 = vec_ok(x, x_rs, 4) && vec_ok(y, y_rs, 4);
     fr_plan plan;
     st = make_plan(FR_OP_SOFTMAX, rows, cols, FR_F32, num_cus, lengths != nullptr, ws ? ws_bytes : 0, v16,
-                   g_forced_form, &plan);
+                   g_forced_form, override_for(FR_OP_SOFTMAX), &plan);
     if (st != FR_OK) return st;
     SoftmaxArgs args{(const float*)x, (float*)y, (int)rows, (int)cols, x_rs, y_rs, lengths, argmax, ws};
     (void)hipGetLastError();
@@ -252,7 +277,8 @@ int fr_layernorm_rows(const void* x, const void* gamma, const void* beta, void* 
     const int v16 = cols % 8 == 0 && vec_ok(x, x_rs, 8) && vec_ok(y, y_rs, 8) && vec_ok(gamma, 0, 8) &&
                     vec_ok(beta, 0, 8);
     fr_plan plan;
-    st = make_plan(FR_OP_LAYERNORM, rows, cols, FR_BF16, num_cus, 0, 0, v16, g_forced_form, &plan);
+    st = make_plan(FR_OP_LAYERNORM, rows, cols, FR_BF16, num_cus, 0, 0, v16, g_forced_form,
+                   override_for(FR_OP_LAYERNORM), &plan);
     if (st != FR_OK) return st;
     LayerNormArgs args{(const uint16_t*)x, (const uint16_t*)gamma, (const uint16_t*)beta, (uint16_t*)y,
                        (int)rows, (int)cols, x_rs, y_rs, eps};

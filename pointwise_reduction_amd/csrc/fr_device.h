@@ -213,30 +213,58 @@ __device__ __forceinline__ void st4u(uint16_t* p, u32x4 v) {
     else *reinterpret_cast<u32x4*>(p) = v;
 }
 
-// Load the 4 elements j0..j0+3 of a row of length L. A full vector is one
-// 16-byte load when VEC; elements at j >= L are never touched and read as
-// `fill` (the identity of the reduction that follows).
-template <bool VEC, bool NT>
-__device__ __forceinline__ f32x4 load4_masked(const float* row, int j0, int L, float fill) {
-    if (VEC && j0 + 3 < L) return ld4<NT>(row + j0);
-    f32x4 v = {fill, fill, fill, fill};
-    if (j0 + 0 < L) v.x = ld1<NT>(row + j0 + 0);
-    if (j0 + 1 < L) v.y = ld1<NT>(row + j0 + 1);
-    if (j0 + 2 < L) v.z = ld1<NT>(row + j0 + 2);
-    if (j0 + 3 < L) v.w = ld1<NT>(row + j0 + 3);
-    return v;
-}
-template <bool VEC, bool NT>
-__device__ __forceinline__ void store4_masked(float* row, int j0, int L, f32x4 v) {
-    if (VEC && j0 + 3 < L) {
-        st4<NT>(row + j0, v);
-        return;
+// Masking modes of a row access. A masked element is never touched and reads
+// as `fill` (the identity of the reduction that follows); stores skip it.
+//   kNone    every vector is inside the row: straight-line 16-byte accesses
+//   kVec     row length and base allow 16-byte vectors and the length is a
+//            multiple of 4: a vector is wholly inside or wholly outside
+//   kElem    16-byte aligned rows of any length: whole vectors load as one,
+//            the one vector that straddles the end element by element
+//   kScalar  rows not 16-byte aligned: element accesses only
+// Keeping kNone / kVec free of element branches lets the compiler issue all
+// loads of a lane back to back and wait for them one vector at a time.
+enum Mask : int { kNone = 0, kVec = 1, kElem = 2, kScalar = 3 };
+
+template <int M, bool NT>
+__device__ __forceinline__ f32x4 load4m(const float* row, int j0, int L, float fill) {
+    if constexpr (M == kNone) {
+        return ld4<NT>(row + j0);
+    } else if constexpr (M == kVec) {
+        return j0 < L ? ld4<NT>(row + j0) : f32x4{fill, fill, fill, fill};
+    } else {
+        if (M == kElem && j0 + 3 < L) return ld4<NT>(row + j0);
+        f32x4 v = {fill, fill, fill, fill};
+        if (j0 + 0 < L) v.x = ld1<NT>(row + j0 + 0);
+        if (j0 + 1 < L) v.y = ld1<NT>(row + j0 + 1);
+        if (j0 + 2 < L) v.z = ld1<NT>(row + j0 + 2);
+        if (j0 + 3 < L) v.w = ld1<NT>(row + j0 + 3);
+        return v;
     }
-    if (j0 + 0 < L) st1<NT>(row + j0 + 0, v.x);
-    if (j0 + 1 < L) st1<NT>(row + j0 + 1, v.y);
-    if (j0 + 2 < L) st1<NT>(row + j0 + 2, v.z);
-    if (j0 + 3 < L) st1<NT>(row + j0 + 3, v.w);
 }
+
+template <int M, bool NT>
+__device__ __forceinline__ void store4m(float* row, int j0, int L, f32x4 v) {
+    if constexpr (M == kNone) {
+        st4<NT>(row + j0, v);
+    } else if constexpr (M == kVec) {
+        if (j0 < L) st4<NT>(row + j0, v);
+    } else {
+        if (M == kElem && j0 + 3 < L) {
+            st4<NT>(row + j0, v);
+            return;
+        }
+        if (j0 + 0 < L) st1<NT>(row + j0 + 0, v.x);
+        if (j0 + 1 < L) st1<NT>(row + j0 + 1, v.y);
+        if (j0 + 2 < L) st1<NT>(row + j0 + 2, v.z);
+        if (j0 + 3 < L) st1<NT>(row + j0 + 3, v.w);
+    }
+}
+
+// Mask mode for the tail step of a loop whose full steps run unmasked.
+template <bool VEC>
+constexpr int tail_mask() { return VEC ? kElem : kScalar; }
+template <bool VEC>
+constexpr int body_mask() { return VEC ? kNone : kScalar; }
 
 // ------------------------------------------------------------------ bf16
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }

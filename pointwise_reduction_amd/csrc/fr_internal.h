@@ -54,6 +54,6 @@ hipError_t launch_layernorm(const fr_plan& p, const LayerNormArgs& a, hipStream_
 
 // Planner (host only, no HIP calls).
 int make_plan(int op, int64_t rows, int64_t cols, int dtype, int num_cus, int has_lengths, uint64_t ws_bytes,
-              int aligned16, int forced_form, fr_plan* plan);
+              int aligned16, int forced_form, const fr_plan* override_plan, fr_plan* plan);
 
 }  // namespace fr

@@ -19,12 +19,14 @@
 namespace fr {
 
 // Load the 8 bf16 at j0..j0+7 of a row of length L as packed words; element
-// j >= L is never touched and reads as +0. VEC kernels run only when L is a
-// multiple of 8 (and rows are 16-byte aligned), so a vector is either wholly
-// inside the row or wholly outside it.
-template <bool VEC, bool NT>
-__device__ __forceinline__ u32x4 load8_masked(const uint16_t* row, int j0, int L) {
-    if constexpr (VEC) return j0 < L ? ld4u<NT>(row + j0) : u32x4{0u, 0u, 0u, 0u};
+// j >= L is never touched and reads as +0. Mask modes as for fp32 rows:
+// kNone (every vector inside the row), kVec (16-byte aligned rows whose
+// length is a multiple of 8: a vector is wholly inside or outside), kScalar
+// (element accesses).
+template <int M, bool NT>
+__device__ __forceinline__ u32x4 load8m(const uint16_t* row, int j0, int L) {
+    if constexpr (M == kNone) return ld4u<NT>(row + j0);
+    else if constexpr (M == kVec) return j0 < L ? ld4u<NT>(row + j0) : u32x4{0u, 0u, 0u, 0u};
     uint32_t w[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int c = 0; c < 8; ++c)
@@ -32,9 +34,12 @@ __device__ __forceinline__ u32x4 load8_masked(const uint16_t* row, int j0, int L
     return u32x4{w[0], w[1], w[2], w[3]};
 }
 
-template <bool VEC, bool NT>
-__device__ __forceinline__ void store8_masked(uint16_t* row, int j0, int L, u32x4 v) {
-    if constexpr (VEC) {
+template <int M, bool NT>
+__device__ __forceinline__ void store8m(uint16_t* row, int j0, int L, u32x4 v) {
+    if constexpr (M == kNone) {
+        st4u<NT>(row + j0, v);
+        return;
+    } else if constexpr (M == kVec) {
         if (j0 < L) st4u<NT>(row + j0, v);
         return;
     }
@@ -49,13 +54,13 @@ __device__ __forceinline__ uint32_t word(u32x4 v, int i) { return i == 0 ? v.x :
 // y = (x - mu) * rstd * gamma + beta for the 8 values of one vector, packed
 // back to bf16 with round-to-nearest-even. When x == mu the product is an
 // exact 0 and y is exactly beta.
-template <bool VEC>
+template <int M>
 __device__ __forceinline__ u32x4 normalize8(u32x4 xv, int j0, int L, const uint16_t* __restrict__ gamma,
                                             const uint16_t* __restrict__ beta, float mu, float rstd) {
     u32x4 gv = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // 1.0 in bf16
     u32x4 bv = {0u, 0u, 0u, 0u};
-    if (gamma) gv = load8_masked<VEC, false>(gamma, j0, L);
-    if (beta) bv = load8_masked<VEC, false>(beta, j0, L);
+    if (gamma) gv = load8m<M, false>(gamma, j0, L);
+    if (beta) bv = load8m<M, false>(beta, j0, L);
     uint32_t o[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -68,10 +73,15 @@ __device__ __forceinline__ u32x4 normalize8(u32x4 xv, int j0, int L, const uint1
 }
 
 // ------------------------------------------------------------------ persistent
-template <int T, int NV, bool VEC>
-__global__ __launch_bounds__(T) void fr_per_layernorm_bf16(const uint16_t* x, const uint16_t* __restrict__ gamma,
-                                                           const uint16_t* __restrict__ beta, uint16_t* y, int rows,
-                                                           int cols, int64_t x_rs, int64_t y_rs, float eps) {
+// One workgroup of T threads per row, NV vectors of 8 bf16 per lane (row
+// capacity 8 * T * NV); M is the masking mode (kNone when the row fills the
+// capacity exactly). OCC > 1 would ask the compiler for at least OCC waves
+// per SIMD; the compiled variants use 1 (no request).
+template <int T, int NV, int M, int OCC>
+__global__ __launch_bounds__(T, OCC) void fr_per_layernorm_bf16(const uint16_t* x, const uint16_t* __restrict__ gamma,
+                                                                const uint16_t* __restrict__ beta, uint16_t* y,
+                                                                int rows, int cols, int64_t x_rs, int64_t y_rs,
+                                                                float eps) {
     __shared__ float sl_s[T / kWave];
     __shared__ float sl_q[T / kWave];
     const int tid = threadIdx.x;
@@ -80,7 +90,7 @@ __global__ __launch_bounds__(T) void fr_per_layernorm_bf16(const uint16_t* x, co
         const uint16_t* xr = x + (int64_t)r * x_rs;
         u32x4 v[NV];
 #pragma unroll
-        for (int k = 0; k < NV; ++k) v[k] = load8_masked<VEC, true>(xr, (k * T + tid) * 8, cols);
+        for (int k = 0; k < NV; ++k) v[k] = load8m<M, true>(xr, (k * T + tid) * 8, cols);
         // pass 1 over registers: the sum (masked elements read as +0)
         float s = 0.f;
 #pragma unroll
@@ -97,8 +107,8 @@ __global__ __launch_bounds__(T) void fr_per_layernorm_bf16(const uint16_t* x, co
             const int j0 = (k * T + tid) * 8;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float dl = j0 + 2 * i < cols ? bf16_lo(word(v[k], i)) - mu : 0.f;
-                const float dh = j0 + 2 * i + 1 < cols ? bf16_hi(word(v[k], i)) - mu : 0.f;
+                const float dl = (M == kNone || j0 + 2 * i < cols) ? bf16_lo(word(v[k], i)) - mu : 0.f;
+                const float dh = (M == kNone || j0 + 2 * i + 1 < cols) ? bf16_hi(word(v[k], i)) - mu : 0.f;
                 q += dl * dl + dh * dh;
             }
         }
@@ -109,7 +119,8 @@ __global__ __launch_bounds__(T) void fr_per_layernorm_bf16(const uint16_t* x, co
 #pragma unroll
         for (int k = 0; k < NV; ++k) {
             const int j0 = (k * T + tid) * 8;
-            if (j0 < cols) store8_masked<VEC, true>(yr, j0, cols, normalize8<VEC>(v[k], j0, cols, gamma, beta, mu, rstd));
+            if (M == kNone || j0 < cols)
+                store8m<M, true>(yr, j0, cols, normalize8<M>(v[k], j0, cols, gamma, beta, mu, rstd));
         }
         __syncthreads();  // slots are rewritten by the next row
     }
@@ -141,37 +152,54 @@ __device__ __forceinline__ Stat stat8(u32x4 v, int j0, int L) {
     return Stat{n, mean, m2};
 }
 
+template <int M, int T, int U>
+__device__ __forceinline__ Stat welford_step(const uint16_t* xr, int base, int cols, Stat st) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = load8m<M, false>(xr, base + (u * T + (int)threadIdx.x) * 8, cols);
+#pragma unroll
+    for (int u = 0; u < U; ++u) st = stat_combine(st, stat8(v[u], base + (u * T + (int)threadIdx.x) * 8, cols));
+    return st;
+}
+
+template <int M, int T, int U>
+__device__ __forceinline__ void normalize_step(const uint16_t* xr, uint16_t* yr, int base, int cols,
+                                               const uint16_t* __restrict__ gamma,
+                                               const uint16_t* __restrict__ beta, float mu, float rstd) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = load8m<M, true>(xr, base + (u * T + (int)threadIdx.x) * 8, cols);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int j0 = base + (u * T + (int)threadIdx.x) * 8;
+        if (M == kNone || j0 < cols)
+            store8m<M, true>(yr, j0, cols, normalize8<M>(v[u], j0, cols, gamma, beta, mu, rstd));
+    }
+}
+
+// Steps wholly inside the row run unmasked; only the last step is masked.
 template <int T, int U, bool VEC>
 __global__ __launch_bounds__(T) void fr_red_layernorm_bf16(const uint16_t* x, const uint16_t* __restrict__ gamma,
                                                            const uint16_t* __restrict__ beta, uint16_t* y, int rows,
                                                            int cols, int64_t x_rs, int64_t y_rs, float eps) {
+    constexpr int STEP = T * 8 * U;
+    constexpr int BODY = VEC ? kNone : kScalar;
+    constexpr int TAIL = VEC ? kVec : kScalar;
     __shared__ Stat sl[T / kWave];
-    const int tid = threadIdx.x;
+    const int full = cols - cols % STEP;
     for (int r = blockIdx.x; r < rows; r += gridDim.x) {
         const uint16_t* xr = x + (int64_t)r * x_rs;
         Stat st{0.f, 0.f, 0.f};
-        for (int base = 0; base < cols; base += T * 8 * U) {
-            u32x4 v[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) v[u] = load8_masked<VEC, false>(xr, base + (u * T + tid) * 8, cols);
-#pragma unroll
-            for (int u = 0; u < U; ++u) st = stat_combine(st, stat8(v[u], base + (u * T + tid) * 8, cols));
-        }
+        int base = 0;
+        for (; base < full; base += STEP) st = welford_step<BODY, T, U>(xr, base, cols, st);
+        if (base < cols) st = welford_step<TAIL, T, U>(xr, base, cols, st);
         st = group_reduce<kWave>(st, OpStat());
         st = block_fold(st, sl, T / kWave, OpStat());
         const float mu = st.mu;
         const float rstd = 1.0f / sqrtf(st.m2 / (float)cols + eps);
         uint16_t* yr = y + (int64_t)r * y_rs;
-        for (int base = 0; base < cols; base += T * 8 * U) {
-            u32x4 v[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) v[u] = load8_masked<VEC, true>(xr, base + (u * T + tid) * 8, cols);
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int j0 = base + (u * T + tid) * 8;
-                if (j0 < cols) store8_masked<VEC, true>(yr, j0, cols, normalize8<VEC>(v[u], j0, cols, gamma, beta, mu, rstd));
-            }
-        }
+        for (base = 0; base < full; base += STEP) normalize_step<BODY, T, U>(xr, yr, base, cols, gamma, beta, mu, rstd);
+        if (base < cols) normalize_step<TAIL, T, U>(xr, yr, base, cols, gamma, beta, mu, rstd);
         __syncthreads();  // slots are rewritten by the next row
     }
 }
@@ -183,27 +211,42 @@ using LnFn = void (*)(const uint16_t*, const uint16_t*, const uint16_t*, uint16_
                       float);
 
 // Persistent configurations: 16-byte vector kernels hold up to 8 vectors
-// (64 bf16) per lane without spilling; element-wise kernels (unaligned rows)
-// up to 4.
-template <bool VEC>
-LnFn pick_per(int threads, int nv) {
+// (64 bf16) per lane, or 4 with 1024 threads, without spilling; element-wise
+// kernels (unaligned rows) up to 4. Asking for more waves per SIMD than the
+// compiler's own choice (occ > 1) makes these kernels spill, so no such
+// variant is compiled.
+template <int M>
+LnFn pick_per_m(int threads, int nv) {
+    constexpr bool VEC = M != kScalar;
     if (threads == 64) {
         switch (nv) {
-            case 1: return fr_per_layernorm_bf16<64, 1, VEC>;
-            case 2: return fr_per_layernorm_bf16<64, 2, VEC>;
-            case 4: return fr_per_layernorm_bf16<64, 4, VEC>;
-            case 8: return VEC ? fr_per_layernorm_bf16<64, 8, VEC> : nullptr;
+            case 1: return fr_per_layernorm_bf16<64, 1, M, 1>;
+            case 2: return fr_per_layernorm_bf16<64, 2, M, 1>;
+            case 4: return fr_per_layernorm_bf16<64, 4, M, 1>;
         }
+        if constexpr (VEC)
+            if (nv == 8) return fr_per_layernorm_bf16<64, 8, M, 1>;
         return nullptr;
     }
     if (nv == (VEC ? 8 : 4)) {
         switch (threads) {
-            case 128: return fr_per_layernorm_bf16<128, VEC ? 8 : 4, VEC>;
-            case 256: return fr_per_layernorm_bf16<256, VEC ? 8 : 4, VEC>;
-            case 512: return fr_per_layernorm_bf16<512, VEC ? 8 : 4, VEC>;
+            case 128: return fr_per_layernorm_bf16<128, VEC ? 8 : 4, M, 1>;
+            case 256: return fr_per_layernorm_bf16<256, VEC ? 8 : 4, M, 1>;
+            case 512: return fr_per_layernorm_bf16<512, VEC ? 8 : 4, M, 1>;
         }
     }
+    if constexpr (VEC)
+        if (threads == 1024 && nv == 4) return fr_per_layernorm_bf16<1024, 4, M, 1>;
     return nullptr;
+}
+
+LnFn pick_per(int mask, int threads, int nv, int occ) {
+    if (occ > 1) return nullptr;
+    switch (mask) {
+        case kNone: return pick_per_m<kNone>(threads, nv);
+        case kVec: return pick_per_m<kVec>(threads, nv);
+        default: return pick_per_m<kScalar>(threads, nv);
+    }
 }
 
 template <bool VEC>
@@ -219,9 +262,13 @@ LnFn pick_red(int threads, int u) {
 hipError_t launch_layernorm(const fr_plan& p, const LayerNormArgs& a, hipStream_t s) {
     const bool vec = p.vec16 != 0;
     LnFn f = nullptr;
-    if (p.form == FR_FORM_PER) f = vec ? pick_per<true>(p.threads, p.vec) : pick_per<false>(p.threads, p.vec);
-    else if (p.form == FR_FORM_RED) f = vec ? pick_red<true>(p.threads, p.vec) : pick_red<false>(p.threads, p.vec);
-    if (!f) return hipErrorInvalidValue;
+    if (p.form == FR_FORM_PER) {
+        const int mask = !vec ? kScalar : (a.cols == 8 * p.threads * p.vec ? kNone : kVec);
+        f = pick_per(mask, p.threads, p.vec, p.occupancy);
+    }
+    else if (p.form == FR_FORM_RED)
+        f = vec ? pick_red<true>(p.threads, p.vec) : pick_red<false>(p.threads, p.vec);
+    if (!f) return hipErrorInvalidDeviceFunction;
     hipLaunchKernelGGL(f, dim3((unsigned)p.grid), dim3(p.threads), 0, s, a.x, a.gamma, a.beta, a.y, a.rows, a.cols,
                        a.x_rs, a.y_rs, a.eps);
     return hipGetLastError();

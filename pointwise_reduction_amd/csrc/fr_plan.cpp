@@ -5,8 +5,11 @@
 // Shapes": 9.4 picks the form from the reduction length (persistent when the
 // row fits, looped when it does not, split when there are too few outputs to
 // fill the device); 9.6 makes block sizes and warp counts launch parameters
-// whose grid follows from them; 10.3 decides against the upper bound of a
-// runtime length (here `cols`, the row capacity of a ragged input).
+// whose grid follows from them, chosen by measuring candidates (Algorithm
+// 9.1, run offline here: the constants below are the measured winners on
+// MI355X, and fr_tune_override lets a tuner time any other candidate); 10.3
+// decides against the upper bound of a runtime length (here `cols`, the row
+// capacity of a ragged input).
 //
 // The MI355X thresholds differ from the pages' Triton/H100 rule (persistent
 // up to 1024 elements): a 64-lane wave holding 8 x 16-byte vectors per lane
@@ -20,13 +23,17 @@ namespace fr {
 
 namespace {
 
-constexpr int64_t kMaxGrid = 1 << 20;    // grid-stride loops cover the rest
-constexpr int kPerMaxF32 = 2048;         // 64 lanes x 8 vectors x 4 floats
-constexpr int kSumSplitRows = 512;       // fewer rows than 2 per CU: split
-constexpr int kSoftmaxSplitRows = 1024;  // fewer rows than 4 per CU: split
-constexpr int kSplitTargetWgs = 2048;    // 8 workgroups per CU on 256 CUs
-constexpr int kSumSplitThreads = 256, kSumSplitU = 4;     // 4096 floats per step
-constexpr int kSoftmaxSplitThreads = 256, kSoftmaxSplitNV = 8;  // 8192-float chunks
+constexpr int64_t kMaxGrid = 1 << 20;      // grid-stride loops cover the rest
+constexpr int kPerMaxF32 = 2048;           // 64 lanes x 8 vectors x 4 floats
+constexpr int kSumSplitRows = 512;         // fewer rows than 2 per CU: split
+constexpr int kSoftmaxSplitRows = 1024;    // fewer rows than 4 per CU: split
+constexpr int kSplitTargetWgs = 2048;      // 8 workgroups per CU on 256 CUs
+constexpr int kSumSplitThreads = 256, kSumSplitU = 4;            // 4096 floats per step
+constexpr int kSoftmaxSplitThreads = 256, kSoftmaxSplitNV = 8;   // 8192-float chunks
+// Two rows per wave pay off while the grid would otherwise launch more than
+// ~2 waves per SIMD of one-row waves (measured: 4096 x 1024 fp32 runs 15%
+// faster, 16384 x 1024 3% slower).
+constexpr int64_t kTwoRowsPerWaveMaxRows = 8192;
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
@@ -36,6 +43,8 @@ int pow2_ceil(int v) {
     return p;
 }
 
+bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+
 void clear(fr_plan* p, int op) {
     *p = fr_plan{};
     p->op = op;
@@ -43,51 +52,90 @@ void clear(fr_plan* p, int op) {
     p->rows_per_wg = 1;
 }
 
-// Persistent geometry for fp32 rows of `cols` <= 2048 elements: the smallest
-// lane group (8..64 lanes) whose 16-byte vectors cover the row with at most
-// 8 vectors per lane.
-void per_f32(fr_plan* p, int64_t rows, int64_t cols) {
+// Launch knobs before the grid and workspace follow from the shape.
+struct Knobs {
+    int form = 0;
+    int threads = 256;
+    int seg = 64;
+    int vec = 1;
+    int rpw = 1;     // rows per lane group (persistent fp32)
+    int chunk = 0;   // elements per split chunk (sum split)
+    int occ = 0;     // minimum waves per SIMD (persistent LayerNorm)
+};
+
+// Persistent fp32 geometry: the smallest lane group (8..64 lanes) whose
+// 16-byte vectors cover the row with at most 8 vectors per lane.
+Knobs per_f32_knobs(int64_t rows, int64_t cols, bool two_rows_ok) {
+    Knobs k;
+    k.form = FR_FORM_PER;
     const int q = (int)cdiv(cols, 4);
-    const int seg = q <= 8 ? 8 : (q <= 16 ? 16 : (q <= 32 ? 32 : 64));
-    int nv = (int)cdiv(q, seg);
-    nv = nv <= 1 ? 1 : pow2_ceil(nv);
-    p->form = FR_FORM_PER;
-    p->threads = 256;
-    p->seg = seg;
-    p->vec = nv;
-    p->rows_per_wg = 256 / seg;
-    p->grid = min64(cdiv(rows, p->rows_per_wg), kMaxGrid);
+    k.seg = q <= 8 ? 8 : (q <= 16 ? 16 : (q <= 32 ? 32 : 64));
+    int nv = (int)cdiv(q, k.seg);
+    k.vec = nv <= 1 ? 1 : pow2_ceil(nv);
+    k.rpw = (two_rows_ok && k.seg == 64 && k.vec <= 4 && rows <= kTwoRowsPerWaveMaxRows) ? 2 : 1;
+    return k;
 }
 
-void sum_split(fr_plan* p, int64_t rows, int64_t cols) {
-    const int64_t step = (int64_t)kSumSplitThreads * 4 * kSumSplitU;
+int64_t sum_split_count(int64_t rows, int64_t cols, int64_t step) {
     int64_t s = min64(cdiv(kSplitTargetWgs, rows), cdiv(cols, step));
-    if (s < 1) s = 1;
-    const int64_t chunk = cdiv(cdiv(cols, s), step) * step;
-    s = cdiv(cols, chunk);
-    p->form = FR_FORM_SPLIT;
-    p->threads = kSumSplitThreads;
-    p->vec = kSumSplitU;
-    p->splits = (int)s;
-    p->chunk = (int)chunk;
-    p->grid = rows * s;
-    // finishing pass: a persistent reduction over rows of s partials
-    const int seg = s <= 32 ? 8 : (s <= 64 ? 16 : (s <= 128 ? 32 : 64));
-    p->grid2 = cdiv(rows, 256 / seg);
-    p->ws_bytes = (uint64_t)(rows * s * 4);
+    return s < 1 ? 1 : s;
 }
 
-void softmax_split(fr_plan* p, int64_t rows, int64_t cols) {
-    const int64_t chunk = (int64_t)kSoftmaxSplitThreads * 4 * kSoftmaxSplitNV;
-    const int64_t s = cdiv(cols, chunk);
-    p->form = FR_FORM_SPLIT;
-    p->threads = kSoftmaxSplitThreads;
-    p->vec = kSoftmaxSplitNV;
-    p->splits = (int)s;
-    p->chunk = (int)chunk;
-    p->grid = rows * s;
-    p->grid2 = rows * s;
-    p->ws_bytes = (uint64_t)(rows * s * (int64_t)sizeof(SoftmaxPartial));
+// Turn knobs into a complete plan for this shape: grid, splits, workspace.
+// Returns FR_E_ARG when the knobs cannot serve the shape.
+int finalize_plan(int op, int64_t rows, int64_t cols, const Knobs& k, fr_plan* p) {
+    p->form = k.form;
+    p->threads = k.threads;
+    p->vec = k.vec;
+    p->occupancy = k.occ;
+    if (k.threads < 64 || k.threads > 1024 || k.threads % 64 || k.vec < 1 || k.vec > 16) return FR_E_ARG;
+    const bool f32 = op != FR_OP_LAYERNORM;
+    if (k.form == FR_FORM_PER) {
+        if (f32) {
+            if (k.threads != 256 || !is_pow2(k.seg) || k.seg < 8 || k.seg > 64 || k.rpw < 1 || k.rpw > 2)
+                return FR_E_ARG;
+            if (cols > (int64_t)4 * k.seg * k.vec) return FR_E_ARG;
+            p->seg = k.seg;
+            p->rows_per_wg = 256 / k.seg * k.rpw;
+            p->grid = min64(cdiv(rows, p->rows_per_wg), kMaxGrid);
+        } else {
+            if (cols > (int64_t)k.threads * 8 * k.vec) return FR_E_ARG;
+            p->grid = min64(rows, kMaxGrid);
+        }
+        return FR_OK;
+    }
+    if (k.form == FR_FORM_RED) {
+        p->grid = min64(rows, kMaxGrid);
+        return FR_OK;
+    }
+    if (k.form == FR_FORM_SPLIT) {
+        if (!f32 || rows < 1 || cols < 1) return FR_E_ARG;
+        if (op == FR_OP_SOFTMAX) {
+            const int64_t chunk = (int64_t)k.threads * 4 * k.vec;
+            const int64_t s = cdiv(cols, chunk);
+            p->splits = (int)s;
+            p->chunk = (int)chunk;
+            p->grid = rows * s;
+            p->grid2 = rows * s;
+            p->ws_bytes = (uint64_t)(rows * s * (int64_t)sizeof(SoftmaxPartial));
+        } else {
+            const int64_t step = (int64_t)k.threads * 4 * k.vec;
+            int64_t chunk = k.chunk;
+            if (chunk <= 0) chunk = cdiv(cdiv(cols, sum_split_count(rows, cols, step)), step) * step;
+            if (chunk % step) return FR_E_ARG;
+            const int64_t s = cdiv(cols, chunk);
+            if (s > kPerMaxF32) return FR_E_ARG;  // the finishing pass is one persistent row
+            p->splits = (int)s;
+            p->chunk = (int)chunk;
+            p->grid = rows * s;
+            const int seg = s <= 32 ? 8 : (s <= 64 ? 16 : (s <= 128 ? 32 : 64));
+            p->grid2 = cdiv(rows, 256 / seg);
+            p->ws_bytes = (uint64_t)(rows * s * 4);
+        }
+        if (p->grid * p->threads >= (int64_t(1) << 32)) return FR_E_ARG;
+        return FR_OK;
+    }
+    return FR_E_ARG;
 }
 
 }  // namespace
@@ -96,20 +144,26 @@ uint64_t sum_split_ws(int64_t rows, int64_t cols) {
     if (rows <= 0 || cols <= 0) return 0;
     fr_plan p;
     clear(&p, FR_OP_SUMSQ);
-    sum_split(&p, rows, cols);
-    return p.ws_bytes;
+    Knobs k;
+    k.form = FR_FORM_SPLIT;
+    k.threads = kSumSplitThreads;
+    k.vec = kSumSplitU;
+    return finalize_plan(FR_OP_SUMSQ, rows, cols, k, &p) == FR_OK ? p.ws_bytes : 0;
 }
 
 uint64_t softmax_split_ws(int64_t rows, int64_t cols) {
     if (rows <= 0 || cols <= 0) return 0;
     fr_plan p;
     clear(&p, FR_OP_SOFTMAX);
-    softmax_split(&p, rows, cols);
-    return p.ws_bytes;
+    Knobs k;
+    k.form = FR_FORM_SPLIT;
+    k.threads = kSoftmaxSplitThreads;
+    k.vec = kSoftmaxSplitNV;
+    return finalize_plan(FR_OP_SOFTMAX, rows, cols, k, &p) == FR_OK ? p.ws_bytes : 0;
 }
 
 int make_plan(int op, int64_t rows, int64_t cols, int dtype, int num_cus, int has_lengths, uint64_t ws_bytes,
-              int aligned16, int forced, fr_plan* p) {
+              int aligned16, int forced, const fr_plan* override_plan, fr_plan* p) {
     (void)has_lengths;
     (void)num_cus;  // the thresholds are fixed per library build so that
                     // workspace sizes and results do not depend on the device
@@ -118,55 +172,53 @@ int make_plan(int op, int64_t rows, int64_t cols, int dtype, int num_cus, int ha
     if (forced < FR_FORM_AUTO || forced > FR_FORM_SPLIT) return FR_E_ARG;
     clear(p, op);
     p->vec16 = aligned16 ? 1 : 0;
+    Knobs k;
     switch (op) {
         case FR_OP_SUM_RELU_ADD:
         case FR_OP_SUMSQ: {
             if (dtype != FR_F32) return FR_E_DTYPE;
             const bool per_ok = cols <= kPerMaxF32;
-            const uint64_t need = sum_split_ws(rows, cols);
-            const bool split_ok = cols > 0 && rows > 0 && ws_bytes >= need;
+            const bool split_ok = cols > 0 && rows > 0 && ws_bytes >= sum_split_ws(rows, cols);
             int form = forced;
             if (form == FR_FORM_AUTO)
-                form = per_ok ? FR_FORM_PER
-                              : (split_ok && rows < kSumSplitRows ? FR_FORM_SPLIT : FR_FORM_RED);
+                form = per_ok ? FR_FORM_PER : (split_ok && rows < kSumSplitRows ? FR_FORM_SPLIT : FR_FORM_RED);
             if (form == FR_FORM_PER) {
                 if (!per_ok) return FR_E_ARG;
-                per_f32(p, rows, cols);
+                k = per_f32_knobs(rows, cols, false);
             } else if (form == FR_FORM_RED) {
-                p->form = FR_FORM_RED;
-                p->threads = 256;
-                p->vec = 4;
-                p->grid = min64(rows, kMaxGrid);
+                k.form = FR_FORM_RED;
+                k.threads = 256;
+                k.vec = 4;
             } else {
                 if (!split_ok) return FR_E_ARG;
-                sum_split(p, rows, cols);
-                if (p->grid * p->threads >= (int64_t(1) << 32)) return FR_E_ARG;
+                k.form = FR_FORM_SPLIT;
+                k.threads = kSumSplitThreads;
+                k.vec = kSumSplitU;
             }
-            return FR_OK;
+            break;
         }
         case FR_OP_SOFTMAX: {
             if (dtype != FR_F32) return FR_E_DTYPE;
             const bool per_ok = cols <= kPerMaxF32;
-            const uint64_t need = softmax_split_ws(rows, cols);
-            const bool split_ok = cols > 0 && rows > 0 && ws_bytes >= need;
+            const bool split_ok = cols > 0 && rows > 0 && ws_bytes >= softmax_split_ws(rows, cols);
             int form = forced;
             if (form == FR_FORM_AUTO)
                 form = per_ok ? FR_FORM_PER
                               : (split_ok && rows < kSoftmaxSplitRows ? FR_FORM_SPLIT : FR_FORM_RED);
             if (form == FR_FORM_PER) {
                 if (!per_ok) return FR_E_ARG;
-                per_f32(p, rows, cols);
+                k = per_f32_knobs(rows, cols, true);
             } else if (form == FR_FORM_RED) {
-                p->form = FR_FORM_RED;
-                p->threads = cols > 16384 ? 512 : 256;
-                p->vec = cols > 16384 ? 2 : 4;
-                p->grid = min64(rows, kMaxGrid);
+                k.form = FR_FORM_RED;
+                k.threads = cols > 16384 ? 512 : 256;
+                k.vec = cols > 16384 ? 2 : 4;
             } else {
                 if (!split_ok) return FR_E_ARG;
-                softmax_split(p, rows, cols);
-                if (p->grid * p->threads >= (int64_t(1) << 32)) return FR_E_ARG;
+                k.form = FR_FORM_SPLIT;
+                k.threads = kSoftmaxSplitThreads;
+                k.vec = kSoftmaxSplitNV;
             }
-            return FR_OK;
+            break;
         }
         case FR_OP_LAYERNORM: {
             if (dtype != FR_BF16) return FR_E_DTYPE;
@@ -185,21 +237,38 @@ int make_plan(int op, int64_t rows, int64_t cols, int dtype, int num_cus, int ha
                     t = 64;
                     nv = pow2_ceil((int)cdiv(q, 64));
                 }
-                p->form = FR_FORM_PER;
-                p->threads = t;
-                p->vec = nv;
+                k.form = FR_FORM_PER;
+                k.threads = t;
+                k.vec = nv;
             } else if (form == FR_FORM_RED) {
-                p->form = FR_FORM_RED;
-                p->threads = 512;
-                p->vec = 2;
+                k.form = FR_FORM_RED;
+                k.threads = 512;
+                k.vec = 2;
             } else {
                 return FR_E_ARG;  // rows of LayerNorm are never split
             }
-            p->grid = min64(rows, kMaxGrid);
-            return FR_OK;
+            break;
         }
+        default:
+            return FR_E_ARG;
     }
-    return FR_E_ARG;
+    if (override_plan) {
+        // a tuner's candidate: form and launch knobs from the override,
+        // grid / splits / workspace recomputed for this shape
+        k.form = override_plan->form;
+        k.threads = override_plan->threads;
+        k.seg = override_plan->seg;
+        k.vec = override_plan->vec;
+        k.rpw = (override_plan->seg > 0 && override_plan->form == FR_FORM_PER && op != FR_OP_LAYERNORM)
+                    ? override_plan->rows_per_wg / (256 / override_plan->seg)
+                    : 1;
+        k.chunk = override_plan->chunk;
+        k.occ = override_plan->occupancy;
+    }
+    const int st = finalize_plan(op, rows, cols, k, p);
+    if (st != FR_OK) return st;
+    if (p->form == FR_FORM_SPLIT && ws_bytes < p->ws_bytes) return override_plan ? FR_E_WORKSPACE : FR_E_ARG;
+    return FR_OK;
 }
 
 }  // namespace fr

@@ -37,55 +37,94 @@ __device__ __forceinline__ float comp(f32x4 v, int c) { return c == 0 ? v.x : (c
 // Does x match the row maximum m (a NaN maximum matches the first NaN)?
 __device__ __forceinline__ bool is_max(float x, float m) { return x == m || (m != m && x != x); }
 
+__device__ __forceinline__ float max4(float m, f32x4 v) { return fmax_nan(fmax_nan(m, fmax_nan(v.x, v.y)), fmax_nan(v.z, v.w)); }
+
+// e^(v - m) for the elements j0..j0+3 below L, 0 elsewhere.
+__device__ __forceinline__ f32x4 exp4_masked(f32x4 v, float m, int j0, int L) {
+    return f32x4{j0 + 0 < L ? exp_fast(v.x - m) : 0.f, j0 + 1 < L ? exp_fast(v.y - m) : 0.f,
+                 j0 + 2 < L ? exp_fast(v.z - m) : 0.f, j0 + 3 < L ? exp_fast(v.w - m) : 0.f};
+}
+
+__device__ __forceinline__ f32x4 exp4(f32x4 v, float m) {
+    return f32x4{exp_fast(v.x - m), exp_fast(v.y - m), exp_fast(v.z - m), exp_fast(v.w - m)};
+}
+
 // ------------------------------------------------------------------ persistent
-template <int SEG, int NV, bool VEC>
+// SEG lanes per row and NV 16-byte vectors per lane (row capacity 4*SEG*NV);
+// each lane group takes RPW adjacent rows and issues all their loads before
+// any arithmetic, so RPW * NV loads per lane are in flight at once. A
+// 256-thread workgroup serves 256 / SEG * RPW rows per step of a grid-stride
+// loop over row groups. M is the masking mode (kNone: dense rows that fill
+// the capacity exactly).
+template <int SEG, int NV, int M, int RPW>
 __global__ __launch_bounds__(256) void fr_per_softmax_f32(const float* x, float* y, int rows, int cols,
                                                           int64_t x_rs, int64_t y_rs,
                                                           const int32_t* __restrict__ lengths,
                                                           int32_t* __restrict__ argmax) {
-    constexpr int RPB = 256 / SEG;
+    constexpr int RPB = 256 / SEG * RPW;
     const int g = threadIdx.x / SEG;
     const int l = threadIdx.x % SEG;
     const int ngroups = (rows + RPB - 1) / RPB;
     for (int grp = blockIdx.x; grp < ngroups; grp += gridDim.x) {
-        const int r = grp * RPB + g;
-        const bool live = r < rows;
-        const int L = live ? row_len(lengths, r, cols) : 0;
-        const float* xr = x + (int64_t)(live ? r : 0) * x_rs;
-        f32x4 v[NV];
+        f32x4 v[RPW][NV];
+        int L[RPW];
 #pragma unroll
-        for (int k = 0; k < NV; ++k) v[k] = load4_masked<VEC, true>(xr, (k * SEG + l) * 4, L, -INFINITY);
-        float m = -INFINITY;
+        for (int q = 0; q < RPW; ++q) {
+            const int r = grp * RPB + g * RPW + q;
+            const bool live = r < rows;
+            // kNone (dense rows, no lengths): a row past the end re-reads the
+            // last row, which is in bounds, and stores nothing - so the loads
+            // carry no branch
+            const int rl = live ? r : (M == kNone ? rows - 1 : 0);
+            if constexpr (M == kNone) L[q] = live ? cols : 0;
+            else L[q] = live ? row_len(lengths, r, cols) : 0;
+            const float* xr = x + (int64_t)rl * x_rs;
 #pragma unroll
-        for (int k = 0; k < NV; ++k) m = fmax_nan(fmax_nan(m, fmax_nan(v[k].x, v[k].y)), fmax_nan(v[k].z, v[k].w));
-        m = group_reduce<SEG>(m, OpMax());
-        if (argmax) {
-            int cand = INT_MAX;
+            for (int k = 0; k < NV; ++k) {
+                const int j0 = (k * SEG + l) * 4;
+                if constexpr (M == kNone) v[q][k] = ld4<true>(xr + j0);
+                else v[q][k] = load4m<M, true>(xr, j0, L[q], -INFINITY);
+            }
+        }
 #pragma unroll
-            for (int k = NV - 1; k >= 0; --k)
+        for (int q = 0; q < RPW; ++q) {
+            const int r = grp * RPB + g * RPW + q;
+            const bool live = r < rows;
+            float m = -INFINITY;
 #pragma unroll
-                for (int c = 3; c >= 0; --c) {
-                    const int j = (k * SEG + l) * 4 + c;
-                    if (j < L && is_max(comp(v[k], c), m)) cand = j;
+            for (int k = 0; k < NV; ++k) m = max4(m, v[q][k]);
+            m = group_reduce<SEG>(m, OpMax());
+            if (argmax) {
+                int cand = INT_MAX;
+#pragma unroll
+                for (int k = NV - 1; k >= 0; --k)
+#pragma unroll
+                    for (int c = 3; c >= 0; --c) {
+                        const int j = (k * SEG + l) * 4 + c;
+                        if (j < L[q] && is_max(comp(v[q][k], c), m)) cand = j;
+                    }
+                cand = group_reduce<SEG>(cand, OpMinI());
+                if (live && l == 0) argmax[r] = L[q] > 0 ? cand : -1;
+            }
+            float s = 0.f;
+#pragma unroll
+            for (int k = 0; k < NV; ++k) {
+                v[q][k] = M == kNone ? exp4(v[q][k], m) : exp4_masked(v[q][k], m, (k * SEG + l) * 4, L[q]);
+                s += (v[q][k].x + v[q][k].y) + (v[q][k].z + v[q][k].w);
+            }
+            s = group_reduce<SEG>(s, OpSum());
+            const float inv = 1.0f / s;  // one correctly rounded division per row
+            float* yr = y + (int64_t)(live ? r : 0) * y_rs;
+#pragma unroll
+            for (int k = 0; k < NV; ++k) {
+                const int j0 = (k * SEG + l) * 4;
+                if constexpr (M == kNone) {
+                    if (live) st4<true>(yr + j0, v[q][k] * inv);
+                } else {
+                    store4m<M, true>(yr, j0, L[q], v[q][k] * inv);
                 }
-            cand = group_reduce<SEG>(cand, OpMinI());
-            if (live && l == 0) argmax[r] = L > 0 ? cand : -1;
+            }
         }
-        float s = 0.f;
-#pragma unroll
-        for (int k = 0; k < NV; ++k) {
-            const int j0 = (k * SEG + l) * 4;
-            v[k].x = j0 + 0 < L ? exp_fast(v[k].x - m) : 0.f;
-            v[k].y = j0 + 1 < L ? exp_fast(v[k].y - m) : 0.f;
-            v[k].z = j0 + 2 < L ? exp_fast(v[k].z - m) : 0.f;
-            v[k].w = j0 + 3 < L ? exp_fast(v[k].w - m) : 0.f;
-            s += (v[k].x + v[k].y) + (v[k].z + v[k].w);
-        }
-        s = group_reduce<SEG>(s, OpSum());
-        const float inv = 1.0f / s;  // one correctly rounded division per row
-        float* yr = y + (int64_t)(live ? r : 0) * y_rs;
-#pragma unroll
-        for (int k = 0; k < NV; ++k) store4_masked<VEC, true>(yr, (k * SEG + l) * 4, L, v[k] * inv);
     }
 }
 
@@ -95,66 +134,78 @@ __global__ __launch_bounds__(256) void fr_per_softmax_f32(const float* x, float*
 // sum by e^(m - m') and adds the new terms e^(x - m') - the online update of
 // hello-gpu Chapter 12, 12.3, one rescale per step rather than per element.
 // The lane states are merged with the (m, d) monoid. Pass 2 re-reads the row,
-// writes e^(x - M) / D and finds the first index of the maximum.
+// writes e^(x - M) / D and finds the first index of the maximum. Steps wholly
+// inside the row run unmasked; only the last step of a row is masked.
+template <int M, int T, int U>
+__device__ __forceinline__ MD online_step(const float* xr, int base, int L, MD st) {
+    const int tid = threadIdx.x;
+    f32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = load4m<M, false>(xr, base + (u * T + tid) * 4, L, -INFINITY);
+    float cm = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < U; ++u) cm = max4(cm, v[u]);
+    const float mx = fmax_nan(st.m, cm);
+    float add = 0.f;
+    if (mx != -INFINITY) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const f32x4 e = M == kNone ? exp4(v[u], mx) : exp4_masked(v[u], mx, base + (u * T + tid) * 4, L);
+            add += (e.x + e.y) + (e.z + e.w);
+        }
+    }
+    const float scale = st.m == -INFINITY ? 0.f : exp_fast(st.m - mx);
+    return MD{mx, st.d * scale + add};
+}
+
+template <int M, int T, int U>
+__device__ __forceinline__ int normalize_step(const float* xr, float* yr, int base, int L, float mx, float inv,
+                                              bool want_argmax, int cand) {
+    const int tid = threadIdx.x;
+    f32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = load4m<M, true>(xr, base + (u * T + tid) * 4, L, -INFINITY);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int j0 = base + (u * T + tid) * 4;
+        if (want_argmax && cand == INT_MAX) {
+            for (int c = 0; c < 4; ++c)
+                if (j0 + c < L && cand == INT_MAX && is_max(comp(v[u], c), mx)) cand = j0 + c;
+        }
+        store4m<M, true>(yr, j0, L, exp4(v[u], mx) * inv);
+    }
+    return cand;
+}
+
 template <int T, int U, bool VEC>
 __global__ __launch_bounds__(T) void fr_red_softmax_f32(const float* x, float* y, int rows, int cols,
                                                         int64_t x_rs, int64_t y_rs,
                                                         const int32_t* __restrict__ lengths,
                                                         int32_t* __restrict__ argmax) {
+    constexpr int STEP = T * 4 * U;
     __shared__ MD sl_md[T / kWave];
     __shared__ int sl_i[T / kWave];
-    const int tid = threadIdx.x;
     for (int r = blockIdx.x; r < rows; r += gridDim.x) {
         const int L = row_len(lengths, r, cols);
+        const int full = L - L % STEP;
         const float* xr = x + (int64_t)r * x_rs;
         MD st{-INFINITY, 0.f};
-        for (int base = 0; base < L; base += T * 4 * U) {
-            f32x4 v[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) v[u] = load4_masked<VEC, false>(xr, base + (u * T + tid) * 4, L, -INFINITY);
-            float cm = -INFINITY;
-#pragma unroll
-            for (int u = 0; u < U; ++u) cm = fmax_nan(fmax_nan(cm, fmax_nan(v[u].x, v[u].y)), fmax_nan(v[u].z, v[u].w));
-            const float M = fmax_nan(st.m, cm);
-            float add = 0.f;
-            if (M != -INFINITY) {
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int j0 = base + (u * T + tid) * 4;
-                    add += j0 + 0 < L ? exp_fast(v[u].x - M) : 0.f;
-                    add += j0 + 1 < L ? exp_fast(v[u].y - M) : 0.f;
-                    add += j0 + 2 < L ? exp_fast(v[u].z - M) : 0.f;
-                    add += j0 + 3 < L ? exp_fast(v[u].w - M) : 0.f;
-                }
-            }
-            const float scale = st.m == -INFINITY ? 0.f : exp_fast(st.m - M);
-            st = MD{M, st.d * scale + add};
-        }
+        int base = 0;
+        for (; base < full; base += STEP) st = online_step<body_mask<VEC>(), T, U>(xr, base, L, st);
+        if (base < L) st = online_step<tail_mask<VEC>(), T, U>(xr, base, L, st);
         st = group_reduce<kWave>(st, OpMD());
         st = block_fold(st, sl_md, T / kWave, OpMD());
-        const float M = st.m;
         const float inv = 1.0f / st.d;
         float* yr = y + (int64_t)r * y_rs;
+        const bool want = argmax != nullptr;
         int cand = INT_MAX;
-        for (int base = 0; base < L; base += T * 4 * U) {
-            f32x4 v[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) v[u] = load4_masked<VEC, true>(xr, base + (u * T + tid) * 4, L, -INFINITY);
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int j0 = base + (u * T + tid) * 4;
-                if (argmax && cand == INT_MAX) {
-                    for (int c = 0; c < 4; ++c)
-                        if (j0 + c < L && cand == INT_MAX && is_max(comp(v[u], c), M)) cand = j0 + c;
-                }
-                f32x4 e = {exp_fast(v[u].x - M), exp_fast(v[u].y - M), exp_fast(v[u].z - M), exp_fast(v[u].w - M)};
-                store4_masked<VEC, true>(yr, j0, L, e * inv);
-            }
-        }
-        if (argmax) {
+        for (base = 0; base < full; base += STEP)
+            cand = normalize_step<body_mask<VEC>(), T, U>(xr, yr, base, L, st.m, inv, want, cand);
+        if (base < L) cand = normalize_step<tail_mask<VEC>(), T, U>(xr, yr, base, L, st.m, inv, want, cand);
+        if (want) {
             cand = group_reduce<kWave>(cand, OpMinI());
             cand = block_fold(cand, sl_i, T / kWave, OpMinI());
-            if (tid == 0) argmax[r] = L > 0 ? cand : -1;
+            if (threadIdx.x == 0) argmax[r] = L > 0 ? cand : -1;
         }
         __syncthreads();  // slots are rewritten by the next row
     }
@@ -164,7 +215,41 @@ __global__ __launch_bounds__(T) void fr_red_softmax_f32(const float* x, float* y
 // Chunk c of row r (workgroup r * S + c) covers [c * C, min(len_r, (c+1) * C))
 // with C = 4 * T * NV. Part 1 keeps the chunk in registers and writes its
 // partial (m, d, first index of m). Part 2 merges the row's partials in chunk
-// order, writes the argmax (chunk 0) and the normalized chunk.
+// order, writes the argmax (chunk 0) and the normalized chunk. A chunk wholly
+// inside its row is loaded without masks.
+template <int M, int T, int NV>
+__device__ __forceinline__ void part_body(const float* xr, int start, int end, SoftmaxPartial* out, float* sl_m,
+                                          float* sl_d, int* sl_i) {
+    const int tid = threadIdx.x;
+    f32x4 v[NV];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) v[k] = load4m<M, false>(xr, start + (k * T + tid) * 4, end, -INFINITY);
+    float m = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) m = max4(m, v[k]);
+    m = group_reduce<kWave>(m, OpMax());
+    m = block_fold(m, sl_m, T / kWave, OpMax());
+    int cand = INT_MAX;
+    float s = 0.f;
+#pragma unroll
+    for (int k = NV - 1; k >= 0; --k)
+#pragma unroll
+        for (int c = 3; c >= 0; --c) {
+            const int j = start + (k * T + tid) * 4 + c;
+            if (j < end && is_max(comp(v[k], c), m)) cand = j;
+        }
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+        const f32x4 e = M == kNone ? exp4(v[k], m) : exp4_masked(v[k], m, start + (k * T + tid) * 4, end);
+        s += (e.x + e.y) + (e.z + e.w);
+    }
+    cand = group_reduce<kWave>(cand, OpMinI());
+    cand = block_fold(cand, sl_i, T / kWave, OpMinI());
+    s = group_reduce<kWave>(s, OpSum());
+    s = block_fold(s, sl_d, T / kWave, OpSum());
+    if (tid == 0) *out = SoftmaxPartial{m, s, cand, 0};
+}
+
 template <int T, int NV, bool VEC>
 __global__ __launch_bounds__(T) void fr_split_softmax_part(const float* __restrict__ x, int rows, int cols,
                                                            int64_t x_rs, const int32_t* __restrict__ lengths,
@@ -182,37 +267,18 @@ __global__ __launch_bounds__(T) void fr_split_softmax_part(const float* __restri
     if (start >= L) return;
     const int end = min(L, start + C);
     const float* xr = x + (int64_t)r * x_rs;
+    if (end - start == C) part_body<body_mask<VEC>(), T, NV>(xr, start, end, ws + w, sl_m, sl_d, sl_i);
+    else part_body<tail_mask<VEC>(), T, NV>(xr, start, end, ws + w, sl_m, sl_d, sl_i);
+}
+
+template <int M, int T, int NV>
+__device__ __forceinline__ void fin_body(const float* xr, float* yr, int start, int end, float mx, float inv) {
     const int tid = threadIdx.x;
     f32x4 v[NV];
 #pragma unroll
-    for (int k = 0; k < NV; ++k) v[k] = load4_masked<VEC, false>(xr, start + (k * T + tid) * 4, end, -INFINITY);
-    float m = -INFINITY;
+    for (int k = 0; k < NV; ++k) v[k] = load4m<M, true>(xr, start + (k * T + tid) * 4, end, -INFINITY);
 #pragma unroll
-    for (int k = 0; k < NV; ++k) m = fmax_nan(fmax_nan(m, fmax_nan(v[k].x, v[k].y)), fmax_nan(v[k].z, v[k].w));
-    m = group_reduce<kWave>(m, OpMax());
-    m = block_fold(m, sl_m, T / kWave, OpMax());
-    int cand = INT_MAX;
-    float s = 0.f;
-#pragma unroll
-    for (int k = NV - 1; k >= 0; --k)
-#pragma unroll
-        for (int cc = 3; cc >= 0; --cc) {
-            const int j = start + (k * T + tid) * 4 + cc;
-            if (j < end && is_max(comp(v[k], cc), m)) cand = j;
-        }
-#pragma unroll
-    for (int k = 0; k < NV; ++k) {
-        const int j0 = start + (k * T + tid) * 4;
-        s += j0 + 0 < end ? exp_fast(v[k].x - m) : 0.f;
-        s += j0 + 1 < end ? exp_fast(v[k].y - m) : 0.f;
-        s += j0 + 2 < end ? exp_fast(v[k].z - m) : 0.f;
-        s += j0 + 3 < end ? exp_fast(v[k].w - m) : 0.f;
-    }
-    cand = group_reduce<kWave>(cand, OpMinI());
-    cand = block_fold(cand, sl_i, T / kWave, OpMinI());
-    s = group_reduce<kWave>(s, OpSum());
-    s = block_fold(s, sl_d, T / kWave, OpSum());
-    if (tid == 0) ws[w] = SoftmaxPartial{m, s, cand, 0};
+    for (int k = 0; k < NV; ++k) store4m<M, true>(yr, start + (k * T + tid) * 4, end, exp4(v[k], mx) * inv);
 }
 
 template <int T, int NV, bool VEC>
@@ -243,18 +309,11 @@ __global__ __launch_bounds__(T) void fr_split_softmax_fin(const float* x, float*
         best = mi_combine(best, MI{p.m, p.idx});
     }
     if (c == 0 && argmax && threadIdx.x == 0) argmax[r] = best.i;
-    const float M = st.m;
     const float inv = 1.0f / st.d;
     const float* xr = x + (int64_t)r * x_rs;
     float* yr = y + (int64_t)r * y_rs;
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int k = 0; k < NV; ++k) {
-        const int j0 = start + (k * T + tid) * 4;
-        f32x4 v = load4_masked<VEC, true>(xr, j0, end, -INFINITY);
-        f32x4 e = {exp_fast(v.x - M), exp_fast(v.y - M), exp_fast(v.z - M), exp_fast(v.w - M)};
-        store4_masked<VEC, true>(yr, j0, end, e * inv);
-    }
+    if (end - start == C) fin_body<body_mask<VEC>(), T, NV>(xr, yr, start, end, st.m, inv);
+    else fin_body<tail_mask<VEC>(), T, NV>(xr, yr, start, end, st.m, inv);
 }
 
 // ------------------------------------------------------------------ launchers
@@ -265,21 +324,40 @@ using PartFn = void (*)(const float*, int, int, int64_t, const int32_t*, Softmax
 using FinFn = void (*)(const float*, float*, int, int, int64_t, int64_t, const int32_t*, int32_t*,
                        const SoftmaxPartial*, int);
 
-template <bool VEC>
-SmFn pick_per(int seg, int nv) {
+template <int M>
+SmFn pick_per_m(int seg, int nv, int rpw) {
+    if (rpw == 2) {
+        if (seg != 64) return nullptr;
+        switch (nv) {
+            case 1: return fr_per_softmax_f32<64, 1, M, 2>;
+            case 2: return fr_per_softmax_f32<64, 2, M, 2>;
+            case 4: return fr_per_softmax_f32<64, 4, M, 2>;
+        }
+        return nullptr;
+    }
+    if (rpw != 1) return nullptr;
     switch (seg) {
-        case 8: return fr_per_softmax_f32<8, 1, VEC>;
-        case 16: return fr_per_softmax_f32<16, 1, VEC>;
-        case 32: return fr_per_softmax_f32<32, 1, VEC>;
+        case 8: return fr_per_softmax_f32<8, 1, M, 1>;
+        case 16: return fr_per_softmax_f32<16, 1, M, 1>;
+        case 32: return fr_per_softmax_f32<32, 1, M, 1>;
         case 64:
             switch (nv) {
-                case 1: return fr_per_softmax_f32<64, 1, VEC>;
-                case 2: return fr_per_softmax_f32<64, 2, VEC>;
-                case 4: return fr_per_softmax_f32<64, 4, VEC>;
-                case 8: return fr_per_softmax_f32<64, 8, VEC>;
+                case 1: return fr_per_softmax_f32<64, 1, M, 1>;
+                case 2: return fr_per_softmax_f32<64, 2, M, 1>;
+                case 4: return fr_per_softmax_f32<64, 4, M, 1>;
+                case 8: return fr_per_softmax_f32<64, 8, M, 1>;
             }
     }
     return nullptr;
+}
+
+SmFn pick_per(int mask, int seg, int nv, int rpw) {
+    switch (mask) {
+        case kNone: return pick_per_m<kNone>(seg, nv, rpw);
+        case kVec: return pick_per_m<kVec>(seg, nv, rpw);
+        case kElem: return pick_per_m<kElem>(seg, nv, rpw);
+        default: return pick_per_m<kScalar>(seg, nv, rpw);
+    }
 }
 
 template <bool VEC>
@@ -287,6 +365,7 @@ SmFn pick_red(int threads, int u) {
     if (threads == 256 && u == 4) return fr_red_softmax_f32<256, 4, VEC>;
     if (threads == 512 && u == 2) return fr_red_softmax_f32<512, 2, VEC>;
     if (threads == 1024 && u == 2) return fr_red_softmax_f32<1024, 2, VEC>;
+    if (threads == 1024 && u == 1) return fr_red_softmax_f32<1024, 1, VEC>;
     return nullptr;
 }
 
@@ -311,15 +390,20 @@ void pick_split(int threads, int nv, PartFn* part, FinFn* fin) {
 hipError_t launch_softmax(const fr_plan& p, const SoftmaxArgs& a, hipStream_t s) {
     const bool vec = p.vec16 != 0;
     if (p.form == FR_FORM_PER) {
-        SmFn f = vec ? pick_per<true>(p.seg, p.vec) : pick_per<false>(p.seg, p.vec);
-        if (!f) return hipErrorInvalidValue;
+        const int rpw = p.rows_per_wg / (256 / p.seg);
+        // dense rows that fill the capacity exactly run without masks
+        const int mask = !vec ? kScalar
+                              : (a.lengths ? kElem
+                                           : (a.cols == 4 * p.seg * p.vec ? kNone : (a.cols % 4 == 0 ? kVec : kElem)));
+        SmFn f = pick_per(mask, p.seg, p.vec, rpw);
+        if (!f) return hipErrorInvalidDeviceFunction;
         hipLaunchKernelGGL(f, dim3((unsigned)p.grid), dim3(256), 0, s, a.x, a.y, a.rows, a.cols, a.x_rs, a.y_rs,
                            a.lengths, a.argmax);
         return hipGetLastError();
     }
     if (p.form == FR_FORM_RED) {
         SmFn f = vec ? pick_red<true>(p.threads, p.vec) : pick_red<false>(p.threads, p.vec);
-        if (!f) return hipErrorInvalidValue;
+        if (!f) return hipErrorInvalidDeviceFunction;
         hipLaunchKernelGGL(f, dim3((unsigned)p.grid), dim3(p.threads), 0, s, a.x, a.y, a.rows, a.cols, a.x_rs,
                            a.y_rs, a.lengths, a.argmax);
         return hipGetLastError();
@@ -329,7 +413,7 @@ hipError_t launch_softmax(const fr_plan& p, const SoftmaxArgs& a, hipStream_t s)
         FinFn fin;
         if (vec) pick_split<true>(p.threads, p.vec, &part, &fin);
         else pick_split<false>(p.threads, p.vec, &part, &fin);
-        if (!part || !fin) return hipErrorInvalidValue;
+        if (!part || !fin) return hipErrorInvalidDeviceFunction;
         SoftmaxPartial* ws = static_cast<SoftmaxPartial*>(a.ws);
         hipLaunchKernelGGL(part, dim3((unsigned)p.grid), dim3(p.threads), 0, s, a.x, a.rows, a.cols, a.x_rs,
                            a.lengths, ws, p.splits);

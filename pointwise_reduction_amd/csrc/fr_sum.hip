@@ -46,8 +46,9 @@ __device__ __forceinline__ f32x4 map4(f32x4 a, f32x4 b) {
 // SEG lanes per row, NV 16-byte vectors per lane: row capacity 4 * SEG * NV.
 // A 256-thread workgroup serves 256 / SEG rows per step of a grid-stride
 // loop over row groups. Lane l of a group owns elements (k * SEG + l) * 4 + c,
-// so each load instruction of a group covers 64 * SEG contiguous bytes.
-template <int P, int SEG, int NV, bool VEC>
+// so each load instruction of a group covers 64 * SEG contiguous bytes. M is
+// the masking mode (kNone: dense rows that fill the capacity exactly).
+template <int P, int SEG, int NV, int M>
 __global__ __launch_bounds__(256) void fr_per_sum_f32(const float* __restrict__ a, const float* __restrict__ b,
                                                       float* __restrict__ out, int rows, int cols, int64_t a_rs,
                                                       int64_t b_rs, int64_t out_s, float post) {
@@ -59,14 +60,24 @@ __global__ __launch_bounds__(256) void fr_per_sum_f32(const float* __restrict__ 
         const int r = grp * RPB + g;
         const bool live = r < rows;
         const int L = live ? cols : 0;
-        const float* ar = a + (int64_t)(live ? r : 0) * a_rs;
-        const float* br = P == kReluAdd ? b + (int64_t)(live ? r : 0) * b_rs : nullptr;
+        // kNone: a row past the end re-reads the last row (in bounds) and
+        // stores nothing, so the loads carry no branch
+        const int rl = live ? r : (M == kNone ? rows - 1 : 0);
+        const float* ar = a + (int64_t)rl * a_rs;
+        const float* br = P == kReluAdd ? b + (int64_t)rl * b_rs : nullptr;
         f32x4 va[NV], vb[NV];
 #pragma unroll
         for (int k = 0; k < NV; ++k) {
-            va[k] = load4_masked<VEC, true>(ar, (k * SEG + l) * 4, L, 0.f);
-            if constexpr (P == kReluAdd) vb[k] = load4_masked<VEC, true>(br, (k * SEG + l) * 4, L, 0.f);
-            else vb[k] = va[k];
+            const int j0 = (k * SEG + l) * 4;
+            if constexpr (M == kNone) {
+                va[k] = ld4<true>(ar + j0);
+                if constexpr (P == kReluAdd) vb[k] = ld4<true>(br + j0);
+                else vb[k] = va[k];
+            } else {
+                va[k] = load4m<M, true>(ar, j0, L, 0.f);
+                if constexpr (P == kReluAdd) vb[k] = load4m<M, true>(br, j0, L, 0.f);
+                else vb[k] = va[k];
+            }
         }
         float s = 0.f;
 #pragma unroll
@@ -80,24 +91,33 @@ __global__ __launch_bounds__(256) void fr_per_sum_f32(const float* __restrict__ 
 // One workgroup of T threads per row (grid-stride over rows). Each step loads
 // U independent 16-byte vectors per lane (U * T * 64 bytes in flight per
 // workgroup), accumulating into U x 4 per-lane partial sums in a fixed order.
+// Steps wholly inside [start, end) run unmasked; only the last one is masked.
+template <int P, int M, int T, int U>
+__device__ __forceinline__ void sum_step(const float* __restrict__ ar, const float* __restrict__ br, int base,
+                                         int end, f32x4* acc) {
+    f32x4 va[U], vb[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int j0 = base + (u * T + (int)threadIdx.x) * 4;
+        va[u] = load4m<M, true>(ar, j0, end, 0.f);
+        if constexpr (P == kReluAdd) vb[u] = load4m<M, true>(br, j0, end, 0.f);
+        else vb[u] = va[u];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc[u] += map4<P>(va[u], vb[u]);
+}
+
 template <int P, int T, int U, bool VEC>
 __device__ __forceinline__ float lane_sum_range(const float* __restrict__ ar, const float* __restrict__ br,
                                                 int start, int end) {
+    constexpr int STEP = T * 4 * U;
     f32x4 acc[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int base = start; base < end; base += T * 4 * U) {
-        f32x4 va[U], vb[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int j0 = base + (u * T + (int)threadIdx.x) * 4;
-            va[u] = load4_masked<VEC, true>(ar, j0, end, 0.f);
-            if constexpr (P == kReluAdd) vb[u] = load4_masked<VEC, true>(br, j0, end, 0.f);
-            else vb[u] = va[u];
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) acc[u] += map4<P>(va[u], vb[u]);
-    }
+    const int full = start + (end - start) / STEP * STEP;
+    int base = start;
+    for (; base < full; base += STEP) sum_step<P, body_mask<VEC>(), T, U>(ar, br, base, end, acc);
+    if (base < end) sum_step<P, tail_mask<VEC>(), T, U>(ar, br, base, end, acc);
     float s = 0.f;
 #pragma unroll
     for (int u = 0; u < U; ++u) s += (acc[u].x + acc[u].y) + (acc[u].z + acc[u].w);
@@ -123,8 +143,8 @@ __global__ __launch_bounds__(T) void fr_red_sum_f32(const float* __restrict__ a,
 // ------------------------------------------------------------------ split
 // Workgroup w reduces chunk c = w % S of row r = w / S, i.e. elements
 // [c * chunk, min(cols, (c + 1) * chunk)), and writes the raw partial sum to
-// ws[r * S + c]. chunk is a multiple of 4 * T, so every chunk starts on a
-// 16-byte boundary of its row.
+// ws[r * S + c]. chunk is a multiple of 4 * T * U, so every chunk starts on a
+// 16-byte boundary of its row and all its steps but the row's last are full.
 template <int P, int T, int U, bool VEC>
 __global__ __launch_bounds__(T) void fr_split_sum_f32(const float* __restrict__ a, const float* __restrict__ b,
                                                       float* __restrict__ ws, int rows, int cols, int64_t a_rs,
@@ -150,26 +170,38 @@ namespace {
 using PerFn = void (*)(const float*, const float*, float*, int, int, int64_t, int64_t, int64_t, float);
 using SplitFn = void (*)(const float*, const float*, float*, int, int, int64_t, int64_t, int, int);
 
-template <int P, bool VEC>
-PerFn pick_per(int seg, int nv) {
+template <int P, int M>
+PerFn pick_per_m(int seg, int nv) {
     switch (seg) {
-        case 8: return fr_per_sum_f32<P, 8, 1, VEC>;
-        case 16: return fr_per_sum_f32<P, 16, 1, VEC>;
-        case 32: return fr_per_sum_f32<P, 32, 1, VEC>;
+        case 8: return nv == 1 ? fr_per_sum_f32<P, 8, 1, M> : nullptr;
+        case 16: return nv == 1 ? fr_per_sum_f32<P, 16, 1, M> : nullptr;
+        case 32: return nv == 1 ? fr_per_sum_f32<P, 32, 1, M> : nullptr;
         case 64:
             switch (nv) {
-                case 1: return fr_per_sum_f32<P, 64, 1, VEC>;
-                case 2: return fr_per_sum_f32<P, 64, 2, VEC>;
-                case 4: return fr_per_sum_f32<P, 64, 4, VEC>;
-                case 8: return fr_per_sum_f32<P, 64, 8, VEC>;
+                case 1: return fr_per_sum_f32<P, 64, 1, M>;
+                case 2: return fr_per_sum_f32<P, 64, 2, M>;
+                case 4: return fr_per_sum_f32<P, 64, 4, M>;
+                case 8: return fr_per_sum_f32<P, 64, 8, M>;
             }
     }
     return nullptr;
 }
 
 template <int P>
-PerFn pick_per(int seg, int nv, bool vec) {
-    return vec ? pick_per<P, true>(seg, nv) : pick_per<P, false>(seg, nv);
+PerFn pick_per(int mask, int seg, int nv) {
+    switch (mask) {
+        case kNone: return pick_per_m<P, kNone>(seg, nv);
+        case kVec: return pick_per_m<P, kVec>(seg, nv);
+        case kElem: return pick_per_m<P, kElem>(seg, nv);
+        default: return pick_per_m<P, kScalar>(seg, nv);
+    }
+}
+
+// Mask mode of a persistent launch over dense rows of `cols` elements.
+int per_mask(bool vec, int cols, int seg, int nv) {
+    if (!vec) return kScalar;
+    if (cols == 4 * seg * nv) return kNone;
+    return cols % 4 == 0 ? kVec : kElem;
 }
 
 template <int P, bool VEC>
@@ -192,22 +224,23 @@ template <int P>
 hipError_t launch_sum_p(const fr_plan& p, const SumArgs& a, hipStream_t s) {
     const float post = P == kReluAdd ? 2.f : 1.f;
     if (p.form == FR_FORM_PER) {
-        PerFn f = pick_per<P>(p.seg, p.vec, p.vec16 != 0);
-        if (!f) return hipErrorInvalidValue;
+        if (p.seg < 8 || p.rows_per_wg != 256 / p.seg) return hipErrorInvalidDeviceFunction;  // one row per group
+        PerFn f = pick_per<P>(per_mask(p.vec16 != 0, a.cols, p.seg, p.vec), p.seg, p.vec);
+        if (!f) return hipErrorInvalidDeviceFunction;
         hipLaunchKernelGGL(f, dim3((unsigned)p.grid), dim3(256), 0, s, a.a, a.b, a.out, a.rows, a.cols, a.a_rs,
                            a.b_rs, a.out_s, post);
         return hipGetLastError();
     }
     if (p.form == FR_FORM_RED) {
         PerFn f = p.vec16 ? pick_red<P, true>(p.threads, p.vec) : pick_red<P, false>(p.threads, p.vec);
-        if (!f) return hipErrorInvalidValue;
+        if (!f) return hipErrorInvalidDeviceFunction;
         hipLaunchKernelGGL(f, dim3((unsigned)p.grid), dim3(p.threads), 0, s, a.a, a.b, a.out, a.rows, a.cols,
                            a.a_rs, a.b_rs, a.out_s, post);
         return hipGetLastError();
     }
     if (p.form == FR_FORM_SPLIT) {
         SplitFn f = p.vec16 ? pick_split<P, true>(p.threads, p.vec) : pick_split<P, false>(p.threads, p.vec);
-        if (!f) return hipErrorInvalidValue;
+        if (!f) return hipErrorInvalidDeviceFunction;
         hipLaunchKernelGGL(f, dim3((unsigned)p.grid), dim3(p.threads), 0, s, a.a, a.b, a.ws, a.rows, a.cols,
                            a.a_rs, a.b_rs, p.chunk, p.splits);
         hipError_t e = hipGetLastError();
@@ -217,8 +250,8 @@ hipError_t launch_sum_p(const fr_plan& p, const SumArgs& a, hipStream_t s) {
         const int seg = S <= 32 ? 8 : (S <= 64 ? 16 : (S <= 128 ? 32 : 64));
         int nv = (S + 4 * seg - 1) / (4 * seg);
         nv = nv <= 1 ? 1 : (nv <= 2 ? 2 : (nv <= 4 ? 4 : 8));
-        PerFn fin = pick_per<kIdent>(seg, nv, (S % 4) == 0);
-        if (!fin) return hipErrorInvalidValue;
+        PerFn fin = pick_per<kIdent>(per_mask(S % 4 == 0, S, seg, nv), seg, nv);
+        if (!fin) return hipErrorInvalidDeviceFunction;
         hipLaunchKernelGGL(fin, dim3((unsigned)p.grid2), dim3(256), 0, s, a.ws, nullptr, a.out, a.rows, S,
                            (int64_t)S, (int64_t)0, a.out_s, post);
         return hipGetLastError();

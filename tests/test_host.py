@@ -132,9 +132,9 @@ def test_plans_for_the_five_workloads():
     # Example 1.1, 64 x 128 fp32: half a wave per row, one vector per lane
     p = fr.fr_plan_query(fr.FR_OP_SUM_RELU_ADD, 64, 128)
     assert (p.form, p.seg, p.vec, p.rows_per_wg, p.grid) == (fr.FR_FORM_PER, 32, 1, 8, 8)
-    # softmax 4096 x 1024: a wave per row, 4 x 16-byte vectors per lane
+    # softmax 4096 x 1024: a wave per 2 rows, 4 x 16-byte vectors per lane and row
     p = fr.fr_plan_query(fr.FR_OP_SOFTMAX, 4096, 1024)
-    assert (p.form, p.seg, p.vec, p.grid) == (fr.FR_FORM_PER, 64, 4, 1024)
+    assert (p.form, p.seg, p.vec, p.rows_per_wg, p.grid) == (fr.FR_FORM_PER, 64, 4, 8, 512)
     # LayerNorm 2048 x 32768 bf16: a 512-thread workgroup holds each row
     p = fr.fr_plan_query(fr.FR_OP_LAYERNORM, 2048, 32768, dtype=fr.FR_BF16)
     assert (p.form, p.threads, p.vec, p.grid) == (fr.FR_FORM_PER, 512, 8, 2048)
@@ -207,3 +207,29 @@ def test_workspace_matches_example_6_2_layout(golden):
     assert p.ws_bytes == rows * p.splits * 4
     assert p.splits >= g["splits"]
     assert fr.fr_sum_workspace_bytes(rows, cols) == p.ws_bytes
+
+
+def test_tune_override_replaces_the_launch_knobs():
+    try:
+        fr.fr_tune_override(fr.FR_OP_SOFTMAX, form=fr.FR_FORM_PER, threads=256, seg=64, vec=4, rows_per_wg=4)
+        p = fr.fr_plan_query(fr.FR_OP_SOFTMAX, 4096, 1024)
+        assert (p.form, p.seg, p.vec, p.rows_per_wg, p.grid) == (fr.FR_FORM_PER, 64, 4, 4, 1024)
+        with pytest.raises(fr.FrError) as e:
+            fr.fr_plan_query(fr.FR_OP_SOFTMAX, 10, 4000)  # does not fit 64 lanes x 4 vectors
+        assert e.value.status == fr.FR_E_ARG
+        # a split candidate with smaller chunks needs more workspace than the default query gives
+        fr.fr_tune_override(fr.FR_OP_SOFTMAX, form=fr.FR_FORM_SPLIT, threads=256, vec=4)
+        p = fr.fr_plan_query(fr.FR_OP_SOFTMAX, 512, 131072, ws_bytes=1 << 30)
+        assert (p.splits, p.chunk) == (32, 4096)
+        with pytest.raises(fr.FrError) as e:
+            fr.fr_plan_query(fr.FR_OP_SOFTMAX, 512, 131072, ws_bytes=fr.fr_softmax_rows_workspace_bytes(512, 131072))
+        assert e.value.status == fr.FR_E_WORKSPACE
+        fr.fr_tune_override(fr.FR_OP_LAYERNORM, form=fr.FR_FORM_PER, threads=1024, vec=4)
+        p = fr.fr_plan_query(fr.FR_OP_LAYERNORM, 2048, 32768, dtype=fr.FR_BF16)
+        assert (p.threads, p.vec, p.occupancy) == (1024, 4, 0)
+    finally:
+        fr.fr_tune_override(fr.FR_OP_SOFTMAX)
+        fr.fr_tune_override(fr.FR_OP_LAYERNORM)
+    assert fr.fr_plan_query(fr.FR_OP_SOFTMAX, 4096, 1024).rows_per_wg == 8  # automatic: 2 rows per wave
+    with pytest.raises(fr.FrError):
+        fr.fr_tune_override(99, form=1)
