@@ -267,6 +267,38 @@ def make_workload(name, torch, fr, synth):
 
         return W(), per_set
 
+    if name == "copy":
+        # practical ceiling and counter calibration: torch's own device copy of
+        # a 4096 x 1024 fp32 buffer (16 MiB read + 16 MiB written)
+        rows, cols = 4096, 1024
+        per_set = 2 * rows * cols * 4
+
+        class W(Workload):
+            kernel = "copy"
+            bytes = 2 * rows * cols * 4
+            dtype = "f32"
+
+            def alloc(self, sets):
+                x0 = torch.randn(rows, cols, device=dev)
+                self.args = [(x0 if i == 0 else x0.clone(), torch.empty_like(x0)) for i in range(sets)]
+
+            def launch(self, k):
+                x, y = self.args[k]
+                y.copy_(x)
+
+            def output(self, k):
+                return self.args[k][1]
+
+            def config(self):
+                return {"workload": "plain device copy 4096x1024 fp32 (torch copy_), the practical ceiling",
+                        "rows": rows, "cols": cols}
+
+            def oracle_fn(self):
+                x = np.zeros((rows, cols), dtype=np.float32)
+                return lambda: x.copy(), self.bytes, "numpy copy of the same size"
+
+        return W(), per_set
+
     raise SystemExit(f"unknown workload {name}")
 
 
@@ -317,7 +349,7 @@ def main():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="softmax",
-                    choices=["softmax", "sum_relu_add", "layernorm", "sumsq", "ragged"])
+                    choices=["softmax", "sum_relu_add", "layernorm", "sumsq", "ragged", "copy"])
     ap.add_argument("--warm", action="store_true", help="one buffer set: reads may hit the MALL")
     ap.add_argument("--eager", action="store_true", help="launch each step from the host (no graph)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
