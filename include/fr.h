@@ -88,6 +88,9 @@ typedef struct fr_plan {
     int32_t chunk;        /* elements per chunk (SPLIT), else 0 */
     int32_t vec16;        /* 1: 16-byte vector accesses; 0: element accesses */
     int32_t occupancy;    /* minimum waves per SIMD requested from the compiler (0: none) */
+    int32_t passes;       /* reads of the input (split softmax: 1 = chunks kept in registers while the
+                             row's partials are exchanged in one kernel, 2 = partial + finishing kernels) */
+    int32_t reserved;
     int64_t grid;         /* workgroups of the main kernel */
     int64_t grid2;        /* workgroups of the finishing kernel (0: none) */
     uint64_t ws_bytes;    /* workspace bytes this plan uses */

@@ -61,7 +61,14 @@ struct Knobs {
     int rpw = 1;     // rows per lane group (persistent fp32)
     int chunk = 0;   // elements per split chunk (sum split)
     int occ = 0;     // minimum waves per SIMD (persistent LayerNorm)
+    int passes = 0;  // split softmax: 1 single read with in-kernel exchange, 2 two kernels, 0 automatic
+    int num_cus = 0; // device compute units (sizes persistent grids only; results do not depend on it)
 };
+
+// Single-pass split softmax: workgroups wait for the other chunks of their
+// row, which needs more resident workgroups than chunks per row.
+constexpr int kFusedMaxSplits = 64;
+constexpr int kFusedWgsPerCu = 8;
 
 // Persistent fp32 geometry: the smallest lane group (8..64 lanes) whose
 // 16-byte vectors cover the row with at most 8 vectors per lane.
@@ -113,11 +120,29 @@ int finalize_plan(int op, int64_t rows, int64_t cols, const Knobs& k, fr_plan* p
         if (op == FR_OP_SOFTMAX) {
             const int64_t chunk = (int64_t)k.threads * 4 * k.vec;
             const int64_t s = cdiv(cols, chunk);
+            const bool one_ok = s <= kFusedMaxSplits && rows * s < (int64_t(1) << 31);
+            // Two kernels by default: measured on MI355X (512 ragged rows of up
+            // to 131071), the single pass is 2.4x slower - every workgroup
+            // serializes one load / publish / wait / merge latency chain per
+            // chunk, while the two-kernel form overlaps all chunks.
+            const int passes = k.passes == 0 ? 2 : k.passes;
+            if (passes != 1 && passes != 2) return FR_E_ARG;
+            if (passes == 1 && !one_ok) return FR_E_ARG;
             p->splits = (int)s;
             p->chunk = (int)chunk;
-            p->grid = rows * s;
-            p->grid2 = rows * s;
-            p->ws_bytes = (uint64_t)(rows * s * (int64_t)sizeof(SoftmaxPartial));
+            p->passes = passes;
+            const int64_t parts = rows * s * (int64_t)sizeof(SoftmaxPartial);
+            const uint64_t ws_one = (uint64_t)(64 + cdiv(rows * 4, 16) * 16 + parts);
+            if (passes == 1) {
+                // persistent grid claiming chunks by ticket; the prep kernel is not counted
+                p->grid = min64(rows * s, (int64_t)(k.num_cus > 0 ? k.num_cus : 256) * kFusedWgsPerCu);
+                p->grid2 = 0;
+                p->ws_bytes = ws_one;
+            } else {
+                p->grid = rows * s;
+                p->grid2 = rows * s;
+                p->ws_bytes = (uint64_t)parts;
+            }
         } else {
             const int64_t step = (int64_t)k.threads * 4 * k.vec;
             int64_t chunk = k.chunk;
@@ -165,8 +190,8 @@ uint64_t softmax_split_ws(int64_t rows, int64_t cols) {
 int make_plan(int op, int64_t rows, int64_t cols, int dtype, int num_cus, int has_lengths, uint64_t ws_bytes,
               int aligned16, int forced, const fr_plan* override_plan, fr_plan* p) {
     (void)has_lengths;
-    (void)num_cus;  // the thresholds are fixed per library build so that
-                    // workspace sizes and results do not depend on the device
+    // thresholds are fixed per library build so that workspace sizes and
+    // results do not depend on the device; num_cus only sizes persistent grids
     if (!p) return FR_E_NULL;
     if (rows < 0 || cols < 0 || rows >= (int64_t(1) << 31) || cols >= (int64_t(1) << 30)) return FR_E_SIZE;
     if (forced < FR_FORM_AUTO || forced > FR_FORM_SPLIT) return FR_E_ARG;
@@ -264,7 +289,9 @@ int make_plan(int op, int64_t rows, int64_t cols, int dtype, int num_cus, int ha
                     : 1;
         k.chunk = override_plan->chunk;
         k.occ = override_plan->occupancy;
+        k.passes = override_plan->passes;
     }
+    k.num_cus = num_cus;
     const int st = finalize_plan(op, rows, cols, k, p);
     if (st != FR_OK) return st;
     if (p->form == FR_FORM_SPLIT && ws_bytes < p->ws_bytes) return override_plan ? FR_E_WORKSPACE : FR_E_ARG;

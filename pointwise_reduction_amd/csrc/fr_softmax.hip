@@ -316,6 +316,168 @@ __global__ __launch_bounds__(T) void fr_split_softmax_fin(const float* x, float*
     else fin_body<tail_mask<VEC>(), T, NV>(xr, yr, start, end, st.m, inv);
 }
 
+// ------------------------------------------------------------------ split, single pass
+// The two-kernel split above reads every chunk twice. Here each chunk is read
+// once and kept in registers: workgroups claim chunks through an atomic
+// ticket in row-major order, publish the chunk's partial (m, d, first index
+// of m), wait until every chunk of the row has published, merge the row's
+// partials in chunk order and normalize the registers they still hold.
+//
+// Progress: a claimed ticket always belongs to a running workgroup, and a
+// workgroup publishes before it waits, so only the workgroups on the last
+// partly-claimed row can wait on unclaimed chunks; with more resident
+// workgroups than chunks per row (S <= 64 here) another workgroup claims
+// them. The wait is bounded all the same: past the spin limit the workgroup
+// stops waiting, poisons its chunk with NaN and raises the error word of the
+// workspace header, so every wave always exits.
+//
+// Visibility across XCDs: partial fields are stored and loaded with
+// agent-scope atomics, the row counter is incremented with release
+// semantics and read back with an acquire fence.
+constexpr int kFusedMaxSplits = 64;
+constexpr int kSpinLimit = 1 << 20;
+
+struct FusedWs {
+    uint32_t* hdr;         // [0] ticket, [1] error
+    uint32_t* row_cnt;     // rows counters of published chunks
+    SoftmaxPartial* part;  // rows x S partials
+};
+
+__host__ __device__ inline FusedWs fused_layout(void* ws, int rows) {
+    char* b = static_cast<char*>(ws);
+    FusedWs f;
+    f.hdr = reinterpret_cast<uint32_t*>(b);
+    f.row_cnt = reinterpret_cast<uint32_t*>(b + 64);
+    f.part = reinterpret_cast<SoftmaxPartial*>(b + 64 + ((int64_t)rows * 4 + 15) / 16 * 16);
+    return f;
+}
+
+__global__ __launch_bounds__(256) void fr_split_softmax_prep(uint32_t* hdr, uint32_t* row_cnt, int rows) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < 16) hdr[i] = 0u;
+    if (i < rows) row_cnt[i] = 0u;
+}
+
+template <int M, int T, int NV>
+__device__ __forceinline__ void fused_load(const float* xr, int start, int end, f32x4* v) {
+#pragma unroll
+    for (int k = 0; k < NV; ++k) v[k] = load4m<M, true>(xr, start + (k * T + (int)threadIdx.x) * 4, end, -INFINITY);
+}
+
+template <int M, int T, int NV>
+__device__ __forceinline__ void fused_store(float* yr, int start, int end, const f32x4* v, float mx, float inv) {
+#pragma unroll
+    for (int k = 0; k < NV; ++k) store4m<M, true>(yr, start + (k * T + (int)threadIdx.x) * 4, end, exp4(v[k], mx) * inv);
+}
+
+template <int T, int NV, bool VEC>
+__global__ __launch_bounds__(T) void fr_split_softmax_fused(const float* x, float* y, int rows, int cols,
+                                                            int64_t x_rs, int64_t y_rs,
+                                                            const int32_t* __restrict__ lengths,
+                                                            int32_t* __restrict__ argmax, void* ws, int S) {
+    constexpr int C = 4 * T * NV;
+    __shared__ float sl_m[T / kWave];
+    __shared__ float sl_d[T / kWave];
+    __shared__ int sl_i[T / kWave];
+    __shared__ uint32_t s_ticket;
+    __shared__ float s_max, s_inv;
+    __shared__ int s_timeout;
+    const FusedWs f = fused_layout(ws, rows);
+    const int tid = threadIdx.x;
+    const uint32_t total = (uint32_t)rows * (uint32_t)S;
+    for (;;) {
+        if (tid == 0) s_ticket = __hip_atomic_fetch_add(&f.hdr[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        const uint32_t t = s_ticket;
+        __syncthreads();  // every thread has read the ticket before it is rewritten
+        if (t >= total) break;
+        const int r = (int)(t / (uint32_t)S);
+        const int c = (int)(t % (uint32_t)S);
+        const int L = row_len(lengths, r, cols);
+        const int nc = (L + C - 1) / C;
+        if (c >= nc) {
+            if (c == 0 && argmax && tid == 0) argmax[r] = -1;
+            continue;
+        }
+        const int start = c * C;
+        const int end = min(L, start + C);
+        const bool full = end - start == C;
+        const float* xr = x + (int64_t)r * x_rs;
+        f32x4 v[NV];
+        if (full) fused_load<body_mask<VEC>(), T, NV>(xr, start, end, v);
+        else fused_load<tail_mask<VEC>(), T, NV>(xr, start, end, v);
+        // chunk statistics
+        float m = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < NV; ++k) m = max4(m, v[k]);
+        m = group_reduce<kWave>(m, OpMax());
+        m = block_fold(m, sl_m, T / kWave, OpMax());
+        int cand = INT_MAX;
+        float sum = 0.f;
+#pragma unroll
+        for (int k = NV - 1; k >= 0; --k)
+#pragma unroll
+            for (int cc = 3; cc >= 0; --cc) {
+                const int j = start + (k * T + tid) * 4 + cc;
+                if (j < end && is_max(comp(v[k], cc), m)) cand = j;
+            }
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            const f32x4 e = exp4_masked(v[k], m, start + (k * T + tid) * 4, end);
+            sum += (e.x + e.y) + (e.z + e.w);
+        }
+        cand = group_reduce<kWave>(cand, OpMinI());
+        cand = block_fold(cand, sl_i, T / kWave, OpMinI());
+        sum = group_reduce<kWave>(sum, OpSum());
+        sum = block_fold(sum, sl_d, T / kWave, OpSum());
+        // publish, then wait for the rest of the row
+        if (tid == 0) {
+            SoftmaxPartial* p = f.part + t;
+            __hip_atomic_store(&p->m, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&p->d, sum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&p->idx, cand, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_add(&f.row_cnt[r], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            int spins = 0;
+            while (__hip_atomic_load(&f.row_cnt[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)nc &&
+                   spins < kSpinLimit) {
+                __builtin_amdgcn_s_sleep(2);
+                ++spins;
+            }
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            s_timeout = spins < kSpinLimit ? 0 : 1;
+            if (spins >= kSpinLimit) __hip_atomic_store(&f.hdr[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        const bool timed_out = s_timeout != 0;
+        // merge the row's partials in chunk order (wave 0), broadcast through LDS
+        if (tid < kWave) {
+            MD st{-INFINITY, 0.f};
+            MI best{-INFINITY, INT_MAX};
+            const SoftmaxPartial* pr = f.part + (int64_t)r * S;
+            for (int k = tid; k < nc; k += kWave) {
+                const float pm = __hip_atomic_load(&pr[k].m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const float pd = __hip_atomic_load(&pr[k].d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const int pi = __hip_atomic_load(&pr[k].idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                st = md_combine(st, MD{pm, pd});
+                best = mi_combine(best, MI{pm, pi});
+            }
+            st = group_reduce<kWave>(st, OpMD());
+            best = group_reduce<kWave>(best, OpMI());
+            if (tid == 0) {
+                s_max = timed_out ? NAN : st.m;
+                s_inv = 1.0f / st.d;
+                if (c == 0 && argmax) argmax[r] = timed_out ? -1 : best.i;
+            }
+        }
+        __syncthreads();
+        const float mx = s_max, inv = s_inv;
+        float* yr = y + (int64_t)r * y_rs;
+        if (full) fused_store<body_mask<VEC>(), T, NV>(yr, start, end, v, mx, inv);
+        else fused_store<tail_mask<VEC>(), T, NV>(yr, start, end, v, mx, inv);
+        __syncthreads();  // LDS slots and broadcasts are rewritten by the next chunk
+    }
+}
+
 // ------------------------------------------------------------------ launchers
 namespace {
 
@@ -369,6 +531,16 @@ SmFn pick_red(int threads, int u) {
     return nullptr;
 }
 
+using FusedFn = void (*)(const float*, float*, int, int, int64_t, int64_t, const int32_t*, int32_t*, void*, int);
+
+template <bool VEC>
+FusedFn pick_fused(int threads, int nv) {
+    if (threads == 256 && nv == 8) return fr_split_softmax_fused<256, 8, VEC>;
+    if (threads == 256 && nv == 4) return fr_split_softmax_fused<256, 4, VEC>;
+    if (threads == 512 && nv == 4) return fr_split_softmax_fused<512, 4, VEC>;
+    return nullptr;
+}
+
 template <bool VEC>
 void pick_split(int threads, int nv, PartFn* part, FinFn* fin) {
     *part = nullptr;
@@ -406,6 +578,19 @@ hipError_t launch_softmax(const fr_plan& p, const SoftmaxArgs& a, hipStream_t s)
         if (!f) return hipErrorInvalidDeviceFunction;
         hipLaunchKernelGGL(f, dim3((unsigned)p.grid), dim3(p.threads), 0, s, a.x, a.y, a.rows, a.cols, a.x_rs,
                            a.y_rs, a.lengths, a.argmax);
+        return hipGetLastError();
+    }
+    if (p.form == FR_FORM_SPLIT && p.passes == 1) {
+        if (p.splits > kFusedMaxSplits) return hipErrorInvalidDeviceFunction;
+        FusedFn fused = vec ? pick_fused<true>(p.threads, p.vec) : pick_fused<false>(p.threads, p.vec);
+        if (!fused) return hipErrorInvalidDeviceFunction;
+        const FusedWs f = fused_layout(a.ws, a.rows);
+        hipLaunchKernelGGL(fr_split_softmax_prep, dim3((unsigned)((a.rows + 16 + 255) / 256)), dim3(256), 0, s, f.hdr,
+                           f.row_cnt, a.rows);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(fused, dim3((unsigned)p.grid), dim3(p.threads), 0, s, a.x, a.y, a.rows, a.cols, a.x_rs,
+                           a.y_rs, a.lengths, a.argmax, a.ws, p.splits);
         return hipGetLastError();
     }
     if (p.form == FR_FORM_SPLIT) {

@@ -62,14 +62,16 @@ def workload(name):
         rows, cap = 512, 131072
         x, L = synth.ragged_softmax_inputs(rows, cap, seed=5001)
         nbytes = 8 * int(L.sum()) + 8 * rows
-        cands = [dict(form=S, threads=256, vec=8), dict(form=S, threads=256, vec=4), dict(form=S, threads=512, vec=4),
-                 dict(form=R, threads=256, vec=4), dict(form=R, threads=512, vec=2), dict(form=R, threads=1024, vec=2)]
+        cands = [dict(form=S, threads=256, vec=8, passes=p) for p in (1, 2)]
+        cands += [dict(form=S, threads=256, vec=4, passes=p) for p in (1, 2)]
+        cands += [dict(form=S, threads=512, vec=4, passes=p) for p in (1, 2)]
+        cands += [dict(form=R, threads=512, vec=2), dict(form=R, threads=1024, vec=2)]
 
         def alloc(sets):
             Ld = _d(L)
             xs = [_d(x) for _ in range(sets)]
             ys = [torch.empty_like(xs[0]) for _ in range(sets)]
-            ws = [torch.empty(rows * 64 * 16 // 4, dtype=torch.float32, device="cuda") for _ in range(sets)]
+            ws = [torch.empty((rows * 64 * 16 + 4096) // 4, dtype=torch.float32, device="cuda") for _ in range(sets)]
             am = [torch.empty(rows, dtype=torch.int32, device="cuda") for _ in range(sets)]
             return (lambda k: fr.fr_softmax_rows(xs[k], ys[k], lengths=Ld, argmax=am[k], ws=ws[k])), \
                 (lambda: ys[0].masked_fill(torch.arange(cap, device="cuda")[None, :] >= Ld[:, None].long(), 0))

@@ -34,8 +34,9 @@ def run(x_np, lengths=None, form=fr.FR_FORM_AUTO, use_ws=None, cols=None, y_fill
         use_ws = form == fr.FR_FORM_SPLIT
     ws = None
     if use_ws:
-        nbytes = fr.fr_softmax_rows_workspace_bytes(rows, cols)
-        ws = torch.empty(max(nbytes, 16) // 4 + 4, dtype=torch.float32, device="cuda")
+        # room for either split variant (the single pass adds a header and row counters)
+        nbytes = fr.fr_softmax_rows_workspace_bytes(rows, cols) + 64 + 4 * rows + 64
+        ws = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
     with forced(form):
         fr.fr_softmax_rows(x, y, lengths=L, argmax=am, ws=ws)
     return host(yd)[:, :cols], (host(am) if argmax else None), host(yd)
@@ -198,3 +199,42 @@ def test_softmax_is_deterministic():
     x, L = synth.ragged_softmax_inputs(64, 60000, seed=2800, choices=(1000, 59999, 60000))
     outs = [run(x, lengths=L, use_ws=True)[2] for _ in range(3)]
     assert all(np.array_equal(outs[0].view(np.uint32), o.view(np.uint32)) for o in outs[1:])
+
+
+@pytest.mark.parametrize("passes", [1, 2])
+@pytest.mark.parametrize("cols", [8193, 50257, 131071, 140000])
+def test_softmax_split_passes(passes, cols):
+    """Both split variants: one read with the row's partials exchanged inside
+    one kernel, and the partial + finishing kernels."""
+    x, L = synth.ragged_softmax_inputs(24, cols, seed=2900 + cols, choices=(1, 4000, cols - 7, cols))
+    try:
+        fr.fr_tune_override(fr.FR_OP_SOFTMAX, form=fr.FR_FORM_SPLIT, threads=256, vec=8, passes=passes)
+        y, am, yfull = run(x, lengths=L, use_ws=True)
+    finally:
+        fr.fr_tune_override(fr.FR_OP_SOFTMAX)
+    compare(x, y, am, lengths=L, what=f"split passes={passes} cols={cols}")
+    for r, n in enumerate(L):
+        assert np.isnan(yfull[r, n:]).all()
+
+
+def test_softmax_single_pass_workspace_reports_no_timeout():
+    x, L = synth.ragged_softmax_inputs(512, 131072, seed=5001)
+    xd, Ld = dev(x), dev(L)
+    y = torch.empty_like(xd)
+    nbytes = 64 + 512 * 4 + 512 * 16 * 16
+    ws = torch.full((nbytes // 4,), 0x7FFFFFFF, dtype=torch.int32, device="cuda")  # garbage in the header
+    outs = []
+    try:
+        fr.fr_tune_override(fr.FR_OP_SOFTMAX, form=fr.FR_FORM_SPLIT, threads=256, vec=8, passes=1)
+        plan = fr.fr_plan_query(fr.FR_OP_SOFTMAX, 512, 131072, has_lengths=True, ws_bytes=nbytes)
+        assert plan.passes == 1 and plan.ws_bytes == nbytes
+        for _ in range(3):
+            fr.fr_softmax_rows(xd, y, lengths=Ld, ws=ws)
+            outs.append(host(y).copy())
+            assert int(host(ws)[1]) == 0, "a workgroup gave up waiting for its row"
+    finally:
+        fr.fr_tune_override(fr.FR_OP_SOFTMAX)
+    assert all(np.array_equal(outs[0].view(np.uint32), o.view(np.uint32)) for o in outs[1:])
+    y64, _ = oracle.softmax_rows(x, lengths=L)
+    written = valid_mask(512, 131072, L)
+    check_fp32(np.where(written, outs[0], 0.0), np.where(written, y64, 0.0), what="single pass")

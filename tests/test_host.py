@@ -145,10 +145,19 @@ def test_plans_for_the_five_workloads():
     p = fr.fr_plan_query(fr.FR_OP_SUMSQ, 1, n, ws_bytes=ws)
     assert (p.form, p.splits, p.chunk, p.grid, p.grid2) == (fr.FR_FORM_SPLIT, 2048, 1 << 17, 2048, 1)
     # ragged softmax, 512 rows of capacity 131072, with a workspace: 16 chunks of 8192
+    # (two kernels: 512 x 16 partials of 16 bytes)
     ws = fr.fr_softmax_rows_workspace_bytes(512, 131072)
     assert ws == 512 * 16 * 16
     p = fr.fr_plan_query(fr.FR_OP_SOFTMAX, 512, 131072, has_lengths=True, ws_bytes=ws)
-    assert (p.form, p.splits, p.chunk, p.grid, p.grid2) == (fr.FR_FORM_SPLIT, 16, 8192, 8192, 8192)
+    assert (p.form, p.splits, p.chunk, p.passes, p.grid, p.grid2) == (fr.FR_FORM_SPLIT, 16, 8192, 2, 8192, 8192)
+    # the single pass (a tuning candidate) adds a 64-byte header and 512 row counters, and a
+    # persistent grid of 8 workgroups per CU claims the chunks
+    fr.fr_tune_override(fr.FR_OP_SOFTMAX, form=fr.FR_FORM_SPLIT, threads=256, vec=8, passes=1)
+    try:
+        p = fr.fr_plan_query(fr.FR_OP_SOFTMAX, 512, 131072, has_lengths=True, ws_bytes=1 << 20)
+        assert (p.passes, p.grid, p.grid2, p.ws_bytes) == (1, 2048, 0, 64 + 512 * 4 + 512 * 16 * 16)
+    finally:
+        fr.fr_tune_override(fr.FR_OP_SOFTMAX)
     # ... and without one: one workgroup streams each row
     p = fr.fr_plan_query(fr.FR_OP_SOFTMAX, 512, 131072, has_lengths=True)
     assert (p.form, p.threads, p.grid) == (fr.FR_FORM_RED, 512, 512)
@@ -220,10 +229,18 @@ def test_tune_override_replaces_the_launch_knobs():
         # a split candidate with smaller chunks needs more workspace than the default query gives
         fr.fr_tune_override(fr.FR_OP_SOFTMAX, form=fr.FR_FORM_SPLIT, threads=256, vec=4)
         p = fr.fr_plan_query(fr.FR_OP_SOFTMAX, 512, 131072, ws_bytes=1 << 30)
-        assert (p.splits, p.chunk) == (32, 4096)
+        assert (p.splits, p.chunk, p.passes) == (32, 4096, 2)
+        fr.fr_tune_override(fr.FR_OP_SOFTMAX, form=fr.FR_FORM_SPLIT, threads=256, vec=8, passes=2)
+        p = fr.fr_plan_query(fr.FR_OP_SOFTMAX, 512, 131072, ws_bytes=1 << 30)
+        assert (p.splits, p.passes, p.grid, p.grid2, p.ws_bytes) == (16, 2, 8192, 8192, 512 * 16 * 16)
+        # rows with more than 64 chunks cannot use the single pass
+        fr.fr_tune_override(fr.FR_OP_SOFTMAX, form=fr.FR_FORM_SPLIT, threads=256, vec=8, passes=1)
+        with pytest.raises(fr.FrError):
+            fr.fr_plan_query(fr.FR_OP_SOFTMAX, 4, 65 * 8192, ws_bytes=1 << 30)
+        fr.fr_tune_override(fr.FR_OP_SOFTMAX, form=fr.FR_FORM_SPLIT, threads=256, vec=4)
         with pytest.raises(fr.FrError) as e:
             fr.fr_plan_query(fr.FR_OP_SOFTMAX, 512, 131072, ws_bytes=fr.fr_softmax_rows_workspace_bytes(512, 131072))
-        assert e.value.status == fr.FR_E_WORKSPACE
+        assert e.value.status == fr.FR_E_WORKSPACE  # 32 chunks per row need twice the default partials
         fr.fr_tune_override(fr.FR_OP_LAYERNORM, form=fr.FR_FORM_PER, threads=1024, vec=4)
         p = fr.fr_plan_query(fr.FR_OP_LAYERNORM, 2048, 32768, dtype=fr.FR_BF16)
         assert (p.threads, p.vec, p.occupancy) == (1024, 4, 0)
