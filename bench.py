@@ -235,7 +235,7 @@ def make_workload(name, torch, fr, synth):
         per_set = 2 * rows * cap * 4
 
         class W(Workload):
-            kernel = "fr_split_softmax_fin"
+            kernel = "fr_split_softmax_one"
             bytes = nbytes
             dtype = "f32"
 

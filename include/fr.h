@@ -90,7 +90,10 @@ typedef struct fr_plan {
     int32_t occupancy;    /* minimum waves per SIMD requested from the compiler (0: none) */
     int32_t passes;       /* reads of the input (split softmax: 1 = chunks kept in registers while the
                              row's partials are exchanged in one kernel, 2 = partial + finishing kernels) */
-    int32_t reserved;
+    int32_t wait_us;      /* single-pass split softmax: microseconds a workgroup waits for the other
+                             partials of its row before computing the missing ones itself from x (same
+                             bits); in an override 0 means the default, and < 0 makes every workgroup
+                             compute all partials of its row itself (a test of that path) */
     int64_t grid;         /* workgroups of the main kernel */
     int64_t grid2;        /* workgroups of the finishing kernel (0: none) */
     uint64_t ws_bytes;    /* workspace bytes this plan uses */
@@ -120,7 +123,7 @@ int fr_force_form(int form);
 /* Tuning hook ("Stax (4)", 9.6, Algorithm 9.1: time candidate launch
  * configurations and keep the fastest). Every later call of operation `op`
  * uses the form and launch knobs of `plan` (form, threads, seg, vec,
- * rows_per_wg, chunk, occupancy); grid, splits and workspace size are
+ * rows_per_wg, chunk, occupancy, passes, wait_us); grid, splits and workspace size are
  * recomputed for each call's shape. A candidate that cannot serve a shape,
  * or has no compiled kernel, makes that call return FR_E_ARG; a split
  * candidate needing more workspace than given returns FR_E_WORKSPACE.
@@ -164,6 +167,11 @@ uint64_t fr_sum_workspace_bytes(int64_t rows, int64_t cols, int dtype);
  *            fr_softmax_rows_workspace_bytes(rows, cols, dtype) bytes. With
  *            it, rows too long for registers may be split across
  *            workgroups; without it they are streamed by one workgroup each.
+ *            Its contents need no initialization and are overwritten; word 0
+ *            (uint32) afterwards counts the chunk partials that the
+ *            single-pass split computed a second time because their owner
+ *            had not published them within plan.wait_us (a diagnostic: the
+ *            results are the same either way).
  * A NaN in a row makes that row's outputs NaN. dtype must be FR_F32. */
 uint64_t fr_softmax_rows_workspace_bytes(int64_t rows, int64_t cols, int dtype);
 int fr_softmax_rows(const void* x, void* y, int64_t rows, int64_t cols, int64_t x_rs, int64_t x_cs, int64_t y_rs,

@@ -51,13 +51,13 @@ class fr_plan(ctypes.Structure):
         ("op", ctypes.c_int32), ("form", ctypes.c_int32), ("threads", ctypes.c_int32),
         ("seg", ctypes.c_int32), ("vec", ctypes.c_int32), ("rows_per_wg", ctypes.c_int32),
         ("splits", ctypes.c_int32), ("chunk", ctypes.c_int32), ("vec16", ctypes.c_int32),
-        ("occupancy", ctypes.c_int32), ("passes", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("occupancy", ctypes.c_int32), ("passes", ctypes.c_int32), ("wait_us", ctypes.c_int32),
         ("grid", ctypes.c_int64), ("grid2", ctypes.c_int64),
         ("ws_bytes", ctypes.c_uint64),
     ]
 
     def as_dict(self):
-        return {name: getattr(self, name) for name, _ in self._fields_ if name != "reserved"}
+        return {name: getattr(self, name) for name, _ in self._fields_}
 
 
 def _load():

@@ -39,12 +39,13 @@ constexpr int kMaxDevices = 64;
 struct DeviceInfo {
     int state = 0;  // 0 unknown, 1 usable gfx950, -1 unusable
     int num_cus = 0;
+    int clock_khz = 0;  // constant wall clock read by wall_clock64()
 };
 DeviceInfo g_dev[kMaxDevices];
 std::mutex g_dev_mu;
 
 // Current device: usable gfx950? Queried once per device, then cached.
-int device_check(int* num_cus) {
+int device_check(int* num_cus, int* clock_khz = nullptr) {
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FR_E_DEVICE;
     std::lock_guard<std::mutex> lock(g_dev_mu);
@@ -56,10 +57,15 @@ int device_check(int* num_cus) {
         } else {
             d.state = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
             d.num_cus = prop.multiProcessorCount;
+            int khz = 0;
+            if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz <= 0)
+                khz = 100000;  // the documented 100 MHz constant clock
+            d.clock_khz = khz;
         }
     }
     if (d.state != 1) return FR_E_DEVICE;
     *num_cus = d.num_cus;
+    if (clock_khz) *clock_khz = d.clock_khz;
     return FR_OK;
 }
 
@@ -246,15 +252,16 @@ int fr_softmax_rows(const void* x, void* y, int64_t rows, int64_t cols, int64_t 
         if (!aligned(ws, 16)) return FR_E_ALIGN;
         if (cols > 0 && ws_bytes < softmax_split_ws(rows, cols)) return FR_E_WORKSPACE;
     }
-    int num_cus = 0;
-    st = device_check(&num_cus);
+    int num_cus = 0, clock_khz = 0;
+    st = device_check(&num_cus, &clock_khz);
     if (st != FR_OK) return st;
     const int v16 = vec_ok(x, x_rs, 4) && vec_ok(y, y_rs, 4);
     fr_plan plan;
     st = make_plan(FR_OP_SOFTMAX, rows, cols, FR_F32, num_cus, lengths != nullptr, ws ? ws_bytes : 0, v16,
                    g_forced_form, override_for(FR_OP_SOFTMAX), &plan);
     if (st != FR_OK) return st;
-    SoftmaxArgs args{(const float*)x, (float*)y, (int)rows, (int)cols, x_rs, y_rs, lengths, argmax, ws};
+    const int64_t wait_ticks = plan.wait_us > 0 ? (int64_t)plan.wait_us * clock_khz / 1000 : (plan.wait_us < 0 ? -1 : 0);
+    SoftmaxArgs args{(const float*)x, (float*)y, (int)rows, (int)cols, x_rs, y_rs, lengths, argmax, ws, wait_ticks};
     (void)hipGetLastError();
     return finish_launch(launch_softmax(plan, args, (hipStream_t)stream));
 }

@@ -28,7 +28,8 @@ struct SoftmaxArgs {
     int64_t x_rs, y_rs;
     const int32_t* lengths;  // nullable
     int32_t* argmax;         // nullable
-    void* ws;                // split form: rows x splits partial states
+    void* ws;                // split form: header + rows x splits partial states
+    int64_t wait_ticks;      // single-pass split: wall-clock ticks a workgroup waits for a row's partials
 };
 
 struct LayerNormArgs {
@@ -43,6 +44,13 @@ struct LayerNormArgs {
 
 // Partial state of one chunk of a split softmax row: the (m, d) pair of the
 // chunk and the first index of its maximum. 16 bytes, 16-byte aligned.
+// Workspace of the split softmax: a header of kSplitWsHeader bytes (word 0:
+// partials the single pass computed for another workgroup), then one
+// 16-byte partial slot per chunk.
+constexpr int kSplitWsHeader = 64;
+// The single pass keeps per-row chunk counts in LDS: at most this many rows.
+constexpr int kOnePassMaxRows = 2048;
+
 struct alignas(16) SoftmaxPartial {
     float m, d;
     int32_t idx, pad;

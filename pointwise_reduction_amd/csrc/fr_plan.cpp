@@ -17,6 +17,8 @@
 // 32K-element bf16 row in registers (32 VGPRs of packed bf16 per lane).
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "fr_internal.h"
 
 namespace fr {
@@ -62,13 +64,16 @@ struct Knobs {
     int chunk = 0;   // elements per split chunk (sum split)
     int occ = 0;     // minimum waves per SIMD (persistent LayerNorm)
     int passes = 0;  // split softmax: 1 single read with in-kernel exchange, 2 two kernels, 0 automatic
+    int wait_us = 0; // single-pass split softmax: wait for a row's partials (0 default, < 0 none)
     int num_cus = 0; // device compute units (sizes persistent grids only; results do not depend on it)
 };
 
-// Single-pass split softmax: workgroups wait for the other chunks of their
-// row, which needs more resident workgroups than chunks per row.
-constexpr int kFusedMaxSplits = 64;
-constexpr int kFusedWgsPerCu = 8;
+// Single-pass split softmax: resident waves per SIMD (the compiler's
+// occupancy for the 256-thread, 8-vector kernel; the grid is sized so that
+// every workgroup is resident at once) and the default wait before a
+// workgroup computes a missing partial itself.
+constexpr int kOnePassWavesPerSimd = 5;
+constexpr int kOnePassWaitUs = 200;
 
 // Persistent fp32 geometry: the smallest lane group (8..64 lanes) whose
 // 16-byte vectors cover the row with at most 8 vectors per lane.
@@ -120,28 +125,25 @@ int finalize_plan(int op, int64_t rows, int64_t cols, const Knobs& k, fr_plan* p
         if (op == FR_OP_SOFTMAX) {
             const int64_t chunk = (int64_t)k.threads * 4 * k.vec;
             const int64_t s = cdiv(cols, chunk);
-            const bool one_ok = s <= kFusedMaxSplits && rows * s < (int64_t(1) << 31);
-            // Two kernels by default: measured on MI355X (512 ragged rows of up
-            // to 131071), the single pass is 2.4x slower - every workgroup
-            // serializes one load / publish / wait / merge latency chain per
-            // chunk, while the two-kernel form overlaps all chunks.
-            const int passes = k.passes == 0 ? 2 : k.passes;
+            // One kernel by default where the row lengths fit in LDS: measured
+            // on MI355X (512 ragged rows of up to 131071), it takes 0.78x the
+            // time of the two-kernel form, which reads x twice.
+            const bool one_ok = rows <= kOnePassMaxRows && rows * s < (int64_t(1) << 31);
+            const int passes = k.passes == 0 ? (one_ok ? 1 : 2) : k.passes;
             if (passes != 1 && passes != 2) return FR_E_ARG;
             if (passes == 1 && !one_ok) return FR_E_ARG;
             p->splits = (int)s;
             p->chunk = (int)chunk;
             p->passes = passes;
-            const int64_t parts = rows * s * (int64_t)sizeof(SoftmaxPartial);
-            const uint64_t ws_one = (uint64_t)(64 + cdiv(rows * 4, 16) * 16 + parts);
+            p->ws_bytes = (uint64_t)(kSplitWsHeader + rows * s * (int64_t)sizeof(SoftmaxPartial));
             if (passes == 1) {
-                // persistent grid claiming chunks by ticket; the prep kernel is not counted
-                p->grid = min64(rows * s, (int64_t)(k.num_cus > 0 ? k.num_cus : 256) * kFusedWgsPerCu);
+                const int64_t per_cu = std::max(1, kOnePassWavesPerSimd * 4 / (k.threads / 64));
+                p->grid = min64(rows * s, (int64_t)(k.num_cus > 0 ? k.num_cus : 256) * per_cu);
                 p->grid2 = 0;
-                p->ws_bytes = ws_one;
+                p->wait_us = k.wait_us == 0 ? kOnePassWaitUs : k.wait_us;
             } else {
                 p->grid = rows * s;
                 p->grid2 = rows * s;
-                p->ws_bytes = (uint64_t)parts;
             }
         } else {
             const int64_t step = (int64_t)k.threads * 4 * k.vec;
@@ -290,6 +292,7 @@ int make_plan(int op, int64_t rows, int64_t cols, int dtype, int num_cus, int ha
         k.chunk = override_plan->chunk;
         k.occ = override_plan->occupancy;
         k.passes = override_plan->passes;
+        k.wait_us = override_plan->wait_us;
     }
     k.num_cus = num_cus;
     const int st = finalize_plan(op, rows, cols, k, p);

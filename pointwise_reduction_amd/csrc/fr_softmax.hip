@@ -212,18 +212,17 @@ __global__ __launch_bounds__(T) void fr_red_softmax_f32(const float* x, float* y
 }
 
 // ------------------------------------------------------------------ split
-// Chunk c of row r (workgroup r * S + c) covers [c * C, min(len_r, (c+1) * C))
-// with C = 4 * T * NV. Part 1 keeps the chunk in registers and writes its
-// partial (m, d, first index of m). Part 2 merges the row's partials in chunk
-// order, writes the argmax (chunk 0) and the normalized chunk. A chunk wholly
-// inside its row is loaded without masks.
+// Chunk c of a row covers [c * C, min(len, (c+1) * C)) with C = 4 * T * NV.
+// Its partial state is (m, d, i): the chunk maximum, the sum of e^(x - m)
+// over the chunk and the first index of m ("Stax (4)", 9.5, Proposition 9.1:
+// the (m, d) states of any segmentation of the row merge into the row's).
+// A chunk wholly inside its row is loaded without masks.
+
+// Partial of a chunk held in registers (all threads return it).
 template <int M, int T, int NV>
-__device__ __forceinline__ void part_body(const float* xr, int start, int end, SoftmaxPartial* out, float* sl_m,
-                                          float* sl_d, int* sl_i) {
+__device__ __forceinline__ SoftmaxPartial chunk_partial(const f32x4* v, int start, int end, float* sl_m, float* sl_d,
+                                                        int* sl_i) {
     const int tid = threadIdx.x;
-    f32x4 v[NV];
-#pragma unroll
-    for (int k = 0; k < NV; ++k) v[k] = load4m<M, false>(xr, start + (k * T + tid) * 4, end, -INFINITY);
     float m = -INFINITY;
 #pragma unroll
     for (int k = 0; k < NV; ++k) m = max4(m, v[k]);
@@ -247,9 +246,62 @@ __device__ __forceinline__ void part_body(const float* xr, int start, int end, S
     cand = block_fold(cand, sl_i, T / kWave, OpMinI());
     s = group_reduce<kWave>(s, OpSum());
     s = block_fold(s, sl_d, T / kWave, OpSum());
-    if (tid == 0) *out = SoftmaxPartial{m, s, cand, 0};
+    return SoftmaxPartial{m, s, cand, 0};
 }
 
+// The same partial with the chunk read from memory one vector at a time, so
+// that it needs no second register copy of a chunk. Every thread performs
+// the operations of chunk_partial in the same order on the same values, so
+// the bits are those of chunk_partial.
+template <int M, int T, int NV>
+__device__ SoftmaxPartial chunk_partial_streamed(const float* xr, int start, int end, float* sl_m, float* sl_d,
+                                                 int* sl_i) {
+    const int tid = threadIdx.x;
+    float m = -INFINITY;
+#pragma unroll 1
+    for (int k = 0; k < NV; ++k) m = max4(m, load4m<M, false>(xr, start + (k * T + tid) * 4, end, -INFINITY));
+    m = group_reduce<kWave>(m, OpMax());
+    m = block_fold(m, sl_m, T / kWave, OpMax());
+    int cand = INT_MAX;
+    float s = 0.f;
+#pragma unroll 1
+    for (int k = NV - 1; k >= 0; --k) {
+        const f32x4 v = load4m<M, false>(xr, start + (k * T + tid) * 4, end, -INFINITY);
+#pragma unroll
+        for (int c = 3; c >= 0; --c) {
+            const int j = start + (k * T + tid) * 4 + c;
+            if (j < end && is_max(comp(v, c), m)) cand = j;
+        }
+    }
+#pragma unroll 1
+    for (int k = 0; k < NV; ++k) {
+        const f32x4 v = load4m<M, false>(xr, start + (k * T + tid) * 4, end, -INFINITY);
+        const f32x4 e = M == kNone ? exp4(v, m) : exp4_masked(v, m, start + (k * T + tid) * 4, end);
+        s += (e.x + e.y) + (e.z + e.w);
+    }
+    cand = group_reduce<kWave>(cand, OpMinI());
+    cand = block_fold(cand, sl_i, T / kWave, OpMinI());
+    s = group_reduce<kWave>(s, OpSum());
+    s = block_fold(s, sl_d, T / kWave, OpSum());
+    return SoftmaxPartial{m, s, cand, 0};
+}
+
+template <int M, int T, int NV, bool NT>
+__device__ __forceinline__ void load_chunk(const float* xr, int start, int end, f32x4* v) {
+#pragma unroll
+    for (int k = 0; k < NV; ++k) v[k] = load4m<M, NT>(xr, start + (k * T + (int)threadIdx.x) * 4, end, -INFINITY);
+}
+
+template <int M, int T, int NV>
+__device__ __forceinline__ void store_chunk(float* yr, int start, int end, const f32x4* v, float mx, float inv) {
+#pragma unroll
+    for (int k = 0; k < NV; ++k) store4m<M, true>(yr, start + (k * T + (int)threadIdx.x) * 4, end, exp4(v[k], mx) * inv);
+}
+
+// ---- two kernels: workgroup r * S + c takes chunk c of row r. Part 1 writes
+// the chunk's partial; part 2 merges the row's partials in chunk order,
+// writes the argmax (chunk 0) and the normalized chunk. Part 1 reads x with
+// ordinary loads so that part 2 can find it in the device caches.
 template <int T, int NV, bool VEC>
 __global__ __launch_bounds__(T) void fr_split_softmax_part(const float* __restrict__ x, int rows, int cols,
                                                            int64_t x_rs, const int32_t* __restrict__ lengths,
@@ -267,18 +319,23 @@ __global__ __launch_bounds__(T) void fr_split_softmax_part(const float* __restri
     if (start >= L) return;
     const int end = min(L, start + C);
     const float* xr = x + (int64_t)r * x_rs;
-    if (end - start == C) part_body<body_mask<VEC>(), T, NV>(xr, start, end, ws + w, sl_m, sl_d, sl_i);
-    else part_body<tail_mask<VEC>(), T, NV>(xr, start, end, ws + w, sl_m, sl_d, sl_i);
+    f32x4 v[NV];
+    SoftmaxPartial p;
+    if (end - start == C) {
+        load_chunk<body_mask<VEC>(), T, NV, false>(xr, start, end, v);
+        p = chunk_partial<body_mask<VEC>(), T, NV>(v, start, end, sl_m, sl_d, sl_i);
+    } else {
+        load_chunk<tail_mask<VEC>(), T, NV, false>(xr, start, end, v);
+        p = chunk_partial<tail_mask<VEC>(), T, NV>(v, start, end, sl_m, sl_d, sl_i);
+    }
+    if (threadIdx.x == 0) ws[w] = p;
 }
 
 template <int M, int T, int NV>
 __device__ __forceinline__ void fin_body(const float* xr, float* yr, int start, int end, float mx, float inv) {
-    const int tid = threadIdx.x;
     f32x4 v[NV];
-#pragma unroll
-    for (int k = 0; k < NV; ++k) v[k] = load4m<M, true>(xr, start + (k * T + tid) * 4, end, -INFINITY);
-#pragma unroll
-    for (int k = 0; k < NV; ++k) store4m<M, true>(yr, start + (k * T + tid) * 4, end, exp4(v[k], mx) * inv);
+    load_chunk<M, T, NV, true>(xr, start, end, v);
+    store_chunk<M, T, NV>(yr, start, end, v, mx, inv);
 }
 
 template <int T, int NV, bool VEC>
@@ -316,165 +373,187 @@ __global__ __launch_bounds__(T) void fr_split_softmax_fin(const float* x, float*
     else fin_body<tail_mask<VEC>(), T, NV>(xr, yr, start, end, st.m, inv);
 }
 
-// ------------------------------------------------------------------ split, single pass
-// The two-kernel split above reads every chunk twice. Here each chunk is read
-// once and kept in registers: workgroups claim chunks through an atomic
-// ticket in row-major order, publish the chunk's partial (m, d, first index
-// of m), wait until every chunk of the row has published, merge the row's
-// partials in chunk order and normalize the registers they still hold.
-//
-// Progress: a claimed ticket always belongs to a running workgroup, and a
-// workgroup publishes before it waits, so only the workgroups on the last
-// partly-claimed row can wait on unclaimed chunks; with more resident
-// workgroups than chunks per row (S <= 64 here) another workgroup claims
-// them. The wait is bounded all the same: past the spin limit the workgroup
-// stops waiting, poisons its chunk with NaN and raises the error word of the
-// workspace header, so every wave always exits.
-//
-// Visibility across XCDs: partial fields are stored and loaded with
-// agent-scope atomics, the row counter is incremented with release
-// semantics and read back with an acquire fence.
-constexpr int kFusedMaxSplits = 64;
-constexpr int kSpinLimit = 1 << 20;
+// ---- one kernel: every chunk is read once and stays in registers while the
+// row's partials are exchanged through the workspace.
+//  - Each workgroup derives the list of non-empty chunks from the row
+//    lengths (chunk counts and their exclusive prefix sum, kept in LDS), and
+//    workgroup w takes list entries w, w + G, w + 2G, ... (G = grid size):
+//    no workgroup is spent on the empty tail of a ragged row, and the chunks
+//    of one row are worked on at the same time by neighbouring workgroups.
+//  - A chunk's partial is published in its slot as two 64-bit words, (index,
+//    m) and (index, d); a slot whose index half is kUnpublished (the reset
+//    kernel's fill) is not yet written. Each word is written and read as one
+//    64-bit atomic, so a reader that sees the index sees the value beside it
+//    and no fence is needed.
+//  - A workgroup waits, up to a wall-clock limit, for the other slots of its
+//    row (a negative limit: it reads none of them). A partial still missing
+//    at the limit it computes itself from x
+//    with chunk_partial_streamed, which gives the owner's bits. Nothing
+//    depends on other workgroups being resident, so every launch finishes
+//    and the result does not depend on scheduling. Each partial computed this
+//    way is counted in the workspace header.
+//  - The row's partials are merged in a fixed order (64-lane butterflies over
+//    groups of 64 chunks, groups in order), so every chunk of a row is
+//    normalized with the same (m, d) bits.
+constexpr uint32_t kUnpublished = 0xFFFFFFFFu;
 
-struct FusedWs {
-    uint32_t* hdr;         // [0] ticket, [1] error
-    uint32_t* row_cnt;     // rows counters of published chunks
-    SoftmaxPartial* part;  // rows x S partials
-};
-
-__host__ __device__ inline FusedWs fused_layout(void* ws, int rows) {
-    char* b = static_cast<char*>(ws);
-    FusedWs f;
-    f.hdr = reinterpret_cast<uint32_t*>(b);
-    f.row_cnt = reinterpret_cast<uint32_t*>(b + 64);
-    f.part = reinterpret_cast<SoftmaxPartial*>(b + 64 + ((int64_t)rows * 4 + 15) / 16 * 16);
-    return f;
+__device__ __forceinline__ uint64_t slot_word(int idx, float v) {
+    return ((uint64_t)(uint32_t)idx << 32) | __builtin_bit_cast(uint32_t, v);
 }
+__device__ __forceinline__ bool published(uint64_t w) { return (uint32_t)(w >> 32) != kUnpublished; }
 
-__global__ __launch_bounds__(256) void fr_split_softmax_prep(uint32_t* hdr, uint32_t* row_cnt, int rows) {
-    const int i = blockIdx.x * 256 + threadIdx.x;
-    if (i < 16) hdr[i] = 0u;
-    if (i < rows) row_cnt[i] = 0u;
-}
-
-template <int M, int T, int NV>
-__device__ __forceinline__ void fused_load(const float* xr, int start, int end, f32x4* v) {
-#pragma unroll
-    for (int k = 0; k < NV; ++k) v[k] = load4m<M, true>(xr, start + (k * T + (int)threadIdx.x) * 4, end, -INFINITY);
-}
-
-template <int M, int T, int NV>
-__device__ __forceinline__ void fused_store(float* yr, int start, int end, const f32x4* v, float mx, float inv) {
-#pragma unroll
-    for (int k = 0; k < NV; ++k) store4m<M, true>(yr, start + (k * T + (int)threadIdx.x) * 4, end, exp4(v[k], mx) * inv);
+// Header words cleared, slots marked unpublished.
+__global__ __launch_bounds__(256) void fr_split_softmax_reset(uint32_t* __restrict__ hdr, u32x4* __restrict__ slots,
+                                                              int64_t nslots) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < kSplitWsHeader / 4) hdr[i] = 0u;
+    if (i < nslots) slots[i] = u32x4{~0u, ~0u, ~0u, ~0u};
 }
 
 template <int T, int NV, bool VEC>
-__global__ __launch_bounds__(T) void fr_split_softmax_fused(const float* x, float* y, int rows, int cols,
-                                                            int64_t x_rs, int64_t y_rs,
-                                                            const int32_t* __restrict__ lengths,
-                                                            int32_t* __restrict__ argmax, void* ws, int S) {
+__global__ __launch_bounds__(T) void fr_split_softmax_one(const float* x, float* y, int rows, int cols, int64_t x_rs,
+                                                          int64_t y_rs, const int32_t* __restrict__ lengths,
+                                                          int32_t* __restrict__ argmax, void* ws,
+                                                          int64_t wait_ticks) {
     constexpr int C = 4 * T * NV;
+    __shared__ int s_base[kOnePassMaxRows + 1];  // first list entry of each row; [rows] = list length
+    __shared__ int s_len[kOnePassMaxRows];
+    __shared__ int s_scan[T];
     __shared__ float sl_m[T / kWave];
     __shared__ float sl_d[T / kWave];
     __shared__ int sl_i[T / kWave];
-    __shared__ uint32_t s_ticket;
+    __shared__ uint64_t s_missing;
     __shared__ float s_max, s_inv;
-    __shared__ int s_timeout;
-    const FusedWs f = fused_layout(ws, rows);
+    uint32_t* hdr = static_cast<uint32_t*>(ws);
+    uint64_t* slots = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + kSplitWsHeader);
     const int tid = threadIdx.x;
-    const uint32_t total = (uint32_t)rows * (uint32_t)S;
-    for (;;) {
-        if (tid == 0) s_ticket = __hip_atomic_fetch_add(&f.hdr[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __syncthreads();
-        const uint32_t t = s_ticket;
-        __syncthreads();  // every thread has read the ticket before it is rewritten
-        if (t >= total) break;
-        const int r = (int)(t / (uint32_t)S);
-        const int c = (int)(t % (uint32_t)S);
+
+    // chunk list: thread tid counts the chunks of rows [r0, r1)
+    const int per = (rows + T - 1) / T;
+    const int r0 = min(rows, tid * per), r1 = min(rows, r0 + per);
+    int local = 0;
+    for (int r = r0; r < r1; ++r) {
         const int L = row_len(lengths, r, cols);
-        const int nc = (L + C - 1) / C;
-        if (c >= nc) {
-            if (c == 0 && argmax && tid == 0) argmax[r] = -1;
-            continue;
+        s_len[r] = L;
+        local += (L + C - 1) / C;
+    }
+    s_scan[tid] = local;
+    __syncthreads();
+    for (int off = 1; off < T; off <<= 1) {  // inclusive scan (Hillis-Steele)
+        const int add = tid >= off ? s_scan[tid - off] : 0;
+        __syncthreads();
+        s_scan[tid] += add;
+        __syncthreads();
+    }
+    int run = s_scan[tid] - local;
+    for (int r = r0; r < r1; ++r) {
+        s_base[r] = run;
+        run += (s_len[r] + C - 1) / C;
+    }
+    if (tid == T - 1) s_base[rows] = s_scan[T - 1];
+    __syncthreads();
+    const int total = s_base[rows];
+    if (blockIdx.x == 0 && argmax)
+        for (int r = tid; r < rows; r += T)
+            if (s_len[r] == 0) argmax[r] = -1;
+
+    for (int t = blockIdx.x; t < total; t += gridDim.x) {
+        int lo = 0, hi = rows;  // s_base[lo] <= t < s_base[hi]; rows without chunks never qualify
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (s_base[mid] <= t) lo = mid;
+            else hi = mid;
         }
+        const int r = lo;
+        const int base = s_base[r];
+        const int nc = s_base[r + 1] - base;
+        const int c = t - base;
+        const int L = s_len[r];
         const int start = c * C;
         const int end = min(L, start + C);
         const bool full = end - start == C;
         const float* xr = x + (int64_t)r * x_rs;
         f32x4 v[NV];
-        if (full) fused_load<body_mask<VEC>(), T, NV>(xr, start, end, v);
-        else fused_load<tail_mask<VEC>(), T, NV>(xr, start, end, v);
-        // chunk statistics
-        float m = -INFINITY;
-#pragma unroll
-        for (int k = 0; k < NV; ++k) m = max4(m, v[k]);
-        m = group_reduce<kWave>(m, OpMax());
-        m = block_fold(m, sl_m, T / kWave, OpMax());
-        int cand = INT_MAX;
-        float sum = 0.f;
-#pragma unroll
-        for (int k = NV - 1; k >= 0; --k)
-#pragma unroll
-            for (int cc = 3; cc >= 0; --cc) {
-                const int j = start + (k * T + tid) * 4 + cc;
-                if (j < end && is_max(comp(v[k], cc), m)) cand = j;
-            }
-#pragma unroll
-        for (int k = 0; k < NV; ++k) {
-            const f32x4 e = exp4_masked(v[k], m, start + (k * T + tid) * 4, end);
-            sum += (e.x + e.y) + (e.z + e.w);
+        SoftmaxPartial own;
+        if (full) {
+            load_chunk<body_mask<VEC>(), T, NV, true>(xr, start, end, v);
+            own = chunk_partial<body_mask<VEC>(), T, NV>(v, start, end, sl_m, sl_d, sl_i);
+        } else {
+            load_chunk<tail_mask<VEC>(), T, NV, true>(xr, start, end, v);
+            own = chunk_partial<tail_mask<VEC>(), T, NV>(v, start, end, sl_m, sl_d, sl_i);
         }
-        cand = group_reduce<kWave>(cand, OpMinI());
-        cand = block_fold(cand, sl_i, T / kWave, OpMinI());
-        sum = group_reduce<kWave>(sum, OpSum());
-        sum = block_fold(sum, sl_d, T / kWave, OpSum());
-        // publish, then wait for the rest of the row
+        uint64_t* rs = slots + 2 * (int64_t)base;
         if (tid == 0) {
-            SoftmaxPartial* p = f.part + t;
-            __hip_atomic_store(&p->m, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&p->d, sum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&p->idx, cand, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_fetch_add(&f.row_cnt[r], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-            int spins = 0;
-            while (__hip_atomic_load(&f.row_cnt[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)nc &&
-                   spins < kSpinLimit) {
-                __builtin_amdgcn_s_sleep(2);
-                ++spins;
-            }
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-            s_timeout = spins < kSpinLimit ? 0 : 1;
-            if (spins >= kSpinLimit) __hip_atomic_store(&f.hdr[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&rs[2 * c], slot_word(own.idx, own.m), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&rs[2 * c + 1], slot_word(own.idx, own.d), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        __syncthreads();
-        const bool timed_out = s_timeout != 0;
-        // merge the row's partials in chunk order (wave 0), broadcast through LDS
-        if (tid < kWave) {
-            MD st{-INFINITY, 0.f};
-            MI best{-INFINITY, INT_MAX};
-            const SoftmaxPartial* pr = f.part + (int64_t)r * S;
-            for (int k = tid; k < nc; k += kWave) {
-                const float pm = __hip_atomic_load(&pr[k].m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                const float pd = __hip_atomic_load(&pr[k].d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                const int pi = __hip_atomic_load(&pr[k].idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                st = md_combine(st, MD{pm, pd});
-                best = mi_combine(best, MI{pm, pi});
+        // merge the row's partials, 64 at a time: wave 0 gathers (lane j: chunk g0 + j)
+        MD st{-INFINITY, 0.f};
+        MI best{-INFINITY, INT_MAX};
+        for (int g0 = 0; g0 < nc; g0 += kWave) {
+            const int k = g0 + (tid & (kWave - 1));
+            uint64_t w0 = ~0ull, w1 = ~0ull;
+            if (tid < kWave) {
+                bool ok = k >= nc;
+                if (k == c) {
+                    w0 = slot_word(own.idx, own.m);
+                    w1 = slot_word(own.idx, own.d);
+                    ok = true;
+                }
+                const uint64_t t0 = wall_clock64();
+                for (; wait_ticks >= 0;) {  // < 0: read no other partial (all are recomputed)
+                    if (!ok) {
+                        if (!published(w0)) w0 = __hip_atomic_load(&rs[2 * k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        if (!published(w1))
+                            w1 = __hip_atomic_load(&rs[2 * k + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        ok = published(w0) && published(w1);
+                    }
+                    if (__all(ok)) break;
+                    if ((int64_t)(wall_clock64() - t0) >= wait_ticks) break;
+                    __builtin_amdgcn_s_sleep(2);
+                }
+                const uint64_t miss = __ballot(!ok);
+                if (tid == 0) s_missing = miss;
             }
-            st = group_reduce<kWave>(st, OpMD());
-            best = group_reduce<kWave>(best, OpMI());
-            if (tid == 0) {
-                s_max = timed_out ? NAN : st.m;
-                s_inv = 1.0f / st.d;
-                if (c == 0 && argmax) argmax[r] = timed_out ? -1 : best.i;
+            __syncthreads();
+            uint64_t miss = s_missing;
+            while (miss) {  // rare: the owner has not published in time
+                const int j = __builtin_ctzll(miss);
+                miss &= miss - 1;
+                const int ks = (g0 + j) * C;
+                const int ke = min(L, ks + C);
+                const SoftmaxPartial p =
+                    ke - ks == C ? chunk_partial_streamed<body_mask<VEC>(), T, NV>(xr, ks, ke, sl_m, sl_d, sl_i)
+                                 : chunk_partial_streamed<tail_mask<VEC>(), T, NV>(xr, ks, ke, sl_m, sl_d, sl_i);
+                if (tid == j) {
+                    w0 = slot_word(p.idx, p.m);
+                    w1 = slot_word(p.idx, p.d);
+                }
+                if (tid == 0) __hip_atomic_fetch_add(&hdr[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
+            if (tid < kWave) {
+                MD a{-INFINITY, 0.f};
+                MI b{-INFINITY, INT_MAX};
+                if (k < nc) {
+                    const float pm = __builtin_bit_cast(float, (uint32_t)w0);
+                    a = MD{pm, __builtin_bit_cast(float, (uint32_t)w1)};
+                    b = MI{pm, (int)(uint32_t)(w0 >> 32)};
+                }
+                st = md_combine(st, group_reduce<kWave>(a, OpMD()));
+                best = mi_combine(best, group_reduce<kWave>(b, OpMI()));
+            }
+            __syncthreads();  // s_missing and the fold slots are rewritten next
+        }
+        if (tid == 0) {
+            s_max = st.m;
+            s_inv = 1.0f / st.d;
+            if (c == 0 && argmax) argmax[r] = best.i;
         }
         __syncthreads();
         const float mx = s_max, inv = s_inv;
         float* yr = y + (int64_t)r * y_rs;
-        if (full) fused_store<body_mask<VEC>(), T, NV>(yr, start, end, v, mx, inv);
-        else fused_store<tail_mask<VEC>(), T, NV>(yr, start, end, v, mx, inv);
-        __syncthreads();  // LDS slots and broadcasts are rewritten by the next chunk
+        if (full) store_chunk<body_mask<VEC>(), T, NV>(yr, start, end, v, mx, inv);
+        else store_chunk<tail_mask<VEC>(), T, NV>(yr, start, end, v, mx, inv);
     }
 }
 
@@ -531,13 +610,13 @@ SmFn pick_red(int threads, int u) {
     return nullptr;
 }
 
-using FusedFn = void (*)(const float*, float*, int, int, int64_t, int64_t, const int32_t*, int32_t*, void*, int);
+using OneFn = void (*)(const float*, float*, int, int, int64_t, int64_t, const int32_t*, int32_t*, void*, int64_t);
 
 template <bool VEC>
-FusedFn pick_fused(int threads, int nv) {
-    if (threads == 256 && nv == 8) return fr_split_softmax_fused<256, 8, VEC>;
-    if (threads == 256 && nv == 4) return fr_split_softmax_fused<256, 4, VEC>;
-    if (threads == 512 && nv == 4) return fr_split_softmax_fused<512, 4, VEC>;
+OneFn pick_one(int threads, int nv) {
+    if (threads == 256 && nv == 8) return fr_split_softmax_one<256, 8, VEC>;
+    if (threads == 256 && nv == 4) return fr_split_softmax_one<256, 4, VEC>;
+    if (threads == 512 && nv == 4) return fr_split_softmax_one<512, 4, VEC>;
     return nullptr;
 }
 
@@ -581,16 +660,17 @@ hipError_t launch_softmax(const fr_plan& p, const SoftmaxArgs& a, hipStream_t s)
         return hipGetLastError();
     }
     if (p.form == FR_FORM_SPLIT && p.passes == 1) {
-        if (p.splits > kFusedMaxSplits) return hipErrorInvalidDeviceFunction;
-        FusedFn fused = vec ? pick_fused<true>(p.threads, p.vec) : pick_fused<false>(p.threads, p.vec);
-        if (!fused) return hipErrorInvalidDeviceFunction;
-        const FusedWs f = fused_layout(a.ws, a.rows);
-        hipLaunchKernelGGL(fr_split_softmax_prep, dim3((unsigned)((a.rows + 16 + 255) / 256)), dim3(256), 0, s, f.hdr,
-                           f.row_cnt, a.rows);
+        if (a.rows > kOnePassMaxRows) return hipErrorInvalidDeviceFunction;
+        OneFn one = vec ? pick_one<true>(p.threads, p.vec) : pick_one<false>(p.threads, p.vec);
+        if (!one) return hipErrorInvalidDeviceFunction;
+        const int64_t nslots = (int64_t)a.rows * p.splits;
+        hipLaunchKernelGGL(fr_split_softmax_reset, dim3((unsigned)((nslots + 255) / 256)), dim3(256), 0, s,
+                           static_cast<uint32_t*>(a.ws),
+                           reinterpret_cast<u32x4*>(static_cast<char*>(a.ws) + kSplitWsHeader), nslots);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(fused, dim3((unsigned)p.grid), dim3(p.threads), 0, s, a.x, a.y, a.rows, a.cols, a.x_rs,
-                           a.y_rs, a.lengths, a.argmax, a.ws, p.splits);
+        hipLaunchKernelGGL(one, dim3((unsigned)p.grid), dim3(p.threads), 0, s, a.x, a.y, a.rows, a.cols, a.x_rs,
+                           a.y_rs, a.lengths, a.argmax, a.ws, a.wait_ticks);
         return hipGetLastError();
     }
     if (p.form == FR_FORM_SPLIT) {
@@ -599,7 +679,7 @@ hipError_t launch_softmax(const fr_plan& p, const SoftmaxArgs& a, hipStream_t s)
         if (vec) pick_split<true>(p.threads, p.vec, &part, &fin);
         else pick_split<false>(p.threads, p.vec, &part, &fin);
         if (!part || !fin) return hipErrorInvalidDeviceFunction;
-        SoftmaxPartial* ws = static_cast<SoftmaxPartial*>(a.ws);
+        SoftmaxPartial* ws = reinterpret_cast<SoftmaxPartial*>(static_cast<char*>(a.ws) + kSplitWsHeader);
         hipLaunchKernelGGL(part, dim3((unsigned)p.grid), dim3(p.threads), 0, s, a.x, a.rows, a.cols, a.x_rs,
                            a.lengths, ws, p.splits);
         hipError_t e = hipGetLastError();

@@ -34,8 +34,7 @@ def run(x_np, lengths=None, form=fr.FR_FORM_AUTO, use_ws=None, cols=None, y_fill
         use_ws = form == fr.FR_FORM_SPLIT
     ws = None
     if use_ws:
-        # room for either split variant (the single pass adds a header and row counters)
-        nbytes = fr.fr_softmax_rows_workspace_bytes(rows, cols) + 64 + 4 * rows + 64
+        nbytes = fr.fr_softmax_rows_workspace_bytes(rows, cols)
         ws = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
     with forced(form):
         fr.fr_softmax_rows(x, y, lengths=L, argmax=am, ws=ws)
@@ -202,11 +201,13 @@ def test_softmax_is_deterministic():
 
 
 @pytest.mark.parametrize("passes", [1, 2])
-@pytest.mark.parametrize("cols", [8193, 50257, 131071, 140000])
+@pytest.mark.parametrize("cols", [8193, 50257, 131071, 140000, 600001])
 def test_softmax_split_passes(passes, cols):
     """Both split variants: one read with the row's partials exchanged inside
-    one kernel, and the partial + finishing kernels."""
-    x, L = synth.ragged_softmax_inputs(24, cols, seed=2900 + cols, choices=(1, 4000, cols - 7, cols))
+    one kernel, and the partial + finishing kernels. 600001 columns make 74
+    chunks per row (more than one 64-lane merge group)."""
+    rows = 24 if cols < 600000 else 5
+    x, L = synth.ragged_softmax_inputs(rows, cols, seed=2900 + cols, choices=(1, 4000, cols - 7, cols))
     try:
         fr.fr_tune_override(fr.FR_OP_SOFTMAX, form=fr.FR_FORM_SPLIT, threads=256, vec=8, passes=passes)
         y, am, yfull = run(x, lengths=L, use_ws=True)
@@ -217,24 +218,32 @@ def test_softmax_split_passes(passes, cols):
         assert np.isnan(yfull[r, n:]).all()
 
 
-def test_softmax_single_pass_workspace_reports_no_timeout():
-    x, L = synth.ragged_softmax_inputs(512, 131072, seed=5001)
+@pytest.mark.parametrize("shape", [(64, 131072), (3, 600001)], ids=["64x131072", "3x600001"])
+def test_softmax_single_pass_fallback_gives_the_same_bits(shape):
+    """In the single pass a workgroup that stops waiting computes the missing
+    partials of its row from x itself. Forced for every partial (wait_us < 0),
+    y and the argmax keep their bits, and the workspace header counts each
+    recomputed partial: sum over rows of nc * (nc - 1). With the default wait
+    on an idle device nothing is recomputed. The workspace starts as garbage:
+    the reset kernel clears it."""
+    rows, cols = shape
+    x, L = synth.ragged_softmax_inputs(rows, cols, seed=2950 + rows, choices=(1000, cols // 2 + 3, cols - 1, cols))
     xd, Ld = dev(x), dev(L)
-    y = torch.empty_like(xd)
-    nbytes = 64 + 512 * 4 + 512 * 16 * 16
-    ws = torch.full((nbytes // 4,), 0x7FFFFFFF, dtype=torch.int32, device="cuda")  # garbage in the header
-    outs = []
+    nbytes = fr.fr_softmax_rows_workspace_bytes(rows, cols)
+    ws = torch.full((nbytes // 4,), 0x5A5A5A5A, dtype=torch.int32, device="cuda")
+    outs = {}
     try:
-        fr.fr_tune_override(fr.FR_OP_SOFTMAX, form=fr.FR_FORM_SPLIT, threads=256, vec=8, passes=1)
-        plan = fr.fr_plan_query(fr.FR_OP_SOFTMAX, 512, 131072, has_lengths=True, ws_bytes=nbytes)
-        assert plan.passes == 1 and plan.ws_bytes == nbytes
-        for _ in range(3):
-            fr.fr_softmax_rows(xd, y, lengths=Ld, ws=ws)
-            outs.append(host(y).copy())
-            assert int(host(ws)[1]) == 0, "a workgroup gave up waiting for its row"
+        for wait in (0, -1):
+            fr.fr_tune_override(fr.FR_OP_SOFTMAX, form=fr.FR_FORM_SPLIT, threads=256, vec=8, passes=1, wait_us=wait)
+            y = torch.full_like(xd, float("nan"))
+            am = torch.full((rows,), -7, dtype=torch.int32, device="cuda")
+            fr.fr_softmax_rows(xd, y, lengths=Ld, argmax=am, ws=ws)
+            outs[wait] = (host(y), host(am), int(host(ws)[0]))
     finally:
         fr.fr_tune_override(fr.FR_OP_SOFTMAX)
-    assert all(np.array_equal(outs[0].view(np.uint32), o.view(np.uint32)) for o in outs[1:])
-    y64, _ = oracle.softmax_rows(x, lengths=L)
-    written = valid_mask(512, 131072, L)
-    check_fp32(np.where(written, outs[0], 0.0), np.where(written, y64, 0.0), what="single pass")
+    nc = (np.asarray(L, dtype=np.int64) + 8191) // 8192
+    assert outs[0][2] == 0, "a workgroup recomputed a partial with the default wait"
+    assert outs[-1][2] == int((nc * (nc - 1)).sum())
+    assert np.array_equal(outs[0][0].view(np.uint32), outs[-1][0].view(np.uint32))
+    assert np.array_equal(outs[0][1], outs[-1][1])
+    compare(x, outs[0][0], outs[0][1], lengths=L, what=f"single pass {rows}x{cols}")

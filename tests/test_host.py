@@ -144,20 +144,28 @@ def test_plans_for_the_five_workloads():
     assert ws == 2048 * 4
     p = fr.fr_plan_query(fr.FR_OP_SUMSQ, 1, n, ws_bytes=ws)
     assert (p.form, p.splits, p.chunk, p.grid, p.grid2) == (fr.FR_FORM_SPLIT, 2048, 1 << 17, 2048, 1)
-    # ragged softmax, 512 rows of capacity 131072, with a workspace: 16 chunks of 8192
-    # (two kernels: 512 x 16 partials of 16 bytes)
+    # ragged softmax, 512 rows of capacity 131072, with a workspace: 16 chunks of 8192, a
+    # 64-byte header and 512 x 16 partial slots of 16 bytes; one kernel whose grid is every
+    # workgroup that can be resident at once (5 per CU at 256 threads), waiting 200 us by default
     ws = fr.fr_softmax_rows_workspace_bytes(512, 131072)
-    assert ws == 512 * 16 * 16
+    assert ws == 64 + 512 * 16 * 16
     p = fr.fr_plan_query(fr.FR_OP_SOFTMAX, 512, 131072, has_lengths=True, ws_bytes=ws)
-    assert (p.form, p.splits, p.chunk, p.passes, p.grid, p.grid2) == (fr.FR_FORM_SPLIT, 16, 8192, 2, 8192, 8192)
-    # the single pass (a tuning candidate) adds a 64-byte header and 512 row counters, and a
-    # persistent grid of 8 workgroups per CU claims the chunks
-    fr.fr_tune_override(fr.FR_OP_SOFTMAX, form=fr.FR_FORM_SPLIT, threads=256, vec=8, passes=1)
+    assert (p.form, p.splits, p.chunk, p.passes, p.grid, p.grid2, p.wait_us) == \
+        (fr.FR_FORM_SPLIT, 16, 8192, 1, 256 * 5, 0, 200)
+    # the two-kernel form (a tuning candidate) uses the same workspace
+    fr.fr_tune_override(fr.FR_OP_SOFTMAX, form=fr.FR_FORM_SPLIT, threads=256, vec=8, passes=2)
     try:
-        p = fr.fr_plan_query(fr.FR_OP_SOFTMAX, 512, 131072, has_lengths=True, ws_bytes=1 << 20)
-        assert (p.passes, p.grid, p.grid2, p.ws_bytes) == (1, 2048, 0, 64 + 512 * 4 + 512 * 16 * 16)
+        p = fr.fr_plan_query(fr.FR_OP_SOFTMAX, 512, 131072, has_lengths=True, ws_bytes=ws)
+        assert (p.passes, p.grid, p.grid2, p.ws_bytes, p.wait_us) == (2, 8192, 8192, ws, 0)
     finally:
         fr.fr_tune_override(fr.FR_OP_SOFTMAX)
+    # more rows than the single pass keeps in LDS: two kernels
+    fr.fr_force_form(fr.FR_FORM_SPLIT)
+    try:
+        p = fr.fr_plan_query(fr.FR_OP_SOFTMAX, 3000, 131072, ws_bytes=1 << 30)
+        assert (p.form, p.passes, p.grid) == (fr.FR_FORM_SPLIT, 2, 3000 * 16)
+    finally:
+        fr.fr_force_form(fr.FR_FORM_AUTO)
     # ... and without one: one workgroup streams each row
     p = fr.fr_plan_query(fr.FR_OP_SOFTMAX, 512, 131072, has_lengths=True)
     assert (p.form, p.threads, p.grid) == (fr.FR_FORM_RED, 512, 512)
@@ -229,14 +237,17 @@ def test_tune_override_replaces_the_launch_knobs():
         # a split candidate with smaller chunks needs more workspace than the default query gives
         fr.fr_tune_override(fr.FR_OP_SOFTMAX, form=fr.FR_FORM_SPLIT, threads=256, vec=4)
         p = fr.fr_plan_query(fr.FR_OP_SOFTMAX, 512, 131072, ws_bytes=1 << 30)
-        assert (p.splits, p.chunk, p.passes) == (32, 4096, 2)
+        assert (p.splits, p.chunk, p.passes) == (32, 4096, 1)
         fr.fr_tune_override(fr.FR_OP_SOFTMAX, form=fr.FR_FORM_SPLIT, threads=256, vec=8, passes=2)
         p = fr.fr_plan_query(fr.FR_OP_SOFTMAX, 512, 131072, ws_bytes=1 << 30)
-        assert (p.splits, p.passes, p.grid, p.grid2, p.ws_bytes) == (16, 2, 8192, 8192, 512 * 16 * 16)
-        # rows with more than 64 chunks cannot use the single pass
-        fr.fr_tune_override(fr.FR_OP_SOFTMAX, form=fr.FR_FORM_SPLIT, threads=256, vec=8, passes=1)
+        assert (p.splits, p.passes, p.grid, p.grid2, p.ws_bytes) == (16, 2, 8192, 8192, 64 + 512 * 16 * 16)
+        # the single pass with 512 threads: 2 resident workgroups per CU; wait overrides pass through
+        fr.fr_tune_override(fr.FR_OP_SOFTMAX, form=fr.FR_FORM_SPLIT, threads=512, vec=4, passes=1, wait_us=-1)
+        p = fr.fr_plan_query(fr.FR_OP_SOFTMAX, 512, 131072, ws_bytes=1 << 30)
+        assert (p.splits, p.passes, p.grid, p.wait_us) == (16, 1, 512, -1)
+        # more rows than the single pass keeps in LDS
         with pytest.raises(fr.FrError):
-            fr.fr_plan_query(fr.FR_OP_SOFTMAX, 4, 65 * 8192, ws_bytes=1 << 30)
+            fr.fr_plan_query(fr.FR_OP_SOFTMAX, 2049, 65 * 8192, ws_bytes=1 << 40)
         fr.fr_tune_override(fr.FR_OP_SOFTMAX, form=fr.FR_FORM_SPLIT, threads=256, vec=4)
         with pytest.raises(fr.FrError) as e:
             fr.fr_plan_query(fr.FR_OP_SOFTMAX, 512, 131072, ws_bytes=fr.fr_softmax_rows_workspace_bytes(512, 131072))
