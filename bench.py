@@ -299,6 +299,49 @@ def make_workload(name, torch, fr, synth):
 
         return W(), per_set
 
+    if name in ("stream_copy", "stream_copy_c3", "stream_read"):
+        # practical ceilings: the library's streaming reference kernels over the
+        # bytes of the softmax 4096x1024 step (16 MiB in, 16 MiB out), of the
+        # LayerNorm 2048x32768 bf16 step (128 MiB in, 128 MiB out), or a
+        # read-only pass over the softmax input
+        nin = 16 << 20 if name != "stream_copy_c3" else 128 << 20
+        reads_only = name == "stream_read"
+        per_set = nin if reads_only else 2 * nin
+
+        class W(Workload):
+            kernel = "fr_stream_read_k" if reads_only else "fr_stream_copy_k"
+            bytes = nin if reads_only else 2 * nin
+            dtype = "u8"
+
+            def alloc(self, sets):
+                x0 = torch.randint(-2**31, 2**31 - 1, (nin // 4,), dtype=torch.int32, device=dev)
+                self.args = [(x0 if i == 0 else x0.clone(),
+                              torch.zeros(fr.FR_STREAM_SINK_WORDS, dtype=torch.int32, device=dev) if reads_only
+                              else torch.empty_like(x0)) for i in range(sets)]
+
+            def launch(self, k):
+                x, out = self.args[k]
+                if reads_only:
+                    fr.fr_stream_read(x, out)
+                else:
+                    fr.fr_stream_copy(x, out)
+
+            def output(self, k):
+                return self.args[k][1]
+
+            def config(self):
+                what = {"stream_copy": "streaming copy of 16 MiB (the bytes of the softmax 4096x1024 step)",
+                        "stream_copy_c3": "streaming copy of 128 MiB (the bytes of the LayerNorm 2048x32768 "
+                                          "bf16 step)",
+                        "stream_read": "streaming read of 16 MiB (the softmax 4096x1024 input)"}[name]
+                return {"workload": what + ", the practical ceiling", "bytes_in": nin}
+
+            def oracle_fn(self):
+                x = np.zeros(nin // 4, dtype=np.int32)
+                return lambda: x.copy(), self.bytes, "numpy copy of the same size"
+
+        return W(), per_set
+
     raise SystemExit(f"unknown workload {name}")
 
 
@@ -349,7 +392,8 @@ def main():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="softmax",
-                    choices=["softmax", "sum_relu_add", "layernorm", "sumsq", "ragged", "copy"])
+                    choices=["softmax", "sum_relu_add", "layernorm", "sumsq", "ragged", "copy", "stream_copy",
+                             "stream_copy_c3", "stream_read"])
     ap.add_argument("--warm", action="store_true", help="one buffer set: reads may hit the MALL")
     ap.add_argument("--eager", action="store_true", help="launch each step from the host (no graph)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)

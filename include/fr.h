@@ -208,6 +208,21 @@ int fr_sumsq_rows(const void* x, void* out, int64_t rows, int64_t cols, int64_t 
 uint64_t fr_sumsq_full_workspace_bytes(int64_t n, int dtype);
 int fr_sumsq_full(const void* x, int64_t n, void* out, void* ws, uint64_t ws_bytes, int dtype, void* stream);
 
+/* ------------------------------------------------------------ streaming references
+ * The practical ceiling of an HBM-bound step ("Stax (4)", 9.1: memory-bound
+ * kernels are judged by the bandwidth they reach): the plainest kernels that
+ * move the same bytes with the same access hints, timed by the same harness.
+ * fr_stream_copy: y = x, nbytes bytes; x and y 16-byte aligned and not
+ *   overlapping, nbytes a multiple of 16 (FR_E_ALIGN / FR_E_SIZE otherwise).
+ * fr_stream_read: reads nbytes of x (same rules) and writes to sink[w], for
+ *   each of its workgroups w, the XOR of all 32-bit words that workgroup
+ *   read; the XOR of sink[0 .. FR_STREAM_SINK_WORDS) is then the XOR of all
+ *   words of x (unused entries are not written: clear them first). sink:
+ *   device array of FR_STREAM_SINK_WORDS uint32. */
+#define FR_STREAM_SINK_WORDS 1024
+int fr_stream_copy(const void* x, void* y, int64_t nbytes, void* stream);
+int fr_stream_read(const void* x, int64_t nbytes, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -37,6 +37,7 @@ EXPORTS = (
     "fr_softmax_rows_workspace_bytes", "fr_softmax_rows",
     "fr_layernorm_rows",
     "fr_sumsq_rows", "fr_sumsq_full_workspace_bytes", "fr_sumsq_full",
+    "fr_stream_copy", "fr_stream_read",
 )
 
 
@@ -80,6 +81,8 @@ def _load():
         "fr_sumsq_rows": (I32, [P, P, I64, I64, I64, I64, P, U64, I32, P]),
         "fr_sumsq_full_workspace_bytes": (U64, [I64, I32]),
         "fr_sumsq_full": (I32, [P, I64, P, P, U64, I32, P]),
+        "fr_stream_copy": (I32, [P, P, I64, P]),
+        "fr_stream_read": (I32, [P, I64, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -216,3 +219,26 @@ def fr_sumsq_full(x, out, ws=None, stream=None):
     _check(lib.fr_sumsq_full(_ptr(x), x.numel(), _ptr(out), _ptr(ws), ws_bytes, _dtype_code(x), _stream(stream)),
            "fr_sumsq_full")
     return out
+
+
+FR_STREAM_SINK_WORDS = 1024
+
+
+def fr_stream_copy(x, y, stream=None):
+    """y = x for contiguous tensors of the same byte size (a multiple of 16):
+    the streaming reference copy."""
+    nbytes = x.numel() * x.element_size()
+    if not (x.is_contiguous() and y.is_contiguous()) or y.numel() * y.element_size() != nbytes:
+        raise ValueError("expected contiguous tensors of the same byte size")
+    _check(lib.fr_stream_copy(_ptr(x), _ptr(y), nbytes, _stream(stream)), "fr_stream_copy")
+    return y
+
+
+def fr_stream_read(x, sink, stream=None):
+    """Read every byte of contiguous x; sink (FR_STREAM_SINK_WORDS int32 or
+    uint32) receives per-workgroup XORs of the 32-bit words read."""
+    if not x.is_contiguous() or sink.numel() * sink.element_size() < 4 * FR_STREAM_SINK_WORDS:
+        raise ValueError("expected a contiguous input and a sink of FR_STREAM_SINK_WORDS words")
+    _check(lib.fr_stream_read(_ptr(x), x.numel() * x.element_size(), _ptr(sink), _stream(stream)),
+           "fr_stream_read")
+    return sink

@@ -293,4 +293,30 @@ int fr_layernorm_rows(const void* x, const void* gamma, const void* beta, void* 
     return finish_launch(launch_layernorm(plan, args, (hipStream_t)stream));
 }
 
+int fr_stream_copy(const void* x, void* y, int64_t nbytes, void* stream) {
+    if (nbytes < 0 || nbytes % 16) return FR_E_SIZE;
+    if (nbytes == 0) return FR_OK;
+    if (!x || !y) return FR_E_NULL;
+    if (!aligned(x, 16) || !aligned(y, 16)) return FR_E_ALIGN;
+    const uintptr_t a = (uintptr_t)x, b = (uintptr_t)y;
+    if (a < b + (uintptr_t)nbytes && b < a + (uintptr_t)nbytes) return FR_E_ARG;  // overlap
+    int num_cus = 0;
+    const int st = device_check(&num_cus);
+    if (st != FR_OK) return st;
+    (void)hipGetLastError();
+    return finish_launch(launch_stream_copy(x, y, nbytes / 16, (hipStream_t)stream));
+}
+
+int fr_stream_read(const void* x, int64_t nbytes, uint32_t* sink, void* stream) {
+    static_assert(FR_STREAM_SINK_WORDS == kStreamGrid, "one sink word per workgroup");
+    if (nbytes < 0 || nbytes % 16) return FR_E_SIZE;
+    if (!sink || (nbytes > 0 && !x)) return FR_E_NULL;
+    if (!aligned(x, 16) || !aligned(sink, 4)) return FR_E_ALIGN;
+    int num_cus = 0;
+    const int st = device_check(&num_cus);
+    if (st != FR_OK) return st;
+    (void)hipGetLastError();
+    return finish_launch(launch_stream_read(x, nbytes / 16, sink, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -60,6 +60,12 @@ hipError_t launch_sum(const fr_plan& p, const SumArgs& a, hipStream_t s);
 hipError_t launch_softmax(const fr_plan& p, const SoftmaxArgs& a, hipStream_t s);
 hipError_t launch_layernorm(const fr_plan& p, const LayerNormArgs& a, hipStream_t s);
 
+// Streaming reference kernels: at most kStreamGrid workgroups of 256 threads,
+// 4 vectors of 16 bytes per thread per step.
+constexpr int kStreamGrid = 1024;
+hipError_t launch_stream_copy(const void* x, void* y, int64_t nvec, hipStream_t s);
+hipError_t launch_stream_read(const void* x, int64_t nvec, uint32_t* sink, hipStream_t s);
+
 // Planner (host only, no HIP calls).
 int make_plan(int op, int64_t rows, int64_t cols, int dtype, int num_cus, int has_lengths, uint64_t ws_bytes,
               int aligned16, int forced_form, const fr_plan* override_plan, fr_plan* plan);

@@ -1,0 +1,67 @@
+// fr_stream.hip - streaming reference kernels: the practical ceiling of an
+// HBM-bound step, measured with the same harness as the reduction kernels
+// ("Stax (4): GPU Codegen and Dynamic Shapes", 9.1: a memory-bound kernel is
+// judged by the bandwidth it reaches, and Little's law sets the bytes that
+// must be in flight). Both move contiguous 16-byte vectors with the hints the
+// reduction kernels use (non-temporal loads and stores), grid-stride over a
+// fixed grid.
+//   fr_stream_copy_k  y = x
+//   fr_stream_read_k  per-workgroup XOR of every 32-bit word read, so that
+//                     the loads are observable and the result checkable
+#include "fr_device.h"
+#include "fr_internal.h"
+
+namespace fr {
+
+template <int T, int NV>
+__global__ __launch_bounds__(T) void fr_stream_copy_k(const f32x4* __restrict__ x, f32x4* __restrict__ y,
+                                                      int64_t nvec) {
+    const int64_t step = (int64_t)gridDim.x * T * NV;
+    for (int64_t b = (int64_t)blockIdx.x * T * NV + threadIdx.x; b < nvec; b += step) {
+        f32x4 v[NV];
+#pragma unroll
+        for (int k = 0; k < NV; ++k)
+            v[k] = b + k * T < nvec ? __builtin_nontemporal_load(x + b + k * T) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < NV; ++k)
+            if (b + k * T < nvec) __builtin_nontemporal_store(v[k], y + b + k * T);
+    }
+}
+
+template <int T, int NV>
+__global__ __launch_bounds__(T) void fr_stream_read_k(const u32x4* __restrict__ x, int64_t nvec,
+                                                      uint32_t* __restrict__ sink) {
+    __shared__ int sl[T / kWave];
+    const int64_t step = (int64_t)gridDim.x * T * NV;
+    uint32_t acc = 0u;
+    for (int64_t b = (int64_t)blockIdx.x * T * NV + threadIdx.x; b < nvec; b += step) {
+        u32x4 v[NV];
+#pragma unroll
+        for (int k = 0; k < NV; ++k)
+            v[k] = b + k * T < nvec ? __builtin_nontemporal_load(x + b + k * T) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int k = 0; k < NV; ++k) acc ^= (v[k].x ^ v[k].y) ^ (v[k].z ^ v[k].w);
+    }
+    struct OpXor {
+        __device__ int operator()(int a, int b) const { return a ^ b; }
+    };
+    int r = group_reduce<kWave>((int)acc, OpXor());
+    r = block_fold(r, sl, T / kWave, OpXor());
+    if (threadIdx.x == 0) sink[blockIdx.x] = (uint32_t)r;
+}
+
+hipError_t launch_stream_copy(const void* x, void* y, int64_t nvec, hipStream_t s) {
+    const int64_t grid = std::min<int64_t>(kStreamGrid, (nvec + 1023) / 1024);
+    hipLaunchKernelGGL((fr_stream_copy_k<256, 4>), dim3((unsigned)grid), dim3(256), 0, s,
+                       static_cast<const f32x4*>(x), static_cast<f32x4*>(y), nvec);
+    return hipGetLastError();
+}
+
+hipError_t launch_stream_read(const void* x, int64_t nvec, uint32_t* sink, hipStream_t s) {
+    const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(kStreamGrid, (nvec + 1023) / 1024));
+    hipLaunchKernelGGL((fr_stream_read_k<256, 4>), dim3((unsigned)grid), dim3(256), 0, s,
+                       static_cast<const u32x4*>(x), nvec, sink);
+    return hipGetLastError();
+}
+
+}  // namespace fr

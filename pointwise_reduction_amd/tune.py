@@ -65,6 +65,7 @@ def workload(name):
         cands = [dict(form=S, threads=256, vec=8, passes=p) for p in (1, 2)]
         cands += [dict(form=S, threads=256, vec=4, passes=p) for p in (1, 2)]
         cands += [dict(form=S, threads=512, vec=4, passes=p) for p in (1, 2)]
+        cands += [dict(form=S, threads=256, vec=8, passes=1, wait_us=w) for w in (20, 1000)]
         cands += [dict(form=R, threads=512, vec=2), dict(form=R, threads=1024, vec=2)]
 
         def alloc(sets):

@@ -125,6 +125,19 @@ def test_sumsq_argument_errors():
     assert rows_f(FAKE, None, 4, 8, 8, 1, None, 0, fr.FR_F32, None) == fr.FR_E_NULL
 
 
+def test_stream_reference_argument_errors():
+    copy, read = fr.lib.fr_stream_copy, fr.lib.fr_stream_read
+    assert copy(FAKE, P(0x20000), 17, None) == fr.FR_E_SIZE
+    assert copy(FAKE, P(0x20000), -16, None) == fr.FR_E_SIZE
+    assert copy(FAKE, None, 32, None) == fr.FR_E_NULL
+    assert copy(P(0x10008), P(0x20000), 32, None) == fr.FR_E_ALIGN
+    assert copy(P(0x10000), P(0x10010), 64, None) == fr.FR_E_ARG  # overlapping
+    assert copy(None, None, 0, None) == fr.FR_OK  # nothing to move, no HIP call
+    assert read(FAKE, 8, FAKE, None) == fr.FR_E_SIZE
+    assert read(FAKE, 16, None, None) == fr.FR_E_NULL
+    assert read(P(0x10004), 16, FAKE, None) == fr.FR_E_ALIGN
+
+
 # ------------------------------------------------------------------ planning
 
 
