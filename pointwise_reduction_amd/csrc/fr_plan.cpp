@@ -104,7 +104,7 @@ int finalize_plan(int op, int64_t rows, int64_t cols, const Knobs& k, fr_plan* p
     const bool f32 = op != FR_OP_LAYERNORM;
     if (k.form == FR_FORM_PER) {
         if (f32) {
-            if (k.threads != 256 || !is_pow2(k.seg) || k.seg < 8 || k.seg > 64 || k.rpw < 1 || k.rpw > 2)
+            if (k.threads != 256 || !is_pow2(k.seg) || k.seg < 8 || k.seg > 64 || !is_pow2(k.rpw) || k.rpw > 4)
                 return FR_E_ARG;
             if (cols > (int64_t)4 * k.seg * k.vec) return FR_E_ARG;
             p->seg = k.seg;

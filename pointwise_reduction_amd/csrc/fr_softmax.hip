@@ -86,42 +86,57 @@ __global__ __launch_bounds__(256) void fr_per_softmax_f32(const float* x, float*
                 else v[q][k] = load4m<M, true>(xr, j0, L[q], -INFINITY);
             }
         }
+        // The RPW rows go through each phase together, so their reduction
+        // chains overlap: maxima, then argmax, then sums, then stores.
+        float m[RPW], inv[RPW];
 #pragma unroll
         for (int q = 0; q < RPW; ++q) {
-            const int r = grp * RPB + g * RPW + q;
-            const bool live = r < rows;
-            float m = -INFINITY;
+            m[q] = -INFINITY;
 #pragma unroll
-            for (int k = 0; k < NV; ++k) m = max4(m, v[q][k]);
-            m = group_reduce<SEG>(m, OpMax());
-            if (argmax) {
+            for (int k = 0; k < NV; ++k) m[q] = max4(m[q], v[q][k]);
+        }
+#pragma unroll
+        for (int q = 0; q < RPW; ++q) m[q] = group_reduce<SEG>(m[q], OpMax());
+        if (argmax) {
+#pragma unroll
+            for (int q = 0; q < RPW; ++q) {
+                const int r = grp * RPB + g * RPW + q;
                 int cand = INT_MAX;
 #pragma unroll
                 for (int k = NV - 1; k >= 0; --k)
 #pragma unroll
                     for (int c = 3; c >= 0; --c) {
                         const int j = (k * SEG + l) * 4 + c;
-                        if (j < L[q] && is_max(comp(v[q][k], c), m)) cand = j;
+                        if (j < L[q] && is_max(comp(v[q][k], c), m[q])) cand = j;
                     }
                 cand = group_reduce<SEG>(cand, OpMinI());
-                if (live && l == 0) argmax[r] = L[q] > 0 ? cand : -1;
+                if (r < rows && l == 0) argmax[r] = L[q] > 0 ? cand : -1;
             }
+        }
+#pragma unroll
+        for (int q = 0; q < RPW; ++q) {
             float s = 0.f;
 #pragma unroll
             for (int k = 0; k < NV; ++k) {
-                v[q][k] = M == kNone ? exp4(v[q][k], m) : exp4_masked(v[q][k], m, (k * SEG + l) * 4, L[q]);
+                v[q][k] = M == kNone ? exp4(v[q][k], m[q]) : exp4_masked(v[q][k], m[q], (k * SEG + l) * 4, L[q]);
                 s += (v[q][k].x + v[q][k].y) + (v[q][k].z + v[q][k].w);
             }
-            s = group_reduce<SEG>(s, OpSum());
-            const float inv = 1.0f / s;  // one correctly rounded division per row
+            inv[q] = s;
+        }
+#pragma unroll
+        for (int q = 0; q < RPW; ++q) inv[q] = 1.0f / group_reduce<SEG>(inv[q], OpSum());  // one division per row
+#pragma unroll
+        for (int q = 0; q < RPW; ++q) {
+            const int r = grp * RPB + g * RPW + q;
+            const bool live = r < rows;
             float* yr = y + (int64_t)(live ? r : 0) * y_rs;
 #pragma unroll
             for (int k = 0; k < NV; ++k) {
                 const int j0 = (k * SEG + l) * 4;
                 if constexpr (M == kNone) {
-                    if (live) st4<true>(yr + j0, v[q][k] * inv);
+                    if (live) st4<true>(yr + j0, v[q][k] * inv[q]);
                 } else {
-                    store4m<M, true>(yr, j0, L[q], v[q][k] * inv);
+                    store4m<M, true>(yr, j0, L[q], v[q][k] * inv[q]);
                 }
             }
         }
@@ -567,7 +582,17 @@ using FinFn = void (*)(const float*, float*, int, int, int64_t, int64_t, const i
 
 template <int M>
 SmFn pick_per_m(int seg, int nv, int rpw) {
+    if (rpw == 4) {
+        if (seg != 64) return nullptr;
+        switch (nv) {
+            case 1: return fr_per_softmax_f32<64, 1, M, 4>;
+            case 2: return fr_per_softmax_f32<64, 2, M, 4>;
+            case 4: return fr_per_softmax_f32<64, 4, M, 4>;
+        }
+        return nullptr;
+    }
     if (rpw == 2) {
+        if (seg == 32) return nv == 8 ? fr_per_softmax_f32<32, 8, M, 2> : nullptr;
         if (seg != 64) return nullptr;
         switch (nv) {
             case 1: return fr_per_softmax_f32<64, 1, M, 2>;
@@ -578,9 +603,16 @@ SmFn pick_per_m(int seg, int nv, int rpw) {
     }
     if (rpw != 1) return nullptr;
     switch (seg) {
-        case 8: return fr_per_softmax_f32<8, 1, M, 1>;
-        case 16: return fr_per_softmax_f32<16, 1, M, 1>;
-        case 32: return fr_per_softmax_f32<32, 1, M, 1>;
+        case 8: return nv == 1 ? fr_per_softmax_f32<8, 1, M, 1> : nullptr;
+        case 16: return nv == 1 ? fr_per_softmax_f32<16, 1, M, 1> : nullptr;
+        case 32:
+            switch (nv) {
+                case 1: return fr_per_softmax_f32<32, 1, M, 1>;
+                case 2: return fr_per_softmax_f32<32, 2, M, 1>;
+                case 4: return fr_per_softmax_f32<32, 4, M, 1>;
+                case 8: return fr_per_softmax_f32<32, 8, M, 1>;
+            }
+            return nullptr;
         case 64:
             switch (nv) {
                 case 1: return fr_per_softmax_f32<64, 1, M, 1>;

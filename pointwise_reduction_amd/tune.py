@@ -51,6 +51,9 @@ def workload(name):
         x = synth.softmax_inputs(rows, cols, seed=2001)
         cands = [dict(form=P, threads=256, seg=64, vec=4, rows_per_wg=4),
                  dict(form=P, threads=256, seg=64, vec=4, rows_per_wg=8),
+                 dict(form=P, threads=256, seg=64, vec=4, rows_per_wg=16),
+                 dict(form=P, threads=256, seg=32, vec=8, rows_per_wg=8),
+                 dict(form=P, threads=256, seg=32, vec=8, rows_per_wg=16),
                  dict(form=R, threads=256, vec=4), dict(form=R, threads=512, vec=2)]
 
         def alloc(sets):
