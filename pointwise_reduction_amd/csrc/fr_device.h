@@ -266,6 +266,11 @@ constexpr int tail_mask() { return VEC ? kElem : kScalar; }
 template <bool VEC>
 constexpr int body_mask() { return VEC ? kNone : kScalar; }
 
+// Word 3 of a raw buffer resource on gfx9-family devices (gfx950): 32-bit
+// data format, no swizzle; with stride 0 the record count is a byte range
+// and accesses past it read zero and drop stores.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+
 // ------------------------------------------------------------------ bf16
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }

@@ -69,11 +69,16 @@ def test_layernorm_constant_row_is_beta(form):
         assert np.array_equal(got, np.broadcast_to(b, got.shape)), f"{form} cols={cols}"
 
 
-def test_layernorm_without_affine_and_eps():
-    x, _, _ = synth.layernorm_inputs(16, 3000, seed=3300)
+@pytest.mark.parametrize("shape", [(16, 3000), (8, 4096), (4, 32768)], ids=["16x3000", "8x4096", "4x32768"])
+def test_layernorm_without_affine_and_eps(shape):
+    """gamma and/or beta absent (1 and 0), on masked rows and on rows that
+    fill a workgroup exactly (the buffer-resource path)."""
+    x, g, b = synth.layernorm_inputs(*shape, seed=3300 + shape[1])
     for eps in (1e-5, 0.0, 1.0):
         got = gpu_ln(x, None, None, eps=eps)
         compare(x, None, None, got, eps=eps, what=f"no affine eps={eps}")
+    compare(x, g, None, gpu_ln(x, g, None), what="gamma only")
+    compare(x, None, b, gpu_ln(x, None, b), what="beta only")
 
 
 def test_layernorm_row_stride():
