@@ -52,6 +52,8 @@ def _load():
         "orc_layernorm_rows": (None, [P, P, P, I64, I64, I64, F64, P, P, P, I64]),
         "orc_sumsq": (F64, [P, I64]),
         "orc_sumsq_rows": (None, [P, I64, I64, I64, P]),
+        "orc_attn_decode": (None, [P, P, P, I64, I64, I64, I64, I64, P, F64, P, P, P, P, P]),
+        "orc_attn_merge": (None, [F64, F64, P, F64, F64, P, I64, P, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -157,6 +159,49 @@ def online_attention_row(scores, V):
     l = ctypes.c_double()
     _load().orc_online_attention_row(_p(s), _p(V), n, dv, ctypes.byref(m), ctypes.byref(l), _p(a), _p(o))
     return m.value, l.value, a, o
+
+
+# ------------------------------------------------------------------ attention decode
+
+
+def attn_decode(q, k, v, lengths=None, scale=None):
+    """Decode attention ([Stax4] 9.10; [HG12] 12.1) in fp64.
+
+    q: [B, Hq, D]; k, v: [B, Hkv, S, D] (any float dtype; bf16 callers pass
+    decoded values). Returns (o64 [B, Hq, D], lse [B, Hq], mag [B, Hq, D],
+    smag [B, Hq]) as defined at orc_attn_decode."""
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    k = np.ascontiguousarray(k, dtype=np.float64)
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    B, Hq, D = q.shape
+    Bk, Hkv, S, Dk = k.shape
+    assert (Bk, Dk) == (B, D) and v.shape == k.shape and Hq % Hkv == 0
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    L = None if lengths is None else np.ascontiguousarray(lengths, dtype=np.int32)
+    assert L is None or L.shape == (B,)
+    o = np.empty((B, Hq, D))
+    lse = np.empty((B, Hq))
+    mag = np.empty((B, Hq, D))
+    smag = np.empty((B, Hq))
+    scratch = np.empty(max(S, 1))
+    _load().orc_attn_decode(_p(q), _p(k), _p(v), B, Hq, Hkv, S, D, _p(L), float(scale), _p(scratch), _p(o), _p(lse),
+                            _p(mag), _p(smag))
+    return o, lse, mag, smag
+
+
+def attn_merge(p1, p2):
+    """(m, l, a) (+) (m, l, a) ([Stax4] 9.10)."""
+    m1, l1, a1 = p1
+    m2, l2, a2 = p2
+    a1 = np.ascontiguousarray(a1, dtype=np.float64)
+    a2 = np.ascontiguousarray(a2, dtype=np.float64)
+    a = np.empty_like(a1)
+    m = ctypes.c_double()
+    l = ctypes.c_double()
+    _load().orc_attn_merge(float(m1), float(l1), _p(a1), float(m2), float(l2), _p(a2), a1.shape[0], ctypes.byref(m),
+                           ctypes.byref(l), _p(a))
+    return m.value, l.value, a
 
 
 # ------------------------------------------------------------------ LayerNorm

@@ -15,8 +15,11 @@
  *            section 9.2 (Listing 9.1, Example 1.1), 9.4 (Listing 9.4,
  *            Example 6.2), 9.5 (softmax definition, Listing 9.5, the (m, d)
  *            merge and Proposition 9.1), 10.2 (Example 10.1).
- *   [HG12]   "hello-gpu, Chapter 12: Fusion", section 12.1 (worked example)
- *            and 12.3 (online m, l, a update).
+ *   [HG12]   "hello-gpu, Chapter 12: Fusion", section 12.1 (attention of one
+ *            query row, worked example) and 12.3 (online m, l, a update).
+ *   [Stax4]  also 9.10 (attention S = QK^T / sqrt(d), row softmax, O = PV; the
+ *            (m, l, a) triple, its merge, and LSE = m + log l; the decode
+ *            template that splits the keys).
  *   [L8]     "CMU 15-779 Lecture 8: ML Compilers Part 1, Tile-based DSLs",
  *            section 3 (fused softmax) and Exercise 1 (row L2 norm).
  * Readings of points the pages leave open are stated at each function.
@@ -193,6 +196,106 @@ void orc_online_attention_row(const double* s, const double* V, int64_t n, int64
     *m_out = m;
     *l_out = l;
     for (int64_t k = 0; k < dv; ++k) o[k] = a[k] / l;
+}
+
+/* ------------------------------------------------------ attention decode */
+
+/*
+ * One query row per (batch b, query head h) against the keys and values of
+ * its key-value head ([Stax4] 9.10: S = Q K^T / sqrt(d), P = softmax(S) by
+ * rows, O = P V; [HG12] 12.1: s_j = q . k_j / sqrt(D), p_j = e^{s_j} /
+ * sum_k e^{s_k}, o = sum_j p_j v_j). Written out as the definition: scores,
+ * their maximum, the exponentials, their sum, the weighted sum of values,
+ * one division; all in fp64.
+ * Readings where the pages are silent:
+ *  - several query heads may share one key-value head: head h reads head
+ *    h / (Hq / Hkv) (Hq a multiple of Hkv; the pages have one head);
+ *  - scale multiplies q . k (the pages' 1 / sqrt(d));
+ *  - lengths (nullable, [B]) limits batch b to its first len_b keys,
+ *    clamped to [0, S]; an empty key set gives o = 0 and lse = -inf;
+ *  - a NaN among the scores makes the maximum NaN, so o and lse are NaN.
+ * Layouts (row-major, contiguous): q, o64, mag [B, Hq, D]; k, v [B, Hkv, S,
+ * D]; lse, smag [B, Hq].
+ *   lse  = m + log(l) ([Stax4] 9.10), the log of the sum of e^{s_j}.
+ *   mag  (nullable): sum_j p_j |v_jd|, the size of the terms of o.
+ *   smag (nullable): max_j sum_d |scale q_d k_jd|, the size of the terms of
+ *                    the scores.
+ */
+void orc_attn_decode(const double* q, const double* k, const double* v, int64_t B, int64_t Hq, int64_t Hkv, int64_t S,
+                     int64_t D, const int32_t* lengths, double scale, double* s_scratch, double* o64, double* lse,
+                     double* mag, double* smag) {
+    const int64_t G = Hq / Hkv;
+    for (int64_t b = 0; b < B; ++b) {
+        int64_t L = lengths ? lengths[b] : S;
+        if (L < 0) L = 0;
+        if (L > S) L = S;
+        for (int64_t h = 0; h < Hq; ++h) {
+            const double* qr = q + (b * Hq + h) * D;
+            const double* kh = k + (b * Hkv + h / G) * S * D;
+            const double* vh = v + (b * Hkv + h / G) * S * D;
+            double* orow = o64 + (b * Hq + h) * D;
+            double* mrow = mag ? mag + (b * Hq + h) * D : 0;
+            double sm = 0.0;
+            for (int64_t d = 0; d < D; ++d) {
+                orow[d] = 0.0;
+                if (mrow) mrow[d] = 0.0;
+            }
+            if (L == 0) {
+                lse[b * Hq + h] = -INFINITY;
+                if (smag) smag[b * Hq + h] = 0.0;
+                continue;
+            }
+            double m = -INFINITY;
+            int nan = 0;
+            for (int64_t j = 0; j < L; ++j) {
+                double s = 0.0, t = 0.0;
+                for (int64_t d = 0; d < D; ++d) {
+                    s += qr[d] * kh[j * D + d];
+                    t += fabs(scale * qr[d] * kh[j * D + d]);
+                }
+                s *= scale;
+                s_scratch[j] = s;
+                if (isnan(s)) nan = 1;
+                if (s > m) m = s;
+                if (t > sm) sm = t;
+            }
+            if (nan) m = NAN;
+            double l = 0.0;
+            for (int64_t j = 0; j < L; ++j) {
+                const double p = exp(s_scratch[j] - m);
+                s_scratch[j] = p;
+                l += p;
+            }
+            for (int64_t j = 0; j < L; ++j)
+                for (int64_t d = 0; d < D; ++d) {
+                    orow[d] += s_scratch[j] * vh[j * D + d];
+                    if (mrow) mrow[d] += s_scratch[j] * fabs(vh[j * D + d]);
+                }
+            for (int64_t d = 0; d < D; ++d) {
+                orow[d] /= l;
+                if (mrow) mrow[d] /= l;
+            }
+            lse[b * Hq + h] = m + log(l);
+            if (smag) smag[b * Hq + h] = sm;
+        }
+    }
+}
+
+/*
+ * The merge of two partial states of one query row over disjoint key sets
+ * ([Stax4] 9.10): with mu = max(m1, m2),
+ *   (m1, l1, a1) (+) (m2, l2, a2) = (mu, l1 e^{m1-mu} + l2 e^{m2-mu},
+ *                                    a1 e^{m1-mu} + a2 e^{m2-mu}).
+ * The identity is (-inf, 0, 0): its factor e^{-inf - mu} is 0.
+ */
+void orc_attn_merge(double m1, double l1, const double* a1, double m2, double l2, const double* a2, int64_t D,
+                    double* m, double* l, double* a) {
+    const double mu = m1 > m2 ? m1 : m2;
+    const double f1 = m1 == -INFINITY ? 0.0 : exp(m1 - mu);
+    const double f2 = m2 == -INFINITY ? 0.0 : exp(m2 - mu);
+    *m = mu;
+    *l = l1 * f1 + l2 * f2;
+    for (int64_t d = 0; d < D; ++d) a[d] = a1[d] * f1 + a2[d] * f2;
 }
 
 /* ------------------------------------------------------ LayerNorm (C3) */

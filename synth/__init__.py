@@ -160,3 +160,26 @@ def ragged_softmax_inputs(rows=512, row_stride=131072, seed=5001, choices=RAGGED
     x = np.empty((rows, row_stride), dtype=np.float32)
     _load().syn_ragged_normal_rows(_p(x), rows, row_stride, _p(L), seed, 0.0, std, tail)
     return x, L
+
+
+def attn_decode_inputs(batch=8, heads_q=32, heads_kv=8, seq=8192, dim=128, seed=6001, lengths=None, choices=None,
+                       bf16=True, tail=float("nan")):
+    """Decode attention: q [B, Hq, D], k, v [B, Hkv, S, D], all N(0, 1); with
+    bf16 the values are rounded to bf16 and returned as uint16 bits, else as
+    fp32. lengths: explicit [B] valid key counts, or drawn from `choices`,
+    or None (every batch has S keys). Keys and values at j >= len_b hold
+    `tail` (NaN by default: they must never be read)."""
+    q = normal((batch, heads_q, dim), seed, stream=0)
+    k = normal((batch, heads_kv, seq, dim), seed, stream=1)
+    v = normal((batch, heads_kv, seq, dim), seed, stream=2)
+    if lengths is None and choices is not None:
+        lengths = ragged_lengths(batch, seed, choices)
+    L = None if lengths is None else np.ascontiguousarray(lengths, dtype=np.int32)
+    if L is not None:
+        for b in range(batch):
+            n = int(np.clip(L[b], 0, seq))
+            k[b, :, n:] = tail
+            v[b, :, n:] = tail
+    if bf16:
+        return to_bf16(q), to_bf16(k), to_bf16(v), L
+    return q, k, v, L

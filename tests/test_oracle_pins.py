@@ -13,6 +13,7 @@ from fractions import Fraction
 
 import numpy as np
 import pytest
+import scipy.special
 
 import oracle
 import synth
@@ -341,3 +342,120 @@ def test_example_6_2_split_rows_and_l2_norm(golden):
     np.testing.assert_allclose(s, [h0 + h1 for h0, h1 in halves], rtol=1e-13)
     # CMU 15-779 Lecture 8, Exercise 1: the row L2 norm is sqrt of this sum
     np.testing.assert_allclose(np.sqrt(s), np.linalg.norm(x.astype(np.float64), axis=1), rtol=1e-13)
+
+
+# ------------------------------------------------------------------ attention decode
+
+
+def _attn_np(q, k, v, lengths, scale):
+    """Independent numpy statement of the same definition (matrix form)."""
+    B, Hq, D = q.shape
+    Hkv, S = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    o = np.zeros((B, Hq, D))
+    lse = np.full((B, Hq), -np.inf)
+    for b in range(B):
+        L = S if lengths is None else int(np.clip(lengths[b], 0, S))
+        if L == 0:
+            continue
+        for h in range(Hq):
+            s = scale * (k[b, h // G, :L] @ q[b, h])
+            o[b, h] = scipy.special.softmax(s) @ v[b, h // G, :L]
+            lse[b, h] = scipy.special.logsumexp(s)
+    return o, lse
+
+
+def test_attn_decode_worked_example(golden):
+    """[HG12] 12.1: scores [2, 1, 4] (q = [1, 0], keys [2,0], [1,0], [4,0],
+    scale 1) with values [1,0], [0,2], [3,1] give o = [2.6456, 0.9278]; lse
+    is log(e^2 + e^1 + e^4) and log of the page's exponent sum plus the max."""
+    g = golden("hello_gpu_ch12_worked_example.txt")
+    q = np.array([[[1.0, 0.0]]])
+    k = np.array([[[[s, 0.0] for s in g["scores"]]]])
+    v = np.array([[g["values"]]])
+    o, lse, mag, smag = oracle.attn_decode(q, k, v, scale=1.0)
+    assert np.allclose(o[0, 0], g["output"], atol=g["tolerance"])
+    assert lse[0, 0] == pytest.approx(np.log(np.exp(2) + np.exp(1) + np.exp(4)), rel=1e-15)
+    assert lse[0, 0] == pytest.approx(4 + np.log(g["exp_sum"]), abs=g["tolerance"])
+    assert np.allclose(mag[0, 0], o[0, 0])  # nonnegative values: the size of the terms is o itself
+    assert smag[0, 0] == 4.0
+
+
+def test_attn_decode_closed_forms():
+    rng = np.random.default_rng(71)
+    v = rng.normal(size=(1, 1, 5, 8))
+    k = rng.normal(size=(1, 1, 5, 8))
+    # one key: o is that value row, lse its score
+    q = rng.normal(size=(1, 1, 8))
+    o, lse, _, _ = oracle.attn_decode(q, k[:, :, :1], v[:, :, :1], scale=0.5)
+    assert np.array_equal(o[0, 0], v[0, 0, 0])
+    assert lse[0, 0] == pytest.approx(0.5 * float(q[0, 0] @ k[0, 0, 0]), rel=1e-14)
+    # a zero query scores every key 0: uniform weights, o = mean of the rows, lse = log(n)
+    o, lse, _, _ = oracle.attn_decode(np.zeros((1, 1, 8)), k, v)
+    assert np.allclose(o[0, 0], v[0, 0].mean(axis=0), rtol=0, atol=1e-15)
+    assert lse[0, 0] == pytest.approx(np.log(5), rel=1e-15)
+    # adding one vector u to every key shifts every score by scale * q.u:
+    # o unchanged, lse shifted by that amount
+    u = rng.normal(size=8)
+    o1, l1, _, _ = oracle.attn_decode(q, k, v, scale=0.3)
+    o2, l2, _, _ = oracle.attn_decode(q, k + u, v, scale=0.3)
+    assert np.allclose(o1, o2, rtol=0, atol=1e-13)
+    assert l2[0, 0] - l1[0, 0] == pytest.approx(0.3 * float(q[0, 0] @ u), abs=1e-13)
+
+
+def test_attn_decode_matches_matrix_form_with_groups_and_lengths():
+    """Grouped heads (query head h reads key-value head h // (Hq / Hkv)),
+    per-batch lengths (0, partial, full, beyond S clamped), against an
+    independent numpy + scipy statement of softmax(scale q K^T) V."""
+    rng = np.random.default_rng(72)
+    B, Hq, Hkv, S, D = 4, 6, 2, 37, 16
+    q = rng.normal(size=(B, Hq, D))
+    k = rng.normal(size=(B, Hkv, S, D)) * 2
+    v = rng.normal(size=(B, Hkv, S, D))
+    lengths = np.array([0, 11, S, S + 5], dtype=np.int32)
+    o, lse, mag, _ = oracle.attn_decode(q, k, v, lengths=lengths)
+    o_np, lse_np = _attn_np(q, k, v, lengths, 1 / np.sqrt(D))
+    assert np.allclose(o, o_np, rtol=1e-12, atol=1e-13)
+    assert np.array_equal(o[0], np.zeros((Hq, D))) and np.all(np.isneginf(lse[0]))
+    assert np.allclose(lse[1:], lse_np[1:], rtol=1e-13)
+    assert np.all(mag >= np.abs(o) - 1e-15)
+    # a mistake in the head mapping shows: swapping the key-value heads changes the result
+    o_sw, _, _, _ = oracle.attn_decode(q, k[:, ::-1], v[:, ::-1], lengths=lengths)
+    assert not np.allclose(o_sw[1:], o[1:])
+
+
+def test_attn_merge_any_split_equals_the_whole():
+    """[Stax4] 9.10: the (m, l, a) triples of any segmentation of the keys,
+    merged with (+), give the triple of the whole row; o = a / l."""
+    rng = np.random.default_rng(73)
+    n, D = 23, 4
+    s = rng.normal(size=n) * 3
+    V = rng.normal(size=(n, D))
+    m_all, l_all, a_all, o_all = oracle.online_attention_row(s, V)
+    ident = (-np.inf, 0.0, np.zeros(D))
+    for cut in range(0, n + 1):
+        parts = [oracle.online_attention_row(s[:cut], V[:cut])[:3] if cut else ident,
+                 oracle.online_attention_row(s[cut:], V[cut:])[:3] if cut < n else ident]
+        m, l, a = oracle.attn_merge(parts[0], parts[1])
+        assert m == m_all
+        assert l == pytest.approx(l_all, rel=1e-14)
+        assert np.allclose(a / l, o_all, rtol=1e-13, atol=1e-15)
+    # three segments merged in either grouping (associativity)
+    segs = [(0, 5), (5, 17), (17, n)]
+    p = [oracle.online_attention_row(s[a:b], V[a:b])[:3] for a, b in segs]
+    left = oracle.attn_merge(oracle.attn_merge(p[0], p[1]), p[2])
+    right = oracle.attn_merge(p[0], oracle.attn_merge(p[1], p[2]))
+    assert left[0] == right[0]
+    assert np.allclose(left[2] / left[1], right[2] / right[1], rtol=1e-14)
+    # the identity leaves a state unchanged
+    m, l, a = oracle.attn_merge(ident, p[1])
+    assert (m, l) == (p[1][0], p[1][1]) and np.array_equal(a, p[1][2])
+
+
+def test_attn_decode_nan_propagates():
+    q = np.ones((1, 1, 4))
+    k = np.ones((1, 1, 3, 4))
+    v = np.ones((1, 1, 3, 4))
+    k[0, 0, 1, 2] = np.nan
+    o, lse, _, _ = oracle.attn_decode(q, k, v)
+    assert np.all(np.isnan(o)) and np.isnan(lse[0, 0])
