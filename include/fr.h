@@ -208,6 +208,37 @@ int fr_sumsq_rows(const void* x, void* out, int64_t rows, int64_t cols, int64_t 
 uint64_t fr_sumsq_full_workspace_bytes(int64_t n, int dtype);
 int fr_sumsq_full(const void* x, int64_t n, void* out, void* ws, uint64_t ws_bytes, int dtype, void* stream);
 
+/* ------------------------------------------------------------ decode attention
+ * One query row per (batch b, query head h), keys and values of key-value
+ * head g = h / (heads_q / heads_kv):
+ *   s_j = scale * q[b,h,:] . k[b,g,j,:]                       (j < len_b)
+ *   o[b,h,:] = sum_j e^{s_j - m} v[b,g,j,:] / sum_j e^{s_j - m},  m = max_j s_j
+ *   lse[b,h] = m + log sum_j e^{s_j - m}
+ * ("Stax (4)", 9.10: attention as a row softmax between two contractions;
+ * the (m, l, a) triple and its merge let the keys be split across
+ * workgroups, as the decode template does; hello-gpu, Chapter 12, 12.1).
+ * The keys of a row are cut into chunks of 256; each chunk's triple goes to
+ * the workspace and a second kernel merges them in chunk order, so results
+ * are bit-identical run to run.
+ *  q, o:    [batch, heads_q, dim], contiguous; k, v: [batch, heads_kv, seq,
+ *           dim], contiguous; all of dtype FR_F32 or FR_BF16 (fp32
+ *           arithmetic; a bf16 o is rounded to nearest even). 16-byte aligned.
+ *  lengths: optional int32 [batch] device array, clamped to [0, seq] (NULL:
+ *           seq). Keys and values at j >= len_b are never read.
+ *  lse:     optional fp32 [batch, heads_q] device output.
+ *  scale:   finite (the pages use 1 / sqrt(dim)).
+ *  ws:      16-byte aligned workspace of at least
+ *           fr_attn_decode_workspace_bytes(batch, heads_q, seq, dim) bytes
+ *           (FR_E_WORKSPACE if smaller).
+ * An empty key set gives o = 0 and lse = -inf; a NaN score makes the row's
+ * o and lse NaN. dim must be 64 or 128 (FR_E_SIZE); heads_q must be 1, 2, 4
+ * or 8 times heads_kv (FR_E_ARG); batch and heads_kv at most 65535, seq
+ * below 2^30 (FR_E_SIZE). */
+uint64_t fr_attn_decode_workspace_bytes(int64_t batch, int64_t heads_q, int64_t seq, int64_t dim);
+int fr_attn_decode(const void* q, const void* k, const void* v, void* o, float* lse, int64_t batch, int64_t heads_q,
+                   int64_t heads_kv, int64_t seq, int64_t dim, const int32_t* lengths, float scale, void* ws,
+                   uint64_t ws_bytes, int dtype, void* stream);
+
 /* ------------------------------------------------------------ streaming references
  * The practical ceiling of an HBM-bound step ("Stax (4)", 9.1: memory-bound
  * kernels are judged by the bandwidth they reach): the plainest kernels that

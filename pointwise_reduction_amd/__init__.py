@@ -12,6 +12,7 @@ raises, and on a machine without a gfx950 GPU every compute call returns
 FR_E_DEVICE (raised as FrError).
 """
 import ctypes
+import math
 import os
 
 try:  # load torch first so that libfr binds to the same HIP runtime as torch
@@ -38,6 +39,7 @@ EXPORTS = (
     "fr_layernorm_rows",
     "fr_sumsq_rows", "fr_sumsq_full_workspace_bytes", "fr_sumsq_full",
     "fr_stream_copy", "fr_stream_read",
+    "fr_attn_decode_workspace_bytes", "fr_attn_decode",
 )
 
 
@@ -81,6 +83,8 @@ def _load():
         "fr_sumsq_rows": (I32, [P, P, I64, I64, I64, I64, P, U64, I32, P]),
         "fr_sumsq_full_workspace_bytes": (U64, [I64, I32]),
         "fr_sumsq_full": (I32, [P, I64, P, P, U64, I32, P]),
+        "fr_attn_decode_workspace_bytes": (U64, [I64, I64, I64, I64]),
+        "fr_attn_decode": (I32, [P, P, P, P, P, I64, I64, I64, I64, I64, P, ctypes.c_float, P, U64, I32, P]),
         "fr_stream_copy": (I32, [P, P, I64, P]),
         "fr_stream_read": (I32, [P, I64, P, P]),
     }
@@ -242,3 +246,31 @@ def fr_stream_read(x, sink, stream=None):
     _check(lib.fr_stream_read(_ptr(x), x.numel() * x.element_size(), _ptr(sink), _stream(stream)),
            "fr_stream_read")
     return sink
+
+
+def fr_attn_decode_workspace_bytes(batch, heads_q, seq, dim):
+    return int(lib.fr_attn_decode_workspace_bytes(batch, heads_q, seq, dim))
+
+
+def fr_attn_decode(q, k, v, o, lse=None, lengths=None, scale=None, ws=None, stream=None):
+    """Decode attention: q, o [B, Hq, D]; k, v [B, Hkv, S, D] (contiguous,
+    float32 or bfloat16); lse optional fp32 [B, Hq]; lengths optional int32
+    [B]. scale defaults to 1/sqrt(D). A workspace of the queried size is
+    allocated with torch when none is given."""
+    if q.dim() != 3 or k.dim() != 4 or v.shape != k.shape or o.shape != q.shape:
+        raise ValueError("expected q, o [B, Hq, D] and k, v [B, Hkv, S, D]")
+    B, Hq, D = q.shape
+    if k.shape[0] != B or k.shape[3] != D:
+        raise ValueError("shape mismatch")
+    if not all(t.is_contiguous() for t in (q, k, v, o)):
+        raise ValueError("expected contiguous tensors")
+    Hkv, S = k.shape[1], k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    need = fr_attn_decode_workspace_bytes(B, Hq, S, D)
+    if ws is None and need > 0:
+        ws = torch.empty((need + 15) // 16 * 4, dtype=torch.float32, device=q.device)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.fr_attn_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, S, D, _ptr(lengths),
+                              float(scale), _ptr(ws), ws_bytes, _dtype_code(q), _stream(stream)), "fr_attn_decode")
+    return o

@@ -293,6 +293,38 @@ int fr_layernorm_rows(const void* x, const void* gamma, const void* beta, void* 
     return finish_launch(launch_layernorm(plan, args, (hipStream_t)stream));
 }
 
+uint64_t fr_attn_decode_workspace_bytes(int64_t batch, int64_t heads_q, int64_t seq, int64_t dim) {
+    if (batch < 0 || heads_q < 0 || seq < 0 || seq >= kMaxCols || (dim != 64 && dim != 128)) return 0;
+    return attn_ws_bytes(batch, heads_q, seq, dim);
+}
+
+int fr_attn_decode(const void* q, const void* k, const void* v, void* o, float* lse, int64_t batch, int64_t heads_q,
+                   int64_t heads_kv, int64_t seq, int64_t dim, const int32_t* lengths, float scale, void* ws,
+                   uint64_t ws_bytes, int dtype, void* stream) {
+    if (dtype != FR_F32 && dtype != FR_BF16) return FR_E_DTYPE;
+    if (batch < 0 || heads_q < 0 || heads_kv < 0 || seq < 0) return FR_E_SIZE;
+    if (dim != 64 && dim != 128) return FR_E_SIZE;
+    if (batch > 65535 || heads_kv > 65535 || seq >= kMaxCols || batch * heads_q >= kMaxRows) return FR_E_SIZE;
+    if (batch == 0 || heads_q == 0) return FR_OK;
+    if (heads_kv == 0 || heads_q % heads_kv) return FR_E_ARG;
+    const int64_t G = heads_q / heads_kv;
+    if (G != 1 && G != 2 && G != 4 && G != 8) return FR_E_ARG;
+    if (!isfinite(scale)) return FR_E_ARG;
+    if (!q || !o || (seq > 0 && (!k || !v))) return FR_E_NULL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4) ||
+        !aligned(lengths, 4) || !aligned(ws, 16))
+        return FR_E_ALIGN;
+    const uint64_t need = attn_ws_bytes(batch, heads_q, seq, dim);
+    if (need > 0 && (!ws || ws_bytes < need)) return FR_E_WORKSPACE;
+    int num_cus = 0;
+    const int st = device_check(&num_cus);
+    if (st != FR_OK) return st;
+    AttnArgs args{q, k, v, o, lse, (int)batch, (int)heads_q, (int)heads_kv, (int)seq, (int)dim, lengths, scale,
+                  static_cast<float*>(ws), dtype == FR_BF16};
+    (void)hipGetLastError();
+    return finish_launch(launch_attn_decode(args, (hipStream_t)stream));
+}
+
 int fr_stream_copy(const void* x, void* y, int64_t nbytes, void* stream) {
     if (nbytes < 0 || nbytes % 16) return FR_E_SIZE;
     if (nbytes == 0) return FR_OK;

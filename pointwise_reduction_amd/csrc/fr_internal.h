@@ -60,6 +60,28 @@ hipError_t launch_sum(const fr_plan& p, const SumArgs& a, hipStream_t s);
 hipError_t launch_softmax(const fr_plan& p, const SoftmaxArgs& a, hipStream_t s);
 hipError_t launch_layernorm(const fr_plan& p, const LayerNormArgs& a, hipStream_t s);
 
+// Decode attention: keys are split into chunks of kAttnChunk per workgroup;
+// the workspace holds one (m, l, pad, pad, a[dim]) fp32 slot per (batch,
+// query head, chunk).
+constexpr int kAttnChunk = 256;
+inline int64_t attn_chunks(int64_t seq) { return (seq + kAttnChunk - 1) / kAttnChunk; }
+inline uint64_t attn_ws_bytes(int64_t batch, int64_t heads_q, int64_t seq, int64_t dim) {
+    return (uint64_t)(batch * heads_q * attn_chunks(seq) * (dim + 4) * 4);
+}
+struct AttnArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;              // nullable
+    int batch, heads_q, heads_kv, seq, dim;
+    const int32_t* lengths;  // nullable
+    float scale;
+    float* ws;
+    bool bf16;
+};
+hipError_t launch_attn_decode(const AttnArgs& a, hipStream_t s);
+
 // Streaming reference kernels: at most kStreamGrid workgroups of 256 threads,
 // 4 vectors of 16 bytes per thread per step.
 constexpr int kStreamGrid = 1024;

@@ -138,6 +138,31 @@ def test_stream_reference_argument_errors():
     assert read(P(0x10004), 16, FAKE, None) == fr.FR_E_ALIGN
 
 
+def test_attn_decode_argument_errors():
+    f = fr.lib.fr_attn_decode
+    ws_need = fr.fr_attn_decode_workspace_bytes(2, 8, 1000, 128)
+    assert ws_need == 2 * 8 * 4 * (128 + 4) * 4  # 4 chunks of 256 keys, one (m, l, pad, pad, a) slot each
+
+    def call(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=2, Hq=8, Hkv=2, S=1000, D=128, L=None, scale=0.1,
+             ws=FAKE, wsb=ws_need, dt=fr.FR_BF16):
+        return f(q, k, v, o, lse, B, Hq, Hkv, S, D, L, scale, ws, wsb, dt, None)
+    assert call(dt=7) == fr.FR_E_DTYPE
+    assert call(D=96) == fr.FR_E_SIZE
+    assert call(S=-1) == fr.FR_E_SIZE
+    assert call(B=70000) == fr.FR_E_SIZE
+    assert call(Hkv=3) == fr.FR_E_ARG   # 8 query heads on 3 key-value heads
+    assert call(Hq=32, Hkv=2) == fr.FR_E_ARG  # 16 query heads per key-value head
+    assert call(scale=float("inf")) == fr.FR_E_ARG
+    assert call(q=None) == fr.FR_E_NULL
+    assert call(k=None) == fr.FR_E_NULL
+    assert call(o=P(0x10008)) == fr.FR_E_ALIGN
+    assert call(lse=P(0x10002)) == fr.FR_E_ALIGN
+    assert call(wsb=ws_need - 1) == fr.FR_E_WORKSPACE
+    assert call(ws=None) == fr.FR_E_WORKSPACE
+    assert call(B=0) == fr.FR_OK and call(Hq=0) == fr.FR_OK  # nothing to compute, no HIP call
+    assert fr.fr_attn_decode_workspace_bytes(2, 8, 1000, 80) == 0
+
+
 # ------------------------------------------------------------------ planning
 
 
