@@ -299,6 +299,48 @@ def make_workload(name, torch, fr, synth):
 
         return W(), per_set
 
+    if name == "attn_decode":
+        # decode attention: batch 8, 32 query heads on 8 key-value heads,
+        # 8192 keys, head dim 128, bf16 (each key and value byte read once)
+        B, Hq, Hkv, S, D = 8, 32, 8, 8192, 128
+        q_h, k_h, v_h, _ = synth.attn_decode_inputs(B, Hq, Hkv, S, D, seed=6001, bf16=True)
+        kv_bytes = 2 * B * Hkv * S * D * 2
+        nbytes = kv_bytes + 2 * B * Hq * D * 2 + B * Hq * 4
+        per_set = kv_bytes
+
+        class W(Workload):
+            kernel = "fr_attn_part"
+            bytes = nbytes
+            dtype = "bf16"
+
+            def alloc(self, sets):
+                bf = lambda u: torch.from_numpy(np.ascontiguousarray(u).view(np.int16)).to(dev).view(torch.bfloat16)  # noqa: E731
+                q0, k0, v0 = bf(q_h), bf(k_h), bf(v_h)
+                ws_n = fr.fr_attn_decode_workspace_bytes(B, Hq, S, D) // 4
+                self.args = [(q0, k0 if i == 0 else k0.clone(), v0 if i == 0 else v0.clone(), torch.empty_like(q0),
+                              torch.empty((B, Hq), dtype=torch.float32, device=dev),
+                              torch.empty(ws_n, dtype=torch.float32, device=dev)) for i in range(sets)]
+
+            def launch(self, k):
+                q, kk, vv, o, lse, ws = self.args[k]
+                fr.fr_attn_decode(q, kk, vv, o, lse=lse, ws=ws)
+
+            def output(self, k):
+                return self.args[k][3]
+
+            def config(self):
+                return {"workload": "decode attention, batch 8, 32 query heads on 8 key-value heads, 8192 keys, "
+                                    "head dim 128, bf16", "batch": B, "heads_q": Hq, "heads_kv": Hkv, "seq": S,
+                        "dim": D, "chunk_keys": 256}
+
+            def oracle_fn(self):
+                import oracle
+                from_bf = lambda u: (u.astype(np.uint32) << 16).view(np.float32).astype(np.float64)  # noqa: E731
+                qs, ks, vs = from_bf(q_h[:1]), from_bf(k_h[:1]), from_bf(v_h[:1])
+                return (lambda: oracle.attn_decode(qs, ks, vs), nbytes // B, "batch 1 of 8")
+
+        return W(), per_set
+
     if name in ("stream_copy", "stream_copy_c3", "stream_read"):
         # practical ceilings: the library's streaming reference kernels over the
         # bytes of the softmax 4096x1024 step (16 MiB in, 16 MiB out), of the
@@ -393,7 +435,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="softmax",
                     choices=["softmax", "sum_relu_add", "layernorm", "sumsq", "ragged", "copy", "stream_copy",
-                             "stream_copy_c3", "stream_read"])
+                             "stream_copy_c3", "stream_read", "attn_decode"])
     ap.add_argument("--warm", action="store_true", help="one buffer set: reads may hit the MALL")
     ap.add_argument("--eager", action="store_true", help="launch each step from the host (no graph)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)

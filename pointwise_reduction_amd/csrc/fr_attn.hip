@@ -12,21 +12,35 @@
 //
 //   fr_attn_part     workgroup (chunk c, key-value head, batch): the keys
 //                    [c * kAttnChunk, ...) of that head. Scores s = scale q.k
-//                    for the G rows (lane groups of VPR lanes hold one key row
-//                    each, so a wave instruction reads KPW whole rows), the
-//                    chunk maximum and sum of e^{s - m}, then a = sum p v.
-//                    Writes the chunk's (m, l, a[D]) for each of the G rows.
-//   fr_attn_combine  wave per (b, h): merges the chunk triples in chunk order
-//                    with (+), writes o = a / l and lse = m + log l.
+//                    for the G rows (bf16: 16x16 tiles of the matrix cores,
+//                    query rows padded to 16; fp32: lane groups of VPR lanes
+//                    hold one key row each and sum their partial dots), the
+//                    chunk maximum and sum of e^{s - m}, then a = sum p v on
+//                    the vector units (p stays fp32). Writes the chunk's
+//                    (m, l, a[D]) for each of the G rows.
+//   fr_attn_combine  workgroup per (b, h): merges the chunk triples with (+) (the
+//                    largest maximum first, then weighted sums in chunk
+//                    order), writes o = a / l and lse = m + log l.
 //
-// Memory-bound: each key and value row is read once (no contraction is
-// large enough for the matrix cores: G <= 8 rows per key-value head).
+// Memory-bound: each key and value row is read once. The score contraction
+// runs on the matrix cores for bf16, which takes it off the vector units;
+// the value contraction stays on the vector units because its left operand
+// (the probabilities) would lose precision as bf16.
 #include <limits.h>
 
 #include "fr_device.h"
 #include "fr_internal.h"
 
 namespace fr {
+
+#ifndef FR_ATTN_VALUE_BATCH
+#define FR_ATTN_VALUE_BATCH 16
+#endif
+constexpr int kAttnValueBatch = FR_ATTN_VALUE_BATCH;  // value vectors in flight per lane
+#ifndef FR_ATTN_KEY_TILES
+#define FR_ATTN_KEY_TILES 2
+#endif
+constexpr int kAttnKeyTiles = FR_ATTN_KEY_TILES;  // bf16: 16-key tiles whose loads are in flight together
 
 // Element access for fp32 and bf16 (uint16 bits) rows, 16 bytes at a time.
 template <typename DT>
@@ -39,6 +53,10 @@ struct Elems<float> {
         out[1] = raw.y;
         out[2] = raw.z;
         out[3] = raw.w;
+    }
+    // q . k over the 4 elements of one vector
+    __device__ __forceinline__ static float dot(f32x4 a, f32x4 b) {
+        return ((a.x * b.x + a.y * b.y) + a.z * b.z) + a.w * b.w;
     }
 };
 template <>
@@ -92,8 +110,9 @@ __global__ __launch_bounds__(256) void fr_attn_part(const DT* __restrict__ q, co
     constexpr int KPW = kWave / VPR;               // keys per wave instruction
     constexpr int KPS = 4 * KPW;                   // keys per workgroup step (4 waves)
     constexpr int NSTEP = kAttnChunk / KPS;        // steps per chunk
-    constexpr int BATCH = NSTEP < 8 ? NSTEP : 8;   // vectors loaded per lane before use
-    static_assert(kAttnChunk % KPS == 0 && NSTEP % BATCH == 0, "chunk geometry");
+    constexpr int BATCH = NSTEP < 8 ? NSTEP : 8;   // key vectors loaded per lane before use (fp32)
+    constexpr int VB = NSTEP < kAttnValueBatch ? NSTEP : kAttnValueBatch;  // value vectors likewise
+    static_assert(kAttnChunk % KPS == 0 && NSTEP % BATCH == 0 && NSTEP % VB == 0, "chunk geometry");
     constexpr int SLOT = D + 4;                    // floats per (row, chunk) triple: m, l, pad, pad, a[D]
     __shared__ float s_p[G][kAttnChunk];           // scores, then e^{s - m}
     __shared__ float s_red[2][G][4];               // cross-wave folds of the maxima and sums
@@ -109,10 +128,52 @@ __global__ __launch_bounds__(256) void fr_attn_part(const DT* __restrict__ q, co
     const int64_t kv_base = ((int64_t)b * Hkv + hk) * S;
     const int h0 = hk * G;
 
-    // this lane's slice of the G query rows
-    float qs[G][EPV];
+    if constexpr (EPV == 8) {
+        // bf16: the scores of 16 keys x 16 query rows (rows >= G are zero)
+        // are one 16x16 tile of v_mfma_f32_16x16x32_bf16 per 32 dims: lane l
+        // holds query row l % 16 and key l % 16 at dims 8 (l / 16) .. +7 of
+        // each 32-dim slice, and receives the scores of key l % 16 for rows
+        // 4 (l / 16) .. +3. Wave w scores the keys 64 w .. 64 w + 63 of the chunk.
+        typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+        constexpr int NS = D / 32;  // 32-dim slices
+        constexpr int TPW = kAttnChunk / (4 * 16);  // key tiles per wave
+        const int n = lane & 15, kq = lane >> 4;
+        f32x4 qa[NS];
 #pragma unroll
-    for (int g = 0; g < G; ++g) E::unpack(ld16(q + ((int64_t)b * Hq + h0 + g) * D + vl * EPV), qs[g]);
+        for (int sl = 0; sl < NS; ++sl)
+            qa[sl] = n < G ? ld16(q + ((int64_t)b * Hq + h0 + n) * D + sl * 32 + kq * 8) : f32x4{0.f, 0.f, 0.f, 0.f};
+        constexpr int KT = TPW < kAttnKeyTiles ? TPW : kAttnKeyTiles;
+#pragma unroll
+        for (int t0 = 0; t0 < TPW; t0 += KT) {
+            f32x4 kb[KT][NS];
+#pragma unroll
+            for (int t = 0; t < KT; ++t) {
+                const int j = c0 + w * 64 + (t0 + t) * 16 + n;
+#pragma unroll
+                for (int sl = 0; sl < NS; ++sl)
+                    kb[t][sl] = j < L ? ld16_nt(k + (kv_base + j) * D + sl * 32 + kq * 8) : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int t = 0; t < KT; ++t) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int sl = 0; sl < NS; ++sl)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[sl]),
+                                                                  __builtin_bit_cast(bf16x8, kb[t][sl]), acc, 0, 0, 0);
+                const int jj = w * 64 + (t0 + t) * 16 + n;  // key index within the chunk
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int g = kq * 4 + i;
+                    if (g < G) s_p[g][jj] = c0 + jj < L ? acc[i] * scale : -INFINITY;
+                }
+            }
+        }
+    } else {
+    // fp32: lane groups of VPR lanes hold one key row; partial dot products
+    // are summed across the group
+    f32x4 qs[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) qs[g] = ld16(q + ((int64_t)b * Hq + h0 + g) * D + vl * EPV);
 
     // scores: step i, wave w, lane group grp hold key c0 + i * KPS + w * KPW + grp
 #pragma unroll
@@ -126,17 +187,22 @@ __global__ __launch_bounds__(256) void fr_attn_part(const DT* __restrict__ q, co
 #pragma unroll
         for (int u = 0; u < BATCH; ++u) {
             const int jj = (i0 + u) * KPS + w * KPW + grp;  // key index within the chunk
-            float ke[EPV];
-            E::unpack(kv[u], ke);
 #pragma unroll
             for (int g = 0; g < G; ++g) {
-                float d = 0.f;
-#pragma unroll
-                for (int e = 0; e < EPV; ++e) d += qs[g][e] * ke[e];
-                d = lane_group_sum<VPR>(d);
+                const float d = lane_group_sum<VPR>(E::dot(qs[g], kv[u]));
                 if (vl == 0) s_p[g][jj] = c0 + jj < L ? d * scale : -INFINITY;
             }
         }
+    }
+    }
+    // the first batch of values goes out now, so that its latency overlaps
+    // the chunk softmax below
+    f32x4 vpre[VB];
+#pragma unroll
+    for (int u = 0; u < VB; ++u) {
+        const int j = c0 + u * KPS + w * KPW + grp;
+        // past len_b: zeros (the tail is never read, and p = 0 there)
+        vpre[u] = j < L ? ld16_nt(v + (kv_base + j) * D + vl * EPV) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
     __syncthreads();
 
@@ -173,16 +239,15 @@ __global__ __launch_bounds__(256) void fr_attn_part(const DT* __restrict__ q, co
 #pragma unroll
         for (int e = 0; e < EPV; ++e) acc[g][e] = 0.f;
 #pragma unroll
-    for (int i0 = 0; i0 < NSTEP; i0 += BATCH) {
-        f32x4 vv[BATCH];
+    for (int i0 = 0; i0 < NSTEP; i0 += VB) {
+        f32x4 vv[VB];
 #pragma unroll
-        for (int u = 0; u < BATCH; ++u) {
+        for (int u = 0; u < VB; ++u) {
             const int j = c0 + (i0 + u) * KPS + w * KPW + grp;
-            // past len_b: zeros (the tail is never read, and p = 0 there)
-            vv[u] = j < L ? ld16_nt(v + (kv_base + j) * D + vl * EPV) : f32x4{0.f, 0.f, 0.f, 0.f};
+            vv[u] = i0 == 0 ? vpre[u] : (j < L ? ld16_nt(v + (kv_base + j) * D + vl * EPV) : f32x4{0.f, 0.f, 0.f, 0.f});
         }
 #pragma unroll
-        for (int u = 0; u < BATCH; ++u) {
+        for (int u = 0; u < VB; ++u) {
             const int jj = (i0 + u) * KPS + w * KPW + grp;
             float ve[EPV];
             E::unpack(vv[u], ve);
@@ -222,48 +287,109 @@ __device__ __forceinline__ void store_out(uint16_t* o, int d, float x) {
     o[d] = (uint16_t)(pack_bf16(x, 0.f) & 0xFFFFu);
 }
 
-// Wave per (b, h); lane l owns dims l, l + 64, ... The chunks of the row are
-// merged in chunk order: mu = max(m, m_c), factors e^{m - mu} and e^{m_c - mu}
-// (0 for a state whose maximum is -inf: the identity).
+// Workgroup of four waves per (b, h); lane l owns dims l, l + 64, ... The
+// chunk triples of the row are merged as one (+) over all of them: mu = the
+// largest chunk maximum, weights f_c = e^{m_c - mu} (0 for a state whose
+// maximum is -inf, the identity), l = sum_c f_c l_c and a = sum_c f_c a_c.
+// Wave w sums the chunks of the w-th quarter of each group of 64 in chunk
+// order; the four quarter sums are added in wave order. Every thread derives
+// mu and l itself (the same reads, the same order), so all agree.
 template <int D, typename DT>
-__global__ __launch_bounds__(64) void fr_attn_combine(const float* __restrict__ ws,
-                                                      const int32_t* __restrict__ lengths, DT* __restrict__ o,
-                                                      float* __restrict__ lse, int Hq, int S, int nchunks) {
+__global__ __launch_bounds__(256) void fr_attn_combine(const float* __restrict__ ws,
+                                                       const int32_t* __restrict__ lengths, DT* __restrict__ o,
+                                                       float* __restrict__ lse, int Hq, int S, int nchunks) {
     constexpr int SLOT = D + 4;
     constexpr int PER = D / kWave;
+    __shared__ float s_f[kWave];
+    __shared__ float s_a[4][D];
     const int row = blockIdx.x;  // b * Hq + h
     const int b = row / Hq;
-    const int lane = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid >> 6;
     int L = lengths ? lengths[b] : S;
     L = L < 0 ? 0 : (L > S ? S : L);
     const int nc = (L + kAttnChunk - 1) / kAttnChunk;
-    float mm = -INFINITY, ll = 0.f;
+    DT* orow = o + (int64_t)row * D;
+    if (nc == 0) {
+        if (w == 0) {
+#pragma unroll
+            for (int e = 0; e < PER; ++e) store_out(orow, lane + e * kWave, 0.f);
+            if (lse && lane == 0) lse[row] = -INFINITY;
+        }
+        return;
+    }
+    const float* base = ws + (int64_t)row * nchunks * SLOT;
+    float mu = -INFINITY;
+    float ll = 0.f;
     float a[PER];
 #pragma unroll
     for (int e = 0; e < PER; ++e) a[e] = 0.f;
-    const float* base = ws + (int64_t)row * nchunks * SLOT;
-    for (int c = 0; c < nc; ++c) {
-        const float* slot = base + (int64_t)c * SLOT;
-        const float mc = slot[0], lc = slot[1];
-        const float mu = fmax_nan(mm, mc);
-        const float f1 = mm == -INFINITY ? 0.f : exp_fast(mm - mu);
-        const float f2 = mc == -INFINITY ? 0.f : exp_fast(mc - mu);
-        ll = ll * f1 + lc * f2;
+    if (nc <= kWave) {
+        // one group of chunks: every read is issued before any arithmetic
+        // (same operations in the same order as the general loop below)
+        constexpr int QMAX = kWave / 4;
+        const int q0 = (nc * w) / 4, q1 = (nc * (w + 1)) / 4;
+        float mc = -INFINITY, lc = 0.f;
+        if (lane < nc) {
+            mc = base[(int64_t)lane * SLOT];
+            lc = base[(int64_t)lane * SLOT + 1];
+        }
+        float av[QMAX][PER];
 #pragma unroll
-        for (int e = 0; e < PER; ++e) a[e] = a[e] * f1 + slot[4 + lane + e * kWave] * f2;
-        mm = mu;
+        for (int j = 0; j < QMAX; ++j)
+#pragma unroll
+            for (int e = 0; e < PER; ++e)
+                av[j][e] = q0 + j < q1 ? base[(int64_t)(q0 + j) * SLOT + 4 + lane + e * kWave] : 0.f;
+        mu = group_reduce<kWave>(mc, OpMax());
+        const float f = lane < nc && mc != -INFINITY ? exp_fast(mc - mu) : 0.f;
+        ll = group_reduce<kWave>(f * lc, OpSum());
+#pragma unroll
+        for (int j = 0; j < QMAX; ++j) {
+            const float fj = __shfl(f, q0 + j, kWave);
+            if (q0 + j < q1) {
+#pragma unroll
+                for (int e = 0; e < PER; ++e) a[e] += fj * av[j][e];
+            }
+        }
+    } else {
+    for (int g0 = 0; g0 < nc; g0 += kWave) {
+        const int c = g0 + lane;
+        mu = fmax_nan(mu, group_reduce<kWave>(c < nc ? base[(int64_t)c * SLOT] : -INFINITY, OpMax()));
     }
-    DT* orow = o + (int64_t)row * D;
-    if (nc == 0) {
+    for (int g0 = 0; g0 < nc; g0 += kWave) {
+        const int c = g0 + lane;
+        float f = 0.f, lc = 0.f;
+        if (c < nc) {
+            const float mc = base[(int64_t)c * SLOT];
+            lc = base[(int64_t)c * SLOT + 1];
+            f = mc == -INFINITY ? 0.f : exp_fast(mc - mu);
+        }
+        ll += group_reduce<kWave>(f * lc, OpSum());
+        if (w == 0) s_f[lane] = f;
+        __syncthreads();
+        const int n = nc - g0 < kWave ? nc - g0 : kWave;
+        const int q0 = (n * w) / 4, q1 = (n * (w + 1)) / 4;  // this wave's quarter of the group
+#pragma unroll 4
+        for (int j = q0; j < q1; ++j) {
+            const float fj = s_f[j];
+            const float* slot = base + (int64_t)(g0 + j) * SLOT + 4;
 #pragma unroll
-        for (int e = 0; e < PER; ++e) store_out(orow, lane + e * kWave, 0.f);
-        if (lse && lane == 0) lse[row] = -INFINITY;
-        return;
+            for (int e = 0; e < PER; ++e) a[e] += fj * slot[lane + e * kWave];
+        }
+        __syncthreads();  // s_f is rewritten by the next group
     }
-    const float inv = 1.0f / ll;
+    }
 #pragma unroll
-    for (int e = 0; e < PER; ++e) store_out(orow, lane + e * kWave, a[e] * inv);
-    if (lse && lane == 0) lse[row] = mm + logf(ll);
+    for (int e = 0; e < PER; ++e) s_a[w][lane + e * kWave] = a[e];
+    __syncthreads();
+    if (w == 0) {
+        const float inv = 1.0f / ll;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            const int d = lane + e * kWave;
+            store_out(orow, d, ((s_a[0][d] + s_a[1][d]) + (s_a[2][d] + s_a[3][d])) * inv);
+        }
+        if (lse && lane == 0) lse[row] = mu + logf(ll);
+    }
 }
 
 namespace {
@@ -302,7 +428,7 @@ hipError_t launch_attn_t(const AttnArgs& a, hipStream_t s) {
         if (e != hipSuccess) return e;
     }
     auto comb = a.dim == 128 ? fr_attn_combine<128, DT> : fr_attn_combine<64, DT>;
-    hipLaunchKernelGGL(comb, dim3((unsigned)(a.batch * a.heads_q)), dim3(64), 0, s, a.ws, a.lengths,
+    hipLaunchKernelGGL(comb, dim3((unsigned)(a.batch * a.heads_q)), dim3(256), 0, s, a.ws, a.lengths,
                        static_cast<DT*>(a.o), a.lse, a.heads_q, a.seq, nchunks);
     return hipGetLastError();
 }

@@ -83,6 +83,7 @@ CASES = [
     (2, 16, 4, 1100, 64, False, None),
     (1, 2, 1, 256, 64, True, None),
     (1, 1, 1, 1, 128, False, None),
+    (2, 4, 2, 20000, 64, True, (20000, 16385)),  # more than 64 chunks of 256 keys
 ]
 
 
