@@ -52,6 +52,7 @@ def _load():
         "orc_layernorm_rows": (None, [P, P, P, I64, I64, I64, F64, P, P, P, I64]),
         "orc_sumsq": (F64, [P, I64]),
         "orc_sumsq_rows": (None, [P, I64, I64, I64, P]),
+        "orc_softmax_backward_rows": (None, [P, P, I64, I64, I64, I64, P, P, P]),
         "orc_attn_decode": (None, [P, P, P, I64, I64, I64, I64, I64, P, F64, P, P, P, P, P]),
         "orc_attn_merge": (None, [F64, F64, P, F64, F64, P, I64, P, P, P]),
     }
@@ -130,6 +131,20 @@ def softmax_rows(x, lengths=None, cols=None):
     scratch = np.empty(2 * max(cols, 1), dtype=np.float64)
     _load().orc_softmax_rows(_p(x), rows, cols, x_rs, _p(L), None, _p(y64), cols, _p(am), _p(scratch))
     return y64, am
+
+
+def softmax_backward_rows(y, dy, lengths=None):
+    """dx = y * (dy - sum(dy * y)) per row in fp64 (see orc_softmax_backward_rows).
+    y, dy: fp32 [rows, cols] (2-D views with unit inner stride). Returns
+    (dx64, mag), NaN past each row's length."""
+    y, rows, cols, y_rs = _rows2d(y, np.float32)
+    dy, rows2, cols2, dy_rs = _rows2d(dy, np.float32)
+    assert (rows2, cols2) == (rows, cols)
+    L = None if lengths is None else np.ascontiguousarray(lengths, dtype=np.int32)
+    dx = np.full((rows, cols), np.nan)
+    mag = np.full((rows, cols), np.nan)
+    _load().orc_softmax_backward_rows(_p(y), _p(dy), rows, cols, y_rs, dy_rs, _p(L), _p(dx), _p(mag))
+    return dx, mag
 
 
 def md_combine(m1, d1, m2, d2):

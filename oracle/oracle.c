@@ -22,6 +22,8 @@
  *            template that splits the keys).
  *   [L8]     "CMU 15-779 Lecture 8: ML Compilers Part 1, Tile-based DSLs",
  *            section 3 (fused softmax) and Exercise 1 (row L2 norm).
+ * Backward passes (softmax, LayerNorm) are not defined on the pages; they
+ * are the derivatives of the forward definitions above, as stated at each.
  * Readings of points the pages leave open are stated at each function.
  */
 #include <math.h>
@@ -196,6 +198,39 @@ void orc_online_attention_row(const double* s, const double* V, int64_t n, int64
     *m_out = m;
     *l_out = l;
     for (int64_t k = 0; k < dv; ++k) o[k] = a[k] / l;
+}
+
+/* ------------------------------------------------------ softmax backward */
+
+/*
+ * Gradient of the row softmax ([Stax4] 9.5 defines y = softmax(x); the
+ * gradient is not on the pages and is taken from the calculus of that
+ * definition): with L depending on y and dy = dL/dy,
+ *   dx_j = y_j (dy_j - sum_k dy_k y_k).
+ * Written out in fp64 over fp32 rows; row r covers j < len_r (lengths
+ * clamped to [0, cols], NULL: cols) and nothing beyond is read or written.
+ *   dx64 (row stride cols): the result; untouched past len_r.
+ *   mag  (nullable, row stride cols): |y_j dy_j| + y_j sum_k |dy_k y_k|,
+ *        the size of the terms of dx_j.
+ */
+void orc_softmax_backward_rows(const float* y, const float* dy, int64_t rows, int64_t cols, int64_t y_rs,
+                               int64_t dy_rs, const int32_t* lengths, double* dx64, double* mag) {
+    for (int64_t r = 0; r < rows; ++r) {
+        int64_t L = lengths ? lengths[r] : cols;
+        if (L < 0) L = 0;
+        if (L > cols) L = cols;
+        const float* yr = y + r * y_rs;
+        const float* gr = dy + r * dy_rs;
+        double s = 0.0, sa = 0.0;
+        for (int64_t j = 0; j < L; ++j) {
+            s += (double)gr[j] * (double)yr[j];
+            sa += fabs((double)gr[j] * (double)yr[j]);
+        }
+        for (int64_t j = 0; j < L; ++j) {
+            dx64[r * cols + j] = (double)yr[j] * ((double)gr[j] - s);
+            if (mag) mag[r * cols + j] = fabs((double)yr[j] * (double)gr[j]) + fabs((double)yr[j]) * sa;
+        }
+    }
 }
 
 /* ------------------------------------------------------ attention decode */

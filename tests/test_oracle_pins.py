@@ -459,3 +459,58 @@ def test_attn_decode_nan_propagates():
     k[0, 0, 1, 2] = np.nan
     o, lse, _, _ = oracle.attn_decode(q, k, v)
     assert np.all(np.isnan(o)) and np.isnan(lse[0, 0])
+
+
+# ------------------------------------------------------------------ softmax backward
+
+
+def test_softmax_backward_matches_finite_differences():
+    """dx is the gradient of L(x) = sum_j dy_j softmax(x)_j: its dot product
+    with a direction u equals the central difference of L along u (forward
+    oracle, fp64), for several random rows and directions."""
+    rng = np.random.default_rng(81)
+    for n in (1, 2, 7, 40):
+        x = rng.normal(size=n) * 2
+        dy = rng.normal(size=n)
+        y = oracle.softmax_f64(x)
+        dx, _ = oracle.softmax_backward_rows(y[None].astype(np.float32), dy[None].astype(np.float32))
+        yf, dyf = y.astype(np.float32).astype(np.float64), dy.astype(np.float32).astype(np.float64)
+        dx_exact = yf * (dyf - (dyf * yf).sum())  # same inputs as the oracle saw
+        assert np.allclose(dx[0], dx_exact, rtol=1e-14, atol=1e-16)
+        for _ in range(3):
+            u = rng.normal(size=n)
+            eps = 1e-6
+            Lp = float(dyf @ oracle.softmax_f64(x + eps * u))
+            Lm = float(dyf @ oracle.softmax_f64(x - eps * u))
+            # the gradient formula evaluated at the exact y of x
+            g = y * (dyf - (dyf * y).sum())
+            assert float(g @ u) == pytest.approx((Lp - Lm) / (2 * eps), rel=1e-6, abs=1e-9)
+
+
+def test_softmax_backward_closed_forms():
+    rng = np.random.default_rng(82)
+    y = oracle.softmax_f64(rng.normal(size=9)).astype(np.float32)[None]
+    yd = y.astype(np.float64)[0]
+    # dy constant: dx = y (c - c sum y), zero up to the rounding of sum y
+    dx, _ = oracle.softmax_backward_rows(y, np.full_like(y, 3.0))
+    assert np.allclose(dx, 3.0 * yd * (1 - yd.sum()), rtol=0, atol=1e-15)
+    # dy = e_i: dx_j = y_j (delta_ij - y_i)
+    for i in (0, 4, 8):
+        e = np.zeros_like(y)
+        e[0, i] = 1
+        dx, mag = oracle.softmax_backward_rows(y, e)
+        want = yd * ((np.arange(9) == i) - yd[i])
+        assert np.allclose(dx[0], want, rtol=1e-15, atol=1e-18)
+        assert np.all(mag[0] >= np.abs(dx[0]) - 1e-18)
+
+
+def test_softmax_backward_ragged_rows():
+    rng = np.random.default_rng(83)
+    y = rng.random((4, 10)).astype(np.float32)
+    dy = rng.normal(size=(4, 10)).astype(np.float32)
+    L = np.array([0, 3, 10, 12], dtype=np.int32)
+    dx, _ = oracle.softmax_backward_rows(y, dy, lengths=L)
+    assert np.all(np.isnan(dx[0])) and np.all(np.isnan(dx[1, 3:]))
+    full, _ = oracle.softmax_backward_rows(y[1:2, :3].copy(), dy[1:2, :3].copy())
+    assert np.array_equal(dx[1, :3], full[0])
+    assert not np.isnan(dx[2:]).any()
