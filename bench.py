@@ -299,6 +299,47 @@ def make_workload(name, torch, fr, synth):
 
         return W(), per_set
 
+    if name == "softmax_bwd":
+        # softmax backward over the 4096 x 1024 fp32 softmax output
+        rows, cols = 4096, 1024
+        x_h = synth.softmax_inputs(rows, cols, seed=2001)
+        dy_h = synth.normal((rows, cols), 2001, stream=7)
+        per_set = 3 * rows * cols * 4
+
+        class W(Workload):
+            kernel = "fr_per_softmax_bwd_f32"
+            bytes = 3 * rows * cols * 4
+            dtype = "f32"
+
+            def alloc(self, sets):
+                y0 = torch.empty((rows, cols), dtype=torch.float32, device=dev)
+                fr.fr_softmax_rows(d(x_h), y0)
+                g0 = d(dy_h)
+                torch.cuda.synchronize()
+                self.y_h = y0.cpu().numpy()
+                self.args = [(y0 if i == 0 else y0.clone(), g0 if i == 0 else g0.clone(), torch.empty_like(y0))
+                             for i in range(sets)]
+
+            def launch(self, k):
+                y, g, dx = self.args[k]
+                fr.fr_softmax_rows_backward(y, g, dx)
+
+            def output(self, k):
+                return self.args[k][2]
+
+            def config(self):
+                p = fr.fr_plan_query(fr.FR_OP_SOFTMAX_BWD, rows, cols)
+                return {"workload": "softmax backward 4096x1024 fp32 (y = the forward output, dy ~ N(0,1))",
+                        "rows": rows, "cols": cols, "form": fr.FORM_NAMES[p.form]}
+
+            def oracle_fn(self):
+                import oracle
+                r = 1024
+                y, g = self.y_h[:r].copy(), dy_h[:r].copy()
+                return lambda: oracle.softmax_backward_rows(y, g), 3 * r * cols * 4, f"first {r} of {rows} rows"
+
+        return W(), per_set
+
     if name == "attn_decode":
         # decode attention: batch 8, 32 query heads on 8 key-value heads,
         # 8192 keys, head dim 128, bf16 (each key and value byte read once)
@@ -435,7 +476,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="softmax",
                     choices=["softmax", "sum_relu_add", "layernorm", "sumsq", "ragged", "copy", "stream_copy",
-                             "stream_copy_c3", "stream_read", "attn_decode"])
+                             "stream_copy_c3", "stream_read", "attn_decode", "softmax_bwd"])
     ap.add_argument("--warm", action="store_true", help="one buffer set: reads may hit the MALL")
     ap.add_argument("--eager", action="store_true", help="launch each step from the host (no graph)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)

@@ -73,6 +73,7 @@ extern "C" {
 #define FR_OP_SOFTMAX 2
 #define FR_OP_LAYERNORM 3
 #define FR_OP_SUMSQ 4
+#define FR_OP_SOFTMAX_BWD 5
 
 /* Launch plan chosen for one call: the reduction form and its launch
  * configuration ("Stax (4)", 9.6: block sizes and warp counts are launch
@@ -177,6 +178,22 @@ uint64_t fr_softmax_rows_workspace_bytes(int64_t rows, int64_t cols, int dtype);
 int fr_softmax_rows(const void* x, void* y, int64_t rows, int64_t cols, int64_t x_rs, int64_t x_cs, int64_t y_rs,
                     int64_t y_cs, const int32_t* lengths, int32_t* argmax, void* ws, uint64_t ws_bytes, int dtype,
                     void* stream);
+
+/* ------------------------------------------------------------ row softmax, backward
+ * dx[i,j] = y[i,j] * (dy[i,j] - sum_k dy[i,k] y[i,k]): the gradient of the
+ * row softmax of "Stax (4)", 9.5 with respect to its input, given its output
+ * y and the upstream gradient dy (the derivative of that definition; the
+ * pages define the forward pass). One fused row reduction (the dot product
+ * of dy and y) followed by the pointwise epilogue, in the persistent or the
+ * looped form.
+ *  y, dy, dx: fp32 [rows, cols]; strides as in the conventions; dx may be
+ *             y or dy (same row stride).
+ *  lengths:   optional int32[rows] as in fr_softmax_rows: row i covers
+ *             j < len_i only; nothing beyond is read or written.
+ * dtype must be FR_F32. */
+int fr_softmax_rows_backward(const void* y, const void* dy, void* dx, int64_t rows, int64_t cols, int64_t y_rs,
+                             int64_t y_cs, int64_t dy_rs, int64_t dy_cs, int64_t dx_rs, int64_t dx_cs,
+                             const int32_t* lengths, int dtype, void* stream);
 
 /* ------------------------------------------------------------ LayerNorm
  * y[i,j] = (x[i,j] - mu_i) * rstd_i * gamma[j] + beta[j],

@@ -28,14 +28,14 @@ FR_E_NULL, FR_E_SIZE, FR_E_STRIDE, FR_E_DTYPE, FR_E_ALIGN = -1, -2, -3, -4, -5
 FR_E_WORKSPACE, FR_E_ARG, FR_E_DEVICE, FR_E_LAUNCH = -6, -7, -8, -9
 FR_F32, FR_BF16 = 0, 1
 FR_FORM_AUTO, FR_FORM_PER, FR_FORM_RED, FR_FORM_SPLIT = 0, 1, 2, 3
-FR_OP_SUM_RELU_ADD, FR_OP_SOFTMAX, FR_OP_LAYERNORM, FR_OP_SUMSQ = 1, 2, 3, 4
+FR_OP_SUM_RELU_ADD, FR_OP_SOFTMAX, FR_OP_LAYERNORM, FR_OP_SUMSQ, FR_OP_SOFTMAX_BWD = 1, 2, 3, 4, 5
 FORM_NAMES = {FR_FORM_PER: "per", FR_FORM_RED: "red", FR_FORM_SPLIT: "split"}
 
 # Every symbol include/fr.h declares.
 EXPORTS = (
     "fr_status_string", "fr_version", "fr_plan_query", "fr_force_form", "fr_tune_override",
     "fr_sum_relu_add", "fr_sum_workspace_bytes",
-    "fr_softmax_rows_workspace_bytes", "fr_softmax_rows",
+    "fr_softmax_rows_workspace_bytes", "fr_softmax_rows", "fr_softmax_rows_backward",
     "fr_layernorm_rows",
     "fr_sumsq_rows", "fr_sumsq_full_workspace_bytes", "fr_sumsq_full",
     "fr_stream_copy", "fr_stream_read",
@@ -79,6 +79,7 @@ def _load():
         "fr_sum_workspace_bytes": (U64, [I64, I64, I32]),
         "fr_softmax_rows_workspace_bytes": (U64, [I64, I64, I32]),
         "fr_softmax_rows": (I32, [P, P, I64, I64, I64, I64, I64, I64, P, P, P, U64, I32, P]),
+        "fr_softmax_rows_backward": (I32, [P, P, P, I64, I64, I64, I64, I64, I64, I64, I64, P, I32, P]),
         "fr_layernorm_rows": (I32, [P, P, P, P, I64, I64, I64, I64, I64, I64, ctypes.c_float, I32, P]),
         "fr_sumsq_rows": (I32, [P, P, I64, I64, I64, I64, P, U64, I32, P]),
         "fr_sumsq_full_workspace_bytes": (U64, [I64, I32]),
@@ -196,6 +197,18 @@ def fr_softmax_rows(x, y, lengths=None, argmax=None, ws=None, stream=None):
     _check(lib.fr_softmax_rows(_ptr(x), _ptr(y), rows, cols, x_rs, x_cs, y_rs, y_cs, _ptr(lengths), _ptr(argmax),
                                _ptr(ws), ws_bytes, _dtype_code(x), _stream(stream)), "fr_softmax_rows")
     return y
+
+
+def fr_softmax_rows_backward(y, dy, dx, lengths=None, stream=None):
+    """dx = y * (dy - sum(dy * y)) per row (fp32 [rows, cols] views)."""
+    rows, cols, y_rs, y_cs = _mat(y)
+    r2, c2, dy_rs, dy_cs = _mat(dy)
+    r3, c3, dx_rs, dx_cs = _mat(dx)
+    if (r2, c2) != (rows, cols) or (r3, c3) != (rows, cols):
+        raise ValueError("shape mismatch")
+    _check(lib.fr_softmax_rows_backward(_ptr(y), _ptr(dy), _ptr(dx), rows, cols, y_rs, y_cs, dy_rs, dy_cs, dx_rs, dx_cs,
+                                        _ptr(lengths), _dtype_code(y), _stream(stream)), "fr_softmax_rows_backward")
+    return dx
 
 
 def fr_layernorm_rows(x, y, gamma=None, beta=None, eps=1e-5, stream=None):

@@ -29,9 +29,9 @@ namespace {
 int g_forced_form = FR_FORM_AUTO;
 
 // Tuning overrides, one per operation (index = FR_OP_*).
-constexpr int kOps = 5;
+constexpr int kOps = 6;
 fr_plan g_override[kOps];
-bool g_has_override[kOps] = {false, false, false, false, false};
+bool g_has_override[kOps] = {};
 
 const fr_plan* override_for(int op) { return (op > 0 && op < kOps && g_has_override[op]) ? &g_override[op] : nullptr; }
 
@@ -291,6 +291,32 @@ int fr_layernorm_rows(const void* x, const void* gamma, const void* beta, void* 
                        (int)rows, (int)cols, x_rs, y_rs, eps};
     (void)hipGetLastError();
     return finish_launch(launch_layernorm(plan, args, (hipStream_t)stream));
+}
+
+int fr_softmax_rows_backward(const void* y, const void* dy, void* dx, int64_t rows, int64_t cols, int64_t y_rs,
+                             int64_t y_cs, int64_t dy_rs, int64_t dy_cs, int64_t dx_rs, int64_t dx_cs,
+                             const int32_t* lengths, int dtype, void* stream) {
+    int st = check_sizes(rows, cols);
+    if (st != FR_OK) return st;
+    if (dtype != FR_F32) return FR_E_DTYPE;
+    if (rows == 0 || cols == 0) return FR_OK;  // nothing to read or write
+    if ((st = check_matrix(y, rows, cols, y_rs, y_cs, 4)) != FR_OK) return st;
+    if ((st = check_matrix(dy, rows, cols, dy_rs, dy_cs, 4)) != FR_OK) return st;
+    if ((st = check_matrix(dx, rows, cols, dx_rs, dx_cs, 4)) != FR_OK) return st;
+    if ((dx == y && dx_rs != y_rs) || (dx == dy && dx_rs != dy_rs)) return FR_E_STRIDE;
+    if (!aligned(lengths, 4)) return FR_E_ALIGN;
+    int num_cus = 0;
+    st = device_check(&num_cus);
+    if (st != FR_OK) return st;
+    const int v16 = vec_ok(y, y_rs, 4) && vec_ok(dy, dy_rs, 4) && vec_ok(dx, dx_rs, 4);
+    fr_plan plan;
+    st = make_plan(FR_OP_SOFTMAX_BWD, rows, cols, FR_F32, num_cus, lengths != nullptr, 0, v16, g_forced_form,
+                   override_for(FR_OP_SOFTMAX_BWD), &plan);
+    if (st != FR_OK) return st;
+    SoftmaxBwdArgs args{(const float*)y, (const float*)dy, (float*)dx, (int)rows, (int)cols, y_rs, dy_rs, dx_rs,
+                        lengths};
+    (void)hipGetLastError();
+    return finish_launch(launch_softmax_bwd(plan, args, (hipStream_t)stream));
 }
 
 uint64_t fr_attn_decode_workspace_bytes(int64_t batch, int64_t heads_q, int64_t seq, int64_t dim) {

@@ -32,6 +32,15 @@ struct SoftmaxArgs {
     int64_t wait_ticks;      // single-pass split: wall-clock ticks a workgroup waits for a row's partials
 };
 
+struct SoftmaxBwdArgs {
+    const float* y;
+    const float* dy;
+    float* dx;
+    int rows, cols;
+    int64_t y_rs, dy_rs, dx_rs;
+    const int32_t* lengths;  // nullable
+};
+
 struct LayerNormArgs {
     const uint16_t* x;
     const uint16_t* gamma;  // nullable
@@ -59,6 +68,7 @@ struct alignas(16) SoftmaxPartial {
 hipError_t launch_sum(const fr_plan& p, const SumArgs& a, hipStream_t s);
 hipError_t launch_softmax(const fr_plan& p, const SoftmaxArgs& a, hipStream_t s);
 hipError_t launch_layernorm(const fr_plan& p, const LayerNormArgs& a, hipStream_t s);
+hipError_t launch_softmax_bwd(const fr_plan& p, const SoftmaxBwdArgs& a, hipStream_t s);
 
 // Decode attention: keys are split into chunks of kAttnChunk per workgroup;
 // the workspace holds one (m, l, pad, pad, a[dim]) fp32 slot per (batch,

@@ -572,6 +572,128 @@ __global__ __launch_bounds__(T) void fr_split_softmax_one(const float* x, float*
     }
 }
 
+// ------------------------------------------------------------------ backward
+// dx = y (dy - s), s = sum_k dy_k y_k: one row reduction (the dot product of
+// the upstream gradient with the forward output) and a pointwise epilogue.
+// Masked lanes read y = dy = 0 (the identity of the dot product); elements
+// past a row's length are neither read nor written.
+__device__ __forceinline__ float dot4(f32x4 a, f32x4 b) { return (a.x * b.x + a.y * b.y) + (a.z * b.z + a.w * b.w); }
+
+// Persistent: SEG lanes per row, NV vectors of y and NV of dy per lane, RPW
+// rows per lane group through each phase together (as the forward kernel).
+template <int SEG, int NV, int M, int RPW>
+__global__ __launch_bounds__(256) void fr_per_softmax_bwd_f32(const float* y, const float* dy, float* dx, int rows,
+                                                              int cols, int64_t y_rs, int64_t dy_rs, int64_t dx_rs,
+                                                              const int32_t* __restrict__ lengths) {
+    constexpr int RPB = 256 / SEG * RPW;
+    const int g = threadIdx.x / SEG;
+    const int l = threadIdx.x % SEG;
+    const int ngroups = (rows + RPB - 1) / RPB;
+    for (int grp = blockIdx.x; grp < ngroups; grp += gridDim.x) {
+        f32x4 a[RPW][NV], b[RPW][NV];
+        int L[RPW];
+#pragma unroll
+        for (int q = 0; q < RPW; ++q) {
+            const int r = grp * RPB + g * RPW + q;
+            const bool live = r < rows;
+            // kNone: a row past the end re-reads the last row (in bounds) and stores nothing
+            const int rl = live ? r : (M == kNone ? rows - 1 : 0);
+            if constexpr (M == kNone) L[q] = live ? cols : 0;
+            else L[q] = live ? row_len(lengths, r, cols) : 0;
+            const float* yr = y + (int64_t)rl * y_rs;
+            const float* gr = dy + (int64_t)rl * dy_rs;
+#pragma unroll
+            for (int k = 0; k < NV; ++k) {
+                const int j0 = (k * SEG + l) * 4;
+                if constexpr (M == kNone) {
+                    a[q][k] = ld4<true>(yr + j0);
+                    b[q][k] = ld4<true>(gr + j0);
+                } else {
+                    a[q][k] = load4m<M, true>(yr, j0, L[q], 0.f);
+                    b[q][k] = load4m<M, true>(gr, j0, L[q], 0.f);
+                }
+            }
+        }
+        float sdot[RPW];
+#pragma unroll
+        for (int q = 0; q < RPW; ++q) {
+            sdot[q] = 0.f;
+#pragma unroll
+            for (int k = 0; k < NV; ++k) sdot[q] += dot4(a[q][k], b[q][k]);
+        }
+#pragma unroll
+        for (int q = 0; q < RPW; ++q) sdot[q] = group_reduce<SEG>(sdot[q], OpSum());
+#pragma unroll
+        for (int q = 0; q < RPW; ++q) {
+            const int r = grp * RPB + g * RPW + q;
+            const bool live = r < rows;
+            float* xr = dx + (int64_t)(live ? r : 0) * dx_rs;
+#pragma unroll
+            for (int k = 0; k < NV; ++k) {
+                const int j0 = (k * SEG + l) * 4;
+                const f32x4 d = a[q][k] * (b[q][k] - sdot[q]);
+                if constexpr (M == kNone) {
+                    if (live) st4<true>(xr + j0, d);
+                } else {
+                    store4m<M, true>(xr, j0, L[q], d);
+                }
+            }
+        }
+    }
+}
+
+// Looped: one workgroup of T threads per row, U vectors per lane per step.
+// Pass 1 accumulates the dot product per lane in step order; pass 2 reads
+// the row again and writes dx. Steps wholly inside the row run unmasked.
+template <int M, int T, int U>
+__device__ __forceinline__ float bwd_dot_step(const float* yr, const float* gr, int base, int L, float s) {
+    f32x4 a[U], b[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        a[u] = load4m<M, false>(yr, base + (u * T + (int)threadIdx.x) * 4, L, 0.f);
+        b[u] = load4m<M, false>(gr, base + (u * T + (int)threadIdx.x) * 4, L, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) s += dot4(a[u], b[u]);
+    return s;
+}
+
+template <int M, int T, int U>
+__device__ __forceinline__ void bwd_out_step(const float* yr, const float* gr, float* xr, int base, int L, float s) {
+    f32x4 a[U], b[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        a[u] = load4m<M, true>(yr, base + (u * T + (int)threadIdx.x) * 4, L, 0.f);
+        b[u] = load4m<M, true>(gr, base + (u * T + (int)threadIdx.x) * 4, L, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) store4m<M, true>(xr, base + (u * T + (int)threadIdx.x) * 4, L, a[u] * (b[u] - s));
+}
+
+template <int T, int U, bool VEC>
+__global__ __launch_bounds__(T) void fr_red_softmax_bwd_f32(const float* y, const float* dy, float* dx, int rows,
+                                                            int cols, int64_t y_rs, int64_t dy_rs, int64_t dx_rs,
+                                                            const int32_t* __restrict__ lengths) {
+    constexpr int STEP = T * 4 * U;
+    __shared__ float sl[T / kWave];
+    for (int r = blockIdx.x; r < rows; r += gridDim.x) {
+        const int L = row_len(lengths, r, cols);
+        const int full = L - L % STEP;
+        const float* yr = y + (int64_t)r * y_rs;
+        const float* gr = dy + (int64_t)r * dy_rs;
+        float s = 0.f;
+        int base = 0;
+        for (; base < full; base += STEP) s = bwd_dot_step<body_mask<VEC>(), T, U>(yr, gr, base, L, s);
+        if (base < L) s = bwd_dot_step<tail_mask<VEC>(), T, U>(yr, gr, base, L, s);
+        s = group_reduce<kWave>(s, OpSum());
+        s = block_fold(s, sl, T / kWave, OpSum());
+        float* xr = dx + (int64_t)r * dx_rs;
+        for (base = 0; base < full; base += STEP) bwd_out_step<body_mask<VEC>(), T, U>(yr, gr, xr, base, L, s);
+        if (base < L) bwd_out_step<tail_mask<VEC>(), T, U>(yr, gr, xr, base, L, s);
+        __syncthreads();  // the slots are rewritten by the next row
+    }
+}
+
 // ------------------------------------------------------------------ launchers
 namespace {
 
@@ -669,6 +791,67 @@ void pick_split(int threads, int nv, PartFn* part, FinFn* fin) {
 }
 
 }  // namespace
+
+namespace {
+using BwdFn = void (*)(const float*, const float*, float*, int, int, int64_t, int64_t, int64_t, const int32_t*);
+
+template <int M>
+BwdFn pick_bwd_per_m(int seg, int nv, int rpw) {
+    if (rpw == 2) {
+        if (seg != 64) return nullptr;
+        switch (nv) {
+            case 1: return fr_per_softmax_bwd_f32<64, 1, M, 2>;
+            case 2: return fr_per_softmax_bwd_f32<64, 2, M, 2>;
+            case 4: return fr_per_softmax_bwd_f32<64, 4, M, 2>;
+        }
+        return nullptr;
+    }
+    if (rpw != 1) return nullptr;
+    switch (seg) {
+        case 8: return nv == 1 ? fr_per_softmax_bwd_f32<8, 1, M, 1> : nullptr;
+        case 16: return nv == 1 ? fr_per_softmax_bwd_f32<16, 1, M, 1> : nullptr;
+        case 32: return nv == 1 ? fr_per_softmax_bwd_f32<32, 1, M, 1> : nullptr;
+        case 64:
+            switch (nv) {
+                case 1: return fr_per_softmax_bwd_f32<64, 1, M, 1>;
+                case 2: return fr_per_softmax_bwd_f32<64, 2, M, 1>;
+                case 4: return fr_per_softmax_bwd_f32<64, 4, M, 1>;
+                case 8: return fr_per_softmax_bwd_f32<64, 8, M, 1>;
+            }
+    }
+    return nullptr;
+}
+
+template <bool VEC>
+BwdFn pick_bwd_red(int threads, int u) {
+    if (threads == 256 && u == 4) return fr_red_softmax_bwd_f32<256, 4, VEC>;
+    if (threads == 512 && u == 2) return fr_red_softmax_bwd_f32<512, 2, VEC>;
+    return nullptr;
+}
+}  // namespace
+
+hipError_t launch_softmax_bwd(const fr_plan& p, const SoftmaxBwdArgs& a, hipStream_t s) {
+    const bool vec = p.vec16 != 0;
+    BwdFn f = nullptr;
+    if (p.form == FR_FORM_PER) {
+        const int rpw = p.rows_per_wg / (256 / p.seg);
+        const int mask = !vec ? kScalar
+                              : (a.lengths ? kElem
+                                           : (a.cols == 4 * p.seg * p.vec ? kNone : (a.cols % 4 == 0 ? kVec : kElem)));
+        switch (mask) {
+            case kNone: f = pick_bwd_per_m<kNone>(p.seg, p.vec, rpw); break;
+            case kVec: f = pick_bwd_per_m<kVec>(p.seg, p.vec, rpw); break;
+            case kElem: f = pick_bwd_per_m<kElem>(p.seg, p.vec, rpw); break;
+            default: f = pick_bwd_per_m<kScalar>(p.seg, p.vec, rpw); break;
+        }
+    } else if (p.form == FR_FORM_RED) {
+        f = vec ? pick_bwd_red<true>(p.threads, p.vec) : pick_bwd_red<false>(p.threads, p.vec);
+    }
+    if (!f) return hipErrorInvalidDeviceFunction;
+    hipLaunchKernelGGL(f, dim3((unsigned)p.grid), dim3(p.form == FR_FORM_PER ? 256 : p.threads), 0, s, a.y, a.dy,
+                       a.dx, a.rows, a.cols, a.y_rs, a.dy_rs, a.dx_rs, a.lengths);
+    return hipGetLastError();
+}
 
 hipError_t launch_softmax(const fr_plan& p, const SoftmaxArgs& a, hipStream_t s) {
     const bool vec = p.vec16 != 0;

@@ -61,6 +61,20 @@ def workload(name):
             ys = [torch.empty_like(xs[0]) for _ in range(sets)]
             return (lambda k: fr.fr_softmax_rows(xs[k], ys[k])), (lambda: ys[0])
         return fr.FR_OP_SOFTMAX, 8 * rows * cols, 8 * rows * cols, alloc, cands, "f32"
+    if name == "softmax_bwd":
+        rows, cols = 4096, 1024
+        y = synth.softmax_inputs(rows, cols, seed=2001)  # any fp32 rows serve as y for timing
+        g = synth.normal((rows, cols), 2001, stream=7)
+        cands = [dict(form=P, threads=256, seg=64, vec=4, rows_per_wg=4),
+                 dict(form=P, threads=256, seg=64, vec=4, rows_per_wg=8),
+                 dict(form=R, threads=256, vec=4), dict(form=R, threads=512, vec=2)]
+
+        def alloc(sets):
+            ys = [_d(y) for _ in range(sets)]
+            gs = [_d(g) for _ in range(sets)]
+            xs = [torch.empty_like(ys[0]) for _ in range(sets)]
+            return (lambda k: fr.fr_softmax_rows_backward(ys[k], gs[k], xs[k])), (lambda: xs[0])
+        return fr.FR_OP_SOFTMAX_BWD, 12 * rows * cols, 12 * rows * cols, alloc, cands, "f32row"
     if name == "ragged":
         rows, cap = 512, 131072
         x, L = synth.ragged_softmax_inputs(rows, cap, seed=5001)
@@ -125,6 +139,9 @@ def close(a, b, kind):
     if kind == "bf16":
         ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(b), 2.0 ** -126))) - 7)
         return bool(np.all(np.abs(a - b) <= 2 * ulp + 1e-6))
+    if kind == "f32row":  # differences of products cancel: scale by the row's largest value
+        scale = np.max(np.abs(b), axis=-1, keepdims=True)
+        return bool(np.all(np.abs(a - b) <= 2e-5 * scale + 2e-6))
     return bool(np.all(np.abs(a - b) <= 2e-5 * np.abs(b) + 2e-6))
 
 

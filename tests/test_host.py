@@ -163,6 +163,32 @@ def test_attn_decode_argument_errors():
     assert fr.fr_attn_decode_workspace_bytes(2, 8, 1000, 80) == 0
 
 
+def test_softmax_backward_argument_errors_and_plans():
+    f = fr.lib.fr_softmax_rows_backward
+
+    def call(y=FAKE, dy=FAKE, dx=P(0x20000), rows=4, cols=8, ys=(8, 1), gs=(8, 1), xs=(8, 1), L=None,
+             dt=fr.FR_F32):
+        return f(y, dy, dx, rows, cols, ys[0], ys[1], gs[0], gs[1], xs[0], xs[1], L, dt, None)
+    assert call(dt=fr.FR_BF16) == fr.FR_E_DTYPE
+    assert call(cols=-1) == fr.FR_E_SIZE
+    assert call(y=None) == fr.FR_E_NULL
+    assert call(gs=(8, 2)) == fr.FR_E_STRIDE
+    assert call(dx=FAKE, xs=(16, 1)) == fr.FR_E_STRIDE  # dx aliases y with another row stride
+    assert call(dx=FAKE_ODD) == fr.FR_E_ALIGN
+    assert call(L=P(0x10002)) == fr.FR_E_ALIGN
+    assert call(rows=0) == fr.FR_OK and call(cols=0) == fr.FR_OK  # nothing to do, no HIP call
+    p = fr.fr_plan_query(fr.FR_OP_SOFTMAX_BWD, 4096, 1024)
+    assert (p.form, p.seg, p.vec, p.rows_per_wg) == (fr.FR_FORM_PER, 64, 4, 4)
+    p = fr.fr_plan_query(fr.FR_OP_SOFTMAX_BWD, 512, 50257)
+    assert (p.form, p.threads, p.vec, p.grid) == (fr.FR_FORM_RED, 512, 2, 512)
+    fr.fr_force_form(fr.FR_FORM_SPLIT)
+    try:
+        with pytest.raises(fr.FrError):
+            fr.fr_plan_query(fr.FR_OP_SOFTMAX_BWD, 4, 1 << 20, ws_bytes=1 << 30)
+    finally:
+        fr.fr_force_form(fr.FR_FORM_AUTO)
+
+
 # ------------------------------------------------------------------ planning
 
 
