@@ -55,6 +55,8 @@ def _load():
         "orc_softmax_backward_rows": (None, [P, P, I64, I64, I64, I64, P, P, P]),
         "orc_attn_decode": (None, [P, P, P, I64, I64, I64, I64, I64, P, F64, P, P, P, P, P]),
         "orc_attn_merge": (None, [F64, F64, P, F64, F64, P, I64, P, P, P]),
+        "orc_add_2d": (None, [P, I64, I64, P, I64, I64, P, I64, I64, I64]),
+        "orc_gelu_backward": (None, [P, I64, P, I64, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -247,3 +249,39 @@ def sumsq_rows(x):
     out = np.empty(rows, dtype=np.float64)
     _load().orc_sumsq_rows(_p(x), rows, cols, rs, _p(out))
     return out
+
+
+# ------------------------------------------------------------------ pointwise
+
+
+def _elem_strides(x):
+    assert all(st % x.itemsize == 0 and st >= 0 for st in x.strides)
+    return [st // x.itemsize for st in x.strides]
+
+
+def add_2d(a, b):
+    """out = a + b for fp32 2-D arrays of one shape; either may be a strided
+    view (a transposed array, [Stax4] 9.3 Example 6.1). Returns a contiguous
+    fp32 array, each element the correctly rounded fp32 sum."""
+    a = np.asarray(a)
+    b = np.asarray(b)
+    assert a.dtype == np.float32 and b.dtype == np.float32 and a.ndim == 2 and a.shape == b.shape
+    rows, cols = a.shape
+    (a_rs, a_cs), (b_rs, b_cs) = _elem_strides(a), _elem_strides(b)
+    out = np.empty((rows, cols), dtype=np.float32)
+    _load().orc_add_2d(_p(a), a_rs, a_cs, _p(b), b_rs, b_cs, _p(out), cols, rows, cols)
+    return out
+
+
+def gelu_backward(dy, h):
+    """dx = dy * (Phi(h) + h phi(h)) in fp64 ([Stax4] 9.3, Listing 9.3).
+    h: 1-D values (any float dtype; bf16 callers convert first). dy: one
+    value (broadcast) or an array shaped like h. Returns (dx64, mag)."""
+    h = np.ascontiguousarray(h, dtype=np.float64).ravel()
+    dy = np.ascontiguousarray(dy, dtype=np.float64).ravel()
+    assert dy.size in (1, h.size)
+    stride = 0 if dy.size == 1 and h.size != 1 else 1
+    dx = np.empty(h.size)
+    mag = np.empty(h.size)
+    _load().orc_gelu_backward(_p(dy), stride, _p(h), h.size, _p(dx), _p(mag))
+    return dx, mag

@@ -12,7 +12,9 @@
  * loops and fp64 accumulation. No blocking, fusion or reordering is done
  * beyond what the cited definition states. Sources (web pages):
  *   [Stax4]  "Stax (4): GPU Codegen and Dynamic Shapes" (TensorPlay blog),
- *            section 9.2 (Listing 9.1, Example 1.1), 9.4 (Listing 9.4,
+ *            section 9.2 (Listing 9.1, Example 1.1), 9.3 (Listing 9.2, the
+ *            transposed add of Example 6.1; Listing 9.3, the GELU backward
+ *            of Example 5.1), 9.4 (Listing 9.4,
  *            Example 6.2), 9.5 (softmax definition, Listing 9.5, the (m, d)
  *            merge and Proposition 9.1), 10.2 (Example 10.1).
  *   [HG12]   "hello-gpu, Chapter 12: Fusion", section 12.1 (attention of one
@@ -392,4 +394,48 @@ double orc_sumsq(const float* x, int64_t n) {
 
 void orc_sumsq_rows(const float* x, int64_t rows, int64_t cols, int64_t x_rs, double* out) {
     for (int64_t r = 0; r < rows; ++r) out[r] = orc_sumsq(x + r * x_rs, cols);
+}
+
+/* ------------------------------------------------------------- pointwise */
+
+/*
+ * Elementwise add of two 2-D operands with independent strides ([Stax4]
+ * 9.3, Listing 9.2: Example 6.1, x.t() + y, where the first operand is
+ * contiguous along the output's rows and the second along its columns):
+ *   out[i * out_rs + j] = a[i * a_rs + j * a_cs] + b[i * b_rs + j * b_cs]
+ * for i < rows, j < cols. Each sum is formed in fp64 and rounded once to
+ * fp32. For two fp32 operands that equals the correctly rounded fp32 sum:
+ * fp64 carries more than twice the fp32 significand plus two bits, so the
+ * second rounding cannot change the first.
+ */
+void orc_add_2d(const float* a, int64_t a_rs, int64_t a_cs, const float* b, int64_t b_rs, int64_t b_cs, float* out,
+                int64_t out_rs, int64_t rows, int64_t cols) {
+    for (int64_t i = 0; i < rows; ++i)
+        for (int64_t j = 0; j < cols; ++j)
+            out[i * out_rs + j] = (float)((double)a[i * a_rs + j * a_cs] + (double)b[i * b_rs + j * b_cs]);
+}
+
+/*
+ * GELU backward ([Stax4] 9.3, Listing 9.3, the backward pointwise kernel of
+ * Example 5.1): with h the saved pre-activation and GELU(h) = h Phi(h),
+ *   GELU'(h) = Phi(h) + h phi(h),   dx = dy * GELU'(h),
+ * Phi the standard normal distribution function and phi its density. dy is
+ * one element broadcast to every output when dy_stride is 0 (the pages'
+ * case: the loss is a scalar), else element i reads dy[i * dy_stride].
+ * In fp64: Phi(h) = erfc(-h / sqrt 2) / 2, the same function as
+ * (1 + erf(h / sqrt 2)) / 2 without its cancellation for negative h;
+ * phi(h) = exp(-h^2 / 2) / sqrt(2 pi).
+ *   mag (nullable): |dy| (Phi(h) + |h| phi(h)), the size of the terms of dx.
+ */
+void orc_gelu_backward(const double* dy, int64_t dy_stride, const double* h, int64_t n, double* dx64, double* mag) {
+    const double inv_sqrt2 = 0.70710678118654752440;
+    const double inv_sqrt2pi = 0.39894228040143267794;
+    for (int64_t i = 0; i < n; ++i) {
+        const double hi = h[i];
+        const double g = dy[i * dy_stride];
+        const double cdf = 0.5 * erfc(-hi * inv_sqrt2);
+        const double pdf = inv_sqrt2pi * exp(-0.5 * hi * hi);
+        dx64[i] = g * (cdf + hi * pdf);
+        if (mag) mag[i] = fabs(g) * (cdf + fabs(hi) * pdf);
+    }
 }

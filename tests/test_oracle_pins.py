@@ -514,3 +514,74 @@ def test_softmax_backward_ragged_rows():
     full, _ = oracle.softmax_backward_rows(y[1:2, :3].copy(), dy[1:2, :3].copy())
     assert np.array_equal(dx[1, :3], full[0])
     assert not np.isnan(dx[2:]).any()
+
+
+# ------------------------------------------------------- pointwise ([Stax4] 9.3)
+
+
+def test_add_2d_transposed_by_hand():
+    # Example 6.1 in small: x is 2 x 3, out = x.t() + y is 3 x 2
+    x = np.array([[1, 2, 3], [4, 5, 6]], dtype=np.float32)
+    y = np.array([[10, 20], [30, 40], [50, 60]], dtype=np.float32)
+    out = oracle.add_2d(x.T, y)
+    assert out.tolist() == [[11, 24], [32, 45], [53, 66]]
+    # the other operand transposed, and both
+    assert oracle.add_2d(y, x.T).tolist() == [[11, 24], [32, 45], [53, 66]]
+    assert oracle.add_2d(x.T, x.T).tolist() == [[2, 8], [4, 10], [6, 12]]
+
+
+def test_add_2d_rounds_once_to_nearest_even():
+    u = 2.0 ** -24  # half an fp32 ulp of 1
+    a = np.array([[1.0, 1.0 + 2 * u, 1.0, 1.0]], dtype=np.float32)
+    b = np.array([[u, u, 1.5 * u, 0.5 * u]], dtype=np.float32)
+    out = oracle.add_2d(a, b)
+    # ties go to the even significand; above half rounds up, below down
+    assert out.tolist()[0] == [1.0, 1.0 + 4 * u, 1.0 + 2 * u, 1.0]
+
+
+def test_add_2d_equals_fp32_addition_on_strided_views():
+    rng = np.random.default_rng(91)
+    x = rng.normal(size=(53, 37)).astype(np.float32) * np.float32(1e3)
+    y = rng.normal(size=(37, 60)).astype(np.float32)
+    want = x.T + y[:, :53]  # numpy's fp32 add is correctly rounded
+    assert np.array_equal(oracle.add_2d(x.T, y[:, :53]), want)
+    z = rng.normal(size=(74, 106)).astype(np.float32)
+    assert np.array_equal(oracle.add_2d(z[::2, ::2], z[1::2, 1::2]), z[::2, ::2] + z[1::2, 1::2])
+
+
+def test_gelu_backward_matches_finite_differences():
+    # GELU(h) = h Phi(h) with Phi from scipy; dx / dy is its derivative
+    gelu = lambda t: t * scipy.special.ndtr(t)  # noqa: E731
+    h = np.array([-6.0, -3.0, -1.3, -0.75, -0.2, 0.0, 0.4, 1.0, 2.5, 5.0])
+    eps = 1e-6
+    fd = (gelu(h + eps) - gelu(h - eps)) / (2 * eps)
+    dx, mag = oracle.gelu_backward(1.0, h)
+    assert np.allclose(dx, fd, rtol=1e-7, atol=1e-9)
+    assert np.all(mag >= np.abs(dx))
+
+
+def test_gelu_backward_closed_forms():
+    dx, _ = oracle.gelu_backward(1.0, np.array([0.0, 1.0, 40.0, -40.0]))
+    assert dx[0] == 0.5  # Phi(0) = 1/2
+    # Phi(1) + phi(1), textbook values of the normal distribution and density
+    assert dx[1] == pytest.approx(0.8413447460685429 + 0.24197072451914337, rel=1e-15)
+    assert dx[2] == 1.0 and dx[3] == 0.0
+    # GELU'(h) + GELU'(-h) = 1 (Phi(-h) = 1 - Phi(h), phi even)
+    h = np.linspace(-5, 5, 41)
+    a, _ = oracle.gelu_backward(1.0, h)
+    b, _ = oracle.gelu_backward(1.0, -h)
+    assert np.allclose(a + b, 1.0, rtol=0, atol=1e-15)
+    # GELU has its minimum near h = -0.7518: the derivative changes sign there
+    d, _ = oracle.gelu_backward(1.0, np.array([-0.76, -0.74]))
+    assert d[0] < 0 < d[1]
+
+
+def test_gelu_backward_broadcasts_one_upstream_value():
+    h = np.linspace(-3, 3, 7)
+    one, _ = oracle.gelu_backward(np.array([-2.5]), h)
+    each, _ = oracle.gelu_backward(np.full(7, -2.5), h)
+    unit, _ = oracle.gelu_backward(1.0, h)
+    assert np.array_equal(one, each) and np.array_equal(one, -2.5 * unit)
+    g = np.arange(1, 8, dtype=np.float64)
+    per, _ = oracle.gelu_backward(g, h)
+    assert np.allclose(per, g * unit, rtol=1e-15)
