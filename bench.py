@@ -340,6 +340,81 @@ def make_workload(name, torch, fr, synth):
 
         return W(), per_set
 
+    if name == "add_2d":
+        # x.t() + y ("Stax (4)", 9.3, Example 6.1) at 8192 x 8192 fp32: the
+        # first operand transposed, staged through LDS tile by tile
+        n = 8192
+        x_h = synth.normal((n, n), 62, stream=1)
+        y_h = synth.normal((n, n), 62, stream=2)
+        per_set = 3 * n * n * 4
+
+        class W(Workload):
+            kernel = "fr_add_2d_f32"
+            bytes = 3 * n * n * 4
+            dtype = "f32"
+
+            def alloc(self, sets):
+                x0, y0 = d(x_h), d(y_h)
+                self.args = [(x0 if i == 0 else x0.clone(), y0 if i == 0 else y0.clone(), torch.empty_like(y0))
+                             for i in range(sets)]
+
+            def launch(self, k):
+                x, y, out = self.args[k]
+                fr.fr_add_2d(x.t(), y, out)
+
+            def output(self, k):
+                return self.args[k][2]
+
+            def config(self):
+                p = fr.fr_plan_query(fr.FR_OP_ADD_2D, n, n)
+                return {"workload": "x.t() + y, 8192x8192 fp32 (x, y ~ N(0,1))", "rows": n, "cols": n,
+                        "tile": [p.rows_per_wg, p.chunk], "form": fr.FORM_NAMES[p.form]}
+
+            def oracle_fn(self):
+                import oracle
+                r = 1024
+                a, b = x_h[:, :r].T, y_h[:r]
+                return lambda: oracle.add_2d(a, b), 3 * r * n * 4, f"first {r} of {n} output rows"
+
+        return W(), per_set
+
+    if name == "gelu_bwd":
+        # GELU backward ("Stax (4)", 9.3, Listing 9.3) over 2^28 fp32
+        # pre-activations h ~ N(0, 4), one broadcast upstream value
+        n = 1 << 28
+        h_h = synth.normal((n,), 54, stream=3, std=2.0)
+        per_set = 2 * n * 4
+
+        class W(Workload):
+            kernel = "fr_gelu_bwd"
+            bytes = 2 * n * 4 + 4
+            dtype = "f32"
+
+            def alloc(self, sets):
+                h0 = d(h_h)
+                g = torch.tensor([0.5], dtype=torch.float32, device=dev)
+                self.args = [(g, h0 if i == 0 else h0.clone(), torch.empty_like(h0)) for i in range(sets)]
+
+            def launch(self, k):
+                g, h, dx = self.args[k]
+                fr.fr_gelu_backward(g, h, dx)
+
+            def output(self, k):
+                return self.args[k][2]
+
+            def config(self):
+                p = fr.fr_plan_query(fr.FR_OP_GELU_BWD, 1, n)
+                return {"workload": "GELU backward, 2^28 fp32 (h ~ N(0,4), one broadcast dy)", "n": n,
+                        "vectors_per_lane": p.vec, "grid": p.grid, "form": fr.FORM_NAMES[p.form]}
+
+            def oracle_fn(self):
+                import oracle
+                m = 1 << 21
+                h = h_h[:m].astype(np.float64)
+                return lambda: oracle.gelu_backward(0.5, h), 8 * m, f"first {m} of {n} elements"
+
+        return W(), per_set
+
     if name == "attn_decode":
         # decode attention: batch 8, 32 query heads on 8 key-value heads,
         # 8192 keys, head dim 128, bf16 (each key and value byte read once)
@@ -476,7 +551,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="softmax",
                     choices=["softmax", "sum_relu_add", "layernorm", "sumsq", "ragged", "copy", "stream_copy",
-                             "stream_copy_c3", "stream_read", "attn_decode", "softmax_bwd"])
+                             "stream_copy_c3", "stream_read", "attn_decode", "softmax_bwd", "add_2d",
+                             "gelu_bwd"])
     ap.add_argument("--warm", action="store_true", help="one buffer set: reads may hit the MALL")
     ap.add_argument("--eager", action="store_true", help="launch each step from the host (no graph)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)

@@ -67,6 +67,8 @@ extern "C" {
 #define FR_FORM_PER 1
 #define FR_FORM_RED 2
 #define FR_FORM_SPLIT 3
+/* Pointwise operations have no reduction dimension and one form. */
+#define FR_FORM_POINTWISE 4
 
 /* ------------------------------------------------------------ operations */
 #define FR_OP_SUM_RELU_ADD 1
@@ -74,6 +76,8 @@ extern "C" {
 #define FR_OP_LAYERNORM 3
 #define FR_OP_SUMSQ 4
 #define FR_OP_SOFTMAX_BWD 5
+#define FR_OP_ADD_2D 6
+#define FR_OP_GELU_BWD 7
 
 /* Launch plan chosen for one call: the reduction form and its launch
  * configuration ("Stax (4)", 9.6: block sizes and warp counts are launch
@@ -194,6 +198,41 @@ int fr_softmax_rows(const void* x, void* y, int64_t rows, int64_t cols, int64_t 
 int fr_softmax_rows_backward(const void* y, const void* dy, void* dx, int64_t rows, int64_t cols, int64_t y_rs,
                              int64_t y_cs, int64_t dy_rs, int64_t dy_cs, int64_t dx_rs, int64_t dx_cs,
                              const int32_t* lengths, int dtype, void* stream);
+
+/* ------------------------------------------------------------ pointwise: 2-D add
+ * out[i,j] = a[i*a_rs + j*a_cs] + b[i*b_rs + j*b_cs] for i < rows, j < cols
+ * ("Stax (4)", 9.3, Listing 9.2: Example 6.1, x.t() + y, where one operand is
+ * contiguous along the output's columns and the other along its rows). Each
+ * operand is either row-major (a_cs = 1, a_rs >= cols) or column-major, i.e.
+ * a transposed view (a_rs = 1, a_cs >= rows); any other layout returns
+ * FR_E_STRIDE. The output is row-major (unit inner stride, out_rs >= cols).
+ * Each element is the correctly rounded fp32 sum. The kernel tiles the output
+ * in two dimensions (fr_plan: rows_per_wg x chunk elements per workgroup) and
+ * passes transposed operands through LDS, so every access coalesces.
+ *  a, b, out: fp32 device pointers, 4-byte aligned; 16-byte alignment of the
+ *             bases and strides enables 16-byte accesses.
+ *  out may be a or b only with the same (row-major) layout; other overlaps
+ *  are undefined. rows < 2^31, cols < 2^30. dtype must be FR_F32. */
+int fr_add_2d(const void* a, int64_t a_rs, int64_t a_cs, const void* b, int64_t b_rs, int64_t b_cs, void* out,
+              int64_t out_rs, int64_t rows, int64_t cols, int dtype, void* stream);
+
+/* ------------------------------------------------------------ pointwise: GELU backward
+ * dx[i] = dy * GELU'(h[i]), GELU'(h) = Phi(h) + h phi(h), with Phi(h) =
+ * (1 + erf(h / sqrt 2)) / 2 and phi(h) = exp(-h^2 / 2) / sqrt(2 pi)
+ * ("Stax (4)", 9.3, Listing 9.3: the backward pointwise kernel of Example 5.1;
+ * h is the pre-activation the forward pass saved).
+ *  dy:        dy_stride 0: one element broadcast to every output (the
+ *             upstream gradient of a scalar loss, as on the pages);
+ *             dy_stride 1: one element per output. Other strides return
+ *             FR_E_STRIDE.
+ *  h, dx:     n contiguous elements; dx may be h or dy (elementwise, in
+ *             place). n < 2^40.
+ *  dtype:     FR_F32, or FR_BF16 for all three arrays (arithmetic in fp32,
+ *             dx rounded to nearest even).
+ * h = +-inf gives NaN (inf * 0 in h phi(h)), as the formula evaluates; NaN
+ * propagates. */
+int fr_gelu_backward(const void* dy, int64_t dy_stride, const void* h, void* dx, int64_t n, int dtype,
+                     void* stream);
 
 /* ------------------------------------------------------------ LayerNorm
  * y[i,j] = (x[i,j] - mu_i) * rstd_i * gamma[j] + beta[j],

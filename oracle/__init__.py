@@ -56,6 +56,7 @@ def _load():
         "orc_attn_decode": (None, [P, P, P, I64, I64, I64, I64, I64, P, F64, P, P, P, P, P]),
         "orc_attn_merge": (None, [F64, F64, P, F64, F64, P, I64, P, P, P]),
         "orc_add_2d": (None, [P, I64, I64, P, I64, I64, P, I64, I64, I64]),
+        "orc_round_bf16": (None, [P, I64, P]),
         "orc_gelu_backward": (None, [P, I64, P, I64, P, P]),
     }
     for name, (res, args) in sig.items():
@@ -87,6 +88,14 @@ def bf16_to_f64(bits):
 
 def f64_to_bf16(v):
     return int(_load().orc_double_to_bf16(float(v)))
+
+
+def round_bf16(v):
+    """fp64 array -> bf16 bit patterns (uint16), each rounded once to nearest even."""
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    out = np.empty(v.shape, dtype=np.uint16)
+    _load().orc_round_bf16(_p(v), v.size, _p(out))
+    return out
 
 
 # ------------------------------------------------------------------ C1

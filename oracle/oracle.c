@@ -396,6 +396,11 @@ void orc_sumsq_rows(const float* x, int64_t rows, int64_t cols, int64_t x_rs, do
     for (int64_t r = 0; r < rows; ++r) out[r] = orc_sumsq(x + r * x_rs, cols);
 }
 
+/* fp64 values -> bf16 bit patterns, each rounded once to nearest even. */
+void orc_round_bf16(const double* v, int64_t n, uint16_t* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_double_to_bf16(v[i]);
+}
+
 /* ------------------------------------------------------------- pointwise */
 
 /*

@@ -27,9 +27,10 @@ FR_OK = 0
 FR_E_NULL, FR_E_SIZE, FR_E_STRIDE, FR_E_DTYPE, FR_E_ALIGN = -1, -2, -3, -4, -5
 FR_E_WORKSPACE, FR_E_ARG, FR_E_DEVICE, FR_E_LAUNCH = -6, -7, -8, -9
 FR_F32, FR_BF16 = 0, 1
-FR_FORM_AUTO, FR_FORM_PER, FR_FORM_RED, FR_FORM_SPLIT = 0, 1, 2, 3
+FR_FORM_AUTO, FR_FORM_PER, FR_FORM_RED, FR_FORM_SPLIT, FR_FORM_POINTWISE = 0, 1, 2, 3, 4
 FR_OP_SUM_RELU_ADD, FR_OP_SOFTMAX, FR_OP_LAYERNORM, FR_OP_SUMSQ, FR_OP_SOFTMAX_BWD = 1, 2, 3, 4, 5
-FORM_NAMES = {FR_FORM_PER: "per", FR_FORM_RED: "red", FR_FORM_SPLIT: "split"}
+FR_OP_ADD_2D, FR_OP_GELU_BWD = 6, 7
+FORM_NAMES = {FR_FORM_PER: "per", FR_FORM_RED: "red", FR_FORM_SPLIT: "split", FR_FORM_POINTWISE: "pointwise"}
 
 # Every symbol include/fr.h declares.
 EXPORTS = (
@@ -40,6 +41,7 @@ EXPORTS = (
     "fr_sumsq_rows", "fr_sumsq_full_workspace_bytes", "fr_sumsq_full",
     "fr_stream_copy", "fr_stream_read",
     "fr_attn_decode_workspace_bytes", "fr_attn_decode",
+    "fr_add_2d", "fr_gelu_backward",
 )
 
 
@@ -88,6 +90,8 @@ def _load():
         "fr_attn_decode": (I32, [P, P, P, P, P, I64, I64, I64, I64, I64, P, ctypes.c_float, P, U64, I32, P]),
         "fr_stream_copy": (I32, [P, P, I64, P]),
         "fr_stream_read": (I32, [P, I64, P, P]),
+        "fr_add_2d": (I32, [P, I64, I64, P, I64, I64, P, I64, I64, I64, I32, P]),
+        "fr_gelu_backward": (I32, [P, I64, P, P, I64, I32, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -287,3 +291,36 @@ def fr_attn_decode(q, k, v, o, lse=None, lengths=None, scale=None, ws=None, stre
     _check(lib.fr_attn_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, S, D, _ptr(lengths),
                               float(scale), _ptr(ws), ws_bytes, _dtype_code(q), _stream(stream)), "fr_attn_decode")
     return o
+
+
+def fr_add_2d(a, b, out, stream=None):
+    """out = a + b for fp32 2-D views of one shape; a or b may be a
+    transposed view (x.t()). out must be row-major."""
+    rows, cols, a_rs, a_cs = _mat(a)
+    rb, cb, b_rs, b_cs = _mat(b)
+    ro, co, out_rs, out_cs = _mat(out)
+    if (rb, cb) != (rows, cols) or (ro, co) != (rows, cols):
+        raise ValueError("shape mismatch")
+    if out_cs != 1 and rows * cols > 0 and cols > 1:
+        raise ValueError("out must have unit inner stride")
+    if _dtype_code(b) != _dtype_code(a) or _dtype_code(out) != _dtype_code(a):
+        raise ValueError("dtype mismatch")
+    _check(lib.fr_add_2d(_ptr(a), a_rs, a_cs, _ptr(b), b_rs, b_cs, _ptr(out), out_rs, rows, cols, _dtype_code(a),
+                         _stream(stream)), "fr_add_2d")
+    return out
+
+
+def fr_gelu_backward(dy, h, dx, stream=None):
+    """dx = dy * (Phi(h) + h phi(h)); dy holds one element (broadcast) or as
+    many as h. h, dx contiguous, fp32 or bf16 (all three alike)."""
+    n = h.numel()
+    if dx.numel() != n or not h.is_contiguous() or not dx.is_contiguous() or not dy.is_contiguous():
+        raise ValueError("h, dx and dy must be contiguous and dx shaped like h")
+    if dy.numel() not in (1, n):
+        raise ValueError("dy must hold one element or one per element of h")
+    if _dtype_code(dy) != _dtype_code(h) or _dtype_code(dx) != _dtype_code(h):
+        raise ValueError("dtype mismatch")
+    stride = 0 if dy.numel() == 1 and n != 1 else 1
+    _check(lib.fr_gelu_backward(_ptr(dy), stride, _ptr(h), _ptr(dx), n, _dtype_code(h), _stream(stream)),
+           "fr_gelu_backward")
+    return dx

@@ -29,7 +29,7 @@ namespace {
 int g_forced_form = FR_FORM_AUTO;
 
 // Tuning overrides, one per operation (index = FR_OP_*).
-constexpr int kOps = 6;
+constexpr int kOps = 8;
 fr_plan g_override[kOps];
 bool g_has_override[kOps] = {};
 
@@ -119,6 +119,15 @@ int run_sum(int prologue, const void* a, const void* b, void* out, int64_t rows,
     return finish_launch(launch_sum(plan, args, (hipStream_t)stream));
 }
 
+// Layout of one operand of the 2-D add: 0 row-major, 1 column-major (a
+// transposed view), -1 neither.
+int add2d_layout(int64_t rows, int64_t cols, int64_t rs, int64_t cs) {
+    if (rs < 0 || cs < 0) return -1;
+    if (cs == 1 && (rows == 1 || rs >= cols)) return 0;
+    if (rs == 1 && (cols == 1 || cs >= rows)) return 1;
+    return -1;
+}
+
 }  // namespace
 
 extern "C" {
@@ -143,13 +152,15 @@ int fr_version(void) { return 100; }
 
 int fr_force_form(int form) {
     const int prev = g_forced_form;
-    if (form >= FR_FORM_AUTO && form <= FR_FORM_SPLIT) g_forced_form = form;
+    if (form >= FR_FORM_AUTO && form <= FR_FORM_POINTWISE) g_forced_form = form;
     return prev;
 }
 
 int fr_plan_query(int op, int64_t rows, int64_t cols, int dtype, int num_cus, int has_lengths, uint64_t ws_bytes,
                   int aligned16, fr_plan* plan) {
     if (!plan) return FR_E_NULL;
+    if (op == FR_OP_ADD_2D || op == FR_OP_GELU_BWD)
+        return make_pointwise_plan(op, rows, cols, dtype, num_cus, aligned16, g_forced_form, override_for(op), plan);
     return make_plan(op, rows, cols, dtype, num_cus, has_lengths, ws_bytes, aligned16, g_forced_form,
                      override_for(op), plan);
 }
@@ -375,6 +386,56 @@ int fr_stream_read(const void* x, int64_t nbytes, uint32_t* sink, void* stream) 
     if (st != FR_OK) return st;
     (void)hipGetLastError();
     return finish_launch(launch_stream_read(x, nbytes / 16, sink, (hipStream_t)stream));
+}
+
+int fr_add_2d(const void* a, int64_t a_rs, int64_t a_cs, const void* b, int64_t b_rs, int64_t b_cs, void* out,
+              int64_t out_rs, int64_t rows, int64_t cols, int dtype, void* stream) {
+    int st = check_sizes(rows, cols);
+    if (st != FR_OK) return st;
+    if (dtype != FR_F32) return FR_E_DTYPE;
+    if (rows == 0 || cols == 0) return FR_OK;
+    if (!a || !b || !out) return FR_E_NULL;
+    const int la = add2d_layout(rows, cols, a_rs, a_cs), lb = add2d_layout(rows, cols, b_rs, b_cs);
+    if (la < 0 || lb < 0 || out_rs < 0 || (rows > 1 && out_rs < cols)) return FR_E_STRIDE;
+    if (!aligned(a, 4) || !aligned(b, 4) || !aligned(out, 4)) return FR_E_ALIGN;
+    // in place only over an operand of the output's own layout
+    if ((out == a && (la != 0 || a_rs != out_rs)) || (out == b && (lb != 0 || b_rs != out_rs))) return FR_E_ARG;
+    int num_cus = 0;
+    st = device_check(&num_cus);
+    if (st != FR_OK) return st;
+    // 16-byte vectors along each operand's contiguous direction
+    const int v16 = aligned(a, 16) && aligned(b, 16) && aligned(out, 16) && (la ? a_cs : a_rs) % 4 == 0 &&
+                    (lb ? b_cs : b_rs) % 4 == 0 && out_rs % 4 == 0;
+    fr_plan plan;
+    st = make_pointwise_plan(FR_OP_ADD_2D, rows, cols, FR_F32, num_cus, v16, g_forced_form,
+                             override_for(FR_OP_ADD_2D), &plan);
+    if (st != FR_OK) return st;
+    Add2dArgs args{(const float*)a, (const float*)b, (float*)out, rows, cols, a_rs, a_cs, b_rs, b_cs, out_rs,
+                   la == 1, lb == 1};
+    (void)hipGetLastError();
+    return finish_launch(launch_add_2d(plan, args, (hipStream_t)stream));
+}
+
+int fr_gelu_backward(const void* dy, int64_t dy_stride, const void* h, void* dx, int64_t n, int dtype,
+                     void* stream) {
+    if (dtype != FR_F32 && dtype != FR_BF16) return FR_E_DTYPE;
+    if (n < 0 || n >= (int64_t(1) << 40)) return FR_E_SIZE;
+    if (dy_stride != 0 && dy_stride != 1) return FR_E_STRIDE;
+    if (n == 0) return FR_OK;
+    if (!dy || !h || !dx) return FR_E_NULL;
+    const size_t es = dtype == FR_F32 ? 4 : 2;
+    if (!aligned(dy, es) || !aligned(h, es) || !aligned(dx, es)) return FR_E_ALIGN;
+    int num_cus = 0;
+    const int st0 = device_check(&num_cus);
+    if (st0 != FR_OK) return st0;
+    const int v16 = aligned(h, 16) && aligned(dx, 16) && (dy_stride == 0 || aligned(dy, 16));
+    fr_plan plan;
+    const int st = make_pointwise_plan(FR_OP_GELU_BWD, 1, n, dtype, num_cus, v16, g_forced_form,
+                                       override_for(FR_OP_GELU_BWD), &plan);
+    if (st != FR_OK) return st;
+    GeluBwdArgs args{dy, h, dx, n, dy_stride == 0, dtype == FR_BF16};
+    (void)hipGetLastError();
+    return finish_launch(launch_gelu_bwd(plan, args, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -69,6 +69,26 @@ hipError_t launch_sum(const fr_plan& p, const SumArgs& a, hipStream_t s);
 hipError_t launch_softmax(const fr_plan& p, const SoftmaxArgs& a, hipStream_t s);
 hipError_t launch_layernorm(const fr_plan& p, const LayerNormArgs& a, hipStream_t s);
 hipError_t launch_softmax_bwd(const fr_plan& p, const SoftmaxBwdArgs& a, hipStream_t s);
+// Pointwise: 2-D add (a_t / b_t: the operand is column-major, a transposed
+// view with unit row stride) and GELU backward.
+struct Add2dArgs {
+    const float* a;
+    const float* b;
+    float* out;
+    int64_t rows, cols;
+    int64_t a_rs, a_cs, b_rs, b_cs, out_rs;
+    bool a_t, b_t;
+};
+struct GeluBwdArgs {
+    const void* dy;
+    const void* h;
+    void* dx;
+    int64_t n;
+    bool bcast;  // dy[0] for every element
+    bool bf16;
+};
+hipError_t launch_add_2d(const fr_plan& p, const Add2dArgs& a, hipStream_t s);
+hipError_t launch_gelu_bwd(const fr_plan& p, const GeluBwdArgs& a, hipStream_t s);
 
 // Decode attention: keys are split into chunks of kAttnChunk per workgroup;
 // the workspace holds one (m, l, pad, pad, a[dim]) fp32 slot per (batch,
@@ -101,5 +121,9 @@ hipError_t launch_stream_read(const void* x, int64_t nvec, uint32_t* sink, hipSt
 // Planner (host only, no HIP calls).
 int make_plan(int op, int64_t rows, int64_t cols, int dtype, int num_cus, int has_lengths, uint64_t ws_bytes,
               int aligned16, int forced_form, const fr_plan* override_plan, fr_plan* plan);
+// Pointwise operations: FR_OP_ADD_2D over rows x cols, FR_OP_GELU_BWD over
+// n = rows * cols elements.
+int make_pointwise_plan(int op, int64_t rows, int64_t cols, int dtype, int num_cus, int aligned16, int forced_form,
+                        const fr_plan* override_plan, fr_plan* plan);
 
 }  // namespace fr

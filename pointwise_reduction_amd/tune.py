@@ -61,6 +61,33 @@ def workload(name):
             ys = [torch.empty_like(xs[0]) for _ in range(sets)]
             return (lambda k: fr.fr_softmax_rows(xs[k], ys[k])), (lambda: ys[0])
         return fr.FR_OP_SOFTMAX, 8 * rows * cols, 8 * rows * cols, alloc, cands, "f32"
+    if name == "add_2d":
+        n = 8192
+        x = synth.normal((n, n), 62, stream=1)
+        y = synth.normal((n, n), 62, stream=2)
+        PW = fr.FR_FORM_POINTWISE
+        cands = [dict(form=PW, threads=256, rows_per_wg=ti, chunk=tj, grid=g)
+                 for ti, tj in ((64, 64), (32, 128), (128, 32), (64, 128), (128, 64), (32, 32))
+                 for g in (0, 2048)]
+
+        def alloc(sets):
+            xs = [_d(x) for _ in range(sets)]
+            ys = [_d(y) for _ in range(sets)]
+            outs = [torch.empty_like(ys[0]) for _ in range(sets)]
+            return (lambda k: fr.fr_add_2d(xs[k].t(), ys[k], outs[k])), (lambda: outs[0])
+        return fr.FR_OP_ADD_2D, 12 * n * n, 12 * n * n, alloc, cands, "exact"
+    if name == "gelu_bwd":
+        n = 1 << 28
+        h = synth.normal((n,), 54, stream=3, std=2.0)
+        PW = fr.FR_FORM_POINTWISE
+        cands = [dict(form=PW, threads=256, vec=v, grid=g) for v in (1, 2, 4) for g in (0, 1024, 4096)]
+
+        def alloc(sets):
+            hs = [_d(h) for _ in range(sets)]
+            g = torch.tensor([0.5], dtype=torch.float32, device="cuda")
+            outs = [torch.empty_like(hs[0]) for _ in range(sets)]
+            return (lambda k: fr.fr_gelu_backward(g, hs[k], outs[k])), (lambda: outs[0])
+        return fr.FR_OP_GELU_BWD, 8 * n, 8 * n, alloc, cands, "f32row"
     if name == "softmax_bwd":
         rows, cols = 4096, 1024
         y = synth.softmax_inputs(rows, cols, seed=2001)  # any fp32 rows serve as y for timing
@@ -139,6 +166,8 @@ def close(a, b, kind):
     if kind == "bf16":
         ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(b), 2.0 ** -126))) - 7)
         return bool(np.all(np.abs(a - b) <= 2 * ulp + 1e-6))
+    if kind == "exact":
+        return bool(np.array_equal(a, b))
     if kind == "f32row":  # differences of products cancel: scale by the row's largest value
         scale = np.max(np.abs(b), axis=-1, keepdims=True)
         return bool(np.all(np.abs(a - b) <= 2e-5 * scale + 2e-6))

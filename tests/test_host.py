@@ -325,3 +325,35 @@ def test_tune_override_replaces_the_launch_knobs():
     assert fr.fr_plan_query(fr.FR_OP_SOFTMAX, 4096, 1024).rows_per_wg == 8  # automatic: 2 rows per wave
     with pytest.raises(fr.FrError):
         fr.fr_tune_override(99, form=1)
+
+
+def test_pointwise_plans_and_argument_errors():
+    p = fr.fr_plan_query(fr.FR_OP_ADD_2D, 8192, 8192)
+    assert (p.form, p.rows_per_wg, p.chunk, p.grid) == (fr.FR_FORM_POINTWISE, 64, 128, 128 * 64)
+    p = fr.fr_plan_query(fr.FR_OP_ADD_2D, 0, 5)
+    assert p.grid == 0
+    with pytest.raises(fr.FrError):
+        fr.fr_plan_query(fr.FR_OP_ADD_2D, 4, 4, dtype=fr.FR_BF16)
+    p = fr.fr_plan_query(fr.FR_OP_GELU_BWD, 1, 1 << 28)
+    assert (p.form, p.vec, p.grid) == (fr.FR_FORM_POINTWISE, 2, (1 << 26) // 512)
+    p = fr.fr_plan_query(fr.FR_OP_GELU_BWD, 1, 1000, dtype=fr.FR_BF16, aligned16=False)
+    assert p.grid == 4  # element accesses: 256 per workgroup step
+    prev = fr.fr_force_form(fr.FR_FORM_PER)
+    try:
+        with pytest.raises(fr.FrError):
+            fr.fr_plan_query(fr.FR_OP_ADD_2D, 64, 64)
+    finally:
+        fr.fr_force_form(prev)
+    fr.fr_tune_override(fr.FR_OP_ADD_2D, form=fr.FR_FORM_POINTWISE, threads=256, rows_per_wg=32, chunk=100)
+    try:
+        with pytest.raises(fr.FrError):  # 32 x 100 is not a whole number of 1024-element passes
+            fr.fr_plan_query(fr.FR_OP_ADD_2D, 64, 64)
+    finally:
+        fr.fr_tune_override(fr.FR_OP_ADD_2D)
+    # arguments rejected before any HIP call (no GPU needed)
+    assert fr.lib.fr_add_2d(None, 4, 1, None, 4, 1, None, 4, 2, 4, fr.FR_F32, None) == fr.FR_E_NULL
+    assert fr.lib.fr_add_2d(None, 4, 1, None, 4, 1, None, 4, 0, 4, fr.FR_F32, None) == fr.FR_OK
+    assert fr.lib.fr_add_2d(None, 4, 1, None, 4, 1, None, 4, 2, 4, fr.FR_BF16, None) == fr.FR_E_DTYPE
+    assert fr.lib.fr_gelu_backward(None, 2, None, None, 8, fr.FR_F32, None) == fr.FR_E_STRIDE
+    assert fr.lib.fr_gelu_backward(None, 0, None, None, 0, fr.FR_F32, None) == fr.FR_OK
+    assert fr.lib.fr_gelu_backward(None, 0, None, None, -1, fr.FR_F32, None) == fr.FR_E_SIZE

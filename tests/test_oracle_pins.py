@@ -585,3 +585,8 @@ def test_gelu_backward_broadcasts_one_upstream_value():
     g = np.arange(1, 8, dtype=np.float64)
     per, _ = oracle.gelu_backward(g, h)
     assert np.allclose(per, g * unit, rtol=1e-15)
+
+
+def test_round_bf16_is_the_scalar_rounding_elementwise():
+    v = np.array([1.0, 1.0 + 2.0**-8, 1.0 + 3 * 2.0**-8, -2.0, 0.0, -0.0, math.inf, 3.4e38, 1e-40, -5.5e-3])
+    assert oracle.round_bf16(v).tolist() == [oracle.f64_to_bf16(x) for x in v]
