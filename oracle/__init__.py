@@ -57,6 +57,8 @@ def _load():
         "orc_attn_merge": (None, [F64, F64, P, F64, F64, P, I64, P, P, P]),
         "orc_add_2d": (None, [P, I64, I64, P, I64, I64, P, I64, I64, I64]),
         "orc_round_bf16": (None, [P, I64, P]),
+        "orc_layernorm_stats": (None, [P, I64, I64, I64, F64, P, P]),
+        "orc_layernorm_backward_rows": (None, [P, P, P, P, P, I64, I64, I64, I64, P, P, P, P, P, P]),
         "orc_gelu_backward": (None, [P, I64, P, I64, P, P]),
     }
     for name, (res, args) in sig.items():
@@ -243,6 +245,35 @@ def layernorm_rows(x_bf16, gamma=None, beta=None, eps=1e-5):
     mag = np.empty((rows, cols), dtype=np.float64)
     _load().orc_layernorm_rows(_p(x), _p(g), _p(b), rows, cols, x_rs, float(eps), _p(y), _p(y64), _p(mag), cols)
     return y, y64, mag
+
+
+def layernorm_stats(x_bf16, eps=1e-5):
+    """(mean, rstd) per row in fp64, as the forward pass saves them."""
+    x, rows, cols, x_rs = _rows2d(x_bf16, np.uint16)
+    mean = np.empty(rows)
+    rstd = np.empty(rows)
+    _load().orc_layernorm_stats(_p(x), rows, cols, x_rs, float(eps), _p(mean), _p(rstd))
+    return mean, rstd
+
+
+def layernorm_backward_rows(x_bf16, dy_bf16, gamma, mean, rstd):
+    """LayerNorm backward from saved (mean, rstd) (see orc_layernorm_backward_rows).
+    x, dy: bf16 bits [rows, cols]; gamma: bf16 bits [cols] or None; mean, rstd:
+    [rows] values (any float dtype). Returns a dict with dx64, dxmag [rows, cols]
+    and dgamma64, dbeta64, gmag, bmag [cols]."""
+    x, rows, cols, x_rs = _rows2d(x_bf16, np.uint16)
+    dy, r2, c2, dy_rs = _rows2d(dy_bf16, np.uint16)
+    assert (r2, c2) == (rows, cols)
+    g = None if gamma is None else np.ascontiguousarray(gamma, dtype=np.uint16)
+    mean = np.ascontiguousarray(mean, dtype=np.float64)
+    rstd = np.ascontiguousarray(rstd, dtype=np.float64)
+    assert mean.size == rows and rstd.size == rows
+    out = {k: np.empty((rows, cols)) for k in ("dx64", "dxmag")}
+    out.update({k: np.empty(cols) for k in ("dgamma64", "dbeta64", "gmag", "bmag")})
+    _load().orc_layernorm_backward_rows(_p(x), _p(dy), _p(g), _p(mean), _p(rstd), rows, cols, x_rs, dy_rs,
+                                        *(_p(out[k]) for k in ("dx64", "dxmag", "dgamma64", "dbeta64", "gmag",
+                                                               "bmag")))
+    return out
 
 
 # ------------------------------------------------------------------ sum of squares

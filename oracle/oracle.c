@@ -379,6 +379,81 @@ void orc_layernorm_rows(const uint16_t* x, const uint16_t* gamma, const uint16_t
     }
 }
 
+/*
+ * The row statistics of the LayerNorm above, as the forward pass of a
+ * training step saves them: mu = sum(x)/N and rstd = 1 / sqrt(var + eps) with
+ * the biased two-pass variance, in fp64 over the bf16 row.
+ */
+void orc_layernorm_stats(const uint16_t* x, int64_t rows, int64_t cols, int64_t x_rs, double eps, double* mean,
+                         double* rstd) {
+    for (int64_t r = 0; r < rows; ++r) {
+        const uint16_t* xr = x + r * x_rs;
+        double s = 0.0;
+        for (int64_t j = 0; j < cols; ++j) s += orc_bf16_to_double(xr[j]);
+        const double mu = s / (double)cols;
+        double q = 0.0;
+        for (int64_t j = 0; j < cols; ++j) {
+            const double d = orc_bf16_to_double(xr[j]) - mu;
+            q += d * d;
+        }
+        mean[r] = mu;
+        rstd[r] = 1.0 / sqrt(q / (double)cols + eps);
+    }
+}
+
+/*
+ * LayerNorm backward. The pages define no LayerNorm gradient; this is the
+ * derivative of the forward definition above, in which mu and rstd are
+ * functions of the row. With xh_j = (x_j - mu) rstd, g_j = dy_j gamma_j and
+ * C = cols:
+ *   dx_j     = rstd (g_j - (1/C) sum_k g_k - xh_j (1/C) sum_k g_k xh_k)
+ *   dgamma_j = sum_i dy_ij xh_ij,      dbeta_j = sum_i dy_ij.
+ * mu and rstd are inputs: the values the forward pass saved (read, not
+ * recomputed, by the backward pass). fp64 over bf16 x, dy, gamma (NULL: 1).
+ *   dx64   [rows, cols], row stride cols.
+ *   dxmag  (nullable): rstd (|g_j| + (1/C) sum|g_k| + |xh_j| (1/C) sum|g_k xh_k|),
+ *          the size of the terms of dx_j.
+ *   dgamma64, dbeta64 [cols] (nullable); gmag, bmag (nullable): sum_i |dy_ij xh_ij|
+ *          and sum_i |dy_ij|, the sizes of their terms.
+ */
+void orc_layernorm_backward_rows(const uint16_t* x, const uint16_t* dy, const uint16_t* gamma, const double* mean,
+                                 const double* rstd, int64_t rows, int64_t cols, int64_t x_rs, int64_t dy_rs,
+                                 double* dx64, double* dxmag, double* dgamma64, double* dbeta64, double* gmag,
+                                 double* bmag) {
+    for (int64_t j = 0; j < cols; ++j) {
+        if (dgamma64) dgamma64[j] = 0.0;
+        if (dbeta64) dbeta64[j] = 0.0;
+        if (gmag) gmag[j] = 0.0;
+        if (bmag) bmag[j] = 0.0;
+    }
+    const double C = (double)cols;
+    for (int64_t r = 0; r < rows; ++r) {
+        const uint16_t* xr = x + r * x_rs;
+        const uint16_t* gr = dy + r * dy_rs;
+        const double mu = mean[r], rs = rstd[r];
+        double sg = 0.0, sgx = 0.0, ag = 0.0, agx = 0.0;
+        for (int64_t j = 0; j < cols; ++j) {
+            const double xh = (orc_bf16_to_double(xr[j]) - mu) * rs;
+            const double d = orc_bf16_to_double(gr[j]);
+            const double g = d * (gamma ? orc_bf16_to_double(gamma[j]) : 1.0);
+            sg += g;
+            sgx += g * xh;
+            ag += fabs(g);
+            agx += fabs(g * xh);
+            if (dgamma64) dgamma64[j] += d * xh;
+            if (dbeta64) dbeta64[j] += d;
+            if (gmag) gmag[j] += fabs(d * xh);
+            if (bmag) bmag[j] += fabs(d);
+        }
+        for (int64_t j = 0; j < cols; ++j) {
+            const double xh = (orc_bf16_to_double(xr[j]) - mu) * rs;
+            const double g = orc_bf16_to_double(gr[j]) * (gamma ? orc_bf16_to_double(gamma[j]) : 1.0);
+            dx64[r * cols + j] = rs * (g - sg / C - xh * (sgx / C));
+            if (dxmag) dxmag[r * cols + j] = rs * (fabs(g) + ag / C + fabs(xh) * (agx / C));
+        }
+    }
+}
+
 /* --------------------------------------------------------- sum of squares (C4) */
 
 /*

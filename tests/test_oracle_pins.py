@@ -590,3 +590,80 @@ def test_gelu_backward_broadcasts_one_upstream_value():
 def test_round_bf16_is_the_scalar_rounding_elementwise():
     v = np.array([1.0, 1.0 + 2.0**-8, 1.0 + 3 * 2.0**-8, -2.0, 0.0, -0.0, math.inf, 3.4e38, 1e-40, -5.5e-3])
     assert oracle.round_bf16(v).tolist() == [oracle.f64_to_bf16(x) for x in v]
+
+
+# -------------------------------------------------------------- LayerNorm backward
+
+
+def _ln_forward64(x, gamma, beta, eps):
+    """The LayerNorm definition in fp64 numpy (biased variance), for finite
+    differences: an independent statement of the forward pass."""
+    mu = x.mean(axis=-1, keepdims=True)
+    var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)
+    return (x - mu) / np.sqrt(var + eps) * gamma + beta
+
+
+def _bf16_rows(rng, shape, scale=1.0, shift=0.0):
+    bits = synth.to_bf16((rng.normal(size=shape) * scale + shift).astype(np.float32))
+    return bits, (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def test_layernorm_stats_match_numpy():
+    rng = np.random.default_rng(101)
+    xb, x = _bf16_rows(rng, (5, 300), scale=3.0, shift=7.0)
+    mean, rstd = oracle.layernorm_stats(xb, eps=1e-5)
+    assert np.allclose(mean, x.mean(axis=1), rtol=1e-14)
+    assert np.allclose(rstd, 1.0 / np.sqrt(x.var(axis=1) + 1e-5), rtol=1e-13)
+
+
+def test_layernorm_backward_matches_finite_differences():
+    rng = np.random.default_rng(102)
+    rows, cols, eps = 3, 37, 1e-5
+    xb, x = _bf16_rows(rng, (rows, cols), scale=2.0, shift=0.5)
+    dyb, dy = _bf16_rows(rng, (rows, cols))
+    gb, g = _bf16_rows(rng, (cols,), scale=0.5, shift=1.0)
+    beta = rng.normal(size=cols)
+    mean, rstd = oracle.layernorm_stats(xb, eps)
+    out = oracle.layernorm_backward_rows(xb, dyb, gb, mean, rstd)
+    L = lambda xx, gg: float((dy * _ln_forward64(xx, gg, beta, eps)).sum())  # noqa: E731
+    h = 1e-6
+    for _ in range(4):
+        u = rng.normal(size=(rows, cols))
+        fd = (L(x + h * u, g) - L(x - h * u, g)) / (2 * h)
+        assert float((out["dx64"] * u).sum()) == pytest.approx(fd, rel=1e-6, abs=1e-8)
+        v = rng.normal(size=cols)
+        fd = (L(x, g + h * v) - L(x, g - h * v)) / (2 * h)
+        assert float(out["dgamma64"] @ v) == pytest.approx(fd, rel=1e-6, abs=1e-8)
+    assert np.allclose(out["dbeta64"], dy.sum(axis=0), rtol=1e-15, atol=0)
+    assert np.all(out["dxmag"] >= np.abs(out["dx64"]) - 1e-12)
+    assert np.all(out["gmag"] >= np.abs(out["dgamma64"])) and np.all(out["bmag"] >= np.abs(out["dbeta64"]))
+
+
+def test_layernorm_backward_closed_forms():
+    # x-hat = +-1 exactly (mean 2, variance 1, eps 0); dy = x-hat gives dx = 0
+    xb = synth.to_bf16(np.array([[1, 3, 1, 3, 3, 1]], dtype=np.float32))
+    mean, rstd = oracle.layernorm_stats(xb, eps=0.0)
+    assert mean[0] == 2.0 and rstd[0] == 1.0
+    dyb = synth.to_bf16(np.array([[-1, 1, -1, 1, 1, -1]], dtype=np.float32))
+    out = oracle.layernorm_backward_rows(xb, dyb, None, mean, rstd)
+    assert np.all(out["dx64"] == 0.0)
+    assert out["dgamma64"].tolist() == [1.0] * 6 and out["dbeta64"].tolist() == [-1, 1, -1, 1, 1, -1]
+    # a constant dy (gamma 1) gives dx = 0
+    rng = np.random.default_rng(103)
+    xb, _ = _bf16_rows(rng, (4, 50))
+    mean, rstd = oracle.layernorm_stats(xb, eps=1e-5)
+    out = oracle.layernorm_backward_rows(xb, synth.to_bf16(np.full((4, 50), 0.75, np.float32)), None, mean, rstd)
+    assert np.allclose(out["dx64"], 0.0, atol=1e-13)
+
+
+def test_layernorm_backward_invariants():
+    # with exact statistics: sum_j dx_j = 0; with eps = 0 also sum_j dx_j xh_j = 0
+    rng = np.random.default_rng(104)
+    xb, x = _bf16_rows(rng, (6, 129), scale=4.0, shift=-3.0)
+    dyb, _ = _bf16_rows(rng, (6, 129))
+    gb, _ = _bf16_rows(rng, (129,), scale=0.3, shift=1.0)
+    mean, rstd = oracle.layernorm_stats(xb, eps=0.0)
+    dx = oracle.layernorm_backward_rows(xb, dyb, gb, mean, rstd)["dx64"]
+    xh = (x - mean[:, None]) * rstd[:, None]
+    assert np.allclose(dx.sum(axis=1), 0.0, atol=1e-12)
+    assert np.allclose((dx * xh).sum(axis=1), 0.0, atol=1e-12)
