@@ -340,6 +340,59 @@ def make_workload(name, torch, fr, synth):
 
         return W(), per_set
 
+    if name == "layernorm_bwd":
+        # LayerNorm backward over the 2048 x 32768 bf16 LayerNorm: dx, dgamma
+        # and dbeta from the saved mean and rstd
+        rows, cols = 2048, 32768
+        x_h, g_h, b_h = synth.layernorm_inputs(rows, cols, seed=3001)
+        dy_h = synth.to_bf16(synth.normal((rows, cols), 3001, stream=5))
+        per_set = 3 * rows * cols * 2
+
+        def bf(bits):
+            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+        class W(Workload):
+            kernel = "fr_per_layernorm_bwd_bf16"
+            bytes = 3 * rows * cols * 2 + cols * 2 + rows * 8 + cols * 8
+            dtype = "bf16"
+
+            def alloc(self, sets):
+                x0, dy0, g = bf(x_h), bf(dy_h), bf(g_h)
+                mean = torch.empty(rows, dtype=torch.float32, device=dev)
+                rstd = torch.empty(rows, dtype=torch.float32, device=dev)
+                fr.fr_layernorm_rows_stats(x0, torch.empty_like(x0), mean=mean, rstd=rstd, gamma=g, beta=bf(b_h))
+                nbytes = fr.fr_layernorm_rows_backward_workspace_bytes(rows, cols)
+                self.ws = torch.empty(nbytes // 4, dtype=torch.float32, device=dev)
+                self.g, self.mean, self.rstd = g, mean, rstd
+                self.dg = torch.empty(cols, dtype=torch.float32, device=dev)
+                self.db = torch.empty(cols, dtype=torch.float32, device=dev)
+                self.args = [(x0 if i == 0 else x0.clone(), dy0 if i == 0 else dy0.clone(), torch.empty_like(x0))
+                             for i in range(sets)]
+
+            def launch(self, k):
+                x, dy, dx = self.args[k]
+                fr.fr_layernorm_rows_backward(x, dy, self.mean, self.rstd, dx, gamma=self.g, dgamma=self.dg,
+                                              dbeta=self.db, ws=self.ws)
+
+            def output(self, k):
+                return self.args[k][2]
+
+            def config(self):
+                p = fr.fr_plan_query(fr.FR_OP_LAYERNORM_BWD, rows, cols, dtype=fr.FR_BF16)
+                return {"workload": "LayerNorm backward 2048x32768 bf16 (dx, dgamma, dbeta from saved mean/rstd; "
+                                    "dy ~ N(0,1))", "rows": rows, "cols": cols, "threads": p.threads,
+                        "partial_rows": p.grid, "form": fr.FORM_NAMES[p.form]}
+
+            def oracle_fn(self):
+                import oracle
+                r = 64
+                mean, rstd = oracle.layernorm_stats(x_h[:r], eps=1e-5)
+                x, dy = x_h[:r].copy(), dy_h[:r].copy()
+                return (lambda: oracle.layernorm_backward_rows(x, dy, g_h, mean, rstd), 3 * r * cols * 2,
+                        f"first {r} of {rows} rows")
+
+        return W(), per_set
+
     if name == "add_2d":
         # x.t() + y ("Stax (4)", 9.3, Example 6.1) at 8192 x 8192 fp32: the
         # first operand transposed, staged through LDS tile by tile
@@ -552,7 +605,7 @@ def main():
     ap.add_argument("--workload", default="softmax",
                     choices=["softmax", "sum_relu_add", "layernorm", "sumsq", "ragged", "copy", "stream_copy",
                              "stream_copy_c3", "stream_read", "attn_decode", "softmax_bwd", "add_2d",
-                             "gelu_bwd"])
+                             "gelu_bwd", "layernorm_bwd"])
     ap.add_argument("--warm", action="store_true", help="one buffer set: reads may hit the MALL")
     ap.add_argument("--eager", action="store_true", help="launch each step from the host (no graph)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)

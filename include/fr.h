@@ -78,6 +78,7 @@ extern "C" {
 #define FR_OP_SOFTMAX_BWD 5
 #define FR_OP_ADD_2D 6
 #define FR_OP_GELU_BWD 7
+#define FR_OP_LAYERNORM_BWD 8
 
 /* Launch plan chosen for one call: the reduction form and its launch
  * configuration ("Stax (4)", 9.6: block sizes and warp counts are launch
@@ -247,6 +248,42 @@ int fr_gelu_backward(const void* dy, int64_t dy_stride, const void* h, void* dx,
  * cols must be >= 1 (FR_E_SIZE otherwise). dtype must be FR_BF16. */
 int fr_layernorm_rows(const void* x, const void* gamma, const void* beta, void* y, int64_t rows, int64_t cols,
                       int64_t x_rs, int64_t x_cs, int64_t y_rs, int64_t y_cs, float eps, int dtype, void* stream);
+
+/* The same LayerNorm, also writing the row statistics a training step's
+ * backward pass reads: mean[i] = mu_i and rstd[i] = 1 / sqrt(var_i + eps),
+ * fp32 [rows] device arrays, 4-byte aligned, each nullable. */
+int fr_layernorm_rows_stats(const void* x, const void* gamma, const void* beta, void* y, float* mean, float* rstd,
+                            int64_t rows, int64_t cols, int64_t x_rs, int64_t x_cs, int64_t y_rs, int64_t y_cs,
+                            float eps, int dtype, void* stream);
+
+/* ------------------------------------------------------------ LayerNorm, backward
+ * The gradient of the LayerNorm above (the pages define the forward pass;
+ * this is the derivative of that definition), from the statistics the
+ * forward pass saved. With xh = (x[i,j] - mean[i]) * rstd[i] and
+ * g = dy[i,j] * gamma[j]:
+ *   dx[i,j]   = rstd[i] * (g - (1/cols) sum_k g_k - xh * (1/cols) sum_k g_k xh_k)
+ *   dgamma[j] = sum_i dy[i,j] * xh,        dbeta[j] = sum_i dy[i,j].
+ * One workgroup holds a row of x and dy in registers: two fused row sums,
+ * then dx. The dgamma / dbeta sums over rows are accumulated per workgroup
+ * in registers, written as partial rows to the workspace and summed in a
+ * fixed order by a second kernel (deterministic; no atomics).
+ *  x, dy, dx:     bf16 [rows, cols], strides as in the conventions; dx may be
+ *                 x or dy (same row stride). dx is rounded to nearest even.
+ *  gamma:         bf16 [cols] or NULL (1).
+ *  mean, rstd:    fp32 [rows], as fr_layernorm_rows_stats writes them.
+ *  dgamma, dbeta: fp32 [cols] or NULL. When either is given, ws must hold
+ *                 fr_layernorm_rows_backward_workspace_bytes(rows, cols)
+ *                 bytes (16-byte aligned; FR_E_WORKSPACE otherwise); else ws
+ *                 may be NULL.
+ * 1 <= cols <= 32768 (FR_E_SIZE otherwise). With dgamma or dbeta and more
+ * than 16384 columns, x, dy, dx and gamma must allow 16-byte accesses (bases
+ * and row strides multiples of 8 elements, cols a multiple of 8; FR_E_ALIGN
+ * otherwise). dtype must be FR_BF16. */
+uint64_t fr_layernorm_rows_backward_workspace_bytes(int64_t rows, int64_t cols, int dtype);
+int fr_layernorm_rows_backward(const void* x, const void* dy, const void* gamma, const float* mean,
+                               const float* rstd, void* dx, float* dgamma, float* dbeta, int64_t rows, int64_t cols,
+                               int64_t x_rs, int64_t x_cs, int64_t dy_rs, int64_t dy_cs, int64_t dx_rs,
+                               int64_t dx_cs, void* ws, uint64_t ws_bytes, int dtype, void* stream);
 
 /* ------------------------------------------------------------ sum of squares
  * fr_sumsq_rows: out[i] = sum_j x[i,j]^2 (fp32 squares, fp32 accumulation;

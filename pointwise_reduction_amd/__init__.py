@@ -29,7 +29,7 @@ FR_E_WORKSPACE, FR_E_ARG, FR_E_DEVICE, FR_E_LAUNCH = -6, -7, -8, -9
 FR_F32, FR_BF16 = 0, 1
 FR_FORM_AUTO, FR_FORM_PER, FR_FORM_RED, FR_FORM_SPLIT, FR_FORM_POINTWISE = 0, 1, 2, 3, 4
 FR_OP_SUM_RELU_ADD, FR_OP_SOFTMAX, FR_OP_LAYERNORM, FR_OP_SUMSQ, FR_OP_SOFTMAX_BWD = 1, 2, 3, 4, 5
-FR_OP_ADD_2D, FR_OP_GELU_BWD = 6, 7
+FR_OP_ADD_2D, FR_OP_GELU_BWD, FR_OP_LAYERNORM_BWD = 6, 7, 8
 FORM_NAMES = {FR_FORM_PER: "per", FR_FORM_RED: "red", FR_FORM_SPLIT: "split", FR_FORM_POINTWISE: "pointwise"}
 
 # Every symbol include/fr.h declares.
@@ -37,7 +37,8 @@ EXPORTS = (
     "fr_status_string", "fr_version", "fr_plan_query", "fr_force_form", "fr_tune_override",
     "fr_sum_relu_add", "fr_sum_workspace_bytes",
     "fr_softmax_rows_workspace_bytes", "fr_softmax_rows", "fr_softmax_rows_backward",
-    "fr_layernorm_rows",
+    "fr_layernorm_rows", "fr_layernorm_rows_stats", "fr_layernorm_rows_backward_workspace_bytes",
+    "fr_layernorm_rows_backward",
     "fr_sumsq_rows", "fr_sumsq_full_workspace_bytes", "fr_sumsq_full",
     "fr_stream_copy", "fr_stream_read",
     "fr_attn_decode_workspace_bytes", "fr_attn_decode",
@@ -91,6 +92,10 @@ def _load():
         "fr_stream_copy": (I32, [P, P, I64, P]),
         "fr_stream_read": (I32, [P, I64, P, P]),
         "fr_add_2d": (I32, [P, I64, I64, P, I64, I64, P, I64, I64, I64, I32, P]),
+        "fr_layernorm_rows_stats": (I32, [P, P, P, P, P, P, I64, I64, I64, I64, I64, I64, ctypes.c_float, I32, P]),
+        "fr_layernorm_rows_backward_workspace_bytes": (U64, [I64, I64, I32]),
+        "fr_layernorm_rows_backward": (I32, [P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I64, I64, I64, P, U64,
+                                             I32, P]),
         "fr_gelu_backward": (I32, [P, I64, P, P, I64, I32, P]),
     }
     for name, (res, args) in sig.items():
@@ -223,6 +228,42 @@ def fr_layernorm_rows(x, y, gamma=None, beta=None, eps=1e-5, stream=None):
     _check(lib.fr_layernorm_rows(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), rows, cols, x_rs, x_cs, y_rs, y_cs,
                                  float(eps), _dtype_code(x), _stream(stream)), "fr_layernorm_rows")
     return y
+
+
+def fr_layernorm_rows_stats(x, y, mean=None, rstd=None, gamma=None, beta=None, eps=1e-5, stream=None):
+    """LayerNorm that also writes the per-row mean and rstd (fp32 [rows])."""
+    rows, cols, x_rs, x_cs = _mat(x)
+    ry, cy, y_rs, y_cs = _mat(y)
+    if (ry, cy) != (rows, cols):
+        raise ValueError("shape mismatch")
+    _check(lib.fr_layernorm_rows_stats(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), _ptr(mean), _ptr(rstd), rows, cols,
+                                       x_rs, x_cs, y_rs, y_cs, float(eps), _dtype_code(x), _stream(stream)),
+           "fr_layernorm_rows_stats")
+    return y
+
+
+def fr_layernorm_rows_backward_workspace_bytes(rows, cols, dtype=FR_BF16):
+    return lib.fr_layernorm_rows_backward_workspace_bytes(rows, cols, dtype)
+
+
+def fr_layernorm_rows_backward(x, dy, mean, rstd, dx, gamma=None, dgamma=None, dbeta=None, ws=None, stream=None):
+    """dx (bf16), and optionally dgamma / dbeta (fp32 [cols]), from the saved
+    mean and rstd. A workspace is allocated when dgamma or dbeta is requested
+    and ws is None."""
+    rows, cols, x_rs, x_cs = _mat(x)
+    r2, c2, dy_rs, dy_cs = _mat(dy)
+    r3, c3, dx_rs, dx_cs = _mat(dx)
+    if (r2, c2) != (rows, cols) or (r3, c3) != (rows, cols):
+        raise ValueError("shape mismatch")
+    if ws is None and (dgamma is not None or dbeta is not None):
+        nbytes = fr_layernorm_rows_backward_workspace_bytes(rows, cols)
+        ws = torch.empty(max(nbytes, 16) // 4, dtype=torch.float32, device=x.device)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.fr_layernorm_rows_backward(_ptr(x), _ptr(dy), _ptr(gamma), _ptr(mean), _ptr(rstd), _ptr(dx),
+                                          _ptr(dgamma), _ptr(dbeta), rows, cols, x_rs, x_cs, dy_rs, dy_cs, dx_rs,
+                                          dx_cs, _ptr(ws), ws_bytes, _dtype_code(x), _stream(stream)),
+           "fr_layernorm_rows_backward")
+    return dx
 
 
 def fr_sumsq_rows(x, out, ws=None, stream=None):

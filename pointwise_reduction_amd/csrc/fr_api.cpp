@@ -29,7 +29,7 @@ namespace {
 int g_forced_form = FR_FORM_AUTO;
 
 // Tuning overrides, one per operation (index = FR_OP_*).
-constexpr int kOps = 8;
+constexpr int kOps = 9;
 fr_plan g_override[kOps];
 bool g_has_override[kOps] = {};
 
@@ -279,6 +279,13 @@ int fr_softmax_rows(const void* x, void* y, int64_t rows, int64_t cols, int64_t 
 
 int fr_layernorm_rows(const void* x, const void* gamma, const void* beta, void* y, int64_t rows, int64_t cols,
                       int64_t x_rs, int64_t x_cs, int64_t y_rs, int64_t y_cs, float eps, int dtype, void* stream) {
+    return fr_layernorm_rows_stats(x, gamma, beta, y, nullptr, nullptr, rows, cols, x_rs, x_cs, y_rs, y_cs, eps,
+                                   dtype, stream);
+}
+
+int fr_layernorm_rows_stats(const void* x, const void* gamma, const void* beta, void* y, float* mean, float* rstd,
+                            int64_t rows, int64_t cols, int64_t x_rs, int64_t x_cs, int64_t y_rs, int64_t y_cs,
+                            float eps, int dtype, void* stream) {
     int st = check_sizes(rows, cols);
     if (st != FR_OK) return st;
     if (dtype != FR_BF16) return FR_E_DTYPE;
@@ -288,7 +295,7 @@ int fr_layernorm_rows(const void* x, const void* gamma, const void* beta, void* 
     if ((st = check_matrix(x, rows, cols, x_rs, x_cs, 2)) != FR_OK) return st;
     if ((st = check_matrix(y, rows, cols, y_rs, y_cs, 2)) != FR_OK) return st;
     if (x == y && x_rs != y_rs) return FR_E_STRIDE;
-    if (!aligned(gamma, 2) || !aligned(beta, 2)) return FR_E_ALIGN;
+    if (!aligned(gamma, 2) || !aligned(beta, 2) || !aligned(mean, 4) || !aligned(rstd, 4)) return FR_E_ALIGN;
     int num_cus = 0;
     st = device_check(&num_cus);
     if (st != FR_OK) return st;
@@ -299,9 +306,58 @@ int fr_layernorm_rows(const void* x, const void* gamma, const void* beta, void* 
                    override_for(FR_OP_LAYERNORM), &plan);
     if (st != FR_OK) return st;
     LayerNormArgs args{(const uint16_t*)x, (const uint16_t*)gamma, (const uint16_t*)beta, (uint16_t*)y,
-                       (int)rows, (int)cols, x_rs, y_rs, eps};
+                       (int)rows, (int)cols, x_rs, y_rs, eps, mean, rstd};
     (void)hipGetLastError();
     return finish_launch(launch_layernorm(plan, args, (hipStream_t)stream));
+}
+
+uint64_t fr_layernorm_rows_backward_workspace_bytes(int64_t rows, int64_t cols, int dtype) {
+    if (dtype != FR_BF16 || check_sizes(rows, cols) != FR_OK || rows == 0 || cols == 0) return 0;
+    fr_plan plan;
+    // the workspace does not depend on alignment or the device
+    if (make_plan(FR_OP_LAYERNORM_BWD, rows, cols, FR_BF16, 256, 0, 0, 1, FR_FORM_AUTO,
+                  override_for(FR_OP_LAYERNORM_BWD), &plan) != FR_OK)
+        return 0;
+    return plan.ws_bytes;
+}
+
+int fr_layernorm_rows_backward(const void* x, const void* dy, const void* gamma, const float* mean,
+                               const float* rstd, void* dx, float* dgamma, float* dbeta, int64_t rows, int64_t cols,
+                               int64_t x_rs, int64_t x_cs, int64_t dy_rs, int64_t dy_cs, int64_t dx_rs,
+                               int64_t dx_cs, void* ws, uint64_t ws_bytes, int dtype, void* stream) {
+    int st = check_sizes(rows, cols);
+    if (st != FR_OK) return st;
+    if (dtype != FR_BF16) return FR_E_DTYPE;
+    if (cols < 1) return FR_E_SIZE;
+    if (rows == 0 && !dgamma && !dbeta) return FR_OK;
+    // no rows with dgamma / dbeta: only the column sums run (empty sums: 0)
+    if (rows > 0) {
+        if ((st = check_matrix(x, rows, cols, x_rs, x_cs, 2)) != FR_OK) return st;
+        if ((st = check_matrix(dy, rows, cols, dy_rs, dy_cs, 2)) != FR_OK) return st;
+        if ((st = check_matrix(dx, rows, cols, dx_rs, dx_cs, 2)) != FR_OK) return st;
+        if ((dx == x && dx_rs != x_rs) || (dx == dy && dx_rs != dy_rs)) return FR_E_STRIDE;
+        if (!mean || !rstd) return FR_E_NULL;
+    }
+    if (!aligned(gamma, 2) || !aligned(mean, 4) || !aligned(rstd, 4) || !aligned(dgamma, 4) || !aligned(dbeta, 4) ||
+        !aligned(ws, 16))
+        return FR_E_ALIGN;
+    const int v16 = cols % 8 == 0 && vec_ok(x, x_rs, 8) && vec_ok(dy, dy_rs, 8) && vec_ok(dx, dx_rs, 8) &&
+                    vec_ok(gamma, 0, 8);
+    fr_plan plan;
+    st = make_plan(FR_OP_LAYERNORM_BWD, rows, cols, FR_BF16, 256, 0, 0, v16, g_forced_form,
+                   override_for(FR_OP_LAYERNORM_BWD), &plan);
+    if (st != FR_OK) return st;
+    const bool dg = dgamma || dbeta;
+    if (dg && plan.ws_bytes > 0 && (!ws || ws_bytes < plan.ws_bytes)) return FR_E_WORKSPACE;
+    // rows beyond 16384 columns with dgamma / dbeta need 16-byte accesses
+    if (dg && !v16 && plan.threads * plan.vec > 1024 * 2) return FR_E_ALIGN;
+    int num_cus = 0;
+    st = device_check(&num_cus);
+    if (st != FR_OK) return st;
+    LayerNormBwdArgs args{(const uint16_t*)x, (const uint16_t*)dy, (const uint16_t*)gamma, mean, rstd,
+                          (uint16_t*)dx, dgamma, dbeta, (float*)ws, (int)rows, (int)cols, x_rs, dy_rs, dx_rs};
+    (void)hipGetLastError();
+    return finish_launch(launch_layernorm_bwd(plan, args, (hipStream_t)stream));
 }
 
 int fr_softmax_rows_backward(const void* y, const void* dy, void* dx, int64_t rows, int64_t cols, int64_t y_rs,

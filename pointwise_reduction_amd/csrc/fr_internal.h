@@ -49,6 +49,8 @@ struct LayerNormArgs {
     int rows, cols;
     int64_t x_rs, y_rs;
     float eps;
+    float* mean;  // nullable: per-row mean, as the backward pass reads it
+    float* rstd;  // nullable: per-row 1 / sqrt(var + eps)
 };
 
 // Partial state of one chunk of a split softmax row: the (m, d) pair of the
@@ -68,6 +70,23 @@ struct alignas(16) SoftmaxPartial {
 hipError_t launch_sum(const fr_plan& p, const SumArgs& a, hipStream_t s);
 hipError_t launch_softmax(const fr_plan& p, const SoftmaxArgs& a, hipStream_t s);
 hipError_t launch_layernorm(const fr_plan& p, const LayerNormArgs& a, hipStream_t s);
+// LayerNorm backward from saved statistics; ws holds the dgamma / dbeta
+// partials [2][grid][ln_bwd_ldw(cols)] fp32 when either is requested.
+struct LayerNormBwdArgs {
+    const uint16_t* x;
+    const uint16_t* dy;
+    const uint16_t* gamma;  // nullable: 1
+    const float* mean;
+    const float* rstd;
+    uint16_t* dx;
+    float* dgamma;  // nullable
+    float* dbeta;   // nullable
+    float* ws;
+    int rows, cols;
+    int64_t x_rs, dy_rs, dx_rs;
+};
+inline int64_t ln_bwd_ldw(int64_t cols) { return (cols + 7) / 8 * 8; }
+hipError_t launch_layernorm_bwd(const fr_plan& p, const LayerNormBwdArgs& a, hipStream_t s);
 hipError_t launch_softmax_bwd(const fr_plan& p, const SoftmaxBwdArgs& a, hipStream_t s);
 // Pointwise: 2-D add (a_t / b_t: the operand is column-major, a transposed
 // view with unit row stride) and GELU backward.

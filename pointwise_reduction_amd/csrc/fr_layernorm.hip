@@ -122,11 +122,20 @@ __device__ __forceinline__ void affine_row(const u32x4* v, __amdgpu_buffer_rsrc_
     }
 }
 
+// The statistics a training step's backward pass reads (both nullable).
+__device__ __forceinline__ void save_stats(float* mean_out, float* rstd_out, int r, float mu, float rstd) {
+    if (threadIdx.x == 0) {
+        if (mean_out) mean_out[r] = mu;
+        if (rstd_out) rstd_out[r] = rstd;
+    }
+}
+
 template <int T, int NV, int M, int OCC, bool UNIT_GAMMA = false>
 __global__ __launch_bounds__(T, OCC) void fr_per_layernorm_bf16(const uint16_t* x, const uint16_t* __restrict__ gamma,
                                                                 const uint16_t* __restrict__ beta, uint16_t* y,
                                                                 int rows, int cols, int64_t x_rs, int64_t y_rs,
-                                                                float eps) {
+                                                                float eps, float* __restrict__ mean_out,
+                                                                float* __restrict__ rstd_out) {
     __shared__ float sl_s[T / kWave];
     __shared__ float sl_q[T / kWave];
     const int tid = threadIdx.x;
@@ -180,6 +189,7 @@ __global__ __launch_bounds__(T, OCC) void fr_per_layernorm_bf16(const uint16_t* 
         q = group_reduce<kWave>(q, OpSum());
         q = block_fold(q, sl_q, T / kWave, OpSum());
         const float rstd = 1.0f / sqrtf(q / n + eps);
+        save_stats(mean_out, rstd_out, r, mu, rstd);
         uint16_t* yr = y + (int64_t)r * y_rs;
         if constexpr (BUF) {
             const __amdgpu_buffer_rsrc_t ry = row_rsrc(yr, bytes);
@@ -250,7 +260,9 @@ __device__ __forceinline__ void normalize_step(const uint16_t* xr, uint16_t* yr,
 template <int T, int U, bool VEC>
 __global__ __launch_bounds__(T) void fr_red_layernorm_bf16(const uint16_t* x, const uint16_t* __restrict__ gamma,
                                                            const uint16_t* __restrict__ beta, uint16_t* y, int rows,
-                                                           int cols, int64_t x_rs, int64_t y_rs, float eps) {
+                                                           int cols, int64_t x_rs, int64_t y_rs, float eps,
+                                                           float* __restrict__ mean_out,
+                                                           float* __restrict__ rstd_out) {
     constexpr int STEP = T * 8 * U;
     constexpr int BODY = VEC ? kNone : kScalar;
     constexpr int TAIL = VEC ? kVec : kScalar;
@@ -266,6 +278,7 @@ __global__ __launch_bounds__(T) void fr_red_layernorm_bf16(const uint16_t* x, co
         st = block_fold(st, sl, T / kWave, OpStat());
         const float mu = st.mu;
         const float rstd = 1.0f / sqrtf(st.m2 / (float)cols + eps);
+        save_stats(mean_out, rstd_out, r, mu, rstd);
         uint16_t* yr = y + (int64_t)r * y_rs;
         for (base = 0; base < full; base += STEP) normalize_step<BODY, T, U>(xr, yr, base, cols, gamma, beta, mu, rstd);
         if (base < cols) normalize_step<TAIL, T, U>(xr, yr, base, cols, gamma, beta, mu, rstd);
@@ -273,11 +286,230 @@ __global__ __launch_bounds__(T) void fr_red_layernorm_bf16(const uint16_t* x, co
     }
 }
 
+// ------------------------------------------------------------------ backward
+// The derivative of the forward definition, from the statistics the forward
+// pass saved: with xh = (x - mu) rstd and g = dy gamma,
+//   dx = rstd (g - mean(g) - xh mean(g xh)),
+//   dgamma = sum over rows of dy xh,  dbeta = sum over rows of dy.
+// Persistent: one workgroup of T threads holds a row of x and of dy in
+// registers (NV vectors of 8 bf16 per lane and array), forms the two row
+// sums in a first pass over the registers and writes dx in a second. Each
+// lane keeps the same columns for every row its workgroup handles, so with
+// DG the second pass also accumulates that workgroup's dgamma and dbeta
+// contributions (there, where x-hat and dy are unpacked anyway; in the first
+// pass the compiler kept both unpacked copies alive) and the workgroup writes
+// them as one partial row of ws[2][G][ldw] at the end; fr_layernorm_bwd_fin
+// sums the G partials of each column in a fixed order. Masked elements read
+// x = dy = 0 and contribute nothing (g = 0 and dy = 0). With 4 vectors per lane the dbeta partials
+// live in LDS instead (each lane reads and writes only its own 8 x NV
+// slots, so no barrier is involved): up to 128 KB for a 32768-column row,
+// which keeps the register count under the 128 that 16 waves of a
+// 1024-thread workgroup may use.
+__device__ __forceinline__ float lane8(u32x4 v, int e) { return (e & 1) ? bf16_hi(word(v, e >> 1)) : bf16_lo(word(v, e >> 1)); }
+
+template <int T, int NV, int M, bool DG>
+__global__ __launch_bounds__(T) void fr_per_layernorm_bwd_bf16(const uint16_t* x, const uint16_t* dy,
+                                                               const uint16_t* __restrict__ gamma,
+                                                               const float* __restrict__ mean,
+                                                               const float* __restrict__ rstd, uint16_t* dx,
+                                                               float* __restrict__ ws, int rows, int cols,
+                                                               int64_t x_rs, int64_t dy_rs, int64_t dx_rs,
+                                                               int64_t ldw) {
+    constexpr bool BL = DG && NV == 4;  // dbeta partials in LDS
+    // 16-byte aligned rows use buffer instructions: the row base sits in a
+    // scalar resource and a lane needs no 64-bit addresses. Whole rows
+    // (kNone) put the vector's offset in the scalar offset; with kVec the
+    // whole offset is in the lane's offset register, which the resource's
+    // range check covers: vectors past the row read zeros and are not stored.
+    constexpr bool BUF = M == kNone || M == kVec;
+    auto bvo = [](int k) { return M == kNone ? (int)threadIdx.x * 16 : (k * T + (int)threadIdx.x) * 16; };
+    auto bso = [](int k) { return M == kNone ? k * T * 16 : 0; };
+    __shared__ float sl_a[T / kWave];
+    __shared__ float sl_b[T / kWave];
+    __shared__ f32x4 lb[BL ? T * NV * 2 : 1];
+    const int tid = threadIdx.x;
+    const float n = (float)cols;
+    u32x4 gv[NV];
+#pragma unroll
+    for (int k = 0; k < NV; ++k)
+        gv[k] = gamma ? load8m<M, false>(gamma, (k * T + tid) * 8, cols)
+                      : u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // 1.0
+    float ag[DG ? NV : 1][8], ab[DG && !BL ? NV : 1][8];
+    if constexpr (DG) {
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ag[k][e] = 0.f;
+            if constexpr (BL) {
+                lb[(k * T + tid) * 2] = f32x4{0.f, 0.f, 0.f, 0.f};
+                lb[(k * T + tid) * 2 + 1] = f32x4{0.f, 0.f, 0.f, 0.f};
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ab[k][e] = 0.f;
+            }
+        }
+    }
+    for (int r = blockIdx.x; r < rows; r += gridDim.x) {
+        const uint16_t* xr = x + (int64_t)r * x_rs;
+        const uint16_t* dr = dy + (int64_t)r * dy_rs;
+        u32x4 xv[NV], dv[NV];
+        if constexpr (BUF) {
+            const __amdgpu_buffer_rsrc_t rx = row_rsrc(xr, (uint32_t)cols * 2u);
+            const __amdgpu_buffer_rsrc_t rd = row_rsrc(dr, (uint32_t)cols * 2u);
+#pragma unroll
+            for (int k = 0; k < NV; ++k) {
+                xv[k] = __builtin_amdgcn_raw_buffer_load_b128(rx, bvo(k), bso(k), kAuxNT);
+                dv[k] = __builtin_amdgcn_raw_buffer_load_b128(rd, bvo(k), bso(k), kAuxNT);
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < NV; ++k) {
+                xv[k] = load8m<M, true>(xr, (k * T + tid) * 8, cols);
+                dv[k] = load8m<M, true>(dr, (k * T + tid) * 8, cols);
+            }
+        }
+        const float mu = mean[r], rs = rstd[r];
+        float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+        for (int k = 0; k < NV; ++k)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float xh = (lane8(xv[k], e) - mu) * rs;
+                const float g = lane8(dv[k], e) * lane8(gv[k], e);
+                s1 += g;
+                s2 += g * xh;
+            }
+        // the second pass unpacks x, dy and gamma again rather than keeping
+        // 3 x 8 fp32 copies per vector alive across the row sums
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            hide(xv[k]);
+            hide(dv[k]);
+            hide(gv[k]);
+        }
+        s1 = group_reduce<kWave>(s1, OpSum());
+        s2 = group_reduce<kWave>(s2, OpSum());
+        s1 = block_fold(s1, sl_a, T / kWave, OpSum());
+        s2 = block_fold(s2, sl_b, T / kWave, OpSum());
+        const float m1 = s1 / n, m2 = s2 / n;
+        // second pass: dx, and this row's dgamma / dbeta contributions
+        uint16_t* outr = dx + (int64_t)r * dx_rs;
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            const int j0 = (k * T + tid) * 8;
+            f32x4 b0, b1;
+            if constexpr (BL) {
+                b0 = lb[(k * T + tid) * 2];
+                b1 = lb[(k * T + tid) * 2 + 1];
+            }
+            uint32_t o[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float v[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int e = 2 * i + h;
+                    const float d = lane8(dv[k], e);
+                    const float xh = (lane8(xv[k], e) - mu) * rs;
+                    const float g = d * lane8(gv[k], e);
+                    v[h] = rs * ((g - m1) - xh * m2);
+                    if constexpr (DG) {
+                        ag[k][e] += d * xh;
+                        if constexpr (BL) {
+                            if (e < 4) b0[e] += d;
+                            else b1[e - 4] += d;
+                        } else {
+                            ab[k][e] += d;
+                        }
+                    }
+                }
+                o[i] = pack_bf16(v[0], v[1]);
+            }
+            if constexpr (BL) {
+                lb[(k * T + tid) * 2] = b0;
+                lb[(k * T + tid) * 2 + 1] = b1;
+            }
+            if constexpr (BUF)
+                __builtin_amdgcn_raw_buffer_store_b128(u32x4{o[0], o[1], o[2], o[3]},
+                                                       row_rsrc(outr, (uint32_t)cols * 2u), bvo(k), bso(k), kAuxNT);
+            else if (j0 < cols)
+                store8m<M, true>(outr, j0, cols, u32x4{o[0], o[1], o[2], o[3]});
+        }
+        __syncthreads();  // slots are rewritten by the next row
+    }
+    if constexpr (DG) {
+        float* pg = ws + (int64_t)blockIdx.x * ldw;
+        float* pb = ws + ((int64_t)gridDim.x + blockIdx.x) * ldw;
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            const int j0 = (k * T + tid) * 8;
+            f32x4 b0, b1;
+            if constexpr (BL) {
+                b0 = lb[(k * T + tid) * 2];
+                b1 = lb[(k * T + tid) * 2 + 1];
+            } else {
+                b0 = f32x4{ab[k][0], ab[k][1], ab[k][2], ab[k][3]};
+                b1 = f32x4{ab[k][4], ab[k][5], ab[k][6], ab[k][7]};
+            }
+            if (M == kNone || j0 + 8 <= cols) {
+                // ldw and ws are multiples of 8 floats / 16-byte aligned
+                st4<false>(pg + j0, f32x4{ag[k][0], ag[k][1], ag[k][2], ag[k][3]});
+                st4<false>(pg + j0 + 4, f32x4{ag[k][4], ag[k][5], ag[k][6], ag[k][7]});
+                st4<false>(pb + j0, b0);
+                st4<false>(pb + j0 + 4, b1);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (j0 + e < cols) {
+                        pg[j0 + e] = ag[k][e];
+                        pb[j0 + e] = e < 4 ? b0[e] : b1[e - 4];
+                    }
+            }
+        }
+    }
+}
+
+// dgamma[j] = sum_g ws[0][g][j], dbeta[j] = sum_g ws[1][g][j]: 256 threads as
+// Q column quads x S slices; slice s sums partials g = s, s + S, ... in
+// order, then slice 0 adds the slices in order. Every run gives the same bits.
+template <int Q, int S>
+__global__ __launch_bounds__(Q * S) void fr_layernorm_bwd_fin(const float* __restrict__ ws, float* __restrict__ dgamma,
+                                                              float* __restrict__ dbeta, int G, int cols,
+                                                              int64_t ldw) {
+    __shared__ f32x4 sg[S][Q];
+    __shared__ f32x4 sb[S][Q];
+    const int q = threadIdx.x % Q, sl = threadIdx.x / Q;
+    const int j = (blockIdx.x * Q + q) * 4;
+    f32x4 ag = {0.f, 0.f, 0.f, 0.f}, ab = {0.f, 0.f, 0.f, 0.f};
+    if (j < cols) {
+        for (int g = sl; g < G; g += S) {
+            ag += ld4<true>(ws + (int64_t)g * ldw + j);
+            ab += ld4<true>(ws + ((int64_t)G + g) * ldw + j);
+        }
+    }
+    sg[sl][q] = ag;
+    sb[sl][q] = ab;
+    __syncthreads();
+    if (sl == 0 && j < cols) {
+#pragma unroll
+        for (int t = 1; t < S; ++t) {
+            ag += sg[t][q];
+            ab += sb[t][q];
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            if (j + c < cols) {
+                if (dgamma) dgamma[j + c] = ag[c];
+                if (dbeta) dbeta[j + c] = ab[c];
+            }
+    }
+}
+
 // ------------------------------------------------------------------ launchers
 namespace {
 
 using LnFn = void (*)(const uint16_t*, const uint16_t*, const uint16_t*, uint16_t*, int, int, int64_t, int64_t,
-                      float);
+                      float, float*, float*);
 
 // Persistent configurations: 16-byte vector kernels hold up to 8 vectors
 // (64 bf16) per lane, or 4 with 1024 threads, without spilling; element-wise
@@ -329,7 +561,62 @@ LnFn pick_red(int threads, int u) {
     return nullptr;
 }
 
+using LnBwdFn = void (*)(const uint16_t*, const uint16_t*, const uint16_t*, const float*, const float*, uint16_t*,
+                         float*, int, int, int64_t, int64_t, int64_t, int64_t);
+
+template <int M, bool DG>
+LnBwdFn pick_bwd_m(int threads, int nv) {
+    // element accesses with 4 vectors per lane and column partials need more
+    // than the 128 registers a 1024-thread workgroup allows: not compiled
+    if constexpr (M != kScalar || !DG)
+        if (threads == 1024 && nv == 4) return fr_per_layernorm_bwd_bf16<1024, 4, M, DG>;
+    switch (threads * 16 + nv) {
+        case 128 * 16 + 1: return fr_per_layernorm_bwd_bf16<128, 1, M, DG>;
+        case 256 * 16 + 1: return fr_per_layernorm_bwd_bf16<256, 1, M, DG>;
+        case 256 * 16 + 2: return fr_per_layernorm_bwd_bf16<256, 2, M, DG>;
+        case 256 * 16 + 4: return fr_per_layernorm_bwd_bf16<256, 4, M, DG>;
+        case 512 * 16 + 1: return fr_per_layernorm_bwd_bf16<512, 1, M, DG>;
+        case 512 * 16 + 2: return fr_per_layernorm_bwd_bf16<512, 2, M, DG>;
+        case 512 * 16 + 4: return fr_per_layernorm_bwd_bf16<512, 4, M, DG>;
+        case 1024 * 16 + 1: return fr_per_layernorm_bwd_bf16<1024, 1, M, DG>;
+        case 1024 * 16 + 2: return fr_per_layernorm_bwd_bf16<1024, 2, M, DG>;
+    }
+    return nullptr;
+}
+
+template <bool DG>
+LnBwdFn pick_bwd(int mask, int threads, int nv) {
+    switch (mask) {
+        case kNone: return pick_bwd_m<kNone, DG>(threads, nv);
+        case kVec: return pick_bwd_m<kVec, DG>(threads, nv);
+        default: return pick_bwd_m<kScalar, DG>(threads, nv);
+    }
+}
+
 }  // namespace
+
+hipError_t launch_layernorm_bwd(const fr_plan& p, const LayerNormBwdArgs& a, hipStream_t s) {
+    const bool vec = p.vec16 != 0;
+    const bool dg = a.dgamma || a.dbeta;
+    const int mask = !vec ? kScalar : (a.cols == 8 * p.threads * p.vec ? kNone : kVec);
+    LnBwdFn f = p.form == FR_FORM_PER ? (dg ? pick_bwd<true>(mask, p.threads, p.vec)
+                                             : pick_bwd<false>(mask, p.threads, p.vec))
+                                      : nullptr;
+    if (!f) return hipErrorInvalidDeviceFunction;
+    const int64_t ldw = ln_bwd_ldw(a.cols);
+    if (a.rows > 0) {
+        hipLaunchKernelGGL(f, dim3((unsigned)p.grid), dim3(p.threads), 0, s, a.x, a.dy, a.gamma, a.mean, a.rstd,
+                           a.dx, a.ws, a.rows, a.cols, a.x_rs, a.dy_rs, a.dx_rs, ldw);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (!dg) return hipSuccess;
+    constexpr int Q = 16, S = 16;
+    const int64_t grid2 = (a.cols + 4 * Q - 1) / (4 * Q);
+    hipLaunchKernelGGL((fr_layernorm_bwd_fin<Q, S>), dim3((unsigned)grid2), dim3(Q * S), 0, s, a.ws, a.dgamma,
+                       a.dbeta, (int)p.grid, a.cols, ldw);
+    return hipGetLastError();
+}
 
 hipError_t launch_layernorm(const fr_plan& p, const LayerNormArgs& a, hipStream_t s) {
     const bool vec = p.vec16 != 0;
@@ -342,7 +629,7 @@ hipError_t launch_layernorm(const fr_plan& p, const LayerNormArgs& a, hipStream_
         f = vec ? pick_red<true>(p.threads, p.vec) : pick_red<false>(p.threads, p.vec);
     if (!f) return hipErrorInvalidDeviceFunction;
     hipLaunchKernelGGL(f, dim3((unsigned)p.grid), dim3(p.threads), 0, s, a.x, a.gamma, a.beta, a.y, a.rows, a.cols,
-                       a.x_rs, a.y_rs, a.eps);
+                       a.x_rs, a.y_rs, a.eps, a.mean, a.rstd);
     return hipGetLastError();
 }
 

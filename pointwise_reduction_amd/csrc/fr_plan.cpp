@@ -37,6 +37,12 @@ constexpr int kSoftmaxSplitThreads = 256, kSoftmaxSplitNV = 8;   // 8192-float c
 // faster, 16384 x 1024 3% slower).
 constexpr int64_t kTwoRowsPerWaveMaxRows = 8192;
 
+// LayerNorm backward: rows up to 1024 threads x 4 vectors x 8 bf16; the
+// grid (and the number of dgamma / dbeta partial rows) is at most 256
+// workgroups of 1024 threads, or as many threads in smaller workgroups.
+constexpr int kLnBwdMaxCols = 1024 * 4 * 8;
+constexpr int kLnBwdWgs1024 = 256;
+
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
 int pow2_ceil(int v) {
@@ -101,8 +107,19 @@ int finalize_plan(int op, int64_t rows, int64_t cols, const Knobs& k, fr_plan* p
     p->vec = k.vec;
     p->occupancy = k.occ;
     if (k.threads < 64 || k.threads > 1024 || k.threads % 64 || k.vec < 1 || k.vec > 16) return FR_E_ARG;
-    const bool f32 = op != FR_OP_LAYERNORM;
+    const bool f32 = op != FR_OP_LAYERNORM && op != FR_OP_LAYERNORM_BWD;
     if (k.form == FR_FORM_PER) {
+        if (op == FR_OP_LAYERNORM_BWD) {
+            if (cols > (int64_t)k.threads * 8 * k.vec) return FR_E_ARG;
+            // one partial row of dgamma / dbeta per workgroup: enough
+            // workgroups to fill the device, and at least 16 rows per
+            // workgroup where the rows allow it, so the partials stay small
+            // next to the rows themselves
+            p->grid = min64(min64(rows, std::max<int64_t>(kLnBwdWgs1024, rows / 16)),
+                            (int64_t)kLnBwdWgs1024 * 1024 / k.threads);
+            p->ws_bytes = (uint64_t)(2 * p->grid * ln_bwd_ldw(cols) * 4);
+            return FR_OK;
+        }
         if (f32) {
             if (k.threads != 256 || !is_pow2(k.seg) || k.seg < 8 || k.seg > 64 || !is_pow2(k.rpw) || k.rpw > 4)
                 return FR_E_ARG;
@@ -294,6 +311,20 @@ int make_plan(int op, int64_t rows, int64_t cols, int dtype, int num_cus, int ha
             } else {
                 return FR_E_ARG;  // rows of LayerNorm are never split
             }
+            break;
+        }
+        case FR_OP_LAYERNORM_BWD: {
+            // persistent only: a workgroup holds the rows of x and dy, and
+            // each lane the dgamma / dbeta partials of its columns, in
+            // registers (at most 4 vectors of 8 bf16 per lane and array)
+            if (dtype != FR_BF16) return FR_E_DTYPE;
+            if (cols < 1 || cols > kLnBwdMaxCols) return FR_E_SIZE;
+            if (forced != FR_FORM_AUTO && forced != FR_FORM_PER) return FR_E_ARG;
+            const int q = (int)cdiv(cols, 8);
+            const int t = std::min(1024, std::max(128, pow2_ceil(q)));
+            k.form = FR_FORM_PER;
+            k.threads = t;
+            k.vec = pow2_ceil((int)cdiv(q, t));
             break;
         }
         default:
