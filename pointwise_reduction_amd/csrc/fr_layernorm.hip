@@ -482,6 +482,7 @@ __global__ __launch_bounds__(Q * S) void fr_layernorm_bwd_fin(const float* __res
     const int j = (blockIdx.x * Q + q) * 4;
     f32x4 ag = {0.f, 0.f, 0.f, 0.f}, ab = {0.f, 0.f, 0.f, 0.f};
     if (j < cols) {
+#pragma unroll 4
         for (int g = sl; g < G; g += S) {
             ag += ld4<true>(ws + (int64_t)g * ldw + j);
             ab += ld4<true>(ws + ((int64_t)G + g) * ldw + j);
@@ -611,7 +612,7 @@ hipError_t launch_layernorm_bwd(const fr_plan& p, const LayerNormBwdArgs& a, hip
         if (e != hipSuccess) return e;
     }
     if (!dg) return hipSuccess;
-    constexpr int Q = 16, S = 16;
+    constexpr int Q = 8, S = 32;
     const int64_t grid2 = (a.cols + 4 * Q - 1) / (4 * Q);
     hipLaunchKernelGGL((fr_layernorm_bwd_fin<Q, S>), dim3((unsigned)grid2), dim3(Q * S), 0, s, a.ws, a.dgamma,
                        a.dbeta, (int)p.grid, a.cols, ldw);
