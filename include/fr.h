@@ -347,6 +347,44 @@ int fr_attn_decode(const void* q, const void* k, const void* v, void* o, float* 
 int fr_stream_copy(const void* x, void* y, int64_t nbytes, void* stream);
 int fr_stream_read(const void* x, int64_t nbytes, uint32_t* sink, void* stream);
 
+/* ------------------------------------------------------------ recorded regions
+ * "Stax (4)", 9.9: a region of n short kernels launched one by one costs
+ * about max(n * t_launch, sum t_k); recorded once as a graph and replayed
+ * with one call it costs about t_graph + sum t_k. A region records the
+ * launches that a callback enqueues on a stream (HIP stream capture) and
+ * replays them while the call is the same:
+ *  - fn(ctx, stream) enqueues the region's work on `stream` (fr_* calls with
+ *    caller-owned buffers; no host synchronization, no allocation, no value
+ *    read back to the host) and returns FR_OK or an error status. For one
+ *    key it must enqueue the same kernels with the same grids (9.9,
+ *    condition 1).
+ *  - key / key_bytes: caller-chosen bytes naming everything a replay fixes,
+ *    i.e. the shapes and the device pointers of the call (condition 2). They
+ *    are compared on every call.
+ *  - First call: records (the recording itself executes nothing), then
+ *    replays once. Later calls with the same key, on the device of the
+ *    recording: one graph launch. A different key or device: fn runs
+ *    directly and the recording is kept. If recording, instantiating or
+ *    replaying fails (for example on the legacy default stream, which cannot
+ *    be captured), the region enters the fallback state and fn runs directly
+ *    from then on.
+ * A replay writes to the recorded output addresses; results that must
+ * outlive the next call are the caller's to copy. The region object is host
+ * memory owned by the caller (create / destroy). Not thread-safe. */
+#define FR_REGION_EMPTY 0
+#define FR_REGION_RECORDED 1
+#define FR_REGION_FALLBACK 2
+typedef struct fr_region fr_region;
+typedef int (*fr_region_fn)(void* ctx, void* stream);
+int fr_region_create(fr_region** out);
+void fr_region_destroy(fr_region* r);
+/* Returns FR_OK after a replay, else what fn returned. */
+int fr_region_run(fr_region* r, const void* key, uint64_t key_bytes, fr_region_fn fn, void* ctx, void* stream);
+/* FR_REGION_* state, or FR_E_NULL. */
+int fr_region_state(const fr_region* r);
+/* Graph launches and direct runs so far (either pointer may be NULL). */
+int fr_region_counts(const fr_region* r, uint64_t* replays, uint64_t* direct);
+
 #ifdef __cplusplus
 }
 #endif

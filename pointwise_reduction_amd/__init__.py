@@ -43,6 +43,7 @@ EXPORTS = (
     "fr_stream_copy", "fr_stream_read",
     "fr_attn_decode_workspace_bytes", "fr_attn_decode",
     "fr_add_2d", "fr_gelu_backward",
+    "fr_region_create", "fr_region_destroy", "fr_region_run", "fr_region_state", "fr_region_counts",
 )
 
 
@@ -97,6 +98,11 @@ def _load():
         "fr_layernorm_rows_backward": (I32, [P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I64, I64, I64, P, U64,
                                              I32, P]),
         "fr_gelu_backward": (I32, [P, I64, P, P, I64, I32, P]),
+        "fr_region_create": (I32, [ctypes.POINTER(P)]),
+        "fr_region_destroy": (None, [P]),
+        "fr_region_run": (I32, [P, P, U64, P, P, P]),
+        "fr_region_state": (I32, [P]),
+        "fr_region_counts": (I32, [P, ctypes.POINTER(U64), ctypes.POINTER(U64)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -365,3 +371,57 @@ def fr_gelu_backward(dy, h, dx, stream=None):
     _check(lib.fr_gelu_backward(_ptr(dy), stride, _ptr(h), _ptr(dx), n, _dtype_code(h), _stream(stream)),
            "fr_gelu_backward")
     return dx
+
+
+# ------------------------------------------------------------------ recorded regions
+
+FR_REGION_EMPTY, FR_REGION_RECORDED, FR_REGION_FALLBACK = 0, 1, 2
+_REGION_FN = ctypes.CFUNCTYPE(ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p)
+
+
+class Region:
+    """A recorded region ("Stax (4)", 9.9): the launches fn(stream) enqueues
+    are recorded once as a HIP graph and replayed while `key` (the shapes and
+    device pointers of the call, as integers) stays the same; otherwise fn
+    runs directly. fn receives the stream as an integer handle and passes it
+    to the fr_* calls it makes; it must use preallocated buffers only."""
+
+    def __init__(self):
+        p = ctypes.c_void_p()
+        _check(lib.fr_region_create(ctypes.byref(p)), "fr_region_create")
+        self._r = p
+
+    def __del__(self):
+        r, self._r = getattr(self, "_r", None), None
+        if r is not None and lib is not None:
+            lib.fr_region_destroy(r)
+
+    def run(self, key, fn, stream=None):
+        kb = b"".join(int(k).to_bytes(8, "little", signed=True) for k in key)
+        err = []
+
+        def cb(_ctx, s):
+            try:
+                fn(0 if s is None else s)
+                return FR_OK
+            except FrError as e:
+                err.append(e)
+                return e.status
+            except Exception as e:  # noqa: BLE001  (reported after the C call returns)
+                err.append(e)
+                return FR_E_ARG
+
+        c = _REGION_FN(cb)
+        st = lib.fr_region_run(self._r, kb, len(kb), c, None, _stream(stream))
+        if err:
+            raise err[-1]
+        _check(st, "fr_region_run")
+
+    @property
+    def state(self):
+        return lib.fr_region_state(self._r)
+
+    def counts(self):
+        rep, direct = ctypes.c_uint64(), ctypes.c_uint64()
+        _check(lib.fr_region_counts(self._r, ctypes.byref(rep), ctypes.byref(direct)), "fr_region_counts")
+        return rep.value, direct.value

@@ -357,3 +357,13 @@ def test_pointwise_plans_and_argument_errors():
     assert fr.lib.fr_gelu_backward(None, 2, None, None, 8, fr.FR_F32, None) == fr.FR_E_STRIDE
     assert fr.lib.fr_gelu_backward(None, 0, None, None, 0, fr.FR_F32, None) == fr.FR_OK
     assert fr.lib.fr_gelu_backward(None, 0, None, None, -1, fr.FR_F32, None) == fr.FR_E_SIZE
+
+
+def test_region_object_without_a_gpu():
+    # create / state / counts / destroy and the argument checks make no HIP call
+    r = fr.Region()
+    assert r.state == fr.FR_REGION_EMPTY and r.counts() == (0, 0)
+    assert fr.lib.fr_region_run(r._r, None, 0, None, None, None) == fr.FR_E_NULL
+    assert fr.lib.fr_region_run(r._r, None, 8, fr._REGION_FN(lambda c, s: 0), None, None) == fr.FR_E_NULL
+    assert fr.lib.fr_region_state(None) == fr.FR_E_NULL
+    del r
