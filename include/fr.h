@@ -347,6 +347,43 @@ int fr_attn_decode(const void* q, const void* k, const void* v, void* o, float* 
 int fr_stream_copy(const void* x, void* y, int64_t nbytes, void* stream);
 int fr_stream_read(const void* x, int64_t nbytes, uint32_t* sink, void* stream);
 
+/* ------------------------------------------------------------ configuration search
+ * "Stax (4)", 9.6: choosing a launch configuration is black-box optimisation
+ * over a configuration space Pi = A_1 x ... x A_p of finite integer value
+ * sets (Definition 9.2), with a measured cost t (+infinity, or any negative
+ * or NaN value, for a configuration that cannot run). Host code only.
+ *  values[i][0 .. counts[i]) is A_i; p <= FR_TUNE_MAX_PARAMS.
+ *  cost(ctx, config, p) returns t for one configuration (config[i] a value
+ *  of A_i). Each configuration is evaluated at most once per search.
+ * fr_tune_coordinate_descent (Algorithm 9.2): starting from `config` (which
+ * must lie in Pi with finite cost), for each parameter try twice and half
+ * its value when in A_i, accept when t(c') < (1 - eps) t(c), repeat until a
+ * round accepts nothing; writes the final configuration to `config`.
+ * Returns FR_E_ARG for a bad space, start or eps (0 < eps < 1).
+ * fr_tune_random_search (Proposition 9.3): `draws` independent uniform
+ * configurations (splitmix64 stream from `seed`); the fastest is written to
+ * `best`. FR_E_ARG if every draw is infinite.
+ * fr_tune_random_draws(q, delta): the N = ceil(ln(1/delta) / q) draws after
+ * which the best lies in the fastest q-fraction with probability >= 1 - delta.
+ * fr_tune_threshold(eta_max): an eps above 2 eta / (1 + eta) (and >= 1e-3),
+ * so that under relative timing noise |eta| <= eta_max every accepted step
+ * of the descent is a real improvement (the remark after Proposition 9.2);
+ * -1 for eta_max outside [0, 1). */
+#define FR_TUNE_MAX_PARAMS 16
+typedef double (*fr_tune_cost_fn)(void* ctx, const int32_t* config, int p);
+typedef struct fr_tune_result {
+    double cost;          /* t of the configuration returned */
+    int64_t evaluations;  /* distinct configurations evaluated */
+    int64_t accepted;     /* accepted moves (coordinate descent) */
+    int64_t rounds;       /* rounds of the outer loop, or draws */
+} fr_tune_result;
+int fr_tune_coordinate_descent(const int32_t* const* values, const int32_t* counts, int p, int32_t* config,
+                               double eps, fr_tune_cost_fn cost, void* ctx, fr_tune_result* out);
+int fr_tune_random_search(const int32_t* const* values, const int32_t* counts, int p, int draws, uint64_t seed,
+                          fr_tune_cost_fn cost, void* ctx, int32_t* best, fr_tune_result* out);
+int fr_tune_random_draws(double q, double delta);
+double fr_tune_threshold(double eta_max);
+
 /* ------------------------------------------------------------ recorded regions
  * "Stax (4)", 9.9: a region of n short kernels launched one by one costs
  * about max(n * t_launch, sum t_k); recorded once as a graph and replayed

@@ -44,6 +44,7 @@ EXPORTS = (
     "fr_attn_decode_workspace_bytes", "fr_attn_decode",
     "fr_add_2d", "fr_gelu_backward",
     "fr_region_create", "fr_region_destroy", "fr_region_run", "fr_region_state", "fr_region_counts",
+    "fr_tune_coordinate_descent", "fr_tune_random_search", "fr_tune_random_draws", "fr_tune_threshold",
 )
 
 
@@ -98,6 +99,10 @@ def _load():
         "fr_layernorm_rows_backward": (I32, [P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I64, I64, I64, P, U64,
                                              I32, P]),
         "fr_gelu_backward": (I32, [P, I64, P, P, I64, I32, P]),
+        "fr_tune_coordinate_descent": (I32, [P, P, I32, P, ctypes.c_double, P, P, P]),
+        "fr_tune_random_search": (I32, [P, P, I32, I32, U64, P, P, P, P]),
+        "fr_tune_random_draws": (I32, [ctypes.c_double, ctypes.c_double]),
+        "fr_tune_threshold": (ctypes.c_double, [ctypes.c_double]),
         "fr_region_create": (I32, [ctypes.POINTER(P)]),
         "fr_region_destroy": (None, [P]),
         "fr_region_run": (I32, [P, P, U64, P, P, P]),
@@ -425,3 +430,74 @@ class Region:
         rep, direct = ctypes.c_uint64(), ctypes.c_uint64()
         _check(lib.fr_region_counts(self._r, ctypes.byref(rep), ctypes.byref(direct)), "fr_region_counts")
         return rep.value, direct.value
+
+
+# ------------------------------------------------------------------ configuration search
+
+_TUNE_COST = ctypes.CFUNCTYPE(ctypes.c_double, ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32), ctypes.c_int)
+
+
+class fr_tune_result(ctypes.Structure):
+    _fields_ = [("cost", ctypes.c_double), ("evaluations", ctypes.c_int64), ("accepted", ctypes.c_int64),
+                ("rounds", ctypes.c_int64)]
+
+
+def _space(space):
+    """space: list of value lists -> (values**, counts*, keepalive)."""
+    arrs = [(ctypes.c_int32 * len(v))(*v) for v in space]
+    ptrs = (ctypes.POINTER(ctypes.c_int32) * len(space))(*[ctypes.cast(a, ctypes.POINTER(ctypes.c_int32))
+                                                             for a in arrs])
+    counts = (ctypes.c_int32 * len(space))(*[len(v) for v in space])
+    return ptrs, counts, arrs
+
+
+def _cost_cb(cost):
+    err = []
+
+    def cb(_ctx, cfg, p):
+        try:
+            t = float(cost(tuple(cfg[i] for i in range(p))))
+            return t if math.isfinite(t) else math.inf
+        except Exception as e:  # noqa: BLE001  (re-raised after the C call)
+            err.append(e)
+            return math.inf
+    return _TUNE_COST(cb), err
+
+
+def fr_tune_coordinate_descent(space, start, eps, cost):
+    """Algorithm 9.2 over `space` (a list of value lists) from `start`; cost
+    maps a configuration tuple to a time (math.inf if it cannot run).
+    Returns (configuration, fr_tune_result)."""
+    ptrs, counts, keep = _space(space)
+    cfg = (ctypes.c_int32 * len(space))(*start)
+    cb, err = _cost_cb(cost)
+    res = fr_tune_result()
+    st = lib.fr_tune_coordinate_descent(ptrs, counts, len(space), cfg, float(eps), cb, None, ctypes.byref(res))
+    if err:
+        raise err[-1]
+    _check(st, "fr_tune_coordinate_descent")
+    return tuple(cfg), res
+
+
+def fr_tune_random_search(space, draws, seed, cost):
+    """Proposition 9.3's random search: the best of `draws` uniform draws."""
+    ptrs, counts, keep = _space(space)
+    best = (ctypes.c_int32 * len(space))()
+    cb, err = _cost_cb(cost)
+    res = fr_tune_result()
+    st = lib.fr_tune_random_search(ptrs, counts, len(space), int(draws), int(seed), cb, None, best,
+                                   ctypes.byref(res))
+    if err:
+        raise err[-1]
+    _check(st, "fr_tune_random_search")
+    return tuple(best), res
+
+
+def fr_tune_random_draws(q, delta):
+    n = lib.fr_tune_random_draws(float(q), float(delta))
+    _check(min(n, 0), "fr_tune_random_draws")
+    return n
+
+
+def fr_tune_threshold(eta_max):
+    return lib.fr_tune_threshold(float(eta_max))
