@@ -136,6 +136,20 @@ int fr_force_form(int form);
  * plan = NULL clears the override. Not thread-safe. */
 int fr_tune_override(int op, const fr_plan* plan);
 
+/* Recorded selections ("Stax (4)", 9.6, Algorithm 9.1: measure once, keep
+ * the winner): later calls of `op` with exactly these rows, cols and dtype
+ * use the knobs of `plan` (as fr_tune_override does, but for this shape
+ * only; a process-wide override still wins). For FR_OP_SUMSQ full
+ * reductions and FR_OP_GELU_BWD, rows = 1 and cols = n. plan = NULL removes
+ * the record. A record that cannot serve a call makes it return FR_E_ARG, or
+ * FR_E_WORKSPACE if its split needs more workspace than the call passes (the
+ * tuner only records configurations measured with the workspace the query
+ * functions report). fr_tune_lookup returns FR_E_ARG when there is no
+ * record. Thread-safe. */
+int fr_tune_record(int op, int64_t rows, int64_t cols, int dtype, const fr_plan* plan);
+int fr_tune_lookup(int op, int64_t rows, int64_t cols, int dtype, fr_plan* plan);
+void fr_tune_clear(void);
+
 /* ------------------------------------------------------------ Example 1.1
  * out[i] = sum_j 2 * relu(a[i,j] + b[i,j])   ("Stax (4)", 9.2, Listing 9.1,
  * the kernel of Example 1.1; 10.2, Example 10.1 with a runtime row count).

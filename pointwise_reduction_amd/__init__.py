@@ -45,6 +45,7 @@ EXPORTS = (
     "fr_add_2d", "fr_gelu_backward",
     "fr_region_create", "fr_region_destroy", "fr_region_run", "fr_region_state", "fr_region_counts",
     "fr_tune_coordinate_descent", "fr_tune_random_search", "fr_tune_random_draws", "fr_tune_threshold",
+    "fr_tune_record", "fr_tune_lookup", "fr_tune_clear",
 )
 
 
@@ -102,6 +103,9 @@ def _load():
         "fr_tune_coordinate_descent": (I32, [P, P, I32, P, ctypes.c_double, P, P, P]),
         "fr_tune_random_search": (I32, [P, P, I32, I32, U64, P, P, P, P]),
         "fr_tune_random_draws": (I32, [ctypes.c_double, ctypes.c_double]),
+        "fr_tune_record": (I32, [I32, I64, I64, I32, ctypes.POINTER(fr_plan)]),
+        "fr_tune_lookup": (I32, [I32, I64, I64, I32, ctypes.POINTER(fr_plan)]),
+        "fr_tune_clear": (None, []),
         "fr_tune_threshold": (ctypes.c_double, [ctypes.c_double]),
         "fr_region_create": (I32, [ctypes.POINTER(P)]),
         "fr_region_destroy": (None, [P]),
@@ -497,6 +501,28 @@ def fr_tune_random_draws(q, delta):
     n = lib.fr_tune_random_draws(float(q), float(delta))
     _check(min(n, 0), "fr_tune_random_draws")
     return n
+
+
+def fr_tune_record(op, rows, cols, dtype=FR_F32, plan=None, **knobs):
+    """Record the configuration for calls of `op` at exactly (rows, cols,
+    dtype); plan=None and no knobs removes the record."""
+    if plan is None and knobs:
+        plan = fr_plan()
+        for k, v in knobs.items():
+            setattr(plan, k, v)
+    _check(lib.fr_tune_record(op, rows, cols, dtype, None if plan is None else ctypes.byref(plan)),
+           "fr_tune_record")
+
+
+def fr_tune_lookup(op, rows, cols, dtype=FR_F32):
+    """The recorded configuration for this shape, or None."""
+    plan = fr_plan()
+    st = lib.fr_tune_lookup(op, rows, cols, dtype, ctypes.byref(plan))
+    return plan if st == FR_OK else None
+
+
+def fr_tune_clear():
+    lib.fr_tune_clear()
 
 
 def fr_tune_threshold(eta_max):

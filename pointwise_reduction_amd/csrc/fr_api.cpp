@@ -12,6 +12,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <map>
 #include <mutex>
 
 #include "fr.h"
@@ -33,7 +34,34 @@ constexpr int kOps = 9;
 fr_plan g_override[kOps];
 bool g_has_override[kOps] = {};
 
-const fr_plan* override_for(int op) { return (op > 0 && op < kOps && g_has_override[op]) ? &g_override[op] : nullptr; }
+// Recorded selections ("Stax (4)", 9.6, Algorithm 9.1, lines 1 and 7): the
+// configuration a tuner measured best for one (operation, shape, dtype).
+struct RecordKey {
+    int op;
+    int64_t rows, cols;
+    int dtype;
+    bool operator<(const RecordKey& o) const {
+        if (op != o.op) return op < o.op;
+        if (rows != o.rows) return rows < o.rows;
+        if (cols != o.cols) return cols < o.cols;
+        return dtype < o.dtype;
+    }
+};
+std::map<RecordKey, fr_plan> g_records;
+std::mutex g_records_mu;
+thread_local fr_plan t_record;  // the record in use by this thread's current call
+
+// A process-wide override (tuning) wins; then a recorded selection for this
+// exact shape; else the planner's defaults.
+const fr_plan* override_for(int op, int64_t rows, int64_t cols, int dtype) {
+    if (op > 0 && op < kOps && g_has_override[op]) return &g_override[op];
+    std::lock_guard<std::mutex> lk(g_records_mu);
+    if (g_records.empty()) return nullptr;
+    auto it = g_records.find(RecordKey{op, rows, cols, dtype});
+    if (it == g_records.end()) return nullptr;
+    t_record = it->second;
+    return &t_record;
+}
 
 constexpr int kMaxDevices = 64;
 struct DeviceInfo {
@@ -111,7 +139,8 @@ int run_sum(int prologue, const void* a, const void* b, void* out, int64_t rows,
     const int v16 = vec_ok(a, a_rs, 4) && vec_ok(b, b_rs, 4);
     fr_plan plan;
     const int op = prologue == kReluAdd ? FR_OP_SUM_RELU_ADD : FR_OP_SUMSQ;
-    st = make_plan(op, rows, cols, FR_F32, num_cus, 0, ws ? ws_bytes : 0, v16, g_forced_form, override_for(op), &plan);
+    st = make_plan(op, rows, cols, FR_F32, num_cus, 0, ws ? ws_bytes : 0, v16, g_forced_form,
+                   override_for(op, rows, cols, FR_F32), &plan);
     if (st != FR_OK) return st;
     SumArgs args{prologue, (const float*)a, (const float*)b, (float*)out, (int)rows, (int)cols, a_rs, b_rs, out_s,
                  (float*)ws};
@@ -160,9 +189,10 @@ int fr_plan_query(int op, int64_t rows, int64_t cols, int dtype, int num_cus, in
                   int aligned16, fr_plan* plan) {
     if (!plan) return FR_E_NULL;
     if (op == FR_OP_ADD_2D || op == FR_OP_GELU_BWD)
-        return make_pointwise_plan(op, rows, cols, dtype, num_cus, aligned16, g_forced_form, override_for(op), plan);
+        return make_pointwise_plan(op, rows, cols, dtype, num_cus, aligned16, g_forced_form,
+                                   override_for(op, rows, cols, dtype), plan);
     return make_plan(op, rows, cols, dtype, num_cus, has_lengths, ws_bytes, aligned16, g_forced_form,
-                     override_for(op), plan);
+                     override_for(op, rows, cols, dtype), plan);
 }
 
 int fr_tune_override(int op, const fr_plan* plan) {
@@ -174,6 +204,30 @@ int fr_tune_override(int op, const fr_plan* plan) {
         g_has_override[op] = false;
     }
     return FR_OK;
+}
+
+int fr_tune_record(int op, int64_t rows, int64_t cols, int dtype, const fr_plan* plan) {
+    if (op <= 0 || op >= kOps) return FR_E_ARG;
+    if (rows < 0 || cols < 0) return FR_E_SIZE;
+    std::lock_guard<std::mutex> lk(g_records_mu);
+    const RecordKey key{op, rows, cols, dtype};
+    if (plan) g_records[key] = *plan;
+    else g_records.erase(key);
+    return FR_OK;
+}
+
+int fr_tune_lookup(int op, int64_t rows, int64_t cols, int dtype, fr_plan* plan) {
+    if (!plan) return FR_E_NULL;
+    std::lock_guard<std::mutex> lk(g_records_mu);
+    auto it = g_records.find(RecordKey{op, rows, cols, dtype});
+    if (it == g_records.end()) return FR_E_ARG;
+    *plan = it->second;
+    return FR_OK;
+}
+
+void fr_tune_clear(void) {
+    std::lock_guard<std::mutex> lk(g_records_mu);
+    g_records.clear();
 }
 
 uint64_t fr_sum_workspace_bytes(int64_t rows, int64_t cols, int dtype) {
@@ -235,7 +289,7 @@ int fr_sumsq_full(const void* x, int64_t n, void* out, void* ws, uint64_t ws_byt
     // not fit one persistent row (the form is not left to the row heuristics).
     const int form = need > 0 ? FR_FORM_SPLIT : FR_FORM_PER;
     st = make_plan(FR_OP_SUMSQ, 1, n, FR_F32, num_cus, 0, need > 0 ? ws_bytes : 0, v16, form,
-                   override_for(FR_OP_SUMSQ), &plan);
+                   override_for(FR_OP_SUMSQ, 1, n, FR_F32), &plan);
     if (st != FR_OK) return st;
     SumArgs args{kSquare, (const float*)x, nullptr, (float*)out, 1, (int)n, n, 0, 1, (float*)ws};
     (void)hipGetLastError();
@@ -269,7 +323,7 @@ int fr_softmax_rows(const void* x, void* y, int64_t rows, int64_t cols, int64_t 
     const int v16 = vec_ok(x, x_rs, 4) && vec_ok(y, y_rs, 4);
     fr_plan plan;
     st = make_plan(FR_OP_SOFTMAX, rows, cols, FR_F32, num_cus, lengths != nullptr, ws ? ws_bytes : 0, v16,
-                   g_forced_form, override_for(FR_OP_SOFTMAX), &plan);
+                   g_forced_form, override_for(FR_OP_SOFTMAX, rows, cols, FR_F32), &plan);
     if (st != FR_OK) return st;
     const int64_t wait_ticks = plan.wait_us > 0 ? (int64_t)plan.wait_us * clock_khz / 1000 : (plan.wait_us < 0 ? -1 : 0);
     SoftmaxArgs args{(const float*)x, (float*)y, (int)rows, (int)cols, x_rs, y_rs, lengths, argmax, ws, wait_ticks};
@@ -303,7 +357,7 @@ int fr_layernorm_rows_stats(const void* x, const void* gamma, const void* beta, 
                     vec_ok(beta, 0, 8);
     fr_plan plan;
     st = make_plan(FR_OP_LAYERNORM, rows, cols, FR_BF16, num_cus, 0, 0, v16, g_forced_form,
-                   override_for(FR_OP_LAYERNORM), &plan);
+                   override_for(FR_OP_LAYERNORM, rows, cols, FR_BF16), &plan);
     if (st != FR_OK) return st;
     LayerNormArgs args{(const uint16_t*)x, (const uint16_t*)gamma, (const uint16_t*)beta, (uint16_t*)y,
                        (int)rows, (int)cols, x_rs, y_rs, eps, mean, rstd};
@@ -316,7 +370,7 @@ uint64_t fr_layernorm_rows_backward_workspace_bytes(int64_t rows, int64_t cols, 
     fr_plan plan;
     // the workspace does not depend on alignment or the device
     if (make_plan(FR_OP_LAYERNORM_BWD, rows, cols, FR_BF16, 256, 0, 0, 1, FR_FORM_AUTO,
-                  override_for(FR_OP_LAYERNORM_BWD), &plan) != FR_OK)
+                  override_for(FR_OP_LAYERNORM_BWD, rows, cols, FR_BF16), &plan) != FR_OK)
         return 0;
     return plan.ws_bytes;
 }
@@ -345,7 +399,7 @@ int fr_layernorm_rows_backward(const void* x, const void* dy, const void* gamma,
                     vec_ok(gamma, 0, 8);
     fr_plan plan;
     st = make_plan(FR_OP_LAYERNORM_BWD, rows, cols, FR_BF16, 256, 0, 0, v16, g_forced_form,
-                   override_for(FR_OP_LAYERNORM_BWD), &plan);
+                   override_for(FR_OP_LAYERNORM_BWD, rows, cols, FR_BF16), &plan);
     if (st != FR_OK) return st;
     const bool dg = dgamma || dbeta;
     if (dg && plan.ws_bytes > 0 && (!ws || ws_bytes < plan.ws_bytes)) return FR_E_WORKSPACE;
@@ -378,7 +432,7 @@ int fr_softmax_rows_backward(const void* y, const void* dy, void* dx, int64_t ro
     const int v16 = vec_ok(y, y_rs, 4) && vec_ok(dy, dy_rs, 4) && vec_ok(dx, dx_rs, 4);
     fr_plan plan;
     st = make_plan(FR_OP_SOFTMAX_BWD, rows, cols, FR_F32, num_cus, lengths != nullptr, 0, v16, g_forced_form,
-                   override_for(FR_OP_SOFTMAX_BWD), &plan);
+                   override_for(FR_OP_SOFTMAX_BWD, rows, cols, FR_F32), &plan);
     if (st != FR_OK) return st;
     SoftmaxBwdArgs args{(const float*)y, (const float*)dy, (float*)dx, (int)rows, (int)cols, y_rs, dy_rs, dx_rs,
                         lengths};
@@ -464,7 +518,7 @@ int fr_add_2d(const void* a, int64_t a_rs, int64_t a_cs, const void* b, int64_t 
                     (lb ? b_cs : b_rs) % 4 == 0 && out_rs % 4 == 0;
     fr_plan plan;
     st = make_pointwise_plan(FR_OP_ADD_2D, rows, cols, FR_F32, num_cus, v16, g_forced_form,
-                             override_for(FR_OP_ADD_2D), &plan);
+                             override_for(FR_OP_ADD_2D, rows, cols, FR_F32), &plan);
     if (st != FR_OK) return st;
     Add2dArgs args{(const float*)a, (const float*)b, (float*)out, rows, cols, a_rs, a_cs, b_rs, b_cs, out_rs,
                    la == 1, lb == 1};
@@ -487,7 +541,7 @@ int fr_gelu_backward(const void* dy, int64_t dy_stride, const void* h, void* dx,
     const int v16 = aligned(h, 16) && aligned(dx, 16) && (dy_stride == 0 || aligned(dy, 16));
     fr_plan plan;
     const int st = make_pointwise_plan(FR_OP_GELU_BWD, 1, n, dtype, num_cus, v16, g_forced_form,
-                                       override_for(FR_OP_GELU_BWD), &plan);
+                                       override_for(FR_OP_GELU_BWD, 1, n, dtype), &plan);
     if (st != FR_OK) return st;
     GeluBwdArgs args{dy, h, dx, n, dy_stride == 0, dtype == FR_BF16};
     (void)hipGetLastError();

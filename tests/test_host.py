@@ -202,12 +202,12 @@ def test_plans_for_the_five_workloads():
     # LayerNorm 2048 x 32768 bf16: a 512-thread workgroup holds each row
     p = fr.fr_plan_query(fr.FR_OP_LAYERNORM, 2048, 32768, dtype=fr.FR_BF16)
     assert (p.form, p.threads, p.vec, p.grid) == (fr.FR_FORM_PER, 512, 8, 2048)
-    # sum of squares over 2^28: 2048 chunks of 2^17 plus a finishing pass
+    # sum of squares over 2^28: 512 chunks of 2^19 plus a finishing pass
     n = 1 << 28
     ws = fr.fr_sumsq_full_workspace_bytes(n)
-    assert ws == 2048 * 4
+    assert ws == 512 * 4
     p = fr.fr_plan_query(fr.FR_OP_SUMSQ, 1, n, ws_bytes=ws)
-    assert (p.form, p.splits, p.chunk, p.grid, p.grid2) == (fr.FR_FORM_SPLIT, 2048, 1 << 17, 2048, 1)
+    assert (p.form, p.splits, p.chunk, p.grid, p.grid2) == (fr.FR_FORM_SPLIT, 512, 1 << 19, 512, 1)
     # ragged softmax, 512 rows of capacity 131072, with a workspace: 16 chunks of 8192, a
     # 64-byte header and 512 x 16 partial slots of 16 bytes; one kernel whose grid is every
     # workgroup that can be resident at once (5 per CU at 256 threads), waiting 200 us by default

@@ -138,3 +138,66 @@ def test_search_argument_errors():
         fr.fr_tune_random_search(SPACE, 10, 1, lambda c: math.inf)
     with pytest.raises(ZeroDivisionError):
         fr.fr_tune_random_search(SPACE, 10, 1, lambda c: 1 / 0)
+
+
+def test_records_are_used_by_the_planner_for_that_shape_only():
+    fr.fr_tune_clear()
+    try:
+        base = fr.fr_plan_query(fr.FR_OP_SOFTMAX, 4096, 1024)
+        assert fr.fr_tune_lookup(fr.FR_OP_SOFTMAX, 4096, 1024) is None
+        fr.fr_tune_record(fr.FR_OP_SOFTMAX, 4096, 1024, fr.FR_F32, form=fr.FR_FORM_PER, threads=256, seg=32,
+                          vec=8, rows_per_wg=16)
+        p = fr.fr_plan_query(fr.FR_OP_SOFTMAX, 4096, 1024)
+        assert (p.seg, p.vec, p.rows_per_wg) == (32, 8, 16) != (base.seg, base.vec, base.rows_per_wg)
+        other = fr.fr_plan_query(fr.FR_OP_SOFTMAX, 4096, 1000)  # another shape: defaults
+        assert (other.seg, other.vec) == (base.seg, base.vec)
+        assert fr.fr_tune_lookup(fr.FR_OP_SOFTMAX, 4096, 1024).seg == 32
+        fr.fr_tune_record(fr.FR_OP_SOFTMAX, 4096, 1024, fr.FR_F32)  # remove
+        assert fr.fr_plan_query(fr.FR_OP_SOFTMAX, 4096, 1024).seg == base.seg
+    finally:
+        fr.fr_tune_clear()
+
+
+def test_cache_records_only_entries_of_the_current_sources(tmp_path):
+    import json
+
+    from pointwise_reduction_amd import tune
+    fr.fr_tune_clear()
+    src = tune.source_hash()
+    knobs = dict(form=fr.FR_FORM_POINTWISE, threads=256, rows_per_wg=32, chunk=128, grid=0)
+    key = [fr.FR_OP_ADD_2D, 1024, 2048, fr.FR_F32]
+    cache = {tune._cache_key(src, key, []): {"key": key, "knobs": knobs, "ms_per_step": 0.1},
+             tune._cache_key("0" * 64, key[:2] + [4096, 0], []): {"key": key[:2] + [4096, 0], "knobs": knobs,
+                                                               "ms_per_step": 0.1}}
+    path = tmp_path / "cache.json"
+    path.write_text(json.dumps(cache))
+    try:
+        assert tune.load_cache(str(path)) == 1
+        p = fr.fr_plan_query(fr.FR_OP_ADD_2D, 1024, 2048)
+        assert (p.rows_per_wg, p.chunk) == (32, 128)
+        assert fr.fr_tune_lookup(fr.FR_OP_ADD_2D, 1024, 4096) is None  # stale sources: not recorded
+    finally:
+        fr.fr_tune_clear()
+
+
+def test_every_search_space_holds_the_planner_default():
+    # the planner's measured default for each workload's shape is a point of
+    # that workload's configuration space (so the search can only improve on it)
+    from pointwise_reduction_amd import tune
+    for name in ("softmax", "softmax_bwd", "sum_relu_add", "layernorm", "add_2d", "gelu_bwd", "sumsq"):
+        (op, rows, cols, dtype), names, sets, knobs_of, config_of = tune.search_space(name)
+        if name == "sumsq":  # a full reduction always takes the split form
+            prev = fr.fr_force_form(fr.FR_FORM_SPLIT)
+            try:
+                p = fr.fr_plan_query(op, rows, cols, dtype=dtype, ws_bytes=1 << 30)
+            finally:
+                fr.fr_force_form(prev)
+        else:
+            p = fr.fr_plan_query(op, rows, cols, dtype=dtype)
+        kn = {k: getattr(p, k) for k in ("form", "threads", "seg", "vec", "rows_per_wg", "chunk", "grid")}
+        if name == "add_2d":
+            kn["grid"] = 0
+        if name == "gelu_bwd":
+            kn["grid"] = 0
+        cfg = config_of(kn)
+        assert cfg is not None and all(v in s for v, s in zip(cfg, sets)), (name, kn, cfg)
