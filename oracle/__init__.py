@@ -56,6 +56,7 @@ def _load():
         "orc_attn_decode": (None, [P, P, P, I64, I64, I64, I64, I64, P, F64, P, P, P, P, P]),
         "orc_attn_merge": (None, [F64, F64, P, F64, F64, P, I64, P, P, P]),
         "orc_add_2d": (None, [P, I64, I64, P, I64, I64, P, I64, I64, I64]),
+        "orc_attn_fwd": (None, [P, P, P, I64, I64, I64, I64, I64, I64, I32, F64, P, P, P, P, P]),
         "orc_round_bf16": (None, [P, I64, P]),
         "orc_layernorm_stats": (None, [P, I64, I64, I64, F64, P, P]),
         "orc_layernorm_backward_rows": (None, [P, P, P, P, P, I64, I64, I64, I64, P, P, P, P, P, P]),
@@ -215,6 +216,30 @@ def attn_decode(q, k, v, lengths=None, scale=None):
     scratch = np.empty(max(S, 1))
     _load().orc_attn_decode(_p(q), _p(k), _p(v), B, Hq, Hkv, S, D, _p(L), float(scale), _p(scratch), _p(o), _p(lse),
                             _p(mag), _p(smag))
+    return o, lse, mag, smag
+
+
+def attn_fwd(q, k, v, causal=False, scale=None):
+    """Attention of blocks of query rows ([Stax4] 9.10) in fp64.
+
+    q: [B, Hq, Nq, D]; k, v: [B, Hkv, Nk, D] (any float dtype; bf16 callers
+    pass decoded values). Returns (o64 [B, Hq, Nq, D], lse [B, Hq, Nq],
+    mag [B, Hq, Nq, D], smag [B, Hq, Nq]) as defined at orc_attn_fwd."""
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    k = np.ascontiguousarray(k, dtype=np.float64)
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    B, Hq, Nq, D = q.shape
+    Bk, Hkv, Nk, Dk = k.shape
+    assert (Bk, Dk) == (B, D) and v.shape == k.shape and Hq % Hkv == 0
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    o = np.empty((B, Hq, Nq, D))
+    lse = np.empty((B, Hq, Nq))
+    mag = np.empty((B, Hq, Nq, D))
+    smag = np.empty((B, Hq, Nq))
+    scratch = np.empty(max(Nk, 1))
+    _load().orc_attn_fwd(_p(q), _p(k), _p(v), B, Hq, Hkv, Nq, Nk, D, int(bool(causal)), float(scale), _p(scratch),
+                         _p(o), _p(lse), _p(mag), _p(smag))
     return o, lse, mag, smag
 
 

@@ -335,6 +335,81 @@ void orc_attn_merge(double m1, double l1, const double* a1, double m2, double l2
     for (int64_t d = 0; d < D; ++d) a[d] = a1[d] * f1 + a2[d] * f2;
 }
 
+/* ------------------------------------------------------ attention, many query rows */
+
+/*
+ * Attention of a block of query rows ([Stax4] 9.10: S = Q K^T scaled,
+ * P = softmax(S) by rows, O = P V, LSE = m + log l kept for the backward
+ * pass; the causal mask of Listing 9.7 lets query i see key j when i >= j).
+ * Each query row is the plain definition, as in orc_attn_decode: scores
+ * over the keys it may see, their maximum, exponentials, sum, weighted sum
+ * of values, one division; fp64 throughout.
+ * Readings: heads as in orc_attn_decode (query head h reads key-value head
+ * h / (Hq / Hkv)); the causal rule compares the query's and the key's
+ * positions from the start of the sequence (so with Nq < Nk the last keys
+ * are seen by no query); a row that sees no key gives o = 0, lse = -inf.
+ * Layouts (row-major, contiguous): q, o64, mag [B, Hq, Nq, D]; k, v [B, Hkv,
+ * Nk, D]; lse, smag [B, Hq, Nq]. mag: sum_j p_j |v_jd|; smag: max_j sum_d
+ * |scale q_d k_jd| (the sizes of the terms, for tolerances).
+ */
+void orc_attn_fwd(const double* q, const double* k, const double* v, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq,
+                  int64_t Nk, int64_t D, int causal, double scale, double* s_scratch, double* o64, double* lse,
+                  double* mag, double* smag) {
+    const int64_t G = Hq / Hkv;
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t h = 0; h < Hq; ++h) {
+            const double* kh = k + (b * Hkv + h / G) * Nk * D;
+            const double* vh = v + (b * Hkv + h / G) * Nk * D;
+            for (int64_t i = 0; i < Nq; ++i) {
+                const int64_t row = (b * Hq + h) * Nq + i;
+                const double* qr = q + row * D;
+                double* orow = o64 + row * D;
+                double* mrow = mag ? mag + row * D : 0;
+                const int64_t L = causal ? (i + 1 < Nk ? i + 1 : Nk) : Nk;
+                for (int64_t d = 0; d < D; ++d) {
+                    orow[d] = 0.0;
+                    if (mrow) mrow[d] = 0.0;
+                }
+                double m = -INFINITY, sm = 0.0;
+                int nan = 0;
+                for (int64_t j = 0; j < L; ++j) {
+                    double s = 0.0, t = 0.0;
+                    for (int64_t d = 0; d < D; ++d) {
+                        s += qr[d] * kh[j * D + d];
+                        t += fabs(scale * qr[d] * kh[j * D + d]);
+                    }
+                    s *= scale;
+                    s_scratch[j] = s;
+                    if (isnan(s)) nan = 1;
+                    if (s > m) m = s;
+                    if (t > sm) sm = t;
+                }
+                if (smag) smag[row] = sm;
+                if (L == 0) {
+                    lse[row] = -INFINITY;
+                    continue;
+                }
+                if (nan) m = NAN;
+                double l = 0.0;
+                for (int64_t j = 0; j < L; ++j) {
+                    const double e = exp(s_scratch[j] - m);
+                    s_scratch[j] = e;
+                    l += e;
+                }
+                for (int64_t j = 0; j < L; ++j)
+                    for (int64_t d = 0; d < D; ++d) {
+                        orow[d] += s_scratch[j] * vh[j * D + d];
+                        if (mrow) mrow[d] += s_scratch[j] * fabs(vh[j * D + d]);
+                    }
+                for (int64_t d = 0; d < D; ++d) {
+                    orow[d] /= l;
+                    if (mrow) mrow[d] /= l;
+                }
+                lse[row] = m + log(l);
+            }
+        }
+}
+
 /* ------------------------------------------------------ LayerNorm (C3) */
 
 /*

@@ -667,3 +667,69 @@ def test_layernorm_backward_invariants():
     xh = (x - mean[:, None]) * rstd[:, None]
     assert np.allclose(dx.sum(axis=1), 0.0, atol=1e-12)
     assert np.allclose((dx * xh).sum(axis=1), 0.0, atol=1e-12)
+
+
+# ------------------------------------------------------ attention, many query rows
+
+
+def test_attn_fwd_worked_example(golden):
+    """[HG12] 12.1 as a block of one query row: o = [2.6456, 0.9278]."""
+    g = golden("hello_gpu_ch12_worked_example.txt")
+    q = np.array([[[[1.0, 0.0]]]])
+    k = np.array([[[[s, 0.0] for s in g["scores"]]]])
+    v = np.array([[g["values"]]])
+    o, lse, _, _ = oracle.attn_fwd(q, k, v, scale=1.0)
+    assert np.allclose(o[0, 0, 0], g["output"], atol=g["tolerance"])
+    assert lse[0, 0, 0] == pytest.approx(4 + np.log(g["exp_sum"]), abs=g["tolerance"])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("nq,nk", [(7, 7), (5, 9), (9, 5)])
+def test_attn_fwd_matches_a_matrix_statement(causal, nq, nk):
+    """softmax(scale Q K^T + mask) V with scipy's softmax and logsumexp and
+    numpy's matmul, grouped heads by repetition: an independent statement."""
+    rng = np.random.default_rng(nq * 10 + nk + causal)
+    B, Hq, Hkv, D = 2, 4, 2, 6
+    q = rng.normal(size=(B, Hq, nq, D))
+    k = rng.normal(size=(B, Hkv, nk, D))
+    v = rng.normal(size=(B, Hkv, nk, D))
+    scale = 0.37
+    o, lse, mag, smag = oracle.attn_fwd(q, k, v, causal=causal, scale=scale)
+    kr, vr = np.repeat(k, Hq // Hkv, axis=1), np.repeat(v, Hq // Hkv, axis=1)
+    s = scale * (q @ kr.transpose(0, 1, 3, 2))
+    if causal:
+        s = np.where(np.arange(nk)[None, :] <= np.arange(nq)[:, None], s, -np.inf)
+    p = scipy.special.softmax(s, axis=-1)
+    assert np.allclose(o, p @ vr, rtol=1e-12, atol=1e-13)
+    assert np.allclose(lse, scipy.special.logsumexp(s, axis=-1), rtol=1e-13, atol=1e-13)
+    assert np.allclose(mag, p @ np.abs(vr), rtol=1e-12, atol=1e-13)
+    assert np.all(mag >= np.abs(o) - 1e-12)
+
+
+def test_attn_fwd_rows_are_decode_rows():
+    # a causal row i is the decode query over the first i + 1 keys
+    rng = np.random.default_rng(7)
+    q = rng.normal(size=(1, 2, 6, 4))
+    k = rng.normal(size=(1, 1, 6, 4))
+    v = rng.normal(size=(1, 1, 6, 4))
+    o, lse, _, _ = oracle.attn_fwd(q, k, v, causal=True)
+    for i in range(6):
+        od, ld, _, _ = oracle.attn_decode(q[:, :, i], k, v, lengths=np.array([i + 1], np.int32))
+        assert np.allclose(o[:, :, i], od, rtol=1e-14, atol=1e-15) and np.allclose(lse[:, :, i], ld, rtol=1e-14)
+
+
+def test_attn_fwd_key_permutation_and_shift():
+    # without the mask the keys form a set: permuting keys and values together
+    # changes nothing; adding scale-invisible u to every key shifts lse only
+    rng = np.random.default_rng(8)
+    q = rng.normal(size=(1, 1, 5, 3))
+    k = rng.normal(size=(1, 1, 8, 3))
+    v = rng.normal(size=(1, 1, 8, 3))
+    o, lse, _, _ = oracle.attn_fwd(q, k, v)
+    perm = rng.permutation(8)
+    o2, lse2, _, _ = oracle.attn_fwd(q, k[:, :, perm], v[:, :, perm])
+    assert np.allclose(o, o2, rtol=1e-13, atol=1e-14) and np.allclose(lse, lse2, rtol=1e-14)
+    u = rng.normal(size=3)
+    o3, lse3, _, _ = oracle.attn_fwd(q, k + u, v)
+    assert np.allclose(o, o3, rtol=1e-12, atol=1e-13)
+    assert np.allclose(lse3, lse + (q[0, 0] @ u) / np.sqrt(3), rtol=1e-12)
