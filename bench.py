@@ -34,6 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+PEAK_MFMA_BF16_TFS = 2500.0  # MI355X dense bf16 matrix-core peak
 METRIC = "effective HBM GB/s and % of MI355X peak for fused reductions (softmax 4096x1024)"
 ROTATE_BYTES = 1 << 30
 
@@ -514,6 +515,54 @@ def make_workload(name, torch, fr, synth):
 
         return W(), per_set
 
+    if name in ("attn_block", "attn_block_full"):
+        # tiled attention ("Stax (4)", 9.10) at the pages' N = 4096, d = 128
+        # (Listing 9.7: causal; attn_block_full: no mask): 4 x 16 heads bf16
+        B, H, N, D = 4, 16, 4096, 128
+        causal = name == "attn_block"
+        q_h, k_h, v_h = synth.attn_block_inputs(B, H, H, N, N, D, seed=7001)
+        per_set = 4 * B * H * N * D * 2
+        pairs = N * (N + 1) // 2 if causal else N * N
+
+        def bf(bits):
+            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+        class W(Workload):
+            kernel = "fr_attn_block_bf16"
+            bytes = 4 * B * H * N * D * 2 + B * H * N * 4
+            flops = 4 * D * pairs * B * H
+            dtype = "bf16"
+
+            def alloc(self, sets):
+                q0, k0, v0 = bf(q_h), bf(k_h), bf(v_h)
+                self.args = [(q0 if i == 0 else q0.clone(), k0 if i == 0 else k0.clone(),
+                              v0 if i == 0 else v0.clone(), torch.empty_like(q0),
+                              torch.empty((B, H, N), dtype=torch.float32, device=dev)) for i in range(sets)]
+
+            def launch(self, kk):
+                q, k, v, o, lse = self.args[kk]
+                fr.fr_attn_block(q, k, v, o, lse, causal=causal)
+
+            def output(self, kk):
+                return self.args[kk][3]
+
+            def config(self):
+                return {"workload": f"tiled attention, batch 4, 16 heads, N 4096, d 128, bf16, "
+                                    f"{'causal' if causal else 'no mask'}",
+                        "batch": B, "heads": H, "seq": N, "dim": D, "causal": causal, "flops_per_step": self.flops}
+
+            def oracle_fn(self):
+                import oracle
+                r = 2  # query rows of one head, over all keys they see
+                qf = (q_h[:1, :1, -r:].astype(np.uint32) << 16).view(np.float32)
+                kf = (k_h[:1, :1].astype(np.uint32) << 16).view(np.float32)
+                vf = (v_h[:1, :1].astype(np.uint32) << 16).view(np.float32)
+                L = np.array([N], np.int32)
+                return (lambda: [oracle.attn_decode(qf[:, :, i], kf, vf, lengths=L) for i in range(r)],
+                        r * 2 * N * D * 2, f"{r} query rows of one head against all {N} keys")
+
+        return W(), per_set
+
     if name == "attn_decode":
         # decode attention: batch 8, 32 query heads on 8 key-value heads,
         # 8192 keys, head dim 128, bf16 (each key and value byte read once)
@@ -651,7 +700,8 @@ def main():
     ap.add_argument("--workload", default="softmax",
                     choices=["softmax", "sum_relu_add", "layernorm", "sumsq", "ragged", "copy", "stream_copy",
                              "stream_copy_c3", "stream_read", "attn_decode", "softmax_bwd", "add_2d",
-                             "gelu_bwd", "layernorm_bwd", "c1_region"])
+                             "gelu_bwd", "layernorm_bwd", "c1_region", "attn_block",
+                             "attn_block_full"])
     ap.add_argument("--warm", action="store_true", help="one buffer set: reads may hit the MALL")
     ap.add_argument("--eager", action="store_true", help="launch each step from the host (no graph)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -709,6 +759,7 @@ def main():
 
     ms_per_step = ms / K
     gbs = wl.bytes / (ms_per_step * 1e-3) / 1e9
+    flops = getattr(wl, "flops", None)
     cfg = wl.config()
     timing_label = ("eager" if args.eager else
                     ("host loop, one region replay per step" if host_timed else "hip graph of K launches"))
@@ -740,6 +791,13 @@ def main():
             "algorithmic_bytes_per_launch": wl.bytes,
         },
     }
+    if flops:
+        # a contraction: the matrix cores' dense bf16 peak bounds it
+        tfs = flops / (ms_per_step * 1e-3) / 1e12
+        result["value"], result["unit"] = round(tfs, 2), "TFLOP/s"
+        result["roofline"].update({"bound": "mfma", "achieved": round(tfs, 2), "peak": PEAK_MFMA_BF16_TFS,
+                                   "unit": "TFLOP/s", "frac": round(tfs / PEAK_MFMA_BF16_TFS, 4),
+                                   "algorithmic_flops_per_launch": flops, "hbm_GB_per_s": round(gbs, 2)})
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(wl.oracle_fn(), args.cpu_seconds)
     print(json.dumps(result), flush=True)

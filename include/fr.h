@@ -346,6 +346,27 @@ int fr_attn_decode(const void* q, const void* k, const void* v, void* o, float* 
                    int64_t heads_kv, int64_t seq, int64_t dim, const int32_t* lengths, float scale, void* ws,
                    uint64_t ws_bytes, int dtype, void* stream);
 
+/* ------------------------------------------------------------ attention over blocks of query rows
+ * O = softmax(scale * Q K^T [+ causal mask]) V and LSE = m + log l per query
+ * row, the tiled single-pass algorithm of "Stax (4)", 9.10 (Theorem 9.2,
+ * Figure 9.2): one workgroup keeps a block of 128 query rows on chip and
+ * scans K and V in blocks of 64 keys with the online (m, l, a) update; S
+ * and P never reach memory. Both products run on the matrix cores in bf16
+ * with fp32 accumulation; P enters the second product as bf16.
+ *  q, o:   bf16 [batch, heads_q, seq_q, dim]; k, v: bf16 [batch, heads_kv,
+ *          seq_kv, dim]; contiguous, 16-byte aligned. Query head h reads
+ *          key-value head h / (heads_q / heads_kv).
+ *  lse:    fp32 [batch, heads_q, seq_q] (natural log), 4-byte aligned.
+ *  causal: query i sees key j only when i >= j (Listing 9.7's mask_mod);
+ *          key blocks wholly above the diagonal are skipped.
+ *  scale:  finite (commonly 1 / sqrt(dim)).
+ * dim 64 or 128; heads_q a multiple of heads_kv; batch and heads_q <=
+ * 65535; seq lengths < 2^30. A row that sees no key (seq_kv = 0) gives
+ * o = 0 and lse = -inf. dtype must be FR_BF16. */
+int fr_attn_block(const void* q, const void* k, const void* v, void* o, float* lse, int64_t batch, int64_t heads_q,
+                  int64_t heads_kv, int64_t seq_q, int64_t seq_kv, int64_t dim, int causal, float scale, int dtype,
+                  void* stream);
+
 /* ------------------------------------------------------------ streaming references
  * The practical ceiling of an HBM-bound step ("Stax (4)", 9.1: memory-bound
  * kernels are judged by the bandwidth they reach): the plainest kernels that

@@ -42,7 +42,7 @@ EXPORTS = (
     "fr_sumsq_rows", "fr_sumsq_full_workspace_bytes", "fr_sumsq_full",
     "fr_stream_copy", "fr_stream_read",
     "fr_attn_decode_workspace_bytes", "fr_attn_decode",
-    "fr_add_2d", "fr_gelu_backward",
+    "fr_add_2d", "fr_gelu_backward", "fr_attn_block",
     "fr_region_create", "fr_region_destroy", "fr_region_run", "fr_region_state", "fr_region_counts",
     "fr_tune_coordinate_descent", "fr_tune_random_search", "fr_tune_random_draws", "fr_tune_threshold",
     "fr_tune_record", "fr_tune_lookup", "fr_tune_clear",
@@ -93,6 +93,7 @@ def _load():
         "fr_attn_decode_workspace_bytes": (U64, [I64, I64, I64, I64]),
         "fr_attn_decode": (I32, [P, P, P, P, P, I64, I64, I64, I64, I64, P, ctypes.c_float, P, U64, I32, P]),
         "fr_stream_copy": (I32, [P, P, I64, P]),
+        "fr_attn_block": (I32, [P, P, P, P, P, I64, I64, I64, I64, I64, I64, I32, ctypes.c_float, I32, P]),
         "fr_stream_read": (I32, [P, I64, P, P]),
         "fr_add_2d": (I32, [P, I64, I64, P, I64, I64, P, I64, I64, I64, I32, P]),
         "fr_layernorm_rows_stats": (I32, [P, P, P, P, P, P, I64, I64, I64, I64, I64, I64, ctypes.c_float, I32, P]),
@@ -346,6 +347,25 @@ def fr_attn_decode(q, k, v, o, lse=None, lengths=None, scale=None, ws=None, stre
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib.fr_attn_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, S, D, _ptr(lengths),
                               float(scale), _ptr(ws), ws_bytes, _dtype_code(q), _stream(stream)), "fr_attn_decode")
+    return o
+
+
+def fr_attn_block(q, k, v, o, lse, causal=False, scale=None, stream=None):
+    """Tiled attention: q, o [B, Hq, Nq, D]; k, v [B, Hkv, Nk, D] bf16
+    contiguous; lse fp32 [B, Hq, Nq]. scale defaults to 1 / sqrt(D)."""
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape or o.shape != q.shape:
+        raise ValueError("q, o: [B, Hq, Nq, D]; k, v: [B, Hkv, Nk, D]")
+    B, Hq, Nq, D = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if k.shape[0] != B or k.shape[3] != D or tuple(lse.shape) != (B, Hq, Nq):
+        raise ValueError("shape mismatch")
+    for t in (q, k, v, o, lse):
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    _check(lib.fr_attn_block(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, D, int(bool(causal)),
+                             float(scale), _dtype_code(q), _stream(stream)), "fr_attn_block")
     return o
 
 

@@ -472,6 +472,28 @@ int fr_attn_decode(const void* q, const void* k, const void* v, void* o, float* 
     return finish_launch(launch_attn_decode(args, (hipStream_t)stream));
 }
 
+int fr_attn_block(const void* q, const void* k, const void* v, void* o, float* lse, int64_t batch, int64_t heads_q,
+                  int64_t heads_kv, int64_t seq_q, int64_t seq_kv, int64_t dim, int causal, float scale, int dtype,
+                  void* stream) {
+    if (dtype != FR_BF16) return FR_E_DTYPE;
+    if (batch < 0 || heads_q < 0 || heads_kv < 0 || seq_q < 0 || seq_kv < 0) return FR_E_SIZE;
+    if (dim != 64 && dim != 128) return FR_E_SIZE;
+    if (batch > 65535 || heads_q > 65535 || seq_q >= kMaxCols || seq_kv >= kMaxCols) return FR_E_SIZE;
+    if (batch == 0 || heads_q == 0 || seq_q == 0) return FR_OK;
+    if (heads_kv == 0 || heads_q % heads_kv) return FR_E_ARG;
+    if (!isfinite(scale)) return FR_E_ARG;
+    if (!q || !o || !lse || (seq_kv > 0 && (!k || !v))) return FR_E_NULL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+        return FR_E_ALIGN;
+    int num_cus = 0;
+    const int st = device_check(&num_cus);
+    if (st != FR_OK) return st;
+    AttnBlockArgs args{q, k, v, o, lse, (int)batch, (int)heads_q, (int)heads_kv, (int)seq_q, (int)seq_kv, (int)dim,
+                       causal != 0, scale};
+    (void)hipGetLastError();
+    return finish_launch(launch_attn_block(args, (hipStream_t)stream));
+}
+
 int fr_stream_copy(const void* x, void* y, int64_t nbytes, void* stream) {
     if (nbytes < 0 || nbytes % 16) return FR_E_SIZE;
     if (nbytes == 0) return FR_OK;

@@ -1,0 +1,265 @@
+// fr_attn_block.hip - tiled single-pass attention over blocks of query rows
+// ("Stax (4): GPU Codegen and Dynamic Shapes", 9.10: Theorem 9.2's tiled
+// algorithm, Figure 9.2; the (m, l, a) triple updated online; LSE = m +
+// log l kept for the backward pass; the causal mask of Listing 9.7).
+//
+// One workgroup of 4 waves owns a block of 128 query rows of one head (each
+// wave 32 rows) and scans the keys and values in blocks of 64. Both products
+// run on the matrix cores (v_mfma_f32_16x16x32_bf16, lane l: A row l % 16,
+// B column l % 16, k = 8 (l / 16) .. +7; D rows 4 (l / 16) .. +3, column
+// l % 16):
+//   S^T = K Q^T   A = a K tile (key rows, read from LDS), B = the wave's Q
+//                 rows (registers, loaded once). D holds, for lane l's query
+//                 (column l % 16), the keys 4 (l / 16) .. +3 of each 16-key
+//                 tile.
+//   O  += P V     A = P. A lane's D registers of two consecutive key tiles
+//                 hold exactly 8 keys of its own query: they are its A
+//                 fragment, with the k positions of the 32-key step mapped
+//                 to keys 4 (l / 16) + i and 16 + 4 (l / 16) + i. B = V with
+//                 the same key mapping, read from a transposed V tile in LDS
+//                 (two 8-byte reads per fragment).
+// Computing S transposed is what lets P stay in the registers that received
+// it: no exchange between lanes before the second product. The online
+// softmax works in base 2 (the scale carries log2 e); a row's maximum and
+// sum need one butterfly over the 4 lane groups; the rescale factor of a row
+// reaches the O rows 4 (l / 16) + i with one shuffle each.
+// The next key / value block is loaded into registers while the current one
+// is computed; K is staged row-major and V transposed in LDS. With the
+// causal mask, blocks wholly above the diagonal are skipped and the heaviest
+// query blocks are launched first.
+#include "fr_device.h"
+#include "fr_internal.h"
+
+namespace fr {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+
+constexpr int kBM = kAttnBlockRows;  // query rows per workgroup
+constexpr int kBN = 64;              // keys per block
+constexpr int kWaves = 4;
+constexpr int kKPad = 8;   // bf16 padding per K row in LDS
+constexpr int kVPad = 8;   // bf16 padding per transposed V row in LDS
+
+__device__ __forceinline__ f32x4 mfma(f32x4 a, f32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 ld16g(const uint16_t* p) { return *reinterpret_cast<const f32x4*>(p); }
+
+// two fp32 -> packed bf16 (round to nearest even)
+__device__ __forceinline__ float pk(float lo, float hi) { return __builtin_bit_cast(float, pack_bf16(lo, hi)); }
+
+}  // namespace
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void fr_attn_block_bf16(const uint16_t* __restrict__ q,
+                                                          const uint16_t* __restrict__ k,
+                                                          const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
+                                                          float* __restrict__ lse, int Hq, int Hkv, int Nq, int Nk,
+                                                          float scale_log2) {
+    constexpr int NS = D / 32;        // 32-dim steps of S^T
+    constexpr int NT = D / 16;        // 16-dim tiles of O
+    constexpr int KCH = kBN * D / 8;  // 16-byte chunks of a K block
+    constexpr int KPT = KCH / 256;    // per thread
+    constexpr int VUN = kBN / 2 * D / 8;  // (key pair, dim octet) units of a V block
+    constexpr int VPT = VUN / 256;
+    constexpr int KLD = D + kKPad, VLD = kBN + kVPad;
+    static_assert(KCH % 256 == 0 && VUN % 256 == 0, "block shape");
+    __shared__ __align__(16) uint16_t sk[kBN * KLD];
+    __shared__ __align__(16) uint16_t sv[D * VLD];
+
+    const int nqb = (Nq + kBM - 1) / kBM;
+    const int qb = CAUSAL ? nqb - 1 - (int)blockIdx.x : (int)blockIdx.x;  // heaviest first
+    const int h = blockIdx.y, b = blockIdx.z;
+    const int hk = h / (Hq / Hkv);
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int n = lane & 15, g = lane >> 4;
+    const int64_t qrow0 = ((int64_t)b * Hq + h) * Nq;
+    const int64_t kv0 = ((int64_t)b * Hkv + hk) * Nk;
+    const int qbase = qb * kBM + w * 32;  // the wave's first query row
+
+    // the wave's Q rows as B fragments: query 16 bq + n, dims 32 s + 8 g .. +7
+    f32x4 qf[2][NS];
+#pragma unroll
+    for (int bq = 0; bq < 2; ++bq) {
+        const int qi = qbase + 16 * bq + n;
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+            qf[bq][s] = qi < Nq ? ld16g(q + (qrow0 + qi) * D + 32 * s + 8 * g) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    int nkb = (Nk + kBN - 1) / kBN;
+    if (CAUSAL) {
+        const int last = qb * kBM + kBM - 1;  // the block's last query sees keys <= last
+        const int need = last / kBN + 1;
+        nkb = need < nkb ? need : nkb;
+    }
+
+    // the next block's K chunks and V units, in registers
+    f32x4 kr[KPT], vr[VPT][2];
+    auto fetch = [&](int jb) {
+#pragma unroll
+        for (int r = 0; r < KPT; ++r) {
+            const int c = tid + 256 * r, j = jb * kBN + c / (D / 8), oc = c % (D / 8);
+            kr[r] = j < Nk ? ld16g(k + (kv0 + j) * D + 8 * oc) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int r = 0; r < VPT; ++r) {
+            const int u = tid + 256 * r, j = jb * kBN + 2 * (u / (D / 8)), oc = u % (D / 8);
+            vr[r][0] = j < Nk ? ld16g(v + (kv0 + j) * D + 8 * oc) : f32x4{0.f, 0.f, 0.f, 0.f};
+            vr[r][1] = j + 1 < Nk ? ld16g(v + (kv0 + j + 1) * D + 8 * oc) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    };
+    auto stage = [&]() {
+#pragma unroll
+        for (int r = 0; r < KPT; ++r) {
+            const int c = tid + 256 * r, j = c / (D / 8), oc = c % (D / 8);
+            *reinterpret_cast<f32x4*>(&sk[j * KLD + 8 * oc]) = kr[r];
+        }
+#pragma unroll
+        for (int r = 0; r < VPT; ++r) {
+            const int u = tid + 256 * r, j = 2 * (u / (D / 8)), oc = u % (D / 8);
+            const uint32_t* a0 = reinterpret_cast<const uint32_t*>(&vr[r][0]);
+            const uint32_t* a1 = reinterpret_cast<const uint32_t*>(&vr[r][1]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t lo = (e & 1) ? (a0[e >> 1] >> 16) : (a0[e >> 1] & 0xFFFFu);
+                const uint32_t hi = (e & 1) ? (a1[e >> 1] >> 16) : (a1[e >> 1] & 0xFFFFu);
+                *reinterpret_cast<uint32_t*>(&sv[(8 * oc + e) * VLD + j]) = lo | (hi << 16);
+            }
+        }
+    };
+
+    f32x4 acc[2][NT];
+#pragma unroll
+    for (int bq = 0; bq < 2; ++bq)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[bq][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+
+    if (nkb > 0) fetch(0);
+    for (int jb = 0; jb < nkb; ++jb) {
+        stage();
+        __syncthreads();
+        if (jb + 1 < nkb) fetch(jb + 1);  // in flight while this block is computed
+
+        // S^T for 4 key tiles x 2 query tiles
+        f32x4 st[4][2];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int bq = 0; bq < 2; ++bq) st[t][bq] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const f32x4 a = *reinterpret_cast<const f32x4*>(&sk[(16 * t + n) * KLD + 32 * s + 8 * g]);
+#pragma unroll
+                for (int bq = 0; bq < 2; ++bq) st[t][bq] = mfma(a, qf[bq][s], st[t][bq]);
+            }
+
+        // online softmax per query (lane's column), base 2
+        float alpha[2];
+#pragma unroll
+        for (int bq = 0; bq < 2; ++bq) {
+            const int qi = qbase + 16 * bq + n;
+            float mx = -INFINITY;
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int j = jb * kBN + 16 * t + 4 * g + i;
+                    const bool ok = j < Nk && (!CAUSAL || j <= qi);
+                    const float sc = ok ? st[t][bq][i] * scale_log2 : -INFINITY;
+                    st[t][bq][i] = sc;
+                    mx = fmaxf(mx, sc);
+                }
+            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            const float mn = fmaxf(m[bq], mx);
+            const float mu = mn == -INFINITY ? 0.f : mn;  // nothing seen yet: keep everything at 0
+            alpha[bq] = __builtin_amdgcn_exp2f(m[bq] - mu);
+            float sum = 0.f;
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float p = __builtin_amdgcn_exp2f(st[t][bq][i] - mu);
+                    st[t][bq][i] = p;
+                    sum += p;
+                }
+            sum += __shfl_xor(sum, 16, 64);
+            sum += __shfl_xor(sum, 32, 64);
+            l[bq] = l[bq] * alpha[bq] + sum;
+            m[bq] = mn;
+        }
+        // rescale the O rows 4 g + i by their query's factor
+#pragma unroll
+        for (int bq = 0; bq < 2; ++bq)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float a = __shfl(alpha[bq], 4 * g + i, 64);
+#pragma unroll
+                for (int t = 0; t < NT; ++t) acc[bq][t][i] *= a;
+            }
+        // O += P V, two 32-key steps
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            f32x4 pa[2];
+#pragma unroll
+            for (int bq = 0; bq < 2; ++bq) {
+                const f32x4 lo = st[2 * kk][bq], hi = st[2 * kk + 1][bq];
+                pa[bq] = f32x4{pk(lo[0], lo[1]), pk(lo[2], lo[3]), pk(hi[0], hi[1]), pk(hi[2], hi[3])};
+            }
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const uint16_t* row = &sv[(16 * t + n) * VLD + 32 * kk + 4 * g];
+                const short4v v0 = *reinterpret_cast<const short4v*>(row);
+                const short4v v1 = *reinterpret_cast<const short4v*>(row + 16);
+                const f32x4 bv = __builtin_bit_cast(
+                    f32x4, (short __attribute__((ext_vector_type(8)))){v0[0], v0[1], v0[2], v0[3], v1[0], v1[1],
+                                                                        v1[2], v1[3]});
+#pragma unroll
+                for (int bq = 0; bq < 2; ++bq) acc[bq][t] = mfma(pa[bq], bv, acc[bq][t]);
+            }
+        }
+        __syncthreads();  // the next block overwrites the LDS tiles
+    }
+
+    // o = a / l (rows 4 g + i of each query tile); lse = (m + log2 l) ln 2
+#pragma unroll
+    for (int bq = 0; bq < 2; ++bq) {
+        const int qi = qbase + 16 * bq + n;
+        if (g == 0 && qi < Nq)
+            lse[qrow0 + qi] = l[bq] > 0.f ? (m[bq] + __log2f(l[bq])) * 0.69314718055994531f : -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float li = __shfl(l[bq], 4 * g + i, 64);
+            const float inv = li > 0.f ? 1.0f / li : 0.f;
+            const int qr = qbase + 16 * bq + 4 * g + i;
+            if (qr < Nq) {
+                uint16_t* orow = o + (qrow0 + qr) * D;
+#pragma unroll
+                for (int t = 0; t < NT; ++t) orow[16 * t + n] = (uint16_t)(pack_bf16(acc[bq][t][i] * inv, 0.f) & 0xFFFFu);
+            }
+        }
+    }
+}
+
+hipError_t launch_attn_block(const AttnBlockArgs& a, hipStream_t s) {
+    const dim3 grid((unsigned)((a.seq_q + kBM - 1) / kBM), (unsigned)a.heads_q, (unsigned)a.batch);
+    const float sl2 = a.scale * 1.4426950408889634f;
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                           (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.heads_q, a.heads_kv, a.seq_q, a.seq_kv, sl2);
+    };
+    if (a.dim == 128) a.causal ? go(fr_attn_block_bf16<128, true>) : go(fr_attn_block_bf16<128, false>);
+    else a.causal ? go(fr_attn_block_bf16<64, true>) : go(fr_attn_block_bf16<64, false>);
+    return hipGetLastError();
+}
+
+}  // namespace fr

@@ -130,6 +130,19 @@ struct AttnArgs {
     bool bf16;
 };
 hipError_t launch_attn_decode(const AttnArgs& a, hipStream_t s);
+// Tiled attention over blocks of kAttnBlockRows query rows (bf16).
+constexpr int kAttnBlockRows = 128;
+struct AttnBlockArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    int batch, heads_q, heads_kv, seq_q, seq_kv, dim;
+    bool causal;
+    float scale;
+};
+hipError_t launch_attn_block(const AttnBlockArgs& a, hipStream_t s);
 
 // Streaming reference kernels: at most kStreamGrid workgroups of 256 threads,
 // 4 vectors of 16 bytes per thread per step.

@@ -183,3 +183,12 @@ def attn_decode_inputs(batch=8, heads_q=32, heads_kv=8, seq=8192, dim=128, seed=
     if bf16:
         return to_bf16(q), to_bf16(k), to_bf16(v), L
     return q, k, v, L
+
+
+def attn_block_inputs(batch=4, heads_q=16, heads_kv=16, seq_q=4096, seq_kv=4096, dim=128, seed=7001):
+    """Attention over blocks of query rows: q [B, Hq, Nq, D], k, v [B, Hkv, Nk,
+    D], all N(0, 1), rounded to bf16 and returned as uint16 bits."""
+    q = normal((batch, heads_q, seq_q, dim), seed, stream=0)
+    k = normal((batch, heads_kv, seq_kv, dim), seed, stream=1)
+    v = normal((batch, heads_kv, seq_kv, dim), seed, stream=2)
+    return to_bf16(q), to_bf16(k), to_bf16(v)
