@@ -359,7 +359,8 @@ int fr_attn_decode(const void* q, const void* k, const void* v, void* o, float* 
  *  lse:    fp32 [batch, heads_q, seq_q] (natural log), 4-byte aligned.
  *  causal: query i sees key j only when i >= j (Listing 9.7's mask_mod);
  *          key blocks wholly above the diagonal are skipped.
- *  scale:  finite (commonly 1 / sqrt(dim)).
+ *  scale:  finite and > 0 (commonly 1 / sqrt(dim)); the row maxima are
+ *          taken on the unscaled scores.
  * dim 64 or 128; heads_q a multiple of heads_kv; batch and heads_q <=
  * 65535; seq lengths < 2^30. A row that sees no key (seq_kv = 0) gives
  * o = 0 and lse = -inf. dtype must be FR_BF16. */

@@ -480,8 +480,10 @@ int fr_attn_block(const void* q, const void* k, const void* v, void* o, float* l
     if (dim != 64 && dim != 128) return FR_E_SIZE;
     if (batch > 65535 || heads_q > 65535 || seq_q >= kMaxCols || seq_kv >= kMaxCols) return FR_E_SIZE;
     if (batch == 0 || heads_q == 0 || seq_q == 0) return FR_OK;
+    // one workgroup per (block of 128 query rows, head, batch): a 1-D grid
+    if ((seq_q + kAttnBlockRows - 1) / kAttnBlockRows * heads_q * batch >= (int64_t(1) << 31)) return FR_E_SIZE;
     if (heads_kv == 0 || heads_q % heads_kv) return FR_E_ARG;
-    if (!isfinite(scale)) return FR_E_ARG;
+    if (!isfinite(scale) || !(scale > 0.0f)) return FR_E_ARG;
     if (!q || !o || !lse || (seq_kv > 0 && (!k || !v))) return FR_E_NULL;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
         return FR_E_ALIGN;

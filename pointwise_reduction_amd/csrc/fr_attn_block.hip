@@ -23,10 +23,13 @@
 // softmax works in base 2 (the scale carries log2 e); a row's maximum and
 // sum need one butterfly over the 4 lane groups; the rescale factor of a row
 // reaches the O rows 4 (l / 16) + i with one shuffle each.
-// The next key / value block is loaded into registers while the current one
-// is computed; K is staged row-major and V transposed in LDS. With the
-// causal mask, blocks wholly above the diagonal are skipped and the heaviest
-// query blocks are launched first.
+// K is staged row-major and V transposed in LDS, one block at a time. The
+// kernel is held to 256 registers so that two workgroups share a CU: one's
+// softmax then overlaps the other's matrix products (measured at 4 x 16 x
+// 4096 x 128: 1126 us against 1495 us for one workgroup per CU that also
+// prefetched the next block into registers). With the causal mask, blocks
+// wholly above the diagonal are skipped and the heaviest query blocks of a
+// head are launched first.
 #include "fr_device.h"
 #include "fr_internal.h"
 
@@ -40,6 +43,7 @@ typedef short short4v __attribute__((ext_vector_type(4)));
 constexpr int kBM = kAttnBlockRows;  // query rows per workgroup
 constexpr int kBN = 64;              // keys per block
 constexpr int kWaves = 4;
+constexpr int kXcds = 8;  // MI355X: 8 XCDs, each with its own L2
 constexpr int kKPad = 8;   // bf16 padding per K row in LDS
 constexpr int kVPad = 8;   // bf16 padding per transposed V row in LDS
 
@@ -56,7 +60,7 @@ __device__ __forceinline__ float pk(float lo, float hi) { return __builtin_bit_c
 }  // namespace
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void fr_attn_block_bf16(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(256, 2) void fr_attn_block_bf16(const uint16_t* __restrict__ q,
                                                           const uint16_t* __restrict__ k,
                                                           const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
                                                           float* __restrict__ lse, int Hq, int Hkv, int Nq, int Nk,
@@ -72,9 +76,16 @@ __global__ __launch_bounds__(256) void fr_attn_block_bf16(const uint16_t* __rest
     __shared__ __align__(16) uint16_t sk[kBN * KLD];
     __shared__ __align__(16) uint16_t sv[D * VLD];
 
+    // XCD-aware order: the dispatcher sends workgroup L to XCD L % 8, so
+    // logical tile L % 8 * (G / 8) + L / 8 gives each XCD a contiguous run of
+    // tiles, i.e. whole heads, whose K and V then stay in that XCD's L2
     const int nqb = (Nq + kBM - 1) / kBM;
-    const int qb = CAUSAL ? nqb - 1 - (int)blockIdx.x : (int)blockIdx.x;  // heaviest first
-    const int h = blockIdx.y, b = blockIdx.z;
+    const int G = (int)gridDim.x;
+    const int L = (int)blockIdx.x;
+    const int tile = (G % kXcds == 0) ? (L % kXcds) * (G / kXcds) + L / kXcds : L;
+    const int qi0 = tile % nqb;
+    const int qb = CAUSAL ? nqb - 1 - qi0 : qi0;  // heaviest first within a head
+    const int h = (tile / nqb) % Hq, b = tile / (nqb * Hq);
     const int hk = h / (Hq / Hkv);
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int n = lane & 15, g = lane >> 4;
@@ -141,11 +152,10 @@ __global__ __launch_bounds__(256) void fr_attn_block_bf16(const uint16_t* __rest
         for (int t = 0; t < NT; ++t) acc[bq][t] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
 
-    if (nkb > 0) fetch(0);
     for (int jb = 0; jb < nkb; ++jb) {
+        fetch(jb);
         stage();
         __syncthreads();
-        if (jb + 1 < nkb) fetch(jb + 1);  // in flight while this block is computed
 
         // S^T for 4 key tiles x 2 query tiles
         f32x4 st[4][2];
@@ -162,33 +172,40 @@ __global__ __launch_bounds__(256) void fr_attn_block_bf16(const uint16_t* __rest
                 for (int bq = 0; bq < 2; ++bq) st[t][bq] = mfma(a, qf[bq][s], st[t][bq]);
             }
 
-        // online softmax per query (lane's column), base 2
+        // online softmax per query (lane's column), base 2. m holds raw
+        // scores (scale > 0 keeps the order); exponents are fma(s, c, -m c).
+        // Blocks wholly inside the keys (and, causal, wholly at or below
+        // every query of the wave) need no mask.
+        const bool full = (jb + 1) * kBN <= Nk && (!CAUSAL || (jb + 1) * kBN - 1 <= qbase);
         float alpha[2];
 #pragma unroll
         for (int bq = 0; bq < 2; ++bq) {
-            const int qi = qbase + 16 * bq + n;
+            if (!full) {
+                const int qi = qbase + 16 * bq + n;
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int j = jb * kBN + 16 * t + 4 * g + i;
+                        if (!(j < Nk && (!CAUSAL || j <= qi))) st[t][bq][i] = -INFINITY;
+                    }
+            }
             float mx = -INFINITY;
 #pragma unroll
             for (int t = 0; t < 4; ++t)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int j = jb * kBN + 16 * t + 4 * g + i;
-                    const bool ok = j < Nk && (!CAUSAL || j <= qi);
-                    const float sc = ok ? st[t][bq][i] * scale_log2 : -INFINITY;
-                    st[t][bq][i] = sc;
-                    mx = fmaxf(mx, sc);
-                }
+                for (int i = 0; i < 4; ++i) mx = fmaxf(mx, st[t][bq][i]);
             mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
             mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
             const float mn = fmaxf(m[bq], mx);
-            const float mu = mn == -INFINITY ? 0.f : mn;  // nothing seen yet: keep everything at 0
-            alpha[bq] = __builtin_amdgcn_exp2f(m[bq] - mu);
+            const float mu = mn == -INFINITY ? 0.f : mn * scale_log2;  // nothing seen yet: everything stays 0
+            alpha[bq] = __builtin_amdgcn_exp2f(fmaf(m[bq], scale_log2, -mu));
             float sum = 0.f;
 #pragma unroll
             for (int t = 0; t < 4; ++t)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float p = __builtin_amdgcn_exp2f(st[t][bq][i] - mu);
+                    const float p = __builtin_amdgcn_exp2f(fmaf(st[t][bq][i], scale_log2, -mu));
                     st[t][bq][i] = p;
                     sum += p;
                 }
@@ -235,7 +252,7 @@ __global__ __launch_bounds__(256) void fr_attn_block_bf16(const uint16_t* __rest
     for (int bq = 0; bq < 2; ++bq) {
         const int qi = qbase + 16 * bq + n;
         if (g == 0 && qi < Nq)
-            lse[qrow0 + qi] = l[bq] > 0.f ? (m[bq] + __log2f(l[bq])) * 0.69314718055994531f : -INFINITY;
+            lse[qrow0 + qi] = l[bq] > 0.f ? fmaf(m[bq], scale_log2, __log2f(l[bq])) * 0.69314718055994531f : -INFINITY;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const float li = __shfl(l[bq], 4 * g + i, 64);
@@ -251,7 +268,7 @@ __global__ __launch_bounds__(256) void fr_attn_block_bf16(const uint16_t* __rest
 }
 
 hipError_t launch_attn_block(const AttnBlockArgs& a, hipStream_t s) {
-    const dim3 grid((unsigned)((a.seq_q + kBM - 1) / kBM), (unsigned)a.heads_q, (unsigned)a.batch);
+    const dim3 grid((unsigned)((int64_t)(a.seq_q + kBM - 1) / kBM * a.heads_q * a.batch));
     const float sl2 = a.scale * 1.4426950408889634f;
     auto go = [&](auto kern) {
         hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, (const uint16_t*)a.q, (const uint16_t*)a.k,
