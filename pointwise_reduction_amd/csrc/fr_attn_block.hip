@@ -23,13 +23,13 @@
 // softmax works in base 2 (the scale carries log2 e); a row's maximum and
 // sum need one butterfly over the 4 lane groups; the rescale factor of a row
 // reaches the O rows 4 (l / 16) + i with one shuffle each.
-// K is staged row-major and V transposed in LDS, one block at a time. The
-// kernel is held to 256 registers so that two workgroups share a CU: one's
-// softmax then overlaps the other's matrix products (measured at 4 x 16 x
-// 4096 x 128: 1126 us against 1495 us for one workgroup per CU that also
-// prefetched the next block into registers). With the causal mask, blocks
-// wholly above the diagonal are skipped and the heaviest query blocks of a
-// head are launched first.
+// K is staged row-major and V transposed in LDS (one byte permute per staged
+// word); the next key / value block is loaded into registers while the
+// current one is computed. The block's Q rows sit in LDS rather than in
+// registers, which holds the kernel to 256 registers: two workgroups share a
+// CU and one's softmax overlaps the other's matrix products. With the causal
+// mask, blocks wholly above the diagonal are skipped and the heaviest query
+// blocks of a head are launched first.
 #include "fr_device.h"
 #include "fr_internal.h"
 
@@ -81,6 +81,7 @@ __global__ __launch_bounds__(256, 2) void fr_attn_block_bf16(const uint16_t* __r
     static_assert(KCH % 256 == 0 && VUN % 256 == 0, "block shape");
     __shared__ __align__(16) uint16_t sk[kBN * KLD];
     __shared__ __align__(16) uint16_t sv[D * VLD];
+    __shared__ __align__(16) uint16_t sq[kBM * KLD];
 
     // XCD-aware order: the dispatcher sends workgroup L to XCD L % 8, so
     // logical tile L % 8 * (G / 8) + L / 8 gives each XCD a contiguous run of
@@ -99,14 +100,13 @@ __global__ __launch_bounds__(256, 2) void fr_attn_block_bf16(const uint16_t* __r
     const int64_t kv0 = ((int64_t)b * Hkv + hk) * Nk;
     const int qbase = qb * kBM + w * 32;  // the wave's first query row
 
-    // the wave's Q rows as B fragments: query 16 bq + n, dims 32 s + 8 g .. +7
-    f32x4 qf[2][NS];
+    // the block's Q rows in LDS; B fragments are read from there per key block
 #pragma unroll
-    for (int bq = 0; bq < 2; ++bq) {
-        const int qi = qbase + 16 * bq + n;
-#pragma unroll
-        for (int s = 0; s < NS; ++s)
-            qf[bq][s] = qi < Nq ? ld16g(q + (qrow0 + qi) * D + 32 * s + 8 * g) : f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < kBM * D / 8 / 256; ++r) {
+        const int c = tid + 256 * r, row = c / (D / 8), oc = c % (D / 8);
+        const int qi = qb * kBM + row;
+        *reinterpret_cast<f32x4*>(&sq[row * KLD + 8 * oc]) =
+            qi < Nq ? ld16g(q + (qrow0 + qi) * D + 8 * oc) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
     int nkb = (Nk + kBN - 1) / kBN;
@@ -142,12 +142,12 @@ __global__ __launch_bounds__(256, 2) void fr_attn_block_bf16(const uint16_t* __r
             const int u = tid + 256 * r, j = 2 * (u % (kBN / 2)), oc = u / (kBN / 2);
             const uint32_t* a0 = reinterpret_cast<const uint32_t*>(&vr[r][0]);
             const uint32_t* a1 = reinterpret_cast<const uint32_t*>(&vr[r][1]);
+            // element e of keys j and j + 1 as one word: one byte permute
+            // (low halves: bytes 0, 1 of each word; high halves: bytes 2, 3)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t lo = (e & 1) ? (a0[e >> 1] >> 16) : (a0[e >> 1] & 0xFFFFu);
-                const uint32_t hi = (e & 1) ? (a1[e >> 1] >> 16) : (a1[e >> 1] & 0xFFFFu);
-                *reinterpret_cast<uint32_t*>(&sv[(8 * oc + e) * VLD + j]) = lo | (hi << 16);
-            }
+            for (int e = 0; e < 8; ++e)
+                *reinterpret_cast<uint32_t*>(&sv[(8 * oc + e) * VLD + j]) =
+                    __builtin_amdgcn_perm(a1[e >> 1], a0[e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
         }
     };
 
@@ -158,10 +158,11 @@ __global__ __launch_bounds__(256, 2) void fr_attn_block_bf16(const uint16_t* __r
         for (int t = 0; t < NT; ++t) acc[bq][t] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
 
+    if (nkb > 0) fetch(0);
     for (int jb = 0; jb < nkb; ++jb) {
-        fetch(jb);
         stage();
         __syncthreads();
+        if (jb + 1 < nkb) fetch(jb + 1);  // in flight while this block is computed
 
         // S^T for 4 key tiles x 2 query tiles
         f32x4 st[4][2];
@@ -175,7 +176,10 @@ __global__ __launch_bounds__(256, 2) void fr_attn_block_bf16(const uint16_t* __r
             for (int t = 0; t < 4; ++t) {
                 const f32x4 a = *reinterpret_cast<const f32x4*>(&sk[(16 * t + n) * KLD + 32 * s + 8 * g]);
 #pragma unroll
-                for (int bq = 0; bq < 2; ++bq) st[t][bq] = mfma(a, qf[bq][s], st[t][bq]);
+                for (int bq = 0; bq < 2; ++bq) {
+                    const f32x4 qv = *reinterpret_cast<const f32x4*>(&sq[(w * 32 + 16 * bq + n) * KLD + 32 * s + 8 * g]);
+                    st[t][bq] = mfma(a, qv, st[t][bq]);
+                }
             }
 
         // online softmax per query (lane's column), base 2. m holds raw
