@@ -50,6 +50,7 @@ constexpr int kXcds = 8;  // MI355X: 8 XCDs, each with its own L2
 // (consecutive 4-byte words); the first layout, 8 elements of padding with
 // consecutive lanes on different octets, spent 68% of the LDS-active cycles
 // in bank conflicts (1100 us against 760 us at 4 x 16 x 4096 x 128).
+constexpr float kLazy = 8.0f;  // P <= 2^8 between rescales (base-2 exponent)
 constexpr int kKPad = 16;
 constexpr int kVPad = 4;
 
@@ -182,12 +183,18 @@ __global__ __launch_bounds__(256, 2) void fr_attn_block_bf16(const uint16_t* __r
                 }
             }
 
-        // online softmax per query (lane's column), base 2. m holds raw
-        // scores (scale > 0 keeps the order); exponents are fma(s, c, -m c).
-        // Blocks wholly inside the keys (and, causal, wholly at or below
-        // every query of the wave) need no mask.
+        // online softmax per query (lane's column), base 2, against a
+        // reference: m holds a per-row reference maximum (scaled), the
+        // exponents are exp2(fma(s, c, -m)) and l and the O rows are relative
+        // to it. The reference moves (and O, l are rescaled) only when some
+        // row of the wave sees a block maximum more than kLazy above its
+        // reference, so P stays <= 2^kLazy and o = a / l is unchanged; after
+        // the first blocks the rescale is rarely needed. Blocks wholly inside
+        // the keys (and, causal, wholly at or below every query of the wave)
+        // need no mask.
         const bool full = (jb + 1) * kBN <= Nk && (!CAUSAL || (jb + 1) * kBN - 1 <= qbase);
-        float alpha[2];
+        float mxs[2];
+        bool need = false;
 #pragma unroll
         for (int bq = 0; bq < 2; ++bq) {
             if (!full) {
@@ -207,9 +214,27 @@ __global__ __launch_bounds__(256, 2) void fr_attn_block_bf16(const uint16_t* __r
                 for (int i = 0; i < 4; ++i) mx = fmaxf(mx, st[t][bq][i]);
             mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
             mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            const float mn = fmaxf(m[bq], mx);
-            const float mu = mn == -INFINITY ? 0.f : mn * scale_log2;  // nothing seen yet: everything stays 0
-            alpha[bq] = __builtin_amdgcn_exp2f(fmaf(m[bq], scale_log2, -mu));
+            mxs[bq] = mx * scale_log2;
+            need |= mxs[bq] > m[bq] + kLazy;
+        }
+        if (__any(need)) {
+#pragma unroll
+            for (int bq = 0; bq < 2; ++bq) {
+                const float nm = fmaxf(m[bq], mxs[bq]);
+                const float alpha = nm == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[bq] - nm);
+                l[bq] *= alpha;
+                m[bq] = nm;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float a = __shfl(alpha, 4 * g + i, 64);
+#pragma unroll
+                    for (int t = 0; t < NT; ++t) acc[bq][t][i] *= a;
+                }
+            }
+        }
+#pragma unroll
+        for (int bq = 0; bq < 2; ++bq) {
+            const float mu = m[bq] == -INFINITY ? 0.f : m[bq];  // nothing seen yet: everything stays 0
             float sum = 0.f;
 #pragma unroll
             for (int t = 0; t < 4; ++t)
@@ -221,18 +246,8 @@ __global__ __launch_bounds__(256, 2) void fr_attn_block_bf16(const uint16_t* __r
                 }
             sum += __shfl_xor(sum, 16, 64);
             sum += __shfl_xor(sum, 32, 64);
-            l[bq] = l[bq] * alpha[bq] + sum;
-            m[bq] = mn;
+            l[bq] += sum;
         }
-        // rescale the O rows 4 g + i by their query's factor
-#pragma unroll
-        for (int bq = 0; bq < 2; ++bq)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float a = __shfl(alpha[bq], 4 * g + i, 64);
-#pragma unroll
-                for (int t = 0; t < NT; ++t) acc[bq][t][i] *= a;
-            }
         // O += P V, two 32-key steps
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
@@ -262,7 +277,7 @@ __global__ __launch_bounds__(256, 2) void fr_attn_block_bf16(const uint16_t* __r
     for (int bq = 0; bq < 2; ++bq) {
         const int qi = qbase + 16 * bq + n;
         if (g == 0 && qi < Nq)
-            lse[qrow0 + qi] = l[bq] > 0.f ? fmaf(m[bq], scale_log2, __log2f(l[bq])) * 0.69314718055994531f : -INFINITY;
+            lse[qrow0 + qi] = l[bq] > 0.f ? (m[bq] + __log2f(l[bq])) * 0.69314718055994531f : -INFINITY;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const float li = __shfl(l[bq], 4 * g + i, 64);
