@@ -119,7 +119,23 @@ __global__ __launch_bounds__(256, 2) void fr_attn_block_bf16(const uint16_t* __r
 
     // the next block's K chunks and V units, in registers
     f32x4 kr[KPT], vr[VPT][2];
+    // loads of the next block; only a block that crosses the end of the keys
+    // checks each row (the branch is the same for the whole workgroup)
     auto fetch = [&](int jb) {
+        if ((jb + 1) * kBN <= Nk) {
+#pragma unroll
+            for (int r = 0; r < KPT; ++r) {
+                const int c = tid + 256 * r, j = jb * kBN + c / (D / 8), oc = c % (D / 8);
+                kr[r] = ld16g(k + (kv0 + j) * D + 8 * oc);
+            }
+#pragma unroll
+            for (int r = 0; r < VPT; ++r) {
+                const int u = tid + 256 * r, j = jb * kBN + 2 * (u % (kBN / 2)), oc = u / (kBN / 2);
+                vr[r][0] = ld16g(v + (kv0 + j) * D + 8 * oc);
+                vr[r][1] = ld16g(v + (kv0 + j + 1) * D + 8 * oc);
+            }
+            return;
+        }
 #pragma unroll
         for (int r = 0; r < KPT; ++r) {
             const int c = tid + 256 * r, j = jb * kBN + c / (D / 8), oc = c % (D / 8);
