@@ -209,11 +209,9 @@ __global__ __launch_bounds__(256, 2) void fr_attn_block_bf16(const uint16_t* __r
         // the keys (and, causal, wholly at or below every query of the wave)
         // need no mask.
         const bool full = (jb + 1) * kBN <= Nk && (!CAUSAL || (jb + 1) * kBN - 1 <= qbase);
-        float mxs[2];
-        bool need = false;
+        if (!full) [[unlikely]] {
 #pragma unroll
-        for (int bq = 0; bq < 2; ++bq) {
-            if (!full) {
+            for (int bq = 0; bq < 2; ++bq) {
                 const int qi = qbase + 16 * bq + n;
 #pragma unroll
                 for (int t = 0; t < 4; ++t)
@@ -223,6 +221,11 @@ __global__ __launch_bounds__(256, 2) void fr_attn_block_bf16(const uint16_t* __r
                         if (!(j < Nk && (!CAUSAL || j <= qi))) st[t][bq][i] = -INFINITY;
                     }
             }
+        }
+        float mxs[2];
+        bool need = false;
+#pragma unroll
+        for (int bq = 0; bq < 2; ++bq) {
             float mx = -INFINITY;
 #pragma unroll
             for (int t = 0; t < 4; ++t)
