@@ -4,9 +4,13 @@
 
 A step is one pass of the whole operation over one batch of synthetic input
 already resident in HBM. The default workload is the row softmax over
-4096 x 1024 fp32 (the headline configuration). The other workloads (Example
-1.1 sums, LayerNorm 2048 x 32768 bf16, the 2^28 sum of squares, the ragged
-512-row softmax) are selected with --workload.
+4096 x 1024 fp32 (the headline configuration). The other workloads are
+selected with --workload: Example 1.1 sums, LayerNorm 2048 x 32768 bf16, the
+2^28 sum of squares, the ragged 512-row softmax, decode and tiled attention,
+softmax and LayerNorm backward, x.t() + y, GELU backward, a recorded region
+of 16 Example 1.1 launches, and streaming references (copy, read). Tiled
+attention reports TFLOP/s against the matrix cores' bf16 peak; the others
+report GB/s against HBM.
 
 Timing: W untimed steps, then exactly K steps between two events on the
 launch stream, with a device synchronization on both sides. Consecutive
