@@ -16,16 +16,18 @@
 //                 hold exactly 8 keys of its own query: they are its A
 //                 fragment, with the k positions of the 32-key step mapped
 //                 to keys 4 (l / 16) + i and 16 + 4 (l / 16) + i. B = V with
-//                 the same key mapping, read from a transposed V tile in LDS
-//                 (two 8-byte reads per fragment).
+//                 the same key mapping, read from the row-major V tile in LDS
+//                 with gfx950's transposing read (ds_read_b64_tr_b16: within
+//                 each 16-lane group, lane j's element e comes from the
+//                 8-byte piece that lane 4 e + j / 4 addresses, component
+//                 j % 4; two reads per fragment).
 // Computing S transposed is what lets P stay in the registers that received
 // it: no exchange between lanes before the second product. The online
 // softmax works in base 2 (the scale carries log2 e); a row's maximum and
 // sum need one butterfly over the 4 lane groups; the rescale factor of a row
 // reaches the O rows 4 (l / 16) + i with one shuffle each.
-// K is staged row-major and V transposed in LDS (one byte permute per staged
-// word); the next key / value block is loaded into registers while the
-// current one is computed. The block's Q rows sit in LDS rather than in
+// K and V are staged row-major in LDS with 16-byte writes; the next key /
+// value block is loaded into registers while the current one is computed. The block's Q rows sit in LDS rather than in
 // registers, which holds the kernel to 256 registers: two workgroups share a
 // CU and one's softmax overlaps the other's matrix products. With the causal
 // mask, blocks wholly above the diagonal are skipped and the heaviest query
@@ -39,20 +41,18 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short short4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4v* lds_s4p;
 
 constexpr int kBM = kAttnBlockRows;  // query rows per workgroup
 constexpr int kBN = 64;              // keys per block
 constexpr int kWaves = 4;
 constexpr int kXcds = 8;  // MI355X: 8 XCDs, each with its own L2
-// LDS row padding (bf16 elements). A transposed V row of 64 + 4 elements
-// puts the 16 rows that one fragment read touches on distinct bank pairs,
-// and consecutive lanes stage consecutive key pairs of one dimension octet
-// (consecutive 4-byte words); the first layout, 8 elements of padding with
-// consecutive lanes on different octets, spent 68% of the LDS-active cycles
-// in bank conflicts (1100 us against 760 us at 4 x 16 x 4096 x 128).
 constexpr float kLazy = 8.0f;  // P <= 2^8 between rescales (base-2 exponent)
+// LDS row padding (bf16 elements) of the K, V and Q tiles: rows 288 bytes
+// apart (D = 128) keep every fragment read free of bank conflicts. An
+// earlier layout (V staged transposed, consecutive lanes on different
+// dimension octets) spent 68% of the LDS-active cycles in bank conflicts.
 constexpr int kKPad = 16;
-constexpr int kVPad = 4;
 
 __device__ __forceinline__ f32x4 mfma(f32x4 a, f32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
@@ -76,12 +76,11 @@ __global__ __launch_bounds__(256, 2) void fr_attn_block_bf16(const uint16_t* __r
     constexpr int NT = D / 16;        // 16-dim tiles of O
     constexpr int KCH = kBN * D / 8;  // 16-byte chunks of a K block
     constexpr int KPT = KCH / 256;    // per thread
-    constexpr int VUN = kBN / 2 * D / 8;  // (key pair, dim octet) units of a V block
-    constexpr int VPT = VUN / 256;
-    constexpr int KLD = D + kKPad, VLD = kBN + kVPad;
-    static_assert(KCH % 256 == 0 && VUN % 256 == 0, "block shape");
+    constexpr int VPT = KPT;
+    constexpr int KLD = D + kKPad;
+    static_assert(KCH % 256 == 0, "block shape");
     __shared__ __align__(16) uint16_t sk[kBN * KLD];
-    __shared__ __align__(16) uint16_t sv[D * VLD];
+    __shared__ __align__(16) uint16_t sv[kBN * KLD];  // V row-major, like K
     __shared__ __align__(16) uint16_t sq[kBM * KLD];
 
     // XCD-aware order: the dispatcher sends workgroup L to XCD L % 8, so
@@ -118,7 +117,7 @@ __global__ __launch_bounds__(256, 2) void fr_attn_block_bf16(const uint16_t* __r
     }
 
     // the next block's K chunks and V units, in registers
-    f32x4 kr[KPT], vr[VPT][2];
+    f32x4 kr[KPT], vr[VPT];
     // loads of the next block; only a block that crosses the end of the keys
     // checks each row (the branch is the same for the whole workgroup)
     auto fetch = [&](int jb) {
@@ -127,12 +126,7 @@ __global__ __launch_bounds__(256, 2) void fr_attn_block_bf16(const uint16_t* __r
             for (int r = 0; r < KPT; ++r) {
                 const int c = tid + 256 * r, j = jb * kBN + c / (D / 8), oc = c % (D / 8);
                 kr[r] = ld16g(k + (kv0 + j) * D + 8 * oc);
-            }
-#pragma unroll
-            for (int r = 0; r < VPT; ++r) {
-                const int u = tid + 256 * r, j = jb * kBN + 2 * (u % (kBN / 2)), oc = u / (kBN / 2);
-                vr[r][0] = ld16g(v + (kv0 + j) * D + 8 * oc);
-                vr[r][1] = ld16g(v + (kv0 + j + 1) * D + 8 * oc);
+                vr[r] = ld16g(v + (kv0 + j) * D + 8 * oc);
             }
             return;
         }
@@ -140,12 +134,7 @@ __global__ __launch_bounds__(256, 2) void fr_attn_block_bf16(const uint16_t* __r
         for (int r = 0; r < KPT; ++r) {
             const int c = tid + 256 * r, j = jb * kBN + c / (D / 8), oc = c % (D / 8);
             kr[r] = j < Nk ? ld16g(k + (kv0 + j) * D + 8 * oc) : f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-#pragma unroll
-        for (int r = 0; r < VPT; ++r) {
-            const int u = tid + 256 * r, j = jb * kBN + 2 * (u % (kBN / 2)), oc = u / (kBN / 2);
-            vr[r][0] = j < Nk ? ld16g(v + (kv0 + j) * D + 8 * oc) : f32x4{0.f, 0.f, 0.f, 0.f};
-            vr[r][1] = j + 1 < Nk ? ld16g(v + (kv0 + j + 1) * D + 8 * oc) : f32x4{0.f, 0.f, 0.f, 0.f};
+            vr[r] = j < Nk ? ld16g(v + (kv0 + j) * D + 8 * oc) : f32x4{0.f, 0.f, 0.f, 0.f};
         }
     };
     auto stage = [&]() {
@@ -153,18 +142,7 @@ __global__ __launch_bounds__(256, 2) void fr_attn_block_bf16(const uint16_t* __r
         for (int r = 0; r < KPT; ++r) {
             const int c = tid + 256 * r, j = c / (D / 8), oc = c % (D / 8);
             *reinterpret_cast<f32x4*>(&sk[j * KLD + 8 * oc]) = kr[r];
-        }
-#pragma unroll
-        for (int r = 0; r < VPT; ++r) {
-            const int u = tid + 256 * r, j = 2 * (u % (kBN / 2)), oc = u / (kBN / 2);
-            const uint32_t* a0 = reinterpret_cast<const uint32_t*>(&vr[r][0]);
-            const uint32_t* a1 = reinterpret_cast<const uint32_t*>(&vr[r][1]);
-            // element e of keys j and j + 1 as one word: one byte permute
-            // (low halves: bytes 0, 1 of each word; high halves: bytes 2, 3)
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                *reinterpret_cast<uint32_t*>(&sv[(8 * oc + e) * VLD + j]) =
-                    __builtin_amdgcn_perm(a1[e >> 1], a0[e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
+            *reinterpret_cast<f32x4*>(&sv[j * KLD + 8 * oc]) = vr[r];
         }
     };
 
@@ -278,9 +256,13 @@ __global__ __launch_bounds__(256, 2) void fr_attn_block_bf16(const uint16_t* __r
             }
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
-                const uint16_t* row = &sv[(16 * t + n) * VLD + 32 * kk + 4 * g];
-                const short4v v0 = *reinterpret_cast<const short4v*>(row);
-                const short4v v1 = *reinterpret_cast<const short4v*>(row + 16);
+                // transposing reads of the row-major V tile: lane p of lane
+                // group g points at key 32 kk + 4 g + p / 4 (+ 16), dims
+                // 16 t + 4 (p % 4) .. +3; lane n then receives dim 16 t + n
+                // of the 4 keys
+                const uint16_t* row = &sv[(32 * kk + 4 * g + (n >> 2)) * KLD + 16 * t + 4 * (n & 3)];
+                const short4v v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4p)row);
+                const short4v v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4p)(row + 16 * KLD));
                 const f32x4 bv = __builtin_bit_cast(
                     f32x4, (short __attribute__((ext_vector_type(8)))){v0[0], v0[1], v0[2], v0[3], v1[0], v1[1],
                                                                         v1[2], v1[3]});
