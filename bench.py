@@ -5,7 +5,8 @@
 A step is one pass of the whole operation over one batch of synthetic input
 already resident in HBM. The default workload is the row softmax over
 4096 x 1024 fp32 (the headline configuration). The other workloads are
-selected with --workload: Example 1.1 sums, LayerNorm 2048 x 32768 bf16, the
+selected with --workload: Example 1.1 sums, the softmax at 65536 rows and
+Example 1.1 at 2^20 rows (the largest shapes), LayerNorm 2048 x 32768 bf16, the
 2^28 sum of squares, the ragged 512-row softmax, decode and tiled attention,
 softmax and LayerNorm backward, x.t() + y, GELU backward, a recorded region
 of 16 Example 1.1 launches, and streaming references (copy, read). Tiled
@@ -94,8 +95,10 @@ def make_workload(name, torch, fr, synth):
     def d(a):
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
-    if name == "softmax":
-        rows, cols = 4096, 1024
+    if name in ("softmax", "softmax_large"):
+        # the headline 4096 x 1024, or the same distribution at 65536 rows
+        # (256 MiB in, 256 MiB out): the largest shape of the row sweep
+        rows, cols = (4096, 1024) if name == "softmax" else (65536, 1024)
         x_host = synth.softmax_inputs(rows, cols, seed=2001)
         per_set = 2 * rows * cols * 4
 
@@ -119,19 +122,25 @@ def make_workload(name, torch, fr, synth):
 
             def config(self):
                 p = fr.fr_plan_query(fr.FR_OP_SOFTMAX, rows, cols)
-                return {"workload": "row softmax 4096x1024 fp32, x ~ N(0,1)*4 with 1% entries +/-30",
+                return {"workload": f"row softmax {rows}x{cols} fp32, x ~ N(0,1)*4 with 1% entries +/-30",
                         "rows": rows, "cols": cols, "form": fr.FORM_NAMES[p.form],
                         "launch": {"threads": p.threads, "lanes_per_row": p.seg, "vec16_per_lane": p.vec,
                                    "grid": p.grid}}
 
             def oracle_fn(self):
                 import oracle
-                return lambda: oracle.softmax_rows(x_host), self.bytes, "full 4096x1024 batch"
+                if rows == 4096:
+                    return lambda: oracle.softmax_rows(x_host), self.bytes, "full 4096x1024 batch"
+                r = 4096
+                return (lambda: oracle.softmax_rows(x_host[:r]), softmax_bytes(r, cols),
+                        f"first {r} of {rows} rows")
 
         return W(), per_set
 
-    if name == "sum_relu_add":
-        rows, cols = 64, 128
+    if name in ("sum_relu_add", "sum_relu_add_large"):
+        # Example 1.1 at 64 x 128 (latency-bound), or 2^20 rows of 128
+        # (1 GiB read): the largest shape of the row sweep
+        rows, cols = (64, 128) if name == "sum_relu_add" else (1 << 20, 128)
         a_h, b_h, _ = synth.sum_relu_add_inputs(rows, cols, seed=1001)
         per_set = sum_relu_add_bytes(rows, cols)
 
@@ -152,12 +161,17 @@ def make_workload(name, torch, fr, synth):
                 return self.args[k][2]
 
             def config(self):
-                return {"workload": "Example 1.1 sum_r 2*relu(a+b), fp32 [64,128] (latency-bound)",
+                return {"workload": f"Example 1.1 sum_r 2*relu(a+b), fp32 [{rows},{cols}]"
+                                    + (" (latency-bound)" if rows == 64 else ""),
                         "rows": rows, "cols": cols, "form": "per"}
 
             def oracle_fn(self):
                 import oracle
-                return lambda: oracle.sum_relu_add(a_h, b_h), self.bytes, "full 64x128 batch"
+                if rows == 64:
+                    return lambda: oracle.sum_relu_add(a_h, b_h), self.bytes, "full 64x128 batch"
+                r = 1 << 17
+                return (lambda: oracle.sum_relu_add(a_h[:r], b_h[:r]), sum_relu_add_bytes(r, cols),
+                        f"first {r} of {rows} rows")
 
         return W(), per_set
 
@@ -702,8 +716,8 @@ def main():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="softmax",
-                    choices=["softmax", "sum_relu_add", "layernorm", "sumsq", "ragged", "copy", "stream_copy",
-                             "stream_copy_c3", "stream_read", "attn_decode", "softmax_bwd", "add_2d",
+                    choices=["softmax", "softmax_large", "sum_relu_add", "sum_relu_add_large", "layernorm",
+                             "sumsq", "ragged", "copy", "stream_copy", "stream_copy_c3", "stream_read", "attn_decode", "softmax_bwd", "add_2d",
                              "gelu_bwd", "layernorm_bwd", "c1_region", "attn_block",
                              "attn_block_full"])
     ap.add_argument("--warm", action="store_true", help="one buffer set: reads may hit the MALL")
