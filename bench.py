@@ -428,6 +428,9 @@ def make_workload(name, torch, fr, synth):
                 fr.fr_layernorm_rows_stats(x0, torch.empty_like(x0), mean=mean, rstd=rstd, gamma=g, beta=bf(b_h))
                 nbytes = fr.fr_layernorm_rows_backward_workspace_bytes(rows, cols)
                 self.ws = torch.empty(nbytes // 4, dtype=torch.float32, device=dev)
+                self.plan = fr.fr_plan_query(fr.FR_OP_LAYERNORM_BWD, rows, cols, dtype=fr.FR_BF16, ws_bytes=nbytes)
+                self.kernel = ("fr_team_layernorm_bwd_bf16" if self.plan.form == fr.FR_FORM_SPLIT
+                               else "fr_per_layernorm_bwd_bf16")
                 self.g, self.mean, self.rstd = g, mean, rstd
                 self.dg = torch.empty(cols, dtype=torch.float32, device=dev)
                 self.db = torch.empty(cols, dtype=torch.float32, device=dev)
@@ -443,10 +446,12 @@ def make_workload(name, torch, fr, synth):
                 return self.args[k][2]
 
             def config(self):
-                p = fr.fr_plan_query(fr.FR_OP_LAYERNORM_BWD, rows, cols, dtype=fr.FR_BF16)
+                p = self.plan
+                split = p.form == fr.FR_FORM_SPLIT
                 return {"workload": "LayerNorm backward 2048x32768 bf16 (dx, dgamma, dbeta from saved mean/rstd; "
                                     "dy ~ N(0,1))", "rows": rows, "cols": cols, "threads": p.threads,
-                        "partial_rows": p.grid, "form": fr.FORM_NAMES[p.form]}
+                        "workgroups": p.grid, "workgroups_per_row": p.splits if split else 1,
+                        "partial_rows": p.grid // p.splits if split else p.grid, "form": fr.FORM_NAMES[p.form]}
 
             def oracle_fn(self):
                 import oracle

@@ -277,10 +277,15 @@ int fr_layernorm_rows_stats(const void* x, const void* gamma, const void* beta, 
  * g = dy[i,j] * gamma[j]:
  *   dx[i,j]   = rstd[i] * (g - (1/cols) sum_k g_k - xh * (1/cols) sum_k g_k xh_k)
  *   dgamma[j] = sum_i dy[i,j] * xh,        dbeta[j] = sum_i dy[i,j].
- * One workgroup holds a row of x and dy in registers: two fused row sums,
- * then dx. The dgamma / dbeta sums over rows are accumulated per workgroup
- * in registers, written as partial rows to the workspace and summed in a
- * fixed order by a second kernel (deterministic; no atomics).
+ * Persistent form: one workgroup holds a row of x and dy in registers: two
+ * fused row sums, then dx. Split form (rows of more than 8192 columns with
+ * 16-byte accesses, at least 256 rows, a workspace given, dx not aliasing x
+ * or dy): a team of up to 4 workgroups shares each row, each holding a part
+ * of it; the parts' row sums are exchanged through the workspace and added
+ * in part order, so every member uses the same bits. The dgamma / dbeta
+ * sums over rows are accumulated per workgroup (persistent) or per team
+ * (split) in registers, written as partial rows to the workspace and summed
+ * in a fixed order by a second kernel (deterministic; no atomics).
  *  x, dy, dx:     bf16 [rows, cols], strides as in the conventions; dx may be
  *                 x or dy (same row stride). dx is rounded to nearest even.
  *  gamma:         bf16 [cols] or NULL (1).
@@ -288,7 +293,10 @@ int fr_layernorm_rows_stats(const void* x, const void* gamma, const void* beta, 
  *  dgamma, dbeta: fp32 [cols] or NULL. When either is given, ws must hold
  *                 fr_layernorm_rows_backward_workspace_bytes(rows, cols)
  *                 bytes (16-byte aligned; FR_E_WORKSPACE otherwise); else ws
- *                 may be NULL.
+ *                 may be NULL (then the persistent form runs). That size
+ *                 serves every form. The workspace's contents are the
+ *                 library's during the call; calls that share one workspace
+ *                 must not overlap.
  * 1 <= cols <= 32768 (FR_E_SIZE otherwise). With dgamma or dbeta and more
  * than 16384 columns, x, dy, dx and gamma must allow 16-byte accesses (bases
  * and row strides multiples of 8 elements, cols a multiple of 8; FR_E_ALIGN

@@ -367,12 +367,18 @@ int fr_layernorm_rows_stats(const void* x, const void* gamma, const void* beta, 
 
 uint64_t fr_layernorm_rows_backward_workspace_bytes(int64_t rows, int64_t cols, int dtype) {
     if (dtype != FR_BF16 || check_sizes(rows, cols) != FR_OK || rows == 0 || cols == 0) return 0;
-    fr_plan plan;
-    // the workspace does not depend on alignment or the device
-    if (make_plan(FR_OP_LAYERNORM_BWD, rows, cols, FR_BF16, 256, 0, 0, 1, FR_FORM_AUTO,
-                  override_for(FR_OP_LAYERNORM_BWD, rows, cols, FR_BF16), &plan) != FR_OK)
-        return 0;
-    return plan.ws_bytes;
+    // enough for every form the call may take (split rows with 16-byte
+    // accesses, persistent rows otherwise or when dx aliases an input); it
+    // does not depend on alignment or the device
+    const fr_plan* ov = override_for(FR_OP_LAYERNORM_BWD, rows, cols, FR_BF16);
+    uint64_t need = 0;
+    for (int form : {FR_FORM_AUTO, FR_FORM_PER, FR_FORM_SPLIT}) {
+        fr_plan plan;
+        if (make_plan(FR_OP_LAYERNORM_BWD, rows, cols, FR_BF16, 256, 0, UINT64_MAX, 1, form, ov, &plan) == FR_OK &&
+            plan.ws_bytes > need)
+            need = plan.ws_bytes;
+    }
+    return need;
 }
 
 int fr_layernorm_rows_backward(const void* x, const void* dy, const void* gamma, const float* mean,
@@ -397,19 +403,28 @@ int fr_layernorm_rows_backward(const void* x, const void* dy, const void* gamma,
         return FR_E_ALIGN;
     const int v16 = cols % 8 == 0 && vec_ok(x, x_rs, 8) && vec_ok(dy, dy_rs, 8) && vec_ok(dx, dx_rs, 8) &&
                     vec_ok(gamma, 0, 8);
+    // split rows read a partner's part of x and dy when its sums are late:
+    // never while dx overwrites them
+    const bool alias = rows > 0 && (dx == x || dx == dy);
+    int forced = g_forced_form;
+    if (alias && forced == FR_FORM_AUTO) forced = FR_FORM_PER;
     fr_plan plan;
-    st = make_plan(FR_OP_LAYERNORM_BWD, rows, cols, FR_BF16, 256, 0, 0, v16, g_forced_form,
+    st = make_plan(FR_OP_LAYERNORM_BWD, rows, cols, FR_BF16, 256, 0, ws ? ws_bytes : 0, v16, forced,
                    override_for(FR_OP_LAYERNORM_BWD, rows, cols, FR_BF16), &plan);
     if (st != FR_OK) return st;
+    if (alias && plan.form == FR_FORM_SPLIT) return FR_E_ARG;
     const bool dg = dgamma || dbeta;
-    if (dg && plan.ws_bytes > 0 && (!ws || ws_bytes < plan.ws_bytes)) return FR_E_WORKSPACE;
+    if ((dg || plan.form == FR_FORM_SPLIT) && plan.ws_bytes > 0 && (!ws || ws_bytes < plan.ws_bytes))
+        return FR_E_WORKSPACE;
     // rows beyond 16384 columns with dgamma / dbeta need 16-byte accesses
     if (dg && !v16 && plan.threads * plan.vec > 1024 * 2) return FR_E_ALIGN;
-    int num_cus = 0;
-    st = device_check(&num_cus);
+    int num_cus = 0, clock_khz = 0;
+    st = device_check(&num_cus, &clock_khz);
     if (st != FR_OK) return st;
+    const int64_t wait_ticks = plan.wait_us > 0 ? (int64_t)plan.wait_us * clock_khz / 1000 : (plan.wait_us < 0 ? -1 : 0);
     LayerNormBwdArgs args{(const uint16_t*)x, (const uint16_t*)dy, (const uint16_t*)gamma, mean, rstd,
-                          (uint16_t*)dx, dgamma, dbeta, (float*)ws, (int)rows, (int)cols, x_rs, dy_rs, dx_rs};
+                          (uint16_t*)dx, dgamma, dbeta, (float*)ws, (int)rows, (int)cols, x_rs, dy_rs, dx_rs,
+                          wait_ticks};
     (void)hipGetLastError();
     return finish_launch(launch_layernorm_bwd(plan, args, (hipStream_t)stream));
 }

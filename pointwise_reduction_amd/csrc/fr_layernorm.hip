@@ -96,7 +96,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* p, uint32
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, kBufferRsrcWord3);
 }
 __device__ __forceinline__ void hide(u32x4& v) { asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w)); }
-constexpr int kAuxNT = 2;  // buffer instruction cache policy: non-temporal
+constexpr int kAuxNT = 2;    // buffer instruction cache policy: non-temporal
+constexpr int kAuxSc1 = 16;  // buffer instruction cache policy: sc1 (coherent across the compute dies)
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // y = affine of the row held in v, through buffer resources; gamma and beta
 // are loaded in two halves so that only half of them is live at a time.
@@ -469,6 +471,308 @@ __global__ __launch_bounds__(T) void fr_per_layernorm_bwd_bf16(const uint16_t* x
     }
 }
 
+// ---- rows split across a team of P workgroups of 1024 threads. Member p of
+// team k holds columns [p W, p W + W) of rows k, k + K, k + 2K, ... (K
+// teams), one vector of 8 bf16 per lane and array. Each member forms the two
+// row sums over its part and publishes them in the workspace; every member
+// adds the P parts in part order, so all of them use the same bits. The
+// dgamma / dbeta partials are then per team (K partial rows, not one per
+// workgroup), which cuts the partial traffic by the team size.
+// A member works in steps of R rows and keeps NB = DL + 1 steps in
+// registers. Step s issues the loads of step s + DL, forms and publishes the
+// sums of step s + DL - 1 (one workgroup fold for all R rows) and finishes
+// step s, whose partner sums were published DL - 1 steps earlier and whose
+// slot words were loaded one step ahead: loads and exchange are in flight
+// while other rows are worked on.
+// A partner sum still missing after wait_ticks is computed from x and dy by
+// the waiting member with the partner's lane mapping and reduction tree,
+// which gives the partner's bits (so dx must not alias x or dy here; the
+// launcher never picks this form then). Every wait ends, and the result does
+// not depend on which members are resident. Slots: 16 bytes per (row, part),
+// words (row | a) and (row | b), set to "unpublished" by fr_ln_team_reset.
+constexpr uint32_t kLnUnpublished = 0xFFFFFFFFu;
+constexpr int kLnTeamT = 1024;
+constexpr int kLnTeamW = kLnTeamT / kWave;
+
+__global__ __launch_bounds__(256) void fr_ln_team_reset(uint32_t* __restrict__ hdr, u32x4* __restrict__ slots,
+                                                        int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < kLnTeamHeader / 4) hdr[i] = 0u;
+    if (i < n) slots[i] = u32x4{~0u, ~0u, ~0u, ~0u};
+}
+
+__device__ __forceinline__ uint64_t ln_slot_word(int row, float v) {
+    return ((uint64_t)(uint32_t)row << 32) | __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ bool ln_published(uint64_t w) { return (uint32_t)(w >> 32) != kLnUnpublished; }
+
+// this lane's contribution to the two sums of one part of a row
+__device__ __forceinline__ void ln_lane_sums(u32x4 xv, u32x4 dv, u32x4 gv, float mu, float rs, float& a, float& b) {
+    a = 0.f;
+    b = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float xh = (lane8(xv, e) - mu) * rs;
+        const float g = lane8(dv, e) * lane8(gv, e);
+        a += g;
+        b += g * xh;
+    }
+}
+
+// N values reduced over the workgroup: wave butterflies, then the waves in
+// order through f[kLnTeamW][N]; every thread returns the N totals
+template <int N>
+__device__ __forceinline__ void ln_fold(float (&v)[N], float (*f)[N]) {
+#pragma unroll
+    for (int k = 0; k < N; ++k) v[k] = group_reduce<kWave>(v[k], OpSum());
+    const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+    if (lane == 0)
+#pragma unroll
+        for (int k = 0; k < N; ++k) f[w][k] = v[k];
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+        float r = f[0][k];
+#pragma unroll
+        for (int u = 1; u < kLnTeamW; ++u) r += f[u][k];
+        v[k] = r;
+    }
+}
+
+template <int P, int R, int DL, bool DG>
+__global__ __launch_bounds__(kLnTeamT) void fr_team_layernorm_bwd_bf16(
+    const uint16_t* x, const uint16_t* dy, const uint16_t* __restrict__ gamma, const float* __restrict__ mean,
+    const float* __restrict__ rstd, uint16_t* dx, float* __restrict__ part, uint32_t* hdr, uint64_t* slots, int rows,
+    int cols, int W, int64_t x_rs, int64_t dy_rs, int64_t dx_rs, int64_t ldw, int64_t wait_ticks) {
+    constexpr int NB = DL + 1;
+    static_assert(P * R <= kWave, "one polling lane per (part, row)");
+    // workgroup folds: step s uses set s & 1 (two folds run back to back with
+    // only their own barrier between them at the pipeline's start); a
+    // recomputed partner sum uses sfb. Each value is reduced on its own, so
+    // a sum folded alone has the bits it has when folded with others.
+    __shared__ float sf[2][kLnTeamW][2 * R];
+    __shared__ float sfb[kLnTeamW][2];
+    // the member's own sums of each step in flight, by register buffer
+    __shared__ float own[NB][2 * R];
+    // exchange results by step parity: a step's writes are separated from
+    // the reads two steps earlier by the barrier of the step between
+    __shared__ float ex[2][P][2 * R];
+    __shared__ uint32_t s_miss[2];
+    const int tid = threadIdx.x;
+    const int K = gridDim.x / P;
+    const int team = blockIdx.x / P, p = blockIdx.x % P;
+    const int c0 = p * W;
+    const uint32_t pbytes = (uint32_t)min(W, cols - c0) * 2u;
+    const int voff = tid * 16;
+    const int n = team < rows ? (rows - 1 - team) / K + 1 : 0;  // rows of this team
+    const int ns = (n + R - 1) / R;                               // steps
+    const float fn = (float)cols;
+    const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+    auto gamma_of = [&](int q) __attribute__((always_inline)) {
+        return gamma ? __builtin_amdgcn_raw_buffer_load_b128(
+                           row_rsrc(gamma + q * W, (uint32_t)min(W, cols - q * W) * 2u), voff, 0, 0)
+                     : ones;
+    };
+    const u32x4 gv = gamma_of(p);
+    u32x4 xb[NB][R], db[NB][R];
+    float mub[NB][R], rsb[NB][R];
+    float ag[8], ab[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ag[e] = ab[e] = 0.f;
+
+    // Every step issues the same memory instructions whether or not its rows
+    // exist (a row past the team's end loads and stores through an empty
+    // range: zeros, no memory access), and no memory instruction of the
+    // common path sits under a branch, so the compiler's waits for older
+    // loads count the newer ones exactly instead of waiting for all of them
+    // (the rare paths drain the counter before they rejoin).
+    auto load = [&](int st, int bi) __attribute__((always_inline)) {
+#pragma unroll
+        for (int t = 0; t < R; ++t) {
+            const int i = st * R + t;
+            const bool live = i < n;
+            const int r = team + (live ? i : 0) * K;  // n >= 1: row `team` exists
+            const uint32_t nb = live ? pbytes : 0u;
+            xb[bi][t] =
+                __builtin_amdgcn_raw_buffer_load_b128(row_rsrc(x + (int64_t)r * x_rs + c0, nb), voff, 0, kAuxNT);
+            db[bi][t] =
+                __builtin_amdgcn_raw_buffer_load_b128(row_rsrc(dy + (int64_t)r * dy_rs + c0, nb), voff, 0, kAuxNT);
+            mub[bi][t] = live ? mean[r] : 0.f;
+            rsb[bi][t] = live ? rstd[r] : 0.f;
+        }
+    };
+    auto sums = [&](int st, int bi) __attribute__((always_inline)) {
+        float v[2 * R];
+#pragma unroll
+        for (int t = 0; t < R; ++t) ln_lane_sums(xb[bi][t], db[bi][t], gv, mub[bi][t], rsb[bi][t], v[2 * t], v[2 * t + 1]);
+        // finish unpacks the rows again rather than keeping fp32 copies of
+        // them alive across the steps between
+#pragma unroll
+        for (int t = 0; t < R; ++t) {
+            hide(xb[bi][t]);
+            hide(db[bi][t]);
+        }
+        ln_fold<2 * R>(v, sf[st & 1]);
+#pragma unroll
+        for (int t = 0; t < R; ++t) {
+            if (tid == 0) {
+                own[bi][2 * t] = v[2 * t];
+                own[bi][2 * t + 1] = v[2 * t + 1];
+            }
+            // one store instruction for every lane, no branch: the slot's
+            // range admits lanes 0 and 1 (its two words); the others, and
+            // every lane for a row past the team's end, fall outside it and
+            // write nothing. sc1: visible to the other compute dies.
+            const int i = st * R + t;
+            const int r = team + i * K;
+            const uint64_t word = ln_slot_word(r, tid & 1 ? v[2 * t + 1] : v[2 * t]);
+            __builtin_amdgcn_raw_buffer_store_b64(
+                u32x2{(uint32_t)word, (uint32_t)(word >> 32)},
+                __builtin_amdgcn_make_buffer_rsrc(slots + 2 * ((int64_t)(i < n ? r : 0) * P + p), 0, i < n ? 16 : 0,
+                                                  kBufferRsrcWord3),
+                min(tid, 2) * 8, 0, kAuxSc1);
+        }
+    };
+    // wave 0, lane l = q + P t < P R: the slot of part q of row t of the
+    // step. Partners' words are loaded one step ahead.
+    const int lq = tid % P, lt = tid / P;
+    // One load instruction for every lane of every wave, no branch: lane
+    // q + P t < P R reads slot (row t of the step, part q); the others point
+    // past the slots' range and read zeros without a memory access. The
+    // words are looked at only in the next finish.
+    const int slot_bytes = rows * P * 16;  // < 2^31 (the planner's bound)
+    const __amdgpu_buffer_rsrc_t rslots = __builtin_amdgcn_make_buffer_rsrc(slots, 0, slot_bytes, kBufferRsrcWord3);
+    uint64_t pw0 = ~0ull, pw1 = ~0ull;
+    auto poll_ahead = [&](int st) __attribute__((always_inline)) {
+        const int i = st * R + lt;
+        const bool use = tid < P * R && i < n;
+        const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(
+            rslots, use ? ((team + i * K) * P + lq) * 16 : slot_bytes, 0, kAuxSc1);
+        pw0 = ((uint64_t)w.y << 32) | w.x;
+        pw1 = ((uint64_t)w.w << 32) | w.z;
+    };
+    auto finish = [&](int st, int bi) __attribute__((always_inline)) {
+        float(*e)[2 * R] = ex[st & 1];
+        if (tid < kWave) {
+            const int i = st * R + lt;
+            uint64_t w0 = pw0, w1 = pw1;
+            // own part and rows past the team's end need no slot; with no
+            // wait (wait_ticks < 0) every partner's sums are recomputed
+            const bool need = tid < P * R && i < n && lq != p;
+            bool ok = !need || (wait_ticks >= 0 && ln_published(w0) && ln_published(w1));
+            const uint64_t* ws = slots + 2 * ((int64_t)(team + i * K) * P + lq);
+            if (!__all(ok) && wait_ticks >= 0) {  // < 0: read no partner's slot (all are recomputed)
+                const uint64_t t0 = wall_clock64();
+                for (;;) {
+                    if ((int64_t)(wall_clock64() - t0) >= wait_ticks) break;
+                    __builtin_amdgcn_s_sleep(2);
+                    if (!ok) {
+                        if (!ln_published(w0))
+                            w0 = __hip_atomic_load(&ws[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        if (!ln_published(w1))
+                            w1 = __hip_atomic_load(&ws[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        ok = ln_published(w0) && ln_published(w1);
+                    }
+                    if (__all(ok)) break;
+                }
+            }
+            const uint64_t miss = __ballot(!ok);
+            if (tid < P * R && lq != p && i < n && ok) {
+                e[lq][2 * lt] = __builtin_bit_cast(float, (uint32_t)w0);
+                e[lq][2 * lt + 1] = __builtin_bit_cast(float, (uint32_t)w1);
+            }
+            if (tid == 0) s_miss[st & 1] = (uint32_t)miss;
+        }
+        __syncthreads();
+        const uint32_t miss = s_miss[st & 1];
+#pragma unroll
+        for (int l = 0; l < P * R; ++l) {
+            if (!(miss >> l & 1u)) continue;  // rare: a partner has not published in time
+            const int q = l % P, t = l / P;
+            const int r = team + (st * R + t) * K;
+            const uint32_t qb = (uint32_t)min(W, cols - q * W) * 2u;
+            const u32x4 xq =
+                __builtin_amdgcn_raw_buffer_load_b128(row_rsrc(x + (int64_t)r * x_rs + q * W, qb), voff, 0, 0);
+            const u32x4 dq =
+                __builtin_amdgcn_raw_buffer_load_b128(row_rsrc(dy + (int64_t)r * dy_rs + q * W, qb), voff, 0, 0);
+            float v[2];
+            ln_lane_sums(xq, dq, gamma_of(q), mub[bi][t], rsb[bi][t], v[0], v[1]);
+            ln_fold<2>(v, sfb);
+            if (tid == 0) {
+                e[q][2 * t] = v[0];
+                e[q][2 * t + 1] = v[1];
+                __hip_atomic_fetch_add(&hdr[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
+#pragma unroll
+        for (int t = 0; t < R; ++t) {
+            // a row past the team's end (last step) holds zeros: it adds
+            // nothing to the column sums and its store has an empty range
+            const int i = st * R + t;
+            const bool live = i < n;
+            const int r = team + (live ? i : 0) * K;
+            // part order; the member's own sums from its own slots
+            float a = p == 0 ? own[bi][2 * t] : e[0][2 * t], b = p == 0 ? own[bi][2 * t + 1] : e[0][2 * t + 1];
+#pragma unroll
+            for (int q = 1; q < P; ++q) {
+                a += q == p ? own[bi][2 * t] : e[q][2 * t];
+                b += q == p ? own[bi][2 * t + 1] : e[q][2 * t + 1];
+            }
+            const float m1 = a / fn, m2 = b / fn, mu = mub[bi][t], rs = rsb[bi][t];
+            uint32_t o[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                float vv[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int el = 2 * k + h;
+                    const float d = lane8(db[bi][t], el);
+                    const float xh = (lane8(xb[bi][t], el) - mu) * rs;
+                    const float g = d * lane8(gv, el);
+                    vv[h] = rs * ((g - m1) - xh * m2);
+                    if constexpr (DG) {
+                        ag[el] += d * xh;
+                        ab[el] += d;
+                    }
+                }
+                o[k] = pack_bf16(vv[0], vv[1]);
+            }
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4{o[0], o[1], o[2], o[3]},
+                                                   row_rsrc(dx + (int64_t)r * dx_rs + c0, live ? pbytes : 0u), voff,
+                                                   0, kAuxNT);
+        }
+        poll_ahead(st + 1);
+    };
+
+#pragma unroll
+    for (int u = 0; u < DL; ++u) load(u, u);
+#pragma unroll
+    for (int u = 0; u < DL - 1; ++u) sums(u, u);
+    poll_ahead(0);
+    for (int s0 = 0; s0 < ns; s0 += NB) {
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+            const int st = s0 + u;
+            if (st >= ns) break;
+            load(st + DL, (u + DL) % NB);
+            sums(st + DL - 1, (u + DL - 1) % NB);
+            finish(st, u);
+        }
+    }
+    if constexpr (DG) {
+        if (tid * 8 < (int)(pbytes / 2)) {
+            float* pg = part + (int64_t)team * ldw + c0 + tid * 8;
+            float* pbp = part + ((int64_t)K + team) * ldw + c0 + tid * 8;
+            st4<false>(pg, f32x4{ag[0], ag[1], ag[2], ag[3]});
+            st4<false>(pg + 4, f32x4{ag[4], ag[5], ag[6], ag[7]});
+            st4<false>(pbp, f32x4{ab[0], ab[1], ab[2], ab[3]});
+            st4<false>(pbp + 4, f32x4{ab[4], ab[5], ab[6], ab[7]});
+        }
+    }
+}
+
 // dgamma[j] = sum_g ws[0][g][j], dbeta[j] = sum_g ws[1][g][j]: 256 threads as
 // Q column quads x S slices; slice s sums partials g = s, s + S, ... in
 // order, then slice 0 adds the slices in order. Every run gives the same bits.
@@ -482,7 +786,7 @@ __global__ __launch_bounds__(Q * S) void fr_layernorm_bwd_fin(const float* __res
     const int j = (blockIdx.x * Q + q) * 4;
     f32x4 ag = {0.f, 0.f, 0.f, 0.f}, ab = {0.f, 0.f, 0.f, 0.f};
     if (j < cols) {
-#pragma unroll 4
+#pragma unroll 8
         for (int g = sl; g < G; g += S) {
             ag += ld4<true>(ws + (int64_t)g * ldw + j);
             ab += ld4<true>(ws + ((int64_t)G + g) * ldw + j);
@@ -596,15 +900,67 @@ LnBwdFn pick_bwd(int mask, int threads, int nv) {
 
 }  // namespace
 
+namespace {
+using LnTeamFn = void (*)(const uint16_t*, const uint16_t*, const uint16_t*, const float*, const float*, uint16_t*,
+                         float*, uint32_t*, uint64_t*, int, int, int, int64_t, int64_t, int64_t, int64_t, int64_t);
+
+#ifndef FR_LN_TEAM_DL
+#define FR_LN_TEAM_DL 3
+#endif
+#ifndef FR_LN_TEAM_R
+#define FR_LN_TEAM_R 1
+#endif
+#ifndef FR_LN_FIN_Q
+#define FR_LN_FIN_Q 32
+#endif
+template <bool DG>
+LnTeamFn pick_team(int parts) {
+    constexpr int DL = FR_LN_TEAM_DL, R = FR_LN_TEAM_R;
+    switch (parts) {
+        case 2: return fr_team_layernorm_bwd_bf16<2, R, DL, DG>;
+        case 3: return fr_team_layernorm_bwd_bf16<3, R, DL, DG>;
+        case 4: return fr_team_layernorm_bwd_bf16<4, R, DL, DG>;
+    }
+    return nullptr;
+}
+}  // namespace
+
 hipError_t launch_layernorm_bwd(const fr_plan& p, const LayerNormBwdArgs& a, hipStream_t s) {
     const bool vec = p.vec16 != 0;
     const bool dg = a.dgamma || a.dbeta;
+    constexpr int Q = 8, S = 32;
+    const int64_t ldw = ln_bwd_ldw(a.cols);
+    const int64_t grid2 = (a.cols + 4 * Q - 1) / (4 * Q);
+    if (p.form == FR_FORM_SPLIT) {
+        // reset of the exchange slots, the team kernel, the column sums
+        const int parts = p.splits;
+        LnTeamFn f = dg ? pick_team<true>(parts) : pick_team<false>(parts);
+        if (!f || !vec || a.rows < 1 || p.grid % parts) return hipErrorInvalidDeviceFunction;
+        char* base = reinterpret_cast<char*>(a.ws);
+        uint32_t* hdr = reinterpret_cast<uint32_t*>(base);
+        u32x4* slots = reinterpret_cast<u32x4*>(base + kLnTeamHeader);
+        float* part = reinterpret_cast<float*>(base + kLnTeamHeader + ln_team_slots_bytes(a.rows, parts));
+        const int64_t nslots = (int64_t)a.rows * parts;
+        const int64_t nreset = nslots > kLnTeamHeader / 4 ? nslots : kLnTeamHeader / 4;
+        hipLaunchKernelGGL(fr_ln_team_reset, dim3((unsigned)((nreset + 255) / 256)), dim3(256), 0, s, hdr, slots,
+                           nslots);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(f, dim3((unsigned)p.grid), dim3(kLnTeamT), 0, s, a.x, a.dy, a.gamma, a.mean, a.rstd, a.dx,
+                           part, hdr, reinterpret_cast<uint64_t*>(slots), a.rows, a.cols, p.chunk, a.x_rs, a.dy_rs,
+                           a.dx_rs, ldw, a.wait_ticks);
+        e = hipGetLastError();
+        if (e != hipSuccess || !dg) return e;
+        constexpr int TQ = FR_LN_FIN_Q, TS = 256 / TQ;
+        hipLaunchKernelGGL((fr_layernorm_bwd_fin<TQ, TS>), dim3((unsigned)((a.cols + 4 * TQ - 1) / (4 * TQ))),
+                           dim3(256), 0, s, part, a.dgamma, a.dbeta, (int)(p.grid / parts), a.cols, ldw);
+        return hipGetLastError();
+    }
     const int mask = !vec ? kScalar : (a.cols == 8 * p.threads * p.vec ? kNone : kVec);
     LnBwdFn f = p.form == FR_FORM_PER ? (dg ? pick_bwd<true>(mask, p.threads, p.vec)
                                              : pick_bwd<false>(mask, p.threads, p.vec))
                                       : nullptr;
     if (!f) return hipErrorInvalidDeviceFunction;
-    const int64_t ldw = ln_bwd_ldw(a.cols);
     if (a.rows > 0) {
         hipLaunchKernelGGL(f, dim3((unsigned)p.grid), dim3(p.threads), 0, s, a.x, a.dy, a.gamma, a.mean, a.rstd,
                            a.dx, a.ws, a.rows, a.cols, a.x_rs, a.dy_rs, a.dx_rs, ldw);
@@ -612,8 +968,6 @@ hipError_t launch_layernorm_bwd(const fr_plan& p, const LayerNormBwdArgs& a, hip
         if (e != hipSuccess) return e;
     }
     if (!dg) return hipSuccess;
-    constexpr int Q = 8, S = 32;
-    const int64_t grid2 = (a.cols + 4 * Q - 1) / (4 * Q);
     hipLaunchKernelGGL((fr_layernorm_bwd_fin<Q, S>), dim3((unsigned)grid2), dim3(Q * S), 0, s, a.ws, a.dgamma,
                        a.dbeta, (int)p.grid, a.cols, ldw);
     return hipGetLastError();

@@ -80,6 +80,10 @@ struct Knobs {
 // workgroup computes a missing partial itself.
 constexpr int kOnePassWavesPerSimd = 5;
 constexpr int kOnePassWaitUs = 200;
+// Split-row LayerNorm backward: the default wait for a partner's row sums,
+// and the fewest rows for which the automatic choice takes that form.
+constexpr int kLnTeamWaitUs = 200;
+constexpr int64_t kLnTeamMinRows = 256;
 
 // Persistent fp32 geometry: the smallest lane group (8..64 lanes) whose
 // 16-byte vectors cover the row with at most 8 vectors per lane.
@@ -141,6 +145,22 @@ int finalize_plan(int op, int64_t rows, int64_t cols, const Knobs& k, fr_plan* p
     }
     if (k.form == FR_FORM_RED) {
         p->grid = min64(rows, kMaxGrid);
+        return FR_OK;
+    }
+    if (k.form == FR_FORM_SPLIT && op == FR_OP_LAYERNORM_BWD) {
+        // a team of P workgroups per row, one 16-byte vector per lane and
+        // member; as many teams as fill the device, at most one per row
+        if (rows < 1 || cols <= kLnTeamPartCols || cols > 4 * kLnTeamPartCols) return FR_E_ARG;
+        const int64_t parts = cdiv(cols, kLnTeamPartCols);
+        if (rows * parts * 16 >= (int64_t(1) << 31)) return FR_E_ARG;  // slot offsets are 32-bit
+        const int64_t teams = min64(rows, std::max<int64_t>(1, kLnBwdWgs1024 / parts));
+        p->threads = 1024;
+        p->vec = 1;
+        p->splits = (int)parts;
+        p->chunk = (int)(cdiv(cdiv(cols, parts), 8) * 8);
+        p->grid = teams * parts;
+        p->ws_bytes = (uint64_t)(kLnTeamHeader + ln_team_slots_bytes(rows, parts) + 2 * teams * ln_bwd_ldw(cols) * 4);
+        p->wait_us = k.wait_us == 0 ? kLnTeamWaitUs : k.wait_us;
         return FR_OK;
     }
     if (k.form == FR_FORM_SPLIT) {
@@ -320,11 +340,26 @@ int make_plan(int op, int64_t rows, int64_t cols, int dtype, int num_cus, int ha
             break;
         }
         case FR_OP_LAYERNORM_BWD: {
-            // persistent only: a workgroup holds the rows of x and dy, and
-            // each lane the dgamma / dbeta partials of its columns, in
-            // registers (at most 4 vectors of 8 bf16 per lane and array)
+            // persistent: a workgroup holds the rows of x and dy, and each
+            // lane the dgamma / dbeta partials of its columns, in registers
+            // (at most 4 vectors of 8 bf16 per lane and array). Split: rows
+            // longer than one member's part, shared by a team of workgroups,
+            // when the accesses are 16-byte and the workspace holds the
+            // exchange slots (automatic from kLnTeamMinRows rows on).
             if (dtype != FR_BF16) return FR_E_DTYPE;
             if (cols < 1 || cols > kLnBwdMaxCols) return FR_E_SIZE;
+            if (forced == FR_FORM_SPLIT || forced == FR_FORM_AUTO) {
+                Knobs t;
+                t.form = FR_FORM_SPLIT;
+                fr_plan tp;
+                clear(&tp, op);
+                const bool fits = aligned16 && finalize_plan(op, rows, cols, t, &tp) == FR_OK && ws_bytes >= tp.ws_bytes;
+                if (forced == FR_FORM_SPLIT || (fits && rows >= kLnTeamMinRows)) {
+                    if (!aligned16 || rows < 1) return FR_E_ARG;
+                    k = t;
+                    break;
+                }
+            }
             if (forced != FR_FORM_AUTO && forced != FR_FORM_PER) return FR_E_ARG;
             const int q = (int)cdiv(cols, 8);
             const int t = std::min(1024, std::max(128, pow2_ceil(q)));
@@ -354,7 +389,8 @@ int make_plan(int op, int64_t rows, int64_t cols, int dtype, int num_cus, int ha
     k.num_cus = num_cus;
     const int st = finalize_plan(op, rows, cols, k, p);
     if (st != FR_OK) return st;
-    if (p->form == FR_FORM_SPLIT && ws_bytes < p->ws_bytes) return override_plan ? FR_E_WORKSPACE : FR_E_ARG;
+    if (p->form == FR_FORM_SPLIT && ws_bytes < p->ws_bytes)
+        return (override_plan || op == FR_OP_LAYERNORM_BWD) ? FR_E_WORKSPACE : FR_E_ARG;
     return FR_OK;
 }
 

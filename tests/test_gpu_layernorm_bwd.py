@@ -139,13 +139,105 @@ def test_layernorm_stats_output(shape):
 
 
 def test_layernorm_backward_full_size():
-    # 2048 x 32768 bf16 with gamma: the benchmark's launch. Column sums over
-    # all rows against the oracle; dx on sampled rows.
+    # 2048 x 32768 bf16 with gamma: the benchmark's launch (split rows, a
+    # team of 4 workgroups per row). Every output against the oracle.
     rows, cols = 2048, 32768
     x, dy, g, mean, rstd = inputs(rows, cols, seed=3001)
     got = run_bwd(x, dy, g, mean, rstd)
     ref = oracle.layernorm_backward_rows(x, dy, g, mean.astype(np.float64), rstd.astype(np.float64))
     check_fp32(got["dgamma"], ref["dgamma64"], terms=ref["gmag"], what="full dgamma")
     check_fp32(got["dbeta"], ref["dbeta64"], terms=ref["bmag"], what="full dbeta")
-    rs = np.array([0, 1, 255, 256, 1023, 2047])
-    check_bf16(got["dx"][rs], oracle.round_bf16(ref["dx64"][rs]), ref["dx64"][rs], ref["dxmag"][rs], what="full dx")
+    check_bf16(got["dx"], oracle.round_bf16(ref["dx64"]), ref["dx64"], ref["dxmag"], what="full dx")
+    # the persistent form on the same inputs (dx overwrites dy: no split)
+    got2 = run_bwd(x, dy, g, mean, rstd, inplace=True)
+    check_bf16(got2["dx"], oracle.round_bf16(ref["dx64"]), ref["dx64"], ref["dxmag"], what="full dx, persistent")
+    check_fp32(got2["dgamma"], ref["dgamma64"], terms=ref["gmag"], what="full dgamma, persistent")
+
+
+# ---- split rows: a team of workgroups per row (rows longer than 8192 columns)
+
+def team_ws(rows, cols):
+    n = fr.fr_layernorm_rows_backward_workspace_bytes(rows, cols)
+    return torch.zeros(n // 4, dtype=torch.float32, device="cuda")
+
+
+@pytest.mark.parametrize("shape", [(1, 8200), (3, 16384), (7, 20000), (5, 24576), (9, 32768), (300, 16392),
+                                   (257, 32768)])
+def test_layernorm_backward_split_rows(shape):
+    # forced split form: 2, 3 and 4 parts, a narrower last part, fewer rows
+    # than teams and more, with and without gamma and the column sums
+    x, dy, g, mean, rstd = inputs(*shape, seed=shape[0] * 7 + shape[1])
+    fr.fr_force_form(fr.FR_FORM_SPLIT)
+    try:
+        p = fr.fr_plan_query(fr.FR_OP_LAYERNORM_BWD, *shape, dtype=fr.FR_BF16, ws_bytes=1 << 40)
+        assert p.form == fr.FR_FORM_SPLIT and p.splits == -(-shape[1] // 8192)
+        compare(x, dy, g, mean, rstd, run_bwd(x, dy, g, mean, rstd, ws=team_ws(*shape)), what=f"split {shape}")
+        compare(x, dy, None, mean, rstd, run_bwd(x, dy, None, mean, rstd, ws=team_ws(*shape)),
+                what=f"split no gamma {shape}")
+        compare(x, dy, g, mean, rstd, run_bwd(x, dy, g, mean, rstd, want_dg=False, ws=team_ws(*shape)),
+                what=f"split dx only {shape}")
+    finally:
+        fr.fr_force_form(fr.FR_FORM_AUTO)
+
+
+def test_layernorm_backward_split_rows_recomputed_partner_sums():
+    # with no wait every partner's row sums are recomputed by the waiting
+    # workgroup: the same bits as the exchanged ones, and the workspace
+    # header counts them (rows x parts x (parts - 1))
+    rows, cols = 300, 32768
+    x, dy, g, mean, rstd = inputs(rows, cols, seed=23)
+    ws = team_ws(rows, cols)
+    fr.fr_force_form(fr.FR_FORM_SPLIT)
+    try:
+        a = run_bwd(x, dy, g, mean, rstd, ws=ws)
+        assert int(ws[:1].view(torch.int32).item()) == 0
+        fr.fr_tune_override(fr.FR_OP_LAYERNORM_BWD, form=fr.FR_FORM_SPLIT, threads=1024, vec=1, wait_us=-1)
+        try:
+            b = run_bwd(x, dy, g, mean, rstd, ws=ws)
+        finally:
+            fr.fr_tune_override(fr.FR_OP_LAYERNORM_BWD)
+        assert int(ws[:1].view(torch.int32).item()) == rows * 4 * 3
+    finally:
+        fr.fr_force_form(fr.FR_FORM_AUTO)
+    for k in ("dx", "dgamma", "dbeta"):
+        assert np.array_equal(a[k], b[k]), k
+    compare(x, dy, g, mean, rstd, a, what="split 300x32768")
+
+
+def test_layernorm_backward_split_rows_choice_and_errors():
+    rows, cols = 256, 16384
+    x, dy, g, mean, rstd = inputs(rows, cols, seed=29)
+    ws = team_ws(rows, cols)
+    # automatic: split rows with a workspace and 16-byte accesses ...
+    p = fr.fr_plan_query(fr.FR_OP_LAYERNORM_BWD, rows, cols, dtype=fr.FR_BF16, ws_bytes=ws.numel() * 4)
+    assert (p.form, p.splits, p.chunk, p.grid) == (fr.FR_FORM_SPLIT, 2, 8192, 256)
+    a = run_bwd(x, dy, g, mean, rstd, ws=ws)
+    compare(x, dy, g, mean, rstd, a, what="auto split")
+    # ... persistent rows when dx overwrites an input, with the same workspace
+    b = run_bwd(x, dy, g, mean, rstd, ws=ws, inplace=True)
+    compare(x, dy, g, mean, rstd, b, what="in place")
+    # persistent rows without a workspace (dx only)
+    compare(x, dy, g, mean, rstd, run_bwd(x, dy, g, mean, rstd, want_dg=False), what="dx only, no workspace")
+    fr.fr_force_form(fr.FR_FORM_SPLIT)
+    try:
+        with pytest.raises(fr.FrError) as ei:  # split rows never write over x or dy
+            run_bwd(x, dy, g, mean, rstd, ws=ws, inplace=True)
+        assert ei.value.status == fr.FR_E_ARG
+        with pytest.raises(fr.FrError) as ei:  # the exchange slots need a workspace
+            run_bwd(x, dy, g, mean, rstd, want_dg=False)
+        assert ei.value.status == fr.FR_E_WORKSPACE
+        with pytest.raises(fr.FrError) as ei:  # 16-byte accesses only
+            run_bwd(x, dy, g, mean, rstd, offset=1, ws=ws)
+        assert ei.value.status == fr.FR_E_ARG
+    finally:
+        fr.fr_force_form(fr.FR_FORM_AUTO)
+
+
+def test_layernorm_backward_split_rows_deterministic():
+    rows, cols = 2048, 32768
+    x, dy, g, mean, rstd = inputs(rows, cols, seed=31)
+    ws = team_ws(rows, cols)
+    a = run_bwd(x, dy, g, mean, rstd, ws=ws)
+    b = run_bwd(x, dy, g, mean, rstd, ws=ws)
+    for k in ("dx", "dgamma", "dbeta"):
+        assert np.array_equal(a[k], b[k]), k
