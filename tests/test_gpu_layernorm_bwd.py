@@ -241,3 +241,46 @@ def test_layernorm_backward_split_rows_deterministic():
     b = run_bwd(x, dy, g, mean, rstd, ws=ws)
     for k in ("dx", "dgamma", "dbeta"):
         assert np.array_equal(a[k], b[k]), k
+
+
+def test_layernorm_backward_split_rows_graph_replays():
+    # the reset of the exchange slots is a fill kernel, so the call can be
+    # recorded in a graph: every replay (with eager calls on other data and
+    # synchronisations between them) equals the eager result bit for bit
+    rows, cols = 512, 32768
+    x, dy, g, mean, rstd = inputs(rows, cols, seed=37)
+    x2, dy2, _, mean2, rstd2 = inputs(rows, cols, seed=41)
+    xd, dyd, gd, md, rd = bf16_bits_tensor(x), bf16_bits_tensor(dy), bf16_bits_tensor(g), dev(mean), dev(rstd)
+    x2d, dy2d, m2d, r2d = bf16_bits_tensor(x2), bf16_bits_tensor(dy2), dev(mean2), dev(rstd2)
+    ws = team_ws(rows, cols)
+    dx = torch.empty_like(xd)
+    dg = torch.empty(cols, dtype=torch.float32, device="cuda")
+    db = torch.empty_like(dg)
+    dx2, dg2, db2 = torch.empty_like(dx), torch.empty_like(dg), torch.empty_like(db)
+
+    def call():
+        fr.fr_layernorm_rows_backward(xd, dyd, md, rd, dx, gamma=gd, dgamma=dg, dbeta=db, ws=ws)
+
+    call()
+    torch.cuda.synchronize()
+    ref = (bf16_bits_of(dx), host(dg), host(db))
+    compare(x, dy, g, mean, rstd, {"dx": ref[0], "dgamma": ref[1], "dbeta": ref[2]}, what="eager")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for rep in range(4):
+        dx.fill_(0)
+        dg.fill_(float("nan"))
+        # eager work on other data through the same workspace
+        fr.fr_layernorm_rows_backward(x2d, dy2d, m2d, r2d, dx2, gamma=gd, dgamma=dg2, dbeta=db2, ws=ws)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bf16_bits_of(dx), ref[0]), rep
+        assert np.array_equal(host(dg), ref[1]) and np.array_equal(host(db), ref[2]), rep
