@@ -90,16 +90,17 @@ typedef struct fr_plan {
     int32_t seg;          /* lanes that share one row (persistent form) */
     int32_t vec;          /* 16-byte vectors per lane: per pass (PER, SPLIT chunk) or per loop step (RED) */
     int32_t rows_per_wg;  /* rows handled by one workgroup */
-    int32_t splits;       /* chunks per row (SPLIT), else 1 */
-    int32_t chunk;        /* elements per chunk (SPLIT), else 0 */
+    int32_t splits;       /* chunks per row (SPLIT; LayerNorm backward: workgroups per row), else 1 */
+    int32_t chunk;        /* elements per chunk (SPLIT; LayerNorm backward: columns per workgroup), else 0 */
     int32_t vec16;        /* 1: 16-byte vector accesses; 0: element accesses */
     int32_t occupancy;    /* minimum waves per SIMD requested from the compiler (0: none) */
     int32_t passes;       /* reads of the input (split softmax: 1 = chunks kept in registers while the
                              row's partials are exchanged in one kernel, 2 = partial + finishing kernels) */
-    int32_t wait_us;      /* single-pass split softmax: microseconds a workgroup waits for the other
-                             partials of its row before computing the missing ones itself from x (same
-                             bits); in an override 0 means the default, and < 0 makes every workgroup
-                             compute all partials of its row itself (a test of that path) */
+    int32_t wait_us;      /* single-pass split softmax and split LayerNorm backward: microseconds a
+                             workgroup waits for the other partials of its row before computing the
+                             missing ones itself from the inputs (same bits); in an override 0 means
+                             the default, and < 0 makes every workgroup compute all partials of its
+                             row itself (a test of that path) */
     int64_t grid;         /* workgroups of the main kernel */
     int64_t grid2;        /* workgroups of the finishing kernel (0: none) */
     uint64_t ws_bytes;    /* workspace bytes this plan uses */

@@ -33,14 +33,8 @@
 
 namespace fr {
 
-#ifndef FR_ATTN_VALUE_BATCH
-#define FR_ATTN_VALUE_BATCH 16
-#endif
-constexpr int kAttnValueBatch = FR_ATTN_VALUE_BATCH;  // value vectors in flight per lane
-#ifndef FR_ATTN_KEY_TILES
-#define FR_ATTN_KEY_TILES 2
-#endif
-constexpr int kAttnKeyTiles = FR_ATTN_KEY_TILES;  // bf16: 16-key tiles whose loads are in flight together
+constexpr int kAttnValueBatch = 16;  // value vectors in flight per lane
+constexpr int kAttnKeyTiles = 2;     // bf16: 16-key tiles whose loads are in flight together
 
 // Element access for fp32 and bf16 (uint16 bits) rows, 16 bytes at a time.
 template <typename DT>
