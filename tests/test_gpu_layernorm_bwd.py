@@ -180,11 +180,14 @@ def test_layernorm_backward_split_rows(shape):
         fr.fr_force_form(fr.FR_FORM_AUTO)
 
 
-def test_layernorm_backward_split_rows_recomputed_partner_sums():
+@pytest.mark.parametrize("shape", [(300, 32768), (7, 20000), (5, 16392)])
+def test_layernorm_backward_split_rows_recomputed_partner_sums(shape):
     # with no wait every partner's row sums are recomputed by the waiting
     # workgroup: the same bits as the exchanged ones, and the workspace
-    # header counts them (rows x parts x (parts - 1))
-    rows, cols = 300, 32768
+    # header counts them (rows x parts x (parts - 1)); 4, 3 and 3 parts, the
+    # last one narrower in the second and third shapes
+    rows, cols = shape
+    parts = -(-cols // 8192)
     x, dy, g, mean, rstd = inputs(rows, cols, seed=23)
     ws = team_ws(rows, cols)
     fr.fr_force_form(fr.FR_FORM_SPLIT)
@@ -196,12 +199,12 @@ def test_layernorm_backward_split_rows_recomputed_partner_sums():
             b = run_bwd(x, dy, g, mean, rstd, ws=ws)
         finally:
             fr.fr_tune_override(fr.FR_OP_LAYERNORM_BWD)
-        assert int(ws[:1].view(torch.int32).item()) == rows * 4 * 3
+        assert int(ws[:1].view(torch.int32).item()) == rows * parts * (parts - 1)
     finally:
         fr.fr_force_form(fr.FR_FORM_AUTO)
     for k in ("dx", "dgamma", "dbeta"):
         assert np.array_equal(a[k], b[k]), k
-    compare(x, dy, g, mean, rstd, a, what="split 300x32768")
+    compare(x, dy, g, mean, rstd, a, what=f"split {shape}")
 
 
 def test_layernorm_backward_split_rows_choice_and_errors():
