@@ -128,6 +128,39 @@ def test_sumsq_full_2_28_and_determinism():
     assert abs(got - ref) <= 1e-5 * ref + 1e-6, (got, ref)
 
 
+_CHILD = """
+import sys, numpy as np, torch
+sys.path.insert(0, {root!r})
+import synth, pointwise_reduction_amd as fr
+n = 1 << 28
+x = torch.from_numpy(synth.sumsq_inputs(n, seed=4001)).cuda()
+ws = torch.empty(fr.fr_sumsq_full_workspace_bytes(n) // 4, dtype=torch.float32, device="cuda")
+out = torch.zeros(1, dtype=torch.float32, device="cuda")
+fr.fr_sumsq_full(x, out, ws=ws)
+print(int(out.cpu().numpy().view(np.uint32)[0]))
+"""
+
+
+def test_sumsq_full_bits_across_processes():
+    # the same bits in separate processes (each one its own HIP context), as
+    # in repeated launches of one process
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    n = 1 << 28
+    xd = dev(synth.sumsq_inputs(n, seed=4001))
+    ws = torch.empty(fr.fr_sumsq_full_workspace_bytes(n) // 4, dtype=torch.float32, device="cuda")
+    out = torch.zeros(1, dtype=torch.float32, device="cuda")
+    fr.fr_sumsq_full(xd, out, ws=ws)
+    mine = int(host(out).view(np.uint32)[0])
+    for _ in range(2):
+        r = subprocess.run([sys.executable, "-c", _CHILD.format(root=root)], capture_output=True, text=True,
+                           timeout=240)
+        assert r.returncode == 0, r.stderr[-2000:]
+        assert int(r.stdout.strip().splitlines()[-1]) == mine
+
+
 @pytest.mark.parametrize("n", [0, 1, 7, 2048, 2049, 98432, 1 << 24, 1 << 28])
 def test_sumsq_full_of_ones_is_exact(n):
     xd = torch.ones(n, dtype=torch.float32, device="cuda")
