@@ -358,7 +358,7 @@ int fr_attn_decode(const void* q, const void* k, const void* v, void* o, float* 
 /* ------------------------------------------------------------ attention over blocks of query rows
  * O = softmax(scale * Q K^T [+ causal mask]) V and LSE = m + log l per query
  * row, the tiled single-pass algorithm of "Stax (4)", 9.10 (Theorem 9.2,
- * Figure 9.2): one workgroup keeps a block of 128 query rows on chip and
+ * Figure 9.2): one workgroup keeps a block of 256 query rows on chip and
  * scans K and V in blocks of 64 keys with the online (m, l, a) update; S
  * and P never reach memory. Both products run on the matrix cores in bf16
  * with fp32 accumulation; P enters the second product as bf16.
@@ -371,7 +371,8 @@ int fr_attn_decode(const void* q, const void* k, const void* v, void* o, float* 
  *  scale:  finite and > 0 (commonly 1 / sqrt(dim)); the row maxima are
  *          taken on the unscaled scores.
  * dim 64 or 128; heads_q a multiple of heads_kv; batch and heads_q <=
- * 65535; seq lengths < 2^30. A row that sees no key (seq_kv = 0) gives
+ * 65535; seq lengths < 2^30 and seq_kv * dim * 2 < 2^31 (one head's keys
+ * addressed with 32-bit offsets). A row that sees no key (seq_kv = 0) gives
  * o = 0 and lse = -inf. dtype must be FR_BF16. */
 int fr_attn_block(const void* q, const void* k, const void* v, void* o, float* lse, int64_t batch, int64_t heads_q,
                   int64_t heads_kv, int64_t seq_q, int64_t seq_kv, int64_t dim, int causal, float scale, int dtype,

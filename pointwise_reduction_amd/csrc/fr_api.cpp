@@ -494,8 +494,9 @@ int fr_attn_block(const void* q, const void* k, const void* v, void* o, float* l
     if (batch < 0 || heads_q < 0 || heads_kv < 0 || seq_q < 0 || seq_kv < 0) return FR_E_SIZE;
     if (dim != 64 && dim != 128) return FR_E_SIZE;
     if (batch > 65535 || heads_q > 65535 || seq_q >= kMaxCols || seq_kv >= kMaxCols) return FR_E_SIZE;
+    if (seq_kv * dim * 2 >= (int64_t(1) << 31)) return FR_E_SIZE;  // one head's keys: 32-bit byte offsets
     if (batch == 0 || heads_q == 0 || seq_q == 0) return FR_OK;
-    // one workgroup per (block of 128 query rows, head, batch): a 1-D grid
+    // one workgroup per (block of kAttnBlockRows query rows, head, batch): a 1-D grid
     if ((seq_q + kAttnBlockRows - 1) / kAttnBlockRows * heads_q * batch >= (int64_t(1) << 31)) return FR_E_SIZE;
     if (heads_kv == 0 || heads_q % heads_kv) return FR_E_ARG;
     if (!isfinite(scale) || !(scale > 0.0f)) return FR_E_ARG;

@@ -3,15 +3,14 @@
 // algorithm, Figure 9.2; the (m, l, a) triple updated online; LSE = m +
 // log l kept for the backward pass; the causal mask of Listing 9.7).
 //
-// One workgroup of 4 waves owns a block of 128 query rows of one head (each
+// One workgroup of 8 waves owns a block of 256 query rows of one head (each
 // wave 32 rows) and scans the keys and values in blocks of 64. Both products
 // run on the matrix cores (v_mfma_f32_16x16x32_bf16, lane l: A row l % 16,
 // B column l % 16, k = 8 (l / 16) .. +7; D rows 4 (l / 16) .. +3, column
 // l % 16):
 //   S^T = K Q^T   A = a K tile (key rows, read from LDS), B = the wave's Q
-//                 rows (registers, loaded once). D holds, for lane l's query
-//                 (column l % 16), the keys 4 (l / 16) .. +3 of each 16-key
-//                 tile.
+//                 rows (read from LDS). D holds, for lane l's query (column
+//                 l % 16), the keys 4 (l / 16) .. +3 of each 16-key tile.
 //   O  += P V     A = P. A lane's D registers of two consecutive key tiles
 //                 hold exactly 8 keys of its own query: they are its A
 //                 fragment, with the k positions of the 32-key step mapped
@@ -26,12 +25,14 @@
 // softmax works in base 2 (the scale carries log2 e); a row's maximum and
 // sum need one butterfly over the 4 lane groups; the rescale factor of a row
 // reaches the O rows 4 (l / 16) + i with one shuffle each.
-// K and V are staged row-major in LDS with 16-byte writes; the next key /
-// value block is loaded into registers while the current one is computed. The block's Q rows sit in LDS rather than in
-// registers, which holds the kernel to 256 registers: two workgroups share a
-// CU and one's softmax overlaps the other's matrix products. With the causal
-// mask, blocks wholly above the diagonal are skipped and the heaviest query
-// blocks of a head are launched first.
+// LDS holds the block's Q rows and two K and two V blocks (147 KB at 128
+// dimensions: one workgroup, 8 waves, per CU). K runs one block ahead of V,
+// so a step forms the next block's S^T while it turns this block's S^T into
+// P and accumulates P V, stages the blocks in flight (loaded into registers
+// by buffer loads one step earlier) into the buffers the previous step
+// finished with, and needs one barrier. With the causal mask, blocks wholly
+// above the diagonal are skipped, and each XCD takes its heads' query blocks
+// heaviest first.
 #include "fr_device.h"
 #include "fr_internal.h"
 
@@ -45,7 +46,8 @@ typedef __attribute__((address_space(3))) short4v* lds_s4p;
 
 constexpr int kBM = kAttnBlockRows;  // query rows per workgroup
 constexpr int kBN = 64;              // keys per block
-constexpr int kWaves = 4;
+constexpr int kWaves = kBM / 32;     // 32 query rows per wave
+constexpr int kThreads = kWaves * 64;
 constexpr int kXcds = 8;  // MI355X: 8 XCDs, each with its own L2
 constexpr float kLazy = 8.0f;  // P <= 2^8 between rescales (base-2 exponent)
 // LDS row padding (bf16 elements) of the K, V and Q tiles: rows 288 bytes
@@ -67,32 +69,49 @@ __device__ __forceinline__ float pk(float lo, float hi) { return __builtin_bit_c
 }  // namespace
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void fr_attn_block_bf16(const uint16_t* __restrict__ q,
-                                                          const uint16_t* __restrict__ k,
-                                                          const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
-                                                          float* __restrict__ lse, int Hq, int Hkv, int Nq, int Nk,
-                                                          float scale_log2) {
+__global__ __launch_bounds__(kThreads, 2) void fr_attn_block_bf16(const uint16_t* __restrict__ q,
+                                                                 const uint16_t* __restrict__ k,
+                                                                 const uint16_t* __restrict__ v,
+                                                                 uint16_t* __restrict__ o, float* __restrict__ lse,
+                                                                 int Hq, int Hkv, int Nq, int Nk, float scale_log2) {
     constexpr int NS = D / 32;        // 32-dim steps of S^T
     constexpr int NT = D / 16;        // 16-dim tiles of O
-    constexpr int KCH = kBN * D / 8;  // 16-byte chunks of a K block
-    constexpr int KPT = KCH / 256;    // per thread
-    constexpr int VPT = KPT;
+    constexpr int KCH = kBN * D / 8;  // 16-byte chunks of a K (or V) block
+    constexpr int KPT = KCH / kThreads;
     constexpr int KLD = D + kKPad;
-    static_assert(KCH % 256 == 0, "block shape");
-    __shared__ __align__(16) uint16_t sk[kBN * KLD];
-    __shared__ __align__(16) uint16_t sv[kBN * KLD];  // V row-major, like K
+    static_assert(KCH % kThreads == 0, "block shape");
+    // K and V blocks, two of each (K runs one block ahead of V), and the
+    // workgroup's Q rows (147 KB in all for D = 128: one workgroup per CU)
+    __shared__ __align__(16) uint16_t sk[2][kBN * KLD];
+    __shared__ __align__(16) uint16_t sv[2][kBN * KLD];
     __shared__ __align__(16) uint16_t sq[kBM * KLD];
 
     // XCD-aware order: the dispatcher sends workgroup L to XCD L % 8, so
     // logical tile L % 8 * (G / 8) + L / 8 gives each XCD a contiguous run of
     // tiles, i.e. whole heads, whose K and V then stay in that XCD's L2
+    // (causal: each XCD's heads are taken heaviest query block first across
+    // all of them, longest-first list scheduling over the XCD's CUs)
     const int nqb = (Nq + kBM - 1) / kBM;
     const int G = (int)gridDim.x;
     const int L = (int)blockIdx.x;
-    const int tile = (G % kXcds == 0) ? (L % kXcds) * (G / kXcds) + L / kXcds : L;
-    const int qi0 = tile % nqb;
-    const int qb = CAUSAL ? nqb - 1 - qi0 : qi0;  // heaviest first within a head
-    const int h = (tile / nqb) % Hq, b = tile / (nqb * Hq);
+    int qi0, hb;  // query block (0 = the heaviest when causal), head x batch
+    if (G % kXcds == 0) {
+        const int x = L % kXcds, i = L / kXcds, R = G / kXcds;
+        if (CAUSAL && R % nqb == 0) {
+            const int hpx = R / nqb;  // whole heads per XCD
+            qi0 = i / hpx;
+            hb = x * hpx + i % hpx;
+        } else {
+            const int tile = x * R + i;
+            qi0 = tile % nqb;
+            hb = tile / nqb;
+        }
+    } else {
+        qi0 = L % nqb;
+        hb = L / nqb;
+    }
+    const int qb = CAUSAL ? nqb - 1 - qi0 : qi0;
+    const int h = hb % Hq, b = hb / Hq;
     const int hk = h / (Hq / Hkv);
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int n = lane & 15, g = lane >> 4;
@@ -100,10 +119,11 @@ __global__ __launch_bounds__(256, 2) void fr_attn_block_bf16(const uint16_t* __r
     const int64_t kv0 = ((int64_t)b * Hkv + hk) * Nk;
     const int qbase = qb * kBM + w * 32;  // the wave's first query row
 
-    // the block's Q rows in LDS; B fragments are read from there per key block
+    // the workgroup's Q rows in LDS; B fragments are read from there per key
+    // block (in registers they would leave too few for the pipeline)
 #pragma unroll
-    for (int r = 0; r < kBM * D / 8 / 256; ++r) {
-        const int c = tid + 256 * r, row = c / (D / 8), oc = c % (D / 8);
+    for (int r = 0; r < kBM * D / 8 / kThreads; ++r) {
+        const int c = tid + kThreads * r, row = c / (D / 8), oc = c % (D / 8);
         const int qi = qb * kBM + row;
         *reinterpret_cast<f32x4*>(&sq[row * KLD + 8 * oc]) =
             qi < Nq ? ld16g(q + (qrow0 + qi) * D + 8 * oc) : f32x4{0.f, 0.f, 0.f, 0.f};
@@ -116,33 +136,39 @@ __global__ __launch_bounds__(256, 2) void fr_attn_block_bf16(const uint16_t* __r
         nkb = need < nkb ? need : nkb;
     }
 
-    // the next block's K chunks and V units, in registers
-    f32x4 kr[KPT], vr[VPT];
-    // loads of the next block; only a block that crosses the end of the keys
-    // checks each row (the branch is the same for the whole workgroup)
-    auto fetch = [&](int jb) {
-        if ((jb + 1) * kBN <= Nk) {
-#pragma unroll
-            for (int r = 0; r < KPT; ++r) {
-                const int c = tid + 256 * r, j = jb * kBN + c / (D / 8), oc = c % (D / 8);
-                kr[r] = ld16g(k + (kv0 + j) * D + 8 * oc);
-                vr[r] = ld16g(v + (kv0 + j) * D + 8 * oc);
-            }
-            return;
-        }
+    // K block jk and V block jv, in registers until staged. Buffer loads
+    // over the head's keys: rows past the end read zeros without a memory
+    // access (the range check), and so does a block past the last (its
+    // offsets point past the range). No branch around a load, so the
+    // compiler's waits count the loads in flight exactly.
+    const uint32_t kvbytes = (uint32_t)Nk * D * 2;  // < 2^31 (checked by the entry point)
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(k + kv0 * D), 0, (int)kvbytes, kBufferRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(v + kv0 * D), 0, (int)kvbytes, kBufferRsrcWord3);
+    f32x4 kr[KPT], vr[KPT];
+    auto fetch = [&](int jk, int jv) __attribute__((always_inline)) {
 #pragma unroll
         for (int r = 0; r < KPT; ++r) {
-            const int c = tid + 256 * r, j = jb * kBN + c / (D / 8), oc = c % (D / 8);
-            kr[r] = j < Nk ? ld16g(k + (kv0 + j) * D + 8 * oc) : f32x4{0.f, 0.f, 0.f, 0.f};
-            vr[r] = j < Nk ? ld16g(v + (kv0 + j) * D + 8 * oc) : f32x4{0.f, 0.f, 0.f, 0.f};
+            const int c = tid + kThreads * r, jr = c / (D / 8), oc = c % (D / 8);
+            const uint32_t o1 = jk < nkb ? (uint32_t)((jk * kBN + jr) * D + 8 * oc) * 2u : kvbytes;
+            const uint32_t o2 = jv < nkb ? (uint32_t)((jv * kBN + jr) * D + 8 * oc) * 2u : kvbytes;
+            kr[r] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, (int)o1, 0, 0));
+            vr[r] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, (int)o2, 0, 0));
         }
     };
-    auto stage = [&]() {
+    auto stage_k = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
         for (int r = 0; r < KPT; ++r) {
-            const int c = tid + 256 * r, j = c / (D / 8), oc = c % (D / 8);
-            *reinterpret_cast<f32x4*>(&sk[j * KLD + 8 * oc]) = kr[r];
-            *reinterpret_cast<f32x4*>(&sv[j * KLD + 8 * oc]) = vr[r];
+            const int c = tid + kThreads * r, j = c / (D / 8), oc = c % (D / 8);
+            *reinterpret_cast<f32x4*>(&sk[buf][j * KLD + 8 * oc]) = kr[r];
+        }
+    };
+    auto stage_v = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int r = 0; r < KPT; ++r) {
+            const int c = tid + kThreads * r, j = c / (D / 8), oc = c % (D / 8);
+            *reinterpret_cast<f32x4*>(&sv[buf][j * KLD + 8 * oc]) = vr[r];
         }
     };
 
@@ -153,14 +179,8 @@ __global__ __launch_bounds__(256, 2) void fr_attn_block_bf16(const uint16_t* __r
         for (int t = 0; t < NT; ++t) acc[bq][t] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
 
-    if (nkb > 0) fetch(0);
-    for (int jb = 0; jb < nkb; ++jb) {
-        stage();
-        __syncthreads();
-        if (jb + 1 < nkb) fetch(jb + 1);  // in flight while this block is computed
-
-        // S^T for 4 key tiles x 2 query tiles
-        f32x4 st[4][2];
+    // S^T of the K block in sk[buf]: 4 key tiles x 2 query tiles
+    auto s_block = [&](int buf, f32x4 (&st)[4][2]) __attribute__((always_inline)) {
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -169,23 +189,27 @@ __global__ __launch_bounds__(256, 2) void fr_attn_block_bf16(const uint16_t* __r
         for (int s = 0; s < NS; ++s)
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                const f32x4 a = *reinterpret_cast<const f32x4*>(&sk[(16 * t + n) * KLD + 32 * s + 8 * g]);
+                const f32x4 a = *reinterpret_cast<const f32x4*>(&sk[buf][(16 * t + n) * KLD + 32 * s + 8 * g]);
 #pragma unroll
                 for (int bq = 0; bq < 2; ++bq) {
-                    const f32x4 qv = *reinterpret_cast<const f32x4*>(&sq[(w * 32 + 16 * bq + n) * KLD + 32 * s + 8 * g]);
+                    const f32x4 qv =
+                        *reinterpret_cast<const f32x4*>(&sq[(w * 32 + 16 * bq + n) * KLD + 32 * s + 8 * g]);
                     st[t][bq] = mfma(a, qv, st[t][bq]);
                 }
             }
-
-        // online softmax per query (lane's column), base 2, against a
-        // reference: m holds a per-row reference maximum (scaled), the
-        // exponents are exp2(fma(s, c, -m)) and l and the O rows are relative
-        // to it. The reference moves (and O, l are rescaled) only when some
-        // row of the wave sees a block maximum more than kLazy above its
-        // reference, so P stays <= 2^kLazy and o = a / l is unchanged; after
-        // the first blocks the rescale is rarely needed. Blocks wholly inside
-        // the keys (and, causal, wholly at or below every query of the wave)
-        // need no mask.
+    };
+    // online softmax per query (lane's column), base 2, against a
+    // reference: m holds a per-row reference maximum (scaled), the exponents
+    // are exp2(fma(s, c, -m)) and l and the O rows are relative to it. The
+    // reference moves (and O, l are rescaled) only when some row of the wave
+    // sees a block maximum more than kLazy above its reference, so P stays
+    // <= 2^kLazy and o = a / l is unchanged; after the first blocks the
+    // rescale is rarely needed. Blocks wholly inside the keys (and, causal,
+    // wholly at or below every query of the wave) need no mask. The first
+    // half (mask, maxima, rescale) ends in branches; the second half (the
+    // exponentials and sums) is branch-free, and the next block's S^T
+    // products are issued beside it.
+    auto softmax_max = [&](int jb, f32x4 (&st)[4][2]) __attribute__((always_inline)) {
         const bool full = (jb + 1) * kBN <= Nk && (!CAUSAL || (jb + 1) * kBN - 1 <= qbase);
         if (!full) [[unlikely]] {
 #pragma unroll
@@ -229,6 +253,8 @@ __global__ __launch_bounds__(256, 2) void fr_attn_block_bf16(const uint16_t* __r
                 }
             }
         }
+    };
+    auto softmax_exp = [&](f32x4 (&st)[4][2]) __attribute__((always_inline)) {
 #pragma unroll
         for (int bq = 0; bq < 2; ++bq) {
             const float mu = m[bq] == -INFINITY ? 0.f : m[bq];  // nothing seen yet: everything stays 0
@@ -245,7 +271,9 @@ __global__ __launch_bounds__(256, 2) void fr_attn_block_bf16(const uint16_t* __r
             sum += __shfl_xor(sum, 32, 64);
             l[bq] += sum;
         }
-        // O += P V, two 32-key steps
+    };
+    // O += P V from the V block in sv[buf], two 32-key steps
+    auto pv_block = [&](int buf, const f32x4 (&st)[4][2]) __attribute__((always_inline)) {
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             f32x4 pa[2];
@@ -260,7 +288,7 @@ __global__ __launch_bounds__(256, 2) void fr_attn_block_bf16(const uint16_t* __r
                 // group g points at key 32 kk + 4 g + p / 4 (+ 16), dims
                 // 16 t + 4 (p % 4) .. +3; lane n then receives dim 16 t + n
                 // of the 4 keys
-                const uint16_t* row = &sv[(32 * kk + 4 * g + (n >> 2)) * KLD + 16 * t + 4 * (n & 3)];
+                const uint16_t* row = &sv[buf][(32 * kk + 4 * g + (n >> 2)) * KLD + 16 * t + 4 * (n & 3)];
                 const short4v v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4p)row);
                 const short4v v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4p)(row + 16 * KLD));
                 const f32x4 bv = __builtin_bit_cast(
@@ -270,10 +298,48 @@ __global__ __launch_bounds__(256, 2) void fr_attn_block_bf16(const uint16_t* __r
                 for (int bq = 0; bq < 2; ++bq) acc[bq][t] = mfma(pa[bq], bv, acc[bq][t]);
             }
         }
-        __syncthreads();  // the next block overwrites the LDS tiles
+    };
+
+    // Pipeline over key blocks. At the top of step jb: S^T of block jb is in
+    // registers, sk[(jb + 1) & 1] holds K of block jb + 1, sv[jb & 1] holds V
+    // of block jb, and the registers receive K of block jb + 2 and V of
+    // block jb + 1. Step jb turns S^T(jb) into P while the matrix cores form
+    // S^T(jb + 1), accumulates P V(jb), stages the blocks in flight into the
+    // buffers that step jb - 1 finished with, and issues the next loads. One
+    // barrier per step.
+    f32x4 sa[4][2], sb[4][2];
+    if (nkb > 0) {
+        fetch(0, 0);
+        stage_k(0);
+        stage_v(0);
+        fetch(1, 1);
+        __syncthreads();
+        s_block(0, sa);  // block 0 is never past a wave's last query
+        if (1 < nkb) stage_k(1);
+        fetch(2, 1);  // V of block 1 was loaded above and is not staged yet: the same values again
+        __syncthreads();
+    }
+    auto step = [&](int jb, f32x4 (&cur)[4][2], f32x4 (&nxt)[4][2]) __attribute__((always_inline)) {
+        softmax_max(jb, cur);
+        if (jb + 1 < nkb) s_block((jb + 1) & 1, nxt);
+        softmax_exp(cur);
+        pv_block(jb & 1, cur);
+        if (jb + 2 < nkb) stage_k(jb & 1);
+        if (jb + 1 < nkb) stage_v((jb + 1) & 1);
+        fetch(jb + 3, jb + 2);
+        __syncthreads();
+    };
+    for (int jb = 0; jb < nkb; jb += 2) {
+        step(jb, sa, sb);
+        if (jb + 1 < nkb) step(jb + 1, sb, sa);
     }
 
-    // o = a / l (rows 4 g + i of each query tile); lse = (m + log2 l) ln 2
+    // o = a / l (rows 4 g + i of each query tile); lse = (m + log2 l) ln 2.
+    // The lane's position is taken afresh (mbcnt) rather than kept alive
+    // across the scan, where every register is in use.
+    {
+    const int lane2 = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    const int n = lane2 & 15, g = lane2 >> 4;
 #pragma unroll
     for (int bq = 0; bq < 2; ++bq) {
         const int qi = qbase + 16 * bq + n;
@@ -291,13 +357,14 @@ __global__ __launch_bounds__(256, 2) void fr_attn_block_bf16(const uint16_t* __r
             }
         }
     }
+    }
 }
 
 hipError_t launch_attn_block(const AttnBlockArgs& a, hipStream_t s) {
     const dim3 grid((unsigned)((int64_t)(a.seq_q + kBM - 1) / kBM * a.heads_q * a.batch));
     const float sl2 = a.scale * 1.4426950408889634f;
     auto go = [&](auto kern) {
-        hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, (const uint16_t*)a.q, (const uint16_t*)a.k,
+        hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, s, (const uint16_t*)a.q, (const uint16_t*)a.k,
                            (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.heads_q, a.heads_kv, a.seq_q, a.seq_kv, sl2);
     };
     if (a.dim == 128) a.causal ? go(fr_attn_block_bf16<128, true>) : go(fr_attn_block_bf16<128, false>);

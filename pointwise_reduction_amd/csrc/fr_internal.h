@@ -139,7 +139,7 @@ struct AttnArgs {
 };
 hipError_t launch_attn_decode(const AttnArgs& a, hipStream_t s);
 // Tiled attention over blocks of kAttnBlockRows query rows (bf16).
-constexpr int kAttnBlockRows = 128;
+constexpr int kAttnBlockRows = 256;
 struct AttnBlockArgs {
     const void* q;
     const void* k;
