@@ -49,6 +49,12 @@ constexpr int kBN = 64;              // keys per block
 constexpr int kWaves = kBM / 32;     // 32 query rows per wave
 constexpr int kThreads = kWaves * 64;
 constexpr int kXcds = 8;  // MI355X: 8 XCDs, each with its own L2
+// Causal order: an XCD takes its heads two at a time, each pair's query
+// blocks heaviest first. Longest-first over the pair keeps the CUs busy to
+// the end, and two heads' K and V (4 MB at 4096 x 128) mostly stay in the
+// XCD's L2. At 4096 x 128 causal: one head at a time 374 us, pairs 309,
+// four 302-320, all eight 309-331.
+constexpr int kHeadGroup = 2;
 constexpr float kLazy = 8.0f;  // P <= 2^8 between rescales (base-2 exponent)
 // LDS row padding (bf16 elements) of the K, V and Q tiles: rows 288 bytes
 // apart (D = 128) keep every fragment read free of bank conflicts. An
@@ -99,8 +105,12 @@ __global__ __launch_bounds__(kThreads, 2) void fr_attn_block_bf16(const uint16_t
         const int x = L % kXcds, i = L / kXcds, R = G / kXcds;
         if (CAUSAL && R % nqb == 0) {
             const int hpx = R / nqb;  // whole heads per XCD
-            qi0 = i / hpx;
-            hb = x * hpx + i % hpx;
+            // groups of kHeadGroup heads, each group's query blocks heaviest
+            // first across its heads
+            const int hg = hpx % kHeadGroup == 0 ? kHeadGroup : hpx;
+            const int gi = i / (hg * nqb), r = i % (hg * nqb);
+            qi0 = r / hg;
+            hb = x * hpx + gi * hg + r % hg;
         } else {
             const int tile = x * R + i;
             qi0 = tile % nqb;
