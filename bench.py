@@ -364,9 +364,10 @@ def make_workload(name, torch, fr, synth):
 
         return W(), per_set
 
-    if name == "softmax_bwd":
-        # softmax backward over the 4096 x 1024 fp32 softmax output
-        rows, cols = 4096, 1024
+    if name in ("softmax_bwd", "softmax_bwd_large"):
+        # softmax backward over the 4096 x 1024 fp32 softmax output, or the
+        # same at 65536 rows (256 MiB per array)
+        rows, cols = (4096, 1024) if name == "softmax_bwd" else (65536, 1024)
         x_h = synth.softmax_inputs(rows, cols, seed=2001)
         dy_h = synth.normal((rows, cols), 2001, stream=7)
         per_set = 3 * rows * cols * 4
@@ -381,7 +382,6 @@ def make_workload(name, torch, fr, synth):
                 fr.fr_softmax_rows(d(x_h), y0)
                 g0 = d(dy_h)
                 torch.cuda.synchronize()
-                self.y_h = y0.cpu().numpy()
                 self.args = [(y0 if i == 0 else y0.clone(), g0 if i == 0 else g0.clone(), torch.empty_like(y0))
                              for i in range(sets)]
 
@@ -394,13 +394,15 @@ def make_workload(name, torch, fr, synth):
 
             def config(self):
                 p = fr.fr_plan_query(fr.FR_OP_SOFTMAX_BWD, rows, cols)
-                return {"workload": "softmax backward 4096x1024 fp32 (y = the forward output, dy ~ N(0,1))",
+                return {"workload": f"softmax backward {rows}x{cols} fp32 (y = the forward output, dy ~ N(0,1))",
                         "rows": rows, "cols": cols, "form": fr.FORM_NAMES[p.form]}
 
             def oracle_fn(self):
+                # the oracle's own forward output as its input (timing only)
                 import oracle
                 r = 1024
-                y, g = self.y_h[:r].copy(), dy_h[:r].copy()
+                y = oracle.softmax_rows(x_h[:r])[0].astype(np.float32)
+                g = dy_h[:r].copy()
                 return lambda: oracle.softmax_backward_rows(y, g), 3 * r * cols * 4, f"first {r} of {rows} rows"
 
         return W(), per_set
@@ -721,7 +723,8 @@ def main():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="softmax",
-                    choices=["softmax", "softmax_large", "sum_relu_add", "sum_relu_add_large", "layernorm",
+                    choices=["softmax", "softmax_large", "softmax_bwd_large", "sum_relu_add", "sum_relu_add_large",
+                             "layernorm",
                              "sumsq", "ragged", "copy", "stream_copy", "stream_copy_c3", "stream_read", "attn_decode", "softmax_bwd", "add_2d",
                              "gelu_bwd", "layernorm_bwd", "c1_region", "attn_block",
                              "attn_block_full"])
