@@ -5,8 +5,9 @@
 A step is one pass of the whole operation over one batch of synthetic input
 already resident in HBM. The default workload is the row softmax over
 4096 x 1024 fp32 (the headline configuration). The other workloads are
-selected with --workload: Example 1.1 sums, the softmax at 65536 rows and
-Example 1.1 at 2^20 rows (the largest shapes), LayerNorm 2048 x 32768 bf16, the
+selected with --workload: Example 1.1 sums, the softmax and its backward at
+65536 rows and Example 1.1 at 2^20 rows (the largest shapes), LayerNorm
+2048 x 32768 bf16, the
 2^28 sum of squares, the ragged 512-row softmax, decode and tiled attention,
 softmax and LayerNorm backward, x.t() + y, GELU backward, a recorded region
 of 16 Example 1.1 launches, and streaming references (copy, read). Tiled
