@@ -1,6 +1,6 @@
 """Benchmark of the fused row-reduction kernels on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--warm] [--eager]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--warm] [--eager] [--procs N]
 
 A step is one pass of the whole operation over one batch of synthetic input
 already resident in HBM. The default workload is the row softmax over
@@ -22,6 +22,10 @@ buffers (--warm uses one set). The K launches are captured once into a HIP
 graph and replayed, so host launch overhead does not enter the device time
 (--eager launches them one by one instead); the graph's output is checked
 against an eager launch before the timing is reported.
+
+With --procs N the measurement runs in N separate processes, one after the
+other, and the line is the median process's, with all N values and their
+range under "procs".
 
 Output: one JSON line with the effective HBM bandwidth (logical bytes: each
 input read once, each output written once), the roofline entry for the
@@ -718,6 +722,40 @@ def read_traffic(kernel, workload):
         return None
 
 
+def run_procs(args):
+    """The same measurement in args.procs child processes, one after the
+    other (each its own HIP context); prints the median child's line with the
+    values of all of them. This process never touches the GPU."""
+    import subprocess
+    argv, skip = [], False
+    for a in sys.argv[1:]:
+        if skip:
+            skip = False
+            continue
+        if a == "--procs":
+            skip = True
+            continue
+        if a.startswith("--procs="):
+            continue
+        argv.append(a)
+    lines = []
+    for i in range(args.procs):
+        r = subprocess.run([sys.executable, os.path.abspath(__file__)] + argv + (["--no-cpu"] if i else []),
+                           capture_output=True, text=True)
+        if r.returncode != 0:
+            sys.stderr.write(r.stderr)
+            return r.returncode
+        lines.append(json.loads([ln for ln in r.stdout.splitlines() if ln.startswith("{")][-1]))
+    vals = [ln["value"] for ln in lines]
+    med = sorted(range(len(lines)), key=lambda i: vals[i])[len(lines) // 2]
+    out = dict(lines[med])
+    if "cpu_baseline" in lines[0]:
+        out["cpu_baseline"] = lines[0]["cpu_baseline"]
+    out["procs"] = {"n": len(lines), "values": vals, "median": vals[med], "min": min(vals), "max": max(vals)}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -733,12 +771,16 @@ def main():
     ap.add_argument("--eager", action="store_true", help="launch each step from the host (no graph)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--procs", type=int, default=1,
+                    help="run the measurement in N separate processes and report the median (with the range)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
+    if args.procs > 1:
+        sys.exit(run_procs(args))
 
     import torch
 
