@@ -200,10 +200,19 @@ def test_layernorm_backward_split_rows_recomputed_partner_sums(shape):
         finally:
             fr.fr_tune_override(fr.FR_OP_LAYERNORM_BWD)
         assert int(ws[:1].view(torch.int32).item()) == rows * parts * (parts - 1)
+        # a 1 us wait: partner sums are read where they arrived in time and
+        # recomputed where not (the counter says how many); the same bits
+        fr.fr_tune_override(fr.FR_OP_LAYERNORM_BWD, form=fr.FR_FORM_SPLIT, threads=1024, vec=1, wait_us=1)
+        try:
+            c = run_bwd(x, dy, g, mean, rstd, ws=ws)
+        finally:
+            fr.fr_tune_override(fr.FR_OP_LAYERNORM_BWD)
+        assert 0 <= int(ws[:1].view(torch.int32).item()) <= rows * parts * (parts - 1)
     finally:
         fr.fr_force_form(fr.FR_FORM_AUTO)
     for k in ("dx", "dgamma", "dbeta"):
         assert np.array_equal(a[k], b[k]), k
+        assert np.array_equal(a[k], c[k]), k
     compare(x, dy, g, mean, rstd, a, what=f"split {shape}")
 
 
