@@ -467,6 +467,7 @@ int fr_attn_decode(const void* q, const void* k, const void* v, void* o, float* 
     if (batch < 0 || heads_q < 0 || heads_kv < 0 || seq < 0) return FR_E_SIZE;
     if (dim != 64 && dim != 128) return FR_E_SIZE;
     if (batch > 65535 || heads_kv > 65535 || seq >= kMaxCols || batch * heads_q >= kMaxRows) return FR_E_SIZE;
+    if (seq * dim * (dtype == FR_BF16 ? 2 : 4) >= (int64_t(1) << 31)) return FR_E_SIZE;  // 32-bit offsets per head
     if (batch == 0 || heads_q == 0) return FR_OK;
     if (heads_kv == 0 || heads_q % heads_kv) return FR_E_ARG;
     const int64_t G = heads_q / heads_kv;

@@ -121,6 +121,19 @@ __global__ __launch_bounds__(256) void fr_attn_part(const DT* __restrict__ q, co
     if (c0 >= L) return;  // the combine reads only chunks below len_b
     const int64_t kv_base = ((int64_t)b * Hkv + hk) * S;
     const int h0 = hk * G;
+    // the head's keys and values below len_b as buffer resources: a key past
+    // it reads zeros through the range check, so no load sits under a
+    // branch (the compiler's waits then count the loads in flight exactly)
+    const uint32_t kvb = (uint32_t)L * D * (uint32_t)sizeof(DT);  // < 2^31 (checked by the entry point)
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<DT*>(k + kv_base * D), 0, (int)kvb, kBufferRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<DT*>(v + kv_base * D), 0, (int)kvb, kBufferRsrcWord3);
+    auto kv_load = [&](__amdgpu_buffer_rsrc_t r, int j, int e) __attribute__((always_inline)) {
+        // element e of key j; j >= len_b (or j past the chunk) reads zeros
+        return __builtin_bit_cast(
+            f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)(((uint32_t)j * D + e) * sizeof(DT)), 0, 2));
+    };
 
     if constexpr (EPV == 8) {
         // bf16: the scores of 16 keys x 16 query rows (rows >= G are zero)
@@ -145,7 +158,7 @@ __global__ __launch_bounds__(256) void fr_attn_part(const DT* __restrict__ q, co
                 const int j = c0 + w * 64 + (t0 + t) * 16 + n;
 #pragma unroll
                 for (int sl = 0; sl < NS; ++sl)
-                    kb[t][sl] = j < L ? ld16_nt(k + (kv_base + j) * D + sl * 32 + kq * 8) : f32x4{0.f, 0.f, 0.f, 0.f};
+                    kb[t][sl] = kv_load(rk, j, sl * 32 + kq * 8);
             }
 #pragma unroll
             for (int t = 0; t < KT; ++t) {
@@ -176,7 +189,7 @@ __global__ __launch_bounds__(256) void fr_attn_part(const DT* __restrict__ q, co
 #pragma unroll
         for (int u = 0; u < BATCH; ++u) {
             const int j = c0 + (i0 + u) * KPS + w * KPW + grp;
-            kv[u] = j < L ? ld16_nt(k + (kv_base + j) * D + vl * EPV) : f32x4{0.f, 0.f, 0.f, 0.f};
+            kv[u] = kv_load(rk, j, vl * EPV);
         }
 #pragma unroll
         for (int u = 0; u < BATCH; ++u) {
@@ -196,7 +209,7 @@ __global__ __launch_bounds__(256) void fr_attn_part(const DT* __restrict__ q, co
     for (int u = 0; u < VB; ++u) {
         const int j = c0 + u * KPS + w * KPW + grp;
         // past len_b: zeros (the tail is never read, and p = 0 there)
-        vpre[u] = j < L ? ld16_nt(v + (kv_base + j) * D + vl * EPV) : f32x4{0.f, 0.f, 0.f, 0.f};
+        vpre[u] = kv_load(rv, j, vl * EPV);
     }
     __syncthreads();
 
@@ -238,7 +251,7 @@ __global__ __launch_bounds__(256) void fr_attn_part(const DT* __restrict__ q, co
 #pragma unroll
         for (int u = 0; u < VB; ++u) {
             const int j = c0 + (i0 + u) * KPS + w * KPW + grp;
-            vv[u] = i0 == 0 ? vpre[u] : (j < L ? ld16_nt(v + (kv_base + j) * D + vl * EPV) : f32x4{0.f, 0.f, 0.f, 0.f});
+            vv[u] = i0 == 0 ? vpre[u] : kv_load(rv, j, vl * EPV);
         }
 #pragma unroll
         for (int u = 0; u < VB; ++u) {
