@@ -70,9 +70,6 @@ struct Elems<uint16_t> {
 };
 
 __device__ __forceinline__ f32x4 ld16(const void* p) { return *static_cast<const f32x4*>(p); }
-__device__ __forceinline__ f32x4 ld16_nt(const void* p) {
-    return __builtin_nontemporal_load(static_cast<const f32x4*>(p));
-}
 
 // Sum over aligned groups of W lanes (W a power of two <= 64), every lane
 // of a group ending with the group's sum: DPP below 16 lanes, ds_bpermute
@@ -132,7 +129,8 @@ __global__ __launch_bounds__(256) void fr_attn_part(const DT* __restrict__ q, co
     auto kv_load = [&](__amdgpu_buffer_rsrc_t r, int j, int e) __attribute__((always_inline)) {
         // element e of key j; j >= len_b (or j past the chunk) reads zeros
         return __builtin_bit_cast(
-            f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)(((uint32_t)j * D + e) * sizeof(DT)), 0, 2));
+            f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)(((uint32_t)j * D + e) * sizeof(DT)), 0,
+                                                         2 /* non-temporal */));
     };
 
     if constexpr (EPV == 8) {
