@@ -271,6 +271,14 @@ constexpr int body_mask() { return VEC ? kNone : kScalar; }
 // and accesses past it read zero and drop stores.
 constexpr int kBufferRsrcWord3 = 0x00020000;
 
+// A raw buffer resource over `bytes` bytes from p (at most 2^31 - 1).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, kBufferRsrcWord3);
+}
+constexpr int kAuxNT = 2;    // buffer instruction cache policy: non-temporal
+constexpr int kAuxSc1 = 16;  // buffer instruction cache policy: sc1 (coherent across the compute dies)
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
 // ------------------------------------------------------------------ bf16
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }

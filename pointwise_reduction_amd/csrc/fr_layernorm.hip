@@ -92,13 +92,7 @@ __device__ __forceinline__ u32x4 normalize8(u32x4 xv, int j0, int L, const uint1
 // that it converts bf16 -> fp32 in each pass instead of keeping 64 fp32
 // copies alive, and gamma / beta are loaded in two halves. The row stays in
 // 32 packed registers per lane; the 512 x 8 kernel fits 7 waves per SIMD.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* p, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, kBufferRsrcWord3);
-}
 __device__ __forceinline__ void hide(u32x4& v) { asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w)); }
-constexpr int kAuxNT = 2;    // buffer instruction cache policy: non-temporal
-constexpr int kAuxSc1 = 16;  // buffer instruction cache policy: sc1 (coherent across the compute dies)
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // y = affine of the row held in v, through buffer resources; gamma and beta
 // are loaded in two halves so that only half of them is live at a time.

@@ -75,10 +75,10 @@ struct Knobs {
 };
 
 // Single-pass split softmax: resident waves per SIMD (the compiler's
-// occupancy for the 256-thread, 8-vector kernel; the grid is sized so that
-// every workgroup is resident at once) and the default wait before a
-// workgroup computes a missing partial itself.
-constexpr int kOnePassWavesPerSimd = 5;
+// occupancy for the 256-thread, 8-vector kernel, which holds two chunks in
+// registers; the grid is sized so that every workgroup is resident at once)
+// and the default wait before a workgroup computes a missing partial itself.
+constexpr int kOnePassWavesPerSimd = 4;
 constexpr int kOnePassWaitUs = 200;
 // Split-row LayerNorm backward: the default wait for a partner's row sums,
 // and the fewest rows for which the automatic choice takes that form.

@@ -425,6 +425,215 @@ __global__ __launch_bounds__(256) void fr_split_softmax_reset(uint32_t* __restri
     if (i < nslots) slots[i] = u32x4{~0u, ~0u, ~0u, ~0u};
 }
 
+// Pipelined form of the one-kernel split (16-byte aligned rows): entry
+// t + G is loaded while entry t is reduced, exchanged and stored, so each
+// workgroup keeps a chunk of loads in flight through the wait for its row's
+// other partials. Every memory instruction of the common path is issued by
+// every lane, without a branch: a lane past its chunk, or an entry past the
+// list, lies outside its buffer resource's range, reads zeros and writes
+// nothing. The compiler's waits for older loads then count the newer ones
+// instead of draining them; only the wait loop and the recomputation (the
+// rare paths) drain. A workgroup looks at its partners' slots once right
+// after publishing its own partial, before the next chunk's loads, and waits
+// only if some were not yet there.
+struct OneEntry {
+    int r, c, nc, base, start, n;
+};
+
+// chunk_partial for a chunk of n elements in registers (lanes past n hold
+// -inf) with chunk-relative indices and the thread id passed in: the same
+// operations in the same order, so the same bits (the index is relative).
+template <int T, int NV>
+__device__ __forceinline__ SoftmaxPartial pipe_partial(const f32x4* v, int n, int lt, float* sl_m, float* sl_d,
+                                                       int* sl_i) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) m = max4(m, v[k]);
+    m = group_reduce<kWave>(m, OpMax());
+    m = block_fold(m, sl_m, T / kWave, OpMax());
+    int cand = INT_MAX;
+    float s = 0.f;
+    const int l4 = lt * 4;
+#pragma unroll
+    for (int k = NV - 1; k >= 0; --k)
+#pragma unroll
+        for (int c = 3; c >= 0; --c)
+            if (l4 + c < n - k * T * 4 && is_max(comp(v[k], c), m)) cand = k * T * 4 + l4 + c;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+        const int rem = n - k * T * 4;
+        const f32x4 e = {l4 + 0 < rem ? exp_fast(v[k].x - m) : 0.f, l4 + 1 < rem ? exp_fast(v[k].y - m) : 0.f,
+                         l4 + 2 < rem ? exp_fast(v[k].z - m) : 0.f, l4 + 3 < rem ? exp_fast(v[k].w - m) : 0.f};
+        s += (e.x + e.y) + (e.z + e.w);
+    }
+    cand = group_reduce<kWave>(cand, OpMinI());
+    cand = block_fold(cand, sl_i, T / kWave, OpMinI());
+    s = group_reduce<kWave>(s, OpSum());
+    s = block_fold(s, sl_d, T / kWave, OpSum());
+    return SoftmaxPartial{m, s, cand, 0};
+}
+
+template <int T, int NV>
+__device__ __forceinline__ void one_pass_pipelined(const float* x, float* y, int64_t x_rs, int64_t y_rs,
+                                                   const int* s_base, const int* s_len, int rows, int total,
+                                                   int32_t* argmax, uint32_t* hdr, uint64_t* slots, float* sl_m,
+                                                   float* sl_d, int* sl_i, uint64_t* s_missing, float* s_mx,
+                                                   int64_t wait_ticks) {
+    constexpr int C = 4 * T * NV;
+    const int tid = threadIdx.x;
+    const int G = gridDim.x;
+    // the list lives in LDS; its values are the same for every lane, and
+    // reading them as such keeps the search and the buffer resources scalar
+    auto uni = [](int v) __attribute__((always_inline)) { return __builtin_amdgcn_readfirstlane(v); };
+    auto entry = [&](int t) __attribute__((always_inline)) {
+        const int tt = t < total ? t : 0;
+        int lo = 0, hi = rows;  // s_base[lo] <= tt < s_base[hi]; rows without chunks never qualify
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (uni(s_base[mid]) <= tt) lo = mid;
+            else hi = mid;
+        }
+        OneEntry e;
+        e.r = lo;
+        e.base = uni(s_base[lo]);
+        e.nc = uni(s_base[lo + 1]) - e.base;
+        e.c = tt - e.base;
+        e.start = e.c * C;
+        e.n = t < total ? min(uni(s_len[lo]) - e.start, C) : 0;  // an entry past the list: empty range
+        return e;
+    };
+    // lane offset in a register, vector offset k * T * 16 as a constant
+    auto issue = [&](f32x4(&v)[NV], const OneEntry& e, int lt) __attribute__((always_inline)) {
+        const __amdgpu_buffer_rsrc_t rx = row_rsrc(x + (int64_t)e.r * x_rs + e.start, (uint32_t)e.n * 4u);
+#pragma unroll
+        for (int k = 0; k < NV; ++k)
+            v[k] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, lt * 16, k * T * 16, kAuxNT));
+    };
+    auto step = [&](const OneEntry& ec, f32x4(&cur)[NV], const OneEntry& en, f32x4(&nxt)[NV])
+                    __attribute__((always_inline)) {
+        // the thread id, opaque to the compiler here, so that the per-element
+        // index arithmetic is redone in each step instead of being hoisted
+        // out of the loop into 40 live registers
+        int lt = tid;
+        asm volatile("" : "+v"(lt));
+        const int l4 = lt * 4;
+        // lanes past the chunk read zeros: give them the maximum's identity
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            const int rem = ec.n - k * T * 4;
+            cur[k].x = l4 + 0 < rem ? cur[k].x : -INFINITY;
+            cur[k].y = l4 + 1 < rem ? cur[k].y : -INFINITY;
+            cur[k].z = l4 + 2 < rem ? cur[k].z : -INFINITY;
+            cur[k].w = l4 + 3 < rem ? cur[k].w : -INFINITY;
+        }
+        SoftmaxPartial own = pipe_partial<T, NV>(cur, ec.n, lt, sl_m, sl_d, sl_i);
+        if (own.idx != INT_MAX) own.idx += ec.start;
+        const uint64_t own0 = slot_word(own.idx, own.m), own1 = slot_word(own.idx, own.d);
+        // the row's slots, 16 bytes per chunk
+        uint64_t* rs = slots + 2 * (int64_t)ec.base;
+        const int row_slot_bytes = ec.nc * 16;
+        const __amdgpu_buffer_rsrc_t rslots = row_rsrc(rs, (uint32_t)row_slot_bytes);
+        // publish: threads 0 and 1 write the slot's two words, every other
+        // lane falls outside the range; sc1: seen by the other dies
+        const uint64_t word = tid & 1 ? own1 : own0;
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{(uint32_t)word, (uint32_t)(word >> 32)}, rslots,
+                                              tid < 2 ? ec.c * 16 + tid * 8 : row_slot_bytes, 0, kAuxSc1);
+        // first look at the partners: lane k of wave 0 reads chunk k's slot
+        const bool look = tid < kWave && tid < ec.nc && tid != ec.c;
+        const u32x4 pw = __builtin_amdgcn_raw_buffer_load_b128(rslots, look ? tid * 16 : row_slot_bytes, 0, kAuxSc1);
+        issue(nxt, en, lt);
+
+        const float* xr = x + (int64_t)ec.r * x_rs;
+        const int L = uni(s_len[ec.r]);
+        MD st{-INFINITY, 0.f};
+        MI best{-INFINITY, INT_MAX};
+        for (int g0 = 0; g0 < ec.nc; g0 += kWave) {
+            const int k = g0 + (tid & (kWave - 1));
+            uint64_t w0 = g0 == 0 ? ((uint64_t)pw.y << 32 | pw.x) : ~0ull;
+            uint64_t w1 = g0 == 0 ? ((uint64_t)pw.w << 32 | pw.z) : ~0ull;
+            if (k == ec.c) {
+                w0 = own0;
+                w1 = own1;
+            }
+            if (tid < kWave) {
+                // with no wait (wait_ticks < 0) every partner's partial is recomputed
+                bool ok = k >= ec.nc || k == ec.c || (wait_ticks >= 0 && published(w0) && published(w1));
+                if (!__all(ok) && wait_ticks >= 0) {
+                    const uint64_t t0 = wall_clock64();
+                    for (;;) {
+                        if (!ok) {
+                            if (!published(w0))
+                                w0 = __hip_atomic_load(&rs[2 * k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            if (!published(w1))
+                                w1 = __hip_atomic_load(&rs[2 * k + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            ok = published(w0) && published(w1);
+                        }
+                        if (__all(ok)) break;
+                        if ((int64_t)(wall_clock64() - t0) >= wait_ticks) break;
+                        __builtin_amdgcn_s_sleep(2);
+                    }
+                }
+                const uint64_t miss = __ballot(!ok);
+                if (tid == 0) *s_missing = miss;
+            }
+            __syncthreads();
+            uint64_t miss = *s_missing;
+            while (miss) {  // rare: the owner has not published in time
+                const int j = __builtin_ctzll(miss);
+                miss &= miss - 1;
+                const int ks = (g0 + j) * C;
+                const int ke = min(L, ks + C);
+                const SoftmaxPartial p = chunk_partial_streamed<kElem, T, NV>(xr, ks, ke, sl_m, sl_d, sl_i);
+                if (tid == j) {
+                    w0 = slot_word(p.idx, p.m);
+                    w1 = slot_word(p.idx, p.d);
+                }
+                if (tid == 0) __hip_atomic_fetch_add(&hdr[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __builtin_amdgcn_s_waitcnt(0);
+            }
+            if (tid < kWave) {
+                MD a{-INFINITY, 0.f};
+                MI b{-INFINITY, INT_MAX};
+                if (k < ec.nc) {
+                    const float pm = __builtin_bit_cast(float, (uint32_t)w0);
+                    a = MD{pm, __builtin_bit_cast(float, (uint32_t)w1)};
+                    b = MI{pm, (int)(uint32_t)(w0 >> 32)};
+                }
+                st = md_combine(st, group_reduce<kWave>(a, OpMD()));
+                best = mi_combine(best, group_reduce<kWave>(b, OpMI()));
+            }
+            __syncthreads();  // s_missing and the fold slots are rewritten next
+        }
+        if (tid == 0) {
+            s_mx[0] = st.m;
+            s_mx[1] = 1.0f / st.d;
+        }
+        // the row's argmax from its first chunk's workgroup: thread 0 in range
+        const bool am = argmax != nullptr && ec.c == 0;
+        __builtin_amdgcn_raw_buffer_store_b32(
+            (uint32_t)best.i, row_rsrc(reinterpret_cast<char*>(argmax) + (am ? 4 * (int64_t)ec.r : 0), am ? 4u : 0u),
+            tid == 0 ? 0 : 4, 0, 0);
+        __syncthreads();
+        const float mx = s_mx[0], inv = s_mx[1];
+        const __amdgpu_buffer_rsrc_t ry = row_rsrc(y + (int64_t)ec.r * y_rs + ec.start, (uint32_t)ec.n * 4u);
+#pragma unroll
+        for (int k = 0; k < NV; ++k)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, exp4(cur[k], mx) * inv), ry, lt * 16,
+                                                   k * T * 16, kAuxNT);
+    };
+
+    f32x4 va[NV], vb[NV];
+    OneEntry ea = entry(blockIdx.x);
+    issue(va, ea, tid);
+    for (int t = blockIdx.x; t < total; t += 2 * G) {
+        const OneEntry eb = entry(t + G);
+        step(ea, va, eb, vb);
+        if (t + G >= total) break;
+        ea = entry(t + 2 * G);
+        step(eb, vb, ea, va);
+    }
+}
+
 template <int T, int NV, bool VEC>
 __global__ __launch_bounds__(T) void fr_split_softmax_one(const float* x, float* y, int rows, int cols, int64_t x_rs,
                                                           int64_t y_rs, const int32_t* __restrict__ lengths,
@@ -439,6 +648,7 @@ __global__ __launch_bounds__(T) void fr_split_softmax_one(const float* x, float*
     __shared__ int sl_i[T / kWave];
     __shared__ uint64_t s_missing;
     __shared__ float s_max, s_inv;
+    __shared__ float s_mx[2];
     uint32_t* hdr = static_cast<uint32_t*>(ws);
     uint64_t* slots = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + kSplitWsHeader);
     const int tid = threadIdx.x;
@@ -472,6 +682,11 @@ __global__ __launch_bounds__(T) void fr_split_softmax_one(const float* x, float*
         for (int r = tid; r < rows; r += T)
             if (s_len[r] == 0) argmax[r] = -1;
 
+    if constexpr (VEC) {
+        one_pass_pipelined<T, NV>(x, y, x_rs, y_rs, s_base, s_len, rows, total, argmax, hdr, slots, sl_m, sl_d, sl_i,
+                                  &s_missing, s_mx, wait_ticks);
+        return;
+    }
     for (int t = blockIdx.x; t < total; t += gridDim.x) {
         int lo = 0, hi = rows;  // s_base[lo] <= t < s_base[hi]; rows without chunks never qualify
         while (hi - lo > 1) {

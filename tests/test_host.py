@@ -210,12 +210,13 @@ def test_plans_for_the_five_workloads():
     assert (p.form, p.splits, p.chunk, p.grid, p.grid2) == (fr.FR_FORM_SPLIT, 512, 1 << 19, 512, 1)
     # ragged softmax, 512 rows of capacity 131072, with a workspace: 16 chunks of 8192, a
     # 64-byte header and 512 x 16 partial slots of 16 bytes; one kernel whose grid is every
-    # workgroup that can be resident at once (5 per CU at 256 threads), waiting 200 us by default
+    # workgroup that can be resident at once (4 per CU at 256 threads, two chunks in
+    # registers), waiting 200 us by default
     ws = fr.fr_softmax_rows_workspace_bytes(512, 131072)
     assert ws == 64 + 512 * 16 * 16
     p = fr.fr_plan_query(fr.FR_OP_SOFTMAX, 512, 131072, has_lengths=True, ws_bytes=ws)
     assert (p.form, p.splits, p.chunk, p.passes, p.grid, p.grid2, p.wait_us) == \
-        (fr.FR_FORM_SPLIT, 16, 8192, 1, 256 * 5, 0, 200)
+        (fr.FR_FORM_SPLIT, 16, 8192, 1, 256 * 4, 0, 200)
     # the two-kernel form (a tuning candidate) uses the same workspace
     fr.fr_tune_override(fr.FR_OP_SOFTMAX, form=fr.FR_FORM_SPLIT, threads=256, vec=8, passes=2)
     try:
