@@ -642,7 +642,7 @@ __global__ __launch_bounds__(T) void fr_split_softmax_one(const float* x, float*
     constexpr int C = 4 * T * NV;
     __shared__ int s_base[kOnePassMaxRows + 1];  // first list entry of each row; [rows] = list length
     __shared__ int s_len[kOnePassMaxRows];
-    __shared__ int s_scan[T];
+    __shared__ int s_scan[T / kWave];
     __shared__ float sl_m[T / kWave];
     __shared__ float sl_d[T / kWave];
     __shared__ int sl_i[T / kWave];
@@ -662,20 +662,24 @@ __global__ __launch_bounds__(T) void fr_split_softmax_one(const float* x, float*
         s_len[r] = L;
         local += (L + C - 1) / C;
     }
-    s_scan[tid] = local;
-    __syncthreads();
-    for (int off = 1; off < T; off <<= 1) {  // inclusive scan (Hillis-Steele)
-        const int add = tid >= off ? s_scan[tid - off] : 0;
-        __syncthreads();
-        s_scan[tid] += add;
-        __syncthreads();
+    // exclusive prefix sum of the counts: within each wave by shuffles,
+    // then the wave totals before this wave from LDS
+    const int lane = tid & (kWave - 1), wv = tid / kWave;
+    int incl = local;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int up = __shfl_up(incl, off, kWave);
+        if (lane >= off) incl += up;
     }
-    int run = s_scan[tid] - local;
+    if (lane == kWave - 1) s_scan[wv] = incl;
+    __syncthreads();
+    int run = incl - local;
+    for (int w = 0; w < wv; ++w) run += s_scan[w];
     for (int r = r0; r < r1; ++r) {
         s_base[r] = run;
         run += (s_len[r] + C - 1) / C;
     }
-    if (tid == T - 1) s_base[rows] = s_scan[T - 1];
+    if (tid == T - 1) s_base[rows] = run;
     __syncthreads();
     const int total = s_base[rows];
     if (blockIdx.x == 0 && argmax)
