@@ -194,6 +194,22 @@ def test_softmax_unaligned_rows_use_element_path():
         compare(x, host(y), host(am), what=f"unaligned {form}")
 
 
+@pytest.mark.parametrize("passes", [1, 2])
+def test_softmax_unaligned_rows_split(passes):
+    """Rows that are not 16-byte aligned (row stride 20001 floats) through
+    both split variants: the element-wise path of each kernel (the single pass
+    then keeps one chunk in registers and reads it with masked loads)."""
+    x, L = synth.ragged_softmax_inputs(7, 20001, seed=2710, choices=(1, 8193, 19999, 20001))
+    try:
+        fr.fr_tune_override(fr.FR_OP_SOFTMAX, form=fr.FR_FORM_SPLIT, threads=256, vec=8, passes=passes)
+        y, am, yfull = run(x, lengths=L, use_ws=True)
+    finally:
+        fr.fr_tune_override(fr.FR_OP_SOFTMAX)
+    compare(x, y, am, lengths=L, what=f"unaligned split passes={passes}")
+    for r, n in enumerate(L):
+        assert np.isnan(yfull[r, n:]).all()
+
+
 def test_softmax_is_deterministic():
     x, L = synth.ragged_softmax_inputs(64, 60000, seed=2800, choices=(1000, 59999, 60000))
     outs = [run(x, lengths=L, use_ws=True)[2] for _ in range(3)]
