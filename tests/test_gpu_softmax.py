@@ -210,6 +210,48 @@ def test_softmax_unaligned_rows_split(passes):
         assert np.isnan(yfull[r, n:]).all()
 
 
+def test_softmax_single_pass_graph_replays():
+    # the slot reset is a fill kernel, so the single pass can be recorded in
+    # a graph: every replay (after an eager call on other data through the
+    # same workspace, and a synchronisation) equals the eager result bit for bit
+    rows, cols = 96, 131072
+    x, L = synth.ragged_softmax_inputs(rows, cols, seed=2860)
+    x2, L2 = synth.ragged_softmax_inputs(rows, cols, seed=2861)
+    xd, Ld, x2d, L2d = dev(x), dev(L), dev(x2), dev(L2)
+    ws = torch.empty(fr.fr_softmax_rows_workspace_bytes(rows, cols) // 4, dtype=torch.int32, device="cuda")
+    y, y2 = torch.full_like(xd, float("nan")), torch.empty_like(xd)
+    am = torch.full((rows,), -7, dtype=torch.int32, device="cuda")
+    am2 = torch.empty_like(am)
+
+    def call():
+        fr.fr_softmax_rows(xd, y, lengths=Ld, argmax=am, ws=ws)
+
+    call()
+    torch.cuda.synchronize()
+    ref_y, ref_am = host(y), host(am)
+    compare(x, ref_y, ref_am, lengths=L, what="eager single pass")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    valid = valid_mask(rows, cols, L)
+    for rep in range(4):
+        y.fill_(0.0)
+        am.fill_(-7)
+        fr.fr_softmax_rows(x2d, y2, lengths=L2d, argmax=am2, ws=ws)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        yr = host(y)
+        assert np.array_equal(yr[valid].view(np.uint32), ref_y[valid].view(np.uint32)), rep
+        assert np.array_equal(host(am), ref_am), rep
+
+
 def test_softmax_is_deterministic():
     x, L = synth.ragged_softmax_inputs(64, 60000, seed=2800, choices=(1000, 59999, 60000))
     outs = [run(x, lengths=L, use_ws=True)[2] for _ in range(3)]
