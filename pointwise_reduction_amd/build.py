@@ -7,6 +7,7 @@ here), then linked into pointwise_reduction_amd/libfr.so.
 """
 import concurrent.futures
 import glob
+import re
 import os
 import shutil
 import subprocess
@@ -59,6 +60,24 @@ def parse_resource_usage(lines):
     return usage
 
 
+def check_residency(usage):
+    """The single-pass split softmax sizes its grid so that all of its
+    workgroups are resident at once, from the occupancy the planner assumes
+    for the 256-thread, 8-vector kernel. A kernel compiled to fewer waves per
+    SIMD would still be correct (a workgroup that waits too long computes the
+    missing partials itself) but part of the grid would start only when
+    others end; measured 14% slower. Fail the build instead."""
+    with open(os.path.join(CSRC, "fr_plan.cpp")) as f:
+        m = re.search(r"constexpr int kOnePassWavesPerSimd = (\d+);", f.read())
+    if not m:
+        raise RuntimeError("fr_plan.cpp: kOnePassWavesPerSimd not found")
+    need = int(m.group(1))
+    low = sorted(n for n, u in usage.items()
+                 if "fr_split_softmax_oneILi256ELi8E" in n and u.get("occupancy", 0) < need)
+    if low:
+        raise RuntimeError(f"kernels below the {need} waves per SIMD their grid assumes: " + ", ".join(low))
+
+
 def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
@@ -98,6 +117,7 @@ def build(verbose=False, jobs=None):
     spills = sorted(n for n, u in usage.items() if u.get("scratch", 0) > 0)
     if spills:  # Algorithm 9.1 rejects configurations that spill registers
         raise RuntimeError("kernels spill registers to scratch: " + ", ".join(spills))
+    check_residency(usage)
     tmp = LIB + ".tmp"
     cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     if verbose:

@@ -368,3 +368,11 @@ def test_region_object_without_a_gpu():
     assert fr.lib.fr_region_run(r._r, None, 8, fr._REGION_FN(lambda c, s: 0), None, None) == fr.FR_E_NULL
     assert fr.lib.fr_region_state(None) == fr.FR_E_NULL
     del r
+
+
+def test_build_rejects_a_single_pass_kernel_below_the_occupancy_its_grid_assumes():
+    from pointwise_reduction_amd import build as b
+    name = "_ZN2fr20fr_split_softmax_oneILi256ELi8ELb1EEEvPKfPf"
+    b.check_residency({name: {"occupancy": 4, "vgpr": 111}})
+    with pytest.raises(RuntimeError, match="waves per SIMD"):
+        b.check_residency({name: {"occupancy": 3, "vgpr": 131}})
