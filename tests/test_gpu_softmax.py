@@ -210,6 +210,41 @@ def test_softmax_unaligned_rows_split(passes):
         assert np.isnan(yfull[r, n:]).all()
 
 
+@pytest.mark.parametrize("seed", [3101, 3102, 3103])
+def test_softmax_single_pass_random_ragged(seed):
+    """Seeded random shapes through the single pass: row counts, capacities
+    and lengths drawn around the chunk size (8192), with empty rows, rows of
+    one element and rows that end one element before or after a chunk edge."""
+    rng = np.random.default_rng(seed)
+    rows = int(rng.integers(1, 200))
+    cols = int(rng.integers(8193, 160000))
+    edges = [0, 1, 8191, 8192, 8193, 16383, 16385, cols - 1, cols]
+    L = np.where(rng.random(rows) < 0.5, rng.choice(edges, rows), rng.integers(0, cols + 1, rows))
+    L = np.clip(L, 0, cols).astype(np.int32)
+    x, _ = synth.ragged_softmax_inputs(rows, cols, seed=seed, lengths=L)
+    try:
+        fr.fr_tune_override(fr.FR_OP_SOFTMAX, form=fr.FR_FORM_SPLIT, threads=256, vec=8, passes=1)
+        y, am, yfull = run(x, lengths=L, use_ws=True)
+    finally:
+        fr.fr_tune_override(fr.FR_OP_SOFTMAX)
+    compare(x, y, am, lengths=L, what=f"single pass {rows}x{cols} seed {seed}")
+    for r, n in enumerate(L):
+        assert np.isnan(yfull[r, n:]).all(), f"row {r}: output tail beyond len {n} was written"
+
+
+def test_softmax_single_pass_most_rows():
+    """The largest row count the single pass takes (its chunk list lives in
+    LDS): 2048 rows, each thread of the list scan counting 8 of them."""
+    rows, cols = 2048, 9000
+    x, L = synth.ragged_softmax_inputs(rows, cols, seed=3110, choices=(0, 1, 4000, 8192, 8193, 9000))
+    try:
+        fr.fr_tune_override(fr.FR_OP_SOFTMAX, form=fr.FR_FORM_SPLIT, threads=256, vec=8, passes=1)
+        y, am, _ = run(x, lengths=L, use_ws=True)
+    finally:
+        fr.fr_tune_override(fr.FR_OP_SOFTMAX)
+    compare(x, y, am, lengths=L, what="single pass 2048 rows")
+
+
 def test_softmax_single_pass_graph_replays():
     # the slot reset is a fill kernel, so the single pass can be recorded in
     # a graph: every replay (after an eager call on other data through the
