@@ -193,6 +193,10 @@ uint64_t fr_sum_workspace_bytes(int64_t rows, int64_t cols, int dtype);
  *            single-pass split computed a second time because their owner
  *            had not published them within plan.wait_us (a diagnostic: the
  *            results are the same either way).
+ *  In place: when y shares memory with x, a split takes its two-kernel form
+ *  (the single pass may read a partner's chunk of x after that partner has
+ *  written y there); a tuning override that forces the single pass on such
+ *  a call returns FR_E_ARG.
  * A NaN in a row makes that row's outputs NaN. dtype must be FR_F32. */
 uint64_t fr_softmax_rows_workspace_bytes(int64_t rows, int64_t cols, int dtype);
 int fr_softmax_rows(const void* x, void* y, int64_t rows, int64_t cols, int64_t x_rs, int64_t x_cs, int64_t y_rs,
@@ -392,6 +396,20 @@ int fr_attn_block(const void* q, const void* k, const void* v, void* o, float* l
 #define FR_STREAM_SINK_WORDS 1024
 int fr_stream_copy(const void* x, void* y, int64_t nbytes, void* stream);
 int fr_stream_read(const void* x, int64_t nbytes, uint32_t* sink, void* stream);
+
+/* ------------------------------------------------------------ device clock marks
+ * fr_device_clock enqueues a one-lane kernel that stores the device's
+ * constant wall-clock counter into out[slot] (out: device array of uint64,
+ * 8-byte aligned, at least slot + 1 entries; the caller owns it). Two marks
+ * around a sequence of launches on one stream give the device time of exactly
+ * that sequence, stream order making each mark wait for the work before it;
+ * it is how a benchmark times K steps apart from the host's submission of
+ * them ("Stax (4)", 9.6: device timing carries about 1% noise, so timings
+ * are repeated). fr_device_clock_khz gives the counter's rate in kHz for the
+ * current device. FR_E_NULL / FR_E_ARG / FR_E_ALIGN on bad arguments,
+ * FR_E_DEVICE if the device is not gfx950. */
+int fr_device_clock(uint64_t* out, int slot, void* stream);
+int fr_device_clock_khz(int* khz);
 
 /* ------------------------------------------------------------ configuration search
  * "Stax (4)", 9.6: choosing a launch configuration is black-box optimisation

@@ -8,8 +8,13 @@ share no code: the only common dependency is the seeded input generator
 
 The arithmetic lives in ``oracle.c`` (plain C, fp64, sequential loops; each
 function cites the passage it implements). This module only compiles it with
-gcc and marshals numpy arrays through ctypes.
+gcc and marshals numpy arrays through ctypes. Row-wise functions take a
+``threads`` argument: rows are independent, so a large call hands contiguous
+row ranges to that many threads, each running the same C loop over its
+rows (ctypes releases the GIL). Every row's arithmetic is unchanged, so the
+results do not depend on the thread count.
 """
+import concurrent.futures
 import ctypes
 import os
 import subprocess
@@ -74,6 +79,31 @@ def _p(a):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
 
+def host_threads():
+    """The CPUs this process may run on."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def _row_ranges(rows, cols, threads):
+    """Contiguous row ranges, one per thread; one range for small calls."""
+    if threads is None:
+        threads = min(16, host_threads()) if rows * max(cols, 1) >= (1 << 20) else 1
+    t = max(1, min(int(threads), rows))
+    step = (rows + t - 1) // t if rows else 1
+    return [(r0, min(rows, r0 + step)) for r0 in range(0, rows, step)] or [(0, 0)]
+
+
+def _run_ranges(ranges, fn):
+    if len(ranges) == 1:
+        fn(*ranges[0])
+        return
+    with concurrent.futures.ThreadPoolExecutor(len(ranges)) as ex:
+        list(ex.map(lambda rr: fn(*rr), ranges))
+
+
 def _rows2d(x, dtype):
     """Return (array, rows, cols, row_stride) for a 2-D array whose inner stride is 1."""
     x = np.asarray(x)
@@ -104,14 +134,17 @@ def round_bf16(v):
 # ------------------------------------------------------------------ C1
 
 
-def sum_relu_add(a, b):
+def sum_relu_add(a, b, threads=None):
     """out[i] = sum_r 2*relu(a[i,r]+b[i,r]); returns (out fp32, out fp64)."""
     a, rows, cols, a_rs = _rows2d(a, np.float32)
     b, rows_b, cols_b, b_rs = _rows2d(b, np.float32)
     assert (rows, cols) == (rows_b, cols_b)
     out = np.empty(rows, dtype=np.float32)
     out64 = np.empty(rows, dtype=np.float64)
-    _load().orc_sum_relu_add(_p(a), _p(b), rows, cols, a_rs, b_rs, _p(out), _p(out64))
+    f = _load().orc_sum_relu_add
+    _run_ranges(_row_ranges(rows, cols, threads),
+                lambda r0, r1: f(_p(a[r0:r1]), _p(b[r0:r1]), r1 - r0, cols, a_rs, b_rs, _p(out[r0:r1]),
+                                 _p(out64[r0:r1])))
     return out, out64
 
 
@@ -125,7 +158,7 @@ def softmax_f64(x):
     return y
 
 
-def softmax_rows(x, lengths=None, cols=None):
+def softmax_rows(x, lengths=None, cols=None, threads=None):
     """Row softmax of fp32 rows (ragged when `lengths` is given).
 
     x may be a 2-D view with unit inner stride. `cols` (default x.shape[1]) is
@@ -142,8 +175,14 @@ def softmax_rows(x, lengths=None, cols=None):
         assert L.shape == (rows,)
     y64 = np.full((rows, cols), np.nan, dtype=np.float64)
     am = np.empty(rows, dtype=np.int32)
-    scratch = np.empty(2 * max(cols, 1), dtype=np.float64)
-    _load().orc_softmax_rows(_p(x), rows, cols, x_rs, _p(L), None, _p(y64), cols, _p(am), _p(scratch))
+    f = _load().orc_softmax_rows
+
+    def run(r0, r1):
+        scratch = np.empty(2 * max(cols, 1), dtype=np.float64)
+        f(_p(x[r0:r1]), r1 - r0, cols, x_rs, None if L is None else _p(L[r0:r1]), None, _p(y64[r0:r1]), cols,
+          _p(am[r0:r1]), _p(scratch))
+
+    _run_ranges(_row_ranges(rows, cols, threads), run)
     return y64, am
 
 
@@ -260,7 +299,7 @@ def attn_merge(p1, p2):
 # ------------------------------------------------------------------ LayerNorm
 
 
-def layernorm_rows(x_bf16, gamma=None, beta=None, eps=1e-5):
+def layernorm_rows(x_bf16, gamma=None, beta=None, eps=1e-5, threads=None):
     """LayerNorm over rows of bf16 bits (uint16). Returns (y_bf16, y64, mag)."""
     x, rows, cols, x_rs = _rows2d(x_bf16, np.uint16)
     g = None if gamma is None else np.ascontiguousarray(gamma, dtype=np.uint16)
@@ -268,7 +307,10 @@ def layernorm_rows(x_bf16, gamma=None, beta=None, eps=1e-5):
     y = np.empty((rows, cols), dtype=np.uint16)
     y64 = np.empty((rows, cols), dtype=np.float64)
     mag = np.empty((rows, cols), dtype=np.float64)
-    _load().orc_layernorm_rows(_p(x), _p(g), _p(b), rows, cols, x_rs, float(eps), _p(y), _p(y64), _p(mag), cols)
+    f = _load().orc_layernorm_rows
+    _run_ranges(_row_ranges(rows, cols, threads),
+                lambda r0, r1: f(_p(x[r0:r1]), _p(g), _p(b), r1 - r0, cols, x_rs, float(eps), _p(y[r0:r1]),
+                                 _p(y64[r0:r1]), _p(mag[r0:r1]), cols))
     return y, y64, mag
 
 
@@ -304,15 +346,34 @@ def layernorm_backward_rows(x_bf16, dy_bf16, gamma, mean, rstd):
 # ------------------------------------------------------------------ sum of squares
 
 
-def sumsq(x):
+def sumsq(x, threads=1):
+    """sum of x^2 in fp64. threads > 1 (the all-cores timing leg only) sums
+    equal contiguous slices on separate threads and adds the slice sums in
+    slice order: the same terms in another fp64 order, a difference far
+    below any tolerance. Parity checks use the sequential sum (threads=1)."""
     x = np.ascontiguousarray(x, dtype=np.float32).reshape(-1)
-    return float(_load().orc_sumsq(_p(x), x.size))
+    f = _load().orc_sumsq
+    t = max(1, min(int(threads), x.size))
+    if t == 1:
+        return float(f(_p(x), x.size))
+    step = (x.size + t - 1) // t
+    parts = [None] * t
+    def run(i):
+        seg = x[i * step:(i + 1) * step]
+        parts[i] = float(f(_p(seg), seg.size))
+    with concurrent.futures.ThreadPoolExecutor(t) as ex:
+        list(ex.map(run, range(t)))
+    total = 0.0
+    for v in parts:
+        total += v
+    return total
 
 
-def sumsq_rows(x):
+def sumsq_rows(x, threads=None):
     x, rows, cols, rs = _rows2d(x, np.float32)
     out = np.empty(rows, dtype=np.float64)
-    _load().orc_sumsq_rows(_p(x), rows, cols, rs, _p(out))
+    f = _load().orc_sumsq_rows
+    _run_ranges(_row_ranges(rows, cols, threads), lambda r0, r1: f(_p(x[r0:r1]), r1 - r0, cols, rs, _p(out[r0:r1])))
     return out
 
 

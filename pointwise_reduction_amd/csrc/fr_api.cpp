@@ -109,6 +109,17 @@ int check_matrix(const void* p, int64_t rows, int64_t cols, int64_t rs, int64_t 
     return FR_OK;
 }
 
+// Do two row-major operands share any byte? Each spans from its base to the
+// end of its last row.
+bool spans_overlap(const void* p, int64_t p_rs, const void* q, int64_t q_rs, int64_t rows, int64_t cols,
+                   size_t elem) {
+    if (!p || !q || rows == 0 || cols == 0) return false;
+    const uintptr_t a0 = (uintptr_t)p, b0 = (uintptr_t)q;
+    const uintptr_t a1 = a0 + (uintptr_t)(((rows - 1) * p_rs + cols) * (int64_t)elem);
+    const uintptr_t b1 = b0 + (uintptr_t)(((rows - 1) * q_rs + cols) * (int64_t)elem);
+    return a0 < b1 && b0 < a1;
+}
+
 bool vec_ok(const void* p, int64_t rs, int64_t elems_per_vec) {
     return p == nullptr || (((uintptr_t)p % 16) == 0 && rs % elems_per_vec == 0);
 }
@@ -321,10 +332,24 @@ int fr_softmax_rows(const void* x, void* y, int64_t rows, int64_t cols, int64_t 
     st = device_check(&num_cus, &clock_khz);
     if (st != FR_OK) return st;
     const int v16 = vec_ok(x, x_rs, 4) && vec_ok(y, y_rs, 4);
+    const fr_plan* ov = override_for(FR_OP_SOFTMAX, rows, cols, FR_F32);
     fr_plan plan;
     st = make_plan(FR_OP_SOFTMAX, rows, cols, FR_F32, num_cus, lengths != nullptr, ws ? ws_bytes : 0, v16,
-                   g_forced_form, override_for(FR_OP_SOFTMAX, rows, cols, FR_F32), &plan);
+                   g_forced_form, ov, &plan);
     if (st != FR_OK) return st;
+    // The single-pass split recomputes a late partner's chunk partial from
+    // x, and by then that partner may have overwritten its chunk with y. When
+    // x and y share memory the split takes two kernels instead (every element
+    // is read before it is written, by the same thread); a tuning override
+    // that asks for the single pass is an argument error.
+    if (plan.form == FR_FORM_SPLIT && plan.passes == 1 && spans_overlap(x, x_rs, y, y_rs, rows, cols, 4)) {
+        if (g_has_override[FR_OP_SOFTMAX] && ov && ov->passes == 1) return FR_E_ARG;
+        fr_plan two = ov ? *ov : plan;
+        two.passes = 2;
+        st = make_plan(FR_OP_SOFTMAX, rows, cols, FR_F32, num_cus, lengths != nullptr, ws ? ws_bytes : 0, v16,
+                       g_forced_form, &two, &plan);
+        if (st != FR_OK) return st;
+    }
     const int64_t wait_ticks = plan.wait_us > 0 ? (int64_t)plan.wait_us * clock_khz / 1000 : (plan.wait_us < 0 ? -1 : 0);
     SoftmaxArgs args{(const float*)x, (float*)y, (int)rows, (int)cols, x_rs, y_rs, lengths, argmax, ws, wait_ticks};
     (void)hipGetLastError();
@@ -537,6 +562,26 @@ int fr_stream_read(const void* x, int64_t nbytes, uint32_t* sink, void* stream) 
     if (st != FR_OK) return st;
     (void)hipGetLastError();
     return finish_launch(launch_stream_read(x, nbytes / 16, sink, (hipStream_t)stream));
+}
+
+int fr_device_clock(uint64_t* out, int slot, void* stream) {
+    if (!out) return FR_E_NULL;
+    if (slot < 0) return FR_E_ARG;
+    if (!aligned(out, 8)) return FR_E_ALIGN;
+    int num_cus = 0;
+    const int st = device_check(&num_cus);
+    if (st != FR_OK) return st;
+    (void)hipGetLastError();
+    return finish_launch(launch_device_clock(out, slot, (hipStream_t)stream));
+}
+
+int fr_device_clock_khz(int* khz) {
+    if (!khz) return FR_E_NULL;
+    int num_cus = 0, clock_khz = 0;
+    const int st = device_check(&num_cus, &clock_khz);
+    if (st != FR_OK) return st;
+    *khz = clock_khz;
+    return FR_OK;
 }
 
 int fr_add_2d(const void* a, int64_t a_rs, int64_t a_cs, const void* b, int64_t b_rs, int64_t b_cs, void* out,

@@ -4,8 +4,10 @@ This package draws numbers and does nothing else: it holds none of the
 arithmetic of the reductions. Both ``oracle`` and the tests/benchmark of
 ``pointwise_reduction_amd`` consume what it produces; it imports neither.
 
-The generator is a counter-based SplitMix64 written in C (``synth.c``), so a
-1 GiB input takes about a second. Every function returns numpy arrays.
+The generator is a counter-based SplitMix64 written in C (``synth.c``). Being
+counter based, any slice of a stream can be drawn on its own, so large arrays
+are drawn in slices on a few threads (ctypes releases the GIL); the values do
+not depend on the split. Every function returns numpy arrays.
 
 Workload recipes (the sizes and distributions of the five configurations):
 
@@ -16,6 +18,7 @@ Workload recipes (the sizes and distributions of the five configurations):
 * ``ragged_softmax_inputs`` lengths from {1000, 3000, 50257, 131071}, x ~ N(0,1)*3,
                             padded tail filled with NaN.
 """
+import concurrent.futures
 import ctypes
 import os
 import subprocess
@@ -47,11 +50,11 @@ def _load():
     lib = ctypes.CDLL(_SO)
     sig = {
         "syn_u64": (U64, [U64, U64, U64]),
-        "syn_uniform_f32": (None, [P, I64, U64, U64, F64, F64]),
-        "syn_normal_f32": (None, [P, I64, U64, U64, F64, F64]),
-        "syn_spiky_normal_rows": (None, [P, I64, I64, I64, U64, F64, F64, F64]),
+        "syn_uniform_f32_at": (None, [P, I64, U64, U64, I64, F64, F64]),
+        "syn_normal_f32_at": (None, [P, I64, U64, U64, I64, F64, F64]),
+        "syn_spiky_normal_rows_range": (None, [P, I64, I64, I64, I64, U64, F64, F64, F64]),
         "syn_lengths": (None, [P, I64, U64, P, I32]),
-        "syn_ragged_normal_rows": (None, [P, I64, I64, P, U64, F64, F64, ctypes.c_float]),
+        "syn_ragged_normal_rows_range": (None, [P, I64, I64, I64, P, U64, F64, F64, ctypes.c_float]),
         "syn_pick_cells": (I32, [I64, I64, U64, U64, I32, P, P]),
         "syn_f32_to_bf16": (None, [P, P, I64]),
         "syn_bf16_to_f32": (None, [P, P, I64]),
@@ -68,19 +71,48 @@ def _p(a):
     return a.ctypes.data_as(ctypes.c_void_p)
 
 
+def _addr(a, offset_elems=0):
+    return ctypes.c_void_p(a.ctypes.data + offset_elems * a.itemsize)
+
+
+def threads():
+    """Threads for large draws: the CPUs this process may run on, at most 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+_SLICE_MIN = 1 << 20  # below this many units one thread does it all
+
+
+def _parallel(n, fn):
+    """Run fn(lo, hi) over [0, n) in contiguous slices, one per thread."""
+    t = threads() if n >= _SLICE_MIN else 1
+    if t <= 1:
+        fn(0, n)
+        return
+    step = (n + t - 1) // t
+    with concurrent.futures.ThreadPoolExecutor(t) as ex:
+        list(ex.map(lambda lo: fn(lo, min(n, lo + step)), range(0, n, step)))
+
+
 def u64(seed, stream, i):
     return int(_load().syn_u64(seed, stream, i))
 
 
 def uniform(shape, seed, stream=0, lo=-1.0, hi=1.0):
     out = np.empty(shape, dtype=np.float32)
-    _load().syn_uniform_f32(_p(out), out.size, seed, stream, lo, hi)
+    f = _load().syn_uniform_f32_at
+    _parallel(out.size, lambda a, b: f(_addr(out, a), b - a, seed, stream, a, lo, hi))
     return out
 
 
 def normal(shape, seed, stream=0, mean=0.0, std=1.0):
     out = np.empty(shape, dtype=np.float32)
-    _load().syn_normal_f32(_p(out), out.size, seed, stream, mean, std)
+    f = _load().syn_normal_f32_at
+    _parallel(out.size, lambda a, b: f(_addr(out, a), b - a, seed, stream, a, mean, std))
     return out
 
 
@@ -88,15 +120,28 @@ def to_bf16(x):
     """fp32 array -> bf16 bit patterns (uint16), round to nearest even."""
     x = np.ascontiguousarray(x, dtype=np.float32)
     out = np.empty(x.shape, dtype=np.uint16)
-    _load().syn_f32_to_bf16(_p(x), _p(out), x.size)
+    f = _load().syn_f32_to_bf16
+    _parallel(x.size, lambda a, b: f(_addr(x, a), _addr(out, a), b - a))
     return out
 
 
 def bf16_to_f32(b):
     b = np.ascontiguousarray(b, dtype=np.uint16)
     out = np.empty(b.shape, dtype=np.float32)
-    _load().syn_bf16_to_f32(_p(b), _p(out), b.size)
+    f = _load().syn_bf16_to_f32
+    _parallel(b.size, lambda a, c: f(_addr(b, a), _addr(out, a), c - a))
     return out
+
+
+def _parallel_rows(rows, row_elems, fn):
+    """Run fn(r0, r1) over row ranges; slices hold whole rows."""
+    if rows * row_elems < _SLICE_MIN or rows < 2:
+        fn(0, rows)
+        return
+    t = min(threads(), rows)
+    step = (rows + t - 1) // t
+    with concurrent.futures.ThreadPoolExecutor(t) as ex:
+        list(ex.map(lambda r0: fn(r0, min(rows, r0 + step)), range(0, rows, step)))
 
 
 def pick_cells(rows, cols, seed, stream, count):
@@ -127,7 +172,8 @@ def sum_relu_add_inputs(rows=64, cols=128, seed=1001, n_nan=0):
 def softmax_inputs(rows=4096, cols=1024, seed=2001, scale=4.0, p_spike=0.01, spike=30.0, row_stride=None):
     rs = cols if row_stride is None else row_stride
     x = np.zeros((rows, rs), dtype=np.float32)
-    _load().syn_spiky_normal_rows(_p(x), rows, cols, rs, seed, scale, p_spike, spike)
+    f = _load().syn_spiky_normal_rows_range
+    _parallel_rows(rows, cols, lambda r0, r1: f(_p(x), r0, r1, cols, rs, seed, scale, p_spike, spike))
     return x
 
 
@@ -158,7 +204,8 @@ def ragged_softmax_inputs(rows=512, row_stride=131072, seed=5001, choices=RAGGED
     """x ~ N(0,1)*std over each row's valid prefix; the padded tail holds `tail`."""
     L = ragged_lengths(rows, seed, choices) if lengths is None else np.ascontiguousarray(lengths, dtype=np.int32)
     x = np.empty((rows, row_stride), dtype=np.float32)
-    _load().syn_ragged_normal_rows(_p(x), rows, row_stride, _p(L), seed, 0.0, std, tail)
+    f = _load().syn_ragged_normal_rows_range
+    _parallel_rows(rows, row_stride, lambda r0, r1: f(_p(x), r0, r1, row_stride, _p(L), seed, 0.0, std, tail))
     return x, L
 
 

@@ -47,17 +47,28 @@ static inline double std_normal(uint64_t key, uint64_t i) {
 
 uint64_t syn_u64(uint64_t seed, uint64_t stream, uint64_t i) { return draw(stream_key(seed, stream), i); }
 
-void syn_uniform_f32(float* out, int64_t n, uint64_t seed, uint64_t stream, double lo, double hi) {
+/* Values i0 .. i0+n-1 of a stream into out[0 .. n): a counter-based draw, so
+ * any slice can be produced on its own (callers split large arrays across
+ * threads; the values do not depend on the split). */
+void syn_uniform_f32_at(float* out, int64_t n, uint64_t seed, uint64_t stream, int64_t i0, double lo, double hi) {
     uint64_t key = stream_key(seed, stream);
     for (int64_t i = 0; i < n; ++i) {
-        double u = (double)(draw(key, (uint64_t)i) >> 40) * 0x1.0p-24;
+        double u = (double)(draw(key, (uint64_t)(i0 + i)) >> 40) * 0x1.0p-24;
         out[i] = (float)(lo + (hi - lo) * u);
     }
 }
 
-void syn_normal_f32(float* out, int64_t n, uint64_t seed, uint64_t stream, double mean, double std) {
+void syn_normal_f32_at(float* out, int64_t n, uint64_t seed, uint64_t stream, int64_t i0, double mean, double std) {
     uint64_t key = stream_key(seed, stream);
-    for (int64_t i = 0; i < n; ++i) out[i] = (float)(mean + std * std_normal(key, (uint64_t)i));
+    for (int64_t i = 0; i < n; ++i) out[i] = (float)(mean + std * std_normal(key, (uint64_t)(i0 + i)));
+}
+
+void syn_uniform_f32(float* out, int64_t n, uint64_t seed, uint64_t stream, double lo, double hi) {
+    syn_uniform_f32_at(out, n, seed, stream, 0, lo, hi);
+}
+
+void syn_normal_f32(float* out, int64_t n, uint64_t seed, uint64_t stream, double mean, double std) {
+    syn_normal_f32_at(out, n, seed, stream, 0, mean, std);
 }
 
 /*
@@ -66,12 +77,12 @@ void syn_normal_f32(float* out, int64_t n, uint64_t seed, uint64_t stream, doubl
  * Rows are `cols` long at a row stride of `rs` elements; only the first
  * `cols` of each row are written.
  */
-void syn_spiky_normal_rows(float* out, int64_t rows, int64_t cols, int64_t rs, uint64_t seed,
-                           double scale, double p_spike, double spike) {
+void syn_spiky_normal_rows_range(float* out, int64_t r0, int64_t r1, int64_t cols, int64_t rs, uint64_t seed,
+                                 double scale, double p_spike, double spike) {
     uint64_t kn = stream_key(seed, 0), ks = stream_key(seed, 1);
     uint64_t thresh = (uint64_t)(p_spike * 18446744073709551616.0);
     if (p_spike >= 1.0) thresh = UINT64_MAX;
-    for (int64_t r = 0; r < rows; ++r)
+    for (int64_t r = r0; r < r1; ++r)
         for (int64_t c = 0; c < cols; ++c) {
             uint64_t i = (uint64_t)(r * cols + c);
             uint64_t s = draw(ks, i);
@@ -81,6 +92,11 @@ void syn_spiky_normal_rows(float* out, int64_t rows, int64_t cols, int64_t rs, u
         }
 }
 
+void syn_spiky_normal_rows(float* out, int64_t rows, int64_t cols, int64_t rs, uint64_t seed,
+                           double scale, double p_spike, double spike) {
+    syn_spiky_normal_rows_range(out, 0, rows, cols, rs, seed, scale, p_spike, spike);
+}
+
 /* Each row length is drawn uniformly from `choices[0..nchoices)`. */
 void syn_lengths(int32_t* len, int64_t rows, uint64_t seed, const int32_t* choices, int32_t nchoices) {
     uint64_t key = stream_key(seed, 7);
@@ -88,14 +104,19 @@ void syn_lengths(int32_t* len, int64_t rows, uint64_t seed, const int32_t* choic
 }
 
 /* Ragged rows: N(mean, std) over j < len[r]; the padded tail j >= len[r] is set to `tail`. */
-void syn_ragged_normal_rows(float* out, int64_t rows, int64_t rs, const int32_t* len, uint64_t seed,
-                            double mean, double std, float tail) {
+void syn_ragged_normal_rows_range(float* out, int64_t r0, int64_t r1, int64_t rs, const int32_t* len,
+                                  uint64_t seed, double mean, double std, float tail) {
     uint64_t key = stream_key(seed, 0);
-    for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t r = r0; r < r1; ++r) {
         int64_t L = len[r];
         for (int64_t c = 0; c < rs; ++c)
             out[r * rs + c] = c < L ? (float)(mean + std * std_normal(key, (uint64_t)(r * rs + c))) : tail;
     }
+}
+
+void syn_ragged_normal_rows(float* out, int64_t rows, int64_t rs, const int32_t* len, uint64_t seed,
+                            double mean, double std, float tail) {
+    syn_ragged_normal_rows_range(out, 0, rows, rs, len, seed, mean, std, tail);
 }
 
 /*

@@ -6,6 +6,8 @@ rounds an fp32 result), or - where y is a near-cancellation of its terms -
 within 1e-5 * (|(x - mu) * rstd * gamma| + |beta|) + 1e-6 of the exact
 value. Bit-exact pin: a constant row gives exactly beta.
 """
+import functools
+
 import numpy as np
 import pytest
 
@@ -37,12 +39,21 @@ def compare(x, g, b, got, rows=None, eps=1e-5, what=""):
     check_bf16(gs, ref, y64, mag, what=what)
 
 
-@pytest.mark.parametrize("form", ["per", "red"])
-def test_layernorm_2048x32768_sampled(form):
-    x, g, b = synth.layernorm_inputs(2048, 32768, seed=3001)
-    got = gpu_ln(x, g, b, form=FORMS[form])
-    rows = np.unique(np.concatenate([[0, 1, 1023, 2047], np.random.default_rng(3).integers(0, 2048, 60)]))
-    compare(x, g, b, got, rows=rows, what=f"2048x32768 {form}")
+@functools.lru_cache(maxsize=1)
+def full_case(seed):
+    """The 2048 x 32768 workload and its oracle result (kept for the next form)."""
+    x, g, b = synth.layernorm_inputs(2048, 32768, seed=seed)
+    return (x, g, b) + oracle.layernorm_rows(x, g, b)
+
+
+@pytest.mark.parametrize("form", ["auto", "red"])
+@pytest.mark.parametrize("seed", [3001, 3002, 3003])
+def test_layernorm_2048x32768_full(form, seed):
+    """Every row of the full workload, at three seeds: the automatic plan (the
+    launch the benchmark times) and the looped form."""
+    x, g, b, ref, y64, mag = full_case(seed)
+    got = gpu_ln(x, g, b, form=fr.FR_FORM_AUTO if form == "auto" else FORMS[form])
+    check_bf16(got, ref, y64, mag, what=f"2048x32768 {form} seed {seed}")
 
 
 SHAPES = [(1, 8), (7, 13), (33, 31), (65, 33), (4, 4096), (3, 1000), (5, 32768), (2, 40000), (3, 16385)]

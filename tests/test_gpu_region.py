@@ -3,16 +3,18 @@
 A region records the example 1.1 sums (64 x 128, the tiny shape whose time
 is launch overhead) and a small softmax on a side stream, then is replayed
 several times with new input values copied into the recorded buffers and
-eager work in between; every replay must equal an eager run bit for bit
-(the same kernels on the same inputs). A different key runs directly and
+eager work in between; every replay must match the fp64 oracle on the
+values it was given (the shared tolerance rule) and equal an eager run bit
+for bit (the same kernels on the same inputs). A different key runs directly and
 keeps the recording; the legacy default stream cannot be captured and sends
 the region to its fallback state, where results stay correct.
 """
 import numpy as np
 import pytest
 
+import oracle
 import synth
-from gpu_util import dev, host
+from gpu_util import check_fp32, dev, host
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -47,6 +49,14 @@ def eager(buf):
     return host(out), host(y)
 
 
+def check_oracle(buf, what):
+    """The region's outputs against the oracle on the inputs it read."""
+    _, ref = oracle.sum_relu_add(host(buf["a"]), host(buf["b"]))
+    check_fp32(host(buf["out"]), ref, what=f"{what}: sum_relu_add")
+    y64, _ = oracle.softmax_rows(host(buf["x"]))
+    check_fp32(host(buf["y"]), y64, what=f"{what}: softmax")
+
+
 def test_region_records_then_replays_new_values():
     buf = buffers(1001)
     side = torch.cuda.Stream()
@@ -55,6 +65,7 @@ def test_region_records_then_replays_new_values():
         region.run(key_of(buf), region_fn(buf))
     side.synchronize()
     assert region.state == fr.FR_REGION_RECORDED and region.counts() == (1, 0)
+    check_oracle(buf, "recording run")
     want = eager(buf)
     assert np.array_equal(host(buf["out"]), want[0]) and np.array_equal(host(buf["y"]), want[1])
     for rep in range(4):
@@ -66,6 +77,7 @@ def test_region_records_then_replays_new_values():
         with torch.cuda.stream(side):
             region.run(key_of(buf), region_fn(buf))
         side.synchronize()
+        check_oracle(buf, f"replay {rep}")
         want = eager(buf)
         assert np.array_equal(host(buf["out"]), want[0]), rep
         assert np.array_equal(host(buf["y"]), want[1]), rep
@@ -82,6 +94,8 @@ def test_region_other_key_runs_directly():
         region.run(key_of(buf), region_fn(buf))      # recorded key again: replay
     side.synchronize()
     assert region.state == fr.FR_REGION_RECORDED and region.counts() == (2, 1)
+    check_oracle(buf, "replay after a direct run")
+    check_oracle(other, "direct run")
     want = eager(other)
     assert np.array_equal(host(other["out"]), want[0]) and np.array_equal(host(other["y"]), want[1])
 
@@ -92,6 +106,7 @@ def test_region_fallback_on_the_default_stream_and_on_errors():
     region.run(key_of(buf), region_fn(buf), stream=0)  # legacy default stream: cannot be captured
     torch.cuda.synchronize()
     assert region.state == fr.FR_REGION_FALLBACK and region.counts() == (0, 1)
+    check_oracle(buf, "fallback run")
     want = eager(buf)
     assert np.array_equal(host(buf["out"]), want[0])
     bad = fr.Region()

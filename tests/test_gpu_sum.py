@@ -112,9 +112,10 @@ def test_sum_relu_add_strides_and_empty():
 # ------------------------------------------------------------------ sum of squares
 
 
-def test_sumsq_full_2_28_and_determinism():
+@pytest.mark.parametrize("seed", [4001, 4002, 4003])
+def test_sumsq_full_2_28_and_determinism(seed):
     n = 1 << 28
-    x = synth.sumsq_inputs(n, seed=4001)
+    x = synth.sumsq_inputs(n, seed=seed)
     xd = dev(x)
     ws = torch.empty(fr.fr_sumsq_full_workspace_bytes(n) // 4, dtype=torch.float32, device="cuda")
     out = torch.zeros(1, dtype=torch.float32, device="cuda")
