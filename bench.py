@@ -1,6 +1,7 @@
 """Benchmark of the fused row-reduction kernels on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--warm] [--eager] [--procs N]
+                    [--reps R]
 
 A step is one pass of the whole operation over one batch of synthetic input
 already resident in HBM. The default workload is the row softmax over
@@ -20,12 +21,20 @@ steps rotate through enough distinct buffer sets (>= 1 GiB in total) that
 the 256 MB MALL cannot serve a step's reads from the previous use of the same
 buffers (--warm uses one set). The K launches are captured once into a HIP
 graph and replayed, so host launch overhead does not enter the device time
-(--eager launches them one by one instead); the graph's output is checked
-against an eager launch before the timing is reported.
+(--eager launches them one by one instead). The graph starts with an
+untimed lead-in of one step per buffer set, so every set is touched once
+between two uses whatever K is; then a device clock mark, the K timed steps
+and a second mark. The marks' difference is the reported time: the device
+time of exactly the K steps. Events around a replay of the K steps alone
+(behind a lead-in replay) are reported beside it as events_ms_per_step;
+they also hold a fixed cost of the graph's edges. The graph's output is
+checked against an eager launch before the timing is reported.
 
-With --procs N the measurement runs in N separate processes, one after the
-other, and the line is the median process's, with all N values and their
-range under "procs".
+The measurement runs in --procs N (default 3) separate processes, one after
+the other; each times the K steps --reps R (default 3) times and reports the
+median, and the line is the median process's (the median of medians), with
+all N values and their range under "procs" ("hello-gpu, Chapter 12: Fusion",
+12.5: medians over independent processes).
 
 Output: one JSON line with the effective HBM bandwidth (logical bytes: each
 input read once, each output written once), the roofline entry for the
@@ -132,12 +141,13 @@ def make_workload(name, torch, fr, synth):
                         "launch": {"threads": p.threads, "lanes_per_row": p.seg, "vec16_per_lane": p.vec,
                                    "grid": p.grid}}
 
-            def oracle_fn(self):
+            def oracle_fn(self, threads=1):
                 import oracle
                 if rows == 4096:
-                    return lambda: oracle.softmax_rows(x_host), self.bytes, "full 4096x1024 batch"
+                    return (lambda: oracle.softmax_rows(x_host, threads=threads), self.bytes,
+                            "full 4096x1024 batch")
                 r = 4096
-                return (lambda: oracle.softmax_rows(x_host[:r]), softmax_bytes(r, cols),
+                return (lambda: oracle.softmax_rows(x_host[:r], threads=threads), softmax_bytes(r, cols),
                         f"first {r} of {rows} rows")
 
         return W(), per_set
@@ -170,13 +180,13 @@ def make_workload(name, torch, fr, synth):
                                     + (" (latency-bound)" if rows == 64 else ""),
                         "rows": rows, "cols": cols, "form": "per"}
 
-            def oracle_fn(self):
+            def oracle_fn(self, threads=1):
                 import oracle
                 if rows == 64:
-                    return lambda: oracle.sum_relu_add(a_h, b_h), self.bytes, "full 64x128 batch"
+                    return lambda: oracle.sum_relu_add(a_h, b_h, threads=threads), self.bytes, "full 64x128 batch"
                 r = 1 << 17
-                return (lambda: oracle.sum_relu_add(a_h[:r], b_h[:r]), sum_relu_add_bytes(r, cols),
-                        f"first {r} of {rows} rows")
+                return (lambda: oracle.sum_relu_add(a_h[:r], b_h[:r], threads=threads),
+                        sum_relu_add_bytes(r, cols), f"first {r} of {rows} rows")
 
         return W(), per_set
 
@@ -256,10 +266,10 @@ def make_workload(name, torch, fr, synth):
                 return {"workload": "LayerNorm bf16 [2048,32768], eps 1e-5", "rows": rows, "cols": cols,
                         "form": fr.FORM_NAMES[p.form], "launch": {"threads": p.threads, "vec16_per_lane": p.vec}}
 
-            def oracle_fn(self):
+            def oracle_fn(self, threads=1):
                 import oracle
-                r = 64
-                return (lambda: oracle.layernorm_rows(x_h[:r], g_h, b_h), layernorm_bytes(r, cols),
+                r = 128
+                return (lambda: oracle.layernorm_rows(x_h[:r], g_h, b_h, threads=threads), layernorm_bytes(r, cols),
                         f"first {r} of 2048 rows")
 
         return W(), per_set
@@ -291,10 +301,12 @@ def make_workload(name, torch, fr, synth):
                 return {"workload": "sum of x^2 over fp32 [2^28] to one scalar (split + finish)", "n": n,
                         "form": "split"}
 
-            def oracle_fn(self):
+            def oracle_fn(self, threads=1):
                 import oracle
                 m = 1 << 26
-                return lambda: oracle.sumsq(x_h[:m]), sumsq_bytes(m), "first 2^26 of 2^28 elements"
+                return (lambda: oracle.sumsq(x_h[:m], threads=threads), sumsq_bytes(m),
+                        "first 2^26 of 2^28 elements" + (", fixed slices per thread summed in slice order"
+                                                          if threads > 1 else ""))
 
         return W(), per_set
 
@@ -329,10 +341,10 @@ def make_workload(name, torch, fr, synth):
                                     "{1000,3000,50257,131071}", "rows": rows, "row_capacity": cap,
                         "valid_elements": int(L_h.sum()), "form": "split"}
 
-            def oracle_fn(self):
+            def oracle_fn(self, threads=1):
                 import oracle
-                r = 64
-                return (lambda: oracle.softmax_rows(x_h[:r], lengths=L_h[:r]),
+                r = 128
+                return (lambda: oracle.softmax_rows(x_h[:r], lengths=L_h[:r], threads=threads),
                         softmax_bytes(r, cap, lengths=L_h[:r], argmax=True), f"first {r} of 512 rows")
 
         return W(), per_set
@@ -684,7 +696,25 @@ def make_workload(name, torch, fr, synth):
 # ------------------------------------------------------------------ measurement
 
 
-def cpu_baseline(oracle_fn, budget_s):
+def host_facts():
+    """CPU model, the host's CPU count and the CPUs this process may use."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count() or 1
+    return {"cpu_model": model, "nproc": os.cpu_count(), "usable_cpus": usable}
+
+
+def time_oracle(oracle_fn, budget_s):
+    """GB/s of repeated oracle passes over about budget_s seconds."""
     fn, nbytes, sample = oracle_fn
     t0 = time.perf_counter()
     fn()
@@ -694,8 +724,29 @@ def cpu_baseline(oracle_fn, budget_s):
     for _ in range(reps):
         fn()
     dt = time.perf_counter() - t0
-    return {"value": round(nbytes * reps / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{sample}, {reps} passes in {dt:.1f} s, single thread, fp64"}
+    return nbytes * reps / dt / 1e9, reps, dt, sample
+
+
+def cpu_baseline(wl, budget_s):
+    """The fp64 oracle on the host's cores: one thread, then every usable
+    CPU (at most 16, the CPU share of one GPU) with rows split into
+    contiguous ranges. The all-cores leg is the reported value."""
+    facts = host_facts()
+    one, reps1, dt1, sample = time_oracle(wl.oracle_fn(), budget_s)
+    out = {"value": round(one, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+           "sample": f"{sample}, {reps1} passes in {dt1:.1f} s, single thread, fp64"}
+    threads = min(16, facts["usable_cpus"])
+    try:
+        fn_all = wl.oracle_fn(threads=threads)
+    except TypeError:
+        fn_all = None  # this workload's oracle has no row-parallel leg
+    if fn_all is not None and threads > 1:
+        allc, reps, dt, sample = time_oracle(fn_all, budget_s)
+        out = {"value": round(allc, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+               "sample": f"{sample}, {reps} passes in {dt:.1f} s, {threads} threads over row ranges, fp64",
+               "one_core": {"value": round(one, 4), "cores": 1, "passes": reps1, "seconds": round(dt1, 1)}}
+    out["host"] = facts
+    return out
 
 
 def read_traffic(kernel, workload):
@@ -740,18 +791,21 @@ def run_procs(args):
         argv.append(a)
     lines = []
     for i in range(args.procs):
-        r = subprocess.run([sys.executable, os.path.abspath(__file__)] + argv + (["--no-cpu"] if i else []),
-                           capture_output=True, text=True)
+        r = subprocess.run([sys.executable, os.path.abspath(__file__)] + argv + ["--procs", "1"] +
+                           (["--no-cpu"] if i else []), capture_output=True, text=True)
         if r.returncode != 0:
             sys.stderr.write(r.stderr)
             return r.returncode
         lines.append(json.loads([ln for ln in r.stdout.splitlines() if ln.startswith("{")][-1]))
+        print(f"bench.py: process {i + 1} of {args.procs}: {lines[-1]['value']} {lines[-1]['unit']}",
+              file=sys.stderr, flush=True)
     vals = [ln["value"] for ln in lines]
     med = sorted(range(len(lines)), key=lambda i: vals[i])[len(lines) // 2]
     out = dict(lines[med])
     if "cpu_baseline" in lines[0]:
         out["cpu_baseline"] = lines[0]["cpu_baseline"]
-    out["procs"] = {"n": len(lines), "values": vals, "median": vals[med], "min": min(vals), "max": max(vals)}
+    out["procs"] = {"n": len(lines), "values": vals, "median": vals[med], "min": min(vals), "max": max(vals),
+                    "per_process": "median of that process's timed repetitions"}
     print(json.dumps(out), flush=True)
     return 0
 
@@ -771,8 +825,10 @@ def main():
     ap.add_argument("--eager", action="store_true", help="launch each step from the host (no graph)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--procs", type=int, default=1,
+    ap.add_argument("--procs", type=int, default=3,
                     help="run the measurement in N separate processes and report the median (with the range)")
+    ap.add_argument("--reps", type=int, default=3,
+                    help="timed repetitions of the K steps in each process; the process reports their median")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -788,6 +844,7 @@ def main():
     import synth
 
     torch.cuda.set_device(0)
+    dev_name = "cuda"
     wl, per_set = make_workload(args.workload, torch, fr, synth)
     host_timed = getattr(wl, "host_timed", False)
     wl.eager = args.eager
@@ -796,7 +853,6 @@ def main():
         # legacy default stream) lets a recorded region record
         torch.cuda.set_stream(torch.cuda.Stream())
     sets = 1 if (args.warm or host_timed) else max(2, math.ceil(ROTATE_BYTES / per_set))
-    sets = min(sets, args.steps) if args.steps > 0 else sets
     wl.alloc(sets)
     # eager reference output of set 0
     wl.launch(0)
@@ -810,15 +866,38 @@ def main():
 
     from pointwise_reduction_amd import timing
 
-    graph = None if (args.eager or host_timed) else timing.capture(lambda k: wl.launch(k % sets), K)
+    # Step k of the timed region uses set k % sets. A lead-in of one step per
+    # set, in the same order, runs right before it: every set is then touched
+    # once between two uses (>= 1 GiB of other buffers, so no timed read is
+    # served from the 256 MB MALL, for any K), and the device is busy while
+    # the timed graph is submitted.
+    # The reported time comes from two device clock marks captured in the
+    # same graph right before the first and right after the last timed step
+    # (the lead-in runs first in that graph). Events around a replay of a
+    # graph of the K steps alone, behind a lead-in replay, are reported
+    # beside it: they add a fixed cost at the graph's edges.
+    graph = lead = marked = None
+    marks = torch.zeros(2, dtype=torch.int64, device=dev_name)
+    if not (args.eager or host_timed):
+        graph = timing.capture(lambda k: wl.launch(k % sets), K)
+        lead = timing.capture(lambda k: wl.launch(k % sets), sets)
+        marked = timing.capture_marked(lambda k: wl.launch(k % sets), sets, K,
+                                       lambda i: fr.fr_device_clock(marks, i))
+        clock_khz = fr.fr_device_clock_khz()
     # poison every output so the check below sees what the timed steps wrote
     for k in range(sets):
         wl.output(k).view(torch.uint8).fill_(0xFF)
     torch.cuda.synchronize()
-    if graph is not None:
-        ms = timing.time_replays(graph, K, reps=1)[0] * K
-    else:
-        ms = timing.time_eager(lambda k: wl.launch(k % sets), K) * K
+    reps, ev_reps = [], []
+    for _ in range(max(1, args.reps)):
+        if graph is not None:
+            reps.append(timing.time_marked(marked, marks, K, clock_khz) * K)
+            ev_reps.append(timing.time_after_lead(lead, graph, K) * K)
+        else:
+            for k in range(sets if not host_timed else 0):
+                wl.launch(k)
+            reps.append(timing.time_eager(lambda k: wl.launch(k % sets), K) * K)
+    ms = float(np.median(reps))
 
     # the replayed (or eager) launches computed what an eager launch computes
     same = torch.equal(wl.output(0).view(torch.uint8), ref_out.view(torch.uint8))
@@ -830,11 +909,14 @@ def main():
     gbs = wl.bytes / (ms_per_step * 1e-3) / 1e9
     flops = getattr(wl, "flops", None)
     cfg = wl.config()
-    timing_label = ("eager" if args.eager else
-                    ("host loop, one region replay per step" if host_timed else "hip graph of K launches"))
+    timing_label = ("eager, events around the K launches" if args.eager else
+                    ("host loop, one region replay per step" if host_timed else
+                     "device clock marks around the K launches inside one hip graph, after a lead-in of one "
+                     "step per buffer set"))
     cfg.update({"buffer_sets": sets, "rotated_bytes": sets * per_set, "timing": timing_label,
                 "cache": "warm (one set)" if (args.warm or host_timed) else
-                "rotating sets >= 1 GiB to defeat the 256 MB MALL"})
+                f"{sets} rotating sets, {sets * per_set / 2**30:.2f} GiB touched between two uses of a set "
+                "(the 256 MB MALL cannot serve them)"})
     result = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -843,6 +925,8 @@ def main():
         "steps": K,
         "warmup": W,
         "ms_per_step": round(ms_per_step, 6),
+        "reps_ms_per_step": [round(r / K, 6) for r in reps],
+        "events_ms_per_step": round(float(np.median(ev_reps)) / K, 6) if ev_reps else None,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -868,7 +952,7 @@ def main():
                                    "unit": "TFLOP/s", "frac": round(tfs / PEAK_MFMA_BF16_TFS, 4),
                                    "algorithmic_flops_per_launch": flops, "hbm_GB_per_s": round(gbs, 2)})
     if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(wl.oracle_fn(), args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 

@@ -40,7 +40,7 @@ EXPORTS = (
     "fr_layernorm_rows", "fr_layernorm_rows_stats", "fr_layernorm_rows_backward_workspace_bytes",
     "fr_layernorm_rows_backward",
     "fr_sumsq_rows", "fr_sumsq_full_workspace_bytes", "fr_sumsq_full",
-    "fr_stream_copy", "fr_stream_read",
+    "fr_stream_copy", "fr_stream_read", "fr_device_clock", "fr_device_clock_khz",
     "fr_attn_decode_workspace_bytes", "fr_attn_decode",
     "fr_add_2d", "fr_gelu_backward", "fr_attn_block",
     "fr_region_create", "fr_region_destroy", "fr_region_run", "fr_region_state", "fr_region_counts",
@@ -95,6 +95,8 @@ def _load():
         "fr_stream_copy": (I32, [P, P, I64, P]),
         "fr_attn_block": (I32, [P, P, P, P, P, I64, I64, I64, I64, I64, I64, I32, ctypes.c_float, I32, P]),
         "fr_stream_read": (I32, [P, I64, P, P]),
+        "fr_device_clock": (I32, [P, I32, P]),
+        "fr_device_clock_khz": (I32, [P]),
         "fr_add_2d": (I32, [P, I64, I64, P, I64, I64, P, I64, I64, I64, I32, P]),
         "fr_layernorm_rows_stats": (I32, [P, P, P, P, P, P, I64, I64, I64, I64, I64, I64, ctypes.c_float, I32, P]),
         "fr_layernorm_rows_backward_workspace_bytes": (U64, [I64, I64, I32]),
@@ -320,6 +322,22 @@ def fr_stream_read(x, sink, stream=None):
     _check(lib.fr_stream_read(_ptr(x), x.numel() * x.element_size(), _ptr(sink), _stream(stream)),
            "fr_stream_read")
     return sink
+
+
+def fr_device_clock(out, slot, stream=None):
+    """Enqueue a store of the device's constant wall clock into out[slot]
+    (out: int64 device tensor)."""
+    if out.dtype != torch.int64 or not out.is_contiguous() or not 0 <= slot < out.numel():
+        raise ValueError("expected a contiguous int64 tensor with more than `slot` entries")
+    _check(lib.fr_device_clock(_ptr(out), slot, _stream(stream)), "fr_device_clock")
+    return out
+
+
+def fr_device_clock_khz():
+    """Rate of the counter fr_device_clock stores, in kHz."""
+    khz = ctypes.c_int32()
+    _check(lib.fr_device_clock_khz(ctypes.byref(khz)), "fr_device_clock_khz")
+    return khz.value
 
 
 def fr_attn_decode_workspace_bytes(batch, heads_q, seq, dim):

@@ -50,6 +50,19 @@ __global__ __launch_bounds__(T) void fr_stream_read_k(const u32x4* __restrict__ 
     if (threadIdx.x == 0) sink[blockIdx.x] = (uint32_t)r;
 }
 
+// One lane stores the device's constant wall clock (the counter the wait
+// loops of the split kernels read) into out[slot] when the kernel runs: two
+// of these around a sequence of launches on one stream time exactly that
+// sequence on the device.
+__global__ __launch_bounds__(64) void fr_clock_k(uint64_t* __restrict__ out, int slot) {
+    if (threadIdx.x == 0) out[slot] = wall_clock64();
+}
+
+hipError_t launch_device_clock(uint64_t* out, int slot, hipStream_t s) {
+    hipLaunchKernelGGL(fr_clock_k, dim3(1), dim3(64), 0, s, out, slot);
+    return hipGetLastError();
+}
+
 hipError_t launch_stream_copy(const void* x, void* y, int64_t nvec, hipStream_t s) {
     const int64_t grid = std::min<int64_t>(kStreamGrid, (nvec + 1023) / 1024);
     hipLaunchKernelGGL((fr_stream_copy_k<256, 4>), dim3((unsigned)grid), dim3(256), 0, s,

@@ -33,3 +33,24 @@ def test_stream_read_xor(nbytes):
     got = np.bitwise_xor.reduce(host(sink).view(np.uint32))
     want = np.bitwise_xor.reduce(x) if nbytes else np.uint32(0)
     assert int(got) == int(want)
+
+
+def test_device_clock_marks_bracket_stream_work():
+    """Two clock marks around a 256 MiB copy: the counter runs at the rate
+    fr_device_clock_khz reports, the marks are ordered, and their distance
+    covers the copy (512 MiB moved: at least 67 us at 8 TB/s) without being
+    absurd."""
+    khz = fr.fr_device_clock_khz()
+    assert 1000 <= khz <= 10_000_000
+    marks = torch.zeros(2, dtype=torch.int64, device="cuda")
+    x = torch.zeros((256 << 20) // 4, dtype=torch.int32, device="cuda")
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    fr.fr_device_clock(marks, 0)
+    fr.fr_stream_copy(x, y)
+    fr.fr_device_clock(marks, 1)
+    t = host(marks)
+    us = (int(t[1]) - int(t[0])) / khz * 1000.0
+    assert (256 << 21) / 8e6 <= us < 100_000, us
+    with pytest.raises(ValueError):
+        fr.fr_device_clock(marks, 2)
