@@ -397,6 +397,20 @@ int fr_attn_block(const void* q, const void* k, const void* v, void* o, float* l
 int fr_stream_copy(const void* x, void* y, int64_t nbytes, void* stream);
 int fr_stream_read(const void* x, int64_t nbytes, uint32_t* sink, void* stream);
 
+/* ------------------------------------------------------------ sum of squares, no allocation
+ * For callers that cannot allocate device memory (code under graph capture,
+ * tight serving loops, harnesses that forbid allocation): fr_sumsq_full with
+ * the split's chunk partials in a device array the library owns, of
+ * FR_NOALLOC_SCRATCH_BYTES per GPU (held until the process ends), instead of
+ * a caller workspace. Same kernels, so the same bits as fr_sumsq_full. x, n,
+ * out, dtype and stream as there. It allocates nothing and calls no
+ * allocating routine; its first call on a device looks up that device's
+ * copy of the array. Every valid n fits the array (the split has at most
+ * 2048 partials); a plan needing more returns FR_E_WORKSPACE. Calls on one
+ * GPU share the array: calls that overlap in time on the same GPU race. */
+#define FR_NOALLOC_SCRATCH_BYTES 8192
+int fr_sumsq_full_noalloc(const void* x, int64_t n, void* out, int dtype, void* stream);
+
 /* ------------------------------------------------------------ device clock marks
  * fr_device_clock enqueues a one-lane kernel that stores the device's
  * constant wall-clock counter into out[slot] (out: device array of uint64,

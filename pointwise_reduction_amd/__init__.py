@@ -39,7 +39,7 @@ EXPORTS = (
     "fr_softmax_rows_workspace_bytes", "fr_softmax_rows", "fr_softmax_rows_backward",
     "fr_layernorm_rows", "fr_layernorm_rows_stats", "fr_layernorm_rows_backward_workspace_bytes",
     "fr_layernorm_rows_backward",
-    "fr_sumsq_rows", "fr_sumsq_full_workspace_bytes", "fr_sumsq_full",
+    "fr_sumsq_rows", "fr_sumsq_full_workspace_bytes", "fr_sumsq_full", "fr_sumsq_full_noalloc",
     "fr_stream_copy", "fr_stream_read", "fr_device_clock", "fr_device_clock_khz",
     "fr_attn_decode_workspace_bytes", "fr_attn_decode",
     "fr_add_2d", "fr_gelu_backward", "fr_attn_block",
@@ -90,6 +90,7 @@ def _load():
         "fr_sumsq_rows": (I32, [P, P, I64, I64, I64, I64, P, U64, I32, P]),
         "fr_sumsq_full_workspace_bytes": (U64, [I64, I32]),
         "fr_sumsq_full": (I32, [P, I64, P, P, U64, I32, P]),
+        "fr_sumsq_full_noalloc": (I32, [P, I64, P, I32, P]),
         "fr_attn_decode_workspace_bytes": (U64, [I64, I64, I64, I64]),
         "fr_attn_decode": (I32, [P, P, P, P, P, I64, I64, I64, I64, I64, P, ctypes.c_float, P, U64, I32, P]),
         "fr_stream_copy": (I32, [P, P, I64, P]),
@@ -298,6 +299,19 @@ def fr_sumsq_full(x, out, ws=None, stream=None):
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib.fr_sumsq_full(_ptr(x), x.numel(), _ptr(out), _ptr(ws), ws_bytes, _dtype_code(x), _stream(stream)),
            "fr_sumsq_full")
+    return out
+
+
+FR_NOALLOC_SCRATCH_BYTES = 8192
+
+
+def fr_sumsq_full_noalloc(x, out, stream=None):
+    """fr_sumsq_full with its partials in the library's own device array (no
+    workspace, nothing allocated)."""
+    if x.dim() != 1 or (x.numel() > 1 and x.stride(0) != 1):
+        raise ValueError("expected a contiguous 1-D tensor")
+    _check(lib.fr_sumsq_full_noalloc(_ptr(x), x.numel(), _ptr(out), _dtype_code(x), _stream(stream)),
+           "fr_sumsq_full_noalloc")
     return out
 
 
