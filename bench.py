@@ -327,7 +327,8 @@ def make_workload(name, torch, fr, synth):
                 ws_n = fr.fr_softmax_rows_workspace_bytes(rows, cap) // 4
                 self.args = [(x0 if i == 0 else x0.clone(), torch.empty_like(x0),
                               torch.empty(rows, dtype=torch.int32, device=dev),
-                              torch.empty(ws_n, dtype=torch.float32, device=dev)) for i in range(sets)]
+                              fr.fr_softmax_rows_workspace_init(torch.empty(ws_n, dtype=torch.float32, device=dev)))
+                             for i in range(sets)]
 
             def launch(self, k):
                 x, y, am, ws = self.args[k]

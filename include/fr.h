@@ -188,17 +188,32 @@ uint64_t fr_sum_workspace_bytes(int64_t rows, int64_t cols, int dtype);
  *            fr_softmax_rows_workspace_bytes(rows, cols, dtype) bytes. With
  *            it, rows too long for registers may be split across
  *            workgroups; without it they are streamed by one workgroup each.
- *            Its contents need no initialization and are overwritten; word 0
- *            (uint32) afterwards counts the chunk partials that the
- *            single-pass split computed a second time because their owner
- *            had not published them within plan.wait_us (a diagnostic: the
- *            results are the same either way).
+ *            Initialize it once with fr_softmax_rows_workspace_init before
+ *            its first use (and again after it has held anything else);
+ *            every call leaves it initialized for the next, with no clearing
+ *            between calls. An uninitialized workspace gives the same
+ *            results, but the single-pass split then computes every partner
+ *            partial itself (slower). Word 0 (uint32) counts, since the
+ *            initialization, the chunk partials the single-pass split
+ *            computed a second time because their owner had not published
+ *            them within plan.wait_us (a diagnostic: the results are the
+ *            same either way). Calls that overlap in time on one workspace
+ *            race on it; give concurrent streams their own.
  *  In place: when y shares memory with x, a split takes its two-kernel form
  *  (the single pass may read a partner's chunk of x after that partner has
  *  written y there); a tuning override that forces the single pass on such
  *  a call returns FR_E_ARG.
  * A NaN in a row makes that row's outputs NaN. dtype must be FR_F32. */
 uint64_t fr_softmax_rows_workspace_bytes(int64_t rows, int64_t cols, int dtype);
+/* Initialize a split-softmax workspace of ws_bytes bytes (enqueued on stream;
+ * a fill kernel, no host synchronization, capturable in a graph): the slots
+ * are marked empty and the single pass's call counter starts over. Once
+ * initialized, a workspace stays usable for any shape it is large enough
+ * for. FR_E_NULL / FR_E_ALIGN (16 bytes) / FR_E_WORKSPACE (< 64 bytes). The
+ * single pass counts calls per workspace with a 31-bit counter: after
+ * 2^31 - 1 calls it stops trusting the slots (same results, slower) until
+ * the workspace is initialized again. */
+int fr_softmax_rows_workspace_init(void* ws, uint64_t ws_bytes, void* stream);
 int fr_softmax_rows(const void* x, void* y, int64_t rows, int64_t cols, int64_t x_rs, int64_t x_cs, int64_t y_rs,
                     int64_t y_cs, const int32_t* lengths, int32_t* argmax, void* ws, uint64_t ws_bytes, int dtype,
                     void* stream);

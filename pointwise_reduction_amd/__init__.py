@@ -36,7 +36,8 @@ FORM_NAMES = {FR_FORM_PER: "per", FR_FORM_RED: "red", FR_FORM_SPLIT: "split", FR
 EXPORTS = (
     "fr_status_string", "fr_version", "fr_plan_query", "fr_force_form", "fr_tune_override",
     "fr_sum_relu_add", "fr_sum_workspace_bytes",
-    "fr_softmax_rows_workspace_bytes", "fr_softmax_rows", "fr_softmax_rows_backward",
+    "fr_softmax_rows_workspace_bytes", "fr_softmax_rows_workspace_init", "fr_softmax_rows",
+    "fr_softmax_rows_backward",
     "fr_layernorm_rows", "fr_layernorm_rows_stats", "fr_layernorm_rows_backward_workspace_bytes",
     "fr_layernorm_rows_backward",
     "fr_sumsq_rows", "fr_sumsq_full_workspace_bytes", "fr_sumsq_full", "fr_sumsq_full_noalloc",
@@ -84,6 +85,7 @@ def _load():
         "fr_sum_relu_add": (I32, [P, P, P, I64, I64, I64, I64, I64, I64, I64, P, U64, I32, P]),
         "fr_sum_workspace_bytes": (U64, [I64, I64, I32]),
         "fr_softmax_rows_workspace_bytes": (U64, [I64, I64, I32]),
+        "fr_softmax_rows_workspace_init": (I32, [P, U64, P]),
         "fr_softmax_rows": (I32, [P, P, I64, I64, I64, I64, I64, I64, P, P, P, U64, I32, P]),
         "fr_softmax_rows_backward": (I32, [P, P, P, I64, I64, I64, I64, I64, I64, I64, I64, P, I32, P]),
         "fr_layernorm_rows": (I32, [P, P, P, P, I64, I64, I64, I64, I64, I64, ctypes.c_float, I32, P]),
@@ -198,6 +200,16 @@ def fr_sum_workspace_bytes(rows, cols, dtype=FR_F32):
 
 def fr_softmax_rows_workspace_bytes(rows, cols, dtype=FR_F32):
     return int(lib.fr_softmax_rows_workspace_bytes(rows, cols, dtype))
+
+
+def fr_softmax_rows_workspace_init(ws, stream=None):
+    """Initialize a split-softmax workspace tensor (once, before its first
+    use); every fr_softmax_rows call leaves it initialized."""
+    if not ws.is_contiguous():
+        raise ValueError("expected a contiguous workspace")
+    _check(lib.fr_softmax_rows_workspace_init(_ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "fr_softmax_rows_workspace_init")
+    return ws
 
 
 def fr_sumsq_full_workspace_bytes(n, dtype=FR_F32):

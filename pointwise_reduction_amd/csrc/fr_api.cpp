@@ -312,6 +312,17 @@ uint64_t fr_softmax_rows_workspace_bytes(int64_t rows, int64_t cols, int dtype) 
     return softmax_split_ws(rows, cols);
 }
 
+int fr_softmax_rows_workspace_init(void* ws, uint64_t ws_bytes, void* stream) {
+    if (!ws) return FR_E_NULL;
+    if (!aligned(ws, 16)) return FR_E_ALIGN;
+    if (ws_bytes < (uint64_t)kSplitWsHeader) return FR_E_WORKSPACE;
+    int num_cus = 0;
+    const int st = device_check(&num_cus);
+    if (st != FR_OK) return st;
+    (void)hipGetLastError();
+    return finish_launch(launch_softmax_ws_init(ws, ws_bytes, (hipStream_t)stream));
+}
+
 int fr_softmax_rows(const void* x, void* y, int64_t rows, int64_t cols, int64_t x_rs, int64_t x_cs, int64_t y_rs,
                     int64_t y_cs, const int32_t* lengths, int32_t* argmax, void* ws, uint64_t ws_bytes, int dtype,
                     void* stream) {

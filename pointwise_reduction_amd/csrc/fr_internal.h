@@ -54,11 +54,15 @@ struct LayerNormArgs {
 };
 
 // Partial state of one chunk of a split softmax row: the (m, d) pair of the
-// chunk and the first index of its maximum. 16 bytes, 16-byte aligned.
-// Workspace of the split softmax: a header of kSplitWsHeader bytes (word 0:
-// partials the single pass computed for another workgroup), then one
-// 16-byte partial slot per chunk.
+// chunk and the first index of its maximum.
+// Workspace of the split softmax: a header of kSplitWsHeader bytes (the
+// single pass's call epoch, initialization mark and a count of the partials
+// it computed for another workgroup), one 32-bit flag per workgroup of the
+// single pass (kOnePassMaxGrid of them), then one 16-byte slot per chunk
+// from kSplitWsSlots on: two 64-bit words (tag, m) and (tag, d).
 constexpr int kSplitWsHeader = 64;
+constexpr int kOnePassMaxGrid = 4096;
+constexpr int kSplitWsSlots = kSplitWsHeader + 4 * kOnePassMaxGrid;
 // The single pass keeps per-row chunk counts in LDS: at most this many rows.
 constexpr int kOnePassMaxRows = 2048;
 
@@ -69,6 +73,7 @@ struct alignas(16) SoftmaxPartial {
 
 hipError_t launch_sum(const fr_plan& p, const SumArgs& a, hipStream_t s);
 hipError_t launch_softmax(const fr_plan& p, const SoftmaxArgs& a, hipStream_t s);
+hipError_t launch_softmax_ws_init(void* ws, uint64_t ws_bytes, hipStream_t s);
 hipError_t launch_layernorm(const fr_plan& p, const LayerNormArgs& a, hipStream_t s);
 // LayerNorm backward from saved statistics; ws holds the dgamma / dbeta
 // partials [2][grid][ln_bwd_ldw(cols)] fp32 when either is requested.

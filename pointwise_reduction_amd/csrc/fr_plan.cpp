@@ -178,10 +178,11 @@ int finalize_plan(int op, int64_t rows, int64_t cols, const Knobs& k, fr_plan* p
             p->splits = (int)s;
             p->chunk = (int)chunk;
             p->passes = passes;
-            p->ws_bytes = (uint64_t)(kSplitWsHeader + rows * s * (int64_t)sizeof(SoftmaxPartial));
+            p->ws_bytes = (uint64_t)(kSplitWsSlots + rows * s * (int64_t)sizeof(SoftmaxPartial));
             if (passes == 1) {
                 const int64_t per_cu = std::max(1, kOnePassWavesPerSimd * 4 / (k.threads / 64));
-                p->grid = min64(rows * s, (int64_t)(k.num_cus > 0 ? k.num_cus : 256) * per_cu);
+                p->grid = min64(min64(rows * s, (int64_t)(k.num_cus > 0 ? k.num_cus : 256) * per_cu),
+                                kOnePassMaxGrid);
                 p->grid2 = 0;
                 p->wait_us = k.wait_us == 0 ? kOnePassWaitUs : k.wait_us;
             } else {

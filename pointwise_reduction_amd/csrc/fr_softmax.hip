@@ -226,6 +226,19 @@ __global__ __launch_bounds__(T) void fr_red_softmax_f32(const float* x, float* y
     }
 }
 
+// Workspace slot words (the split forms): a 32-bit tag above a 32-bit value.
+constexpr uint32_t kTwoKernelTag = 0x80000000u;  // never an epoch tag
+constexpr uint32_t kMaxEpoch = 0x7FFFFFFFu;      // tags run 1 .. kMaxEpoch
+constexpr uint64_t kWsMagic = 0x46525753664D4158ull;
+// header words (uint32): 0 recomputed partials (cumulative), 2 epoch, 4-5 magic
+constexpr int kHdrRecomputed = 0, kHdrEpoch = 2, kHdrMagic = 4;
+
+__device__ __forceinline__ uint64_t slot_word(uint32_t tag, float v) {
+    return ((uint64_t)tag << 32) | __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ bool published(uint64_t w, uint32_t tag) { return (uint32_t)(w >> 32) == tag; }
+__device__ __forceinline__ float slot_value(uint64_t w) { return __builtin_bit_cast(float, (uint32_t)w); }
+
 // ------------------------------------------------------------------ split
 // Chunk c of a row covers [c * C, min(len, (c+1) * C)) with C = 4 * T * NV.
 // Its partial state is (m, d, i): the chunk maximum, the sum of e^(x - m)
@@ -314,13 +327,16 @@ __device__ __forceinline__ void store_chunk(float* yr, int start, int end, const
 }
 
 // ---- two kernels: workgroup r * S + c takes chunk c of row r. Part 1 writes
-// the chunk's partial; part 2 merges the row's partials in chunk order,
-// writes the argmax (chunk 0) and the normalized chunk. Part 1 reads x with
+// the chunk's (m, d) as two slot words tagged kTwoKernelTag (a tag the
+// single pass never accepts, so the two forms can share a workspace); part 2
+// merges the row's partials in chunk order and writes the normalized chunk;
+// the workgroup of the first chunk holding the row maximum writes the argmax
+// (the first index of the maximum in that chunk). Part 1 reads x with
 // ordinary loads so that part 2 can find it in the device caches.
 template <int T, int NV, bool VEC>
 __global__ __launch_bounds__(T) void fr_split_softmax_part(const float* __restrict__ x, int rows, int cols,
                                                            int64_t x_rs, const int32_t* __restrict__ lengths,
-                                                           SoftmaxPartial* __restrict__ ws, int S) {
+                                                           uint64_t* __restrict__ slots, int S) {
     constexpr int C = 4 * T * NV;
     __shared__ float sl_m[T / kWave];
     __shared__ float sl_d[T / kWave];
@@ -343,13 +359,30 @@ __global__ __launch_bounds__(T) void fr_split_softmax_part(const float* __restri
         load_chunk<tail_mask<VEC>(), T, NV, false>(xr, start, end, v);
         p = chunk_partial<tail_mask<VEC>(), T, NV>(v, start, end, sl_m, sl_d, sl_i);
     }
-    if (threadIdx.x == 0) ws[w] = p;
+    if (threadIdx.x == 0) {
+        slots[2 * w] = slot_word(kTwoKernelTag, p.m);
+        slots[2 * w + 1] = slot_word(kTwoKernelTag, p.d);
+    }
 }
 
 template <int M, int T, int NV>
-__device__ __forceinline__ void fin_body(const float* xr, float* yr, int start, int end, float mx, float inv) {
+__device__ __forceinline__ void fin_body(const float* xr, float* yr, int start, int end, float mx, float inv,
+                                         int32_t* argmax_r, int* sl_i) {
     f32x4 v[NV];
     load_chunk<M, T, NV, true>(xr, start, end, v);
+    if (argmax_r) {  // this chunk holds the row maximum first: its first index of it
+        int cand = INT_MAX;
+#pragma unroll
+        for (int k = NV - 1; k >= 0; --k)
+#pragma unroll
+            for (int c = 3; c >= 0; --c) {
+                const int j = start + (k * T + (int)threadIdx.x) * 4 + c;
+                if (j < end && is_max(comp(v[k], c), mx)) cand = j;
+            }
+        cand = group_reduce<kWave>(cand, OpMinI());
+        cand = block_fold(cand, sl_i, T / kWave, OpMinI());
+        if (threadIdx.x == 0) *argmax_r = cand;
+    }
     store_chunk<M, T, NV>(yr, start, end, v, mx, inv);
 }
 
@@ -358,8 +391,9 @@ __global__ __launch_bounds__(T) void fr_split_softmax_fin(const float* x, float*
                                                           int64_t x_rs, int64_t y_rs,
                                                           const int32_t* __restrict__ lengths,
                                                           int32_t* __restrict__ argmax,
-                                                          const SoftmaxPartial* __restrict__ ws, int S) {
+                                                          const uint64_t* __restrict__ slots, int S) {
     constexpr int C = 4 * T * NV;
+    __shared__ int sl_i[T / kWave];
     const int64_t w = blockIdx.x;
     const int r = (int)(w / S);
     const int c = (int)(w % S);
@@ -374,18 +408,18 @@ __global__ __launch_bounds__(T) void fr_split_softmax_fin(const float* x, float*
     const int nc = (L + C - 1) / C;
     MD st{-INFINITY, 0.f};
     MI best{-INFINITY, INT_MAX};
-    const SoftmaxPartial* pr = ws + (int64_t)r * S;
+    const uint64_t* pr = slots + 2 * (int64_t)r * S;
     for (int k = 0; k < nc; ++k) {
-        const SoftmaxPartial p = pr[k];
-        st = md_combine(st, MD{p.m, p.d});
-        best = mi_combine(best, MI{p.m, p.idx});
+        const float pm = slot_value(pr[2 * k]);
+        st = md_combine(st, MD{pm, slot_value(pr[2 * k + 1])});
+        best = mi_combine(best, MI{pm, k});  // the first chunk holding the row maximum
     }
-    if (c == 0 && argmax && threadIdx.x == 0) argmax[r] = best.i;
     const float inv = 1.0f / st.d;
     const float* xr = x + (int64_t)r * x_rs;
     float* yr = y + (int64_t)r * y_rs;
-    if (end - start == C) fin_body<body_mask<VEC>(), T, NV>(xr, yr, start, end, st.m, inv);
-    else fin_body<tail_mask<VEC>(), T, NV>(xr, yr, start, end, st.m, inv);
+    int32_t* am = (argmax && c == best.i) ? argmax + r : nullptr;
+    if (end - start == C) fin_body<body_mask<VEC>(), T, NV>(xr, yr, start, end, st.m, inv, am, sl_i);
+    else fin_body<tail_mask<VEC>(), T, NV>(xr, yr, start, end, st.m, inv, am, sl_i);
 }
 
 // ---- one kernel: every chunk is read once and stays in registers while the
@@ -395,34 +429,57 @@ __global__ __launch_bounds__(T) void fr_split_softmax_fin(const float* x, float*
 //    workgroup w takes list entries w, w + G, w + 2G, ... (G = grid size):
 //    no workgroup is spent on the empty tail of a ragged row, and the chunks
 //    of one row are worked on at the same time by neighbouring workgroups.
-//  - A chunk's partial is published in its slot as two 64-bit words, (index,
-//    m) and (index, d); a slot whose index half is kUnpublished (the reset
-//    kernel's fill) is not yet written. Each word is written and read as one
-//    64-bit atomic, so a reader that sees the index sees the value beside it
-//    and no fence is needed.
+//  - A chunk's partial is published in its slot as two 64-bit words, (tag,
+//    m) and (tag, d). The tag is the call's epoch: the workspace header
+//    holds a counter E that every workgroup reads at its start (tag = E + 1)
+//    and then acknowledges by storing the tag in its own flag word (the
+//    store depends on the value read). Workgroup 0, at its end, waits until
+//    every flag holds the tag - every workgroup has read E - and stores
+//    E + 1 for the next call. No two workgroups update one word.
+//    A word whose tag is not this call's (an earlier call's, the zeros of an
+//    initialized workspace, or the reserved tag of the two-kernel form) is
+//    not yet written. Each word is written with one 64-bit store and read
+//    with one 64-bit load, the instructions of 64-bit atomic accesses, so a
+//    reader that sees the tag sees the value beside it and no fence is
+//    needed. Nothing has to be cleared between calls.
+//  - The header also holds a magic number that only the initialization
+//    writes. Without it (a workspace never initialized), or once the epoch
+//    has reached its last value, no slot is trusted: every partner partial
+//    is computed from x, which gives the same bits, only slower.
 //  - A workgroup waits, up to a wall-clock limit, for the other slots of its
 //    row (a negative limit: it reads none of them). A partial still missing
 //    at the limit it computes itself from x
 //    with chunk_partial_streamed, which gives the owner's bits. Nothing
 //    depends on other workgroups being resident, so every launch finishes
 //    and the result does not depend on scheduling. Each partial computed this
-//    way is counted in the workspace header.
+//    way is added to a count in the workspace header.
 //  - The row's partials are merged in a fixed order (64-lane butterflies over
 //    groups of 64 chunks, groups in order), so every chunk of a row is
-//    normalized with the same (m, d) bits.
-constexpr uint32_t kUnpublished = 0xFFFFFFFFu;
-
-__device__ __forceinline__ uint64_t slot_word(int idx, float v) {
-    return ((uint64_t)(uint32_t)idx << 32) | __builtin_bit_cast(uint32_t, v);
-}
-__device__ __forceinline__ bool published(uint64_t w) { return (uint32_t)(w >> 32) != kUnpublished; }
-
-// Header words cleared, slots marked unpublished.
-__global__ __launch_bounds__(256) void fr_split_softmax_reset(uint32_t* __restrict__ hdr, u32x4* __restrict__ slots,
-                                                              int64_t nslots) {
+//    normalized with the same (m, d) bits. The merge also yields the first
+//    chunk whose maximum is the row's; that chunk's workgroup writes the
+//    argmax, the first index of the maximum within its own chunk.
+// Workspace initialization: zeros everywhere, epoch 0, the magic number.
+__global__ __launch_bounds__(256) void fr_split_softmax_init(uint32_t* __restrict__ ws, int64_t nwords) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i < kSplitWsHeader / 4) hdr[i] = 0u;
-    if (i < nslots) slots[i] = u32x4{~0u, ~0u, ~0u, ~0u};
+    if (i < nwords)
+        ws[i] = i == kHdrMagic ? (uint32_t)kWsMagic : (i == kHdrMagic + 1 ? (uint32_t)(kWsMagic >> 32) : 0u);
+}
+
+// End of a single-pass call, workgroup 0 (all its threads): once every
+// workgroup's flag holds this call's tag, every workgroup has read the
+// epoch, which is then advanced for the next call. Workgroups never wait for
+// workgroup 0, so one that has not started yet does so as others finish.
+template <int T>
+__device__ void epoch_advance(uint32_t* hdr, const uint32_t* flags, uint32_t tag, uint32_t epoch) {
+    const int tid = threadIdx.x;
+    for (;;) {
+        bool ok = true;
+        for (int b = tid; b < (int)gridDim.x; b += T)
+            ok &= __hip_atomic_load(&flags[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == tag;
+        if (__syncthreads_and(ok)) break;
+        __builtin_amdgcn_s_sleep(8);
+    }
+    if (tid == 0) __hip_atomic_store(&hdr[kHdrEpoch], epoch + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Pipelined form of the one-kernel split (16-byte aligned rows): entry
@@ -478,7 +535,7 @@ __device__ __forceinline__ void one_pass_pipelined(const float* x, float* y, int
                                                    const int* s_base, const int* s_len, int rows, int total,
                                                    int32_t* argmax, uint32_t* hdr, uint64_t* slots, float* sl_m,
                                                    float* sl_d, int* sl_i, uint64_t* s_missing, float* s_mx,
-                                                   int64_t wait_ticks) {
+                                                   int* s_kstar, uint32_t tag, int64_t wait_ticks) {
     constexpr int C = 4 * T * NV;
     const int tid = threadIdx.x;
     const int G = gridDim.x;
@@ -528,19 +585,23 @@ __device__ __forceinline__ void one_pass_pipelined(const float* x, float* y, int
         }
         SoftmaxPartial own = pipe_partial<T, NV>(cur, ec.n, lt, sl_m, sl_d, sl_i);
         if (own.idx != INT_MAX) own.idx += ec.start;
-        const uint64_t own0 = slot_word(own.idx, own.m), own1 = slot_word(own.idx, own.d);
-        // the row's slots, 16 bytes per chunk
+        const uint64_t own0 = slot_word(tag, own.m), own1 = slot_word(tag, own.d);
+        // the row's slots, 16 bytes per chunk; a row of one chunk exchanges
+        // nothing, and without a tag nothing is published (an empty range)
         uint64_t* rs = slots + 2 * (int64_t)ec.base;
-        const int row_slot_bytes = ec.nc * 16;
+        const int row_slot_bytes = (tag != 0u && ec.nc > 1) ? ec.nc * 16 : 0;
         const __amdgpu_buffer_rsrc_t rslots = row_rsrc(rs, (uint32_t)row_slot_bytes);
         // publish: threads 0 and 1 write the slot's two words, every other
         // lane falls outside the range; sc1: seen by the other dies
         const uint64_t word = tid & 1 ? own1 : own0;
         __builtin_amdgcn_raw_buffer_store_b64(u32x2{(uint32_t)word, (uint32_t)(word >> 32)}, rslots,
                                               tid < 2 ? ec.c * 16 + tid * 8 : row_slot_bytes, 0, kAuxSc1);
-        // first look at the partners: lane k of wave 0 reads chunk k's slot
+        // first look at the partners: lane k of wave 0 reads chunk k's two
+        // words, each with one 64-bit load
         const bool look = tid < kWave && tid < ec.nc && tid != ec.c;
-        const u32x4 pw = __builtin_amdgcn_raw_buffer_load_b128(rslots, look ? tid * 16 : row_slot_bytes, 0, kAuxSc1);
+        const int look_off = look ? tid * 16 : row_slot_bytes;
+        const u32x2 pw0 = __builtin_amdgcn_raw_buffer_load_b64(rslots, look_off, 0, kAuxSc1);
+        const u32x2 pw1 = __builtin_amdgcn_raw_buffer_load_b64(rslots, look_off + 8, 0, kAuxSc1);
         issue(nxt, en, lt);
 
         const float* xr = x + (int64_t)ec.r * x_rs;
@@ -549,24 +610,26 @@ __device__ __forceinline__ void one_pass_pipelined(const float* x, float* y, int
         MI best{-INFINITY, INT_MAX};
         for (int g0 = 0; g0 < ec.nc; g0 += kWave) {
             const int k = g0 + (tid & (kWave - 1));
-            uint64_t w0 = g0 == 0 ? ((uint64_t)pw.y << 32 | pw.x) : ~0ull;
-            uint64_t w1 = g0 == 0 ? ((uint64_t)pw.w << 32 | pw.z) : ~0ull;
+            uint64_t w0 = g0 == 0 ? ((uint64_t)pw0.y << 32 | pw0.x) : 0ull;
+            uint64_t w1 = g0 == 0 ? ((uint64_t)pw1.y << 32 | pw1.x) : 0ull;
             if (k == ec.c) {
                 w0 = own0;
                 w1 = own1;
             }
             if (tid < kWave) {
-                // with no wait (wait_ticks < 0) every partner's partial is recomputed
-                bool ok = k >= ec.nc || k == ec.c || (wait_ticks >= 0 && published(w0) && published(w1));
-                if (!__all(ok) && wait_ticks >= 0) {
+                // with no wait (wait_ticks < 0), or no tag, every partner's
+                // partial is recomputed
+                const bool trust = wait_ticks >= 0 && tag != 0u;
+                bool ok = k >= ec.nc || k == ec.c || (trust && published(w0, tag) && published(w1, tag));
+                if (!__all(ok) && trust) {
                     const uint64_t t0 = wall_clock64();
                     for (;;) {
                         if (!ok) {
-                            if (!published(w0))
+                            if (!published(w0, tag))
                                 w0 = __hip_atomic_load(&rs[2 * k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                            if (!published(w1))
+                            if (!published(w1, tag))
                                 w1 = __hip_atomic_load(&rs[2 * k + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                            ok = published(w0) && published(w1);
+                            ok = published(w0, tag) && published(w1, tag);
                         }
                         if (__all(ok)) break;
                         if ((int64_t)(wall_clock64() - t0) >= wait_ticks) break;
@@ -585,19 +648,20 @@ __device__ __forceinline__ void one_pass_pipelined(const float* x, float* y, int
                 const int ke = min(L, ks + C);
                 const SoftmaxPartial p = chunk_partial_streamed<kElem, T, NV>(xr, ks, ke, sl_m, sl_d, sl_i);
                 if (tid == j) {
-                    w0 = slot_word(p.idx, p.m);
-                    w1 = slot_word(p.idx, p.d);
+                    w0 = slot_word(tag, p.m);
+                    w1 = slot_word(tag, p.d);
                 }
-                if (tid == 0) __hip_atomic_fetch_add(&hdr[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (tid == 0)
+                    __hip_atomic_fetch_add(&hdr[kHdrRecomputed], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 __builtin_amdgcn_s_waitcnt(0);
             }
             if (tid < kWave) {
                 MD a{-INFINITY, 0.f};
                 MI b{-INFINITY, INT_MAX};
                 if (k < ec.nc) {
-                    const float pm = __builtin_bit_cast(float, (uint32_t)w0);
-                    a = MD{pm, __builtin_bit_cast(float, (uint32_t)w1)};
-                    b = MI{pm, (int)(uint32_t)(w0 >> 32)};
+                    const float pm = slot_value(w0);
+                    a = MD{pm, slot_value(w1)};
+                    b = MI{pm, k};  // the first chunk holding the row maximum
                 }
                 st = md_combine(st, group_reduce<kWave>(a, OpMD()));
                 best = mi_combine(best, group_reduce<kWave>(b, OpMI()));
@@ -607,14 +671,16 @@ __device__ __forceinline__ void one_pass_pipelined(const float* x, float* y, int
         if (tid == 0) {
             s_mx[0] = st.m;
             s_mx[1] = 1.0f / st.d;
+            *s_kstar = best.i;
         }
-        // the row's argmax from its first chunk's workgroup: thread 0 in range
-        const bool am = argmax != nullptr && ec.c == 0;
-        __builtin_amdgcn_raw_buffer_store_b32(
-            (uint32_t)best.i, row_rsrc(reinterpret_cast<char*>(argmax) + (am ? 4 * (int64_t)ec.r : 0), am ? 4u : 0u),
-            tid == 0 ? 0 : 4, 0, 0);
         __syncthreads();
         const float mx = s_mx[0], inv = s_mx[1];
+        // the row's argmax is the first index of the maximum in the first
+        // chunk that holds it: that chunk's workgroup writes it (thread 0 in range)
+        const bool am = argmax != nullptr && ec.c == uni(*s_kstar);
+        __builtin_amdgcn_raw_buffer_store_b32(
+            (uint32_t)own.idx, row_rsrc(reinterpret_cast<char*>(argmax) + (am ? 4 * (int64_t)ec.r : 0), am ? 4u : 0u),
+            tid == 0 ? 0 : 4, 0, 0);
         const __amdgpu_buffer_rsrc_t ry = row_rsrc(y + (int64_t)ec.r * y_rs + ec.start, (uint32_t)ec.n * 4u);
 #pragma unroll
         for (int k = 0; k < NV; ++k)
@@ -634,6 +700,122 @@ __device__ __forceinline__ void one_pass_pipelined(const float* x, float* y, int
     }
 }
 
+// Element-wise form of the one-kernel split (rows not 16-byte aligned): one
+// chunk in registers at a time, read with masked loads.
+template <int T, int NV>
+__device__ __forceinline__ void one_pass_elementwise(const float* x, float* y, int64_t x_rs, int64_t y_rs,
+                                                     const int* s_base, const int* s_len, int rows, int total,
+                                                     int32_t* argmax, uint32_t* hdr, uint64_t* slots, float* sl_m,
+                                                     float* sl_d, int* sl_i, uint64_t* s_missing, float* s_mx,
+                                                     int* s_kstar, uint32_t tag, int64_t wait_ticks) {
+    constexpr bool VEC = false;
+    constexpr int C = 4 * T * NV;
+    const int tid = threadIdx.x;
+    for (int t = blockIdx.x; t < total; t += gridDim.x) {
+        int lo = 0, hi = rows;  // s_base[lo] <= t < s_base[hi]; rows without chunks never qualify
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (s_base[mid] <= t) lo = mid;
+            else hi = mid;
+        }
+        const int r = lo;
+        const int base = s_base[r];
+        const int nc = s_base[r + 1] - base;
+        const int c = t - base;
+        const int L = s_len[r];
+        const int start = c * C;
+        const int end = min(L, start + C);
+        const bool full = end - start == C;
+        const float* xr = x + (int64_t)r * x_rs;
+        f32x4 v[NV];
+        SoftmaxPartial own;
+        if (full) {
+            load_chunk<body_mask<VEC>(), T, NV, true>(xr, start, end, v);
+            own = chunk_partial<body_mask<VEC>(), T, NV>(v, start, end, sl_m, sl_d, sl_i);
+        } else {
+            load_chunk<tail_mask<VEC>(), T, NV, true>(xr, start, end, v);
+            own = chunk_partial<tail_mask<VEC>(), T, NV>(v, start, end, sl_m, sl_d, sl_i);
+        }
+        uint64_t* rs = slots + 2 * (int64_t)base;
+        // a row of one chunk exchanges nothing; without a tag nothing is published
+        if (tid == 0 && tag != 0u && nc > 1) {
+            __hip_atomic_store(&rs[2 * c], slot_word(tag, own.m), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&rs[2 * c + 1], slot_word(tag, own.d), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        // merge the row's partials, 64 at a time: wave 0 gathers (lane j: chunk g0 + j)
+        MD st{-INFINITY, 0.f};
+        MI best{-INFINITY, INT_MAX};
+        for (int g0 = 0; g0 < nc; g0 += kWave) {
+            const int k = g0 + (tid & (kWave - 1));
+            uint64_t w0 = 0ull, w1 = 0ull;
+            if (tid < kWave) {
+                bool ok = k >= nc;
+                if (k == c) {
+                    w0 = slot_word(tag, own.m);
+                    w1 = slot_word(tag, own.d);
+                    ok = true;
+                }
+                const uint64_t t0 = wall_clock64();
+                // wait_ticks < 0, or no tag: read no other partial (all are recomputed)
+                for (; wait_ticks >= 0 && tag != 0u;) {
+                    if (!ok) {
+                        if (!published(w0, tag))
+                            w0 = __hip_atomic_load(&rs[2 * k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        if (!published(w1, tag))
+                            w1 = __hip_atomic_load(&rs[2 * k + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        ok = published(w0, tag) && published(w1, tag);
+                    }
+                    if (__all(ok)) break;
+                    if ((int64_t)(wall_clock64() - t0) >= wait_ticks) break;
+                    __builtin_amdgcn_s_sleep(2);
+                }
+                const uint64_t miss = __ballot(!ok);
+                if (tid == 0) *s_missing = miss;
+            }
+            __syncthreads();
+            uint64_t miss = *s_missing;
+            while (miss) {  // rare: the owner has not published in time
+                const int j = __builtin_ctzll(miss);
+                miss &= miss - 1;
+                const int ks = (g0 + j) * C;
+                const int ke = min(L, ks + C);
+                const SoftmaxPartial p =
+                    ke - ks == C ? chunk_partial_streamed<body_mask<VEC>(), T, NV>(xr, ks, ke, sl_m, sl_d, sl_i)
+                                 : chunk_partial_streamed<tail_mask<VEC>(), T, NV>(xr, ks, ke, sl_m, sl_d, sl_i);
+                if (tid == j) {
+                    w0 = slot_word(tag, p.m);
+                    w1 = slot_word(tag, p.d);
+                }
+                if (tid == 0)
+                    __hip_atomic_fetch_add(&hdr[kHdrRecomputed], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            if (tid < kWave) {
+                MD a{-INFINITY, 0.f};
+                MI b{-INFINITY, INT_MAX};
+                if (k < nc) {
+                    const float pm = slot_value(w0);
+                    a = MD{pm, slot_value(w1)};
+                    b = MI{pm, k};  // the first chunk holding the row maximum
+                }
+                st = md_combine(st, group_reduce<kWave>(a, OpMD()));
+                best = mi_combine(best, group_reduce<kWave>(b, OpMI()));
+            }
+            __syncthreads();  // s_missing and the fold slots are rewritten next
+        }
+        if (tid == 0) {
+            s_mx[0] = st.m;
+            s_mx[1] = 1.0f / st.d;
+            // the first index of the maximum, from the first chunk holding it
+            if (c == best.i && argmax) argmax[r] = own.idx;
+        }
+        __syncthreads();
+        const float mx = s_mx[0], inv = s_mx[1];
+        float* yr = y + (int64_t)r * y_rs;
+        if (full) store_chunk<body_mask<VEC>(), T, NV>(yr, start, end, v, mx, inv);
+        else store_chunk<tail_mask<VEC>(), T, NV>(yr, start, end, v, mx, inv);
+    }
+}
+
 template <int T, int NV, bool VEC>
 __global__ __launch_bounds__(T) void fr_split_softmax_one(const float* x, float* y, int rows, int cols, int64_t x_rs,
                                                           int64_t y_rs, const int32_t* __restrict__ lengths,
@@ -647,11 +829,23 @@ __global__ __launch_bounds__(T) void fr_split_softmax_one(const float* x, float*
     __shared__ float sl_d[T / kWave];
     __shared__ int sl_i[T / kWave];
     __shared__ uint64_t s_missing;
-    __shared__ float s_max, s_inv;
     __shared__ float s_mx[2];
+    __shared__ int s_kstar;
+    __shared__ uint32_t s_tag, s_epoch;
     uint32_t* hdr = static_cast<uint32_t*>(ws);
-    uint64_t* slots = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + kSplitWsHeader);
+    uint32_t* flags = hdr + kSplitWsHeader / 4;
+    uint64_t* slots = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + kSplitWsSlots);
     const int tid = threadIdx.x;
+
+    // the initialization mark and the epoch, loaded now and used once the
+    // chunk list is built
+    uint64_t magic = 0;
+    uint32_t epoch = 0;
+    if (tid == 0) {
+        magic = __hip_atomic_load(reinterpret_cast<uint64_t*>(hdr + kHdrMagic), __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+        epoch = __hip_atomic_load(&hdr[kHdrEpoch], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 
     // chunk list: thread tid counts the chunks of rows [r0, r1)
     const int per = (rows + T - 1) / T;
@@ -680,115 +874,29 @@ __global__ __launch_bounds__(T) void fr_split_softmax_one(const float* x, float*
         run += (s_len[r] + C - 1) / C;
     }
     if (tid == T - 1) s_base[rows] = run;
+    if (tid == 0) {
+        // this call's tag (0: no slot is trusted), acknowledged in this
+        // workgroup's flag: the stored value depends on the epoch read
+        const uint32_t t = (magic == kWsMagic && epoch < kMaxEpoch) ? epoch + 1 : 0u;
+        if (t != 0u) __hip_atomic_store(&flags[blockIdx.x], t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_tag = t;
+        s_epoch = epoch;
+    }
     __syncthreads();
     const int total = s_base[rows];
+    const uint32_t tag = __builtin_amdgcn_readfirstlane(s_tag);
     if (blockIdx.x == 0 && argmax)
         for (int r = tid; r < rows; r += T)
             if (s_len[r] == 0) argmax[r] = -1;
 
     if constexpr (VEC) {
         one_pass_pipelined<T, NV>(x, y, x_rs, y_rs, s_base, s_len, rows, total, argmax, hdr, slots, sl_m, sl_d, sl_i,
-                                  &s_missing, s_mx, wait_ticks);
-        return;
+                                  &s_missing, s_mx, &s_kstar, tag, wait_ticks);
+    } else {
+        one_pass_elementwise<T, NV>(x, y, x_rs, y_rs, s_base, s_len, rows, total, argmax, hdr, slots, sl_m, sl_d,
+                                    sl_i, &s_missing, s_mx, &s_kstar, tag, wait_ticks);
     }
-    for (int t = blockIdx.x; t < total; t += gridDim.x) {
-        int lo = 0, hi = rows;  // s_base[lo] <= t < s_base[hi]; rows without chunks never qualify
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (s_base[mid] <= t) lo = mid;
-            else hi = mid;
-        }
-        const int r = lo;
-        const int base = s_base[r];
-        const int nc = s_base[r + 1] - base;
-        const int c = t - base;
-        const int L = s_len[r];
-        const int start = c * C;
-        const int end = min(L, start + C);
-        const bool full = end - start == C;
-        const float* xr = x + (int64_t)r * x_rs;
-        f32x4 v[NV];
-        SoftmaxPartial own;
-        if (full) {
-            load_chunk<body_mask<VEC>(), T, NV, true>(xr, start, end, v);
-            own = chunk_partial<body_mask<VEC>(), T, NV>(v, start, end, sl_m, sl_d, sl_i);
-        } else {
-            load_chunk<tail_mask<VEC>(), T, NV, true>(xr, start, end, v);
-            own = chunk_partial<tail_mask<VEC>(), T, NV>(v, start, end, sl_m, sl_d, sl_i);
-        }
-        uint64_t* rs = slots + 2 * (int64_t)base;
-        if (tid == 0) {
-            __hip_atomic_store(&rs[2 * c], slot_word(own.idx, own.m), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&rs[2 * c + 1], slot_word(own.idx, own.d), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        // merge the row's partials, 64 at a time: wave 0 gathers (lane j: chunk g0 + j)
-        MD st{-INFINITY, 0.f};
-        MI best{-INFINITY, INT_MAX};
-        for (int g0 = 0; g0 < nc; g0 += kWave) {
-            const int k = g0 + (tid & (kWave - 1));
-            uint64_t w0 = ~0ull, w1 = ~0ull;
-            if (tid < kWave) {
-                bool ok = k >= nc;
-                if (k == c) {
-                    w0 = slot_word(own.idx, own.m);
-                    w1 = slot_word(own.idx, own.d);
-                    ok = true;
-                }
-                const uint64_t t0 = wall_clock64();
-                for (; wait_ticks >= 0;) {  // < 0: read no other partial (all are recomputed)
-                    if (!ok) {
-                        if (!published(w0)) w0 = __hip_atomic_load(&rs[2 * k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        if (!published(w1))
-                            w1 = __hip_atomic_load(&rs[2 * k + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        ok = published(w0) && published(w1);
-                    }
-                    if (__all(ok)) break;
-                    if ((int64_t)(wall_clock64() - t0) >= wait_ticks) break;
-                    __builtin_amdgcn_s_sleep(2);
-                }
-                const uint64_t miss = __ballot(!ok);
-                if (tid == 0) s_missing = miss;
-            }
-            __syncthreads();
-            uint64_t miss = s_missing;
-            while (miss) {  // rare: the owner has not published in time
-                const int j = __builtin_ctzll(miss);
-                miss &= miss - 1;
-                const int ks = (g0 + j) * C;
-                const int ke = min(L, ks + C);
-                const SoftmaxPartial p =
-                    ke - ks == C ? chunk_partial_streamed<body_mask<VEC>(), T, NV>(xr, ks, ke, sl_m, sl_d, sl_i)
-                                 : chunk_partial_streamed<tail_mask<VEC>(), T, NV>(xr, ks, ke, sl_m, sl_d, sl_i);
-                if (tid == j) {
-                    w0 = slot_word(p.idx, p.m);
-                    w1 = slot_word(p.idx, p.d);
-                }
-                if (tid == 0) __hip_atomic_fetch_add(&hdr[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-            if (tid < kWave) {
-                MD a{-INFINITY, 0.f};
-                MI b{-INFINITY, INT_MAX};
-                if (k < nc) {
-                    const float pm = __builtin_bit_cast(float, (uint32_t)w0);
-                    a = MD{pm, __builtin_bit_cast(float, (uint32_t)w1)};
-                    b = MI{pm, (int)(uint32_t)(w0 >> 32)};
-                }
-                st = md_combine(st, group_reduce<kWave>(a, OpMD()));
-                best = mi_combine(best, group_reduce<kWave>(b, OpMI()));
-            }
-            __syncthreads();  // s_missing and the fold slots are rewritten next
-        }
-        if (tid == 0) {
-            s_max = st.m;
-            s_inv = 1.0f / st.d;
-            if (c == 0 && argmax) argmax[r] = best.i;
-        }
-        __syncthreads();
-        const float mx = s_max, inv = s_inv;
-        float* yr = y + (int64_t)r * y_rs;
-        if (full) store_chunk<body_mask<VEC>(), T, NV>(yr, start, end, v, mx, inv);
-        else store_chunk<tail_mask<VEC>(), T, NV>(yr, start, end, v, mx, inv);
-    }
+    if (blockIdx.x == 0 && tag != 0u) epoch_advance<T>(hdr, flags, tag, s_epoch);
 }
 
 // ------------------------------------------------------------------ backward
@@ -917,9 +1025,9 @@ __global__ __launch_bounds__(T) void fr_red_softmax_bwd_f32(const float* y, cons
 namespace {
 
 using SmFn = void (*)(const float*, float*, int, int, int64_t, int64_t, const int32_t*, int32_t*);
-using PartFn = void (*)(const float*, int, int, int64_t, const int32_t*, SoftmaxPartial*, int);
+using PartFn = void (*)(const float*, int, int, int64_t, const int32_t*, uint64_t*, int);
 using FinFn = void (*)(const float*, float*, int, int, int64_t, int64_t, const int32_t*, int32_t*,
-                       const SoftmaxPartial*, int);
+                       const uint64_t*, int);
 
 template <int M>
 SmFn pick_per_m(int seg, int nv, int rpw) {
@@ -1097,12 +1205,6 @@ hipError_t launch_softmax(const fr_plan& p, const SoftmaxArgs& a, hipStream_t s)
         if (a.rows > kOnePassMaxRows) return hipErrorInvalidDeviceFunction;
         OneFn one = vec ? pick_one<true>(p.threads, p.vec) : pick_one<false>(p.threads, p.vec);
         if (!one) return hipErrorInvalidDeviceFunction;
-        const int64_t nslots = (int64_t)a.rows * p.splits;
-        hipLaunchKernelGGL(fr_split_softmax_reset, dim3((unsigned)((nslots + 255) / 256)), dim3(256), 0, s,
-                           static_cast<uint32_t*>(a.ws),
-                           reinterpret_cast<u32x4*>(static_cast<char*>(a.ws) + kSplitWsHeader), nslots);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
         hipLaunchKernelGGL(one, dim3((unsigned)p.grid), dim3(p.threads), 0, s, a.x, a.y, a.rows, a.cols, a.x_rs,
                            a.y_rs, a.lengths, a.argmax, a.ws, a.wait_ticks);
         return hipGetLastError();
@@ -1113,16 +1215,23 @@ hipError_t launch_softmax(const fr_plan& p, const SoftmaxArgs& a, hipStream_t s)
         if (vec) pick_split<true>(p.threads, p.vec, &part, &fin);
         else pick_split<false>(p.threads, p.vec, &part, &fin);
         if (!part || !fin) return hipErrorInvalidDeviceFunction;
-        SoftmaxPartial* ws = reinterpret_cast<SoftmaxPartial*>(static_cast<char*>(a.ws) + kSplitWsHeader);
+        uint64_t* ws = reinterpret_cast<uint64_t*>(static_cast<char*>(a.ws) + kSplitWsSlots);
         hipLaunchKernelGGL(part, dim3((unsigned)p.grid), dim3(p.threads), 0, s, a.x, a.rows, a.cols, a.x_rs,
                            a.lengths, ws, p.splits);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(fin, dim3((unsigned)p.grid2), dim3(p.threads), 0, s, a.x, a.y, a.rows, a.cols, a.x_rs,
-                           a.y_rs, a.lengths, a.argmax, (const SoftmaxPartial*)ws, p.splits);
+                           a.y_rs, a.lengths, a.argmax, (const uint64_t*)ws, p.splits);
         return hipGetLastError();
     }
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_softmax_ws_init(void* ws, uint64_t ws_bytes, hipStream_t s) {
+    const int64_t nwords = (int64_t)(ws_bytes / 4);
+    hipLaunchKernelGGL(fr_split_softmax_init, dim3((unsigned)((nwords + 255) / 256)), dim3(256), 0, s,
+                       static_cast<uint32_t*>(ws), nwords);
+    return hipGetLastError();
 }
 
 }  // namespace fr

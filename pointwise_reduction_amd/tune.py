@@ -134,7 +134,8 @@ def workload(name):
             Ld = _d(L)
             xs = [_d(x) for _ in range(sets)]
             ys = [torch.empty_like(xs[0]) for _ in range(sets)]
-            ws = [torch.empty((rows * 64 * 16 + 4096) // 4, dtype=torch.float32, device="cuda") for _ in range(sets)]
+            ws = [fr.fr_softmax_rows_workspace_init(torch.empty((rows * 64 * 16 + 4096) // 4, dtype=torch.float32,
+                                                                device="cuda")) for _ in range(sets)]
             am = [torch.empty(rows, dtype=torch.int32, device="cuda") for _ in range(sets)]
             return (lambda k: fr.fr_softmax_rows(xs[k], ys[k], lengths=Ld, argmax=am[k], ws=ws[k])), \
                 (lambda: ys[0].masked_fill(torch.arange(cap, device="cuda")[None, :] >= Ld[:, None].long(), 0))

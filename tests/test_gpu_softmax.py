@@ -36,11 +36,22 @@ def run(x_np, lengths=None, form=fr.FR_FORM_AUTO, use_ws=None, cols=None, y_fill
         use_ws = form == fr.FR_FORM_SPLIT
     ws = None
     if use_ws:
-        nbytes = fr.fr_softmax_rows_workspace_bytes(rows, cols)
-        ws = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+        ws = new_ws(rows, cols)
     with forced(form):
         fr.fr_softmax_rows(x, y, lengths=L, argmax=am, ws=ws)
     return host(yd)[:, :cols], (host(am) if argmax else None), host(yd)
+
+
+def new_ws(rows, cols, garbage=0x5A5A5A5A, init=True):
+    """A split workspace holding garbage, then initialized (unless init=False)."""
+    nbytes = fr.fr_softmax_rows_workspace_bytes(rows, cols)
+    ws = torch.full((nbytes // 4,), garbage, dtype=torch.int32, device="cuda")
+    return fr.fr_softmax_rows_workspace_init(ws) if init else ws
+
+
+def recomputed(ws):
+    """The workspace's count of partials the single pass computed a second time."""
+    return int(host(ws[:1]).view(np.uint32)[0])
 
 
 def valid_mask(rows, cols, lengths):
@@ -263,7 +274,7 @@ def test_softmax_single_pass_graph_replays():
     x, L = synth.ragged_softmax_inputs(rows, cols, seed=2860)
     x2, L2 = synth.ragged_softmax_inputs(rows, cols, seed=2861)
     xd, Ld, x2d, L2d = dev(x), dev(L), dev(x2), dev(L2)
-    ws = torch.empty(fr.fr_softmax_rows_workspace_bytes(rows, cols) // 4, dtype=torch.int32, device="cuda")
+    ws = new_ws(rows, cols)
     y, y2 = torch.full_like(xd, float("nan")), torch.empty_like(xd)
     am = torch.full((rows,), -7, dtype=torch.int32, device="cuda")
     am2 = torch.empty_like(am)
@@ -325,26 +336,26 @@ def test_softmax_split_passes(passes, cols):
 def test_softmax_single_pass_fallback_gives_the_same_bits(shape):
     """In the single pass a workgroup that stops waiting computes the missing
     partials of its row from x itself. Forced for every partial (wait_us < 0),
-    y and the argmax keep their bits, and the workspace header counts each
+    y and the argmax keep their bits, and the workspace's count grows by each
     recomputed partial: sum over rows of nc * (nc - 1). 7 x 20001 has rows
     that are not 16-byte aligned (row stride 20001 floats): the element-wise
     path, whose recompute streams the chunk instead of taking it from
-    registers. The workspace starts as garbage: the reset kernel clears it.
-    How many partials the default wait recomputed depends on scheduling (a
-    busy device makes partners late), so it is reported, not asserted."""
+    registers. The workspace held garbage before its initialization. How
+    many partials the default wait recomputed depends on scheduling (a busy
+    device makes partners late), so it is reported, not asserted."""
     rows, cols = shape
     x, L = synth.ragged_softmax_inputs(rows, cols, seed=2950 + rows, choices=(1000, cols // 2 + 3, cols - 1, cols))
     xd, Ld = dev(x), dev(L)
-    nbytes = fr.fr_softmax_rows_workspace_bytes(rows, cols)
-    ws = torch.full((nbytes // 4,), 0x5A5A5A5A, dtype=torch.int32, device="cuda")
+    ws = new_ws(rows, cols)
     outs = {}
     try:
         for wait in (0, -1):
             fr.fr_tune_override(fr.FR_OP_SOFTMAX, form=fr.FR_FORM_SPLIT, threads=256, vec=8, passes=1, wait_us=wait)
             y = torch.full_like(xd, float("nan"))
             am = torch.full((rows,), -7, dtype=torch.int32, device="cuda")
+            before = recomputed(ws)
             fr.fr_softmax_rows(xd, y, lengths=Ld, argmax=am, ws=ws)
-            outs[wait] = (host(y), host(am), int(host(ws)[0]))
+            outs[wait] = (host(y), host(am), recomputed(ws) - before)
     finally:
         fr.fr_tune_override(fr.FR_OP_SOFTMAX)
     nc = (np.asarray(L, dtype=np.int64) + 8191) // 8192
@@ -353,6 +364,93 @@ def test_softmax_single_pass_fallback_gives_the_same_bits(shape):
     assert np.array_equal(outs[0][0].view(np.uint32), outs[-1][0].view(np.uint32))
     assert np.array_equal(outs[0][1], outs[-1][1])
     compare(x, outs[0][0], outs[0][1], lengths=L, what=f"single pass {rows}x{cols}")
+
+
+def one_call(x, L, ws, passes=1, vec=8, argmax=True):
+    xd, Ld = dev(x), dev(L)
+    y = torch.full_like(xd, float("nan"))
+    am = torch.full((x.shape[0],), -7, dtype=torch.int32, device="cuda") if argmax else None
+    try:
+        fr.fr_tune_override(fr.FR_OP_SOFTMAX, form=fr.FR_FORM_SPLIT, threads=256, vec=vec, passes=passes)
+        fr.fr_softmax_rows(xd, y, lengths=Ld, argmax=am, ws=ws)
+    finally:
+        fr.fr_tune_override(fr.FR_OP_SOFTMAX)
+    return host(y), (host(am) if argmax else None)
+
+
+def test_softmax_single_pass_workspace_reused_across_calls():
+    """One workspace, initialized once, through a sequence of calls whose
+    chunk lists differ (row counts, lengths, chunk sizes, the two-kernel form
+    in between): slots left by an earlier call carry that call's tag (or the
+    two-kernel form's), which the next call never accepts. Every call equals,
+    bit for bit, the same call on a freshly initialized workspace, and the
+    oracle."""
+    cap = 131072
+    big = fr.fr_softmax_rows_workspace_bytes(96, cap)
+    for vec in (4,):
+        big = max(big, 64 + 96 * (cap // (256 * 4 * vec)) * 16)
+    ws = fr.fr_softmax_rows_workspace_init(torch.full((big // 4,), 0x7F7F7F7F, dtype=torch.int32, device="cuda"))
+    calls = [(96, (131071, 50257, 3000), 1, 8), (40, (131072, 9000), 1, 8), (96, (131071, 70000, 1000), 2, 8),
+             (96, (131071, 50257, 3000), 1, 8), (17, (100000, 30000, 8193), 1, 4), (96, (120000, 1), 1, 8),
+             (40, (131072, 9000), 1, 8)]
+    for i, (rows, choices, passes, vec) in enumerate(calls):
+        x, L = synth.ragged_softmax_inputs(rows, cap, seed=3200 + i, choices=choices)
+        y, am = one_call(x, L, ws, passes=passes, vec=vec)
+        fresh = fr.fr_softmax_rows_workspace_init(torch.empty(big // 4, dtype=torch.int32, device="cuda"))
+        y0, am0 = one_call(x, L, fresh, passes=passes, vec=vec)
+        written = valid_mask(rows, cap, L)
+        assert np.array_equal(y[written].view(np.uint32), y0[written].view(np.uint32)), f"call {i}"
+        assert np.array_equal(am, am0), f"call {i}"
+        compare(x, y, am, lengths=L, what=f"reused workspace, call {i}")
+        assert np.isnan(y[~written]).all(), f"call {i}: an output tail was written"
+
+
+def test_softmax_single_pass_uninitialized_workspace_is_still_exact():
+    """A workspace that was never initialized (no mark in its header) is
+    never trusted: every partner partial is computed from x, giving the same
+    bits as an initialized workspace, and the count grows by sum nc * (nc - 1)."""
+    rows, cols = 48, 131072
+    x, L = synth.ragged_softmax_inputs(rows, cols, seed=3300)
+    good = new_ws(rows, cols)
+    y0, am0 = one_call(x, L, good)
+    for garbage in (0x5A5A5A5A, 0, -1):
+        bad = new_ws(rows, cols, garbage=garbage, init=False)
+        before = recomputed(bad)
+        y, am = one_call(x, L, bad)
+        nc = (np.asarray(L, dtype=np.int64) + 8191) // 8192
+        assert (recomputed(bad) - before) % (1 << 32) == int((nc * (nc - 1)).sum()), hex(garbage & 0xFFFFFFFF)
+        written = valid_mask(rows, cols, L)
+        assert np.array_equal(y[written].view(np.uint32), y0[written].view(np.uint32))
+        assert np.array_equal(am, am0)
+
+
+def test_softmax_single_pass_epoch_limit():
+    """The call counter is 31 bits: the call that takes the last tag still
+    exchanges partials; from the next call on no slot is trusted (same bits,
+    every partner partial recomputed) until the workspace is initialized
+    again. The counter is set near its end through the header word that
+    holds it (word 2)."""
+    rows, cols = 32, 131072
+    x, L = synth.ragged_softmax_inputs(rows, cols, seed=3400)
+    nc = (np.asarray(L, dtype=np.int64) + 8191) // 8192
+    ws = new_ws(rows, cols)
+    y0, am0 = one_call(x, L, ws)
+    ws[2] = 0x7FFFFFFE  # the last call that may take a tag
+    written = valid_mask(rows, cols, L)
+    for expect_all in (False, True):
+        before = recomputed(ws)
+        y, am = one_call(x, L, ws)
+        delta = recomputed(ws) - before
+        if expect_all:
+            assert delta == int((nc * (nc - 1)).sum())
+        assert np.array_equal(y[written].view(np.uint32), y0[written].view(np.uint32))
+        assert np.array_equal(am, am0)
+    assert int(host(ws[2:3])[0]) == 0x7FFFFFFF
+    fr.fr_softmax_rows_workspace_init(ws)
+    assert int(host(ws[2:3])[0]) == 0
+    y, am = one_call(x, L, ws)
+    assert np.array_equal(y[written].view(np.uint32), y0[written].view(np.uint32))
+    assert int(host(ws[2:3])[0]) == 1
 
 
 @pytest.mark.parametrize("wait", [0, -1])
@@ -364,8 +462,7 @@ def test_softmax_split_in_place(wait):
     rows, cols = 24, 50000
     x, L = synth.ragged_softmax_inputs(rows, cols, seed=2970, choices=(1000, 8193, 40000, 50000))
     Ld = dev(L)
-    nbytes = fr.fr_softmax_rows_workspace_bytes(rows, cols)
-    ws = torch.full((nbytes // 4,), 0x5A5A5A5A, dtype=torch.int32, device="cuda")
+    ws = new_ws(rows, cols)
     am = torch.full((rows,), -7, dtype=torch.int32, device="cuda")
     xd = dev(x)
     with forced(fr.FR_FORM_SPLIT):

@@ -209,11 +209,11 @@ def test_plans_for_the_five_workloads():
     p = fr.fr_plan_query(fr.FR_OP_SUMSQ, 1, n, ws_bytes=ws)
     assert (p.form, p.splits, p.chunk, p.grid, p.grid2) == (fr.FR_FORM_SPLIT, 512, 1 << 19, 512, 1)
     # ragged softmax, 512 rows of capacity 131072, with a workspace: 16 chunks of 8192, a
-    # 64-byte header and 512 x 16 partial slots of 16 bytes; one kernel whose grid is every
-    # workgroup that can be resident at once (4 per CU at 256 threads, two chunks in
-    # registers), waiting 200 us by default
+    # 64-byte header, 4096 workgroup flags and 512 x 16 partial slots of 16 bytes; one kernel
+    # whose grid is every workgroup that can be resident at once (4 per CU at 256 threads,
+    # two chunks in registers), waiting 200 us by default
     ws = fr.fr_softmax_rows_workspace_bytes(512, 131072)
-    assert ws == 64 + 512 * 16 * 16
+    assert ws == 64 + 4 * 4096 + 512 * 16 * 16
     p = fr.fr_plan_query(fr.FR_OP_SOFTMAX, 512, 131072, has_lengths=True, ws_bytes=ws)
     assert (p.form, p.splits, p.chunk, p.passes, p.grid, p.grid2, p.wait_us) == \
         (fr.FR_FORM_SPLIT, 16, 8192, 1, 256 * 4, 0, 200)
@@ -305,7 +305,7 @@ def test_tune_override_replaces_the_launch_knobs():
         assert (p.splits, p.chunk, p.passes) == (32, 4096, 1)
         fr.fr_tune_override(fr.FR_OP_SOFTMAX, form=fr.FR_FORM_SPLIT, threads=256, vec=8, passes=2)
         p = fr.fr_plan_query(fr.FR_OP_SOFTMAX, 512, 131072, ws_bytes=1 << 30)
-        assert (p.splits, p.passes, p.grid, p.grid2, p.ws_bytes) == (16, 2, 8192, 8192, 64 + 512 * 16 * 16)
+        assert (p.splits, p.passes, p.grid, p.grid2, p.ws_bytes) == (16, 2, 8192, 8192, 64 + 4 * 4096 + 512 * 16 * 16)
         # the single pass with 512 threads: 2 resident workgroups per CU; wait overrides pass through
         fr.fr_tune_override(fr.FR_OP_SOFTMAX, form=fr.FR_FORM_SPLIT, threads=512, vec=4, passes=1, wait_us=-1)
         p = fr.fr_plan_query(fr.FR_OP_SOFTMAX, 512, 131072, ws_bytes=1 << 30)
