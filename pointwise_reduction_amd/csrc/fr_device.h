@@ -44,7 +44,8 @@ __device__ __forceinline__ int shfl_xor(int v, int m) { return __shfl_xor(v, m, 
 // steps up to k every lane of an aligned 2k-lane group holds the group
 // result: xor 1 and xor 2 inside quads, then the half-row and row mirrors,
 // whose partner always lies in the other (already reduced) half of the
-// group. Steps 16 and 32 cross DPP rows and go through ds_bpermute.
+// group. Steps 16 and 32 cross DPP rows: group_reduce takes them with the
+// permlane swaps below.
 template <int STEP, typename T>
 __device__ __forceinline__ T partner(T v) {
     static_assert(STEP == 1 || STEP == 2 || STEP == 4 || STEP == 8, "DPP butterfly step");
@@ -68,15 +69,60 @@ struct OpMinI {
     __device__ __forceinline__ int operator()(int a, int b) const { return a < b ? a : b; }
 };
 
-// Reduce over aligned groups of SEG lanes (SEG a power of two, <= 64).
+// The two halves of each aligned group of 2 * STEP lanes (STEP 16 or 32),
+// as seen from every lane of the group: lo is the value of lane i & ~STEP,
+// hi that of lane i | STEP. gfx950's v_permlane16_swap / v_permlane32_swap
+// with both operands the same register: the first result keeps the lower
+// rows and receives the lower rows' values in the upper ones, the second
+// the reverse. VALU moves, no LDS traffic.
+template <int STEP>
+__device__ __forceinline__ void halves(uint32_t v, uint32_t& lo, uint32_t& hi) {
+    static_assert(STEP == 16 || STEP == 32, "cross-row step");
+    if constexpr (STEP == 32) {
+        const auto p = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        lo = p[0];
+        hi = p[1];
+    } else {
+        const auto p = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        lo = p[0];
+        hi = p[1];
+    }
+}
+template <int STEP>
+__device__ __forceinline__ void halves(float v, float& lo, float& hi) {
+    uint32_t l, h;
+    halves<STEP>(__builtin_bit_cast(uint32_t, v), l, h);
+    lo = __builtin_bit_cast(float, l);
+    hi = __builtin_bit_cast(float, h);
+}
+template <int STEP>
+__device__ __forceinline__ void halves(int v, int& lo, int& hi) {
+    uint32_t l, h;
+    halves<STEP>((uint32_t)v, l, h);
+    lo = (int)l;
+    hi = (int)h;
+}
+
+// Reduce over aligned groups of SEG lanes (SEG a power of two, <= 64). The
+// steps inside a 16-lane row are DPP butterflies; the steps across rows
+// combine the group's lower and upper halves in that order, so every lane
+// computes the same op(lo, hi).
 template <int SEG, typename T, typename Op>
 __device__ __forceinline__ T group_reduce(T v, Op op) {
     if constexpr (SEG >= 2) v = op(v, partner<1>(v));
     if constexpr (SEG >= 4) v = op(v, partner<2>(v));
     if constexpr (SEG >= 8) v = op(v, partner<4>(v));
     if constexpr (SEG >= 16) v = op(v, partner<8>(v));
-    if constexpr (SEG >= 32) v = op(v, shfl_xor(v, 16));
-    if constexpr (SEG >= 64) v = op(v, shfl_xor(v, 32));
+    if constexpr (SEG >= 32) {
+        T lo, hi;
+        halves<16>(v, lo, hi);
+        v = op(lo, hi);
+    }
+    if constexpr (SEG >= 64) {
+        T lo, hi;
+        halves<32>(v, lo, hi);
+        v = op(lo, hi);
+    }
     return v;
 }
 
@@ -147,10 +193,21 @@ template <int STEP>
 __device__ __forceinline__ Stat partner(Stat v) {
     return Stat{partner<STEP>(v.n), partner<STEP>(v.mu), partner<STEP>(v.m2)};
 }
-__device__ __forceinline__ MD shfl_xor(MD v, int m) { return MD{shfl_xor(v.m, m), shfl_xor(v.d, m)}; }
-__device__ __forceinline__ MI shfl_xor(MI v, int m) { return MI{shfl_xor(v.m, m), shfl_xor(v.i, m)}; }
-__device__ __forceinline__ Stat shfl_xor(Stat v, int m) {
-    return Stat{shfl_xor(v.n, m), shfl_xor(v.mu, m), shfl_xor(v.m2, m)};
+template <int STEP>
+__device__ __forceinline__ void halves(MD v, MD& lo, MD& hi) {
+    halves<STEP>(v.m, lo.m, hi.m);
+    halves<STEP>(v.d, lo.d, hi.d);
+}
+template <int STEP>
+__device__ __forceinline__ void halves(MI v, MI& lo, MI& hi) {
+    halves<STEP>(v.m, lo.m, hi.m);
+    halves<STEP>(v.i, lo.i, hi.i);
+}
+template <int STEP>
+__device__ __forceinline__ void halves(Stat v, Stat& lo, Stat& hi) {
+    halves<STEP>(v.n, lo.n, hi.n);
+    halves<STEP>(v.mu, lo.mu, hi.mu);
+    halves<STEP>(v.m2, lo.m2, hi.m2);
 }
 
 struct OpMD {
