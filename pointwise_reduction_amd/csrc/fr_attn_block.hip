@@ -11,7 +11,9 @@
 //   S^T = K Q^T   A = a K tile (key rows, read from LDS), B = the wave's Q
 //                 rows (read from LDS). D holds, for lane l's query (column
 //                 l % 16), the keys 4 (l / 16) .. +3 of each 16-key tile.
-//   O  += P V     A = P. A lane's D registers of two consecutive key tiles
+//   O  += P V     A = P, as two bf16 parts (its rounding and the rounding
+//                 of the remainder, two products), so that P enters at about
+//                 fp32 accuracy. A lane's D registers of two consecutive key tiles
 //                 hold exactly 8 keys of its own query: they are its A
 //                 fragment, with the k positions of the 32-key step mapped
 //                 to keys 4 (l / 16) + i and 16 + 4 (l / 16) + i. B = V with
@@ -69,8 +71,19 @@ __device__ __forceinline__ f32x4 mfma(f32x4 a, f32x4 b, f32x4 c) {
 
 __device__ __forceinline__ f32x4 ld16g(const uint16_t* p) { return *reinterpret_cast<const f32x4*>(p); }
 
-// two fp32 -> packed bf16 (round to nearest even)
-__device__ __forceinline__ float pk(float lo, float hi) { return __builtin_bit_cast(float, pack_bf16(lo, hi)); }
+// Two fp32 values p0, p1 as two packed bf16 pairs: their roundings to
+// nearest even (hw) and the roundings of what those leave over (lw). The
+// remainders p - bf16(p) are exact in fp32, so hi + lo differs from p only
+// by the rounding of the remainder, at most 2^-9 of it: 2^-18 p. The
+// matrix cores take both pairs, so P V carries P to about fp32 accuracy
+// instead of the 2^-9 of one bf16 rounding.
+__device__ __forceinline__ void split2(float p0, float p1, float& hw, float& lw) {
+    const uint32_t h = pack_bf16(p0, p1);
+    const float r0 = p0 - __builtin_bit_cast(float, h << 16);
+    const float r1 = p1 - __builtin_bit_cast(float, h & 0xFFFF0000u);
+    hw = __builtin_bit_cast(float, h);
+    lw = __builtin_bit_cast(float, pack_bf16(r0, r1));
+}
 
 }  // namespace
 
@@ -286,11 +299,17 @@ __global__ __launch_bounds__(kThreads, 2) void fr_attn_block_bf16(const uint16_t
     auto pv_block = [&](int buf, const f32x4 (&st)[4][2]) __attribute__((always_inline)) {
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-            f32x4 pa[2];
+            f32x4 pa[2], pl[2];  // P as bf16 pairs, and the remainders
 #pragma unroll
             for (int bq = 0; bq < 2; ++bq) {
                 const f32x4 lo = st[2 * kk][bq], hi = st[2 * kk + 1][bq];
-                pa[bq] = f32x4{pk(lo[0], lo[1]), pk(lo[2], lo[3]), pk(hi[0], hi[1]), pk(hi[2], hi[3])};
+                float h0, h1, h2, h3, l0, l1, l2, l3;
+                split2(lo[0], lo[1], h0, l0);
+                split2(lo[2], lo[3], h1, l1);
+                split2(hi[0], hi[1], h2, l2);
+                split2(hi[2], hi[3], h3, l3);
+                pa[bq] = f32x4{h0, h1, h2, h3};
+                pl[bq] = f32x4{l0, l1, l2, l3};
             }
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
@@ -305,7 +324,7 @@ __global__ __launch_bounds__(kThreads, 2) void fr_attn_block_bf16(const uint16_t
                     f32x4, (short __attribute__((ext_vector_type(8)))){v0[0], v0[1], v0[2], v0[3], v1[0], v1[1],
                                                                         v1[2], v1[3]});
 #pragma unroll
-                for (int bq = 0; bq < 2; ++bq) acc[bq][t] = mfma(pa[bq], bv, acc[bq][t]);
+                for (int bq = 0; bq < 2; ++bq) acc[bq][t] = mfma(pl[bq], bv, mfma(pa[bq], bv, acc[bq][t]));
             }
         }
     };
