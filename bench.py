@@ -774,6 +774,53 @@ def read_traffic(kernel, workload):
         return None
 
 
+def measure_latency(torch, fr):
+    """lambda of Little's law ("Stax (4)", 9.1) on this device: dependent
+    loads along random cycles whose entries lie 256 bytes apart (two cache
+    lines), over spans that fit one XCD's L2 (4 MiB), fit the MALL (256 MB)
+    but not the L2, and fit neither. L2: the cycle is walked once first and
+    then measured; MALL: walked once in full, then 100k loads (12.8 MB of
+    lines, three times the L2) measured; HBM: 100k loads over a 4 GiB cycle
+    touched for the first time, each run on a fresh stretch of it.
+    Returns one JSON-ready dict."""
+    khz = fr.fr_device_clock_khz()
+    out = torch.zeros(2, dtype=torch.int64, device="cuda")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(9001)
+    stride = 256
+    levels = {}
+    for name, span, warm, steps in (("l2", 2 << 20, True, 20000), ("mall", 128 << 20, True, 100000),
+                                    ("hbm", 4 << 30, False, 100000)):
+        n = span // 4
+        m = span // stride
+        chain = torch.zeros(n, dtype=torch.int32, device="cuda")
+        order = torch.randperm(m, generator=gen, device="cuda") * (stride // 4)
+        chain[order] = torch.roll(order, -1).to(torch.int32)  # one cycle through every position
+        del order
+        start = 0
+        if warm:
+            fr.fr_pointer_chase(chain, m, start, out)  # the whole cycle once
+        torch.cuda.synchronize()
+        runs = []
+        for _ in range(3):
+            fr.fr_pointer_chase(chain, steps, start, out)
+            torch.cuda.synchronize()
+            runs.append(int(out[0].item()) / khz * 1e6 / steps)  # ns per load
+            if not warm:
+                start = int(out[1].item())  # the next run continues on lines not yet touched
+        levels[name] = {"span_bytes": span, "stride_bytes": stride, "loads": steps,
+                        "ns_per_load": round(float(np.median(runs)), 1), "runs_ns": [round(r, 1) for r in runs]}
+        del chain
+        torch.cuda.empty_cache()
+    lam = levels["hbm"]["ns_per_load"] * 1e-9
+    q = lam * PEAK_HBM_GBS * 1e9
+    return {"metric": "dependent-load latency (lambda of Little's law)", "value": levels["hbm"]["ns_per_load"],
+            "unit": "ns", "n_gpus": 1, "higher_is_better": False, "levels": levels,
+            "littles_law": {"peak_GBs": PEAK_HBM_GBS, "bytes_in_flight_for_peak": round(q),
+                            "per_cu_bytes": round(q / 256)},
+            "data": "synthetic", "config": {"workload": "pointer chase, one lane, random cycles, 256-byte spacing"}}
+
+
 def run_procs(args):
     """The same measurement in args.procs child processes, one after the
     other (each its own HIP context); prints the median child's line with the
@@ -821,7 +868,7 @@ def main():
                              "layernorm",
                              "sumsq", "ragged", "copy", "stream_copy", "stream_copy_c3", "stream_read", "attn_decode", "softmax_bwd", "add_2d",
                              "gelu_bwd", "layernorm_bwd", "c1_region", "attn_block",
-                             "attn_block_full"])
+                             "attn_block_full", "latency"])
     ap.add_argument("--warm", action="store_true", help="one buffer set: reads may hit the MALL")
     ap.add_argument("--eager", action="store_true", help="launch each step from the host (no graph)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -846,6 +893,9 @@ def main():
 
     torch.cuda.set_device(0)
     dev_name = "cuda"
+    if args.workload == "latency":
+        print(json.dumps(measure_latency(torch, fr)), flush=True)
+        return
     wl, per_set = make_workload(args.workload, torch, fr, synth)
     host_timed = getattr(wl, "host_timed", False)
     wl.eager = args.eager

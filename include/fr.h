@@ -440,6 +440,20 @@ int fr_sumsq_full_noalloc(const void* x, int64_t n, void* out, int dtype, void* 
 int fr_device_clock(uint64_t* out, int slot, void* stream);
 int fr_device_clock_khz(int* khz);
 
+/* ------------------------------------------------------------ memory latency
+ * The latency lambda of Little's law ("Stax (4)", 9.1: bytes in flight =
+ * latency x bandwidth), measured by dependent loads: one lane follows
+ * chain[] from index `start` for `steps` loads, each load's address taken
+ * from the previous load's value. chain: device array of n uint32 (n <=
+ * 2^32), caller-owned; each index read is clamped to [0, n) before use, so
+ * the walk never leaves the array whatever it holds. out: device uint64[2]:
+ * out[0] = the walk's duration in the ticks of fr_device_clock (rate from
+ * fr_device_clock_khz), out[1] = the index reached. A random cycle whose
+ * entries lie one cache line or more apart over a span larger than the
+ * device caches gives the idle HBM latency; a small span, the cache's.
+ * FR_E_NULL / FR_E_SIZE / FR_E_ALIGN on bad arguments. */
+int fr_pointer_chase(const uint32_t* chain, int64_t n, int64_t steps, uint32_t start, uint64_t* out, void* stream);
+
 /* ------------------------------------------------------------ configuration search
  * "Stax (4)", 9.6: choosing a launch configuration is black-box optimisation
  * over a configuration space Pi = A_1 x ... x A_p of finite integer value

@@ -41,7 +41,7 @@ EXPORTS = (
     "fr_layernorm_rows", "fr_layernorm_rows_stats", "fr_layernorm_rows_backward_workspace_bytes",
     "fr_layernorm_rows_backward",
     "fr_sumsq_rows", "fr_sumsq_full_workspace_bytes", "fr_sumsq_full", "fr_sumsq_full_noalloc",
-    "fr_stream_copy", "fr_stream_read", "fr_device_clock", "fr_device_clock_khz",
+    "fr_stream_copy", "fr_stream_read", "fr_device_clock", "fr_device_clock_khz", "fr_pointer_chase",
     "fr_attn_decode_workspace_bytes", "fr_attn_decode",
     "fr_add_2d", "fr_gelu_backward", "fr_attn_block",
     "fr_region_create", "fr_region_destroy", "fr_region_run", "fr_region_state", "fr_region_counts",
@@ -100,6 +100,7 @@ def _load():
         "fr_stream_read": (I32, [P, I64, P, P]),
         "fr_device_clock": (I32, [P, I32, P]),
         "fr_device_clock_khz": (I32, [P]),
+        "fr_pointer_chase": (I32, [P, I64, I64, ctypes.c_uint32, P, P]),
         "fr_add_2d": (I32, [P, I64, I64, P, I64, I64, P, I64, I64, I64, I32, P]),
         "fr_layernorm_rows_stats": (I32, [P, P, P, P, P, P, I64, I64, I64, I64, I64, I64, ctypes.c_float, I32, P]),
         "fr_layernorm_rows_backward_workspace_bytes": (U64, [I64, I64, I32]),
@@ -364,6 +365,19 @@ def fr_device_clock_khz():
     khz = ctypes.c_int32()
     _check(lib.fr_device_clock_khz(ctypes.byref(khz)), "fr_device_clock_khz")
     return khz.value
+
+
+def fr_pointer_chase(chain, steps, start, out, stream=None):
+    """Follow chain (contiguous int32/uint32 device tensor of indices) from
+    `start` for `steps` dependent loads; out (int64 device tensor, 2 entries)
+    receives the ticks taken and the index reached."""
+    if chain.dtype not in (torch.int32,) or not chain.is_contiguous():
+        raise ValueError("expected a contiguous int32 chain")
+    if out.dtype != torch.int64 or not out.is_contiguous() or out.numel() < 2:
+        raise ValueError("expected an int64 tensor of 2 entries")
+    _check(lib.fr_pointer_chase(_ptr(chain), chain.numel(), steps, start, _ptr(out), _stream(stream)),
+           "fr_pointer_chase")
+    return out
 
 
 def fr_attn_decode_workspace_bytes(batch, heads_q, seq, dim):

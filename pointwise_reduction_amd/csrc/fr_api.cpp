@@ -586,6 +586,17 @@ int fr_device_clock(uint64_t* out, int slot, void* stream) {
     return finish_launch(launch_device_clock(out, slot, (hipStream_t)stream));
 }
 
+int fr_pointer_chase(const uint32_t* chain, int64_t n, int64_t steps, uint32_t start, uint64_t* out, void* stream) {
+    if (!chain || !out) return FR_E_NULL;
+    if (n < 1 || n > (int64_t(1) << 32) || steps < 0) return FR_E_SIZE;
+    if (!aligned(chain, 4) || !aligned(out, 8)) return FR_E_ALIGN;
+    int num_cus = 0;
+    const int st = device_check(&num_cus);
+    if (st != FR_OK) return st;
+    (void)hipGetLastError();
+    return finish_launch(launch_pointer_chase(chain, n, steps, start, out, (hipStream_t)stream));
+}
+
 int fr_device_clock_khz(int* khz) {
     if (!khz) return FR_E_NULL;
     int num_cus = 0, clock_khz = 0;

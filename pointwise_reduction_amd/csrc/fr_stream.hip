@@ -58,6 +58,32 @@ __global__ __launch_bounds__(64) void fr_clock_k(uint64_t* __restrict__ out, int
     if (threadIdx.x == 0) out[slot] = wall_clock64();
 }
 
+// Dependent loads: one lane follows a chain of indices, next = chain[i],
+// for `steps` loads, each waiting for the one before; out[0] = wall-clock
+// ticks taken, out[1] = the index reached (so the walk is observable and
+// checkable). Indices are clamped to [0, n) before use, so every load stays
+// inside the buffer whatever it holds. Non-temporal loads: the walk's lines
+// are not kept for a later visit.
+__global__ __launch_bounds__(64) void fr_chase_k(const uint32_t* __restrict__ chain, int64_t n, int64_t steps,
+                                                 uint32_t start, uint64_t* __restrict__ out) {
+    if (threadIdx.x != 0) return;
+    uint32_t i = start < n ? start : 0u;
+    const uint64_t t0 = wall_clock64();
+    for (int64_t k = 0; k < steps; ++k) {
+        const uint32_t nx = __builtin_nontemporal_load(chain + i);
+        i = nx < (uint64_t)n ? nx : 0u;
+    }
+    const uint64_t t1 = wall_clock64();
+    out[0] = t1 - t0;
+    out[1] = i;
+}
+
+hipError_t launch_pointer_chase(const uint32_t* chain, int64_t n, int64_t steps, uint32_t start, uint64_t* out,
+                                hipStream_t s) {
+    hipLaunchKernelGGL(fr_chase_k, dim3(1), dim3(64), 0, s, chain, n, steps, start, out);
+    return hipGetLastError();
+}
+
 hipError_t launch_device_clock(uint64_t* out, int slot, hipStream_t s) {
     hipLaunchKernelGGL(fr_clock_k, dim3(1), dim3(64), 0, s, out, slot);
     return hipGetLastError();

@@ -54,3 +54,28 @@ def test_device_clock_marks_bracket_stream_work():
     assert (256 << 21) / 8e6 <= us < 100_000, us
     with pytest.raises(ValueError):
         fr.fr_device_clock(marks, 2)
+
+
+def test_pointer_chase_follows_the_chain():
+    """The latency walk reaches the index a host walk of the same chain
+    reaches; indices outside the array are taken as 0 (clamped), so the walk
+    never leaves it."""
+    rng = np.random.default_rng(5)
+    n, stride = 1 << 14, 16
+    pos = np.arange(0, n, stride)
+    order = pos[rng.permutation(pos.size)]
+    chain = np.zeros(n, dtype=np.int64)
+    chain[order] = np.roll(order, -1)
+    chain[order[7]] = n + 12345  # out of range: the walk goes to 0
+    chain[0] = order[0]
+    cd = dev(chain.astype(np.uint32).view(np.int32))
+    out = torch.zeros(2, dtype=torch.int64, device="cuda")
+    for steps in (0, 1, 5, 100, 3000):
+        fr.fr_pointer_chase(cd, steps, int(order[0]), out)
+        i = int(order[0])
+        for _ in range(steps):
+            nx = int(chain[i])
+            i = nx if nx < n else 0
+        got = host(out)
+        assert int(got[1]) == i, steps
+        assert int(got[0]) >= 0
