@@ -22,17 +22,24 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SO = os.path.join(_HERE, "liboracle.so")
+# ORACLE_LIB names another build (the sanitizer run of the CPU tests)
+_SO = os.environ.get("ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 I64, I32, F64, U16 = ctypes.c_int64, ctypes.c_int32, ctypes.c_double, ctypes.c_uint16
 P = ctypes.c_void_p
 
 
-def build(verbose=False):
-    """Compile oracle.c into liboracle.so (gcc, no GPU toolchain involved)."""
-    cmd = ["gcc", "-O2", "-std=c11", "-fno-fast-math", "-shared", "-fPIC", "-o", _SO,
-           os.path.join(_HERE, "oracle.c"), "-lm"]
+SANITIZE_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                  "-fno-sanitize-recover=undefined"]
+
+
+def build(verbose=False, out=None, cc="gcc", extra=None):
+    """Compile oracle.c into liboracle.so (no GPU toolchain involved). `out`,
+    `cc` and `extra` flags serve the sanitized build (clang, SANITIZE_FLAGS)."""
+    flags = ["-O2"] if extra is None else list(extra)
+    cmd = [cc] + flags + ["-std=c11", "-fno-fast-math", "-shared", "-fPIC", "-o", out or _SO,
+                          os.path.join(_HERE, "oracle.c"), "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.check_call(cmd)

@@ -21,7 +21,9 @@ except ImportError:  # the C ABI is usable without torch
     torch = None
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libfr.so")
+# FR_LIB names another build of the same library (the sanitizer run of the
+# CPU tests loads a build whose host code is instrumented)
+LIB_PATH = os.environ.get("FR_LIB") or os.path.join(_HERE, "libfr.so")
 
 FR_OK = 0
 FR_E_NULL, FR_E_SIZE, FR_E_STRIDE, FR_E_DTYPE, FR_E_ALIGN = -1, -2, -3, -4, -5

@@ -82,16 +82,27 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
-def build(verbose=False, jobs=None):
-    """Compile all sources (in parallel) and link libfr.so. Always rebuilds."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
+# Host-side sanitizers for the CPU test run: each flag reaches the host pass
+# only (-Xarch_host before it); device code is built as usual.
+HOST_SANITIZE_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                       "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+                       "-Xarch_host", "-g"]
+
+
+def build(verbose=False, jobs=None, lib=None, build_dir=None, host_extra=None):
+    """Compile all sources (in parallel) and link libfr.so. Always rebuilds.
+    `lib`, `build_dir` and `host_extra` (e.g. HOST_SANITIZE_FLAGS) serve
+    other builds of the same sources."""
+    lib = lib or LIB
+    build_dir = build_dir or BUILD_DIR
+    os.makedirs(build_dir, exist_ok=True)
     cc = hipcc()
-    flags = common_flags()
+    flags = common_flags() + list(host_extra or [])
 
     usage = {}
 
     def compile_one(src):
-        obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+        obj = os.path.join(build_dir, os.path.basename(src) + ".o")
         lang = ["-x", "hip", "-Rpass-analysis=kernel-resource-usage"] if src.endswith(".hip") else []
         cmd = [cc] + flags + lang + ["-c", src, "-o", obj]
         if verbose:
@@ -111,20 +122,20 @@ def build(verbose=False, jobs=None):
     jobs = jobs or min(8, len(srcs))
     with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(compile_one, srcs))
-    with open(os.path.join(BUILD_DIR, "resource_usage.txt"), "w") as f:
+    with open(os.path.join(build_dir, "resource_usage.txt"), "w") as f:
         for name, u in sorted(usage.items()):
             f.write(f"{name} vgpr={u.get('vgpr')} scratch={u.get('scratch')} occupancy={u.get('occupancy')}\n")
     spills = sorted(n for n, u in usage.items() if u.get("scratch", 0) > 0)
     if spills:  # Algorithm 9.1 rejects configurations that spill registers
         raise RuntimeError("kernels spill registers to scratch: " + ", ".join(spills))
     check_residency(usage)
-    tmp = LIB + ".tmp"
-    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+    tmp = lib + ".tmp"
+    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + list(host_extra or []) + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

@@ -26,16 +26,19 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SO = os.path.join(_HERE, "libsynth.so")
+# SYNTH_LIB names another build (the sanitizer run of the CPU tests)
+_SO = os.environ.get("SYNTH_LIB") or os.path.join(_HERE, "libsynth.so")
 _lib = None
 
 I64, U64, F64, I32 = ctypes.c_int64, ctypes.c_uint64, ctypes.c_double, ctypes.c_int32
 P = ctypes.c_void_p
 
 
-def build(verbose=False):
-    """Compile synth.c into libsynth.so with gcc."""
-    cmd = ["gcc", "-O2", "-std=c11", "-shared", "-fPIC", "-o", _SO, os.path.join(_HERE, "synth.c"), "-lm"]
+def build(verbose=False, out=None, cc="gcc", extra=None):
+    """Compile synth.c into libsynth.so. `out`, `cc` and `extra` flags serve
+    the sanitized build of the CPU tests."""
+    flags = ["-O2"] if extra is None else list(extra)
+    cmd = [cc] + flags + ["-std=c11", "-shared", "-fPIC", "-o", out or _SO, os.path.join(_HERE, "synth.c"), "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.check_call(cmd)
