@@ -733,3 +733,27 @@ def test_attn_fwd_key_permutation_and_shift():
     o3, lse3, _, _ = oracle.attn_fwd(q, k + u, v)
     assert np.allclose(o, o3, rtol=1e-12, atol=1e-13)
     assert np.allclose(lse3, lse + (q[0, 0] @ u) / np.sqrt(3), rtol=1e-12)
+
+
+def test_row_functions_do_not_depend_on_the_thread_count():
+    # the host-thread split only hands out row ranges; every row is the same
+    # sequential loop, so one and eight threads give the same bits (the
+    # all-cores cpu_baseline times exactly these calls)
+    x = synth.normal((37, 515), seed=17) * 3
+    L = np.array([(i * 97) % 516 for i in range(37)], np.int32)
+    for t in (2, 8):
+        y1, a1 = oracle.softmax_rows(x, lengths=L)
+        yt, at = oracle.softmax_rows(x, lengths=L, threads=t)
+        assert np.array_equal(y1, yt, equal_nan=True) and np.array_equal(a1, at)
+        b = synth.uniform((37, 515), seed=18)
+        assert all(np.array_equal(u, v) for u, v in zip(oracle.sum_relu_add(x, b), oracle.sum_relu_add(x, b, threads=t)))
+        assert np.array_equal(oracle.sumsq_rows(x), oracle.sumsq_rows(x, threads=t))
+        xb = synth.to_bf16(x)
+        assert all(np.array_equal(u, v) for u, v in zip(oracle.layernorm_rows(xb), oracle.layernorm_rows(xb, threads=t)))
+    # the whole-vector sum over slices reorders fp64 additions only: both
+    # orders lie within n * 2^-53 (relative) of the exact sum of these
+    # nonnegative terms
+    v = synth.uniform((100_003,), seed=19)
+    exact = math.fsum(float(t) * float(t) for t in v)
+    for t in (1, 8):
+        assert math.isclose(oracle.sumsq(v, threads=t), exact, rel_tol=v.size * 2.0**-53)
