@@ -27,6 +27,12 @@ constexpr int kDppXor1 = 0xB1;
 constexpr int kDppXor2 = 0x4E;
 constexpr int kDppHalfMirror = 0x141;
 constexpr int kDppMirror = 0x140;
+// row_shr:n = 0x110 + n: lane i of a 16-lane row reads lane i - n of the
+// same row; lanes with no such source keep the old value
+constexpr int kDppRowShr1 = 0x111;
+constexpr int kDppRowShr2 = 0x112;
+constexpr int kDppRowShr4 = 0x114;
+constexpr int kDppRowShr8 = 0x118;
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {

@@ -115,11 +115,12 @@ __global__ __launch_bounds__(256) void fr_per_softmax_f32(const float* x, float*
         }
 #pragma unroll
         for (int q = 0; q < RPW; ++q) {
-            float s = 0.f;
+            float s;
 #pragma unroll
             for (int k = 0; k < NV; ++k) {
                 v[q][k] = M == kNone ? exp4(v[q][k], m[q]) : exp4_masked(v[q][k], m[q], (k * SEG + l) * 4, L[q]);
-                s += (v[q][k].x + v[q][k].y) + (v[q][k].z + v[q][k].w);
+                const float t = (v[q][k].x + v[q][k].y) + (v[q][k].z + v[q][k].w);
+                s = k == 0 ? t : s + t;  // the terms are >= +0, so no -0 to keep
             }
             inv[q] = s;
         }
@@ -496,6 +497,8 @@ __device__ void epoch_advance(uint32_t* hdr, const uint32_t* flags, uint32_t tag
 struct OneEntry {
     int r, c, nc, base, start, n;
 };
+// Entries per workgroup whose rows are found while the list is built.
+constexpr int kEntryTable = 8;
 
 // chunk_partial for a chunk of n elements in registers (lanes past n hold
 // -inf) with chunk-relative indices and the thread id passed in: the same
@@ -532,7 +535,8 @@ __device__ __forceinline__ SoftmaxPartial pipe_partial(const f32x4* v, int n, in
 
 template <int T, int NV>
 __device__ __forceinline__ void one_pass_pipelined(const float* x, float* y, int64_t x_rs, int64_t y_rs,
-                                                   const int* s_base, const int* s_len, int rows, int total,
+                                                   const int* s_base, const int* s_len, const int* s_erow,
+                                                   int rows, int total,
                                                    int32_t* argmax, uint32_t* hdr, uint64_t* slots, float* sl_m,
                                                    float* sl_d, int* sl_i, uint64_t* s_missing, float* s_mx,
                                                    int* s_kstar, uint32_t tag, int64_t wait_ticks) {
@@ -542,21 +546,32 @@ __device__ __forceinline__ void one_pass_pipelined(const float* x, float* y, int
     // the list lives in LDS; its values are the same for every lane, and
     // reading them as such keeps the search and the buffer resources scalar
     auto uni = [](int v) __attribute__((always_inline)) { return __builtin_amdgcn_readfirstlane(v); };
-    auto entry = [&](int t) __attribute__((always_inline)) {
-        const int tt = t < total ? t : 0;
-        int lo = 0, hi = rows;  // s_base[lo] <= tt < s_base[hi]; rows without chunks never qualify
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (uni(s_base[mid]) <= tt) lo = mid;
-            else hi = mid;
-        }
+    // entry t = blockIdx.x + k G of the list: its row from the table built
+    // with the list (k < kEntryTable), else by binary search
+    auto entry = [&](int t, int k) __attribute__((always_inline)) {
         OneEntry e;
-        e.r = lo;
+        if (t >= total) {  // past the list: an empty range, nothing read or written
+            e.r = 0, e.base = 0, e.nc = 1, e.c = 0, e.start = 0, e.n = 0;
+            return e;
+        }
+        int lo = k < kEntryTable ? uni(s_erow[k]) : 0;
         e.base = uni(s_base[lo]);
         e.nc = uni(s_base[lo + 1]) - e.base;
-        e.c = tt - e.base;
+        if (k >= kEntryTable || t < e.base || t >= e.base + e.nc) {
+            lo = 0;
+            int hi = rows;  // s_base[lo] <= t < s_base[hi]; rows without chunks never qualify
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (uni(s_base[mid]) <= t) lo = mid;
+                else hi = mid;
+            }
+            e.base = uni(s_base[lo]);
+            e.nc = uni(s_base[lo + 1]) - e.base;
+        }
+        e.r = lo;
+        e.c = t - e.base;
         e.start = e.c * C;
-        e.n = t < total ? min(uni(s_len[lo]) - e.start, C) : 0;  // an entry past the list: empty range
+        e.n = min(uni(s_len[lo]) - e.start, C);
         return e;
     };
     // lane offset in a register, vector offset k * T * 16 as a constant
@@ -689,13 +704,13 @@ __device__ __forceinline__ void one_pass_pipelined(const float* x, float* y, int
     };
 
     f32x4 va[NV], vb[NV];
-    OneEntry ea = entry(blockIdx.x);
+    OneEntry ea = entry(blockIdx.x, 0);
     issue(va, ea, tid);
-    for (int t = blockIdx.x; t < total; t += 2 * G) {
-        const OneEntry eb = entry(t + G);
+    for (int t = blockIdx.x, k = 0; t < total; t += 2 * G, k += 2) {
+        const OneEntry eb = entry(t + G, k + 1);
         step(ea, va, eb, vb);
         if (t + G >= total) break;
-        ea = entry(t + 2 * G);
+        ea = entry(t + 2 * G, k + 2);
         step(eb, vb, ea, va);
     }
 }
@@ -825,6 +840,7 @@ __global__ __launch_bounds__(T) void fr_split_softmax_one(const float* x, float*
     __shared__ int s_base[kOnePassMaxRows + 1];  // first list entry of each row; [rows] = list length
     __shared__ int s_len[kOnePassMaxRows];
     __shared__ int s_scan[T / kWave];
+    __shared__ int s_erow[kEntryTable];  // row of entry blockIdx.x + k G
     __shared__ float sl_m[T / kWave];
     __shared__ float sl_d[T / kWave];
     __shared__ int sl_i[T / kWave];
@@ -837,46 +853,70 @@ __global__ __launch_bounds__(T) void fr_split_softmax_one(const float* x, float*
     uint64_t* slots = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + kSplitWsSlots);
     const int tid = threadIdx.x;
 
-    // the initialization mark and the epoch, loaded now and used once the
-    // chunk list is built
-    uint64_t magic = 0;
-    uint32_t epoch = 0;
-    if (tid == 0) {
-        magic = __hip_atomic_load(reinterpret_cast<uint64_t*>(hdr + kHdrMagic), __ATOMIC_RELAXED,
-                                  __HIP_MEMORY_SCOPE_AGENT);
-        epoch = __hip_atomic_load(&hdr[kHdrEpoch], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-
-    // chunk list: thread tid counts the chunks of rows [r0, r1)
+    // The row lengths (out-of-range offsets read 0), then the initialization
+    // mark and the epoch (loads with sc1, as the agent-scope atomic loads
+    // they stand for; only thread 0's offsets lie in range): every load is
+    // issued, without a branch, before any value is used, so the list build
+    // waits for one memory latency, not one per load, and the lengths do not
+    // wait for the header.
+    constexpr int RPT = kOnePassMaxRows / T;
+    const __amdgpu_buffer_rsrc_t rlen = row_rsrc(lengths, lengths ? (uint32_t)rows * 4u : 0u);
+    int lv[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) lv[i] = (int)__builtin_amdgcn_raw_buffer_load_b32(rlen, (tid + i * T) * 4, 0, 0);
+    const __amdgpu_buffer_rsrc_t rhdr = row_rsrc(hdr, (uint32_t)kSplitWsHeader);
+    const u32x2 magic_w =
+        __builtin_amdgcn_raw_buffer_load_b64(rhdr, tid == 0 ? kHdrMagic * 4 : kSplitWsHeader, 0, kAuxSc1);
+    const uint32_t epoch =
+        __builtin_amdgcn_raw_buffer_load_b32(rhdr, tid == 0 ? kHdrEpoch * 4 : kSplitWsHeader, 0, kAuxSc1);
+    // no lengths: the loads read 0 and every row gets cols elements. Entries
+    // past the rows are written too (never read), so that no store, and no
+    // load, sits under a branch
+    const int len0 = lengths ? 0 : cols;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) s_len[tid + i * T] = min(max(lv[i] + len0, 0), cols);
+    __syncthreads();
+    // ...then thread tid counts the chunks of rows [r0, r1)
     const int per = (rows + T - 1) / T;
     const int r0 = min(rows, tid * per), r1 = min(rows, r0 + per);
     int local = 0;
-    for (int r = r0; r < r1; ++r) {
-        const int L = row_len(lengths, r, cols);
-        s_len[r] = L;
-        local += (L + C - 1) / C;
-    }
-    // exclusive prefix sum of the counts: within each wave by shuffles,
-    // then the wave totals before this wave from LDS
+    for (int r = r0; r < r1; ++r) local += (s_len[r] + C - 1) / C;
+    // exclusive prefix sum of the counts: an inclusive scan inside each
+    // 16-lane DPP row (shifts by 1, 2, 4, 8), the row totals before this
+    // row from lanes 15, 31 and 47, then the wave totals before this wave
     const int lane = tid & (kWave - 1), wv = tid / kWave;
     int incl = local;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        const int up = __shfl_up(incl, off, kWave);
-        if (lane >= off) incl += up;
+    incl += __builtin_amdgcn_update_dpp(0, incl, kDppRowShr1, 0xF, 0xF, false);
+    incl += __builtin_amdgcn_update_dpp(0, incl, kDppRowShr2, 0xF, 0xF, false);
+    incl += __builtin_amdgcn_update_dpp(0, incl, kDppRowShr4, 0xF, 0xF, false);
+    incl += __builtin_amdgcn_update_dpp(0, incl, kDppRowShr8, 0xF, 0xF, false);
+    {
+        const int row16 = lane >> 4;
+        const int a = __builtin_amdgcn_readlane(incl, 15), b = __builtin_amdgcn_readlane(incl, 31),
+                  c = __builtin_amdgcn_readlane(incl, 47);
+        incl += (row16 >= 1 ? a : 0) + (row16 >= 2 ? b : 0) + (row16 >= 3 ? c : 0);
     }
     if (lane == kWave - 1) s_scan[wv] = incl;
     __syncthreads();
     int run = incl - local;
     for (int w = 0; w < wv; ++w) run += s_scan[w];
+    // the first list entry of each row, and the rows of this workgroup's
+    // entries blockIdx.x + k G for k < kEntryTable
     for (int r = r0; r < r1; ++r) {
+        const int cnt = (s_len[r] + C - 1) / C;
         s_base[r] = run;
-        run += (s_len[r] + C - 1) / C;
+#pragma unroll
+        for (int k = 0; k < kEntryTable; ++k) {
+            const int64_t t = (int64_t)blockIdx.x + (int64_t)k * gridDim.x;
+            if (t >= run && t < run + cnt) s_erow[k] = r;
+        }
+        run += cnt;
     }
     if (tid == T - 1) s_base[rows] = run;
     if (tid == 0) {
         // this call's tag (0: no slot is trusted), acknowledged in this
         // workgroup's flag: the stored value depends on the epoch read
+        const uint64_t magic = (uint64_t)magic_w.y << 32 | magic_w.x;
         const uint32_t t = (magic == kWsMagic && epoch < kMaxEpoch) ? epoch + 1 : 0u;
         if (t != 0u) __hip_atomic_store(&flags[blockIdx.x], t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_tag = t;
@@ -890,8 +930,8 @@ __global__ __launch_bounds__(T) void fr_split_softmax_one(const float* x, float*
             if (s_len[r] == 0) argmax[r] = -1;
 
     if constexpr (VEC) {
-        one_pass_pipelined<T, NV>(x, y, x_rs, y_rs, s_base, s_len, rows, total, argmax, hdr, slots, sl_m, sl_d, sl_i,
-                                  &s_missing, s_mx, &s_kstar, tag, wait_ticks);
+        one_pass_pipelined<T, NV>(x, y, x_rs, y_rs, s_base, s_len, s_erow, rows, total, argmax, hdr, slots, sl_m,
+                                  sl_d, sl_i, &s_missing, s_mx, &s_kstar, tag, wait_ticks);
     } else {
         one_pass_elementwise<T, NV>(x, y, x_rs, y_rs, s_base, s_len, rows, total, argmax, hdr, slots, sl_m, sl_d,
                                     sl_i, &s_missing, s_mx, &s_kstar, tag, wait_ticks);
