@@ -434,9 +434,10 @@ __global__ __launch_bounds__(T) void fr_split_softmax_fin(const float* x, float*
 //    m) and (tag, d). The tag is the call's epoch: the workspace header
 //    holds a counter E that every workgroup reads at its start (tag = E + 1)
 //    and then acknowledges by storing the tag in its own flag word (the
-//    store depends on the value read). Workgroup 0, at its end, waits until
-//    every flag holds the tag - every workgroup has read E - and stores
-//    E + 1 for the next call. No two workgroups update one word.
+//    store depends on the value read). The last workgroup (the one with the
+//    fewest entries), at its end, waits until every flag holds the tag -
+//    every workgroup has read E - and stores E + 1 for the next call. No two
+//    workgroups update one word.
 //    A word whose tag is not this call's (an earlier call's, the zeros of an
 //    initialized workspace, or the reserved tag of the two-kernel form) is
 //    not yet written. Each word is written with one 64-bit store and read
@@ -466,10 +467,11 @@ __global__ __launch_bounds__(256) void fr_split_softmax_init(uint32_t* __restric
         ws[i] = i == kHdrMagic ? (uint32_t)kWsMagic : (i == kHdrMagic + 1 ? (uint32_t)(kWsMagic >> 32) : 0u);
 }
 
-// End of a single-pass call, workgroup 0 (all its threads): once every
+// End of a single-pass call, in the last workgroup (all its threads), which
+// has the fewest list entries and so finishes early: once every
 // workgroup's flag holds this call's tag, every workgroup has read the
 // epoch, which is then advanced for the next call. Workgroups never wait for
-// workgroup 0, so one that has not started yet does so as others finish.
+// this one, so one that has not started yet does so as others finish.
 template <int T>
 __device__ void epoch_advance(uint32_t* hdr, const uint32_t* flags, uint32_t tag, uint32_t epoch) {
     const int tid = threadIdx.x;
@@ -494,6 +496,20 @@ __device__ void epoch_advance(uint32_t* hdr, const uint32_t* flags, uint32_t tag
 // rare paths) drain. A workgroup looks at its partners' slots once right
 // after publishing its own partial, before the next chunk's loads, and waits
 // only if some were not yet there.
+// This call's tag (0: no slot is trusted), taken by thread 0 from the
+// header words it loaded at the start and acknowledged in the workgroup's
+// flag (the stored value depends on the epoch read). The other threads read
+// it from LDS after the next barrier, so the header's latency is hidden
+// behind the first chunk's loads.
+__device__ __forceinline__ void take_tag(u32x2 magic_w, uint32_t epoch, uint32_t* flags, uint32_t* s_tag,
+                                         uint32_t* s_epoch) {
+    const uint64_t magic = (uint64_t)magic_w.y << 32 | magic_w.x;
+    const uint32_t t = (magic == kWsMagic && epoch < kMaxEpoch) ? epoch + 1 : 0u;
+    if (t != 0u) __hip_atomic_store(&flags[blockIdx.x], t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *s_tag = t;
+    *s_epoch = epoch;
+}
+
 struct OneEntry {
     int r, c, nc, base, start, n;
 };
@@ -539,7 +555,8 @@ __device__ __forceinline__ void one_pass_pipelined(const float* x, float* y, int
                                                    int rows, int total,
                                                    int32_t* argmax, uint32_t* hdr, uint64_t* slots, float* sl_m,
                                                    float* sl_d, int* sl_i, uint64_t* s_missing, float* s_mx,
-                                                   int* s_kstar, uint32_t tag, int64_t wait_ticks) {
+                                                   int* s_kstar, u32x2 magic_w, uint32_t epoch, uint32_t* flags,
+                                                   uint32_t* s_tag, uint32_t* s_epoch, int64_t wait_ticks) {
     constexpr int C = 4 * T * NV;
     const int tid = threadIdx.x;
     const int G = gridDim.x;
@@ -600,6 +617,7 @@ __device__ __forceinline__ void one_pass_pipelined(const float* x, float* y, int
         }
         SoftmaxPartial own = pipe_partial<T, NV>(cur, ec.n, lt, sl_m, sl_d, sl_i);
         if (own.idx != INT_MAX) own.idx += ec.start;
+        const uint32_t tag = uni((int)*s_tag);  // written before the partial's barriers
         const uint64_t own0 = slot_word(tag, own.m), own1 = slot_word(tag, own.d);
         // the row's slots, 16 bytes per chunk; a row of one chunk exchanges
         // nothing, and without a tag nothing is published (an empty range)
@@ -706,6 +724,7 @@ __device__ __forceinline__ void one_pass_pipelined(const float* x, float* y, int
     f32x4 va[NV], vb[NV];
     OneEntry ea = entry(blockIdx.x, 0);
     issue(va, ea, tid);
+    if (tid == 0) take_tag(magic_w, epoch, flags, s_tag, s_epoch);
     for (int t = blockIdx.x, k = 0; t < total; t += 2 * G, k += 2) {
         const OneEntry eb = entry(t + G, k + 1);
         step(ea, va, eb, vb);
@@ -722,10 +741,13 @@ __device__ __forceinline__ void one_pass_elementwise(const float* x, float* y, i
                                                      const int* s_base, const int* s_len, int rows, int total,
                                                      int32_t* argmax, uint32_t* hdr, uint64_t* slots, float* sl_m,
                                                      float* sl_d, int* sl_i, uint64_t* s_missing, float* s_mx,
-                                                     int* s_kstar, uint32_t tag, int64_t wait_ticks) {
+                                                     int* s_kstar, u32x2 magic_w, uint32_t epoch,
+                                                     uint32_t* flags, uint32_t* s_tag, uint32_t* s_epoch,
+                                                     int64_t wait_ticks) {
     constexpr bool VEC = false;
     constexpr int C = 4 * T * NV;
     const int tid = threadIdx.x;
+    if (tid == 0) take_tag(magic_w, epoch, flags, s_tag, s_epoch);
     for (int t = blockIdx.x; t < total; t += gridDim.x) {
         int lo = 0, hi = rows;  // s_base[lo] <= t < s_base[hi]; rows without chunks never qualify
         while (hi - lo > 1) {
@@ -751,6 +773,7 @@ __device__ __forceinline__ void one_pass_elementwise(const float* x, float* y, i
             load_chunk<tail_mask<VEC>(), T, NV, true>(xr, start, end, v);
             own = chunk_partial<tail_mask<VEC>(), T, NV>(v, start, end, sl_m, sl_d, sl_i);
         }
+        const uint32_t tag = __builtin_amdgcn_readfirstlane(*s_tag);  // written before the partial's barriers
         uint64_t* rs = slots + 2 * (int64_t)base;
         // a row of one chunk exchanges nothing; without a tag nothing is published
         if (tid == 0 && tag != 0u && nc > 1) {
@@ -876,7 +899,7 @@ __global__ __launch_bounds__(T) void fr_split_softmax_one(const float* x, float*
 #pragma unroll
     for (int i = 0; i < RPT; ++i) s_len[tid + i * T] = min(max(lv[i] + len0, 0), cols);
     __syncthreads();
-    // ...then thread tid counts the chunks of rows [r0, r1)
+    // thread tid counts the chunks of rows [r0, r1)
     const int per = (rows + T - 1) / T;
     const int r0 = min(rows, tid * per), r1 = min(rows, r0 + per);
     int local = 0;
@@ -913,30 +936,24 @@ __global__ __launch_bounds__(T) void fr_split_softmax_one(const float* x, float*
         run += cnt;
     }
     if (tid == T - 1) s_base[rows] = run;
-    if (tid == 0) {
-        // this call's tag (0: no slot is trusted), acknowledged in this
-        // workgroup's flag: the stored value depends on the epoch read
-        const uint64_t magic = (uint64_t)magic_w.y << 32 | magic_w.x;
-        const uint32_t t = (magic == kWsMagic && epoch < kMaxEpoch) ? epoch + 1 : 0u;
-        if (t != 0u) __hip_atomic_store(&flags[blockIdx.x], t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_tag = t;
-        s_epoch = epoch;
-    }
     __syncthreads();
     const int total = s_base[rows];
-    const uint32_t tag = __builtin_amdgcn_readfirstlane(s_tag);
     if (blockIdx.x == 0 && argmax)
         for (int r = tid; r < rows; r += T)
             if (s_len[r] == 0) argmax[r] = -1;
 
     if constexpr (VEC) {
         one_pass_pipelined<T, NV>(x, y, x_rs, y_rs, s_base, s_len, s_erow, rows, total, argmax, hdr, slots, sl_m,
-                                  sl_d, sl_i, &s_missing, s_mx, &s_kstar, tag, wait_ticks);
+                                  sl_d, sl_i, &s_missing, s_mx, &s_kstar, magic_w, epoch, flags, &s_tag, &s_epoch,
+                                  wait_ticks);
     } else {
         one_pass_elementwise<T, NV>(x, y, x_rs, y_rs, s_base, s_len, rows, total, argmax, hdr, slots, sl_m, sl_d,
-                                    sl_i, &s_missing, s_mx, &s_kstar, tag, wait_ticks);
+                                    sl_i, &s_missing, s_mx, &s_kstar, magic_w, epoch, flags, &s_tag, &s_epoch,
+                                    wait_ticks);
     }
-    if (blockIdx.x == 0 && tag != 0u) epoch_advance<T>(hdr, flags, tag, s_epoch);
+    __syncthreads();  // a workgroup without entries passed no barrier since thread 0 wrote the tag
+    const uint32_t tag = __builtin_amdgcn_readfirstlane(s_tag);
+    if (blockIdx.x == gridDim.x - 1 && tag != 0u) epoch_advance<T>(hdr, flags, tag, s_epoch);
 }
 
 // ------------------------------------------------------------------ backward
