@@ -639,9 +639,11 @@ __device__ __forceinline__ void one_pass_pipelined(const float* x, float* y, int
 
         const float* xr = x + (int64_t)ec.r * x_rs;
         const int L = uni(s_len[ec.r]);
-        MD st{-INFINITY, 0.f};
-        MI best{-INFINITY, INT_MAX};
-        for (int g0 = 0; g0 < ec.nc; g0 += kWave) {
+        // a row of one chunk: its partial is the row's (the merge below would
+        // return it unchanged, up to the d of a row whose y is all NaN)
+        MD st = ec.nc == 1 ? MD{own.m, own.d} : MD{-INFINITY, 0.f};
+        MI best = ec.nc == 1 ? MI{own.m, 0} : MI{-INFINITY, INT_MAX};
+        for (int g0 = 0; g0 < (ec.nc == 1 ? 0 : ec.nc); g0 += kWave) {
             const int k = g0 + (tid & (kWave - 1));
             uint64_t w0 = g0 == 0 ? ((uint64_t)pw0.y << 32 | pw0.x) : 0ull;
             uint64_t w1 = g0 == 0 ? ((uint64_t)pw1.y << 32 | pw1.x) : 0ull;
@@ -696,8 +698,14 @@ __device__ __forceinline__ void one_pass_pipelined(const float* x, float* y, int
                     a = MD{pm, slot_value(w1)};
                     b = MI{pm, k};  // the first chunk holding the row maximum
                 }
-                st = md_combine(st, group_reduce<kWave>(a, OpMD()));
-                best = mi_combine(best, group_reduce<kWave>(b, OpMI()));
+                // up to 16 chunks sit in one DPP row: 4 butterfly steps, not 6
+                if (ec.nc <= 16) {
+                    st = md_combine(st, group_reduce<16>(a, OpMD()));
+                    best = mi_combine(best, group_reduce<16>(b, OpMI()));
+                } else {
+                    st = md_combine(st, group_reduce<kWave>(a, OpMD()));
+                    best = mi_combine(best, group_reduce<kWave>(b, OpMI()));
+                }
             }
             __syncthreads();  // s_missing and the fold slots are rewritten next
         }

@@ -22,7 +22,7 @@ import pointwise_reduction_amd as fr  # noqa: E402
 FORMS = {"per": fr.FR_FORM_PER, "red": fr.FR_FORM_RED, "split": fr.FR_FORM_SPLIT}
 
 
-def run(x_np, lengths=None, form=fr.FR_FORM_AUTO, use_ws=None, cols=None, y_fill=np.nan, argmax=True):
+def run(x_np, lengths=None, form=fr.FR_FORM_AUTO, use_ws=None, cols=None, y_fill=np.nan, argmax=True, ws_bytes=None):
     """Run the GPU softmax on x_np[:, :cols]; returns (y, argmax)."""
     rows = x_np.shape[0]
     cols = x_np.shape[1] if cols is None else cols
@@ -36,15 +36,15 @@ def run(x_np, lengths=None, form=fr.FR_FORM_AUTO, use_ws=None, cols=None, y_fill
         use_ws = form == fr.FR_FORM_SPLIT
     ws = None
     if use_ws:
-        ws = new_ws(rows, cols)
+        ws = new_ws(rows, cols, nbytes=ws_bytes)
     with forced(form):
         fr.fr_softmax_rows(x, y, lengths=L, argmax=am, ws=ws)
     return host(yd)[:, :cols], (host(am) if argmax else None), host(yd)
 
 
-def new_ws(rows, cols, garbage=0x5A5A5A5A, init=True):
+def new_ws(rows, cols, garbage=0x5A5A5A5A, init=True, nbytes=None):
     """A split workspace holding garbage, then initialized (unless init=False)."""
-    nbytes = fr.fr_softmax_rows_workspace_bytes(rows, cols)
+    nbytes = fr.fr_softmax_rows_workspace_bytes(rows, cols) if nbytes is None else nbytes
     ws = torch.full((nbytes // 4,), garbage, dtype=torch.int32, device="cuda")
     return fr.fr_softmax_rows_workspace_init(ws) if init else ws
 
@@ -330,6 +330,34 @@ def test_softmax_split_passes(passes, cols):
     compare(x, y, am, lengths=L, what=f"split passes={passes} cols={cols}")
     for r, n in enumerate(L):
         assert np.isnan(yfull[r, n:]).all()
+
+
+@pytest.mark.parametrize("vec", [4, 8])
+def test_softmax_single_pass_many_rounds(vec):
+    """2048 ragged rows of up to 20000: the chunk list runs over many rounds of
+    the grid (entries w, w + G, ... per workgroup), more than the rounds
+    whose boundaries rows are moved off, so padded and straddling rows both
+    occur. The single pass matches the oracle and the two-kernel form's
+    argmax, and empty rows get -1."""
+    rows, cols = 2048, 20000
+    rng = np.random.default_rng(2950 + vec)
+    L = rng.integers(0, cols + 1, size=rows).astype(np.int32)
+    L[rng.random(rows) < 0.05] = 0
+    x = synth.normal((rows, cols), seed=2950 + vec) * 3
+    outs = {}
+    try:
+        for passes in (1, 2):
+            fr.fr_tune_override(fr.FR_OP_SOFTMAX, form=fr.FR_FORM_SPLIT, threads=256, vec=vec, passes=passes)
+            need = fr.fr_plan_query(fr.FR_OP_SOFTMAX, rows, cols, has_lengths=True, ws_bytes=1 << 40).ws_bytes
+            outs[passes] = run(x, lengths=L, use_ws=True, ws_bytes=need)
+    finally:
+        fr.fr_tune_override(fr.FR_OP_SOFTMAX)
+    y, am, yfull = outs[1]
+    compare(x, y, am, lengths=L, what=f"single pass, vec {vec}")
+    assert np.array_equal(am, outs[2][1])
+    assert np.all(am[L == 0] == -1)
+    for r in np.nonzero(L < cols)[0][:64]:
+        assert np.isnan(yfull[r, L[r]:]).all()
 
 
 @pytest.mark.parametrize("shape", [(64, 131072), (3, 600001), (7, 20001)], ids=["64x131072", "3x600001", "7x20001"])
