@@ -24,11 +24,15 @@ graph and replayed, so host launch overhead does not enter the device time
 (--eager launches them one by one instead). The graph starts with an
 untimed lead-in of one step per buffer set, so every set is touched once
 between two uses whatever K is; then a device clock mark, the K timed steps
-and a second mark. The marks' difference is the reported time: the device
-time of exactly the K steps. Events around a replay of the K steps alone
-(behind a lead-in replay) are reported beside it as events_ms_per_step;
-they also hold a fixed cost of the graph's edges. The graph's output is
-checked against an eager launch before the timing is reported.
+and a second mark. The marks enclose the K steps and one kernel boundary
+more (the one after the first mark); a graph of the two marks alone behind
+the same lead-in measures it (mark_interval_us), and the reported time is
+the marks' difference less that interval: the device time of exactly the K
+steps, each with its boundary to the next kernel. The marks' raw difference
+is reported as marks_raw_ms_per_step, and events around a replay of the K
+steps alone (behind a lead-in replay) as events_ms_per_step; the events
+also hold a fixed cost of the graph's edges. The graph's output is checked
+against an eager launch before the timing is reported.
 
 The measurement runs in --procs N (default 3) separate processes, one after
 the other; each times the K steps --reps R (default 3) times and reports the
@@ -927,7 +931,7 @@ def main():
     # (the lead-in runs first in that graph). Events around a replay of a
     # graph of the K steps alone, behind a lead-in replay, are reported
     # beside it: they add a fixed cost at the graph's edges.
-    graph = lead = marked = None
+    graph = lead = marked = mark_ms = None
     marks = torch.zeros(2, dtype=torch.int64, device=dev_name)
     if not (args.eager or host_timed):
         graph = timing.capture(lambda k: wl.launch(k % sets), K)
@@ -935,14 +939,19 @@ def main():
         marked = timing.capture_marked(lambda k: wl.launch(k % sets), sets, K,
                                        lambda i: fr.fr_device_clock(marks, i))
         clock_khz = fr.fr_device_clock_khz()
+        # the marks enclose one kernel boundary more than the K steps hold
+        mark_ms = timing.mark_interval(lambda k: wl.launch(k % sets), sets, marks,
+                                       lambda i: fr.fr_device_clock(marks, i), clock_khz)
     # poison every output so the check below sees what the timed steps wrote
     for k in range(sets):
         wl.output(k).view(torch.uint8).fill_(0xFF)
     torch.cuda.synchronize()
-    reps, ev_reps = [], []
+    reps, ev_reps, raw_reps = [], [], []
     for _ in range(max(1, args.reps)):
         if graph is not None:
-            reps.append(timing.time_marked(marked, marks, K, clock_khz) * K)
+            raw = timing.time_marked(marked, marks, K, clock_khz) * K
+            raw_reps.append(raw)
+            reps.append(raw - mark_ms)
             ev_reps.append(timing.time_after_lead(lead, graph, K) * K)
         else:
             for k in range(sets if not host_timed else 0):
@@ -963,7 +972,8 @@ def main():
     timing_label = ("eager, events around the K launches" if args.eager else
                     ("host loop, one region replay per step" if host_timed else
                      "device clock marks around the K launches inside one hip graph, after a lead-in of one "
-                     "step per buffer set"))
+                     "step per buffer set, less the interval of the two marks alone (their own kernel "
+                     "boundary)"))
     cfg.update({"buffer_sets": sets, "rotated_bytes": sets * per_set, "timing": timing_label,
                 "cache": "warm (one set)" if (args.warm or host_timed) else
                 f"{sets} rotating sets, {sets * per_set / 2**30:.2f} GiB touched between two uses of a set "
@@ -978,6 +988,8 @@ def main():
         "ms_per_step": round(ms_per_step, 6),
         "reps_ms_per_step": [round(r / K, 6) for r in reps],
         "events_ms_per_step": round(float(np.median(ev_reps)) / K, 6) if ev_reps else None,
+        "marks_raw_ms_per_step": round(float(np.median(raw_reps)) / K, 6) if raw_reps else None,
+        "mark_interval_us": round(mark_ms * 1000, 3) if mark_ms is not None else None,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -12,9 +12,13 @@ the host submits the timed one. Events around a graph replay still carry a
 fixed cost of their own at the graph's edges (about 9 us per replay on
 MI355X, measured over K = 1 ... 1000 steps), which is spread over the K steps.
 `capture_marked` / `time_marked` avoid it: one graph holds the lead-in, a
-device clock mark, the K steps and a second mark, and the marks' difference
-is the device time of exactly those K steps (each mark waits, in stream
-order, for the work before it).
+device clock mark, the K steps and a second mark (each mark waits, in stream
+order, for the work before it). Between the marks lie the K steps and one
+kernel boundary more than they contain: the one after the first mark. A
+graph of the two marks alone, behind the same lead-in, measures that
+boundary (`mark_interval`); subtracted, the difference is the device time
+of exactly the K steps, each with the boundary to the next kernel, as in a
+long run.
 """
 import torch
 
@@ -81,14 +85,24 @@ def capture_marked(launch, lead, steps, mark):
     return graph
 
 
-def time_marked(graph, marks, steps, clock_khz):
+def time_marked(graph, marks, steps, clock_khz, base_ms=0.0):
     """Milliseconds per step between the two clock marks of one replay of a
-    capture_marked graph (marks: the int64 device tensor the marks write)."""
+    capture_marked graph (marks: the int64 device tensor the marks write),
+    less base_ms, the interval of the marks alone (`mark_interval`)."""
     torch.cuda.synchronize()
     graph.replay()
     torch.cuda.synchronize()
     t = marks.cpu()
-    return float(t[1] - t[0]) / clock_khz / steps
+    return (float(t[1] - t[0]) / clock_khz - base_ms) / steps
+
+
+def mark_interval(launch, lead, marks, mark, clock_khz, reps=5):
+    """Median milliseconds between two clock marks with no step between them,
+    behind the same lead-in: the first mark's end and one kernel boundary."""
+    graph = capture_marked(launch, lead, 0, mark)
+    out = sorted(time_marked(graph, marks, 1, clock_khz) for _ in range(reps))
+    del graph
+    return out[len(out) // 2]
 
 
 def time_eager(launch, steps):
