@@ -22,8 +22,10 @@ the 256 MB MALL cannot serve a step's reads from the previous use of the same
 buffers (--warm uses one set). The K launches are captured once into a HIP
 graph and replayed, so host launch overhead does not enter the device time
 (--eager launches them one by one instead). The graph starts with an
-untimed lead-in of one step per buffer set, so every set is touched once
-between two uses whatever K is; then a device clock mark, the K timed steps
+untimed lead-in of whole rotations over the buffer sets (at least 256
+steps), so every set is touched once between two uses whatever K is and the
+device has been busy for a while when the first timed step starts; then a
+device clock mark, the K timed steps
 and a second mark. The marks enclose the K steps and one kernel boundary
 more (the one after the first mark); a graph of the two marks alone behind
 the same lead-in measures it (mark_interval_us), and the reported time is
@@ -60,6 +62,7 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
 PEAK_MFMA_BF16_TFS = 2500.0  # MI355X dense bf16 matrix-core peak
 METRIC = "effective HBM GB/s and % of MI355X peak for fused reductions (softmax 4096x1024)"
 ROTATE_BYTES = 1 << 30
+LEAD_STEPS = 256  # at least this many lead-in steps, a whole number of rotations
 
 
 # ------------------------------------------------------------------ logical bytes
@@ -921,26 +924,30 @@ def main():
 
     from pointwise_reduction_amd import timing
 
-    # Step k of the timed region uses set k % sets. A lead-in of one step per
-    # set, in the same order, runs right before it: every set is then touched
-    # once between two uses (>= 1 GiB of other buffers, so no timed read is
-    # served from the 256 MB MALL, for any K), and the device is busy while
-    # the timed graph is submitted.
+    # Step k of the timed region uses set k % sets. A lead-in of whole
+    # rotations over the sets, in the same order, runs right before it: every
+    # set is then touched once between two uses (>= 1 GiB of other buffers,
+    # so no timed read is served from the 256 MB MALL, for any K), and the
+    # device is busy while the timed graph is submitted.
     # The reported time comes from two device clock marks captured in the
     # same graph right before the first and right after the last timed step
     # (the lead-in runs first in that graph). Events around a replay of a
     # graph of the K steps alone, behind a lead-in replay, are reported
     # beside it: they add a fixed cost at the graph's edges.
     graph = lead = marked = mark_ms = None
+    # the lead-in runs whole rotations of the buffer sets, at least LEAD_STEPS
+    # steps: the device has been busy for a while (its clocks up) when the
+    # first timed step starts, whatever K is
+    n_lead = sets * max(1, math.ceil(LEAD_STEPS / sets))
     marks = torch.zeros(2, dtype=torch.int64, device=dev_name)
     if not (args.eager or host_timed):
         graph = timing.capture(lambda k: wl.launch(k % sets), K)
-        lead = timing.capture(lambda k: wl.launch(k % sets), sets)
-        marked = timing.capture_marked(lambda k: wl.launch(k % sets), sets, K,
+        lead = timing.capture(lambda k: wl.launch(k % sets), n_lead)
+        marked = timing.capture_marked(lambda k: wl.launch(k % sets), n_lead, K,
                                        lambda i: fr.fr_device_clock(marks, i))
         clock_khz = fr.fr_device_clock_khz()
         # the marks enclose one kernel boundary more than the K steps hold
-        mark_ms = timing.mark_interval(lambda k: wl.launch(k % sets), sets, marks,
+        mark_ms = timing.mark_interval(lambda k: wl.launch(k % sets), n_lead, marks,
                                        lambda i: fr.fr_device_clock(marks, i), clock_khz)
     # poison every output so the check below sees what the timed steps wrote
     for k in range(sets):
@@ -971,8 +978,8 @@ def main():
     cfg = wl.config()
     timing_label = ("eager, events around the K launches" if args.eager else
                     ("host loop, one region replay per step" if host_timed else
-                     "device clock marks around the K launches inside one hip graph, after a lead-in of one "
-                     "step per buffer set, less the interval of the two marks alone (their own kernel "
+                     "device clock marks around the K launches inside one hip graph, after a lead-in of whole "
+                     "rotations over the buffer sets (>= 256 steps), less the interval of the two marks alone (their own kernel "
                      "boundary)"))
     cfg.update({"buffer_sets": sets, "rotated_bytes": sets * per_set, "timing": timing_label,
                 "cache": "warm (one set)" if (args.warm or host_timed) else
