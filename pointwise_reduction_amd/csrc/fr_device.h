@@ -342,12 +342,48 @@ constexpr int kAuxNT = 2;    // buffer instruction cache policy: non-temporal
 constexpr int kAuxSc1 = 16;  // buffer instruction cache policy: sc1 (coherent across the compute dies)
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// A 16-byte buffer store at byte offset `off` of the resource, with the
+// scalar offset held at the constant 0. A store of more than 8 bytes reads
+// its data registers over several cycles after it issues; a VALU write to
+// those registers right behind it must wait one cycle. The compiler inserts
+// that wait only when the scalar offset is not a register. With an SGPR
+// scalar offset it let the next instruction overwrite the first data
+// register, and on MI355X the upper lanes (from lane 12 on) then stored the
+// new value. Every wide buffer store goes through here.
+template <int AUX>
+__device__ __forceinline__ void store16(u32x4 v, __amdgpu_buffer_rsrc_t r, int off) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, AUX);
+}
+
 // ------------------------------------------------------------------ bf16
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
+// Sum of the 8 * NV bf16 values in v: each packed pair enters one of four
+// fp32 accumulators through v_dot2_f32_bf16 against (1, 1), the four are
+// added pairwise at the end. One instruction per pair instead of two unpacks
+// and two adds. Products with 1 are exact, so a sum of equal values that fits
+// the fp32 significand is exact.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// The packed pair of one word, taken by value: clang compiles a bit_cast of a
+// vector element lvalue (v.y) to a load of the vector's first element.
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t w) { return __builtin_bit_cast(bf16x2, w); }
+
+template <int NV>
+__device__ __forceinline__ float sum_bf16(const u32x4* v) {
+    const bf16x2 one = as_bf16x2(0x3F803F80u);
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+        acc[0] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v[k].x), one, acc[0], false);
+        acc[1] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v[k].y), one, acc[1], false);
+        acc[2] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v[k].z), one, acc[2], false);
+        acc[3] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(v[k].w), one, acc[3], false);
+    }
+    return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+}
+
 // Two fp32 -> packed bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     bf16x2 p = {(__bf16)lo, (__bf16)hi};
     return __builtin_bit_cast(uint32_t, p);
 }

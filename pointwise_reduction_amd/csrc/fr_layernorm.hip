@@ -8,6 +8,10 @@
 //                                      NV vectors per lane): exact two-pass
 //                                      mean and variance over registers, one
 //                                      read and one write of the row
+//               fr_pipe_layernorm_bf16 the same per row, one workgroup per CU
+//                                      taking several rows with three in
+//                                      flight (loads overlap the folds and
+//                                      stores of earlier rows)
 //   looped      fr_red_layernorm_bf16  one workgroup streams the row: per-lane
 //                                      Welford statistics, merged per 8-value
 //                                      vector and across lanes and waves with
@@ -84,7 +88,7 @@ __device__ __forceinline__ u32x4 normalize8(u32x4 xv, int j0, int L, const uint1
 //
 // Rows that fill the capacity exactly (kNone) use buffer instructions: the
 // row base lives in a scalar buffer resource and each lane keeps one offset
-// register (the vector index goes into the scalar offset), where 64-bit
+// register (a load's vector index goes into its scalar offset), where 64-bit
 // addresses would take two registers per vector and per operand (x, gamma,
 // beta, y). Every access is inside the row, so the resource's range check
 // never applies (a missing gamma or beta gets an empty range and reads
@@ -106,14 +110,19 @@ __device__ __forceinline__ void affine_row(const u32x4* v, __amdgpu_buffer_rsrc_
 #pragma unroll
         for (int k = 0; k < H; ++k) {
             const int off = (h * H + k) * T * 16;
-            if constexpr (UNIT_GAMMA) gv[k] = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // 1.0
-            else gv[k] = __builtin_amdgcn_raw_buffer_load_b128(rg, voff, off, 0);
+            if constexpr (UNIT_GAMMA) {
+                // 1.0, hidden from the compiler so that it multiplies as with
+                // a loaded gamma (the pipelined kernel gives the same bits)
+                gv[k] = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+                hide(gv[k]);
+            } else {
+                gv[k] = __builtin_amdgcn_raw_buffer_load_b128(rg, voff, off, 0);
+            }
             bv[k] = __builtin_amdgcn_raw_buffer_load_b128(rb, voff, off, 0);
         }
 #pragma unroll
         for (int k = 0; k < H; ++k)
-            __builtin_amdgcn_raw_buffer_store_b128(affine8(v[h * H + k], gv[k], bv[k], mu, rstd), ry, voff,
-                                                   (h * H + k) * T * 16, kAuxNT);
+            store16<kAuxNT>(affine8(v[h * H + k], gv[k], bv[k], mu, rstd), ry, voff + (h * H + k) * T * 16);
         asm volatile("" ::: "memory");  // the next half's loads stay after these stores
     }
 }
@@ -154,11 +163,7 @@ __global__ __launch_bounds__(T, OCC) void fr_per_layernorm_bf16(const uint16_t* 
             for (int k = 0; k < NV; ++k) v[k] = load8m<M, true>(xr, (k * T + tid) * 8, cols);
         }
         // pass 1 over registers: the sum (masked elements read as +0)
-        float s = 0.f;
-#pragma unroll
-        for (int k = 0; k < NV; ++k)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) s += bf16_lo(word(v[k], i)) + bf16_hi(word(v[k], i));
+        float s = sum_bf16<NV>(v);
         if constexpr (BUF) {
 #pragma unroll
             for (int k = 0; k < NV; ++k) hide(v[k]);
@@ -198,6 +203,116 @@ __global__ __launch_bounds__(T, OCC) void fr_per_layernorm_bf16(const uint16_t* 
             }
         }
         __syncthreads();  // slots are rewritten by the next row
+    }
+}
+
+// ------------------------------------------------------------------ persistent, pipelined rows
+// One workgroup per CU takes NR rows (r = blockIdx.x + i * gridDim.x) and
+// keeps R of them in flight in registers: while one row's statistics, affine
+// epilogue and stores run, the next R - 1 rows are loading, and a row's
+// registers are reloaded with row i + R as soon as its stores are issued.
+// When every workgroup holds its rows whole for the full read-fold-write
+// chain (the kernel above), the whole device reads, then folds, then writes
+// in step; here the HBM queue always holds some workgroup's next rows.
+//
+// gamma and beta are read once per workgroup into LDS (2 x 64 KiB at 32768
+// columns, so one workgroup per CU), through the registers of the last two
+// row sets: their loads are issued first, the first R - 2 rows' loads behind
+// them, so waiting for gamma / beta waits for nothing else (vector loads
+// complete in issue order); then the last two rows' loads go out. The row
+// loop is unrolled over all NR rows, so that every wait counts exactly the
+// loads still needed (a loop back edge would make the compiler wait for all).
+// Rows past `rows` (the last workgroups when rows % gridDim.x != 0) load and
+// store through empty buffer ranges: no memory is touched. Each row's
+// arithmetic is the kernel above's with the same lane order (T threads, NV
+// vectors per lane), so both give the same bits. Requires cols == 8 * T * NV
+// and 16-byte aligned rows, gamma and beta.
+template <int T, int NV, int R, int NR, bool STATS>
+__global__ __launch_bounds__(T, 1) void fr_pipe_layernorm_bf16(const uint16_t* x, const uint16_t* __restrict__ gamma,
+                                                              const uint16_t* __restrict__ beta, uint16_t* y, int rows,
+                                                              int cols, int64_t x_rs, int64_t y_rs, float eps,
+                                                              float* __restrict__ mean_out,
+                                                              float* __restrict__ rstd_out) {
+    static_assert(R >= 3 && R <= NR, "gamma and beta are staged through two row sets; one more row loads ahead");
+    __shared__ u32x4 sg[NV * T];
+    __shared__ u32x4 sb[NV * T];
+    __shared__ float sl_s[T / kWave];
+    __shared__ float sl_q[T / kWave];
+    const int tid = threadIdx.x;
+    const uint32_t bytes = (uint32_t)cols * 2u;
+    const int voff = tid * 16;
+    const float n = (float)cols;
+    const int G = gridDim.x;
+    auto load_row = [&](u32x4* v, int r) {
+        const bool ok = r < rows;
+        const __amdgpu_buffer_rsrc_t rx = row_rsrc(ok ? x + (int64_t)r * x_rs : x, ok ? bytes : 0u);
+#pragma unroll
+        for (int k = 0; k < NV; ++k) v[k] = __builtin_amdgcn_raw_buffer_load_b128(rx, voff, k * T * 16, kAuxNT);
+    };
+    u32x4 v[R][NV];
+    {
+        // a missing gamma reads as 1, a missing beta as 0 (empty range)
+        const __amdgpu_buffer_rsrc_t rg = row_rsrc(gamma, gamma ? bytes : 0u);
+        const __amdgpu_buffer_rsrc_t rb = row_rsrc(beta, beta ? bytes : 0u);
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            v[R - 2][k] = __builtin_amdgcn_raw_buffer_load_b128(rg, voff, k * T * 16, 0);
+            v[R - 1][k] = __builtin_amdgcn_raw_buffer_load_b128(rb, voff, k * T * 16, 0);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < R - 2; ++i) load_row(v[i], blockIdx.x + i * G);
+    const u32x4 one = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+        sg[k * T + tid] = gamma ? v[R - 2][k] : one;
+        sb[k * T + tid] = v[R - 1][k];
+    }
+#pragma unroll
+    for (int i = R - 2; i < R; ++i) load_row(v[i], blockIdx.x + i * G);
+    // (the first fold's barrier orders these LDS writes before any read)
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+        const int c = i % R;
+        const int r = blockIdx.x + i * G;
+        float s = sum_bf16<NV>(v[c]);
+#pragma unroll
+        for (int k = 0; k < NV; ++k) hide(v[c][k]);
+        s = group_reduce<kWave>(s, OpSum());
+        s = block_fold(s, sl_s, T / kWave, OpSum());
+        const float mu = s / n;
+        float q = 0.f;
+#pragma unroll
+        for (int k = 0; k < NV; ++k)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float dl = bf16_lo(word(v[c][k], j)) - mu, dh = bf16_hi(word(v[c][k], j)) - mu;
+                q += dl * dl + dh * dh;
+            }
+#pragma unroll
+        for (int k = 0; k < NV; ++k) hide(v[c][k]);
+        q = group_reduce<kWave>(q, OpSum());
+        q = block_fold(q, sl_q, T / kWave, OpSum());
+        const float rstd = 1.0f / sqrtf(q / n + eps);
+        const bool ok = r < rows;
+        if constexpr (STATS) {
+            // the row statistics (each nullable): thread 0 inside a 4-byte
+            // range, no branch (the instances without them run 1% faster)
+            __builtin_amdgcn_raw_buffer_store_b32(
+                __builtin_bit_cast(uint32_t, mu), row_rsrc(mean_out ? mean_out + (ok ? r : 0) : mean_out,
+                                                           mean_out && ok ? 4u : 0u), tid == 0 ? 0 : 4, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(
+                __builtin_bit_cast(uint32_t, rstd), row_rsrc(rstd_out ? rstd_out + (ok ? r : 0) : rstd_out,
+                                                             rstd_out && ok ? 4u : 0u), tid == 0 ? 0 : 4, 0, 0);
+        }
+        const __amdgpu_buffer_rsrc_t ry = row_rsrc(ok ? y + (int64_t)r * y_rs : y, ok ? bytes : 0u);
+#pragma unroll
+        for (int k = 0; k < NV; ++k)
+            store16<kAuxNT>(affine8(v[c][k], sg[k * T + tid], sb[k * T + tid], mu, rstd), ry, voff + k * T * 16);
+        // the two folds' slots are safe to rewrite: every thread has read
+        // this row's sum slots before the variance barrier, and the variance
+        // slots before the next row's sum barrier
+        if (i + R < NR) load_row(v[c], r + R * G);
     }
 }
 
@@ -426,8 +541,7 @@ __global__ __launch_bounds__(T) void fr_per_layernorm_bwd_bf16(const uint16_t* x
                 lb[(k * T + tid) * 2 + 1] = b1;
             }
             if constexpr (BUF)
-                __builtin_amdgcn_raw_buffer_store_b128(u32x4{o[0], o[1], o[2], o[3]},
-                                                       row_rsrc(outr, (uint32_t)cols * 2u), bvo(k), bso(k), kAuxNT);
+                store16<kAuxNT>(u32x4{o[0], o[1], o[2], o[3]}, row_rsrc(outr, (uint32_t)cols * 2u), bvo(k) + bso(k));
             else if (j0 < cols)
                 store8m<M, true>(outr, j0, cols, u32x4{o[0], o[1], o[2], o[3]});
         }
@@ -733,9 +847,8 @@ __global__ __launch_bounds__(kLnTeamT) void fr_team_layernorm_bwd_bf16(
                 }
                 o[k] = pack_bf16(vv[0], vv[1]);
             }
-            __builtin_amdgcn_raw_buffer_store_b128(u32x4{o[0], o[1], o[2], o[3]},
-                                                   row_rsrc(dx + (int64_t)r * dx_rs + c0, live ? pbytes : 0u), voff,
-                                                   0, kAuxNT);
+            store16<kAuxNT>(u32x4{o[0], o[1], o[2], o[3]}, row_rsrc(dx + (int64_t)r * dx_rs + c0, live ? pbytes : 0u),
+                            voff);
         }
         poll_ahead(st + 1);
     };
@@ -852,6 +965,30 @@ LnFn pick_per(int mask, int threads, int nv, int occ, bool unit_gamma) {
     }
 }
 
+// Pipelined rows: 512 threads x 8 vectors (32768 columns), 3 rows in flight.
+// Measured at 2048 x 32768 on MI355X: 3 rows in flight 44.9 us, 2 rows
+// 46.9 us, 4 rows 47.2 us; 1024 threads x 4 vectors with 3 or 4 rows 46.8 /
+// 47.2 us; 256 threads x 16 vectors with 2 rows 49.8 us (the kernel above:
+// 48.8 us on the same box).
+constexpr int kLnPipeR = 3;
+template <bool STATS>
+LnFn pick_pipe_s(int nr) {
+    constexpr int R = kLnPipeR;
+    switch (nr) {
+        case 3: return fr_pipe_layernorm_bf16<512, 8, R, 3, STATS>;
+        case 4: return fr_pipe_layernorm_bf16<512, 8, R, 4, STATS>;
+        case 5: return fr_pipe_layernorm_bf16<512, 8, R, 5, STATS>;
+        case 6: return fr_pipe_layernorm_bf16<512, 8, R, 6, STATS>;
+        case 7: return fr_pipe_layernorm_bf16<512, 8, R, 7, STATS>;
+        case 8: return fr_pipe_layernorm_bf16<512, 8, R, 8, STATS>;
+    }
+    return nullptr;
+}
+LnFn pick_pipe(int threads, int nv, int nr, bool stats) {
+    if (threads != 512 || nv != 8) return nullptr;
+    return stats ? pick_pipe_s<true>(nr) : pick_pipe_s<false>(nr);
+}
+
 template <bool VEC>
 LnFn pick_red(int threads, int u) {
     if (threads == 256 && u == 4) return fr_red_layernorm_bf16<256, 4, VEC>;
@@ -966,7 +1103,11 @@ hipError_t launch_layernorm_bwd(const fr_plan& p, const LayerNormBwdArgs& a, hip
 hipError_t launch_layernorm(const fr_plan& p, const LayerNormArgs& a, hipStream_t s) {
     const bool vec = p.vec16 != 0;
     LnFn f = nullptr;
-    if (p.form == FR_FORM_PER) {
+    if (p.form == FR_FORM_PER && p.rows_per_wg > 1) {
+        // pipelined rows: 16-byte accesses over rows that fill the capacity
+        if (vec && a.cols == 8 * p.threads * p.vec)
+            f = pick_pipe(p.threads, p.vec, p.rows_per_wg, a.mean != nullptr || a.rstd != nullptr);
+    } else if (p.form == FR_FORM_PER) {
         const int mask = !vec ? kScalar : (a.cols == 8 * p.threads * p.vec ? kNone : kVec);
         f = pick_per(mask, p.threads, p.vec, p.occupancy, a.gamma == nullptr);
     }

@@ -725,8 +725,7 @@ __device__ __forceinline__ void one_pass_pipelined(const float* x, float* y, int
         const __amdgpu_buffer_rsrc_t ry = row_rsrc(y + (int64_t)ec.r * y_rs + ec.start, (uint32_t)ec.n * 4u);
 #pragma unroll
         for (int k = 0; k < NV; ++k)
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, exp4(cur[k], mx) * inv), ry, lt * 16,
-                                                   k * T * 16, kAuxNT);
+            store16<kAuxNT>(__builtin_bit_cast(u32x4, exp4(cur[k], mx) * inv), ry, lt * 16 + k * T * 16);
     };
 
     f32x4 va[NV], vb[NV];

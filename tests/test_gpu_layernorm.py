@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import bf16_bits_of, bf16_bits_tensor, check_bf16, forced
+from gpu_util import bf16_bits_of, bf16_bits_tensor, check_bf16, forced, host
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -102,3 +102,46 @@ def test_layernorm_row_stride():
     got = bf16_bits_of(y)
     assert np.all(got[:, 1000:] == 0)
     compare(x, g, b, np.ascontiguousarray(got[:, :1000]), what="row stride 1024")
+
+
+@pytest.mark.parametrize("nr", [3, 5, 8])
+def test_layernorm_pipelined_rows(nr):
+    """The pipelined form (a workgroup takes nr rows, 3 in flight, gamma and
+    beta staged in LDS) through a tuner override, on 300 rows: at nr = 8 the
+    last workgroup has 4 rows past the end, which touch no memory. Every row
+    against the oracle, with and without gamma / beta, in place, and the same
+    bits (outputs and row statistics) as one row per workgroup, which is the
+    automatic plan below 3 rows per CU."""
+    rows, cols = 300, 32768
+    x, g, b = synth.layernorm_inputs(rows, cols, seed=3500 + nr)
+    xd, gd, bd = bf16_bits_tensor(x), bf16_bits_tensor(g), bf16_bits_tensor(b)
+    assert fr.fr_plan_query(fr.FR_OP_LAYERNORM, rows, cols, dtype=fr.FR_BF16).rows_per_wg == 1
+
+    def run(gamma, beta, pipelined, in_place=False):
+        y = xd.clone() if in_place else torch.full_like(xd, float("nan"))
+        mean = torch.full((rows,), float("nan"), device="cuda")
+        rstd = torch.full((rows,), float("nan"), device="cuda")
+        if pipelined:
+            fr.fr_tune_override(fr.FR_OP_LAYERNORM, form=fr.FR_FORM_PER, threads=512, vec=8, rows_per_wg=nr)
+        try:
+            assert fr.fr_plan_query(fr.FR_OP_LAYERNORM, rows, cols, dtype=fr.FR_BF16).rows_per_wg == \
+                (nr if pipelined else 1)
+            fr.fr_layernorm_rows_stats(y if in_place else xd, y, mean=mean, rstd=rstd, gamma=gamma, beta=beta)
+        finally:
+            fr.fr_tune_override(fr.FR_OP_LAYERNORM)
+        return bf16_bits_of(y), host(mean), host(rstd)
+
+    for gamma, beta, what in ((gd, bd, "affine"), (None, None, "no affine"), (gd, None, "gamma only"),
+                              (None, bd, "beta only")):
+        got, mean, rstd = run(gamma, beta, True)
+        gh = None if gamma is None else g
+        bh = None if beta is None else b
+        compare(x, gh, bh, got, what=f"pipelined nr={nr} {what}")
+        ref, ref_mean, ref_rstd = run(gamma, beta, False)
+        assert np.array_equal(got, ref), f"pipelined nr={nr} {what}: bits differ from one row per workgroup"
+        assert np.array_equal(mean.view(np.uint32), ref_mean.view(np.uint32))
+        assert np.array_equal(rstd.view(np.uint32), ref_rstd.view(np.uint32))
+    m64, r64 = oracle.layernorm_stats(x)
+    assert np.allclose(mean, m64, rtol=1e-5, atol=1e-6) and np.allclose(rstd, r64, rtol=1e-5)
+    got, _, _ = run(gd, bd, True, in_place=True)
+    compare(x, g, b, got, what=f"pipelined nr={nr} in place")

@@ -199,9 +199,34 @@ def test_plans_for_the_five_workloads():
     # softmax 4096 x 1024: a wave per 2 rows, 4 x 16-byte vectors per lane and row
     p = fr.fr_plan_query(fr.FR_OP_SOFTMAX, 4096, 1024)
     assert (p.form, p.seg, p.vec, p.rows_per_wg, p.grid) == (fr.FR_FORM_PER, 64, 4, 8, 512)
-    # LayerNorm 2048 x 32768 bf16: a 512-thread workgroup holds each row
+    # LayerNorm 2048 x 32768 bf16: a 512-thread workgroup holds a row; one
+    # workgroup per CU takes 8 rows with 3 in flight
     p = fr.fr_plan_query(fr.FR_OP_LAYERNORM, 2048, 32768, dtype=fr.FR_BF16)
-    assert (p.form, p.threads, p.vec, p.grid) == (fr.FR_FORM_PER, 512, 8, 2048)
+    assert (p.form, p.threads, p.vec, p.rows_per_wg, p.grid) == (fr.FR_FORM_PER, 512, 8, 8, 256)
+    # a workgroup per row below 3 rows per CU, for other row lengths, and for
+    # rows without 16-byte alignment
+    p = fr.fr_plan_query(fr.FR_OP_LAYERNORM, 767, 32768, dtype=fr.FR_BF16)
+    assert (p.rows_per_wg, p.grid) == (1, 767)
+    p = fr.fr_plan_query(fr.FR_OP_LAYERNORM, 768, 32768, dtype=fr.FR_BF16)
+    assert (p.rows_per_wg, p.grid) == (3, 256)
+    p = fr.fr_plan_query(fr.FR_OP_LAYERNORM, 1000, 32768, dtype=fr.FR_BF16, num_cus=304)
+    assert (p.rows_per_wg, p.grid) == (4, 250)
+    p = fr.fr_plan_query(fr.FR_OP_LAYERNORM, 65536, 32768, dtype=fr.FR_BF16)
+    assert (p.rows_per_wg, p.grid) == (8, 8192)
+    assert fr.fr_plan_query(fr.FR_OP_LAYERNORM, 2048, 16384, dtype=fr.FR_BF16).rows_per_wg == 1
+    assert fr.fr_plan_query(fr.FR_OP_LAYERNORM, 2048, 32768, dtype=fr.FR_BF16, aligned16=False).rows_per_wg == 1
+    # a tuner's override picks either form
+    fr.fr_tune_override(fr.FR_OP_LAYERNORM, form=fr.FR_FORM_PER, threads=512, vec=8, rows_per_wg=5)
+    try:
+        p = fr.fr_plan_query(fr.FR_OP_LAYERNORM, 2048, 32768, dtype=fr.FR_BF16)
+        assert (p.rows_per_wg, p.grid) == (5, 410)
+        fr.fr_tune_override(fr.FR_OP_LAYERNORM, form=fr.FR_FORM_PER, threads=512, vec=8)
+        assert fr.fr_plan_query(fr.FR_OP_LAYERNORM, 2048, 32768, dtype=fr.FR_BF16).grid == 2048
+        fr.fr_tune_override(fr.FR_OP_LAYERNORM, form=fr.FR_FORM_PER, threads=1024, vec=4, rows_per_wg=8)
+        with pytest.raises(fr.FrError):
+            fr.fr_plan_query(fr.FR_OP_LAYERNORM, 2048, 32768, dtype=fr.FR_BF16)
+    finally:
+        fr.fr_tune_override(fr.FR_OP_LAYERNORM)
     # sum of squares over 2^28: 512 chunks of 2^19 plus a finishing pass
     n = 1 << 28
     ws = fr.fr_sumsq_full_workspace_bytes(n)
