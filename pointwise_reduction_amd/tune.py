@@ -144,7 +144,9 @@ def workload(name):
         rows, cols = 2048, 32768
         x, g, b = synth.layernorm_inputs(rows, cols, seed=3001)
         cands = [dict(form=P, threads=512, vec=8), dict(form=P, threads=1024, vec=4),
-                 dict(form=P, threads=512, vec=8, rows_per_wg=8), dict(form=P, threads=512, vec=8, rows_per_wg=4),
+                 dict(form=P, threads=512, vec=8, rows_per_wg=8), dict(form=P, threads=512, vec=8, rows_per_wg=6),
+                 dict(form=P, threads=512, vec=8, rows_per_wg=5), dict(form=P, threads=512, vec=8, rows_per_wg=4),
+                 dict(form=P, threads=512, vec=8, rows_per_wg=3),
                  dict(form=R, threads=256, vec=4), dict(form=R, threads=512, vec=2), dict(form=R, threads=1024, vec=2)]
 
         def alloc(sets):
