@@ -260,6 +260,10 @@ def make_workload(name, torch, fr, synth):
                 x0 = bf(x_h)
                 self.g, self.b = bf(g_h), bf(b_h)
                 self.args = [(x0 if i == 0 else x0.clone(), torch.empty_like(x0)) for i in range(sets)]
+                cus = torch.cuda.get_device_properties(dev).multi_processor_count
+                self.plan = fr.fr_plan_query(fr.FR_OP_LAYERNORM, rows, cols, dtype=fr.FR_BF16, num_cus=cus)
+                # several rows per workgroup: the pipelined kernel
+                self.kernel = "fr_pipe_layernorm_bf16" if self.plan.rows_per_wg > 1 else "fr_per_layernorm_bf16"
 
             def launch(self, k):
                 x, y = self.args[k]
@@ -269,9 +273,11 @@ def make_workload(name, torch, fr, synth):
                 return self.args[k][1]
 
             def config(self):
-                p = fr.fr_plan_query(fr.FR_OP_LAYERNORM, rows, cols, dtype=fr.FR_BF16)
+                p = self.plan
                 return {"workload": "LayerNorm bf16 [2048,32768], eps 1e-5", "rows": rows, "cols": cols,
-                        "form": fr.FORM_NAMES[p.form], "launch": {"threads": p.threads, "vec16_per_lane": p.vec}}
+                        "form": fr.FORM_NAMES[p.form],
+                        "launch": {"threads": p.threads, "vec16_per_lane": p.vec, "rows_per_wg": p.rows_per_wg,
+                                   "grid": p.grid}}
 
             def oracle_fn(self, threads=1):
                 import oracle
