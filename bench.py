@@ -8,8 +8,7 @@ already resident in HBM. The default workload is the row softmax over
 4096 x 1024 fp32 (the headline configuration). The other workloads are
 selected with --workload: Example 1.1 sums, the softmax and its backward at
 65536 rows and Example 1.1 at 2^20 rows (the largest shapes), LayerNorm
-2048 x 32768 bf16, the
-2^28 sum of squares, the ragged 512-row softmax, decode and tiled attention,
+2048 x 32768 bf16 and at 8192 rows, the 2^28 sum of squares, the ragged 512-row softmax, decode and tiled attention,
 softmax and LayerNorm backward, x.t() + y, GELU backward, a recorded region
 of 16 Example 1.1 launches, and streaming references (copy, read). Tiled
 attention reports TFLOP/s against the matrix cores' bf16 peak; the others
@@ -243,8 +242,10 @@ def make_workload(name, torch, fr, synth):
 
         return W(), per_set
 
-    if name == "layernorm":
-        rows, cols = 2048, 32768
+    if name in ("layernorm", "layernorm_large"):
+        # the 2048 x 32768 workload, or the same distribution at 8192 rows
+        # (512 MiB in, 512 MiB out): the largest shape measured
+        rows, cols = (2048, 32768) if name == "layernorm" else (8192, 32768)
         x_h, g_h, b_h = synth.layernorm_inputs(rows, cols, seed=3001)
         per_set = 2 * rows * cols * 2
 
@@ -274,7 +275,7 @@ def make_workload(name, torch, fr, synth):
 
             def config(self):
                 p = self.plan
-                return {"workload": "LayerNorm bf16 [2048,32768], eps 1e-5", "rows": rows, "cols": cols,
+                return {"workload": f"LayerNorm bf16 [{rows},{cols}], eps 1e-5", "rows": rows, "cols": cols,
                         "form": fr.FORM_NAMES[p.form],
                         "launch": {"threads": p.threads, "vec16_per_lane": p.vec, "rows_per_wg": p.rows_per_wg,
                                    "grid": p.grid}}
@@ -283,7 +284,7 @@ def make_workload(name, torch, fr, synth):
                 import oracle
                 r = 128
                 return (lambda: oracle.layernorm_rows(x_h[:r], g_h, b_h, threads=threads), layernorm_bytes(r, cols),
-                        f"first {r} of 2048 rows")
+                        f"first {r} of {rows} rows")
 
         return W(), per_set
 
@@ -878,7 +879,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="softmax",
                     choices=["softmax", "softmax_large", "softmax_bwd_large", "sum_relu_add", "sum_relu_add_large",
-                             "layernorm",
+                             "layernorm", "layernorm_large",
                              "sumsq", "ragged", "copy", "stream_copy", "stream_copy_c3", "stream_read", "attn_decode", "softmax_bwd", "add_2d",
                              "gelu_bwd", "layernorm_bwd", "c1_region", "attn_block",
                              "attn_block_full", "latency"])
