@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import bf16_bits_of, bf16_bits_tensor, check_bf16, forced, host
+from gpu_util import bf16_bits_of, bf16_bits_tensor, bf16_to_f64, check_bf16, forced, host
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -145,3 +145,28 @@ def test_layernorm_pipelined_rows(nr):
     assert np.allclose(mean, m64, rtol=1e-5, atol=1e-6) and np.allclose(rstd, r64, rtol=1e-5)
     got, _, _ = run(gd, bd, True, in_place=True)
     compare(x, g, b, got, what=f"pipelined nr={nr} in place")
+
+
+@pytest.mark.parametrize("form", ["per", "pipelined", "red"])
+@pytest.mark.parametrize("cols", [1000, 32768])
+def test_layernorm_nan_and_inf_rows(form, cols):
+    """A NaN or an infinity anywhere in a row makes every output of that row
+    NaN (the mean is NaN or infinite, and x - mean is NaN); the other rows
+    are untouched. Through each form, including the dot-product row sum."""
+    if form == "pipelined" and cols != 32768:
+        pytest.skip("the pipelined form takes rows of 32768")
+    x, g, b = synth.layernorm_inputs(4, cols, seed=3600 + cols)
+    special = {0: 0x7FC0, 1: 0x7F80, 2: 0xFF80}  # NaN, +inf, -inf at a different column each
+    for r, bits in special.items():
+        x[r, (r * 977 + 5) % cols] = bits
+    if form == "pipelined":
+        fr.fr_tune_override(fr.FR_OP_LAYERNORM, form=fr.FR_FORM_PER, threads=512, vec=8, rows_per_wg=3)
+        try:
+            got = gpu_ln(x, g, b)
+        finally:
+            fr.fr_tune_override(fr.FR_OP_LAYERNORM)
+    else:
+        got = gpu_ln(x, g, b, form=FORMS[form])
+    vals = bf16_to_f64(got)
+    assert np.isnan(vals[:3]).all(), f"{form} {cols}: rows with NaN or inf must be all NaN"
+    compare(x[3:], g, b, got[3:], what=f"{form} {cols} clean row")
