@@ -170,3 +170,20 @@ def test_layernorm_nan_and_inf_rows(form, cols):
     vals = bf16_to_f64(got)
     assert np.isnan(vals[:3]).all(), f"{form} {cols}: rows with NaN or inf must be all NaN"
     compare(x[3:], g, b, got[3:], what=f"{form} {cols} clean row")
+
+
+@pytest.mark.parametrize("rows", [1001, 4096])
+def test_layernorm_pipelined_automatic_row_counts(rows):
+    """The automatic plan at row counts other than the workload's: 1001 rows
+    (4 per workgroup, 251 workgroups, the last one with a row past the end)
+    and 4096 rows (8 per workgroup, 512 workgroups: two rounds of one
+    workgroup per CU). 1001: every row against the oracle; 4096: every 7th
+    row and the last."""
+    cols = 32768
+    p = fr.fr_plan_query(fr.FR_OP_LAYERNORM, rows, cols, dtype=fr.FR_BF16,
+                         num_cus=torch.cuda.get_device_properties(0).multi_processor_count)
+    assert p.rows_per_wg > 1
+    x, g, b = synth.layernorm_inputs(rows, cols, seed=3700 + rows)
+    got = gpu_ln(x, g, b)
+    pick = None if rows == 1001 else np.r_[np.arange(0, rows, 7), rows - 1]
+    compare(x, g, b, got, rows=pick, what=f"pipelined {rows}x{cols}")
