@@ -10,9 +10,10 @@ selected with --workload: Example 1.1 sums, the softmax and its backward at
 65536 rows and Example 1.1 at 2^20 rows (the largest shapes), LayerNorm
 2048 x 32768 bf16 and at 8192 rows, the 2^28 sum of squares, the ragged 512-row softmax, decode and tiled attention,
 softmax and LayerNorm backward, x.t() + y, GELU backward, a recorded region
-of 16 Example 1.1 launches, and streaming references (copy, read). Tiled
-attention reports TFLOP/s against the matrix cores' bf16 peak; the others
-report GB/s against HBM.
+of 16 Example 1.1 launches, and streaming references (copy, read, write,
+and an empty kernel: the cost of one kernel boundary, reported in us per
+step). Tiled attention reports TFLOP/s against the matrix cores' bf16 peak;
+the others report GB/s against HBM.
 
 Timing: W untimed steps, then exactly K steps between two events on the
 launch stream, with a device synchronization on both sides. Consecutive
@@ -705,6 +706,57 @@ def make_workload(name, torch, fr, synth):
 
         return W(), per_set
 
+    if name == "stream_write":
+        # the write half of the softmax 4096x1024 step: 16 MiB stored, nothing read
+        nout = 16 << 20
+
+        class W(Workload):
+            kernel = "fr_stream_write_k"
+            bytes = nout
+            dtype = "u8"
+
+            def alloc(self, sets):
+                self.args = [torch.empty(nout // 4, dtype=torch.int32, device=dev) for _ in range(sets)]
+
+            def launch(self, k):
+                fr.fr_stream_write(self.args[k], 0x3F800000)
+
+            def output(self, k):
+                return self.args[k]
+
+            def config(self):
+                return {"workload": "streaming write of 16 MiB (the output of the softmax 4096x1024 step), "
+                                    "the practical ceiling of the write half", "bytes_out": nout}
+
+            def oracle_fn(self):
+                return lambda: np.full(nout // 4, 1.0, dtype=np.float32), self.bytes, "numpy fill of the same size"
+
+        return W(), nout
+
+    if name == "empty":
+        # a kernel that does nothing: back to back, the cost of one kernel
+        # boundary, which every one-launch step pays whatever bytes it moves
+        class W(Workload):
+            kernel = "fr_empty_k"
+            bytes = 0
+            dtype = "none"
+
+            def alloc(self, sets):
+                # never written: the poisoned bytes are what the check expects
+                self.out = torch.full((4,), -1, dtype=torch.int32, device=dev)
+
+            def launch(self, k):
+                fr.fr_stream_empty()
+
+            def output(self, k):
+                return self.out
+
+            def config(self):
+                return {"workload": "empty kernel (one workgroup), launched back to back: the floor of a "
+                                    "one-launch step"}
+
+        return W(), 1 << 30
+
     raise SystemExit(f"unknown workload {name}")
 
 
@@ -880,7 +932,7 @@ def main():
     ap.add_argument("--workload", default="softmax",
                     choices=["softmax", "softmax_large", "softmax_bwd_large", "sum_relu_add", "sum_relu_add_large",
                              "layernorm", "layernorm_large",
-                             "sumsq", "ragged", "copy", "stream_copy", "stream_copy_c3", "stream_read", "attn_decode", "softmax_bwd", "add_2d",
+                             "sumsq", "ragged", "copy", "stream_copy", "stream_copy_c3", "stream_read", "stream_write", "empty", "attn_decode", "softmax_bwd", "add_2d",
                              "gelu_bwd", "layernorm_bwd", "c1_region", "attn_block",
                              "attn_block_full", "latency"])
     ap.add_argument("--warm", action="store_true", help="one buffer set: reads may hit the MALL")
@@ -1028,7 +1080,12 @@ def main():
         result["roofline"].update({"bound": "mfma", "achieved": round(tfs, 2), "peak": PEAK_MFMA_BF16_TFS,
                                    "unit": "TFLOP/s", "frac": round(tfs / PEAK_MFMA_BF16_TFS, 4),
                                    "algorithmic_flops_per_launch": flops, "hbm_GB_per_s": round(gbs, 2)})
-    if not args.no_cpu:
+    if not wl.bytes:
+        # no bytes moved: the line is the time of one step
+        result.update({"metric": "kernel boundary: time per step of back-to-back empty launches",
+                       "value": round(ms_per_step * 1000, 4), "unit": "us", "higher_is_better": False,
+                       "roofline": None})
+    elif not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 

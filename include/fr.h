@@ -407,10 +407,18 @@ int fr_attn_block(const void* q, const void* k, const void* v, void* o, float* l
  *   each of its workgroups w, the XOR of all 32-bit words that workgroup
  *   read; the XOR of sink[0 .. FR_STREAM_SINK_WORDS) is then the XOR of all
  *   words of x (unused entries are not written: clear them first). sink:
- *   device array of FR_STREAM_SINK_WORDS uint32. */
+ *   device array of FR_STREAM_SINK_WORDS uint32.
+ * fr_stream_write: every 32-bit word of y (nbytes bytes, same rules as x
+ *   above) = value; stores only, the write half of a step's traffic.
+ * fr_stream_empty: enqueues a kernel of one workgroup that does nothing.
+ *   Launched back to back, it times one kernel boundary (the end of one
+ *   kernel to the start of the next), which every step that is one launch
+ *   pays whatever bytes it moves. Errors: FR_E_DEVICE / FR_E_LAUNCH only. */
 #define FR_STREAM_SINK_WORDS 1024
 int fr_stream_copy(const void* x, void* y, int64_t nbytes, void* stream);
 int fr_stream_read(const void* x, int64_t nbytes, uint32_t* sink, void* stream);
+int fr_stream_write(void* y, int64_t nbytes, uint32_t value, void* stream);
+int fr_stream_empty(void* stream);
 
 /* ------------------------------------------------------------ sum of squares, no allocation
  * For callers that cannot allocate device memory (code under graph capture,

@@ -43,7 +43,7 @@ EXPORTS = (
     "fr_layernorm_rows", "fr_layernorm_rows_stats", "fr_layernorm_rows_backward_workspace_bytes",
     "fr_layernorm_rows_backward",
     "fr_sumsq_rows", "fr_sumsq_full_workspace_bytes", "fr_sumsq_full", "fr_sumsq_full_noalloc",
-    "fr_stream_copy", "fr_stream_read", "fr_device_clock", "fr_device_clock_khz", "fr_pointer_chase",
+    "fr_stream_copy", "fr_stream_read", "fr_stream_write", "fr_stream_empty", "fr_device_clock", "fr_device_clock_khz", "fr_pointer_chase",
     "fr_attn_decode_workspace_bytes", "fr_attn_decode",
     "fr_add_2d", "fr_gelu_backward", "fr_attn_block",
     "fr_region_create", "fr_region_destroy", "fr_region_run", "fr_region_state", "fr_region_counts",
@@ -100,6 +100,8 @@ def _load():
         "fr_stream_copy": (I32, [P, P, I64, P]),
         "fr_attn_block": (I32, [P, P, P, P, P, I64, I64, I64, I64, I64, I64, I32, ctypes.c_float, I32, P]),
         "fr_stream_read": (I32, [P, I64, P, P]),
+        "fr_stream_write": (I32, [P, I64, ctypes.c_uint32, P]),
+        "fr_stream_empty": (I32, [P]),
         "fr_device_clock": (I32, [P, I32, P]),
         "fr_device_clock_khz": (I32, [P]),
         "fr_pointer_chase": (I32, [P, I64, I64, ctypes.c_uint32, P, P]),
@@ -351,6 +353,21 @@ def fr_stream_read(x, sink, stream=None):
     _check(lib.fr_stream_read(_ptr(x), x.numel() * x.element_size(), _ptr(sink), _stream(stream)),
            "fr_stream_read")
     return sink
+
+
+def fr_stream_write(y, value, stream=None):
+    """Every 32-bit word of contiguous y (a multiple of 16 bytes) = value
+    (an unsigned 32-bit pattern): the streaming reference write."""
+    if not y.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    _check(lib.fr_stream_write(_ptr(y), y.numel() * y.element_size(), value & 0xFFFFFFFF, _stream(stream)),
+           "fr_stream_write")
+    return y
+
+
+def fr_stream_empty(stream=None):
+    """Enqueue a kernel that does nothing: back to back, one kernel boundary."""
+    _check(lib.fr_stream_empty(_stream(stream)), "fr_stream_empty")
 
 
 def fr_device_clock(out, slot, stream=None):

@@ -575,6 +575,26 @@ int fr_stream_read(const void* x, int64_t nbytes, uint32_t* sink, void* stream) 
     return finish_launch(launch_stream_read(x, nbytes / 16, sink, (hipStream_t)stream));
 }
 
+int fr_stream_write(void* y, int64_t nbytes, uint32_t value, void* stream) {
+    if (nbytes < 0 || nbytes % 16) return FR_E_SIZE;
+    if (nbytes == 0) return FR_OK;
+    if (!y) return FR_E_NULL;
+    if (!aligned(y, 16)) return FR_E_ALIGN;
+    int num_cus = 0;
+    const int st = device_check(&num_cus);
+    if (st != FR_OK) return st;
+    (void)hipGetLastError();
+    return finish_launch(launch_stream_write(y, nbytes / 16, value, (hipStream_t)stream));
+}
+
+int fr_stream_empty(void* stream) {
+    int num_cus = 0;
+    const int st = device_check(&num_cus);
+    if (st != FR_OK) return st;
+    (void)hipGetLastError();
+    return finish_launch(launch_empty((hipStream_t)stream));
+}
+
 int fr_device_clock(uint64_t* out, int slot, void* stream) {
     if (!out) return FR_E_NULL;
     if (slot < 0) return FR_E_ARG;

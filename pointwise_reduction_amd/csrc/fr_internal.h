@@ -162,6 +162,8 @@ hipError_t launch_attn_block(const AttnBlockArgs& a, hipStream_t s);
 constexpr int kStreamGrid = 1024;
 hipError_t launch_stream_copy(const void* x, void* y, int64_t nvec, hipStream_t s);
 hipError_t launch_stream_read(const void* x, int64_t nvec, uint32_t* sink, hipStream_t s);
+hipError_t launch_stream_write(void* y, int64_t nvec, uint32_t value, hipStream_t s);
+hipError_t launch_empty(hipStream_t s);
 hipError_t launch_device_clock(uint64_t* out, int slot, hipStream_t s);
 hipError_t launch_pointer_chase(const uint32_t* chain, int64_t n, int64_t steps, uint32_t start, uint64_t* out,
                                 hipStream_t s);

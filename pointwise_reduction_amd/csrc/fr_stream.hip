@@ -8,6 +8,10 @@
 //   fr_stream_copy_k  y = x
 //   fr_stream_read_k  per-workgroup XOR of every 32-bit word read, so that
 //                     the loads are observable and the result checkable
+//   fr_stream_write_k y = a repeated 32-bit word (stores only)
+//   fr_empty_k        one workgroup that does nothing: launched back to back,
+//                     the cost of a kernel boundary alone, the floor under
+//                     every step that is one launch
 #include "fr_device.h"
 #include "fr_internal.h"
 
@@ -49,6 +53,19 @@ __global__ __launch_bounds__(T) void fr_stream_read_k(const u32x4* __restrict__ 
     r = block_fold(r, sl, T / kWave, OpXor());
     if (threadIdx.x == 0) sink[blockIdx.x] = (uint32_t)r;
 }
+
+template <int T, int NV>
+__global__ __launch_bounds__(T) void fr_stream_write_k(u32x4* __restrict__ y, int64_t nvec, uint32_t value) {
+    const int64_t step = (int64_t)gridDim.x * T * NV;
+    const u32x4 v = {value, value, value, value};
+    for (int64_t b = (int64_t)blockIdx.x * T * NV + threadIdx.x; b < nvec; b += step) {
+#pragma unroll
+        for (int k = 0; k < NV; ++k)
+            if (b + k * T < nvec) __builtin_nontemporal_store(v, y + b + k * T);
+    }
+}
+
+__global__ __launch_bounds__(64) void fr_empty_k() {}
 
 // One lane stores the device's constant wall clock (the counter the wait
 // loops of the split kernels read) into out[slot] when the kernel runs: two
@@ -100,6 +117,18 @@ hipError_t launch_stream_read(const void* x, int64_t nvec, uint32_t* sink, hipSt
     const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(kStreamGrid, (nvec + 1023) / 1024));
     hipLaunchKernelGGL((fr_stream_read_k<256, 4>), dim3((unsigned)grid), dim3(256), 0, s,
                        static_cast<const u32x4*>(x), nvec, sink);
+    return hipGetLastError();
+}
+
+hipError_t launch_stream_write(void* y, int64_t nvec, uint32_t value, hipStream_t s) {
+    const int64_t grid = std::min<int64_t>(kStreamGrid, (nvec + 1023) / 1024);
+    hipLaunchKernelGGL((fr_stream_write_k<256, 4>), dim3((unsigned)grid), dim3(256), 0, s, static_cast<u32x4*>(y),
+                       nvec, value);
+    return hipGetLastError();
+}
+
+hipError_t launch_empty(hipStream_t s) {
+    hipLaunchKernelGGL(fr_empty_k, dim3(1), dim3(64), 0, s);
     return hipGetLastError();
 }
 

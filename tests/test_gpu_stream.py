@@ -35,6 +35,31 @@ def test_stream_read_xor(nbytes):
     assert int(got) == int(want)
 
 
+@pytest.mark.parametrize("nbytes", [16, 4096, 16 * 1000 + 16, (16 << 20) + 48])
+def test_stream_write_fills(nbytes):
+    """Every word is the pattern, and the guard words past the end keep theirs."""
+    y = torch.full((nbytes // 4 + 4,), -1, dtype=torch.int32, device="cuda")
+    fr.lib.fr_stream_write(fr._ptr(y), nbytes, 0x9E3779B9, fr._stream(None))
+    got = host(y).view(np.uint32)
+    assert (got[: nbytes // 4] == 0x9E3779B9).all()
+    assert (got[nbytes // 4:] == 0xFFFFFFFF).all()
+
+
+def test_stream_empty_launches_back_to_back():
+    """Empty launches between two clock marks: each costs at least the
+    counter's resolution and far less than a millisecond."""
+    khz = fr.fr_device_clock_khz()
+    marks = torch.zeros(2, dtype=torch.int64, device="cuda")
+    torch.cuda.synchronize()
+    fr.fr_device_clock(marks, 0)
+    for _ in range(100):
+        fr.fr_stream_empty()
+    fr.fr_device_clock(marks, 1)
+    t = host(marks)
+    us = (int(t[1]) - int(t[0])) / khz * 1000.0
+    assert 0 < us < 100_000, us
+
+
 def test_device_clock_marks_bracket_stream_work():
     """Two clock marks around a 256 MiB copy: the counter runs at the rate
     fr_device_clock_khz reports, the marks are ordered, and their distance

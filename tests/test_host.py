@@ -136,6 +136,12 @@ def test_stream_reference_argument_errors():
     assert read(FAKE, 8, FAKE, None) == fr.FR_E_SIZE
     assert read(FAKE, 16, None, None) == fr.FR_E_NULL
     assert read(P(0x10004), 16, FAKE, None) == fr.FR_E_ALIGN
+    write = fr.lib.fr_stream_write
+    assert write(FAKE, 24, 0, None) == fr.FR_E_SIZE
+    assert write(FAKE, -16, 0, None) == fr.FR_E_SIZE
+    assert write(None, 16, 0, None) == fr.FR_E_NULL
+    assert write(P(0x10008), 32, 0, None) == fr.FR_E_ALIGN
+    assert write(None, 0, 0, None) == fr.FR_OK  # nothing to write, no HIP call
 
 
 def test_attn_decode_argument_errors():
