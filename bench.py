@@ -463,6 +463,7 @@ def make_workload(name, torch, fr, synth):
                 fr.fr_layernorm_rows_stats(x0, torch.empty_like(x0), mean=mean, rstd=rstd, gamma=g, beta=bf(b_h))
                 nbytes = fr.fr_layernorm_rows_backward_workspace_bytes(rows, cols)
                 self.ws = torch.empty(nbytes // 4, dtype=torch.float32, device=dev)
+                fr.fr_layernorm_rows_backward_workspace_init(self.ws)
                 self.plan = fr.fr_plan_query(fr.FR_OP_LAYERNORM_BWD, rows, cols, dtype=fr.FR_BF16, ws_bytes=nbytes)
                 self.kernel = ("fr_team_layernorm_bwd_bf16" if self.plan.form == fr.FR_FORM_SPLIT
                                else "fr_per_layernorm_bwd_bf16")

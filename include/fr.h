@@ -316,12 +316,24 @@ int fr_layernorm_rows_stats(const void* x, const void* gamma, const void* beta, 
  *                 may be NULL (then the persistent form runs). That size
  *                 serves every form. The workspace's contents are the
  *                 library's during the call; calls that share one workspace
- *                 must not overlap.
+ *                 must not overlap. The split form exchanges the row sums
+ *                 through slots tagged with a call epoch kept in the
+ *                 workspace, so nothing is cleared between calls: initialize
+ *                 the workspace once with
+ *                 fr_layernorm_rows_backward_workspace_init before its first
+ *                 use, and keep it for this entry point. A workspace never
+ *                 initialized gives the same results, but every member
+ *                 computes its partners' sums itself (slower).
  * 1 <= cols <= 32768 (FR_E_SIZE otherwise). With dgamma or dbeta and more
  * than 16384 columns, x, dy, dx and gamma must allow 16-byte accesses (bases
  * and row strides multiples of 8 elements, cols a multiple of 8; FR_E_ALIGN
  * otherwise). dtype must be FR_BF16. */
 uint64_t fr_layernorm_rows_backward_workspace_bytes(int64_t rows, int64_t cols, int dtype);
+/* Initialize a LayerNorm-backward workspace of ws_bytes bytes (enqueued on
+ * stream; ws 16-byte aligned, FR_E_ALIGN otherwise; at least 64 bytes,
+ * FR_E_WORKSPACE otherwise): zeros, call epoch 0 and the initialization
+ * mark. Once per workspace; every later call leaves it initialized. */
+int fr_layernorm_rows_backward_workspace_init(void* ws, uint64_t ws_bytes, void* stream);
 int fr_layernorm_rows_backward(const void* x, const void* dy, const void* gamma, const float* mean,
                                const float* rstd, void* dx, float* dgamma, float* dbeta, int64_t rows, int64_t cols,
                                int64_t x_rs, int64_t x_cs, int64_t dy_rs, int64_t dy_cs, int64_t dx_rs,

@@ -41,6 +41,7 @@ EXPORTS = (
     "fr_softmax_rows_workspace_bytes", "fr_softmax_rows_workspace_init", "fr_softmax_rows",
     "fr_softmax_rows_backward",
     "fr_layernorm_rows", "fr_layernorm_rows_stats", "fr_layernorm_rows_backward_workspace_bytes",
+    "fr_layernorm_rows_backward_workspace_init",
     "fr_layernorm_rows_backward",
     "fr_sumsq_rows", "fr_sumsq_full_workspace_bytes", "fr_sumsq_full", "fr_sumsq_full_noalloc",
     "fr_stream_copy", "fr_stream_read", "fr_stream_write", "fr_stream_empty", "fr_device_clock", "fr_device_clock_khz", "fr_pointer_chase",
@@ -108,6 +109,7 @@ def _load():
         "fr_add_2d": (I32, [P, I64, I64, P, I64, I64, P, I64, I64, I64, I32, P]),
         "fr_layernorm_rows_stats": (I32, [P, P, P, P, P, P, I64, I64, I64, I64, I64, I64, ctypes.c_float, I32, P]),
         "fr_layernorm_rows_backward_workspace_bytes": (U64, [I64, I64, I32]),
+        "fr_layernorm_rows_backward_workspace_init": (I32, [P, U64, P]),
         "fr_layernorm_rows_backward": (I32, [P, P, P, P, P, P, P, P, I64, I64, I64, I64, I64, I64, I64, I64, P, U64,
                                              I32, P]),
         "fr_gelu_backward": (I32, [P, I64, P, P, I64, I32, P]),
@@ -282,10 +284,19 @@ def fr_layernorm_rows_backward_workspace_bytes(rows, cols, dtype=FR_BF16):
     return lib.fr_layernorm_rows_backward_workspace_bytes(rows, cols, dtype)
 
 
+def fr_layernorm_rows_backward_workspace_init(ws, stream=None):
+    """Initialize a LayerNorm-backward workspace tensor (once, before its
+    first use); every fr_layernorm_rows_backward call leaves it initialized."""
+    if not ws.is_contiguous():
+        raise ValueError("expected a contiguous workspace")
+    _check(lib.fr_layernorm_rows_backward_workspace_init(_ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "fr_layernorm_rows_backward_workspace_init")
+
+
 def fr_layernorm_rows_backward(x, dy, mean, rstd, dx, gamma=None, dgamma=None, dbeta=None, ws=None, stream=None):
     """dx (bf16), and optionally dgamma / dbeta (fp32 [cols]), from the saved
-    mean and rstd. A workspace is allocated when dgamma or dbeta is requested
-    and ws is None."""
+    mean and rstd. A workspace is allocated and initialized when dgamma or
+    dbeta is requested and ws is None."""
     rows, cols, x_rs, x_cs = _mat(x)
     r2, c2, dy_rs, dy_cs = _mat(dy)
     r3, c3, dx_rs, dx_cs = _mat(dx)
@@ -293,7 +304,8 @@ def fr_layernorm_rows_backward(x, dy, mean, rstd, dx, gamma=None, dgamma=None, d
         raise ValueError("shape mismatch")
     if ws is None and (dgamma is not None or dbeta is not None):
         nbytes = fr_layernorm_rows_backward_workspace_bytes(rows, cols)
-        ws = torch.empty(max(nbytes, 16) // 4, dtype=torch.float32, device=x.device)
+        ws = torch.empty(max(nbytes, 64) // 4, dtype=torch.float32, device=x.device)
+        fr_layernorm_rows_backward_workspace_init(ws, stream)
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib.fr_layernorm_rows_backward(_ptr(x), _ptr(dy), _ptr(gamma), _ptr(mean), _ptr(rstd), _ptr(dx),
                                           _ptr(dgamma), _ptr(dbeta), rows, cols, x_rs, x_cs, dy_rs, dy_cs, dx_rs,

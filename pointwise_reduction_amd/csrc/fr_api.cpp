@@ -417,6 +417,17 @@ uint64_t fr_layernorm_rows_backward_workspace_bytes(int64_t rows, int64_t cols, 
     return need;
 }
 
+int fr_layernorm_rows_backward_workspace_init(void* ws, uint64_t ws_bytes, void* stream) {
+    if (!ws) return FR_E_NULL;
+    if (!aligned(ws, 16)) return FR_E_ALIGN;
+    if (ws_bytes < 64) return FR_E_WORKSPACE;
+    int num_cus = 0;
+    const int st = device_check(&num_cus);
+    if (st != FR_OK) return st;
+    (void)hipGetLastError();
+    return finish_launch(launch_layernorm_bwd_ws_init(ws, ws_bytes, (hipStream_t)stream));
+}
+
 int fr_layernorm_rows_backward(const void* x, const void* dy, const void* gamma, const float* mean,
                                const float* rstd, void* dx, float* dgamma, float* dbeta, int64_t rows, int64_t cols,
                                int64_t x_rs, int64_t x_cs, int64_t dy_rs, int64_t dy_cs, int64_t dx_rs,

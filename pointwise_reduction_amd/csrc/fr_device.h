@@ -242,6 +242,41 @@ __device__ __forceinline__ T block_fold(T v, T* slots, int nw, Op op) {
     return r;
 }
 
+// ------------------------------------------------------------------ epoch-tagged workspaces
+// Split kernels that exchange partials between workgroups through a
+// workspace publish each value as one 64-bit word: a 32-bit tag above the
+// 32-bit value. The tag is the call's epoch + 1, read from the workspace
+// header at the start of the call; a word whose tag differs (an earlier
+// call's, or the zeros of an initialized workspace) is not yet written, so
+// nothing has to be cleared between calls. Header words (uint32): 0 a
+// cumulative count of partials a workgroup computed itself instead of
+// reading them, 2 the epoch, 4-5 an initialization mark (a different value
+// per workspace kind), one flag per workgroup after that.
+constexpr uint32_t kMaxEpoch = 0x7FFFFFFFu;  // tags run 1 .. kMaxEpoch
+constexpr int kHdrRecomputed = 0, kHdrEpoch = 2, kHdrMagic = 4;
+
+__device__ __forceinline__ uint64_t slot_word(uint32_t tag, float v) {
+    return ((uint64_t)tag << 32) | __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ bool published(uint64_t w, uint32_t tag) { return (uint32_t)(w >> 32) == tag; }
+
+// End of a call, in one workgroup (all its threads): once every
+// workgroup's flag holds this call's tag, every workgroup has read the
+// epoch, which is then advanced for the next call. Workgroups never wait for
+// this one, so one that has not started yet does so as others finish.
+template <int T>
+__device__ void epoch_advance(uint32_t* hdr, const uint32_t* flags, uint32_t tag, uint32_t epoch) {
+    const int tid = threadIdx.x;
+    for (;;) {
+        bool ok = true;
+        for (int b = tid; b < (int)gridDim.x; b += T)
+            ok &= __hip_atomic_load(&flags[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == tag;
+        if (__syncthreads_and(ok)) break;
+        __builtin_amdgcn_s_sleep(8);
+    }
+    if (tid == 0) __hip_atomic_store(&hdr[kHdrEpoch], epoch + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // ------------------------------------------------------------------ memory
 // Streaming loads/stores: the data is touched once, so they carry the
 // non-temporal hint (the role of evict_first in "Stax (4)", 9.2).

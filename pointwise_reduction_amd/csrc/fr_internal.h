@@ -94,12 +94,17 @@ struct LayerNormBwdArgs {
 inline int64_t ln_bwd_ldw(int64_t cols) { return (cols + 7) / 8 * 8; }
 // Split-row LayerNorm backward (a team of workgroups per row): workspace =
 // a kLnTeamHeader-byte header (word 0: partner sums recomputed after the
-// wait), 16 bytes per (row, part) exchange slot, padded to 256 bytes, then
-// the dgamma / dbeta partials [2][teams][ln_bwd_ldw(cols)] fp32.
-constexpr int kLnTeamHeader = 64;
+// wait, cumulative; word 2: the call epoch; words 4-5: the initialization
+// mark; from word kLnTeamHeaderFlags one flag per workgroup, at most
+// kLnTeamMaxGrid), 16 bytes per (row, part) exchange slot, padded to 256
+// bytes, then the dgamma / dbeta partials [2][teams][ln_bwd_ldw(cols)] fp32.
+constexpr int kLnTeamMaxGrid = 256;
+constexpr int kLnTeamHeaderFlags = 16;
+constexpr int kLnTeamHeader = 4 * kLnTeamHeaderFlags + 4 * kLnTeamMaxGrid;
 constexpr int kLnTeamPartCols = 8192;  // columns per member: one 16-byte vector per lane of 1024
 inline int64_t ln_team_slots_bytes(int64_t rows, int64_t parts) { return (rows * parts * 16 + 255) / 256 * 256; }
 hipError_t launch_layernorm_bwd(const fr_plan& p, const LayerNormBwdArgs& a, hipStream_t s);
+hipError_t launch_layernorm_bwd_ws_init(void* ws, uint64_t ws_bytes, hipStream_t s);
 hipError_t launch_softmax_bwd(const fr_plan& p, const SoftmaxBwdArgs& a, hipStream_t s);
 // Pointwise: 2-D add (a_t / b_t: the operand is column-major, a transposed
 // view with unit row stride) and GELU backward.

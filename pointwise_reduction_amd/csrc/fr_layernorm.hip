@@ -597,22 +597,22 @@ __global__ __launch_bounds__(T) void fr_per_layernorm_bwd_bf16(const uint16_t* x
 // which gives the partner's bits (so dx must not alias x or dy here; the
 // launcher never picks this form then). Every wait ends, and the result does
 // not depend on which members are resident. Slots: 16 bytes per (row, part),
-// words (row | a) and (row | b), set to "unpublished" by fr_ln_team_reset.
-constexpr uint32_t kLnUnpublished = 0xFFFFFFFFu;
+// words (tag | a) and (tag | b), tagged with the call's epoch (fr_device.h):
+// nothing is cleared between calls. The last workgroup advances the epoch at
+// its end. A workspace that fr_ln_team_init has not prepared (no mark), or
+// whose epoch has run out, trusts no slot: every partner's sums are then
+// computed from x and dy, which gives the same bits, only slower.
 constexpr int kLnTeamT = 1024;
 constexpr int kLnTeamW = kLnTeamT / kWave;
+constexpr uint64_t kLnWsMagic = 0x464C4E424B574D4Bull;
 
-__global__ __launch_bounds__(256) void fr_ln_team_reset(uint32_t* __restrict__ hdr, u32x4* __restrict__ slots,
-                                                        int64_t n) {
+// Workspace initialization: zeros everywhere (no slot carries a tag), epoch
+// 0, the mark.
+__global__ __launch_bounds__(256) void fr_ln_team_init(uint32_t* __restrict__ ws, int64_t nwords) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i < kLnTeamHeader / 4) hdr[i] = 0u;
-    if (i < n) slots[i] = u32x4{~0u, ~0u, ~0u, ~0u};
+    if (i < nwords)
+        ws[i] = i == kHdrMagic ? (uint32_t)kLnWsMagic : (i == kHdrMagic + 1 ? (uint32_t)(kLnWsMagic >> 32) : 0u);
 }
-
-__device__ __forceinline__ uint64_t ln_slot_word(int row, float v) {
-    return ((uint64_t)(uint32_t)row << 32) | __builtin_bit_cast(uint32_t, v);
-}
-__device__ __forceinline__ bool ln_published(uint64_t w) { return (uint32_t)(w >> 32) != kLnUnpublished; }
 
 // this lane's contribution to the two sums of one part of a row
 __device__ __forceinline__ void ln_lane_sums(u32x4 xv, u32x4 dv, u32x4 gv, float mu, float rs, float& a, float& b) {
@@ -667,6 +667,15 @@ __global__ __launch_bounds__(kLnTeamT) void fr_team_layernorm_bwd_bf16(
     __shared__ float ex[2][P][2 * R];
     __shared__ uint32_t s_miss[2];
     const int tid = threadIdx.x;
+    // this call's tag, the same in every thread (0: no slot is trusted, none
+    // is written); thread 0 acknowledges it in the workgroup's flag
+    uint32_t* flags = hdr + kLnTeamHeaderFlags;
+    const uint64_t magic = __hip_atomic_load(reinterpret_cast<const uint64_t*>(hdr + kHdrMagic), __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t epoch = __hip_atomic_load(hdr + kHdrEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t tag =
+        __builtin_amdgcn_readfirstlane(magic == kLnWsMagic && epoch < kMaxEpoch ? epoch + 1 : 0u);
+    if (tid == 0 && tag != 0u) __hip_atomic_store(&flags[blockIdx.x], tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int K = gridDim.x / P;
     const int team = blockIdx.x / P, p = blockIdx.x % P;
     const int c0 = p * W;
@@ -733,11 +742,11 @@ __global__ __launch_bounds__(kLnTeamT) void fr_team_layernorm_bwd_bf16(
             // write nothing. sc1: visible to the other compute dies.
             const int i = st * R + t;
             const int r = team + i * K;
-            const uint64_t word = ln_slot_word(r, tid & 1 ? v[2 * t + 1] : v[2 * t]);
+            const uint64_t word = slot_word(tag, tid & 1 ? v[2 * t + 1] : v[2 * t]);
             __builtin_amdgcn_raw_buffer_store_b64(
                 u32x2{(uint32_t)word, (uint32_t)(word >> 32)},
-                __builtin_amdgcn_make_buffer_rsrc(slots + 2 * ((int64_t)(i < n ? r : 0) * P + p), 0, i < n ? 16 : 0,
-                                                  kBufferRsrcWord3),
+                __builtin_amdgcn_make_buffer_rsrc(slots + 2 * ((int64_t)(i < n ? r : 0) * P + p), 0,
+                                                  i < n && tag != 0u ? 16 : 0, kBufferRsrcWord3),
                 min(tid, 2) * 8, 0, kAuxSc1);
         }
     };
@@ -765,21 +774,23 @@ __global__ __launch_bounds__(kLnTeamT) void fr_team_layernorm_bwd_bf16(
             const int i = st * R + lt;
             uint64_t w0 = pw0, w1 = pw1;
             // own part and rows past the team's end need no slot; with no
-            // wait (wait_ticks < 0) every partner's sums are recomputed
+            // wait (wait_ticks < 0), or no tag, every partner's sums are
+            // recomputed
             const bool need = tid < P * R && i < n && lq != p;
-            bool ok = !need || (wait_ticks >= 0 && ln_published(w0) && ln_published(w1));
+            const bool trust = wait_ticks >= 0 && tag != 0u;
+            bool ok = !need || (trust && published(w0, tag) && published(w1, tag));
             const uint64_t* ws = slots + 2 * ((int64_t)(team + i * K) * P + lq);
-            if (!__all(ok) && wait_ticks >= 0) {  // < 0: read no partner's slot (all are recomputed)
+            if (!__all(ok) && trust) {  // else read no partner's slot (all are recomputed)
                 const uint64_t t0 = wall_clock64();
                 for (;;) {
                     if ((int64_t)(wall_clock64() - t0) >= wait_ticks) break;
                     __builtin_amdgcn_s_sleep(2);
                     if (!ok) {
-                        if (!ln_published(w0))
+                        if (!published(w0, tag))
                             w0 = __hip_atomic_load(&ws[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        if (!ln_published(w1))
+                        if (!published(w1, tag))
                             w1 = __hip_atomic_load(&ws[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        ok = ln_published(w0) && ln_published(w1);
+                        ok = published(w0, tag) && published(w1, tag);
                     }
                     if (__all(ok)) break;
                 }
@@ -809,7 +820,7 @@ __global__ __launch_bounds__(kLnTeamT) void fr_team_layernorm_bwd_bf16(
             if (tid == 0) {
                 e[q][2 * t] = v[0];
                 e[q][2 * t + 1] = v[1];
-                __hip_atomic_fetch_add(&hdr[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_fetch_add(&hdr[kHdrRecomputed], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
@@ -878,6 +889,7 @@ __global__ __launch_bounds__(kLnTeamT) void fr_team_layernorm_bwd_bf16(
             st4<false>(pbp + 4, f32x4{ab[4], ab[5], ab[6], ab[7]});
         }
     }
+    if (blockIdx.x == gridDim.x - 1 && tag != 0u) epoch_advance<kLnTeamT>(hdr, flags, tag, epoch);
 }
 
 // dgamma[j] = sum_g ws[0][g][j], dbeta[j] = sum_g ws[1][g][j]: 256 threads as
@@ -1059,24 +1071,20 @@ hipError_t launch_layernorm_bwd(const fr_plan& p, const LayerNormBwdArgs& a, hip
     const int64_t ldw = ln_bwd_ldw(a.cols);
     const int64_t grid2 = (a.cols + 4 * Q - 1) / (4 * Q);
     if (p.form == FR_FORM_SPLIT) {
-        // reset of the exchange slots, the team kernel, the column sums
+        // the team kernel (its slots are epoch-tagged: no clearing), then
+        // the column sums
         const int parts = p.splits;
         LnTeamFn f = dg ? pick_team<true>(parts) : pick_team<false>(parts);
-        if (!f || !vec || a.rows < 1 || p.grid % parts) return hipErrorInvalidDeviceFunction;
+        if (!f || !vec || a.rows < 1 || p.grid % parts || p.grid > kLnTeamMaxGrid)
+            return hipErrorInvalidDeviceFunction;
         char* base = reinterpret_cast<char*>(a.ws);
         uint32_t* hdr = reinterpret_cast<uint32_t*>(base);
         u32x4* slots = reinterpret_cast<u32x4*>(base + kLnTeamHeader);
         float* part = reinterpret_cast<float*>(base + kLnTeamHeader + ln_team_slots_bytes(a.rows, parts));
-        const int64_t nslots = (int64_t)a.rows * parts;
-        const int64_t nreset = nslots > kLnTeamHeader / 4 ? nslots : kLnTeamHeader / 4;
-        hipLaunchKernelGGL(fr_ln_team_reset, dim3((unsigned)((nreset + 255) / 256)), dim3(256), 0, s, hdr, slots,
-                           nslots);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
         hipLaunchKernelGGL(f, dim3((unsigned)p.grid), dim3(kLnTeamT), 0, s, a.x, a.dy, a.gamma, a.mean, a.rstd, a.dx,
                            part, hdr, reinterpret_cast<uint64_t*>(slots), a.rows, a.cols, p.chunk, a.x_rs, a.dy_rs,
                            a.dx_rs, ldw, a.wait_ticks);
-        e = hipGetLastError();
+        hipError_t e = hipGetLastError();
         if (e != hipSuccess || !dg) return e;
         constexpr int TQ = kLnTeamFinQ, TS = 256 / TQ;
         hipLaunchKernelGGL((fr_layernorm_bwd_fin<TQ, TS>), dim3((unsigned)((a.cols + 4 * TQ - 1) / (4 * TQ))),
@@ -1097,6 +1105,13 @@ hipError_t launch_layernorm_bwd(const fr_plan& p, const LayerNormBwdArgs& a, hip
     if (!dg) return hipSuccess;
     hipLaunchKernelGGL((fr_layernorm_bwd_fin<Q, S>), dim3((unsigned)grid2), dim3(Q * S), 0, s, a.ws, a.dgamma,
                        a.dbeta, (int)p.grid, a.cols, ldw);
+    return hipGetLastError();
+}
+
+hipError_t launch_layernorm_bwd_ws_init(void* ws, uint64_t ws_bytes, hipStream_t s) {
+    const int64_t nwords = (int64_t)(ws_bytes / 4);
+    hipLaunchKernelGGL(fr_ln_team_init, dim3((unsigned)((nwords + 255) / 256)), dim3(256), 0, s,
+                       static_cast<uint32_t*>(ws), nwords);
     return hipGetLastError();
 }
 

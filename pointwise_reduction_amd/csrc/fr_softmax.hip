@@ -227,17 +227,10 @@ __global__ __launch_bounds__(T) void fr_red_softmax_f32(const float* x, float* y
     }
 }
 
-// Workspace slot words (the split forms): a 32-bit tag above a 32-bit value.
+// Workspace slot words (the split forms): a 32-bit tag above a 32-bit value
+// (slot_word, published and the header layout in fr_device.h).
 constexpr uint32_t kTwoKernelTag = 0x80000000u;  // never an epoch tag
-constexpr uint32_t kMaxEpoch = 0x7FFFFFFFu;      // tags run 1 .. kMaxEpoch
 constexpr uint64_t kWsMagic = 0x46525753664D4158ull;
-// header words (uint32): 0 recomputed partials (cumulative), 2 epoch, 4-5 magic
-constexpr int kHdrRecomputed = 0, kHdrEpoch = 2, kHdrMagic = 4;
-
-__device__ __forceinline__ uint64_t slot_word(uint32_t tag, float v) {
-    return ((uint64_t)tag << 32) | __builtin_bit_cast(uint32_t, v);
-}
-__device__ __forceinline__ bool published(uint64_t w, uint32_t tag) { return (uint32_t)(w >> 32) == tag; }
 __device__ __forceinline__ float slot_value(uint64_t w) { return __builtin_bit_cast(float, (uint32_t)w); }
 
 // ------------------------------------------------------------------ split
@@ -465,24 +458,6 @@ __global__ __launch_bounds__(256) void fr_split_softmax_init(uint32_t* __restric
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i < nwords)
         ws[i] = i == kHdrMagic ? (uint32_t)kWsMagic : (i == kHdrMagic + 1 ? (uint32_t)(kWsMagic >> 32) : 0u);
-}
-
-// End of a single-pass call, in the last workgroup (all its threads), which
-// has the fewest list entries and so finishes early: once every
-// workgroup's flag holds this call's tag, every workgroup has read the
-// epoch, which is then advanced for the next call. Workgroups never wait for
-// this one, so one that has not started yet does so as others finish.
-template <int T>
-__device__ void epoch_advance(uint32_t* hdr, const uint32_t* flags, uint32_t tag, uint32_t epoch) {
-    const int tid = threadIdx.x;
-    for (;;) {
-        bool ok = true;
-        for (int b = tid; b < (int)gridDim.x; b += T)
-            ok &= __hip_atomic_load(&flags[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == tag;
-        if (__syncthreads_and(ok)) break;
-        __builtin_amdgcn_s_sleep(8);
-    }
-    if (tid == 0) __hip_atomic_store(&hdr[kHdrEpoch], epoch + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Pipelined form of the one-kernel split (16-byte aligned rows): entry

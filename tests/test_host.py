@@ -125,6 +125,26 @@ def test_sumsq_argument_errors():
     assert rows_f(FAKE, None, 4, 8, 8, 1, None, 0, fr.FR_F32, None) == fr.FR_E_NULL
 
 
+def test_workspace_init_argument_errors():
+    # both split workspaces: checked before any HIP call
+    for init in (fr.lib.fr_softmax_rows_workspace_init, fr.lib.fr_layernorm_rows_backward_workspace_init):
+        assert init(None, 4096, None) == fr.FR_E_NULL
+        assert init(P(0x10008), 4096, None) == fr.FR_E_ALIGN
+        assert init(FAKE, 8, None) == fr.FR_E_WORKSPACE
+
+
+def test_layernorm_backward_team_header_holds_every_flag():
+    # the split-row backward's grid never exceeds the flags its header holds
+    # (256 workgroups): the largest team grids the planner makes
+    fr.fr_force_form(fr.FR_FORM_SPLIT)
+    try:
+        for rows, cols in ((100000, 32768), (4096, 8200), (300, 16392), (1 << 20, 24576), (1, 8200)):
+            p = fr.fr_plan_query(fr.FR_OP_LAYERNORM_BWD, rows, cols, dtype=fr.FR_BF16, ws_bytes=1 << 40)
+            assert p.form == fr.FR_FORM_SPLIT and p.grid <= 256 and p.grid % p.splits == 0, (rows, cols, p.grid)
+    finally:
+        fr.fr_force_form(fr.FR_FORM_AUTO)
+
+
 def test_stream_reference_argument_errors():
     copy, read = fr.lib.fr_stream_copy, fr.lib.fr_stream_read
     assert copy(FAKE, P(0x20000), 17, None) == fr.FR_E_SIZE
