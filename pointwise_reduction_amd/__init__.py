@@ -291,6 +291,7 @@ def fr_layernorm_rows_backward_workspace_init(ws, stream=None):
         raise ValueError("expected a contiguous workspace")
     _check(lib.fr_layernorm_rows_backward_workspace_init(_ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "fr_layernorm_rows_backward_workspace_init")
+    return ws
 
 
 def fr_layernorm_rows_backward(x, dy, mean, rstd, dx, gamma=None, dgamma=None, dbeta=None, ws=None, stream=None):
