@@ -64,9 +64,14 @@ SHAPES = [(1, 8), (7, 13), (33, 31), (65, 33), (4, 4096), (3, 1000), (5, 32768),
 def test_layernorm_forms(form, shape):
     rows, cols = shape
     plan_ok = cols <= (32768 if cols % 8 == 0 else 16384)
-    if form == "per" and not plan_ok:
-        pytest.skip("row does not fit the persistent form")
     x, g, b = synth.layernorm_inputs(rows, cols, seed=3100 + cols)
+    if form == "per" and not plan_ok:
+        # a row the persistent form cannot hold: the forced call is refused
+        # before any launch
+        with pytest.raises(fr.FrError) as e:
+            gpu_ln(x, g, b, form=FORMS[form])
+        assert e.value.status == fr.FR_E_ARG
+        return
     got = gpu_ln(x, g, b, form=FORMS[form])
     compare(x, g, b, got, what=f"{form} {rows}x{cols}")
 
@@ -153,9 +158,18 @@ def test_layernorm_nan_and_inf_rows(form, cols):
     """A NaN or an infinity anywhere in a row makes every output of that row
     NaN (the mean is NaN or infinite, and x - mean is NaN); the other rows
     are untouched. Through each form, including the dot-product row sum."""
-    if form == "pipelined" and cols != 32768:
-        pytest.skip("the pipelined form takes rows of 32768")
     x, g, b = synth.layernorm_inputs(4, cols, seed=3600 + cols)
+    if form == "pipelined" and cols != 32768:
+        # the pipelined form takes rows of 32768 only: a candidate plan that
+        # asks for it on other rows is refused
+        fr.fr_tune_override(fr.FR_OP_LAYERNORM, form=fr.FR_FORM_PER, threads=512, vec=8, rows_per_wg=3)
+        try:
+            with pytest.raises(fr.FrError) as e:
+                gpu_ln(x, g, b)
+        finally:
+            fr.fr_tune_override(fr.FR_OP_LAYERNORM)
+        assert e.value.status == fr.FR_E_ARG
+        return
     special = {0: 0x7FC0, 1: 0x7F80, 2: 0xFF80}  # NaN, +inf, -inf at a different column each
     for r, bits in special.items():
         x[r, (r * 977 + 5) % cols] = bits

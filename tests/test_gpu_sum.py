@@ -76,9 +76,13 @@ SHAPES = [(1, 1), (7, 13), (33, 31), (65, 33), (64, 128), (5, 2048), (3, 2049), 
 @pytest.mark.parametrize("shape", SHAPES, ids=[f"{r}x{c}" for r, c in SHAPES])
 def test_sum_relu_add_forms(form, shape):
     rows, cols = shape
-    if form == "per" and cols > 2048:
-        pytest.skip("row does not fit the persistent form")
     a, b, _ = synth.sum_relu_add_inputs(rows, cols, seed=1100 + rows + cols)
+    if form == "per" and cols > 2048:
+        # a row the persistent form cannot hold: the forced call is refused
+        with pytest.raises(fr.FrError) as e:
+            gpu_sum_relu_add(a, b, form=FORMS[form])
+        assert e.value.status == fr.FR_E_ARG
+        return
     out = gpu_sum_relu_add(a, b, form=FORMS[form])
     _, ref = oracle.sum_relu_add(a, b)
     check_fp32(out, ref, what=f"{form} {rows}x{cols}")
