@@ -677,7 +677,12 @@ __global__ __launch_bounds__(kLnTeamT) void fr_team_layernorm_bwd_bf16(
         __builtin_amdgcn_readfirstlane(magic == kLnWsMagic && epoch < kMaxEpoch ? epoch + 1 : 0u);
     if (tid == 0 && tag != 0u) __hip_atomic_store(&flags[blockIdx.x], tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int K = gridDim.x / P;
-    const int team = blockIdx.x / P, p = blockIdx.x % P;
+    // a team's members on one XCD (workgroup b runs on XCD b mod 8): when
+    // the grid allows, members are the XCD's consecutive workgroups
+    const bool xcd = gridDim.x % (8 * P) == 0;
+    const int slot = blockIdx.x / 8;
+    const int team = xcd ? (slot / P) * 8 + (int)(blockIdx.x % 8) : blockIdx.x / P;
+    const int p = xcd ? slot % P : blockIdx.x % P;
     const int c0 = p * W;
     const uint32_t pbytes = (uint32_t)min(W, cols - c0) * 2u;
     const int voff = tid * 16;
