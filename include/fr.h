@@ -323,7 +323,11 @@ int fr_layernorm_rows_stats(const void* x, const void* gamma, const void* beta, 
  *                 fr_layernorm_rows_backward_workspace_init before its first
  *                 use, and keep it for this entry point. A workspace never
  *                 initialized gives the same results, but every member
- *                 computes its partners' sums itself (slower).
+ *                 computes its partners' sums itself (slower). A call that
+ *                 takes the persistent form with dgamma or dbeta writes its
+ *                 partial rows over those slots and clears the
+ *                 initialization: initialize again before the next split
+ *                 call, or give the two forms separate workspaces.
  * 1 <= cols <= 32768 (FR_E_SIZE otherwise). With dgamma or dbeta and more
  * than 16384 columns, x, dy, dx and gamma must allow 16-byte accesses (bases
  * and row strides multiples of 8 elements, cols a multiple of 8; FR_E_ALIGN

@@ -900,10 +900,18 @@ __global__ __launch_bounds__(kLnTeamT) void fr_team_layernorm_bwd_bf16(
 // dgamma[j] = sum_g ws[0][g][j], dbeta[j] = sum_g ws[1][g][j]: 256 threads as
 // Q column quads x S slices; slice s sums partials g = s, s + S, ... in
 // order, then slice 0 adds the slices in order. Every run gives the same bits.
+// With hdr (the persistent form's call), thread 0 of workgroup 0 also
+// clears the workspace's initialization mark: the partial rows went to the
+// bytes that the split form's slots use, so no slot may be trusted until
+// the workspace is initialized again.
 template <int Q, int S>
 __global__ __launch_bounds__(Q * S) void fr_layernorm_bwd_fin(const float* __restrict__ ws, float* __restrict__ dgamma,
                                                               float* __restrict__ dbeta, int G, int cols,
-                                                              int64_t ldw) {
+                                                              int64_t ldw, uint32_t* __restrict__ hdr) {
+    if (hdr && blockIdx.x == 0 && threadIdx.x == 0) {
+        hdr[kHdrMagic] = 0u;
+        hdr[kHdrMagic + 1] = 0u;
+    }
     __shared__ f32x4 sg[S][Q];
     __shared__ f32x4 sb[S][Q];
     const int q = threadIdx.x % Q, sl = threadIdx.x / Q;
@@ -1093,7 +1101,7 @@ hipError_t launch_layernorm_bwd(const fr_plan& p, const LayerNormBwdArgs& a, hip
         if (e != hipSuccess || !dg) return e;
         constexpr int TQ = kLnTeamFinQ, TS = 256 / TQ;
         hipLaunchKernelGGL((fr_layernorm_bwd_fin<TQ, TS>), dim3((unsigned)((a.cols + 4 * TQ - 1) / (4 * TQ))),
-                           dim3(256), 0, s, part, a.dgamma, a.dbeta, (int)(p.grid / parts), a.cols, ldw);
+                           dim3(256), 0, s, part, a.dgamma, a.dbeta, (int)(p.grid / parts), a.cols, ldw, nullptr);
         return hipGetLastError();
     }
     const int mask = !vec ? kScalar : (a.cols == 8 * p.threads * p.vec ? kNone : kVec);
@@ -1101,15 +1109,20 @@ hipError_t launch_layernorm_bwd(const fr_plan& p, const LayerNormBwdArgs& a, hip
                                              : pick_bwd<false>(mask, p.threads, p.vec))
                                       : nullptr;
     if (!f) return hipErrorInvalidDeviceFunction;
+    // the partial rows start after the split form's header, which the
+    // finishing kernel marks uninitialized (the split form's slots may now
+    // hold partial-row bytes); with no rows nothing is written there
+    const bool rows_part = dg && a.rows > 0;
+    float* part = rows_part ? a.ws + kLnTeamHeader / 4 : nullptr;
     if (a.rows > 0) {
         hipLaunchKernelGGL(f, dim3((unsigned)p.grid), dim3(p.threads), 0, s, a.x, a.dy, a.gamma, a.mean, a.rstd,
-                           a.dx, a.ws, a.rows, a.cols, a.x_rs, a.dy_rs, a.dx_rs, ldw);
+                           a.dx, part, a.rows, a.cols, a.x_rs, a.dy_rs, a.dx_rs, ldw);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     if (!dg) return hipSuccess;
-    hipLaunchKernelGGL((fr_layernorm_bwd_fin<Q, S>), dim3((unsigned)grid2), dim3(Q * S), 0, s, a.ws, a.dgamma,
-                       a.dbeta, (int)p.grid, a.cols, ldw);
+    hipLaunchKernelGGL((fr_layernorm_bwd_fin<Q, S>), dim3((unsigned)grid2), dim3(Q * S), 0, s, part, a.dgamma,
+                       a.dbeta, (int)p.grid, a.cols, ldw, rows_part ? reinterpret_cast<uint32_t*>(a.ws) : nullptr);
     return hipGetLastError();
 }
 

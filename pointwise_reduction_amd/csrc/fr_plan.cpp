@@ -134,7 +134,9 @@ int finalize_plan(int op, int64_t rows, int64_t cols, const Knobs& k, fr_plan* p
             // next to the rows themselves
             p->grid = min64(min64(rows, std::max<int64_t>(kLnBwdWgs1024, rows / 16)),
                             (int64_t)kLnBwdWgs1024 * 1024 / k.threads);
-            p->ws_bytes = (uint64_t)(2 * p->grid * ln_bwd_ldw(cols) * 4);
+            // the partial rows after the split form's header (see
+            // launch_layernorm_bwd)
+            p->ws_bytes = p->grid > 0 ? (uint64_t)(kLnTeamHeader + 2 * p->grid * ln_bwd_ldw(cols) * 4) : 0;
             return FR_OK;
         }
         if (f32) {

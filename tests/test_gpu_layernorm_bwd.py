@@ -260,6 +260,39 @@ def test_layernorm_backward_split_rows_untrusted_workspace(kind):
     compare(x, dy, g, mean, rstd, b, what=f"{kind} workspace")
 
 
+def test_layernorm_backward_persistent_call_leaves_no_trusted_slot():
+    """A call that takes the persistent form writes its partial rows into
+    the bytes the split form's slots use, and clears the workspace's mark:
+    a split call that follows trusts no slot (every partner's sums
+    recomputed, the same bits), until the workspace is initialized again."""
+    rows, cols = 48, 32768
+    parts = 4
+    x, dy, g, mean, rstd = inputs(rows, cols, seed=47)
+    ws = team_ws(rows, cols)
+    fr.fr_force_form(fr.FR_FORM_SPLIT)
+    try:
+        a = run_bwd(x, dy, g, mean, rstd, ws=ws)
+    finally:
+        fr.fr_force_form(fr.FR_FORM_AUTO)
+    # in place: the persistent form, same workspace
+    b = run_bwd(x, dy, g, mean, rstd, ws=ws, inplace=True)
+    compare(x, dy, g, mean, rstd, b, what="persistent, in place")
+    fr.fr_force_form(fr.FR_FORM_SPLIT)
+    try:
+        n0 = recomputed(ws)
+        c = run_bwd(x, dy, g, mean, rstd, ws=ws)
+        assert (recomputed(ws) - n0) % (1 << 32) == rows * parts * (parts - 1)
+        fr.fr_layernorm_rows_backward_workspace_init(ws)
+        n0 = recomputed(ws)
+        d = run_bwd(x, dy, g, mean, rstd, ws=ws)
+        assert recomputed(ws) - n0 <= rows * parts * (parts - 1)
+    finally:
+        fr.fr_force_form(fr.FR_FORM_AUTO)
+    for k in ("dx", "dgamma", "dbeta"):
+        assert np.array_equal(a[k], c[k]), k
+        assert np.array_equal(a[k], d[k]), k
+
+
 def test_layernorm_backward_split_rows_workspace_reused_across_calls():
     """Calls that share one workspace, with different inputs in between,
     never read an earlier call's sums: every call matches the oracle, and
